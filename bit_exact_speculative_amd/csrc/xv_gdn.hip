@@ -1,0 +1,195 @@
+// xv_gdn.hip -- gated-delta-net verify and rollback on an fp32 state.
+//
+// The post's first verify change: verify must run the GDN recurrence with the
+// decode arithmetic, because the old verify kernel tiled the state in another
+// order and used a different beta precision.  Here there is exactly one
+// per-token routine, xv_gdn_token(), used by decode (T = 1), verify (any T) and
+// the rollback recompute; its dk-reduction order is fixed at compile time and
+// depends on nothing but dk.
+//
+// Per value head h, value index j, the column S[j][0..dk) evolves on its own:
+//     s_i <- a s_i                         (decay, one fp32 multiply each)
+//     kv   = sum_i s_i k_i                 (fixed-order dot, below)
+//     u    = b (v_j - kv)
+//     s_i <- fma(u, k_i, s_i)
+//     o_j  = sum_i s_i q_i                 (same fixed-order dot)
+// which is S_t = a S_{t-1} (I - b k k^T) + b v k^T, o = S_t q.
+//
+// Work mapping (gfx950, wave64): a workgroup of 4 waves owns 32 value indices
+// of one (request, value head); in a wave, 8 lanes share one j and each holds
+// R = dk/8 consecutive key indices of the column in VGPRs, for the whole call.
+// The fixed dot order: in each lane four fp32 chains over i mod 4 in ascending
+// i, combined as (c0 + c1) + (c2 + c3); then a butterfly over the 8 lanes
+// (xor 1, 2, 4).  Every lane ends with the same bits, so all lanes of a column
+// compute the same u.  The state is read once and written once per call.
+#include "xv_common.h"
+
+namespace {
+
+constexpr int XV_GDN_JW = 32;       // value indices per workgroup (4 waves x 8)
+
+template <int R>
+__device__ __forceinline__ float xv_gdn_dot(const float (&s)[R], const float (&x)[R]) {
+    float c0 = s[0] * x[0];
+    float c1 = s[1] * x[1];
+    float c2 = s[2] * x[2];
+    float c3 = s[3] * x[3];
+#pragma unroll
+    for (int r = 4; r < R; r += 4) {
+        c0 = __builtin_fmaf(s[r + 0], x[r + 0], c0);
+        c1 = __builtin_fmaf(s[r + 1], x[r + 1], c1);
+        c2 = __builtin_fmaf(s[r + 2], x[r + 2], c2);
+        c3 = __builtin_fmaf(s[r + 3], x[r + 3], c3);
+    }
+    float p = (c0 + c1) + (c2 + c3);
+    p = p + __shfl_xor(p, 1);
+    p = p + __shfl_xor(p, 2);
+    p = p + __shfl_xor(p, 4);
+    return p;
+}
+
+// The one per-token state update (decode, verify and rollback all call this).
+template <int R>
+__device__ __forceinline__ void xv_gdn_token(float (&s)[R], const float (&kk)[R],
+                                             float vj, float at, float bt) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = at * s[r];
+    const float kv = xv_gdn_dot<R>(s, kk);
+    const float u = bt * (vj - kv);
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = __builtin_fmaf(u, kk[r], s[r]);
+}
+
+template <int R>
+__device__ __forceinline__ void xv_load_bf16_row(const uint16_t* p, float (&out)[R]) {
+#pragma unroll
+    for (int c = 0; c < R / 8; ++c) {
+        const xv_u32x4 v = xv_load16(p + c * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            out[c * 8 + 2 * e] = xv_bf16_lo(v[e]);
+            out[c * 8 + 2 * e + 1] = xv_bf16_hi(v[e]);
+        }
+    }
+}
+
+// ROLLBACK = false: verify of T tokens from state_in, writes o (and o32) and S_T.
+// ROLLBACK = true : n = n_keep[b]; n == T leaves state_out; otherwise recomputes
+//                   S_n from state_in; kv_len[b] += n.
+template <int DK, bool ROLLBACK>
+__global__ __launch_bounds__(256)
+void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                   const uint16_t* __restrict__ v, const float* __restrict__ a,
+                   const float* __restrict__ beta, const float* __restrict__ S_in,
+                   float* __restrict__ S_out, uint16_t* __restrict__ o, float* __restrict__ o32,
+                   int T, int Hk, int Hv, int dv, int32_t* __restrict__ kv_len,
+                   const int32_t* __restrict__ n_keep)
+{
+    constexpr int R = DK / 8;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int ig = lane & 7;                 // key-index group: i in [ig*R, ig*R + R)
+    const int jl = lane >> 3;
+    const int j = blockIdx.x * XV_GDN_JW + wave * 8 + jl;
+    const int h = blockIdx.y;
+    const int b = blockIdx.z;
+    const int g = h / (Hv / Hk);
+
+    int n = T;
+    if (ROLLBACK) {
+        n = n_keep[b];
+        n = n < 0 ? 0 : (n > T ? T : n);
+        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) kv_len[b] += n;
+        if (n == T) return;                  // state_out already holds S_T
+    }
+
+    const size_t sbase = ((size_t)(b * Hv + h) * DK + ig * R) * dv + j;
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = S_in[sbase + (size_t)r * dv];
+
+    for (int t = 0; t < n; ++t) {
+        const size_t row = (size_t)b * T + t;
+        float kk[R];
+        xv_load_bf16_row<R>(k + (row * Hk + g) * DK + ig * R, kk);
+        const float vj = xv_bf16_to_f32(v[(row * Hv + h) * dv + j]);
+        const float at = a[row * Hv + h];
+        const float bt = beta[row * Hv + h];
+        xv_gdn_token<R>(s, kk, vj, at, bt);
+        if (!ROLLBACK) {
+            float qq[R];
+            xv_load_bf16_row<R>(q + (row * Hk + g) * DK + ig * R, qq);
+            const float ot = xv_gdn_dot<R>(s, qq);
+            if (ig == 0) {
+                const size_t oi = (row * Hv + h) * dv + j;
+                o[oi] = xv_f32_to_bf16(ot);
+                if (o32) o32[oi] = ot;
+            }
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < R; ++r) S_out[sbase + (size_t)r * dv] = s[r];
+}
+
+int xv_gdn_check(const void* k, const void* v, const void* a, const void* b,
+                 const void* sin, const void* sout, int B, int T, int Hk, int Hv, int dk, int dv)
+{
+    XV_REQUIRE(B >= 0 && T >= 1 && T <= 16 && Hk >= 1 && Hv >= 1 && Hv % Hk == 0, XV_ERR_SHAPE);
+    XV_REQUIRE(dk == 64 || dk == 128, XV_ERR_SHAPE);
+    XV_REQUIRE(dv >= 32 && dv <= 128 && dv % 32 == 0, XV_ERR_SHAPE);
+    if (B == 0) return XV_OK;
+    XV_REQUIRE(k && v && a && b && sin && sout, XV_ERR_NULL);
+    XV_REQUIRE(xv_aligned16(k) && xv_aligned(v, 2) && xv_aligned(a, 4) && xv_aligned(b, 4) &&
+               xv_aligned(sin, 4) && xv_aligned(sout, 4), XV_ERR_ALIGN);
+    XV_REQUIRE(sin != sout, XV_ERR_ALIAS);
+    return XV_OK;
+}
+
+template <bool ROLLBACK>
+int xv_gdn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* a,
+                  const float* beta, const float* S_in, float* S_out, uint16_t* o, float* o32,
+                  int B, int T, int Hk, int Hv, int dk, int dv, int32_t* kv_len,
+                  const int32_t* n_keep, hipStream_t st)
+{
+    dim3 grid(dv / XV_GDN_JW, Hv, B), block(256);
+    (void)hipGetLastError();
+    if (dk == 128)
+        hipLaunchKernelGGL((xv_gdn_kernel<128, ROLLBACK>), grid, block, 0, st, q, k, v, a, beta,
+                           S_in, S_out, o, o32, T, Hk, Hv, dv, kv_len, n_keep);
+    else
+        hipLaunchKernelGGL((xv_gdn_kernel<64, ROLLBACK>), grid, block, 0, st, q, k, v, a, beta,
+                           S_in, S_out, o, o32, T, Hk, Hv, dv, kv_len, n_keep);
+    return xv_launch_status();
+}
+
+}  // namespace
+
+extern "C" int xv_gdn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const float* a, const float* b,
+                             const float* state_in, float* state_out,
+                             uint16_t* o, float* o32,
+                             int B, int T, int Hk, int Hv, int dk, int dv, void* stream)
+{
+    int s = xv_gdn_check(k, v, a, b, state_in, state_out, B, T, Hk, Hv, dk, dv);
+    if (s != XV_OK || B == 0) return s;
+    XV_REQUIRE(q && o, XV_ERR_NULL);
+    XV_REQUIRE(xv_aligned16(q) && xv_aligned(o, 2) && xv_aligned(o32, 4), XV_ERR_ALIGN);
+    return xv_gdn_launch<false>(q, k, v, a, b, state_in, state_out, o, o32, B, T, Hk, Hv, dk, dv,
+                                nullptr, nullptr, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int xv_rollback_to_prefix(const uint16_t* k, const uint16_t* v,
+                                     const float* a, const float* b,
+                                     const float* state_in, float* state_out,
+                                     int32_t* kv_len, const int32_t* n_keep,
+                                     int B, int T, int Hk, int Hv, int dk, int dv, void* stream)
+{
+    int s = xv_gdn_check(k, v, a, b, state_in, state_out, B, T, Hk, Hv, dk, dv);
+    if (s != XV_OK || B == 0) return s;
+    XV_REQUIRE(kv_len && n_keep, XV_ERR_NULL);
+    XV_REQUIRE(xv_aligned(kv_len, 4) && xv_aligned(n_keep, 4), XV_ERR_ALIGN);
+    return xv_gdn_launch<true>(nullptr, k, v, a, b, state_in, state_out, nullptr, nullptr,
+                               B, T, Hk, Hv, dk, dv, kv_len, n_keep,
+                               reinterpret_cast<hipStream_t>(stream));
+}

@@ -17,9 +17,11 @@ with the shapes and lengths the recipe card and the post give):
           repeatability prompts of the post), accepted lengths uniform 0..8
   long    the same shapes with 127735 cached tokens (the card's long prompt)
 
-Draw order (numpy PCG64 seeded with the workload index, every draw fp32
-standard normal unless stated), fixed so that a change of capacity (Lmax) or
-of workspace does not move any value:
+Draw order.  Two numpy PCG64 streams come from SeedSequence(workload index):
+stream A draws items 1-5 and stream B items 6-7 (so skipping the large weight
+draws never moves the draft ids).  Every draw is fp32 standard normal unless
+stated; the order is fixed, and no capacity (Lmax) or workspace choice moves a
+value:
    1. GDN prefix rows (32 tokens): q, k [B][32][Hk][dk]; v [B][32][Hv][dv];
       raw decay [B][32][Hv]; raw beta [B][32][Hv]
    2. GDN verify rows: q, k, v, raw decay, raw beta, same layouts with T rows
@@ -28,8 +30,8 @@ of workspace does not move any value:
       KV head g the cached keys [L0_b][d] followed by the cached values [L0_b][d]
    4. GEMM: x [M][K]; W1 [N1][K] * 0.02; W2 [N2][K] * 0.02
    5. synthetic head: W_head_gdn [NH][Hv*dv] * 0.02; W_head_attn [NH][Hq*d] * 0.02
-   6. draft ids [B][T] uniform integers in [0, NH)
-   7. batch8 only: accepted draft counts uniform integers 0..k
+   6. (stream B) draft ids [B][T] uniform integers in [0, NH)
+   7. (stream B) batch8 only: accepted draft counts uniform integers 0..k
 
 Input recipe: q and k are L2-normalised per (token, head) vector in fp64, then
 rounded to fp32 and then to bf16 (round to nearest even); v, x, caches and
@@ -178,7 +180,9 @@ def make_inputs(wl: Workload, *, Lmax: Optional[int] = None, pad_value: int = BF
     with_gemm / with_head=False skip the (large) weight draws; they come last in
     the draw order, so skipping them changes nothing else.
     """
-    rng = np.random.Generator(np.random.PCG64(wl.seed))
+    sa, sb = np.random.SeedSequence(wl.seed).spawn(2)
+    rng = np.random.Generator(np.random.PCG64(sa))
+    rng_ids = np.random.Generator(np.random.PCG64(sb))
     B, T = wl.B, wl.T
     prefix = gdn_rows(rng, B, PREFIX_TOKENS, wl.Hk, wl.Hv, wl.dk, wl.dv)
     gdn = gdn_rows(rng, B, T, wl.Hk, wl.Hv, wl.dk, wl.dv)
@@ -203,6 +207,9 @@ def make_inputs(wl: Workload, *, Lmax: Optional[int] = None, pad_value: int = BF
             v_cache[bb, g, :n] = f32_to_bf16_bits(_normal(rng, (n, wl.d)))
     inp = Inputs(wl=wl, prefix=prefix, gdn=gdn, L0=L0, Lmax=Lmax, q_attn=q_attn,
                  k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache)
+    inp.draft = rng_ids.integers(0, wl.NH, size=(B, T), dtype=np.int64).astype(np.int32)
+    if wl.accept_draw:
+        inp.accepted = rng_ids.integers(0, wl.k_drafts + 1, size=B, dtype=np.int64).astype(np.int32)
     if not with_gemm:
         return inp
     inp.x = f32_to_bf16_bits(_normal(rng, (wl.M, wl.K)))
@@ -212,9 +219,6 @@ def make_inputs(wl: Workload, *, Lmax: Optional[int] = None, pad_value: int = BF
         return inp
     inp.Wh_gdn = f32_to_bf16_bits(_normal(rng, (wl.NH, wl.Hv * wl.dv), 0.02))
     inp.Wh_attn = f32_to_bf16_bits(_normal(rng, (wl.NH, wl.Hq * wl.d), 0.02))
-    inp.draft = rng.integers(0, wl.NH, size=(B, T), dtype=np.int64).astype(np.int32)
-    if wl.accept_draw:
-        inp.accepted = rng.integers(0, wl.k_drafts + 1, size=B, dtype=np.int64).astype(np.int32)
     return inp
 
 

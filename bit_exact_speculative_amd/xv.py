@@ -1,0 +1,175 @@
+"""Thin Python binding of libxv (ctypes).  Argument marshalling only.
+
+Every function has the name of the C entry point it calls and takes device
+tensors (PyTorch is used for device memory and streams, nothing else).  Sizes
+are read from the tensor shapes, pointers from ``data_ptr()``, the stream from
+``torch.cuda.current_stream()`` unless one is given.  A non-zero status from the
+library raises :class:`XvError`.  There is no fallback of any kind: if libxv.so
+is missing this module fails to import.
+
+bf16 tensors may be ``torch.bfloat16`` or ``torch.int16`` / ``torch.uint16``
+bit views; fp32 tensors are ``torch.float32``; lengths and ids ``torch.int32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libxv.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "xv.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libxv.so is not built (%s); run __graft_entry__.build() first" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+
+_lib.xv_abi_version.restype = _I
+_lib.xv_abi_version.argtypes = []
+_lib.xv_status_string.restype = ctypes.c_char_p
+_lib.xv_status_string.argtypes = [_I]
+_lib.xv_gemm_small_m.restype = _I
+_lib.xv_gemm_small_m.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P]
+_lib.xv_gdn_verify.restype = _I
+_lib.xv_gdn_verify.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
+_lib.xv_attn_chunk_tokens.restype = _I
+_lib.xv_attn_chunk_tokens.argtypes = []
+_lib.xv_attn_workspace_bytes.restype = _S
+_lib.xv_attn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+_lib.xv_attn_verify_rows.restype = _I
+_lib.xv_attn_verify_rows.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+                                     _I, _I, _I, _I, _I, _I, _F, _P]
+_lib.xv_rollback_to_prefix.restype = _I
+_lib.xv_rollback_to_prefix.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
+_lib.xv_greedy_accept.restype = _I
+_lib.xv_greedy_accept.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P]
+
+XV_OK = 0
+STATUS = {0: "XV_OK", -1: "XV_ERR_NULL", -2: "XV_ERR_SHAPE", -3: "XV_ERR_ALIGN",
+          -4: "XV_ERR_WORKSPACE", -5: "XV_ERR_LAUNCH", -6: "XV_ERR_ALIAS"}
+
+
+class XvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = _lib.xv_status_string(status).decode()
+        super().__init__("%s failed: %s (%s)" % (fn, STATUS.get(status, status), msg))
+
+
+def lib():
+    """The loaded ctypes library (for raw-pointer calls)."""
+    return _lib
+
+
+def exported_symbols_from_header(path: str = HEADER_PATH):
+    """Names of every function the C header declares."""
+    src = open(path).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(xv_[a-z0-9_]+)\s*\(", src)))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libxv must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != XV_OK:
+        raise XvError(fn, status)
+
+
+def xv_abi_version() -> int:
+    return _lib.xv_abi_version()
+
+
+def xv_attn_chunk_tokens() -> int:
+    return _lib.xv_attn_chunk_tokens()
+
+
+def xv_attn_workspace_bytes(B: int, T: int, Hq: int, d: int, Lmax: int) -> int:
+    return int(_lib.xv_attn_workspace_bytes(B, T, Hq, d, Lmax))
+
+
+def xv_gemm_small_m(x, w, y, y32=None, stream=None):
+    """y[M][N] (bf16) = x[M][K] @ w[N][K]^T; y32 optional fp32 copy before rounding."""
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or tuple(y.shape) != (M, N) or (y32 is not None and tuple(y32.shape) != (M, N)):
+        raise ValueError("xv_gemm_small_m: shape mismatch")
+    _check("xv_gemm_small_m", _lib.xv_gemm_small_m(_ptr(x), _ptr(w), _ptr(y), _ptr(y32),
+                                                  M, N, K, _stream(stream)))
+
+
+def xv_gdn_verify(q, k, v, a, b, state_in, state_out, o, o32=None, stream=None):
+    """Gated delta rule over T rows: shapes q,k [B][T][Hk][dk], v [B][T][Hv][dv], ..."""
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, T, Hk, dk) or tuple(v.shape[:2]) != (B, T) or \
+            tuple(a.shape) != (B, T, Hv) or tuple(b.shape) != (B, T, Hv) or \
+            tuple(state_in.shape) != (B, Hv, dk, dv) or tuple(state_out.shape) != (B, Hv, dk, dv) or \
+            tuple(o.shape) != (B, T, Hv, dv) or (o32 is not None and tuple(o32.shape) != (B, T, Hv, dv)):
+        raise ValueError("xv_gdn_verify: shape mismatch")
+    _check("xv_gdn_verify", _lib.xv_gdn_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                              _ptr(state_in), _ptr(state_out), _ptr(o), _ptr(o32),
+                                              B, T, Hk, Hv, dk, dv, _stream(stream)))
+
+
+def xv_attn_verify_rows(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32=None, workspace=None,
+                        scale=None, stream=None):
+    """Attention rows + KV append.  q [B][T][Hq][d]; caches [B][Hkv][Lmax][d]; kv_len int32 [B]."""
+    B, T, Hq, d = q.shape
+    Hkv = k_new.shape[2]
+    Lmax = k_cache.shape[2]
+    if tuple(k_new.shape) != (B, T, Hkv, d) or tuple(v_new.shape) != (B, T, Hkv, d) or \
+            tuple(k_cache.shape) != (B, Hkv, Lmax, d) or tuple(v_cache.shape) != (B, Hkv, Lmax, d) or \
+            tuple(kv_len.shape) != (B,) or tuple(o.shape) != (B, T, Hq, d) or \
+            (o32 is not None and tuple(o32.shape) != (B, T, Hq, d)):
+        raise ValueError("xv_attn_verify_rows: shape mismatch")
+    if workspace is None:
+        raise ValueError("xv_attn_verify_rows: a workspace tensor is required")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    wbytes = workspace.numel() * workspace.element_size()
+    _check("xv_attn_verify_rows", _lib.xv_attn_verify_rows(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
+        _ptr(o), _ptr(o32), _ptr(workspace), wbytes, B, T, Hq, Hkv, d, Lmax, float(scale),
+        _stream(stream)))
+
+
+def xv_rollback_to_prefix(k, v, a, b, state_in, state_out, kv_len, n_keep, stream=None):
+    """Keep n_keep[b] verify rows: state_out <- S_n, kv_len += n."""
+    B, T, Hk, dk = k.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if tuple(state_in.shape) != (B, Hv, dk, dv) or tuple(state_out.shape) != (B, Hv, dk, dv) or \
+            tuple(kv_len.shape) != (B,) or tuple(n_keep.shape) != (B,):
+        raise ValueError("xv_rollback_to_prefix: shape mismatch")
+    _check("xv_rollback_to_prefix", _lib.xv_rollback_to_prefix(
+        _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(state_in), _ptr(state_out), _ptr(kv_len),
+        _ptr(n_keep), B, T, Hk, Hv, dk, dv, _stream(stream)))
+
+
+def xv_greedy_accept(logits_a, logits_b, draft, ids, n_keep, stream=None):
+    """ids = argmax(logits_a + logits_b) per row (lowest index on ties); n_keep per request."""
+    B, T, N = logits_a.shape
+    if (logits_b is not None and tuple(logits_b.shape) != (B, T, N)) or tuple(draft.shape) != (B, T) \
+            or tuple(ids.shape) != (B, T) or tuple(n_keep.shape) != (B,):
+        raise ValueError("xv_greedy_accept: shape mismatch")
+    _check("xv_greedy_accept", _lib.xv_greedy_accept(_ptr(logits_a), _ptr(logits_b), _ptr(draft),
+                                                    B, T, N, _ptr(ids), _ptr(n_keep), _stream(stream)))

@@ -1,0 +1,181 @@
+/*
+ * xv.h -- C ABI of libxv, the batch-invariant speculative-decoding verify step
+ * for one hybrid (gated-delta-net + attention) layer on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What the library guarantees.  The r/LocalLLaMA post on bit-exact speculative
+ * decoding of Qwen3.8-27B (feedman.me mirror; the paragraph on the two verify
+ * changes) makes a k-draft verify reproduce k single-token decode steps bit for
+ * bit by running the decode arithmetic in verify: the GDN recurrence through
+ * the decode kernel, attention as one decode row per draft position, and (the
+ * DeepGEMM paragraph of the same post) small-M projection GEMMs through one
+ * tile that gives the same bits at every M.  Every entry point here has ONE
+ * code path whose per-row arithmetic does not depend on the number of rows
+ * (T or M), the batch size, the row's position in a tile, the cache capacity
+ * or the workspace size.  Decode is simply T = 1 (or M = 1).
+ *
+ * Conventions (all entry points):
+ *  - bf16 tensors are passed as uint16_t bit patterns; fp32 as float.
+ *  - Every pointer is a DEVICE pointer owned by the caller, dense (C order) in
+ *    the stated layout.  Tensors marked [16B] are read or written with 16-byte
+ *    vector accesses and must be 16-byte aligned; every other pointer must be
+ *    aligned to its element size (2 for bf16, 4 for fp32 / int32), else
+ *    XV_ERR_ALIGN.  Nothing is retained after return.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream), allocates nothing and never synchronises.
+ *  - Arguments are validated on the host before any launch; a failed check
+ *    returns a negative xv_status and launches nothing.  Device-resident values
+ *    (kv_len, n_keep) cannot be checked on the host: their preconditions are
+ *    stated per call, and kernels clamp them so that no access leaves its
+ *    buffer even when a precondition is broken (results are then undefined).
+ *  - Stateless and thread-safe; concurrent calls on different streams are
+ *    independent as long as their output buffers do not overlap.
+ *  - An empty problem (B == 0 or M == 0) returns XV_OK and launches nothing.
+ */
+#ifndef XV_H
+#define XV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define XV_ABI_VERSION 1
+
+typedef enum {
+    XV_OK = 0,
+    XV_ERR_NULL = -1,       /* a required pointer is NULL                         */
+    XV_ERR_SHAPE = -2,      /* a size is outside the supported set (see each call) */
+    XV_ERR_ALIGN = -3,      /* a pointer breaks its alignment rule                 */
+    XV_ERR_WORKSPACE = -4,  /* workspace smaller than xv_attn_workspace_bytes()    */
+    XV_ERR_LAUNCH = -5,     /* the HIP runtime rejected a kernel launch            */
+    XV_ERR_ALIAS = -6       /* an output buffer is the same as an input it must not overwrite */
+} xv_status;
+
+/* Version of this ABI (XV_ABI_VERSION) and a static message for a status code. */
+int xv_abi_version(void);
+const char* xv_status_string(int status);
+
+/*
+ * Small-M projection GEMM:  y[m][n] = bf16( sum_k x[m][k] * w[n][k] ).
+ * The post's DeepGEMM paragraph (weights read at a third of DRAM bandwidth at
+ * small batch, the fix being a tile that gives the same bits) and the recipe
+ * card's runtime env (the M <= 16 gate).
+ *
+ *   x   : bf16 [M][K]   [16B]  activations (rows = verify rows of all requests)
+ *   w   : bf16 [N][K]   [16B]  weights, one output feature per row (K contiguous)
+ *   y   : bf16 [M][N]          output, fp32 sum rounded to nearest even
+ *   y32 : fp32 [M][N] or NULL  the same sums before rounding
+ * Rows are processed in tiles of 16 ([0,16), [16,32), ...; the last may be
+ * partial), all tiles against one pass over w.  The bits of row m depend only
+ * on x[m][:], w and K: not on M, on the other rows, or on m's place in a tile.
+ * Shapes: M >= 0, N >= 16 and N % 16 == 0, K >= 32 and K % 32 == 0.
+ */
+int xv_gemm_small_m(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
+                    int M, int N, int K, void* stream);
+
+/*
+ * GDN verify: T tokens of the gated delta rule per request, fp32 state.
+ * The post, the two verify changes (the GDN recurrence through the decode
+ * arithmetic, the old verify kernel having tiled the state differently and
+ * kept a different beta precision); the state is fp32 (post, launch command,
+ * the mamba SSM dtype flag).  Rule, per value head h (key head g = h / (Hv/Hk)),
+ * per token t:
+ *     S <- a_t S ;  u = b_t (v_t - S k_t) ;  S <- S + u k_t^T ;  o_t = S q_t
+ * which equals S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T.
+ * Decode is T = 1; verify of k drafts is T = k + 1.
+ *
+ *   q, k      : bf16 [B][T][Hk][dk]    [16B] (L2-normalised by the caller)
+ *   v         : bf16 [B][T][Hv][dv]
+ *   a, b      : fp32 [B][T][Hv]        decay and beta, already activated
+ *   state_in  : fp32 [B][Hv][dk][dv]   S_0, element (value j, key i) at [i][j]; read only
+ *   state_out : fp32 [B][Hv][dk][dv]   S_T; must not be state_in (XV_ERR_ALIAS)
+ *   o         : bf16 [B][T][Hv][dv]    outputs o_t rounded to nearest even
+ *   o32       : fp32 [B][T][Hv][dv] or NULL
+ * Shapes: B >= 0, 1 <= T <= 16, Hk >= 1, Hv % Hk == 0, dk in {64, 128},
+ * dv in {32, 64, 96, 128} (multiple of 32, at most 128).
+ */
+int xv_gdn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                  const float* a, const float* b,
+                  const float* state_in, float* state_out,
+                  uint16_t* o, float* o32,
+                  int B, int T, int Hk, int Hv, int dk, int dv, void* stream);
+
+/*
+ * Attention verify rows with the KV append.
+ * The post, the two verify changes (verify attention as one decode row per
+ * draft position) and the launch command (BF16 KV cache).  Request b holds
+ * L0 = kv_len[b] cached positions.  The T new key/value rows are written to
+ * cache positions L0..L0+T-1, and row r (query head h, KV head h / (Hq/Hkv))
+ * attends positions 0..L0+r:  o = sum_j softmax_j(scale * q.k_j) v_j.
+ * The context is split into chunks of xv_attn_chunk_tokens() positions at
+ * absolute boundaries; per chunk the partial (max, sum, weighted values) is
+ * formed in a fixed order, and the chunks are merged in ascending order
+ * against the row's overall maximum.  All of it depends on the row's length
+ * and data only, never on T, B, Lmax or the workspace size.
+ *
+ *   q        : bf16 [B][T][Hq][d]      [16B]
+ *   k_new    : bf16 [B][T][Hkv][d]     [16B]  v_new: same
+ *   k_cache  : bf16 [B][Hkv][Lmax][d]  [16B]  v_cache: same; rows L0..L0+T-1 are written
+ *   kv_len   : int32 [B] device        L0 per request; read only
+ *   o        : bf16 [B][T][Hq][d]
+ *   o32      : fp32 [B][T][Hq][d] or NULL
+ *   workspace: [16B] device scratch of workspace_bytes >= xv_attn_workspace_bytes(B,T,Hq,d,Lmax)
+ * Shapes: B >= 0, 1 <= T <= 16, Hq % Hkv == 0, (Hq/Hkv) * T <= 128,
+ * d in {64, 128, 256}, Lmax >= T.  Device precondition: 0 <= L0 and
+ * L0 + T <= Lmax (kernels clamp positions to the buffer otherwise).
+ * Cache positions >= L0 + T are never read, so they may hold anything.
+ */
+int    xv_attn_chunk_tokens(void);
+size_t xv_attn_workspace_bytes(int B, int T, int Hq, int d, int Lmax);
+int    xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                           uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
+                           uint16_t* o, float* o32, void* workspace, size_t workspace_bytes,
+                           int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
+                           void* stream);
+
+/*
+ * Rollback to the accepted prefix.
+ * The post: the exactness held also with every draft forced to reject and
+ * with 8 requests in flight, i.e. keeping any prefix of the verify rows must
+ * leave exactly the state sequential decode would have.  For request b with
+ * n = n_keep[b] kept rows (0 <= n <= T):
+ *   n == T      : state_out already holds S_T; left as is
+ *   n == 0      : state_out <- state_in (bit copy)
+ *   0 < n < T   : state_out <- S_n, recomputed from state_in over rows 0..n-1
+ *                 with the per-token arithmetic of xv_gdn_verify
+ *   kv_len[b]  <- kv_len[b] + n
+ * The argument arrays are those of the xv_gdn_verify call being rolled back
+ * (q is not needed; k is [16B]).
+ *   state_out : in S_T, out S_n; must not be state_in
+ *   kv_len    : int32 [B] device, updated in place
+ *   n_keep    : int32 [B] device; values outside [0, T] are clamped
+ * Shapes as xv_gdn_verify.
+ */
+int xv_rollback_to_prefix(const uint16_t* k, const uint16_t* v,
+                          const float* a, const float* b,
+                          const float* state_in, float* state_out,
+                          int32_t* kv_len, const int32_t* n_keep,
+                          int B, int T, int Hk, int Hv, int dk, int dv, void* stream);
+
+/*
+ * Greedy acceptance at temperature 0 on device (the post compares token ids of
+ * greedy decoding).  logits[b][t][n] = logits_a[...] + logits_b[...] (one fp32
+ * add; logits_b may be NULL).  ids[b][t] = the lowest n among the maxima of row
+ * (b, t).  Row t consumed input token draft[b][t] (draft[b][0] is the root);
+ * draft t+1 is accepted when it equals ids[b][t] and all earlier drafts were
+ * accepted.  n_keep[b] = 1 + accepted drafts (the verify rows to keep, ready
+ * for xv_rollback_to_prefix).
+ *   logits_a, logits_b : fp32 [B][T][N]     draft : int32 [B][T]
+ *   ids : int32 [B][T]   n_keep : int32 [B]
+ * Shapes: B >= 0, 1 <= T <= 16, N >= 1.  Logits must be finite.
+ */
+int xv_greedy_accept(const float* logits_a, const float* logits_b, const int32_t* draft,
+                     int B, int T, int N, int32_t* ids, int32_t* n_keep, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* XV_H */

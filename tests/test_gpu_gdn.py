@@ -1,0 +1,150 @@
+"""xv_gdn_verify / xv_rollback_to_prefix on the GPU: oracle parity, verify == sequential
+decode bit for bit for every T, exact rollback to every prefix, batch invariance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_exact_speculative_amd.inputs import f32_to_bf16_bits, random_gdn
+from tests.gpu_util import OUT_MAX_REL, STATE_REL_L2, max_rel, rel_l2, same_bits, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _xv():
+    import bit_exact_speculative_amd.xv as xv
+    return xv
+
+
+def _dev(r):
+    from bit_exact_speculative_amd.layer import dev, dev_bf16
+    return dict(q=dev_bf16(r["q"], "cuda"), k=dev_bf16(r["k"], "cuda"), v=dev_bf16(r["v"], "cuda"),
+                a=dev(r["a"], "cuda"), b=dev(r["b"], "cuda"))
+
+
+def _verify(d, S_in):
+    B, T, Hk, dk = d["q"].shape
+    Hv, dv = d["v"].shape[2], d["v"].shape[3]
+    S_out = torch.empty_like(S_in)
+    o = torch.empty((B, T, Hv, dv), dtype=torch.bfloat16, device="cuda")
+    o32 = torch.empty((B, T, Hv, dv), dtype=torch.float32, device="cuda")
+    _xv().xv_gdn_verify(d["q"], d["k"], d["v"], d["a"], d["b"], S_in, S_out, o, o32)
+    return o, o32, S_out
+
+
+def _decode(d, S_in, n):
+    """n single-token steps (T = 1) from S_in; per-token outputs and states."""
+    S = S_in.clone()
+    os_, o32s, Ss = [], [], []
+    for t in range(n):
+        dt = {k: v[:, t:t + 1].contiguous() for k, v in d.items()}
+        o, o32, S = _verify(dt, S)
+        os_.append(o[:, 0]); o32s.append(o32[:, 0]); Ss.append(S)
+    return torch.stack(os_, 1), torch.stack(o32s, 1), Ss
+
+
+def _case(seed, B, T, Hk, Hv, dk, dv):
+    rng = np.random.default_rng(seed)
+    r = random_gdn(rng, B, T, Hk, Hv, dk, dv)
+    S0 = (rng.standard_normal((B, Hv, dk, dv)) * 0.05).astype(np.float32)
+    return r, S0
+
+
+@pytest.mark.parametrize("shape", [(1, 5, 2, 4, 64, 64), (2, 9, 2, 6, 128, 128), (1, 3, 1, 2, 64, 32),
+                                   (3, 16, 2, 4, 128, 96), (1, 1, 4, 4, 128, 128)])
+def test_gdn_matches_oracle(shape):
+    B, T, Hk, Hv, dk, dv = shape
+    r, S0 = _case(sum(shape), *shape)
+    d = _dev(r)
+    o, o32, S = _verify(d, torch.from_numpy(S0).cuda())
+    torch.cuda.synchronize()
+    o_ref, S_ref, _ = oracle.gdn(r["q"], r["k"], r["v"], r["a"], r["b"], S0)
+    assert rel_l2(S.cpu().numpy(), S_ref) <= STATE_REL_L2
+    assert max_rel(o32.cpu().numpy(), o_ref) <= OUT_MAX_REL
+    from bit_exact_speculative_amd.layer import host_bits
+    assert np.array_equal(host_bits(o), f32_to_bf16_bits(o32.cpu().numpy()))
+
+
+def test_gdn_real_shapes_vs_oracle():
+    """16 key / 48 value heads, d = 128, 9 rows, from the oracle's 32-token prefix state."""
+    inp, S0 = workload("short", gemm=False, head=False)
+    d = _dev(inp.gdn)
+    o, o32, S = _verify(d, torch.from_numpy(S0).cuda())
+    torch.cuda.synchronize()
+    g = inp.gdn
+    o_ref, S_ref, Sall = oracle.gdn(g["q"], g["k"], g["v"], g["a"], g["b"], S0, want_all=True)
+    assert rel_l2(S.cpu().numpy(), S_ref) <= STATE_REL_L2
+    assert max_rel(o32.cpu().numpy(), o_ref) <= OUT_MAX_REL
+
+
+@pytest.mark.parametrize("T", list(range(1, 17)))
+def test_gdn_verify_equals_sequential_decode(T):
+    r, S0 = _case(500 + T, 2, T, 2, 4, 128, 128)
+    d = _dev(r)
+    S_in = torch.from_numpy(S0).cuda()
+    o, o32, S = _verify(d, S_in)
+    od, o32d, Sd = _decode(d, S_in, T)
+    torch.cuda.synchronize()
+    assert same_bits(o, od) and same_bits(o32, o32d) and same_bits(S, Sd[-1])
+
+
+@pytest.mark.parametrize("dk", [64, 128])
+def test_rollback_every_prefix(dk):
+    T = 9
+    r, S0 = _case(600 + dk, 3, T, 2, 4, dk, 64)
+    d = _dev(r)
+    S_in = torch.from_numpy(S0).cuda()
+    _, _, S_T = _verify(d, S_in)
+    _, _, Sd = _decode(d, S_in, T)
+    for n in range(0, T + 1):
+        for mix in (False, True):
+            nk = [n, n, n] if not mix else [n, (n + 4) % (T + 1), T - n]
+            S_out = S_T.clone()
+            kv = torch.tensor([100, 0, 7], dtype=torch.int32, device="cuda")
+            n_keep = torch.tensor(nk, dtype=torch.int32, device="cuda")
+            _xv().xv_rollback_to_prefix(d["k"], d["v"], d["a"], d["b"], S_in, S_out, kv, n_keep)
+            torch.cuda.synchronize()
+            assert kv.tolist() == [100 + nk[0], 0 + nk[1], 7 + nk[2]]
+            for bb in range(3):
+                want = S_in[bb] if nk[bb] == 0 else Sd[nk[bb] - 1][bb]
+                assert same_bits(S_out[bb], want), (n, mix, bb)
+
+
+def test_rollback_oracle_parity_and_clamp():
+    T = 9
+    r, S0 = _case(700, 2, T, 2, 4, 128, 128)
+    d = _dev(r)
+    S_in = torch.from_numpy(S0).cuda()
+    _, _, S_T = _verify(d, S_in)
+    kv = torch.tensor([5, 6], dtype=torch.int32, device="cuda")
+    n_keep = torch.tensor([4, 99], dtype=torch.int32, device="cuda")      # 99 is clamped to T
+    S_out = S_T.clone()
+    _xv().xv_rollback_to_prefix(d["k"], d["v"], d["a"], d["b"], S_in, S_out, kv, n_keep)
+    torch.cuda.synchronize()
+    Sn, kv_ref = oracle.rollback(r["k"], r["v"], r["a"], r["b"], S0, np.array([5, 6], np.int32),
+                                 np.array([4, 9], np.int32))
+    assert kv.tolist() == [9, 15] and kv_ref.tolist() == [9, 15]
+    assert rel_l2(S_out.cpu().numpy(), Sn) <= STATE_REL_L2
+    assert same_bits(S_out[1], S_T[1])
+
+
+def test_gdn_batch_invariance():
+    """Every request of a batch of 8 gets the bits it gets alone."""
+    r, S0 = _case(800, 8, 9, 2, 4, 128, 128)
+    d = _dev(r)
+    S_in = torch.from_numpy(S0).cuda()
+    o, o32, S = _verify(d, S_in)
+    for bb in range(8):
+        db = {k: v[bb:bb + 1].contiguous() for k, v in d.items()}
+        o1, o321, S1 = _verify(db, S_in[bb:bb + 1].contiguous())
+        assert same_bits(o1[0], o[bb]) and same_bits(o321[0], o32[bb]) and same_bits(S1[0], S[bb])
+
+
+def test_gdn_repeatable():
+    r, S0 = _case(900, 2, 9, 2, 6, 128, 128)
+    d = _dev(r)
+    S_in = torch.from_numpy(S0).cuda()
+    o0, o320, S0d = _verify(d, S_in)
+    for _ in range(100):
+        o, o32, S = _verify(d, S_in)
+        assert same_bits(o32, o320) and same_bits(S, S0d)

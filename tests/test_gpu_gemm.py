@@ -1,0 +1,117 @@
+"""xv_gemm_small_m on the GPU: oracle parity and M / row-position invariance of the bits."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_exact_speculative_amd.inputs import f32_to_bf16_bits, random_bf16
+from tests.gpu_util import OUT_MAX_REL, max_rel, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _xv():
+    import bit_exact_speculative_amd.xv as xv
+    return xv
+
+
+def _gemm(x_bits, w_bits):
+    from bit_exact_speculative_amd.layer import dev_bf16, host_bits
+    M, K = x_bits.shape
+    N = w_bits.shape[0]
+    x = dev_bf16(x_bits, "cuda"); w = dev_bf16(w_bits, "cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    _xv().xv_gemm_small_m(x, w, y, y32)
+    torch.cuda.synchronize()
+    return host_bits(y), y32.cpu().numpy()
+
+
+def _gemm_dev(x, w, with32=True):
+    M, N = x.shape[0], w.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y32 = torch.empty((M, N), dtype=torch.float32, device="cuda") if with32 else None
+    _xv().xv_gemm_small_m(x, w, y, y32)
+    return y, y32
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 32), (5, 512, 256), (9, 48, 96), (16, 64, 544),
+                                   (17, 32, 1024), (33, 16, 64), (72, 80, 320), (130, 32, 64),
+                                   (9, 112, 5120)])
+def test_gemm_matches_oracle(M, N, K):
+    rng = np.random.default_rng(100 + M + N + K)
+    x = random_bf16(rng, (M, K))
+    w = random_bf16(rng, (N, K), 0.02)
+    yb, y32 = _gemm(x, w)
+    ref = oracle.gemm(x, w)
+    assert max_rel(y32, ref) <= OUT_MAX_REL
+    # forward error bound of an fp32 dot product of length K (any summation order)
+    xa = np.abs((x.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    wa = np.abs((w.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    u = 2.0 ** -24
+    gamma = K * u / (1 - K * u)
+    assert np.all(np.abs(y32 - ref) <= 2 * gamma * (xa @ wa.T) + 1e-30)
+    assert np.array_equal(yb, f32_to_bf16_bits(y32))          # y is y32 rounded to nearest even
+
+
+def test_gemm_exact_on_integers():
+    """Integer x and w/64: every partial sum is exact in fp32, so y32 must equal the oracle."""
+    rng = np.random.default_rng(7)
+    M, N, K = 9, 64, 544
+    xi = rng.integers(-4, 5, size=(M, K)); wi = rng.integers(-4, 5, size=(N, K))
+    x = f32_to_bf16_bits(xi.astype(np.float32))
+    w = f32_to_bf16_bits((wi / 64.0).astype(np.float32))
+    _, y32 = _gemm(x, w)
+    assert np.array_equal(y32.astype(np.float64), oracle.gemm(x, w))
+
+
+def test_gemm_row_bits_independent_of_m_and_position():
+    """Row bits must not depend on M, on the other rows, or on the row's slot in a 16-row tile."""
+    rng = np.random.default_rng(8)
+    K, N = 5120, 96
+    from bit_exact_speculative_amd.layer import dev_bf16
+    x72 = dev_bf16(random_bf16(rng, (72, K)), "cuda")
+    w = dev_bf16(random_bf16(rng, (N, K), 0.02), "cuda")
+    ref, ref32 = _gemm_dev(x72, w)
+    for M in range(1, 17):
+        y, y32 = _gemm_dev(x72[:M].contiguous(), w)
+        assert torch.equal(y32.view(torch.int32), ref32[:M].view(torch.int32)), M
+        assert torch.equal(y.view(torch.int16), ref[:M].view(torch.int16)), M
+    for b in range(8):                                      # one request's 9 rows alone
+        y, y32 = _gemm_dev(x72[b * 9:(b + 1) * 9].contiguous(), w)
+        assert torch.equal(y32.view(torch.int32), ref32[b * 9:(b + 1) * 9].view(torch.int32)), b
+    for m in (0, 5, 15, 16, 40, 71):                         # single rows (decode, M = 1)
+        y, y32 = _gemm_dev(x72[m:m + 1].contiguous(), w)
+        assert torch.equal(y32.view(torch.int32), ref32[m:m + 1].view(torch.int32)), m
+    for shift in (1, 7, 13):                                 # the same rows at other tile slots
+        pad = dev_bf16(random_bf16(rng, (shift, K)), "cuda")
+        xs = torch.cat([pad, x72[:20]], 0).contiguous()
+        y, y32 = _gemm_dev(xs, w)
+        assert torch.equal(y32[shift:].view(torch.int32), ref32[:20].view(torch.int32)), shift
+    _, none32 = _gemm_dev(x72[:9].contiguous(), w, with32=False)   # y32 = NULL: y unchanged
+    y9, _ = _gemm_dev(x72[:9].contiguous(), w)
+    assert torch.equal(y9.view(torch.int16), ref[:9].view(torch.int16))
+
+
+@pytest.mark.parametrize("which", ["N1", "N2"])
+def test_gemm_real_shapes_vs_oracle(which):
+    """The 27B-class projections (M = 9, K = 5120, N = 10240 / 17408) against the oracle."""
+    inp, _ = workload("short", gemm=True, head=False)
+    W = inp.W1 if which == "N1" else inp.W2
+    yb, y32 = _gemm(inp.x, W)
+    ref = oracle.gemm(inp.x, W)
+    assert max_rel(y32, ref) <= OUT_MAX_REL
+    assert np.array_equal(yb, f32_to_bf16_bits(y32))
+
+
+def test_gemm_empty_and_repeat():
+    from bit_exact_speculative_amd.layer import dev_bf16
+    rng = np.random.default_rng(9)
+    x = dev_bf16(random_bf16(rng, (9, 256)), "cuda")
+    w = dev_bf16(random_bf16(rng, (64, 256), 0.02), "cuda")
+    y = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    _xv().xv_gemm_small_m(x[:0], w, y)                       # M = 0: no launch, ok
+    first, first32 = _gemm_dev(x, w)
+    for _ in range(50):
+        y, y32 = _gemm_dev(x, w)
+        assert torch.equal(y32.view(torch.int32), first32.view(torch.int32))
