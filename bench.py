@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark: verified draft tokens per second for one hybrid layer's verify step.
+
+One step is the whole hot path of a speculative step for one layer, on one
+stream, with every input already resident in HBM:
+    qkv-sized projection GEMM  (M = B*T rows, K = 5120, N = 10240)   xv_gemm_small_m
+    MLP-sized projection GEMM  (M = B*T rows, K = 5120, N = 17408)   xv_gemm_small_m
+    GDN verify, 48 value heads, fp32 state                          xv_gdn_verify
+    attention verify rows + KV append, 24 q / 4 KV heads, d = 256  xv_attn_verify_rows
+    synthetic head over both outputs (2 x 6144 -> 4096)             xv_gemm_small_m x 2
+    greedy ids and accepted rows                                    xv_greedy_accept
+    rollback of state and length to the accepted prefix             xv_rollback_to_prefix
+The default workload is batch 1, k = 8 drafts (9 verify rows), 640 cached
+tokens.  Steps run as a real decoding loop: each step verifies against the
+state and cache the previous step of the same layer left.  Weights, states and
+caches are rotated over several layer replicas (about 1.5 GB in all) so that
+the 256 MB Infinity Cache cannot serve the weights of the step being timed.
+
+Before timing, verify == sequential decode is checked bit for bit on the same
+buffers; a mismatch reports no throughput.  The JSON line carries the roofline
+of the dominant kernel (the N = 17408 GEMM, timed live with HIP events on the
+stream it runs on) and the fp64 CPU oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft tok/s per layer at k=8 (ctx 640/2.2k/128k); HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+PROFILE_PMC = os.path.join(ROOT, "profiles", "gemm_small_m_n17408_short_pmc.md")
+GEMM_SOURCES = ["bit_exact_speculative_amd/csrc/xv_gemm.hip", "bit_exact_speculative_amd/csrc/xv_common.h"]
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the dominant GEMM from the committed rocprofv3 --pmc summary,
+    or None when the summary is missing or the kernel source changed since it was taken."""
+    try:
+        lines = open(PROFILE_PMC).read().splitlines()
+    except OSError:
+        return None
+    vals = {}
+    for ln in lines:
+        if ln.startswith("- ") and ":" in ln:
+            k, v = ln[2:].split(":", 1)
+            vals[k.strip()] = v.strip().split()[0] if v.strip() else ""
+    if vals.get("kernel source hash") != gemm_source_hash():
+        return None
+    try:
+        return int(float(vals["calibrated HBM bytes per launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="short", choices=["short", "medium", "long", "batch8"])
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline time budget")
+    ap.add_argument("--breakdown", action="store_true", help="per-kernel event timing pass")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU; --gpus %d is not supported (use --gpus 1)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from bit_exact_speculative_amd import inputs as gen
+    from bit_exact_speculative_amd.layer import Layer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = gen.WORKLOADS[args.workload]
+    R = max(1, args.replicas)
+    total = args.warmup + args.steps
+    per_replica = (total + R - 1) // R + 2
+    L0max = wl.L0 if wl.L0 is not None else wl.L0_range[1]
+    Lmax = L0max + wl.T * (per_replica + 2)
+    t0 = time.time()
+    inp = gen.make_inputs(wl, Lmax=Lmax, pad_value=0)
+    print("# inputs generated in %.1f s (workload %s, Lmax %d)" % (time.time() - t0, wl.name, Lmax),
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        base = Layer(inp, "cuda")                 # prefix state computed by the GPU path
+        base.proj_fp32 = False                    # projections: bf16 outputs only
+        base.out_fp32 = False                     # GDN / attention: bf16 outputs only
+        # bit-exact gate: verify == sequential decode on these buffers
+        gate = base.clone()
+        gate.proj_fp32 = True
+        gate.verify(rollback=False)
+        dec = gate.decode_sequence()
+        torch.cuda.synchronize()
+        same = lambda a, b: torch.equal(a.contiguous().view(torch.int16 if a.element_size() == 2 else torch.int32),
+                                        b.contiguous().view(torch.int16 if b.element_size() == 2 else torch.int32))
+        n = wl.N1
+        exact = (same(gate.o_gdn, dec["o_gdn"]) and same(gate.S_out, dec["S"][-1]) and
+                 same(gate.o_attn, dec["o_attn"]) and same(gate.Kc, dec["Kc"]) and
+                 same(gate.y1.view(wl.B, wl.T, n), dec["y1"]) and
+                 same(gate.y2_32.view(wl.B, wl.T, wl.N2), dec["y2_32"]) and
+                 torch.equal(gate.ids, dec["ids"]))
+        del gate, dec
+        layers = [base] + [base.clone() for _ in range(R - 1)]
+        torch.cuda.synchronize()
+    print("# %d layer replicas resident; verify==decode bit-exact: %s" % (R, exact), file=sys.stderr, flush=True)
+
+    def step(L, ev=None):
+        L.gemm1()
+        if ev is not None:
+            ev[0].record(stream)
+        L.gemm2()
+        if ev is not None:
+            ev[1].record(stream)
+        L.gdn()
+        L.attn()
+        L.head()
+        L.rollback()
+        L.advance()
+
+    with torch.cuda.stream(stream):
+        for s in range(args.warmup):
+            step(layers[s % R])
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        e_start = torch.cuda.Event(enable_timing=True)
+        e_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e_start.record(stream)
+        for s in range(args.steps):
+            step(layers[(args.warmup + s) % R], evs[s])
+        e_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+    ms_total = e_start.elapsed_time(e_end)
+    ms_per_step = ms_total / args.steps
+    gemm_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    gemm_avg_us = float(np.mean(gemm_us))
+    n_keep = [int(L.n_keep.sum().item()) for L in layers]
+
+    breakdown = None
+    if args.breakdown:
+        names = ["gemm_n%d" % wl.N1, "gemm_n%d" % wl.N2, "gdn_verify", "attn_verify_rows",
+                 "head_gemms", "greedy_accept", "rollback"]
+        acc = {k: [] for k in names}
+        with torch.cuda.stream(stream):
+            for s in range(min(args.steps, 50)):
+                L = layers[s % R]
+                fns = [L.gemm1, L.gemm2, L.gdn, L.attn, L.head_gemms, L.greedy, L.rollback]
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+                ev[0].record(stream)
+                for i, f in enumerate(fns):
+                    f()
+                    ev[i + 1].record(stream)
+                L.advance()
+                torch.cuda.synchronize()
+                for i, k in enumerate(names):
+                    acc[k].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
+        breakdown = {k: round(float(np.median(v)), 2) for k, v in acc.items()}
+
+    if args.calib_copy_mib > 0:
+        with torch.cuda.stream(stream):
+            src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            torch.cuda.synchronize()
+
+    # algorithmic bytes of the dominant kernel (weights + activations in + bf16 out)
+    M = wl.M
+    gemm_bytes = wl.N2 * wl.K * 2 + M * wl.K * 2 + M * wl.N2 * 2
+    achieved = gemm_bytes / (gemm_avg_us * 1e-6) / 1e9
+    value = wl.B * wl.k_drafts / (ms_per_step * 1e-3) if exact else None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1) if value is not None else None,
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: batch %d, k=%d drafts (%d verify rows), ctx %s, hidden %d, GDN %d/%d heads "
+                        "d=%d fp32 state, attention %d/%d heads d=%d bf16 KV, GEMMs %dx%dx%d and %dx%dx%d, "
+                        "head 2x%d->%d" % (wl.name, wl.B, wl.k_drafts, wl.T,
+                                           wl.L0 if wl.L0 is not None else "%d-%d" % wl.L0_range,
+                                           wl.K, wl.Hk, wl.Hv, wl.dk, wl.Hq, wl.Hkv, wl.d,
+                                           M, wl.K, wl.N1, M, wl.K, wl.N2, wl.Hv * wl.dv, wl.NH),
+            "global_batch": wl.B,
+            "verify_rows": wl.T,
+            "layer_replicas": R,
+            "bit_exact_verify_equals_decode": bool(exact),
+            "rows_kept_per_step": round(float(np.mean(n_keep)) / R, 2) if n_keep else None,
+            "compute": "bf16 x bf16 -> fp32 MFMA GEMMs and attention; fp32 GDN state and VALU",
+        },
+        "roofline": {
+            "kernel": "xv_gemm_kernel (N=%d)" % wl.N2,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile(),
+            "algorithmic_bytes": gemm_bytes,
+            "avg_us": round(gemm_avg_us, 3),
+        },
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 4),
+    }
+    if breakdown is not None:
+        out["breakdown_us"] = breakdown
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The fp64 oracle running the same step (both GEMMs, GDN, attention, head, greedy,
+    rollback) on the host, repeated until the time budget is spent; tok/s at the same unit."""
+    import numpy as np
+    import oracle
+    wl = inp.wl
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    p = inp.prefix
+    _, S_pre, _ = oracle.gdn(p["q"], p["k"], p["v"], p["a"], p["b"],
+                             np.zeros((wl.B, wl.Hv, wl.dk, wl.dv), np.float32))
+    S0 = S_pre.astype(np.float32)
+    g = inp.gdn
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm(inp.x, inp.W1)
+        oracle.gemm(inp.x, inp.W2)
+        o_g, _, _ = oracle.gdn(g["q"], g["k"], g["v"], g["a"], g["b"], S0)
+        o_a = oracle.attn(inp.q_attn, inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, inp.L0,
+                          1.0 / np.sqrt(wl.d))
+        from bit_exact_speculative_amd.inputs import f32_to_bf16_bits
+        fg = f32_to_bf16_bits(o_g.astype(np.float32)).reshape(wl.M, -1)
+        fa = f32_to_bf16_bits(o_a.astype(np.float32)).reshape(wl.M, -1)
+        logits = oracle.gemm(fg, inp.Wh_gdn) + oracle.gemm(fa, inp.Wh_attn)
+        _, n_keep = oracle.greedy(logits.reshape(wl.B, wl.T, wl.NH), inp.draft)
+        oracle.rollback(g["k"], g["v"], g["a"], g["b"], S0, inp.L0, n_keep)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end or len(times) >= 50:
+            break
+    t = float(np.median(times))
+    return {"value": round(wl.B * wl.k_drafts / t, 3), "unit": "tok/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "the full %s step (all rows of every kernel), fp64 C oracle with OpenMP, "
+                      "median of %d runs of %.2f s" % (wl.name, len(times), t)}
+
+
+if __name__ == "__main__":
+    main()

@@ -20,13 +20,29 @@
 // R = dk/8 consecutive key indices of the column in VGPRs, for the whole call.
 // The fixed dot order: in each lane four fp32 chains over i mod 4 in ascending
 // i, combined as (c0 + c1) + (c2 + c3); then a butterfly over the 8 lanes
-// (xor 1, 2, 4).  Every lane ends with the same bits, so all lanes of a column
-// compute the same u.  The state is read once and written once per call.
+// (DPP: partner lane^1, then lane^2, then the mirrored half of the group).
+// Every lane ends with the same bits, so all lanes of a column compute the
+// same u.  The state is read once and written once per call, and the rows of
+// all tokens are staged in LDS before the token loop starts.
 #include "xv_common.h"
 
 namespace {
 
 constexpr int XV_GDN_JW = 32;       // value indices per workgroup (4 waves x 8)
+constexpr int XV_GDN_TMAX = 16;
+
+// Exact lane moves within each group of 8 lanes (DPP): swap with lane^1, lane^2,
+// and mirror the group (lane i <-> 7 - i), which after the first two steps
+// brings in the other half's sum.
+__device__ __forceinline__ float xv_dpp_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xv_dpp_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xv_dpp_mirror8(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+}
 
 template <int R>
 __device__ __forceinline__ float xv_gdn_dot(const float (&s)[R], const float (&x)[R]) {
@@ -42,9 +58,9 @@ __device__ __forceinline__ float xv_gdn_dot(const float (&s)[R], const float (&x
         c3 = __builtin_fmaf(s[r + 3], x[r + 3], c3);
     }
     float p = (c0 + c1) + (c2 + c3);
-    p = p + __shfl_xor(p, 1);
-    p = p + __shfl_xor(p, 2);
-    p = p + __shfl_xor(p, 4);
+    p = p + xv_dpp_xor1(p);
+    p = p + xv_dpp_xor2(p);
+    p = p + xv_dpp_mirror8(p);
     return p;
 }
 
@@ -61,10 +77,10 @@ __device__ __forceinline__ void xv_gdn_token(float (&s)[R], const float (&kk)[R]
 }
 
 template <int R>
-__device__ __forceinline__ void xv_load_bf16_row(const uint16_t* p, float (&out)[R]) {
+__device__ __forceinline__ void xv_lds_bf16_row(const uint16_t* p, float (&out)[R]) {
 #pragma unroll
     for (int c = 0; c < R / 8; ++c) {
-        const xv_u32x4 v = xv_load16(p + c * 8);
+        const xv_u32x4 v = *reinterpret_cast<const xv_u32x4*>(p + c * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             out[c * 8 + 2 * e] = xv_bf16_lo(v[e]);
@@ -76,6 +92,8 @@ __device__ __forceinline__ void xv_load_bf16_row(const uint16_t* p, float (&out)
 // ROLLBACK = false: verify of T tokens from state_in, writes o (and o32) and S_T.
 // ROLLBACK = true : n = n_keep[b]; n == T leaves state_out; otherwise recomputes
 //                   S_n from state_in; kv_len[b] += n.
+// Every row the workgroup needs (k and q of its key head, its 32 values, a and b)
+// is staged in LDS once; the state column stays in VGPRs for the whole call.
 template <int DK, bool ROLLBACK>
 __global__ __launch_bounds__(256)
 void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -86,11 +104,17 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    const int32_t* __restrict__ n_keep)
 {
     constexpr int R = DK / 8;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) uint16_t skq[XV_GDN_TMAX][2][DK];
+    __shared__ uint16_t sv[XV_GDN_TMAX][XV_GDN_JW];
+    __shared__ float sab[XV_GDN_TMAX][2];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int ig = lane & 7;                 // key-index group: i in [ig*R, ig*R + R)
     const int jl = lane >> 3;
-    const int j = blockIdx.x * XV_GDN_JW + wave * 8 + jl;
+    const int jw = wave * 8 + jl;            // value index within the workgroup's slice
+    const int j = blockIdx.x * XV_GDN_JW + jw;
     const int h = blockIdx.y;
     const int b = blockIdx.z;
     const int g = h / (Hv / Hk);
@@ -99,7 +123,7 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     if (ROLLBACK) {
         n = n_keep[b];
         n = n < 0 ? 0 : (n > T ? T : n);
-        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) kv_len[b] += n;
+        if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) kv_len[b] += n;
         if (n == T) return;                  // state_out already holds S_T
     }
 
@@ -108,20 +132,48 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
     for (int r = 0; r < R; ++r) s[r] = S_in[sbase + (size_t)r * dv];
 
+    // stage the rows of tokens 0..n-1
+    constexpr int CH = DK / 8;               // 16-byte chunks per k or q row
+    for (int idx = tid; idx < n * 2 * CH; idx += 256) {
+        const int t = idx / (2 * CH), rem = idx % (2 * CH);
+        const int which = rem / CH, c = rem % CH;      // 0: k, 1: q
+        const size_t row = ((size_t)b * T + t) * Hk + g;
+        const uint16_t* src = (which == 0 ? k : q) + row * DK + c * 8;
+        xv_u32x4 val = {0u, 0u, 0u, 0u};
+        if (which == 0 || !ROLLBACK) val = xv_load16(src);
+        *reinterpret_cast<xv_u32x4*>(&skq[t][which][c * 8]) = val;
+    }
+    for (int idx = tid; idx < n * XV_GDN_JW; idx += 256) {
+        const int t = idx / XV_GDN_JW, c = idx % XV_GDN_JW;
+        sv[t][c] = v[(((size_t)b * T + t) * Hv + h) * dv + blockIdx.x * XV_GDN_JW + c];
+    }
+    if (tid < 2 * n) {
+        const int t = tid >> 1;
+        sab[t][tid & 1] = ((tid & 1) ? beta : a)[((size_t)b * T + t) * Hv + h];
+    }
+    __syncthreads();
+
+    float kk[R], qq[R];
+    if (n > 0) {
+        xv_lds_bf16_row<R>(&skq[0][0][ig * R], kk);
+        if (!ROLLBACK) xv_lds_bf16_row<R>(&skq[0][1][ig * R], qq);
+    }
     for (int t = 0; t < n; ++t) {
-        const size_t row = (size_t)b * T + t;
-        float kk[R];
-        xv_load_bf16_row<R>(k + (row * Hk + g) * DK + ig * R, kk);
-        const float vj = xv_bf16_to_f32(v[(row * Hv + h) * dv + j]);
-        const float at = a[row * Hv + h];
-        const float bt = beta[row * Hv + h];
-        xv_gdn_token<R>(s, kk, vj, at, bt);
+        const float vj = xv_bf16_to_f32(sv[t][jw]);
+        const float at = sab[t][0];
+        const float bt = sab[t][1];
+        float kc[R], qc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) { kc[r] = kk[r]; qc[r] = qq[r]; }
+        if (t + 1 < n) {                     // next token's rows, read while this one computes
+            xv_lds_bf16_row<R>(&skq[t + 1][0][ig * R], kk);
+            if (!ROLLBACK) xv_lds_bf16_row<R>(&skq[t + 1][1][ig * R], qq);
+        }
+        xv_gdn_token<R>(s, kc, vj, at, bt);
         if (!ROLLBACK) {
-            float qq[R];
-            xv_load_bf16_row<R>(q + (row * Hk + g) * DK + ig * R, qq);
-            const float ot = xv_gdn_dot<R>(s, qq);
+            const float ot = xv_gdn_dot<R>(s, qc);
             if (ig == 0) {
-                const size_t oi = (row * Hv + h) * dv + j;
+                const size_t oi = (((size_t)b * T + t) * Hv + h) * dv + j;
                 o[oi] = xv_f32_to_bf16(ot);
                 if (o32) o32[oi] = ot;
             }
@@ -135,7 +187,7 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 int xv_gdn_check(const void* k, const void* v, const void* a, const void* b,
                  const void* sin, const void* sout, int B, int T, int Hk, int Hv, int dk, int dv)
 {
-    XV_REQUIRE(B >= 0 && T >= 1 && T <= 16 && Hk >= 1 && Hv >= 1 && Hv % Hk == 0, XV_ERR_SHAPE);
+    XV_REQUIRE(B >= 0 && T >= 1 && T <= XV_GDN_TMAX && Hk >= 1 && Hv >= 1 && Hv % Hk == 0, XV_ERR_SHAPE);
     XV_REQUIRE(dk == 64 || dk == 128, XV_ERR_SHAPE);
     XV_REQUIRE(dv >= 32 && dv <= 128 && dv % 32 == 0, XV_ERR_SHAPE);
     if (B == 0) return XV_OK;

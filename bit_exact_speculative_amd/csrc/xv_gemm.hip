@@ -4,127 +4,268 @@
 // reading the weights, and routing them to one tile whose bits do not depend on
 // M fixed both speed and exactness (recipe card, runtime env: the M <= 16 gate).
 //
-// Design (gfx950):
-//  * A workgroup owns XV_GEMM_CB blocks of 16 output columns and all rows.
-//    Its XV_GEMM_WAVES wavefronts split K into that many contiguous ranges of
-//    32-wide k-steps; the split is a function of K alone.
-//  * Each wave streams its W slice with 16-byte loads (one 64-byte run per
-//    column per instruction) and feeds v_mfma_f32_16x16x32_bf16 with x as the
-//    A operand (16 rows per tile, rows >= M zero) and W as the B operand.
-//    Every row tile of the call is applied to the same W fragments, so W is
-//    read from HBM once whatever M is.
-//  * The per-wave fp32 partials are summed through LDS in wave order 0..7.
-//  Row m's result is therefore the same chain of MFMAs over the same k-steps
-//  followed by the same 8-term ordered sum, for any M and any position of m in
-//  its tile: the M-independent reduction order the bit-exact route needs.
+// Arithmetic (the same for every M, every row position and every launch shape):
+//   K is cut into XV_GEMM_WAVES = 16 contiguous ranges of 32-wide k-steps (the
+//   cut depends on K alone).  For each 16-column block, wave w runs one chain of
+//   v_mfma_f32_16x16x32_bf16 over its range in ascending k-step order (x rows as
+//   the A operand, W rows as the B operand), and the 16 range partials are
+//   summed in wave order: ((p0 + p1) + p2) + ... + p15.  The result is rounded
+//   to bf16 (nearest even) and optionally stored in fp32 as well.
+//
+// Work mapping (gfx950):
+//  * Persistent workgroups of 16 waves, a few per CU; workgroup i walks the
+//    column blocks i, i + grid, i + 2 grid, ...  All of its waves stream their
+//    K range of the block's 16 W rows with 16-byte loads, double-buffered in
+//    registers across column blocks so loads stay in flight through the
+//    per-block reduction barriers.  Loads are straight-line code: addresses are
+//    clamped into the buffers instead of branched around.
+//  * The x fragments of a wave's K range are loaded into registers once per
+//    row-tile group and reused for every column block (small M), or re-read
+//    from L2 per k-step when they would not fit (many row tiles).  Where x comes
+//    from does not change any arithmetic.
+//  * Up to XV_GEMM_MT_MAX row tiles share one pass over W; rows >= M are zeroed
+//    after their (clamped) load.
 #include "xv_common.h"
 
 namespace {
 
-constexpr int XV_GEMM_CB = 2;       // 16-column blocks per workgroup
-constexpr int XV_GEMM_WAVES = 8;    // K ranges per workgroup (one per wave)
-constexpr int XV_GEMM_UNROLL = 4;   // k-steps in flight per wave
-constexpr int XV_GEMM_MT_MAX = 8;   // 16-row tiles per pass over W
+constexpr int XV_GEMM_WAVES = 16;   // K ranges per column block; fixes the sum order
+constexpr int XV_GEMM_THREADS = XV_GEMM_WAVES * 64;
+constexpr int XV_GEMM_MT_MAX = 5;   // 16-row tiles per pass over W (more would spill registers)
 
+// Ordered sum of the 16 wave partials of one column block and the store.
 template <int MT>
-__global__ __launch_bounds__(XV_GEMM_WAVES * 64)
-void xv_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                    uint16_t* __restrict__ y, float* __restrict__ y32,
-                    int M, int N, int K, int mt0)
+__device__ __forceinline__ void xv_gemm_finish(float (&red)[XV_GEMM_WAVES][64][4], xv_f32x4 (&acc)[MT],
+                                               int lane, int wave, int blk, int mt0, int M, int N,
+                                               uint16_t* __restrict__ y, float* __restrict__ y32)
 {
-    __shared__ float red[XV_GEMM_WAVES][XV_GEMM_CB][64][4];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        *reinterpret_cast<xv_f32x4*>(&red[wave][lane][0]) = acc[t];
+        acc[t] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();
+        if (threadIdx.x < 256) {
+            const int rr = threadIdx.x >> 4, cc = threadIdx.x & 15;
+            const int slane = cc + 16 * (rr >> 2), si = rr & 3;
+            float sum = red[0][slane][si];
+#pragma unroll
+            for (int wv = 1; wv < XV_GEMM_WAVES; ++wv) sum = sum + red[wv][slane][si];
+            const int row = (mt0 + t) * 16 + rr;
+            const int col = blk * 16 + cc;
+            if (row < M) {
+                y[(size_t)row * N + col] = xv_f32_to_bf16(sum);
+                if (y32) y32[(size_t)row * N + col] = sum;
+            }
+        }
+        __syncthreads();
+    }
+}
 
+// x fragments in registers: a wave's range has at most KSW k-steps, streamed in
+// two stages of U = KSW / 2 per column block (stage positions are compile-time).
+template <int MT, int KSW>
+__global__ __launch_bounds__(XV_GEMM_THREADS)
+void xv_gemm_xreg_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                         uint16_t* __restrict__ y, float* __restrict__ y32,
+                         int M, int N, int K, int mt0)
+{
+    constexpr int U = KSW / 2;
+    __shared__ float red[XV_GEMM_WAVES][64][4];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    const int n0 = blockIdx.x * (XV_GEMM_CB * 16);
     const int KS = K >> 5;
     const int ks0 = (wave * KS) / XV_GEMM_WAVES;
-    const int ks1 = ((wave + 1) * KS) / XV_GEMM_WAVES;
+    const int nks = ((wave + 1) * KS) / XV_GEMM_WAVES - ks0;
+    const int last = nks > 0 ? nks - 1 : 0;
+    const int nblk = N >> 4;
+    const int grid = gridDim.x;
+    if ((int)blockIdx.x >= nblk) return;      // uniform over the workgroup
+    const xv_u32x4 zero = {0u, 0u, 0u, 0u};
 
-    bool cvalid[XV_GEMM_CB];
-    const uint16_t* wp[XV_GEMM_CB];
+    xv_u32x4 xr[KSW][MT];
 #pragma unroll
-    for (int cb = 0; cb < XV_GEMM_CB; ++cb) {
-        cvalid[cb] = (n0 + cb * 16) < N;                     // uniform per wave
-        const int col = cvalid[cb] ? n0 + cb * 16 + lr : 0;
-        wp[cb] = w + (size_t)col * K + lg * 8;
+    for (int t = 0; t < MT; ++t) {
+        const int row = (mt0 + t) * 16 + lr;
+        const bool ok = row < M;
+        const uint16_t* xp = x + (size_t)(ok ? row : M - 1) * K + (size_t)ks0 * 32 + lg * 8;
+#pragma unroll
+        for (int j = 0; j < KSW; ++j) {
+            const xv_u32x4 v = xv_load16(xp + (size_t)(j < nks ? j : last) * 32);
+            xr[j][t] = ok ? v : zero;
+        }
     }
+    const uint16_t* wl = w + (size_t)lr * K + (size_t)ks0 * 32 + lg * 8;
+    auto load_half = [&](xv_u32x4 (&wf)[U], int blk, int half) {
+        const uint16_t* wb = wl + (size_t)blk * 16 * K;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = half * U + u;
+            wf[u] = xv_load16(wb + (size_t)(j < nks ? j : last) * 32);
+        }
+    };
+    xv_f32x4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+    auto mma_half = [&](xv_u32x4 (&wf)[U], int half) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = half * U + u;
+            if (j < nks) {
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[t] = xv_mfma16x16x32(xr[j][t], wf[u], acc[t]);
+            }
+        }
+    };
+
+    xv_u32x4 w0[U], w1[U];
+    int blk = blockIdx.x;
+    load_half(w0, blk, 0);
+    for (;;) {
+        const int nxt = blk + grid < nblk ? blk + grid : blk;    // clamped prefetch target
+        load_half(w1, blk, 1);
+        mma_half(w0, 0);
+        load_half(w0, nxt, 0);
+        mma_half(w1, 1);
+        xv_gemm_finish<MT>(red, acc, lane, wave, blk, mt0, M, N, y, y32);
+        blk += grid;
+        if (blk >= nblk) break;
+    }
+}
+
+// x fragments re-read per k-step (many row tiles or long K): U k-steps per stage.
+template <int MT, int U>
+__global__ __launch_bounds__(XV_GEMM_THREADS)
+void xv_gemm_xstream_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                            uint16_t* __restrict__ y, float* __restrict__ y32,
+                            int M, int N, int K, int mt0)
+{
+    __shared__ float red[XV_GEMM_WAVES][64][4];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int KS = K >> 5;
+    const int ks0 = (wave * KS) / XV_GEMM_WAVES;
+    const int nks = ((wave + 1) * KS) / XV_GEMM_WAVES - ks0;
+    const int last = nks > 0 ? nks - 1 : 0;
+    const int nblk = N >> 4;
+    const int grid = gridDim.x;
+    if ((int)blockIdx.x >= nblk) return;
+    const xv_u32x4 zero = {0u, 0u, 0u, 0u};
+
     bool rvalid[MT];
     const uint16_t* xp[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         const int row = (mt0 + t) * 16 + lr;
         rvalid[t] = row < M;
-        xp[t] = x + (size_t)(rvalid[t] ? row : 0) * K + lg * 8;
+        xp[t] = x + (size_t)(rvalid[t] ? row : M - 1) * K + (size_t)ks0 * 32 + lg * 8;
     }
+    const uint16_t* wl = w + (size_t)lr * K + (size_t)ks0 * 32 + lg * 8;
+    const int SPB = nks > 0 ? (nks + U - 1) / U : 1;              // stages per column block
+    const int my_blocks = (nblk - 1 - (int)blockIdx.x) / grid + 1;
+    const int nstages = my_blocks * SPB;
 
-    xv_f32x4 acc[MT][XV_GEMM_CB];
+    auto load_stage = [&](xv_u32x4 (&wf)[U], xv_u32x4 (&xf)[U][MT], int s) {
+        const int sc = s < nstages ? s : nstages - 1;
+        const int blk = blockIdx.x + (sc / SPB) * grid;
+        const int j0 = (sc % SPB) * U;
+        const uint16_t* wb = wl + (size_t)blk * 16 * K;
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+        for (int u = 0; u < U; ++u) {
+            int j = j0 + u;
+            j = j < nks ? j : last;
+            wf[u] = xv_load16(wb + (size_t)j * 32);
 #pragma unroll
-        for (int cb = 0; cb < XV_GEMM_CB; ++cb) acc[t][cb] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const xv_u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int ks = ks0; ks < ks1; ks += XV_GEMM_UNROLL) {
-        xv_u32x4 wf[XV_GEMM_UNROLL][XV_GEMM_CB];
-        xv_u32x4 xf[XV_GEMM_UNROLL][MT];
+            for (int t = 0; t < MT; ++t) xf[u][t] = xv_load16(xp[t] + (size_t)j * 32);
+        }
+    };
+    xv_f32x4 acc[MT];
 #pragma unroll
-        for (int u = 0; u < XV_GEMM_UNROLL; ++u) {
-            if (ks + u < ks1) {
+    for (int t = 0; t < MT; ++t) acc[t] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+    auto mma_stage = [&](xv_u32x4 (&wf)[U], xv_u32x4 (&xf)[U][MT], int s) {
+        const int j0 = (s % SPB) * U;
 #pragma unroll
-                for (int cb = 0; cb < XV_GEMM_CB; ++cb)
-                    wf[u][cb] = cvalid[cb] ? xv_load16(wp[cb] + (size_t)(ks + u) * 32) : zero;
+        for (int u = 0; u < U; ++u) {
+            if (j0 + u < nks) {
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
-                    xf[u][t] = rvalid[t] ? xv_load16(xp[t] + (size_t)(ks + u) * 32) : zero;
+                    acc[t] = xv_mfma16x16x32(rvalid[t] ? xf[u][t] : zero, wf[u], acc[t]);
             }
         }
-#pragma unroll
-        for (int u = 0; u < XV_GEMM_UNROLL; ++u) {
-            if (ks + u < ks1) {
-#pragma unroll
-                for (int t = 0; t < MT; ++t)
-#pragma unroll
-                    for (int cb = 0; cb < XV_GEMM_CB; ++cb)
-                        acc[t][cb] = xv_mfma16x16x32(xf[u][t], wf[u][cb], acc[t][cb]);
-            }
-        }
-    }
+    };
 
-    // Ordered cross-wave sum: out = (((p0 + p1) + p2) + ... + p7).
-    const int tid = threadIdx.x;
-    const int rr = tid / (XV_GEMM_CB * 16);          // row within the tile, 0..15
-    const int cc = tid % (XV_GEMM_CB * 16);          // column within the workgroup
-    const int scb = cc >> 4;
-    const int slane = (cc & 15) + 16 * (rr >> 2);
-    const int si = rr & 3;
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-#pragma unroll
-        for (int cb = 0; cb < XV_GEMM_CB; ++cb)
-            *reinterpret_cast<xv_f32x4*>(&red[wave][cb][lane][0]) = acc[t][cb];
-        __syncthreads();
-        float s = red[0][scb][slane][si];
-#pragma unroll
-        for (int wv = 1; wv < XV_GEMM_WAVES; ++wv) s = s + red[wv][scb][slane][si];
-        const int row = (mt0 + t) * 16 + rr;
-        const int col = n0 + cc;
-        if (row < M && col < N) {
-            y[(size_t)row * N + col] = xv_f32_to_bf16(s);
-            if (y32) y32[(size_t)row * N + col] = s;
-        }
-        __syncthreads();
+    xv_u32x4 wA[U], wB[U], xA[U][MT], xB[U][MT];
+    load_stage(wA, xA, 0);
+    for (int s = 0; s < nstages; s += 2) {
+        load_stage(wB, xB, s + 1);
+        mma_stage(wA, xA, s);
+        if ((s + 1) % SPB == 0)
+            xv_gemm_finish<MT>(red, acc, lane, wave, blockIdx.x + (s / SPB) * grid, mt0, M, N, y, y32);
+        if (s + 1 >= nstages) break;
+        load_stage(wA, xA, s + 2);
+        mma_stage(wB, xB, s + 1);
+        if ((s + 2) % SPB == 0)
+            xv_gemm_finish<MT>(red, acc, lane, wave, blockIdx.x + ((s + 1) / SPB) * grid, mt0, M, N, y, y32);
     }
 }
 
-template <int MT>
-void xv_gemm_launch(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
-                    int M, int N, int K, int mt0, hipStream_t st)
+int xv_gemm_grid(int nblk) {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    return nblk < cus ? nblk : cus;
+}
+
+template <int MT, int KSW>
+void xv_gemm_launch_xreg(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
+                         int M, int N, int K, int mt0, hipStream_t st)
 {
-    const int cols = XV_GEMM_CB * 16;
-    dim3 grid((N + cols - 1) / cols), block(XV_GEMM_WAVES * 64);
-    hipLaunchKernelGGL(xv_gemm_kernel<MT>, grid, block, 0, st, x, w, y, y32, M, N, K, mt0);
+    dim3 grid(xv_gemm_grid(N / 16)), block(XV_GEMM_THREADS);
+    hipLaunchKernelGGL((xv_gemm_xreg_kernel<MT, KSW>), grid, block, 0, st, x, w, y, y32, M, N, K, mt0);
+}
+
+template <int MT, int U>
+void xv_gemm_launch_xstream(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
+                            int M, int N, int K, int mt0, hipStream_t st)
+{
+    dim3 grid(xv_gemm_grid(N / 16)), block(XV_GEMM_THREADS);
+    hipLaunchKernelGGL((xv_gemm_xstream_kernel<MT, U>), grid, block, 0, st, x, w, y, y32, M, N, K, mt0);
+}
+
+// Launch shape per row-tile count and K.  None of these choices changes any
+// row's arithmetic: every variant runs the same 16-way K split, the same MFMA
+// chains and the same ordered sum.
+void xv_gemm_dispatch(int mt, int ksw, const uint16_t* x, const uint16_t* w, uint16_t* y,
+                      float* y32, int M, int N, int K, int mt0, hipStream_t st)
+{
+    if (mt == 1 && ksw <= 10) {
+        if (ksw <= 2) xv_gemm_launch_xreg<1, 2>(x, w, y, y32, M, N, K, mt0, st);
+        else if (ksw <= 4) xv_gemm_launch_xreg<1, 4>(x, w, y, y32, M, N, K, mt0, st);
+        else if (ksw <= 6) xv_gemm_launch_xreg<1, 6>(x, w, y, y32, M, N, K, mt0, st);
+        else if (ksw <= 8) xv_gemm_launch_xreg<1, 8>(x, w, y, y32, M, N, K, mt0, st);
+        else xv_gemm_launch_xreg<1, 10>(x, w, y, y32, M, N, K, mt0, st);
+        return;
+    }
+    if (mt == 2 && ksw <= 4) {
+        xv_gemm_launch_xreg<2, 4>(x, w, y, y32, M, N, K, mt0, st);
+        return;
+    }
+    switch (mt) {
+        case 1: xv_gemm_launch_xstream<1, 4>(x, w, y, y32, M, N, K, mt0, st); break;
+        case 2: xv_gemm_launch_xstream<2, 2>(x, w, y, y32, M, N, K, mt0, st); break;
+        case 3: xv_gemm_launch_xstream<3, 1>(x, w, y, y32, M, N, K, mt0, st); break;
+        case 4: xv_gemm_launch_xstream<4, 1>(x, w, y, y32, M, N, K, mt0, st); break;
+        case 5: xv_gemm_launch_xstream<5, 1>(x, w, y, y32, M, N, K, mt0, st); break;
+        case 6: xv_gemm_launch_xstream<6, 1>(x, w, y, y32, M, N, K, mt0, st); break;
+        case 7: xv_gemm_launch_xstream<7, 1>(x, w, y, y32, M, N, K, mt0, st); break;
+        default: xv_gemm_launch_xstream<8, 1>(x, w, y, y32, M, N, K, mt0, st); break;
+    }
 }
 
 }  // namespace
@@ -139,19 +280,12 @@ extern "C" int xv_gemm_small_m(const uint16_t* x, const uint16_t* w, uint16_t* y
                XV_ERR_ALIGN);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    const int KS = K / 32;
+    const int ksw = (KS + XV_GEMM_WAVES - 1) / XV_GEMM_WAVES;   // k-steps of the longest range
     const int tiles = (M + 15) / 16;
     for (int mt0 = 0; mt0 < tiles; mt0 += XV_GEMM_MT_MAX) {
         const int mt = tiles - mt0 < XV_GEMM_MT_MAX ? tiles - mt0 : XV_GEMM_MT_MAX;
-        switch (mt) {
-            case 1: xv_gemm_launch<1>(x, w, y, y32, M, N, K, mt0, st); break;
-            case 2: xv_gemm_launch<2>(x, w, y, y32, M, N, K, mt0, st); break;
-            case 3: xv_gemm_launch<3>(x, w, y, y32, M, N, K, mt0, st); break;
-            case 4: xv_gemm_launch<4>(x, w, y, y32, M, N, K, mt0, st); break;
-            case 5: xv_gemm_launch<5>(x, w, y, y32, M, N, K, mt0, st); break;
-            case 6: xv_gemm_launch<6>(x, w, y, y32, M, N, K, mt0, st); break;
-            case 7: xv_gemm_launch<7>(x, w, y, y32, M, N, K, mt0, st); break;
-            default: xv_gemm_launch<8>(x, w, y, y32, M, N, K, mt0, st); break;
-        }
+        xv_gemm_dispatch(mt, ksw, x, w, y, y32, M, N, K, mt0, st);
         int s = xv_launch_status();
         if (s != XV_OK) return s;
     }

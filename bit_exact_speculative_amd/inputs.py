@@ -103,9 +103,19 @@ WORKLOADS = {
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round finite fp32 values to bf16 (nearest, ties to even); returns uint16 bit patterns."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    out = np.empty(a.shape, np.uint16)
+    _round_into(a.reshape(-1), out.reshape(-1))
+    return out
+
+
+def _round_into(a: np.ndarray, out: np.ndarray) -> None:
+    # finite values only: u + 0x7FFF + lsb stays below 2^32 for every finite pattern
+    u = a.view(np.uint32)
+    t = (u >> 16) & 1
+    t += u
+    t += 0x7FFF
+    t >>= 16
+    out[...] = t
 
 
 def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
@@ -117,8 +127,27 @@ def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
 def _normal(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
     x = rng.standard_normal(size=shape, dtype=np.float32)
     if scale != 1.0:
-        x = x * np.float32(scale)
+        x *= np.float32(scale)
     return x
+
+
+_CHUNK = 1 << 22
+
+
+def _normal_bf16(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
+    """bf16 bits of scaled fp32 normals, drawn in chunks (the same value stream as one draw)."""
+    out = np.empty(shape, np.uint16)
+    flat = out.reshape(-1)
+    n = flat.size
+    buf = np.empty(min(n, _CHUNK), np.float32)
+    for i in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - i)
+        b = buf[:m]
+        rng.standard_normal(out=b, dtype=np.float32)
+        if scale != 1.0:
+            b *= np.float32(scale)
+        _round_into(b, flat[i:i + m])
+    return out
 
 
 def _l2norm_bf16(x: np.ndarray) -> np.ndarray:
@@ -142,7 +171,7 @@ def gdn_rows(rng: np.random.Generator, B: int, T: int, Hk: int, Hv: int, dk: int
     """q, k (bf16, L2-normalised), v (bf16), a, b (fp32) for T rows."""
     q = _l2norm_bf16(_normal(rng, (B, T, Hk, dk)))
     k = _l2norm_bf16(_normal(rng, (B, T, Hk, dk)))
-    v = f32_to_bf16_bits(_normal(rng, (B, T, Hv, dv)))
+    v = _normal_bf16(rng, (B, T, Hv, dv))
     a = _decay(_normal(rng, (B, T, Hv)))
     b = _beta(_normal(rng, (B, T, Hv)))
     return dict(q=q, k=k, v=v, a=a, b=b)
@@ -195,16 +224,16 @@ def make_inputs(wl: Workload, *, Lmax: Optional[int] = None, pad_value: int = BF
         Lmax = int(L0.max()) + T
     if Lmax < int(L0.max()) + T:
         raise ValueError("Lmax too small for L0 + T")
-    q_attn = f32_to_bf16_bits(_normal(rng, (B, T, wl.Hq, wl.d)))
-    k_new = f32_to_bf16_bits(_normal(rng, (B, T, wl.Hkv, wl.d)))
-    v_new = f32_to_bf16_bits(_normal(rng, (B, T, wl.Hkv, wl.d)))
+    q_attn = _normal_bf16(rng, (B, T, wl.Hq, wl.d))
+    k_new = _normal_bf16(rng, (B, T, wl.Hkv, wl.d))
+    v_new = _normal_bf16(rng, (B, T, wl.Hkv, wl.d))
     k_cache = np.full((B, wl.Hkv, Lmax, wl.d), pad_value, np.uint16)
     v_cache = np.full((B, wl.Hkv, Lmax, wl.d), pad_value, np.uint16)
     for bb in range(B):
         n = int(L0[bb])
         for g in range(wl.Hkv):
-            k_cache[bb, g, :n] = f32_to_bf16_bits(_normal(rng, (n, wl.d)))
-            v_cache[bb, g, :n] = f32_to_bf16_bits(_normal(rng, (n, wl.d)))
+            k_cache[bb, g, :n] = _normal_bf16(rng, (n, wl.d))
+            v_cache[bb, g, :n] = _normal_bf16(rng, (n, wl.d))
     inp = Inputs(wl=wl, prefix=prefix, gdn=gdn, L0=L0, Lmax=Lmax, q_attn=q_attn,
                  k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache)
     inp.draft = rng_ids.integers(0, wl.NH, size=(B, T), dtype=np.int64).astype(np.int32)
@@ -212,19 +241,19 @@ def make_inputs(wl: Workload, *, Lmax: Optional[int] = None, pad_value: int = BF
         inp.accepted = rng_ids.integers(0, wl.k_drafts + 1, size=B, dtype=np.int64).astype(np.int32)
     if not with_gemm:
         return inp
-    inp.x = f32_to_bf16_bits(_normal(rng, (wl.M, wl.K)))
-    inp.W1 = f32_to_bf16_bits(_normal(rng, (wl.N1, wl.K), 0.02))
-    inp.W2 = f32_to_bf16_bits(_normal(rng, (wl.N2, wl.K), 0.02))
+    inp.x = _normal_bf16(rng, (wl.M, wl.K))
+    inp.W1 = _normal_bf16(rng, (wl.N1, wl.K), 0.02)
+    inp.W2 = _normal_bf16(rng, (wl.N2, wl.K), 0.02)
     if not with_head:
         return inp
-    inp.Wh_gdn = f32_to_bf16_bits(_normal(rng, (wl.NH, wl.Hv * wl.dv), 0.02))
-    inp.Wh_attn = f32_to_bf16_bits(_normal(rng, (wl.NH, wl.Hq * wl.d), 0.02))
+    inp.Wh_gdn = _normal_bf16(rng, (wl.NH, wl.Hv * wl.dv), 0.02)
+    inp.Wh_attn = _normal_bf16(rng, (wl.NH, wl.Hq * wl.d), 0.02)
     return inp
 
 
 def random_bf16(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
     """bf16 bits of scaled standard normals (for ad-hoc test shapes)."""
-    return f32_to_bf16_bits(_normal(rng, shape, scale))
+    return _normal_bf16(rng, shape, scale)
 
 
 def random_gdn(rng: np.random.Generator, B, T, Hk, Hv, dk, dv):

@@ -105,6 +105,8 @@ class Layer:
             self.draft = dev(inp.draft, device)
             self.ids = torch.empty((B, T), dtype=torch.int32, device=device)
         self.n_keep = torch.full((B,), T, dtype=torch.int32, device=device)
+        self.proj_fp32 = True        # also write the fp32 projection outputs
+        self.out_fp32 = True         # also write the fp32 GDN / attention outputs
 
     # ------------------------------------------------------------------
     def prefix_state_on_device(self):
@@ -134,26 +136,42 @@ class Layer:
         self.kv_len.copy_(self.L0)
 
     # ------------------------------------------------------------------
+    def gemm1(self):
+        xv.xv_gemm_small_m(self.x, self.W1, self.y1, self.y1_32 if self.proj_fp32 else None,
+                           stream=self.stream)
+
+    def gemm2(self):
+        xv.xv_gemm_small_m(self.x, self.W2, self.y2, self.y2_32 if self.proj_fp32 else None,
+                           stream=self.stream)
+
     def gemms(self):
-        xv.xv_gemm_small_m(self.x, self.W1, self.y1, self.y1_32, stream=self.stream)
-        xv.xv_gemm_small_m(self.x, self.W2, self.y2, self.y2_32, stream=self.stream)
+        self.gemm1()
+        self.gemm2()
 
     def gdn(self):
         xv.xv_gdn_verify(self.q, self.k, self.v, self.a, self.b, self.S_in, self.S_out,
-                         self.o_gdn, self.o_gdn32, stream=self.stream)
+                         self.o_gdn, self.o_gdn32 if self.out_fp32 else None, stream=self.stream)
 
     def attn(self):
         xv.xv_attn_verify_rows(self.qa, self.kn, self.vn, self.Kc, self.Vc, self.kv_len,
-                               self.o_attn, self.o_attn32, self.ws, self.scale, stream=self.stream)
+                               self.o_attn, self.o_attn32 if self.out_fp32 else None, self.ws,
+                               self.scale, stream=self.stream)
 
-    def head(self):
+    def head_gemms(self):
         wl, M = self.wl, self.wl.M
         xv.xv_gemm_small_m(self.o_gdn.view(M, wl.Hv * wl.dv), self.Wh_g, self.lg, self.lg32,
                            stream=self.stream)
         xv.xv_gemm_small_m(self.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, self.la, self.la32,
                            stream=self.stream)
+
+    def greedy(self):
+        wl = self.wl
         xv.xv_greedy_accept(self.lg32.view(self.B, self.T, wl.NH), self.la32.view(self.B, self.T, wl.NH),
                             self.draft, self.ids, self.n_keep, stream=self.stream)
+
+    def head(self):
+        self.head_gemms()
+        self.greedy()
 
     def rollback(self, n_keep: Optional[torch.Tensor] = None):
         xv.xv_rollback_to_prefix(self.k, self.v, self.a, self.b, self.S_in, self.S_out, self.kv_len,
@@ -169,6 +187,17 @@ class Layer:
             self.head()
         if rollback:
             self.rollback(n_keep)
+
+    def advance(self):
+        """After verify + rollback: the kept state becomes the next step's input state."""
+        self.S_in, self.S_out = self.S_out, self.S_in
+
+    def clone(self) -> "Layer":
+        """A second layer with the same contents in separate device buffers."""
+        other = Layer.__new__(Layer)
+        for key, val in self.__dict__.items():
+            other.__dict__[key] = val.clone() if isinstance(val, torch.Tensor) else val
+        return other
 
     # ------------------------------------------------------------------
     def decode_sequence(self, n_tokens: Optional[int] = None):
