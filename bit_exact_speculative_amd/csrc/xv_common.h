@@ -34,6 +34,14 @@ __device__ __forceinline__ uint16_t xv_f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Two fp32 values -> packed bf16 pair (low half = a), round to nearest even
+// (v_cvt_pk_bf16_f32 on gfx950).
+typedef float xv_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 xv_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t xv_pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(xv_f32x2{a, b}, xv_bf16x2));
+}
+
 // ---------------------------------------------------------------------------
 // MFMA operand types (v_mfma_f32_16x16x32_bf16: A 16x32, B 32x16, C/D 16x16 fp32)
 //   lane l supplies A[l % 16][8 * (l / 16) + e] and B[8 * (l / 16) + e][l % 16]

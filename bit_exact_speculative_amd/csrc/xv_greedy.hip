@@ -6,84 +6,107 @@
 // before it.  The argmax is unique, so the reduction order below does not
 // matter for the result (the comparison is exact and total on finite values).
 //
-// One 1024-thread workgroup per request scans all T rows at once: every thread
-// keeps a running (value, index) per row over a strided slice, then the rows
-// are reduced across the wave with lane shuffles and across the 16 waves in
-// LDS, and thread 0 counts the accepted drafts.
+// Two kernels on the caller's stream: one workgroup per verify row reduces the
+// row (running (value, index) per thread over a strided slice, then lane
+// shuffles and LDS across the waves), then one thread per request counts the
+// accepted drafts.
 #include "xv_common.h"
 
 namespace {
 
-constexpr int XV_GREEDY_THREADS = 1024;
+constexpr int XV_GREEDY_THREADS = 256;
 constexpr int XV_GREEDY_WAVES = XV_GREEDY_THREADS / 64;
 constexpr int XV_TMAX = 16;           // verify rows per request, at most
+constexpr int XV_GREEDY_UNROLL = 4;   // strides per pass, all loaded before any compare
 
 __device__ __forceinline__ bool xv_better(float v1, int n1, float v0, int n0) {
     return v1 > v0 || (v1 == v0 && n1 < n0);
 }
 
-// TT >= T rows per pass; rows past T re-read row T-1 and are ignored, so the
-// loads of all rows are straight-line code and stay in flight together.
-template <int TT>
+// One workgroup per verify row (grid T x B): argmax of the row's logits.
+// VEC: 16-byte loads (rows 16-byte aligned, N % 4 == 0); otherwise 4-byte loads.
+// Indices past the row re-read its last element and are masked out.
+template <bool VEC>
 __global__ __launch_bounds__(XV_GREEDY_THREADS)
-void xv_greedy_kernel(const float* __restrict__ la, const float* __restrict__ lb,
-                      const int32_t* __restrict__ draft, int T, int N,
-                      int32_t* __restrict__ ids, int32_t* __restrict__ n_keep)
+void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb, int T, int N,
+                      int32_t* __restrict__ ids)
 {
-    __shared__ float sv[XV_GREEDY_WAVES][TT];
-    __shared__ int sn[XV_GREEDY_WAVES][TT];
-    __shared__ int sid[TT];
-    const int b = blockIdx.x;
+    __shared__ float sv[XV_GREEDY_WAVES];
+    __shared__ int sn[XV_GREEDY_WAVES];
+    const int t = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-
-    float best[TT];
-    int bn[TT];
-    size_t rowoff[TT];
+    const size_t row = ((size_t)b * T + t) * N;
+    float best = -INFINITY;
+    int bn = N;                                  // sentinel: after every real index
+    if (VEC) {
+        const float4* pa = reinterpret_cast<const float4*>(la + row);
+        const float4* pb = reinterpret_cast<const float4*>(lb ? lb + row : la + row);
+        const int N4 = N >> 2;
+        for (int v0 = tid; v0 < N4; v0 += XV_GREEDY_THREADS * XV_GREEDY_UNROLL) {
+            float4 va[XV_GREEDY_UNROLL], vb[XV_GREEDY_UNROLL];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
-        best[t] = -INFINITY;
-        bn[t] = N;                                   // sentinel: after every real index
-        rowoff[t] = ((size_t)b * T + (t < T ? t : T - 1)) * N;
-    }
-    for (int n = tid; n < N; n += XV_GREEDY_THREADS) {
-        float val[TT];
+            for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
+                const int v = v0 + u * XV_GREEDY_THREADS;
+                const int vc = v < N4 ? v : N4 - 1;
+                va[u] = pa[vc];
+                vb[u] = pb[vc];
+            }
 #pragma unroll
-        for (int t = 0; t < TT; ++t) val[t] = la[rowoff[t] + n];
-        if (lb) {
-#pragma unroll
-            for (int t = 0; t < TT; ++t) val[t] = val[t] + lb[rowoff[t] + n];
+            for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
+                const int v = v0 + u * XV_GREEDY_THREADS;
+                if (v < N4) {
+                    float4 x = va[u];
+                    if (lb) { x.x = x.x + vb[u].x; x.y = x.y + vb[u].y; x.z = x.z + vb[u].z; x.w = x.w + vb[u].w; }
+                    const int n = 4 * v;
+                    if (xv_better(x.x, n, best, bn)) { best = x.x; bn = n; }
+                    if (xv_better(x.y, n + 1, best, bn)) { best = x.y; bn = n + 1; }
+                    if (xv_better(x.z, n + 2, best, bn)) { best = x.z; bn = n + 2; }
+                    if (xv_better(x.w, n + 3, best, bn)) { best = x.w; bn = n + 3; }
+                }
+            }
         }
+    } else {
+        for (int n0 = tid; n0 < N; n0 += XV_GREEDY_THREADS * XV_GREEDY_UNROLL) {
+            float va[XV_GREEDY_UNROLL], vb[XV_GREEDY_UNROLL];
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
-            if (xv_better(val[t], n, best[t], bn[t])) { best[t] = val[t]; bn[t] = n; }
-    }
+            for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
+                const int n = n0 + u * XV_GREEDY_THREADS;
+                const int nc = n < N ? n : N - 1;
+                va[u] = la[row + nc];
+                vb[u] = lb ? lb[row + nc] : 0.f;
+            }
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(best[t], off);
-            const int on = __shfl_xor(bn[t], off);
-            if (xv_better(ov, on, best[t], bn[t])) { best[t] = ov; bn[t] = on; }
+            for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
+                const int n = n0 + u * XV_GREEDY_THREADS;
+                const float x = lb ? va[u] + vb[u] : va[u];
+                if (n < N && xv_better(x, n, best, bn)) { best = x; bn = n; }
+            }
         }
-        if (lane == 0) { sv[wave][t] = best[t]; sn[wave][t] = bn[t]; }
     }
-    __syncthreads();
-    if (tid < T) {
-        float bv = sv[0][tid];
-        int bi = sn[0][tid];
-        for (int w = 1; w < XV_GREEDY_WAVES; ++w)
-            if (xv_better(sv[w][tid], sn[w][tid], bv, bi)) { bv = sv[w][tid]; bi = sn[w][tid]; }
-        const int id = bi < N ? bi : 0;
-        ids[(size_t)b * T + tid] = id;
-        sid[tid] = id;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(best, off);
+        const int on = __shfl_xor(bn, off);
+        if (xv_better(ov, on, best, bn)) { best = ov; bn = on; }
     }
+    if ((tid & 63) == 0) { sv[tid >> 6] = best; sn[tid >> 6] = bn; }
     __syncthreads();
     if (tid == 0) {
-        int acc = 0;
-        while (acc + 1 < T && draft[(size_t)b * T + acc + 1] == sid[acc]) ++acc;
-        n_keep[b] = acc + 1;
+        for (int w = 1; w < XV_GREEDY_WAVES; ++w)
+            if (xv_better(sv[w], sn[w], best, bn)) { best = sv[w]; bn = sn[w]; }
+        ids[(size_t)b * T + t] = bn < N ? bn : 0;
     }
+}
+
+// One thread per request: accepted drafts = leading rows whose id equals the next draft.
+__global__ void xv_accept_kernel(const int32_t* __restrict__ draft, const int32_t* __restrict__ ids,
+                                 int B, int T, int32_t* __restrict__ n_keep)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    int acc = 0;
+    while (acc + 1 < T && draft[(size_t)b * T + acc + 1] == ids[(size_t)b * T + acc]) ++acc;
+    n_keep[b] = acc + 1;
 }
 
 }  // namespace
@@ -98,14 +121,13 @@ extern "C" int xv_greedy_accept(const float* logits_a, const float* logits_b, co
                xv_aligned(ids, 4) && xv_aligned(n_keep, 4), XV_ERR_ALIGN);
     (void)hipGetLastError();
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const dim3 grid(B), block(XV_GREEDY_THREADS);
-    if (T <= 1)
-        hipLaunchKernelGGL(xv_greedy_kernel<1>, grid, block, 0, st, logits_a, logits_b, draft, T, N, ids, n_keep);
-    else if (T <= 4)
-        hipLaunchKernelGGL(xv_greedy_kernel<4>, grid, block, 0, st, logits_a, logits_b, draft, T, N, ids, n_keep);
-    else if (T <= 9)
-        hipLaunchKernelGGL(xv_greedy_kernel<9>, grid, block, 0, st, logits_a, logits_b, draft, T, N, ids, n_keep);
-    else
-        hipLaunchKernelGGL(xv_greedy_kernel<16>, grid, block, 0, st, logits_a, logits_b, draft, T, N, ids, n_keep);
+    // 16-byte loads when every row starts 16-byte aligned; the argmax is the same either way
+    const bool vec = (N % 4 == 0) && xv_aligned16(logits_a) && xv_aligned16(logits_b);
+    const dim3 grid(T, B), block(XV_GREEDY_THREADS);
+    if (vec) hipLaunchKernelGGL(xv_argmax_kernel<true>, grid, block, 0, st, logits_a, logits_b, T, N, ids);
+    else hipLaunchKernelGGL(xv_argmax_kernel<false>, grid, block, 0, st, logits_a, logits_b, T, N, ids);
+    const int s1 = xv_launch_status();
+    if (s1 != XV_OK) return s1;
+    hipLaunchKernelGGL(xv_accept_kernel, dim3((B + 63) / 64), dim3(64), 0, st, draft, ids, B, T, n_keep);
     return xv_launch_status();
 }
