@@ -122,10 +122,12 @@ void xv_gemm_xreg_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
     int blk = blockIdx.x;
     load_half(w0, blk, 0);
     for (;;) {
-        const int nxt = blk + grid < nblk ? blk + grid : blk;    // clamped prefetch target
+        // prefetch the next block's first half; after the last block re-read the
+        // half just loaded (a cache hit) so the loads stay straight-line code
+        const bool more = blk + grid < nblk;
         load_half(w1, blk, 1);
         mma_half(w0, 0);
-        load_half(w0, nxt, 0);
+        load_half(w0, more ? blk + grid : blk, more ? 0 : 1);
         mma_half(w1, 1);
         xv_gemm_finish<MT>(red, acc, lane, wave, blk, mt0, M, N, y, y32);
         blk += grid;
