@@ -135,6 +135,107 @@ void xv_gemm_xreg_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
     }
 }
 
+// W staged through LDS: the workgroup streams each column block's 16 rows with
+// 1 KB contiguous wave loads (each 16-byte granule of a stage is one thread's
+// load) into a padded LDS stage; each wave then reads the MFMA B fragments of its
+// own K range from LDS.  A column block is NS stages of SL k-steps (stage s holds
+// the ranges of waves s*16/NS .. (s+1)*16/NS - 1); even and odd stages have a
+// register buffer each, so while one stage is consumed the next two are in
+// flight.  x fragments of the wave's range live in registers.  Same K split,
+// MFMA chains and ordered sum as the other variants.
+// Requires K = NS * SL * 32 and SL * NS = 16 * KSW (the 16 ranges split evenly).
+template <int KSW, int SL, int NS>
+__global__ __launch_bounds__(XV_GEMM_THREADS)
+void xv_gemm_wlds_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                         uint16_t* __restrict__ y, float* __restrict__ y32,
+                         int M, int N, int K, int mt0)
+{
+    static_assert(NS % 2 == 0 && SL * NS == XV_GEMM_WAVES * KSW, "stages must split the ranges evenly");
+    constexpr int WPS = XV_GEMM_WAVES / NS;         // waves whose ranges a stage holds
+    constexpr int PITCH = SL * 32 + 8;              // LDS row pitch (bf16): rows fall 4 banks apart
+    constexpr int PER_ROW = SL * 4;                 // 16-byte granules per row per stage
+    constexpr int TOTAL = 16 * PER_ROW;
+    constexpr int GPT = (TOTAL + XV_GEMM_THREADS - 1) / XV_GEMM_THREADS;
+    __shared__ float red[XV_GEMM_WAVES][64][4];
+    __shared__ __attribute__((aligned(16))) uint16_t stage[16 * PITCH];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int ks0 = wave * KSW;
+    const int my_stage = wave / WPS;
+    const int nblk = N >> 4;
+    const int grid = gridDim.x;
+    if ((int)blockIdx.x >= nblk) return;            // uniform over the workgroup
+    const xv_u32x4 zero = {0u, 0u, 0u, 0u};
+
+    xv_u32x4 xr[KSW];
+    {
+        const int row = mt0 * 16 + lr;
+        const bool ok = row < M;
+        const uint16_t* xp = x + (size_t)(ok ? row : M - 1) * K + (size_t)ks0 * 32 + lg * 8;
+#pragma unroll
+        for (int j = 0; j < KSW; ++j) xr[j] = xv_load16(xp + j * 32);
+#pragma unroll
+        for (int j = 0; j < KSW; ++j) xr[j] = ok ? xr[j] : zero;
+    }
+
+    // this thread's granules: (row, 16-byte column) of a stage, the same for every stage
+    int goff[GPT], loff[GPT];
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+        int g = tid + i * XV_GEMM_THREADS;
+        g = g < TOTAL ? g : TOTAL - 1;
+        const int r = g / PER_ROW, c = g % PER_ROW;
+        goff[i] = r * K + c * 8;
+        loff[i] = r * PITCH + c * 8;
+    }
+    auto load_stage = [&](xv_u32x4 (&gr)[GPT], int blk, int st) {
+        const uint16_t* base = w + (size_t)blk * 16 * K + st * (SL * 32);
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) gr[i] = xv_load16(base + goff[i]);
+    };
+    auto store_stage = [&](const xv_u32x4 (&gr)[GPT]) {
+#pragma unroll
+        for (int i = 0; i < GPT; ++i)
+            if (TOTAL % XV_GEMM_THREADS == 0 || tid + i * XV_GEMM_THREADS < TOTAL)
+                *reinterpret_cast<xv_u32x4*>(stage + loff[i]) = gr[i];
+    };
+    xv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+    xv_u32x4 g0[GPT], g1[GPT];
+    int blk = blockIdx.x;
+    load_stage(g0, blk, 0);
+    load_stage(g1, blk, 1);
+    for (;;) {
+        const int nb = blk + grid;
+        const bool more = nb < nblk;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            xv_u32x4 (&gr)[GPT] = (st & 1) ? g1 : g0;
+            __syncthreads();                        // LDS stage free
+            store_stage(gr);
+            // this buffer's next stage: st + 2 of this block, else of the next block;
+            // past the end re-read the stage just stored (a cache hit)
+            if (st + 2 < NS) load_stage(gr, blk, st + 2);
+            else load_stage(gr, more ? nb : blk, more ? st + 2 - NS : st);
+            __syncthreads();
+            if (my_stage == st) {                   // uniform per wave
+                const uint16_t* bp = stage + lr * PITCH + (ks0 - st * SL) * 32 + lg * 8;
+#pragma unroll
+                for (int j = 0; j < KSW; ++j)
+                    acc = xv_mfma16x16x32(xr[j], *reinterpret_cast<const xv_u32x4*>(bp + j * 32), acc);
+            }
+        }
+        xv_f32x4 accs[1] = {acc};
+        xv_gemm_finish<1>(red, accs, lane, wave, blk, mt0, M, N, y, y32);
+        acc = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!more) break;
+        blk = nb;
+    }
+}
+
 // x fragments re-read per k-step (many row tiles or long K): U k-steps per stage.
 template <int MT, int U>
 __global__ __launch_bounds__(XV_GEMM_THREADS)
@@ -232,6 +333,14 @@ void xv_gemm_launch_xreg(const uint16_t* x, const uint16_t* w, uint16_t* y, floa
     hipLaunchKernelGGL((xv_gemm_xreg_kernel<MT, KSW>), grid, block, 0, st, x, w, y, y32, M, N, K, mt0);
 }
 
+template <int KSW, int SL, int NS>
+void xv_gemm_launch_wlds(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
+                         int M, int N, int K, int mt0, hipStream_t st)
+{
+    dim3 grid(xv_gemm_grid(N / 16)), block(XV_GEMM_THREADS);
+    hipLaunchKernelGGL((xv_gemm_wlds_kernel<KSW, SL, NS>), grid, block, 0, st, x, w, y, y32, M, N, K, mt0);
+}
+
 template <int MT, int U>
 void xv_gemm_launch_xstream(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
                             int M, int N, int K, int mt0, hipStream_t st)
@@ -246,6 +355,9 @@ void xv_gemm_launch_xstream(const uint16_t* x, const uint16_t* w, uint16_t* y, f
 void xv_gemm_dispatch(int mt, int ksw, const uint16_t* x, const uint16_t* w, uint16_t* y,
                       float* y32, int M, int N, int K, int mt0, hipStream_t st)
 {
+    // one row tile and the two K of the 27B-class layer: W through LDS in 1 KB contiguous wave loads
+    if (mt == 1 && K == 5120) { xv_gemm_launch_wlds<10, 40, 4>(x, w, y, y32, M, N, K, mt0, st); return; }
+    if (mt == 1 && K == 6144) { xv_gemm_launch_wlds<12, 48, 4>(x, w, y, y32, M, N, K, mt0, st); return; }
     if (mt == 1 && ksw <= 10) {
         if (ksw <= 2) xv_gemm_launch_xreg<1, 2>(x, w, y, y32, M, N, K, mt0, st);
         else if (ksw <= 4) xv_gemm_launch_xreg<1, 4>(x, w, y, y32, M, N, K, mt0, st);

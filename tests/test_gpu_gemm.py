@@ -37,7 +37,7 @@ def _gemm_dev(x, w, with32=True):
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 32), (5, 512, 256), (9, 48, 96), (16, 64, 544),
                                    (17, 32, 1024), (33, 16, 64), (72, 80, 320), (130, 32, 64),
-                                   (9, 112, 5120)])
+                                   (9, 112, 5120), (9, 48, 6144), (1, 32, 6144)])
 def test_gemm_matches_oracle(M, N, K):
     rng = np.random.default_rng(100 + M + N + K)
     x = random_bf16(rng, (M, K))
@@ -65,10 +65,14 @@ def test_gemm_exact_on_integers():
     assert np.array_equal(y32.astype(np.float64), oracle.gemm(x, w))
 
 
-def test_gemm_row_bits_independent_of_m_and_position():
-    """Row bits must not depend on M, on the other rows, or on the row's slot in a 16-row tile."""
-    rng = np.random.default_rng(8)
-    K, N = 5120, 96
+@pytest.mark.parametrize("K", [5120, 6144, 1024])
+def test_gemm_row_bits_independent_of_m_and_position(K):
+    """Row bits must not depend on M, on the other rows, or on the row's slot in a 16-row tile.
+
+    K = 5120 and 6144 take the LDS-staged kernel for M <= 16 and the x-streaming one for M = 72,
+    K = 1024 the register-streamed one for M <= 32: the bits must agree across all of them."""
+    rng = np.random.default_rng(8 + K)
+    N = 96
     from bit_exact_speculative_amd.layer import dev_bf16
     x72 = dev_bf16(random_bf16(rng, (72, K)), "cuda")
     w = dev_bf16(random_bf16(rng, (N, K), 0.02), "cuda")
