@@ -8,23 +8,26 @@
 // batch, on Lmax or on the workspace size.
 //
 // Two kernels on the caller's stream:
-//  1. xv_attn_partial_kernel, grid (chunk, KV head, request).  A chunk is
-//     XV_ATTN_C positions at an absolute boundary.  The workgroup loads the
-//     chunk's keys and values into LDS 64 positions at a time (new rows come
-//     from k_new/v_new and are also appended to the cache by the one
-//     workgroup whose chunk holds them), and computes, for every (query head of
-//     the group, row) pair with a visible position in the chunk:
+//  1. A partial kernel over chunks of XV_ATTN_C positions at absolute
+//     boundaries.  For each (query head, row) pair with a visible position in
+//     the chunk it computes
 //         s_j = (q . k_j) * (scale * log2 e) (bf16 MFMA, fp32 accumulate; log2 units)
 //         m_c = max_j s_j over visible j     (exact)
 //         p_j = 2^(s_j - m_c), 0 for masked j
-//         l_c = sum_j p_j                    (fixed order: in-lane ascending,
-//                                             then lane butterfly 16, 32)
-//         acc_c = sum_j p_j v_j              (MFMA with p split into bf16 hi + lo)
-//     Scores are computed transposed (S^T = K Q^T) so that each lane already
-//     holds the probabilities of its pair in the order the P.V MFMA consumes
-//     them.  A wave owns 16 pairs (one tile); when there are fewer tiles than
-//     waves, the tiles' P.V output dims are split over the spare waves (each
-//     output column is still one MFMA chain over the same k-slots).
+//         l_c = sum_j p_j                    (fixed order: in-lane over positions
+//                                             16 cb + 4 g + i ascending, then
+//                                             lane butterfly 16, 32)
+//         acc_c = sum_j p_j v_j              (MFMA with p split into bf16 hi + lo;
+//                                             per 16 output dims one chain over
+//                                             the chunk's k-slots, ascending)
+//     Scores are computed transposed (S^T = K Q^T) so that each lane holds its
+//     pair's probabilities in the order the P.V MFMA consumes them.  New rows
+//     come from k_new/v_new and are appended to the cache by one workgroup.
+//     Two kernels form exactly these numbers with different work splits:
+//     xv_attn_partial_wide_kernel (workgroup per chunk, KV head and request,
+//     wave per 16-pair tile) and xv_attn_partial_tile_kernel (workgroup per
+//     16-pair tile as well, the waves splitting its positions and output dims);
+//     the host picks by grid size only, so a pair's bits never depend on it.
 //  2. xv_attn_combine_kernel, grid (query head, row, request): with
 //     M = max_c m_c, beta_c = 2^(m_c - M), L = sum_c l_c beta_c and
 //     A = sum_c acc_c beta_c in ascending chunk order; o = A / L, stored as
@@ -37,8 +40,9 @@
 namespace {
 
 constexpr int XV_ATTN_C = 256;      // chunk length (positions), fixed for every call
-constexpr int XV_ATTN_WAVES = 8;    // 16 pairs per wave -> up to 128 (head, row) pairs
+constexpr int XV_ATTN_WAVES = 8;    // waves of a partial-kernel workgroup
 constexpr int XV_ATTN_MAX_NC = 8192;
+constexpr int XV_ATTN_WIDE_MIN = 128; // (chunk, KV head, request) workgroups from which the wide kernel runs
 
 // LDS layouts (16-byte granules, XOR-swizzled so that both the cooperative
 // stores and the MFMA fragment reads spread over the banks):
@@ -50,22 +54,152 @@ __device__ __forceinline__ int xv_vt_granule(int d, int c) {
     return d * (XV_ATTN_C / 8) + (c ^ ((d ^ (d >> 3)) & 7));
 }
 
+// One chunk of one request's KV head, staged through registers: every load is
+// issued at once and is straight-line: a position in [L0, L0 + T) reads the new
+// row, one before L0 the cache, one past L0 + T re-reads cache position 0 (never
+// used, zeroed before it reaches LDS).  The new rows are appended to the cache
+// after the loads.
+template <int D, int NT>
+struct XvChunk {
+    static constexpr int C = XV_ATTN_C;
+    static constexpr int KG = C * (D / 8) / NT;        // K granules per thread
+    static constexpr int VTILES = (C / 8) * (D / 8);   // 8 x 8 V tiles per chunk
+    static constexpr int VT = (VTILES + NT - 1) / NT;  // V tiles per thread (last may be partial)
+    xv_u32x4 kreg[KG];
+    xv_u32x4 vreg[VT][8];
+
+    __device__ __forceinline__ void load(const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+                                         const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                                         size_t kvbase, size_t newbase, int newstride, int L0, int Lend, int c0, int tid) {
+        auto src = [&](const uint16_t* cache, const uint16_t* fresh, int pos) -> const uint16_t* {
+            if (pos < L0) return cache + (kvbase + pos) * D;
+            if (pos < Lend) return fresh + newbase + (size_t)(pos - L0) * newstride;
+            return cache + kvbase * D;
+        };
+#pragma unroll
+        for (int i = 0; i < KG; ++i) {
+            const int idx = tid + i * NT;
+            kreg[i] = xv_load16(src(k_cache, k_new, c0 + idx / (D / 8)) + (idx % (D / 8)) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < VT; ++i) {
+            const int vt = (tid + i * NT) < VTILES ? tid + i * NT : VTILES - 1;
+            const int pg = vt / (D / 8), dg = vt % (D / 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vreg[i][e] = xv_load16(src(v_cache, v_new, c0 + pg * 8 + e) + dg * 8);
+        }
+    }
+    // zero the positions past L0 + T; append the new rows when `append`
+    __device__ __forceinline__ void settle(uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
+                                           size_t kvbase, int L0, int Lend, int c0, int tid, bool append) {
+        const xv_u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < KG; ++i) {
+            const int idx = tid + i * NT;
+            const int pos = c0 + idx / (D / 8);
+            if (pos >= Lend) kreg[i] = zero;
+            else if (append && pos >= L0) xv_store16(k_cache + (kvbase + pos) * D + (idx % (D / 8)) * 8, kreg[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < VT; ++i) {
+            const int vt = tid + i * NT;
+            const int pg = vt / (D / 8), dg = vt % (D / 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int pos = c0 + pg * 8 + e;
+                if (pos >= Lend || vt >= VTILES) vreg[i][e] = zero;
+                else if (append && pos >= L0) xv_store16(v_cache + (kvbase + pos) * D + dg * 8, vreg[i][e]);
+            }
+        }
+    }
+    __device__ __forceinline__ void k_to_lds(xv_u32x4* lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < KG; ++i) {
+            const int idx = tid + i * NT;
+            lds[xv_k_granule<D>(idx / (D / 8), idx % (D / 8))] = kreg[i];
+        }
+    }
+    // V^T into LDS through 8 x 8 register transposes
+    __device__ __forceinline__ void vt_to_lds(xv_u32x4* lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < VT; ++i) {
+            const int vt = tid + i * NT;
+            if (vt < VTILES) {
+                const int pg = vt / (D / 8), dg = vt % (D / 8);
+#pragma unroll
+                for (int dd = 0; dd < 8; ++dd) {
+                    xv_u32x4 outv;
+#pragma unroll
+                    for (int w2 = 0; w2 < 4; ++w2) {
+                        const uint32_t lo = vreg[i][2 * w2][dd >> 1], hi = vreg[i][2 * w2 + 1][dd >> 1];
+                        outv[w2] = (dd & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+                    }
+                    lds[xv_vt_granule(dg * 8 + dd, pg)] = outv;
+                }
+            }
+        }
+    }
+};
+
+// The P.V MFMA operands for k-slot group kk (chunk positions kk*32 ..): k-slot e
+// of lane group lg is position kk*32 + 4*lg + e (e < 4) or kk*32 + 16 + 4*lg + (e - 4),
+// which is where the transposed score MFMA left the lane's probabilities.
+// A: the 8 probabilities as bf16 hi + lo (p = hi + lo to 16 bits).
+__device__ __forceinline__ void xv_p_split(const xv_f32x4& pa, const xv_f32x4& pb, xv_u32x4& phi, xv_u32x4& plo) {
+    const float pe[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+        const uint32_t h = xv_pack_bf16x2(pe[2 * w2], pe[2 * w2 + 1]);
+        phi[w2] = h;
+        plo[w2] = xv_pack_bf16x2(pe[2 * w2] - xv_bf16_lo(h), pe[2 * w2 + 1] - xv_bf16_hi(h));
+    }
+}
+// B: V^T rows d = db*16 + lr at those positions.
+__device__ __forceinline__ xv_u32x4 xv_vt_frag(const xv_u32x4* lds, int db, int kk, int lr, int lg) {
+    const char* ldsb = reinterpret_cast<const char*>(lds);
+    const int d = db * 16 + lr;
+    const char* rowp = ldsb + (size_t)d * (XV_ATTN_C * 2) + (lg & 1) * 8;
+    const int sw = (d ^ (d >> 3)) & 7;
+    const int ca = kk * 4 + (lg >> 1);
+    const uint2 va = *reinterpret_cast<const uint2*>(rowp + ((ca ^ sw) << 4));
+    const uint2 vb = *reinterpret_cast<const uint2*>(rowp + (((ca + 2) ^ sw) << 4));
+    return xv_u32x4{va.x, va.y, vb.x, vb.y};
+}
+
+// Store a wave's P.V output blocks db0 .. db0 + NB - 1 of pairs tile*16 + 4*lg + i.
+template <int D, int NB>
+__device__ __forceinline__ void xv_store_acc(float* __restrict__ ws_acc, const xv_f32x4 (&oacc)[NB], int db0,
+                                             int tile, int lr, int lg, int P, int Hg, int g, int b, int T,
+                                             int Hq, int NC, int c, int L0, int c0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int pair = tile * 16 + 4 * lg + i;
+        if (pair >= P) continue;
+        const int r = pair / Hg;
+        if (L0 + r + 1 <= c0) continue;             // the row sees nothing of this chunk
+        const int h = g * Hg + pair % Hg;
+        float* dst = ws_acc + ((((size_t)b * T + r) * Hq + h) * NC + c) * D + lr;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) dst[(db0 + j) * 16] = oacc[j][i];
+    }
+}
+
+// Many workgroups (large batch or long context): one workgroup per (chunk, KV
+// head, request) serves every pair of the group, one 16-pair tile per wave: each
+// wave computes all of its tile's scores and all output dims.
 template <int D>
 __global__ __launch_bounds__(XV_ATTN_WAVES * 64)
-void xv_attn_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
-                            const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_cache,
-                            uint16_t* __restrict__ v_cache, const int32_t* __restrict__ kv_len,
-                            float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-                            int T, int Hq, int Hkv, int Lmax, int NC, float scale_log2)
+void xv_attn_partial_wide_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
+                                 const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_cache,
+                                 uint16_t* __restrict__ v_cache, const int32_t* __restrict__ kv_len,
+                                 float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+                                 int T, int Hq, int Hkv, int Lmax, int NC, float scale_log2)
 {
     constexpr int C = XV_ATTN_C;
     constexpr int NT = XV_ATTN_WAVES * 64;
     constexpr int KS = D / 32;                  // MFMA k-steps over the head dim
     constexpr int DB = D / 16;                  // 16-wide blocks of output dims
     constexpr int NCB = C / 16;                 // 16-position score blocks per chunk
-    constexpr int KG = C * (D / 8) / NT;        // K granules per thread
-    constexpr int VTILES = (C / 8) * (D / 8);   // 8 x 8 V tiles per chunk
-    constexpr int VT = (VTILES + NT - 1) / NT;  // V tiles per thread (last may be partial)
     __shared__ __attribute__((aligned(16))) xv_u32x4 lds[C * D / 8];
 
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -79,49 +213,20 @@ void xv_attn_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int tile = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    // waves -> (pair tile, slice of the output dims)
-    const int ntiles = (P + 15) / 16;
-    const int dsplit = 1;                       // one wave owns a tile's whole output
-    const int tile = wave / dsplit, dq = wave % dsplit;
-    const int dbw = DB / dsplit;                // output-dim blocks of this wave
-    const bool tile_on = tile < ntiles;
+    const bool tile_on = tile < (P + 15) / 16;
     const int pair = tile * 16 + lr;            // the pair whose scores this lane holds
     const bool pair_ok = pair < P;
     const int pr = pair_ok ? pair / Hg : 0;
     const int ph = g * Hg + (pair_ok ? pair % Hg : 0);
     const int plen = L0 + pr + 1;
     const bool full = c0 + C <= L0 + 1;         // every position visible to every row
-
     const size_t kvbase = ((size_t)b * Hkv + g) * Lmax;
     const xv_u32x4 zero = {0u, 0u, 0u, 0u};
 
-    // ---- issue every load of the chunk at once: K granules, V 8x8 tiles, Q ----
-    // Loads are straight-line: a position in [L0, L0 + T) reads the new row, one
-    // before L0 the cache, one past L0 + T re-reads cache position 0 (never used,
-    // zeroed below).  The new rows are appended to the cache afterwards.
-    auto src_row = [&](const uint16_t* cache, const uint16_t* fresh, int pos) -> const uint16_t* {
-        if (pos < L0) return cache + (kvbase + pos) * D;
-        if (pos < Lend) return fresh + (((size_t)b * T + (pos - L0)) * Hkv + g) * D;
-        return cache + kvbase * D;
-    };
-    xv_u32x4 kreg[KG];
-#pragma unroll
-    for (int i = 0; i < KG; ++i) {
-        const int idx = tid + i * NT;
-        const int pos = c0 + idx / (D / 8), cc = idx % (D / 8);
-        kreg[i] = xv_load16(src_row(k_cache, k_new, pos) + cc * 8);
-    }
-    xv_u32x4 vreg[VT][8];
-#pragma unroll
-    for (int i = 0; i < VT; ++i) {
-        const int tile = (tid + i * NT) < VTILES ? tid + i * NT : VTILES - 1;
-        const int pg = tile / (D / 8), dg = tile % (D / 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            vreg[i][e] = xv_load16(src_row(v_cache, v_new, c0 + pg * 8 + e) + dg * 8);
-    }
+    XvChunk<D, NT> ch;
+    ch.load(k_cache, v_cache, k_new, v_new, kvbase, ((size_t)b * T * Hkv + g) * D, Hkv * D, L0, Lend, c0, tid);
     xv_u32x4 qf[KS];
     {
         const uint16_t* qp = q + (((size_t)b * T + pr) * Hq + ph) * D + lg * 8;
@@ -130,31 +235,10 @@ void xv_attn_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = pair_ok ? qf[ks] : zero;
     }
-#pragma unroll
-    for (int i = 0; i < KG; ++i) {                       // zero past L0 + T; append new rows
-        const int idx = tid + i * NT;
-        const int pos = c0 + idx / (D / 8), cc = idx % (D / 8);
-        if (pos >= Lend) kreg[i] = zero;
-        else if (pos >= L0) xv_store16(k_cache + (kvbase + pos) * D + cc * 8, kreg[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < VT; ++i) {
-        const int tile = tid + i * NT;
-        const int pg = tile / (D / 8), dg = tile % (D / 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int pos = c0 + pg * 8 + e;
-            if (pos >= Lend || tile >= VTILES) vreg[i][e] = zero;
-            else if (pos >= L0) xv_store16(v_cache + (kvbase + pos) * D + dg * 8, vreg[i][e]);
-        }
-    }
+    ch.settle(k_cache, v_cache, kvbase, L0, Lend, c0, tid, true);
 
     // ---- K into LDS; scores S^T[pos][pair] for the whole chunk ----
-#pragma unroll
-    for (int i = 0; i < KG; ++i) {
-        const int idx = tid + i * NT;
-        lds[xv_k_granule<D>(idx / (D / 8), idx % (D / 8))] = kreg[i];
-    }
+    ch.k_to_lds(lds, tid);
     __syncthreads();
     xv_f32x4 sc[NCB];
 #pragma unroll
@@ -194,89 +278,190 @@ void xv_attn_partial_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     l = l + __shfl_xor(l, 16);
     l = l + __shfl_xor(l, 32);
 
-    // ---- V^T into LDS (8 x 8 register transposes), then acc = P V ----
+    // ---- V^T into LDS, then acc = P V: per output block one chain over k-slots, hi then lo ----
     __syncthreads();                            // every wave is done reading K
-#pragma unroll
-    for (int i = 0; i < VT; ++i) {
-        const int tile = tid + i * NT;
-        if (tile < VTILES) {
-            const int pg = tile / (D / 8), dg = tile % (D / 8);
-#pragma unroll
-            for (int dd = 0; dd < 8; ++dd) {
-                xv_u32x4 outv;
-#pragma unroll
-                for (int w2 = 0; w2 < 4; ++w2) {
-                    const uint32_t lo = vreg[i][2 * w2][dd >> 1], hi = vreg[i][2 * w2 + 1][dd >> 1];
-                    outv[w2] = (dd & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u))
-                                        : ((lo & 0xFFFFu) | (hi << 16));
-                }
-                lds[xv_vt_granule(dg * 8 + dd, pg)] = outv;
-            }
-        }
-    }
+    ch.vt_to_lds(lds, tid);
     __syncthreads();
+    if (!tile_on) return;
     xv_f32x4 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
-    if (tile_on) {
-        const char* ldsb = reinterpret_cast<const char*>(lds);
-        const int half = (lg & 1) * 8;          // byte offset inside a 16-byte granule
 #pragma unroll
-        for (int kk = 0; kk < C / 32; ++kk) {
-            // k-slot e of lane group lg <-> chunk position kk*32 + 4*lg + e (e < 4)
-            //                                    or kk*32 + 16 + 4*lg + (e - 4)
-            const xv_f32x4 pa = sc[kk * 2];
-            const xv_f32x4 pb = sc[kk * 2 + 1];
-            const float pe[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
-            xv_u32x4 phi, plo;
+    for (int kk = 0; kk < C / 32; ++kk) {
+        xv_u32x4 phi, plo;
+        xv_p_split(sc[kk * 2], sc[kk * 2 + 1], phi, plo);
+        // blocks of a group of 4 are interleaved so dependent MFMAs never issue back to back
 #pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
-                const uint32_t h = xv_pack_bf16x2(pe[2 * w2], pe[2 * w2 + 1]);
-                phi[w2] = h;
-                plo[w2] = xv_pack_bf16x2(pe[2 * w2] - xv_bf16_lo(h), pe[2 * w2 + 1] - xv_bf16_hi(h));
-            }
-            const int ca = kk * 4 + (lg >> 1);      // granule of positions kk*32 + 4*lg ..
-            // per output block: hi then lo; blocks of a group of 4 are interleaved
+        for (int db0 = 0; db0 < DB; db0 += 4) {
+            xv_u32x4 vf[4];
 #pragma unroll
-            for (int db0 = 0; db0 < DB; db0 += 4) {
-                if (db0 / dbw != dq) continue;      // uniform per wave
-                xv_u32x4 vf[4];
+            for (int u = 0; u < 4; ++u) vf[u] = xv_vt_frag(lds, db0 + u, kk, lr, lg);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int d = (db0 + u) * 16 + lr;
-                    const char* rowp = ldsb + (size_t)d * (C * 2) + half;
-                    const int sw = (d ^ (d >> 3)) & 7;
-                    const uint2 va = *reinterpret_cast<const uint2*>(rowp + ((ca ^ sw) << 4));
-                    const uint2 vb = *reinterpret_cast<const uint2*>(rowp + (((ca + 2) ^ sw) << 4));
-                    vf[u] = xv_u32x4{va.x, va.y, vb.x, vb.y};
-                }
+            for (int u = 0; u < 4; ++u) oacc[db0 + u] = xv_mfma16x16x32(phi, vf[u], oacc[db0 + u]);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) oacc[db0 + u] = xv_mfma16x16x32(phi, vf[u], oacc[db0 + u]);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) oacc[db0 + u] = xv_mfma16x16x32(plo, vf[u], oacc[db0 + u]);
-            }
+            for (int u = 0; u < 4; ++u) oacc[db0 + u] = xv_mfma16x16x32(plo, vf[u], oacc[db0 + u]);
         }
     }
 
-    // ---- write the chunk partials of pairs that see this chunk ----
-    if (!tile_on) return;
-    if (dq == 0 && lg == 0 && pair_ok && plen > c0) {
+    // ---- the chunk partials of pairs that see this chunk ----
+    if (lg == 0 && pair_ok && plen > c0) {
         const size_t idx = (((size_t)b * T + pr) * Hq + ph) * NC + c;
         ws_ml[idx * 2 + 0] = m;
         ws_ml[idx * 2 + 1] = l;
     }
+    xv_store_acc<D, DB>(ws_acc, oacc, 0, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
+}
+
+// Few workgroups (small batch, short context): one workgroup per (request, KV
+// head, chunk, 16-pair tile), so that the chunk's work is spread over more CUs.
+// The waves split the tile's score blocks, the probabilities go through LDS, and
+// each wave forms the output dims of its slice.  Every chain and ordered sum is
+// the one the wide kernel forms, so the two give the same bits.
+template <int D>
+__global__ __launch_bounds__(XV_ATTN_WAVES * 64)
+void xv_attn_partial_tile_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
+                                 const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_cache,
+                                 uint16_t* __restrict__ v_cache, const int32_t* __restrict__ kv_len,
+                                 float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+                                 int T, int Hq, int Hkv, int Lmax, int NC, int NTILE, int items,
+                                 int per_xcd, float scale_log2)
+{
+    constexpr int C = XV_ATTN_C;
+    constexpr int NW = XV_ATTN_WAVES;
+    constexpr int NT = NW * 64;
+    constexpr int KS = D / 32;
+    constexpr int DB = D / 16;
+    constexpr int NCB = C / 16;
+    constexpr int CBW = NCB / NW;               // score blocks per wave
+    constexpr int DBW = DB >= NW ? DB / NW : 1; // output blocks per wave (waves past DB idle)
+    constexpr int PP = C + 4;                   // probability row pitch (floats)
+    static_assert(NCB % NW == 0, "score blocks must split evenly over the waves");
+    __shared__ __attribute__((aligned(16))) xv_u32x4 lds[C * D / 8];
+    __shared__ __attribute__((aligned(16))) float sp[16 * PP];
+    __shared__ float smax[NW][16];
+
+    // work item: consecutive items (the tiles of one chunk first) share an XCD's L2
+    const int u = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+    if (u >= items) return;
+    const int tile = u % NTILE;
+    const int c = (u / NTILE) % NC;
+    const int g = (u / (NTILE * NC)) % Hkv;
+    const int b = u / (NTILE * NC * Hkv);
+    const int Hg = Hq / Hkv;
+    const int P = Hg * T;
+    int L0 = kv_len[b];
+    L0 = L0 < 0 ? 0 : (L0 > Lmax - T ? Lmax - T : L0);
+    const int Lend = L0 + T;
+    const int c0 = c * C;
+    if (c0 >= Lend) return;                     // uniform over the workgroup
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int pair = tile * 16 + lr;            // the pair whose scores this lane holds
+    const bool pair_ok = pair < P;
+    const int pr = pair_ok ? pair / Hg : 0;
+    const int ph = g * Hg + (pair_ok ? pair % Hg : 0);
+    const int plen = L0 + pr + 1;
+    const bool full = c0 + C <= L0 + 1;         // every position visible to every row
+    const size_t kvbase = ((size_t)b * Hkv + g) * Lmax;
+    const xv_u32x4 zero = {0u, 0u, 0u, 0u};
+
+    XvChunk<D, NT> ch;
+    ch.load(k_cache, v_cache, k_new, v_new, kvbase, ((size_t)b * T * Hkv + g) * D, Hkv * D, L0, Lend, c0, tid);
+    xv_u32x4 qf[KS];
+    {
+        const uint16_t* qp = q + (((size_t)b * T + pr) * Hq + ph) * D + lg * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int pair2 = tile * 16 + 4 * lg + i;
-        if (pair2 >= P) continue;
-        const int r2 = pair2 / Hg;
-        if (L0 + r2 + 1 <= c0) continue;
-        const int h2 = g * Hg + pair2 % Hg;
-        float* dst = ws_acc + ((((size_t)b * T + r2) * Hq + h2) * NC + c) * D + lr;
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = xv_load16(qp + ks * 32);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-            if (db / dbw == dq) dst[db * 16] = oacc[db][i];
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = pair_ok ? qf[ks] : zero;
     }
+    ch.settle(k_cache, v_cache, kvbase, L0, Lend, c0, tid, tile == 0);   // tile 0 appends
+
+    // ---- K into LDS; this wave's score blocks S^T[pos][pair] ----
+    ch.k_to_lds(lds, tid);
+    __syncthreads();
+    const int cb0 = wave * CBW;
+    xv_f32x4 sc[CBW];
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) sc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < CBW; ++j)
+            sc[j] = xv_mfma16x16x32(lds[xv_k_granule<D>((cb0 + j) * 16 + lr, ks * 4 + lg)], qf[ks], sc[j]);
+
+    // ---- chunk max over every wave's blocks (exact), probabilities into LDS ----
+    float mw = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < CBW; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float sv = sc[j][i] * scale_log2;
+            sc[j][i] = sv;
+            if (full || c0 + (cb0 + j) * 16 + 4 * lg + i < plen) mw = fmaxf(mw, sv);
+        }
+    mw = fmaxf(mw, __shfl_xor(mw, 16));
+    mw = fmaxf(mw, __shfl_xor(mw, 32));
+    if (lg == 0) smax[wave][lr] = mw;
+    __syncthreads();                            // also: every wave is done reading K
+    float m = smax[0][lr];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, smax[w][lr]);
+    if (!pair_ok) m = 0.f;                      // lanes of padding pairs: keep finite
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+        xv_f32x4 pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool vis = full || c0 + (cb0 + j) * 16 + 4 * lg + i < plen;
+            pv[i] = vis ? __builtin_amdgcn_exp2f(sc[j][i] - m) : 0.f;
+        }
+        *reinterpret_cast<xv_f32x4*>(sp + lr * PP + (cb0 + j) * 16 + 4 * lg) = pv;
+    }
+    ch.vt_to_lds(lds, tid);
+    __syncthreads();
+
+    // ---- chunk sum l (wave 0), in the wide kernel's order ----
+    if (wave == 0) {
+        float l = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const xv_f32x4 pv = *reinterpret_cast<const xv_f32x4*>(sp + lr * PP + cb * 16 + 4 * lg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) l = l + pv[i];
+        }
+        l = l + __shfl_xor(l, 16);
+        l = l + __shfl_xor(l, 32);
+        if (lg == 0 && pair_ok && plen > c0) {
+            const size_t idx = (((size_t)b * T + pr) * Hq + ph) * NC + c;
+            ws_ml[idx * 2 + 0] = m;
+            ws_ml[idx * 2 + 1] = l;
+        }
+    }
+
+    // ---- acc = P V for this wave's output blocks ----
+    const int db0 = wave * DBW;
+    if (db0 >= DB) return;                      // uniform per wave; no barrier follows
+    xv_f32x4 oacc[DBW];
+#pragma unroll
+    for (int j = 0; j < DBW; ++j) oacc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < C / 32; ++kk) {
+        xv_u32x4 phi, plo;
+        xv_p_split(*reinterpret_cast<const xv_f32x4*>(sp + lr * PP + kk * 32 + 4 * lg),
+                   *reinterpret_cast<const xv_f32x4*>(sp + lr * PP + kk * 32 + 16 + 4 * lg), phi, plo);
+        xv_u32x4 vf[DBW];
+#pragma unroll
+        for (int j = 0; j < DBW; ++j) vf[j] = xv_vt_frag(lds, db0 + j, kk, lr, lg);
+#pragma unroll
+        for (int j = 0; j < DBW; ++j) oacc[j] = xv_mfma16x16x32(phi, vf[j], oacc[j]);
+#pragma unroll
+        for (int j = 0; j < DBW; ++j) oacc[j] = xv_mfma16x16x32(plo, vf[j], oacc[j]);
+    }
+    xv_store_acc<D, DBW>(ws_acc, oacc, db0, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
 }
 
 template <int D>
@@ -339,9 +524,22 @@ int xv_attn_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_n
     (void)hipGetLastError();
     // scores are kept in log2 units: s * log2(e), so that 2^(s' - m') = e^(s - m)
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-    hipLaunchKernelGGL(xv_attn_partial_kernel<D>, dim3(NC, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st,
-                       q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
-                       T, Hq, Hkv, Lmax, NC, scale_log2);
+    // Both partial kernels give the same bits; the choice only spreads the work:
+    // one workgroup per (chunk, KV head, request) when those alone fill the chip,
+    // otherwise one per 16-pair tile of each.
+    const int P = (Hq / Hkv) * T;
+    if ((long long)B * Hkv * NC >= XV_ATTN_WIDE_MIN && P <= 16 * XV_ATTN_WAVES) {
+        hipLaunchKernelGGL(xv_attn_partial_wide_kernel<D>, dim3(NC, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st,
+                           q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
+                           T, Hq, Hkv, Lmax, NC, scale_log2);
+    } else {
+        const int ntile = (P + 15) / 16;
+        const int items = B * Hkv * NC * ntile;
+        const int per_xcd = (items + 7) / 8;
+        hipLaunchKernelGGL(xv_attn_partial_tile_kernel<D>, dim3(8 * per_xcd), dim3(XV_ATTN_WAVES * 64), 0, st,
+                           q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
+                           T, Hq, Hkv, Lmax, NC, ntile, items, per_xcd, scale_log2);
+    }
     int s = xv_launch_status();
     if (s != XV_OK) return s;
     const size_t shmem = sizeof(float) * (2 * (size_t)NC + D);
@@ -374,9 +572,13 @@ extern "C" int xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, con
                                    void* stream)
 {
     XV_REQUIRE(B >= 0 && T >= 1 && T <= 16 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, XV_ERR_SHAPE);
-    XV_REQUIRE((Hq / Hkv) * T <= 16 * XV_ATTN_WAVES, XV_ERR_SHAPE);
     XV_REQUIRE(d == 64 || d == 128 || d == 256, XV_ERR_SHAPE);
     XV_REQUIRE(Lmax >= T && (Lmax + XV_ATTN_C - 1) / XV_ATTN_C <= XV_ATTN_MAX_NC, XV_ERR_SHAPE);
+    {   // partial-kernel workgroups (one per request, KV head, chunk, 16 pairs) must fit the grid
+        const long long ntile = ((long long)(Hq / Hkv) * T + 15) / 16;
+        const long long items = (long long)B * Hkv * ((Lmax + XV_ATTN_C - 1) / XV_ATTN_C) * ntile;
+        XV_REQUIRE(items <= (1LL << 30), XV_ERR_SHAPE);
+    }
     XV_REQUIRE(scale == scale, XV_ERR_SHAPE);
     if (B == 0) return XV_OK;
     XV_REQUIRE(q && k_new && v_new && k_cache && v_cache && kv_len && o && workspace, XV_ERR_NULL);

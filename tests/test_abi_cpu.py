@@ -94,7 +94,7 @@ def test_attn_argument_errors(xv):
 
     assert call(B=0) == 0
     assert call(T=17) == -2 and call(Hq=25) == -2 and call(d=96) == -2 and call(Lmax=8) == -2
-    assert call(T=16, Hq=64, Hkv=4) == -2                       # 16 heads per group x 16 rows > 128
+    assert call(B=1 << 13, T=16, Hq=64, Hkv=64, Lmax=1 << 20) == -2   # grid past 2^30 workgroups
     assert call(scale=float("nan")) == -2
     assert call(q=None) == -1 and call(kvl=None) == -1 and call(ws=None) == -1
     assert call(q=MIS) == -3

@@ -79,6 +79,7 @@ CASES = [
     (3, 16, 8, 1, 64, [0, 1, 247]),         # empty cache, 1 position, 128 pairs per group
     (1, 1, 24, 4, 256, [511]),              # decode shape
     (2, 4, 12, 3, 256, [1000, 31]),
+    (1, 16, 16, 1, 128, [300]),             # 256 pairs per group (16 tiles)
 ]
 
 
@@ -134,6 +135,25 @@ def test_attn_capacity_and_workspace_invariance():
     for extra, wsx in ((0, 4096), (300, 0), (4096 * 8, 1 << 20)):
         o2, o322, _, _ = _verify(D, Lmax_extra=extra, ws_extra=wsx)
         assert same_bits(o32, o322) and same_bits(o, o2), (extra, wsx)
+
+
+@pytest.mark.parametrize("case", [(1, 9, 24, 4, 256, [640]), (2, 16, 8, 1, 64, [0, 700]),
+                                  (1, 5, 6, 2, 128, [257]), (3, 1, 24, 4, 256, [5, 300, 1000])],
+                         ids=lambda c: str(c))
+def test_attn_wide_and_tile_kernels_agree(case):
+    """The tile kernel (few (chunk, KV head, request) workgroups) and the wide kernel (at least
+    128 of them) form the same numbers: the same rows at a small and at a large capacity."""
+    B, T, Hq, Hkv, d, L0 = case
+    C = _xv().xv_attn_chunk_tokens()
+    Lmax = max(L0) + T
+    assert B * Hkv * -(-Lmax // C) < 128                     # small capacity: tile kernel
+    D = Dev(*_case(123 + sum(L0), B, T, Hq, Hkv, d, L0, Lmax))
+    o, o32, kc, vc = _verify(D)
+    extra = -(-128 // (B * Hkv)) * C - Lmax                  # large capacity: wide kernel
+    o2, o322, kc2, vc2 = _verify(D, Lmax_extra=extra)
+    torch.cuda.synchronize()
+    assert same_bits(o32, o322) and same_bits(o, o2)
+    assert same_bits(kc, kc2[:, :, :Lmax]) and same_bits(vc, vc2[:, :, :Lmax])
 
 
 def test_attn_batch_invariance():
