@@ -107,6 +107,8 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     __shared__ __attribute__((aligned(16))) uint16_t skq[XV_GDN_TMAX][2][DK];
     __shared__ uint16_t sv[XV_GDN_TMAX][XV_GDN_JW];
     __shared__ float sab[XV_GDN_TMAX][2];
+    constexpr int SP = XV_GDN_JW + 1;        // state slab row pitch (floats)
+    __shared__ float sst[DK * SP];           // the workgroup's state slab [i][32 values]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -127,31 +129,69 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         if (n == T) return;                  // state_out already holds S_T
     }
 
-    const size_t sbase = ((size_t)(b * Hv + h) * DK + ig * R) * dv + j;
-    float s[R];
+    // the state slab S[i][j0 .. j0 + 32) moves through LDS so that global reads and
+    // writes are 16-byte, 8 threads per 128-byte row
+    constexpr int SROWS = 256 / 8;           // slab rows per pass
+    constexpr int SPASS = DK / SROWS;
+    const size_t slab = (size_t)(b * Hv + h) * DK * dv + blockIdx.x * XV_GDN_JW + (tid & 7) * 4;
+    xv_f32x4 sl[SPASS];
 #pragma unroll
-    for (int r = 0; r < R; ++r) s[r] = S_in[sbase + (size_t)r * dv];
+    for (int e = 0; e < SPASS; ++e)
+        sl[e] = *reinterpret_cast<const xv_f32x4*>(S_in + slab + (size_t)(tid / 8 + e * SROWS) * dv);
 
-    // stage the rows of tokens 0..n-1
+    // stage the rows of tokens 0..n-1: every load is issued before any LDS store
+    // (straight-line, clamped to token 0), so the staging costs one round trip
     constexpr int CH = DK / 8;               // 16-byte chunks per k or q row
-    for (int idx = tid; idx < n * 2 * CH; idx += 256) {
-        const int t = idx / (2 * CH), rem = idx % (2 * CH);
-        const int which = rem / CH, c = rem % CH;      // 0: k, 1: q
-        const size_t row = ((size_t)b * T + t) * Hk + g;
-        const uint16_t* src = (which == 0 ? k : q) + row * DK + c * 8;
-        xv_u32x4 val = {0u, 0u, 0u, 0u};
-        if (which == 0 || !ROLLBACK) val = xv_load16(src);
-        *reinterpret_cast<xv_u32x4*>(&skq[t][which][c * 8]) = val;
+    constexpr int KQ_PER = (XV_GDN_TMAX * 2 * CH + 255) / 256;
+    constexpr int V_PER = (XV_GDN_TMAX * XV_GDN_JW + 255) / 256;
+    if (n > 0) {                             // uniform
+        xv_u32x4 kq[KQ_PER];
+        uint16_t vv[V_PER];
+        float abv = 0.f;
+#pragma unroll
+        for (int e = 0; e < KQ_PER; ++e) {
+            int idx = tid + e * 256;
+            idx = idx < n * 2 * CH ? idx : 0;
+            const int t = idx / (2 * CH), rem = idx % (2 * CH);
+            const int which = rem / CH, c = rem % CH;   // 0: k, 1: q
+            const size_t row = ((size_t)b * T + t) * Hk + g;
+            const uint16_t* src = (which == 0 || ROLLBACK ? k : q) + row * DK + c * 8;
+            kq[e] = xv_load16(src);
+        }
+#pragma unroll
+        for (int e = 0; e < V_PER; ++e) {
+            int idx = tid + e * 256;
+            idx = idx < n * XV_GDN_JW ? idx : 0;
+            const int t = idx / XV_GDN_JW, c = idx % XV_GDN_JW;
+            vv[e] = v[(((size_t)b * T + t) * Hv + h) * dv + blockIdx.x * XV_GDN_JW + c];
+        }
+        {
+            const int idx = tid < 2 * n ? tid : 0;
+            abv = ((idx & 1) ? beta : a)[((size_t)b * T + (idx >> 1)) * Hv + h];
+        }
+#pragma unroll
+        for (int e = 0; e < KQ_PER; ++e) {
+            const int idx = tid + e * 256;
+            if (idx < n * 2 * CH) {
+                const int t = idx / (2 * CH), rem = idx % (2 * CH);
+                *reinterpret_cast<xv_u32x4*>(&skq[t][rem / CH][(rem % CH) * 8]) = kq[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < V_PER; ++e) {
+            const int idx = tid + e * 256;
+            if (idx < n * XV_GDN_JW) sv[idx / XV_GDN_JW][idx % XV_GDN_JW] = vv[e];
+        }
+        if (tid < 2 * n) sab[tid >> 1][tid & 1] = abv;
     }
-    for (int idx = tid; idx < n * XV_GDN_JW; idx += 256) {
-        const int t = idx / XV_GDN_JW, c = idx % XV_GDN_JW;
-        sv[t][c] = v[(((size_t)b * T + t) * Hv + h) * dv + blockIdx.x * XV_GDN_JW + c];
-    }
-    if (tid < 2 * n) {
-        const int t = tid >> 1;
-        sab[t][tid & 1] = ((tid & 1) ? beta : a)[((size_t)b * T + t) * Hv + h];
-    }
+#pragma unroll
+    for (int e = 0; e < SPASS; ++e)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sst[(tid / 8 + e * SROWS) * SP + (tid & 7) * 4 + c] = sl[e][c];
     __syncthreads();
+    float s[R];                              // this lane's part of its column, for the whole call
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = sst[(ig * R + r) * SP + jw];
 
     float kk[R], qq[R];
     if (n > 0) {
@@ -181,7 +221,15 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
 
 #pragma unroll
-    for (int r = 0; r < R; ++r) S_out[sbase + (size_t)r * dv] = s[r];
+    for (int r = 0; r < R; ++r) sst[(ig * R + r) * SP + jw] = s[r];   // the lane's own slots
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < SPASS; ++e) {
+        xv_f32x4 out;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) out[c] = sst[(tid / 8 + e * SROWS) * SP + (tid & 7) * 4 + c];
+        *reinterpret_cast<xv_f32x4*>(S_out + slab + (size_t)(tid / 8 + e * SROWS) * dv) = out;
+    }
 }
 
 int xv_gdn_check(const void* k, const void* v, const void* a, const void* b,
@@ -193,7 +241,7 @@ int xv_gdn_check(const void* k, const void* v, const void* a, const void* b,
     if (B == 0) return XV_OK;
     XV_REQUIRE(k && v && a && b && sin && sout, XV_ERR_NULL);
     XV_REQUIRE(xv_aligned16(k) && xv_aligned(v, 2) && xv_aligned(a, 4) && xv_aligned(b, 4) &&
-               xv_aligned(sin, 4) && xv_aligned(sout, 4), XV_ERR_ALIGN);
+               xv_aligned16(sin) && xv_aligned16(sout), XV_ERR_ALIGN);
     XV_REQUIRE(sin != sout, XV_ERR_ALIAS);
     return XV_OK;
 }

@@ -90,8 +90,8 @@ int xv_gemm_small_m(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y3
  *   q, k      : bf16 [B][T][Hk][dk]    [16B] (L2-normalised by the caller)
  *   v         : bf16 [B][T][Hv][dv]
  *   a, b      : fp32 [B][T][Hv]        decay and beta, already activated
- *   state_in  : fp32 [B][Hv][dk][dv]   S_0, element (value j, key i) at [i][j]; read only
- *   state_out : fp32 [B][Hv][dk][dv]   S_T; must not be state_in (XV_ERR_ALIAS)
+ *   state_in  : fp32 [B][Hv][dk][dv]   [16B] S_0, element (value j, key i) at [i][j]; read only
+ *   state_out : fp32 [B][Hv][dk][dv]   [16B] S_T; must not be state_in (XV_ERR_ALIAS)
  *   o         : bf16 [B][T][Hv][dv]    outputs o_t rounded to nearest even
  *   o32       : fp32 [B][T][Hv][dv] or NULL
  * Shapes: B >= 0, 1 <= T <= 16, Hk >= 1, Hv % Hk == 0, dk in {64, 128},
@@ -149,7 +149,7 @@ int    xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, const uint1
  *                 with the per-token arithmetic of xv_gdn_verify
  *   kv_len[b]  <- kv_len[b] + n
  * The argument arrays are those of the xv_gdn_verify call being rolled back
- * (q is not needed; k is [16B]).
+ * (q is not needed; k, state_in and state_out are [16B]).
  *   state_out : in S_T, out S_n; must not be state_in
  *   kv_len    : int32 [B] device, updated in place
  *   n_keep    : int32 [B] device; values outside [0, T] are clamped

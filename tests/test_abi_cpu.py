@@ -78,6 +78,7 @@ def test_gdn_argument_errors(xv):
     assert call(Hv=47) == -2 and call(dk=96) == -2 and call(dv=16) == -2 and call(dv=160) == -2
     assert call(q=None) == -1 and call(si=None) == -1 and call(o=None) == -1
     assert call(k=MIS) == -3 and call(q=MIS) == -3 and call(o32=A + 2) == -3 and call(a=ODD) == -3
+    assert call(si=MIS) == -3 and call(so=A + 0x100004) == -3   # states are read 16 bytes at a time
     assert call(so=A) == -6                                     # state_out aliases state_in
     r = xv.lib().xv_rollback_to_prefix
     assert r(A, A, A, A, A, A + 0x1000, None, A, 1, 9, 16, 48, 128, 128, None) == -1
