@@ -59,14 +59,16 @@ __device__ __forceinline__ int xv_vt_granule(int d, int c) {
 // row, one before L0 the cache, one past L0 + T re-reads cache position 0 (never
 // used, zeroed before it reaches LDS).  The new rows are appended to the cache
 // after the loads.
-template <int D, int NT>
+template <int D, int NT, int DS = 1>
 struct XvChunk {
     static constexpr int C = XV_ATTN_C;
+    static constexpr int DV = D / DS;                  // value dims this workgroup stages
     static constexpr int KG = C * (D / 8) / NT;        // K granules per thread
-    static constexpr int VTILES = (C / 8) * (D / 8);   // 8 x 8 V tiles per chunk
+    static constexpr int VTILES = (C / 8) * (DV / 8);  // 8 x 8 V tiles per chunk
     static constexpr int VT = (VTILES + NT - 1) / NT;  // V tiles per thread (last may be partial)
     xv_u32x4 kreg[KG];
     xv_u32x4 vreg[VT][8];
+    int dg0 = 0;                                       // first 8-dim value group staged
 
     __device__ __forceinline__ void load(const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
                                          const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
@@ -84,31 +86,33 @@ struct XvChunk {
 #pragma unroll
         for (int i = 0; i < VT; ++i) {
             const int vt = (tid + i * NT) < VTILES ? tid + i * NT : VTILES - 1;
-            const int pg = vt / (D / 8), dg = vt % (D / 8);
+            const int pg = vt / (DV / 8), dg = dg0 + vt % (DV / 8);
 #pragma unroll
             for (int e = 0; e < 8; ++e) vreg[i][e] = xv_load16(src(v_cache, v_new, c0 + pg * 8 + e) + dg * 8);
         }
     }
-    // zero the positions past L0 + T; append the new rows when `append`
+    // zero the positions past L0 + T; append the new K rows (append_k) and the staged
+    // dims of the new V rows (append_v)
     __device__ __forceinline__ void settle(uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
-                                           size_t kvbase, int L0, int Lend, int c0, int tid, bool append) {
+                                           size_t kvbase, int L0, int Lend, int c0, int tid,
+                                           bool append_k, bool append_v) {
         const xv_u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < KG; ++i) {
             const int idx = tid + i * NT;
             const int pos = c0 + idx / (D / 8);
             if (pos >= Lend) kreg[i] = zero;
-            else if (append && pos >= L0) xv_store16(k_cache + (kvbase + pos) * D + (idx % (D / 8)) * 8, kreg[i]);
+            else if (append_k && pos >= L0) xv_store16(k_cache + (kvbase + pos) * D + (idx % (D / 8)) * 8, kreg[i]);
         }
 #pragma unroll
         for (int i = 0; i < VT; ++i) {
             const int vt = tid + i * NT;
-            const int pg = vt / (D / 8), dg = vt % (D / 8);
+            const int pg = vt / (DV / 8), dg = dg0 + vt % (DV / 8);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int pos = c0 + pg * 8 + e;
                 if (pos >= Lend || vt >= VTILES) vreg[i][e] = zero;
-                else if (append && pos >= L0) xv_store16(v_cache + (kvbase + pos) * D + dg * 8, vreg[i][e]);
+                else if (append_v && pos >= L0) xv_store16(v_cache + (kvbase + pos) * D + dg * 8, vreg[i][e]);
             }
         }
     }
@@ -119,13 +123,13 @@ struct XvChunk {
             lds[xv_k_granule<D>(idx / (D / 8), idx % (D / 8))] = kreg[i];
         }
     }
-    // V^T into LDS through 8 x 8 register transposes
+    // V^T of the staged dims into LDS (rows d - 8*dg0) through 8 x 8 register transposes
     __device__ __forceinline__ void vt_to_lds(xv_u32x4* lds, int tid) const {
 #pragma unroll
         for (int i = 0; i < VT; ++i) {
             const int vt = tid + i * NT;
             if (vt < VTILES) {
-                const int pg = vt / (D / 8), dg = vt % (D / 8);
+                const int pg = vt / (DV / 8), dg = vt % (DV / 8);
 #pragma unroll
                 for (int dd = 0; dd < 8; ++dd) {
                     xv_u32x4 outv;
@@ -235,7 +239,7 @@ void xv_attn_partial_wide_kernel(const uint16_t* __restrict__ q, const uint16_t*
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = pair_ok ? qf[ks] : zero;
     }
-    ch.settle(k_cache, v_cache, kvbase, L0, Lend, c0, tid, true);
+    ch.settle(k_cache, v_cache, kvbase, L0, Lend, c0, tid, true, true);
 
     // ---- K into LDS; scores S^T[pos][pair] for the whole chunk ----
     ch.k_to_lds(lds, tid);
@@ -313,11 +317,13 @@ void xv_attn_partial_wide_kernel(const uint16_t* __restrict__ q, const uint16_t*
 }
 
 // Few workgroups (small batch, short context): one workgroup per (request, KV
-// head, chunk, 16-pair tile), so that the chunk's work is spread over more CUs.
-// The waves split the tile's score blocks, the probabilities go through LDS, and
-// each wave forms the output dims of its slice.  Every chain and ordered sum is
-// the one the wide kernel forms, so the two give the same bits.
-template <int D>
+// head, chunk, 16-pair tile, 1/DS of the value dims), so that the chunk's work is
+// spread over more CUs.  The tile's queries are staged once in LDS; the waves
+// split the tile's score blocks (every d-part workgroup forms all scores), the
+// probabilities go through LDS, and each wave forms the output dims of its
+// slice.  Every chain and ordered sum is the one the wide kernel forms, so the
+// two give the same bits.
+template <int D, int DS>
 __global__ __launch_bounds__(XV_ATTN_WAVES * 64)
 void xv_attn_partial_tile_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
                                  const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_cache,
@@ -331,22 +337,27 @@ void xv_attn_partial_tile_kernel(const uint16_t* __restrict__ q, const uint16_t*
     constexpr int NT = NW * 64;
     constexpr int KS = D / 32;
     constexpr int DB = D / 16;
+    constexpr int DBP = DB / DS;                // output blocks of this d-part
     constexpr int NCB = C / 16;
     constexpr int CBW = NCB / NW;               // score blocks per wave
-    constexpr int DBW = DB >= NW ? DB / NW : 1; // output blocks per wave (waves past DB idle)
+    constexpr int DBW = DBP >= NW ? DBP / NW : 1; // output blocks per wave (waves past DBP idle)
     constexpr int PP = C + 4;                   // probability row pitch (floats)
-    static_assert(NCB % NW == 0, "score blocks must split evenly over the waves");
+    constexpr int QP = D + 8;                   // query row pitch in LDS (bf16)
+    constexpr int QG = (16 * (D / 8) + NT - 1) / NT;   // query granules per thread
+    static_assert(NCB % NW == 0 && DB % DS == 0, "work must split evenly");
     __shared__ __attribute__((aligned(16))) xv_u32x4 lds[C * D / 8];
     __shared__ __attribute__((aligned(16))) float sp[16 * PP];
+    __shared__ __attribute__((aligned(16))) uint16_t sq[16 * QP];
     __shared__ float smax[NW][16];
 
-    // work item: consecutive items (the tiles of one chunk first) share an XCD's L2
+    // work item: consecutive items (the tiles and d-parts of one chunk) share an XCD's L2
     const int u = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
     if (u >= items) return;
-    const int tile = u % NTILE;
-    const int c = (u / NTILE) % NC;
-    const int g = (u / (NTILE * NC)) % Hkv;
-    const int b = u / (NTILE * NC * Hkv);
+    const int dpart = u % DS;
+    const int tile = (u / DS) % NTILE;
+    const int c = (u / (DS * NTILE)) % NC;
+    const int g = (u / (DS * NTILE * NC)) % Hkv;
+    const int b = u / (DS * NTILE * NC * Hkv);
     const int Hg = Hq / Hkv;
     const int P = Hg * T;
     int L0 = kv_len[b];
@@ -368,21 +379,34 @@ void xv_attn_partial_tile_kernel(const uint16_t* __restrict__ q, const uint16_t*
     const size_t kvbase = ((size_t)b * Hkv + g) * Lmax;
     const xv_u32x4 zero = {0u, 0u, 0u, 0u};
 
-    XvChunk<D, NT> ch;
+    XvChunk<D, NT, DS> ch;
+    ch.dg0 = dpart * (D / 8 / DS);
     ch.load(k_cache, v_cache, k_new, v_new, kvbase, ((size_t)b * T * Hkv + g) * D, Hkv * D, L0, Lend, c0, tid);
-    xv_u32x4 qf[KS];
-    {
-        const uint16_t* qp = q + (((size_t)b * T + pr) * Hq + ph) * D + lg * 8;
+    xv_u32x4 qreg[QG];                          // the tile's 16 query rows, one granule each
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = xv_load16(qp + ks * 32);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = pair_ok ? qf[ks] : zero;
+    for (int i = 0; i < QG; ++i) {
+        int e = tid + i * NT;
+        e = e < 16 * (D / 8) ? e : 0;
+        const int p2 = tile * 16 + e / (D / 8);
+        const int p2c = p2 < P ? p2 : 0;
+        qreg[i] = xv_load16(q + (((size_t)b * T + p2c / Hg) * Hq + g * Hg + p2c % Hg) * D + (e % (D / 8)) * 8);
     }
-    ch.settle(k_cache, v_cache, kvbase, L0, Lend, c0, tid, tile == 0);   // tile 0 appends
+    ch.settle(k_cache, v_cache, kvbase, L0, Lend, c0, tid, tile == 0 && dpart == 0, tile == 0);
+#pragma unroll
+    for (int i = 0; i < QG; ++i) {
+        const int e = tid + i * NT;
+        if (e < 16 * (D / 8)) {
+            const int p2 = tile * 16 + e / (D / 8);
+            *reinterpret_cast<xv_u32x4*>(sq + (e / (D / 8)) * QP + (e % (D / 8)) * 8) = p2 < P ? qreg[i] : zero;
+        }
+    }
 
     // ---- K into LDS; this wave's score blocks S^T[pos][pair] ----
     ch.k_to_lds(lds, tid);
     __syncthreads();
+    xv_u32x4 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const xv_u32x4*>(sq + lr * QP + ks * 32 + lg * 8);
     const int cb0 = wave * CBW;
     xv_f32x4 sc[CBW];
 #pragma unroll
@@ -424,8 +448,8 @@ void xv_attn_partial_tile_kernel(const uint16_t* __restrict__ q, const uint16_t*
     ch.vt_to_lds(lds, tid);
     __syncthreads();
 
-    // ---- chunk sum l (wave 0), in the wide kernel's order ----
-    if (wave == 0) {
+    // ---- chunk sum l (wave 0 of d-part 0), in the wide kernel's order ----
+    if (wave == 0 && dpart == 0) {
         float l = 0.f;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
@@ -443,8 +467,8 @@ void xv_attn_partial_tile_kernel(const uint16_t* __restrict__ q, const uint16_t*
     }
 
     // ---- acc = P V for this wave's output blocks ----
-    const int db0 = wave * DBW;
-    if (db0 >= DB) return;                      // uniform per wave; no barrier follows
+    const int dbl0 = wave * DBW;                // first block, local to the d-part
+    if (dbl0 >= DBP) return;                    // uniform per wave; no barrier follows
     xv_f32x4 oacc[DBW];
 #pragma unroll
     for (int j = 0; j < DBW; ++j) oacc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
@@ -455,13 +479,13 @@ void xv_attn_partial_tile_kernel(const uint16_t* __restrict__ q, const uint16_t*
                    *reinterpret_cast<const xv_f32x4*>(sp + lr * PP + kk * 32 + 16 + 4 * lg), phi, plo);
         xv_u32x4 vf[DBW];
 #pragma unroll
-        for (int j = 0; j < DBW; ++j) vf[j] = xv_vt_frag(lds, db0 + j, kk, lr, lg);
+        for (int j = 0; j < DBW; ++j) vf[j] = xv_vt_frag(lds, dbl0 + j, kk, lr, lg);
 #pragma unroll
         for (int j = 0; j < DBW; ++j) oacc[j] = xv_mfma16x16x32(phi, vf[j], oacc[j]);
 #pragma unroll
         for (int j = 0; j < DBW; ++j) oacc[j] = xv_mfma16x16x32(plo, vf[j], oacc[j]);
     }
-    xv_store_acc<D, DBW>(ws_acc, oacc, db0, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
+    xv_store_acc<D, DBW>(ws_acc, oacc, dpart * DBP + dbl0, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
 }
 
 template <int D>
@@ -533,10 +557,11 @@ int xv_attn_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_n
                            q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
                            T, Hq, Hkv, Lmax, NC, scale_log2);
     } else {
+        constexpr int DS = D == 256 ? 2 : 1;    // value-dim parts per tile
         const int ntile = (P + 15) / 16;
-        const int items = B * Hkv * NC * ntile;
+        const int items = B * Hkv * NC * ntile * DS;
         const int per_xcd = (items + 7) / 8;
-        hipLaunchKernelGGL(xv_attn_partial_tile_kernel<D>, dim3(8 * per_xcd), dim3(XV_ATTN_WAVES * 64), 0, st,
+        hipLaunchKernelGGL((xv_attn_partial_tile_kernel<D, DS>), dim3(8 * per_xcd), dim3(XV_ATTN_WAVES * 64), 0, st,
                            q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
                            T, Hq, Hkv, Lmax, NC, ntile, items, per_xcd, scale_log2);
     }
@@ -574,9 +599,9 @@ extern "C" int xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, con
     XV_REQUIRE(B >= 0 && T >= 1 && T <= 16 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, XV_ERR_SHAPE);
     XV_REQUIRE(d == 64 || d == 128 || d == 256, XV_ERR_SHAPE);
     XV_REQUIRE(Lmax >= T && (Lmax + XV_ATTN_C - 1) / XV_ATTN_C <= XV_ATTN_MAX_NC, XV_ERR_SHAPE);
-    {   // partial-kernel workgroups (one per request, KV head, chunk, 16 pairs) must fit the grid
+    {   // partial-kernel workgroups (per request, KV head, chunk, 16 pairs, value-dim part) fit the grid
         const long long ntile = ((long long)(Hq / Hkv) * T + 15) / 16;
-        const long long items = (long long)B * Hkv * ((Lmax + XV_ATTN_C - 1) / XV_ATTN_C) * ntile;
+        const long long items = (long long)B * Hkv * ((Lmax + XV_ATTN_C - 1) / XV_ATTN_C) * ntile * 2;
         XV_REQUIRE(items <= (1LL << 30), XV_ERR_SHAPE);
     }
     XV_REQUIRE(scale == scale, XV_ERR_SHAPE);

@@ -124,7 +124,7 @@ int xv_gdn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *   o32      : fp32 [B][T][Hq][d] or NULL
  *   workspace: [16B] device scratch of workspace_bytes >= xv_attn_workspace_bytes(B,T,Hq,d,Lmax)
  * Shapes: B >= 0, 1 <= T <= 16, Hq % Hkv == 0, d in {64, 128, 256}, Lmax >= T,
- * B * Hkv * ceil(Lmax / chunk) * ceil((Hq/Hkv) * T / 16) <= 2^30 (the grid;
+ * B * Hkv * ceil(Lmax / chunk) * ceil((Hq/Hkv) * T / 16) <= 2^29 (the grid;
  * XV_ERR_SHAPE otherwise).  Device precondition: 0 <= L0 and
  * L0 + T <= Lmax (kernels clamp positions to the buffer otherwise).
  * Cache positions >= L0 + T are never read, so they may hold anything.
