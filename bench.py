@@ -77,42 +77,27 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline time budget")
     ap.add_argument("--breakdown", action="store_true", help="per-kernel event timing pass")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the medium / batch-8 / long workloads reported beside the headline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py: this build runs on one GPU; --gpus %d is not supported (use --gpus 1)" % args.gpus,
-              file=sys.stderr)
-        sys.exit(2)
-    import numpy as np
+def build_layers(wl, Lmax, R, stream):
+    """Inputs for workload wl, R resident layer replicas, and the bit-exact gate
+    (verify == sequential decode on the same buffers, every output bit)."""
     import torch
     from bit_exact_speculative_amd import inputs as gen
     from bit_exact_speculative_amd.layer import Layer
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    wl = gen.WORKLOADS[args.workload]
-    R = max(1, args.replicas)
-    total = args.warmup + args.steps
-    per_replica = (total + R - 1) // R + 2
-    L0max = wl.L0 if wl.L0 is not None else wl.L0_range[1]
-    Lmax = L0max + wl.T * (per_replica + 2)
     t0 = time.time()
     inp = gen.make_inputs(wl, Lmax=Lmax, pad_value=0)
     print("# inputs generated in %.1f s (workload %s, Lmax %d)" % (time.time() - t0, wl.name, Lmax),
           file=sys.stderr, flush=True)
-
-    stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         base = Layer(inp, "cuda")                 # prefix state computed by the GPU path
         base.proj_fp32 = False                    # projections: bf16 outputs only
         base.out_fp32 = False                     # GDN / attention: bf16 outputs only
-        # bit-exact gate: verify == sequential decode on these buffers
         gate = base.clone()
         gate.proj_fp32 = True
         gate.verify(rollback=False)
@@ -120,16 +105,25 @@ def main():
         torch.cuda.synchronize()
         same = lambda a, b: torch.equal(a.contiguous().view(torch.int16 if a.element_size() == 2 else torch.int32),
                                         b.contiguous().view(torch.int16 if b.element_size() == 2 else torch.int32))
-        n = wl.N1
         exact = (same(gate.o_gdn, dec["o_gdn"]) and same(gate.S_out, dec["S"][-1]) and
                  same(gate.o_attn, dec["o_attn"]) and same(gate.Kc, dec["Kc"]) and
-                 same(gate.y1.view(wl.B, wl.T, n), dec["y1"]) and
+                 same(gate.y1.view(wl.B, wl.T, wl.N1), dec["y1"]) and
                  same(gate.y2_32.view(wl.B, wl.T, wl.N2), dec["y2_32"]) and
                  torch.equal(gate.ids, dec["ids"]))
         del gate, dec
         layers = [base] + [base.clone() for _ in range(R - 1)]
         torch.cuda.synchronize()
     print("# %d layer replicas resident; verify==decode bit-exact: %s" % (R, exact), file=sys.stderr, flush=True)
+    return inp, layers, bool(exact)
+
+
+def run_steps(layers, stream, steps, warmup, keep_all=False, gemm_events=False):
+    """Warmup, then `steps` timed steps rotating over the replicas, bracketed by HIP events
+    on the layers' stream.  keep_all: every request keeps all T rows (full acceptance);
+    otherwise the greedy acceptance decides.  Returns (ms per step, per-step N2 GEMM us, wall s)."""
+    import torch
+    R = len(layers)
+    full = torch.full((layers[0].B,), layers[0].T, dtype=torch.int32, device="cuda") if keep_all else None
 
     def step(L, ev=None):
         L.gemm1()
@@ -141,28 +135,77 @@ def main():
         L.gdn()
         L.attn()
         L.head()
-        L.rollback()
+        L.rollback(full)
         L.advance()
 
     with torch.cuda.stream(stream):
-        for s in range(args.warmup):
+        for s in range(warmup):
             step(layers[s % R])
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+               for _ in range(steps)] if gemm_events else [None] * steps
         e_start = torch.cuda.Event(enable_timing=True)
         e_end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         e_start.record(stream)
-        for s in range(args.steps):
-            step(layers[(args.warmup + s) % R], evs[s])
+        for s in range(steps):
+            step(layers[(warmup + s) % R], evs[s])
         e_end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
-    ms_total = e_start.elapsed_time(e_end)
-    ms_per_step = ms_total / args.steps
-    gemm_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    ms = e_start.elapsed_time(e_end) / steps
+    gemm_us = [a.elapsed_time(b) * 1e3 for a, b in evs] if gemm_events else []
+    return ms, gemm_us, wall
+
+
+def lmax_for(wl, steps_per_replica_n1, steps_per_replica_full):
+    """Cache capacity for a run: one kept row per greedy step, T per full-acceptance step."""
+    L0max = wl.L0 if wl.L0 is not None else wl.L0_range[1]
+    return L0max + max(wl.T * (steps_per_replica_n1 + 4), wl.T * (steps_per_replica_full + 4))
+
+
+def extra_workload(name, stream, steps, warmup, R):
+    """Verified draft tok/s of another workload (bit-exact gate included)."""
+    import torch
+    from bit_exact_speculative_amd import inputs as gen
+    wl = gen.WORKLOADS[name]
+    per = (steps + warmup + R - 1) // R
+    _, layers, exact = build_layers(wl, lmax_for(wl, per, 0), R, stream)
+    ms, _, _ = run_steps(layers, stream, steps, warmup)
+    ctx = wl.L0 if wl.L0 is not None else "%d-%d" % wl.L0_range
+    res = {"ctx": ctx, "batch": wl.B, "tok_s": round(wl.B * wl.k_drafts / (ms * 1e-3), 1) if exact else None,
+           "ms_per_step": round(ms, 5), "bit_exact_verify_equals_decode": exact, "steps": steps,
+           "layer_replicas": R}
+    del layers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU; --gpus %d is not supported (use --gpus 1)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from bit_exact_speculative_amd import inputs as gen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = gen.WORKLOADS[args.workload]
+    R = max(1, args.replicas)
+    full_steps, full_warmup = max(args.steps // 2, 1), max(args.warmup // 2, 1)
+    Lmax = lmax_for(wl, (args.warmup + args.steps + R - 1) // R, (full_warmup + full_steps + R - 1) // R)
+    stream = torch.cuda.Stream()
+    inp, layers, exact = build_layers(wl, Lmax, R, stream)
+
+    # headline: greedy acceptance on the synthetic head (mostly the root row kept, so the
+    # rollback recomputes the state), live HIP events around the dominant GEMM
+    ms_per_step, gemm_us, wall = run_steps(layers, stream, args.steps, args.warmup, gemm_events=True)
     gemm_avg_us = float(np.mean(gemm_us))
     n_keep = [int(L.n_keep.sum().item()) for L in layers]
 
@@ -186,12 +229,30 @@ def main():
                     acc[k].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
         breakdown = {k: round(float(np.median(v)), 2) for k, v in acc.items()}
 
+    # the same workload with every draft accepted (rollback keeps S_T as is)
+    for L in layers:
+        L.reset()
+    ms_full, _, _ = run_steps(layers, stream, full_steps, full_warmup, keep_all=True)
+
     if args.calib_copy_mib > 0:
         with torch.cuda.stream(stream):
             src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
             dst = torch.empty_like(src)
             dst.copy_(src)
             torch.cuda.synchronize()
+            del src, dst
+
+    extras = None
+    if not args.no_extras and args.workload == "short":
+        del layers
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        extras = {}
+        for name, steps, warmup, reps in (("medium", 100, 10, 4), ("batch8", 100, 10, 4), ("long", 40, 4, 4)):
+            try:
+                extras[name] = extra_workload(name, stream, steps, warmup, reps)
+            except Exception as exc:                  # reported, never hides the headline line
+                extras[name] = {"error": "%s: %s" % (type(exc).__name__, exc)}
 
     # algorithmic bytes of the dominant kernel (weights + activations in + bf16 out)
     M = wl.M
@@ -227,8 +288,14 @@ def main():
             "verify_rows": wl.T,
             "layer_replicas": R,
             "bit_exact_verify_equals_decode": bool(exact),
-            "rows_kept_per_step": round(float(np.mean(n_keep)) / R, 2) if n_keep else None,
+            "rows_kept_per_step": round(float(np.mean(n_keep)) / wl.B, 2) if n_keep else None,
             "compute": "bf16 x bf16 -> fp32 MFMA GEMMs and attention; fp32 GDN state and VALU",
+        },
+        "full_accept": {
+            "value": round(wl.B * wl.k_drafts / (ms_full * 1e-3), 1) if exact else None,
+            "ms_per_step": round(ms_full, 5),
+            "steps": full_steps,
+            "note": "same workload, every request keeps all %d rows (no state recompute)" % wl.T,
         },
         "roofline": {
             "kernel": "xv_gemm_small_m, LDS-staged variant (M=9, K=5120, N=%d)" % wl.N2,
@@ -244,6 +311,8 @@ def main():
         "cpu_baseline": cpu,
         "wall_s": round(wall, 4),
     }
+    if extras is not None:
+        out["other_workloads"] = extras
     if breakdown is not None:
         out["breakdown_us"] = breakdown
     print(json.dumps(out), flush=True)

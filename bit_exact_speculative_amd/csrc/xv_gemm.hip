@@ -25,6 +25,9 @@
 //    from does not change any arithmetic.
 //  * Up to XV_GEMM_MT_MAX row tiles share one pass over W; rows >= M are zeroed
 //    after their (clamped) load.
+//  * With several row tiles and many column blocks, a K-loop variant instead
+//    gives each wave whole output tiles: it runs the 16 range chains of a tile
+//    one after the other and folds them in range order, the same operations.
 #include "xv_common.h"
 
 namespace {
@@ -236,6 +239,157 @@ void xv_gemm_wlds_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
     }
 }
 
+// Many row tiles (M > 16): there are enough 16 x 16 output tiles to fill the
+// chip without splitting K over waves.  A workgroup of 4 waves owns MT row tiles
+// x NB column blocks (wave v takes column block v % NB and every (4/NB)-th row
+// tile from v / NB) and walks K in ascending k-steps, W and x staged through
+// double-buffered LDS (KC k-steps per stage, the next stage prefetched in
+// registers).  For each of its tiles a wave runs the 16 range chains one after
+// the other: a chain restarts from zero at its range's first k-step, and a
+// finished range is folded into a running sum in range order (sum = p0, then
+// sum + p1, ...).  Those are exactly the operations of the K-split kernels, so
+// every output bit is the same as theirs.
+constexpr int XV_KL_WAVES = 4;
+constexpr int XV_KL_THREADS = XV_KL_WAVES * 64;
+
+template <int MT, int NB, int KC>
+__global__ __launch_bounds__(XV_KL_THREADS)
+void xv_gemm_kloop_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                          uint16_t* __restrict__ y, float* __restrict__ y32,
+                          int M, int N, int K, int mt0)
+{
+    constexpr int NTH = XV_KL_THREADS;
+    constexpr int RW = XV_KL_WAVES / NB;        // waves sharing a column block
+    constexpr int MTW = (MT + RW - 1) / RW;     // row tiles per wave (the last may be past MT)
+    constexpr int PITCH = KC * 32 + 8;          // LDS row pitch (bf16): rows fall 4 banks apart
+    constexpr int WROWS = NB * 16;
+    constexpr int XROWS = MT * 16;
+    constexpr int GR = KC * 4;                  // 16-byte granules per row per stage
+    constexpr int WPT = (WROWS * GR + NTH - 1) / NTH;
+    constexpr int XPT = (XROWS * GR + NTH - 1) / NTH;
+    static_assert(XV_KL_WAVES % NB == 0, "column blocks must divide the waves");
+    __shared__ __attribute__((aligned(16))) uint16_t sw[2][WROWS * PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t sx[2][XROWS * PITCH];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int wcb = wave % NB;                  // the wave's column block within the workgroup
+    const int wt0 = wave / NB;                  // its row tiles: wt0, wt0 + RW, ...
+    const int KS = K >> 5;
+    const int nst = (KS + KC - 1) / KC;
+    const int col0 = blockIdx.x * WROWS;        // first W row (output column) of the workgroup
+    const xv_u32x4 zero = {0u, 0u, 0u, 0u};
+
+    // this thread's granules of a stage: (row, 16-byte column); addresses clamped into the buffers
+    const uint16_t* wsrc[WPT];
+    int wl[WPT];
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+        int g = tid + i * NTH;
+        g = g < WROWS * GR ? g : WROWS * GR - 1;
+        const int r = g / GR, c = g % GR;
+        const int wr = col0 + r < N ? col0 + r : N - 1;
+        wsrc[i] = w + (size_t)wr * K + c * 8;
+        wl[i] = r * PITCH + c * 8;
+    }
+    const uint16_t* xsrc[XPT];
+    int xl[XPT];
+    bool xok[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        int g = tid + i * NTH;
+        g = g < XROWS * GR ? g : XROWS * GR - 1;
+        const int r = g / GR, c = g % GR;
+        const int xr = mt0 * 16 + r;
+        xok[i] = xr < M;
+        xsrc[i] = x + (size_t)(xr < M ? xr : M - 1) * K + c * 8;
+        xl[i] = r * PITCH + c * 8;
+    }
+    xv_u32x4 wreg[WPT], xreg[XPT];
+    auto load = [&](int s) {                    // stage s; columns past K re-read the row's last granule
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int c8 = ((tid + i * NTH) % GR) * 8;
+            wreg[i] = xv_load16(wsrc[i] + (s * (KC * 32) + c8 < K ? s * (KC * 32) : K - 8 - c8));
+        }
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) {
+            const int c8 = ((tid + i * NTH) % GR) * 8;
+            xreg[i] = xv_load16(xsrc[i] + (s * (KC * 32) + c8 < K ? s * (KC * 32) : K - 8 - c8));
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < WPT; ++i)
+            if ((WROWS * GR) % NTH == 0 || tid + i * NTH < WROWS * GR)
+                *reinterpret_cast<xv_u32x4*>(&sw[buf][wl[i]]) = wreg[i];
+#pragma unroll
+        for (int i = 0; i < XPT; ++i)
+            if ((XROWS * GR) % NTH == 0 || tid + i * NTH < XROWS * GR)
+                *reinterpret_cast<xv_u32x4*>(&sx[buf][xl[i]]) = xok[i] ? xreg[i] : zero;
+    };
+
+    xv_f32x4 acc[MTW], sum[MTW];
+#pragma unroll
+    for (int t = 0; t < MTW; ++t) { acc[t] = xv_f32x4{0.f, 0.f, 0.f, 0.f}; sum[t] = acc[t]; }
+    int r = 0;                                  // the range whose chains are running
+    auto fold = [&]() {                         // range r is complete
+#pragma unroll
+        for (int t = 0; t < MTW; ++t) {
+            sum[t] = r == 0 ? acc[t] : sum[t] + acc[t];
+            acc[t] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        ++r;
+    };
+
+    load(0);
+    store(0);
+    load(nst > 1 ? 1 : 0);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        const int buf = s & 1;
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+            const int ks = s * KC + j;
+            while (r < XV_GEMM_WAVES && ((r + 1) * KS) / XV_GEMM_WAVES <= ks) fold();   // uniform
+            if (ks < KS) {
+                const xv_u32x4 bf = *reinterpret_cast<const xv_u32x4*>(&sw[buf][(wcb * 16 + lr) * PITCH + j * 32 + lg * 8]);
+#pragma unroll
+                for (int t = 0; t < MTW; ++t) {
+                    const int tt = wt0 + t * RW < MT ? wt0 + t * RW : MT - 1;   // past MT: computed, not stored
+                    acc[t] = xv_mfma16x16x32(*reinterpret_cast<const xv_u32x4*>(&sx[buf][(tt * 16 + lr) * PITCH + j * 32 + lg * 8]),
+                                             bf, acc[t]);
+                }
+            }
+        }
+        if (s + 1 < nst) {                      // stage s+1 into the other buffer, stage s+2 in flight
+            store(buf ^ 1);
+            load(s + 2 < nst ? s + 2 : s + 1);
+        }
+        __syncthreads();
+    }
+    while (r < XV_GEMM_WAVES) fold();
+
+    const int cb = blockIdx.x * NB + wcb;
+    if (cb >= (N >> 4)) return;
+#pragma unroll
+    for (int t = 0; t < MTW; ++t) {
+        const int tt = wt0 + t * RW;
+        if (tt >= MT) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (mt0 + tt) * 16 + 4 * lg + i;
+            if (row < M) {
+                const size_t o = (size_t)row * N + cb * 16 + lr;
+                y[o] = xv_f32_to_bf16(sum[t][i]);
+                if (y32) y32[o] = sum[t][i];
+            }
+        }
+    }
+}
+
 // x fragments re-read per k-step (many row tiles or long K): U k-steps per stage.
 template <int MT, int U>
 __global__ __launch_bounds__(XV_GEMM_THREADS)
@@ -341,6 +495,20 @@ void xv_gemm_launch_wlds(const uint16_t* x, const uint16_t* w, uint16_t* y, floa
     hipLaunchKernelGGL((xv_gemm_wlds_kernel<KSW, SL, NS>), grid, block, 0, st, x, w, y, y32, M, N, K, mt0);
 }
 
+template <int MT, int KC>
+void xv_gemm_launch_kloop(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
+                          int M, int N, int K, int mt0, hipStream_t st)
+{
+    // column blocks per workgroup: as many as keep at least one workgroup per CU busy
+    // (callers take this path only for N / 16 >= 2 CUs)
+    const int nblk = N / 16, cus = xv_gemm_grid(1 << 30);
+    const dim3 block(XV_KL_THREADS);
+    if (nblk >= 4 * cus)
+        hipLaunchKernelGGL((xv_gemm_kloop_kernel<MT, 4, KC>), dim3((nblk + 3) / 4), block, 0, st, x, w, y, y32, M, N, K, mt0);
+    else
+        hipLaunchKernelGGL((xv_gemm_kloop_kernel<MT, 2, KC>), dim3((nblk + 1) / 2), block, 0, st, x, w, y, y32, M, N, K, mt0);
+}
+
 template <int MT, int U>
 void xv_gemm_launch_xstream(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
                             int M, int N, int K, int mt0, hipStream_t st)
@@ -366,6 +534,16 @@ void xv_gemm_dispatch(int mt, int ksw, const uint16_t* x, const uint16_t* w, uin
         else xv_gemm_launch_xreg<1, 10>(x, w, y, y32, M, N, K, mt0, st);
         return;
     }
+    // several row tiles and many column blocks: walk K per output tile (x reused over 2-4 column blocks)
+    if (mt >= 2 && N / 16 >= 2 * xv_gemm_grid(1 << 30)) {
+        switch (mt) {
+            case 2: xv_gemm_launch_kloop<2, 4>(x, w, y, y32, M, N, K, mt0, st); break;
+            case 3: xv_gemm_launch_kloop<3, 4>(x, w, y, y32, M, N, K, mt0, st); break;
+            case 4: xv_gemm_launch_kloop<4, 4>(x, w, y, y32, M, N, K, mt0, st); break;
+            default: xv_gemm_launch_kloop<5, 4>(x, w, y, y32, M, N, K, mt0, st); break;
+        }
+        return;
+    }
     if (mt == 2 && ksw <= 4) {
         xv_gemm_launch_xreg<2, 4>(x, w, y, y32, M, N, K, mt0, st);
         return;
@@ -375,10 +553,7 @@ void xv_gemm_dispatch(int mt, int ksw, const uint16_t* x, const uint16_t* w, uin
         case 2: xv_gemm_launch_xstream<2, 2>(x, w, y, y32, M, N, K, mt0, st); break;
         case 3: xv_gemm_launch_xstream<3, 1>(x, w, y, y32, M, N, K, mt0, st); break;
         case 4: xv_gemm_launch_xstream<4, 1>(x, w, y, y32, M, N, K, mt0, st); break;
-        case 5: xv_gemm_launch_xstream<5, 1>(x, w, y, y32, M, N, K, mt0, st); break;
-        case 6: xv_gemm_launch_xstream<6, 1>(x, w, y, y32, M, N, K, mt0, st); break;
-        case 7: xv_gemm_launch_xstream<7, 1>(x, w, y, y32, M, N, K, mt0, st); break;
-        default: xv_gemm_launch_xstream<8, 1>(x, w, y, y32, M, N, K, mt0, st); break;
+        default: xv_gemm_launch_xstream<5, 1>(x, w, y, y32, M, N, K, mt0, st); break;
     }
 }
 

@@ -119,3 +119,25 @@ def test_gemm_empty_and_repeat():
     for _ in range(50):
         y, y32 = _gemm_dev(x, w)
         assert torch.equal(y32.view(torch.int32), first32.view(torch.int32))
+
+
+@pytest.mark.parametrize("M,N,K", [(72, 17408, 5120), (72, 10240, 5120), (33, 16384, 1024), (20, 8192, 544)])
+def test_gemm_many_tiles_k_loop_rows_equal_k_split(M, N, K):
+    """Wide N with several row tiles runs the K-loop kernel (whole output tiles per wave, ranges
+    folded in order); every row must equal the same row computed at M <= 16 by the K-split
+    kernels, and sampled columns must match the oracle."""
+    from bit_exact_speculative_amd.layer import dev_bf16
+    rng = np.random.default_rng(M * 7 + N + K)
+    xh = random_bf16(rng, (M, K))
+    wh = random_bf16(rng, (N, K), 0.02)
+    x = dev_bf16(xh, "cuda"); w = dev_bf16(wh, "cuda")
+    y, y32 = _gemm_dev(x, w)
+    for r0 in range(0, M, 9):                              # 9-row slices, as one request's rows
+        r1 = min(M, r0 + 9)
+        ys, ys32 = _gemm_dev(x[r0:r1].contiguous(), w)
+        assert torch.equal(ys32.view(torch.int32), y32[r0:r1].view(torch.int32)), r0
+        assert torch.equal(ys.view(torch.int16), y[r0:r1].view(torch.int16)), r0
+    cols = np.sort(rng.choice(N, size=64, replace=False))
+    ref = oracle.gemm(xh, wh[cols])
+    torch.cuda.synchronize()
+    assert max_rel(y32.cpu().numpy()[:, cols], ref) <= OUT_MAX_REL
