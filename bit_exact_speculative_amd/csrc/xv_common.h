@@ -28,10 +28,10 @@ __device__ __forceinline__ float xv_bf16_hi(uint32_t w) { return __uint_as_float
 
 // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t xv_f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x0040u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rne = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t qnan = (u >> 16) | 0x0040u;               // NaN: keep the sign, make it quiet
+    return (uint16_t)((u & 0x7FFFFFFFu) > 0x7F800000u ? qnan : rne);   // a select, no branch
 }
 
 // Two fp32 values -> packed bf16 pair (low half = a), round to nearest even

@@ -15,25 +15,30 @@
 //     o_j  = sum_i s_i q_i                 (same fixed-order dot)
 // which is S_t = a S_{t-1} (I - b k k^T) + b v k^T, o = S_t q.
 //
-// Work mapping (gfx950, wave64): a workgroup of 4 waves owns 32 value indices
-// of one (request, value head); in a wave, 8 lanes share one j and each holds
-// R = dk/8 consecutive key indices of the column in VGPRs, for the whole call.
+// Work mapping (gfx950, wave64): a workgroup of 8 waves owns 32 value indices
+// of one (request, value head); in a wave, 16 lanes share one j and each holds
+// R = dk/16 consecutive key indices of the column in VGPRs, for the whole call
+// (so the recurrence's dependency chain per token is short, and a batch-1 call
+// still gives every SIMD more than one wave to interleave).
 // The fixed dot order: in each lane four fp32 chains over i mod 4 in ascending
-// i, combined as (c0 + c1) + (c2 + c3); then a butterfly over the 8 lanes
-// (DPP: partner lane^1, then lane^2, then the mirrored half of the group).
-// Every lane ends with the same bits, so all lanes of a column compute the
-// same u.  The state is read once and written once per call, and the rows of
-// all tokens are staged in LDS before the token loop starts.
+// i, combined as (c0 + c1) + (c2 + c3); then a butterfly over the 16 lanes
+// (DPP: partner lane^1, lane^2, the mirrored half of each 8, the mirrored
+// half of the 16).  Every lane ends with the same bits (each step adds the
+// same two values in either order), so all lanes of a column compute the same
+// u.  The state is read once and written once per call; the rows of all
+// tokens are staged in LDS (k and q already widened to fp32) before the token
+// loop starts.
 #include "xv_common.h"
 
 namespace {
 
-constexpr int XV_GDN_JW = 32;       // value indices per workgroup (4 waves x 8)
+constexpr int XV_GDN_JW = 32;       // value indices per workgroup (8 waves x 4)
+constexpr int XV_GDN_LPJ = 16;      // lanes per value index
+constexpr int XV_GDN_THREADS = XV_GDN_JW * XV_GDN_LPJ;
 constexpr int XV_GDN_TMAX = 16;
 
-// Exact lane moves within each group of 8 lanes (DPP): swap with lane^1, lane^2,
-// and mirror the group (lane i <-> 7 - i), which after the first two steps
-// brings in the other half's sum.
+// Exact lane moves within each row of 16 lanes (DPP): swap with lane^1, lane^2,
+// mirror each half-row (lane i <-> 7 - i), mirror the row (lane i <-> 15 - i).
 __device__ __forceinline__ float xv_dpp_xor1(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
@@ -43,9 +48,13 @@ __device__ __forceinline__ float xv_dpp_xor2(float v) {
 __device__ __forceinline__ float xv_dpp_mirror8(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
 }
+__device__ __forceinline__ float xv_dpp_mirror16(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+}
 
 template <int R>
 __device__ __forceinline__ float xv_gdn_dot(const float (&s)[R], const float (&x)[R]) {
+    static_assert(R % 4 == 0, "four chains");
     float c0 = s[0] * x[0];
     float c1 = s[1] * x[1];
     float c2 = s[2] * x[2];
@@ -61,6 +70,7 @@ __device__ __forceinline__ float xv_gdn_dot(const float (&s)[R], const float (&x
     p = p + xv_dpp_xor1(p);
     p = p + xv_dpp_xor2(p);
     p = p + xv_dpp_mirror8(p);
+    p = p + xv_dpp_mirror16(p);
     return p;
 }
 
@@ -76,26 +86,11 @@ __device__ __forceinline__ void xv_gdn_token(float (&s)[R], const float (&kk)[R]
     for (int r = 0; r < R; ++r) s[r] = __builtin_fmaf(u, kk[r], s[r]);
 }
 
-template <int R>
-__device__ __forceinline__ void xv_lds_bf16_row(const uint16_t* p, float (&out)[R]) {
-#pragma unroll
-    for (int c = 0; c < R / 8; ++c) {
-        const xv_u32x4 v = *reinterpret_cast<const xv_u32x4*>(p + c * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            out[c * 8 + 2 * e] = xv_bf16_lo(v[e]);
-            out[c * 8 + 2 * e + 1] = xv_bf16_hi(v[e]);
-        }
-    }
-}
-
 // ROLLBACK = false: verify of T tokens from state_in, writes o (and o32) and S_T.
 // ROLLBACK = true : n = n_keep[b]; n == T leaves state_out; otherwise recomputes
 //                   S_n from state_in; kv_len[b] += n.
-// Every row the workgroup needs (k and q of its key head, its 32 values, a and b)
-// is staged in LDS once; the state column stays in VGPRs for the whole call.
 template <int DK, bool ROLLBACK>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(XV_GDN_THREADS)
 void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const float* __restrict__ a,
                    const float* __restrict__ beta, const float* __restrict__ S_in,
@@ -103,8 +98,9 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    int T, int Hk, int Hv, int dv, int32_t* __restrict__ kv_len,
                    const int32_t* __restrict__ n_keep)
 {
-    constexpr int R = DK / 8;
-    __shared__ __attribute__((aligned(16))) uint16_t skq[XV_GDN_TMAX][2][DK];
+    constexpr int NT = XV_GDN_THREADS;
+    constexpr int R = DK / XV_GDN_LPJ;
+    __shared__ __attribute__((aligned(16))) float skq[XV_GDN_TMAX][2][DK];   // k, q rows, fp32
     __shared__ uint16_t sv[XV_GDN_TMAX][XV_GDN_JW];
     __shared__ float sab[XV_GDN_TMAX][2];
     constexpr int SP = XV_GDN_JW + 1;        // state slab row pitch (floats)
@@ -113,9 +109,9 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int ig = lane & 7;                 // key-index group: i in [ig*R, ig*R + R)
-    const int jl = lane >> 3;
-    const int jw = wave * 8 + jl;            // value index within the workgroup's slice
+    const int ig = lane & 15;                // key-index group: i in [ig*R, ig*R + R)
+    const int jl = lane >> 4;
+    const int jw = wave * 4 + jl;            // value index within the workgroup's slice
     const int j = blockIdx.x * XV_GDN_JW + jw;
     const int h = blockIdx.y;
     const int b = blockIdx.z;
@@ -131,7 +127,7 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
     // the state slab S[i][j0 .. j0 + 32) moves through LDS so that global reads and
     // writes are 16-byte, 8 threads per 128-byte row
-    constexpr int SROWS = 256 / 8;           // slab rows per pass
+    constexpr int SROWS = NT / 8;            // slab rows per pass
     constexpr int SPASS = DK / SROWS;
     const size_t slab = (size_t)(b * Hv + h) * DK * dv + blockIdx.x * XV_GDN_JW + (tid & 7) * 4;
     xv_f32x4 sl[SPASS];
@@ -142,15 +138,15 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // stage the rows of tokens 0..n-1: every load is issued before any LDS store
     // (straight-line, clamped to token 0), so the staging costs one round trip
     constexpr int CH = DK / 8;               // 16-byte chunks per k or q row
-    constexpr int KQ_PER = (XV_GDN_TMAX * 2 * CH + 255) / 256;
-    constexpr int V_PER = (XV_GDN_TMAX * XV_GDN_JW + 255) / 256;
+    constexpr int KQ_PER = (XV_GDN_TMAX * 2 * CH + NT - 1) / NT;
+    constexpr int V_PER = (XV_GDN_TMAX * XV_GDN_JW + NT - 1) / NT;
     if (n > 0) {                             // uniform
         xv_u32x4 kq[KQ_PER];
         uint16_t vv[V_PER];
         float abv = 0.f;
 #pragma unroll
         for (int e = 0; e < KQ_PER; ++e) {
-            int idx = tid + e * 256;
+            int idx = tid + e * NT;
             idx = idx < n * 2 * CH ? idx : 0;
             const int t = idx / (2 * CH), rem = idx % (2 * CH);
             const int which = rem / CH, c = rem % CH;   // 0: k, 1: q
@@ -160,7 +156,7 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
 #pragma unroll
         for (int e = 0; e < V_PER; ++e) {
-            int idx = tid + e * 256;
+            int idx = tid + e * NT;
             idx = idx < n * XV_GDN_JW ? idx : 0;
             const int t = idx / XV_GDN_JW, c = idx % XV_GDN_JW;
             vv[e] = v[(((size_t)b * T + t) * Hv + h) * dv + blockIdx.x * XV_GDN_JW + c];
@@ -171,15 +167,25 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
 #pragma unroll
         for (int e = 0; e < KQ_PER; ++e) {
-            const int idx = tid + e * 256;
+            const int idx = tid + e * NT;
             if (idx < n * 2 * CH) {
                 const int t = idx / (2 * CH), rem = idx % (2 * CH);
-                *reinterpret_cast<xv_u32x4*>(&skq[t][rem / CH][(rem % CH) * 8]) = kq[e];
+                float* dst = &skq[t][rem / CH][(rem % CH) * 8];
+                xv_f32x4 lo4, hi4;
+#pragma unroll
+                for (int w2 = 0; w2 < 2; ++w2) {
+                    lo4[2 * w2] = xv_bf16_lo(kq[e][w2]);
+                    lo4[2 * w2 + 1] = xv_bf16_hi(kq[e][w2]);
+                    hi4[2 * w2] = xv_bf16_lo(kq[e][2 + w2]);
+                    hi4[2 * w2 + 1] = xv_bf16_hi(kq[e][2 + w2]);
+                }
+                *reinterpret_cast<xv_f32x4*>(dst) = lo4;
+                *reinterpret_cast<xv_f32x4*>(dst + 4) = hi4;
             }
         }
 #pragma unroll
         for (int e = 0; e < V_PER; ++e) {
-            const int idx = tid + e * 256;
+            const int idx = tid + e * NT;
             if (idx < n * XV_GDN_JW) sv[idx / XV_GDN_JW][idx % XV_GDN_JW] = vv[e];
         }
         if (tid < 2 * n) sab[tid >> 1][tid & 1] = abv;
@@ -193,22 +199,36 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
     for (int r = 0; r < R; ++r) s[r] = sst[(ig * R + r) * SP + jw];
 
-    float kk[R], qq[R];
+    // Token t's rows are in registers while token t+1's are already being read from LDS.
+    float kc[R], qc[R], kn[R], qn[R];
+    float vj = 0.f, at = 0.f, bt = 0.f, vn = 0.f, an = 0.f, bn = 0.f;
+    auto fetch = [&](int t) {
+#pragma unroll
+        for (int c = 0; c < R / 4; ++c) {
+            const xv_f32x4 k4 = *reinterpret_cast<const xv_f32x4*>(&skq[t][0][ig * R + c * 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kn[c * 4 + e] = k4[e];
+            if (!ROLLBACK) {
+                const xv_f32x4 q4 = *reinterpret_cast<const xv_f32x4*>(&skq[t][1][ig * R + c * 4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qn[c * 4 + e] = q4[e];
+            }
+        }
+        vn = xv_bf16_to_f32(sv[t][jw]);
+        an = sab[t][0];
+        bn = sab[t][1];
+    };
+    auto take = [&]() {
+#pragma unroll
+        for (int r = 0; r < R; ++r) { kc[r] = kn[r]; qc[r] = ROLLBACK ? 0.f : qn[r]; }
+        vj = vn; at = an; bt = bn;
+    };
     if (n > 0) {
-        xv_lds_bf16_row<R>(&skq[0][0][ig * R], kk);
-        if (!ROLLBACK) xv_lds_bf16_row<R>(&skq[0][1][ig * R], qq);
+        fetch(0);
+        take();
     }
     for (int t = 0; t < n; ++t) {
-        const float vj = xv_bf16_to_f32(sv[t][jw]);
-        const float at = sab[t][0];
-        const float bt = sab[t][1];
-        float kc[R], qc[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) { kc[r] = kk[r]; qc[r] = qq[r]; }
-        if (t + 1 < n) {                     // next token's rows, read while this one computes
-            xv_lds_bf16_row<R>(&skq[t + 1][0][ig * R], kk);
-            if (!ROLLBACK) xv_lds_bf16_row<R>(&skq[t + 1][1][ig * R], qq);
-        }
+        if (t + 1 < n) fetch(t + 1);         // uniform
         xv_gdn_token<R>(s, kc, vj, at, bt);
         if (!ROLLBACK) {
             const float ot = xv_gdn_dot<R>(s, qc);
@@ -218,6 +238,7 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                 if (o32) o32[oi] = ot;
             }
         }
+        if (t + 1 < n) take();
     }
 
 #pragma unroll
@@ -252,7 +273,7 @@ int xv_gdn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
                   int B, int T, int Hk, int Hv, int dk, int dv, int32_t* kv_len,
                   const int32_t* n_keep, hipStream_t st)
 {
-    dim3 grid(dv / XV_GDN_JW, Hv, B), block(256);
+    dim3 grid(dv / XV_GDN_JW, Hv, B), block(XV_GDN_THREADS);
     (void)hipGetLastError();
     if (dk == 128)
         hipLaunchKernelGGL((xv_gdn_kernel<128, ROLLBACK>), grid, block, 0, st, q, k, v, a, beta,
