@@ -18,8 +18,8 @@ the 256 MB Infinity Cache cannot serve the weights of the step being timed.
 
 Before timing, verify == sequential decode is checked bit for bit on the same
 buffers; a mismatch reports no throughput.  The JSON line carries the roofline
-of the dominant kernel (the N = 17408 GEMM, timed live with HIP events on the
-stream it runs on) and the fp64 CPU oracle timed on the host.
+of the dominant kernel (the N = 17408 GEMM, timed live with HIP events that its
+launch records at the kernel's own start and end, on the stream it runs on) and the fp64 CPU oracle timed on the host.
 """
 from __future__ import annotations
 
@@ -127,11 +127,7 @@ def run_steps(layers, stream, steps, warmup, keep_all=False, gemm_events=False):
 
     def step(L, ev=None):
         L.gemm1()
-        if ev is not None:
-            ev[0].record(stream)
-        L.gemm2()
-        if ev is not None:
-            ev[1].record(stream)
+        L.gemm2(ev)                               # ev: recorded at the kernel's own start and end
         L.gdn()
         L.attn()
         L.head()
@@ -144,6 +140,10 @@ def run_steps(layers, stream, steps, warmup, keep_all=False, gemm_events=False):
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)] if gemm_events else [None] * steps
+        for ev in evs:                            # create the events before the timed region
+            if ev is not None:
+                ev[0].record(stream)
+                ev[1].record(stream)
         e_start = torch.cuda.Event(enable_timing=True)
         e_end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -204,7 +204,7 @@ def main():
     inp, layers, exact = build_layers(wl, Lmax, R, stream)
 
     # headline: greedy acceptance on the synthetic head (mostly the root row kept, so the
-    # rollback recomputes the state), live HIP events around the dominant GEMM
+    # rollback recomputes the state), live HIP events on the dominant GEMM's launch
     ms_per_step, gemm_us, wall = run_steps(layers, stream, args.steps, args.warmup, gemm_events=True)
     gemm_avg_us = float(np.mean(gemm_us))
     n_keep = [int(L.n_keep.sum().item()) for L in layers]

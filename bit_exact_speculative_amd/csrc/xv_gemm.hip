@@ -29,6 +29,7 @@
 //    gives each wave whole output tiles: it runs the 16 range chains of a tile
 //    one after the other and folds them in range order, the same operations.
 #include "xv_common.h"
+#include <hip/hip_ext.h>
 
 namespace {
 
@@ -479,104 +480,121 @@ int xv_gemm_grid(int nblk) {
     return nblk < cus ? nblk : cus;
 }
 
+// Where a launch goes: the stream, and optionally events recorded at the start and
+// the end of the kernel's execution (hipExtLaunchKernel).
+struct XvLaunch {
+    hipStream_t st;
+    hipEvent_t e0, e1;
+};
+
 template <int MT, int KSW>
 void xv_gemm_launch_xreg(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
-                         int M, int N, int K, int mt0, hipStream_t st)
+                         int M, int N, int K, int mt0, const XvLaunch& lc)
 {
     dim3 grid(xv_gemm_grid(N / 16)), block(XV_GEMM_THREADS);
-    hipLaunchKernelGGL((xv_gemm_xreg_kernel<MT, KSW>), grid, block, 0, st, x, w, y, y32, M, N, K, mt0);
+    hipExtLaunchKernelGGL((xv_gemm_xreg_kernel<MT, KSW>), grid, block, 0, lc.st, lc.e0, lc.e1, 0, x, w, y, y32, M, N, K, mt0);
 }
 
 template <int KSW, int SL, int NS>
 void xv_gemm_launch_wlds(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
-                         int M, int N, int K, int mt0, hipStream_t st)
+                         int M, int N, int K, int mt0, const XvLaunch& lc)
 {
     dim3 grid(xv_gemm_grid(N / 16)), block(XV_GEMM_THREADS);
-    hipLaunchKernelGGL((xv_gemm_wlds_kernel<KSW, SL, NS>), grid, block, 0, st, x, w, y, y32, M, N, K, mt0);
+    hipExtLaunchKernelGGL((xv_gemm_wlds_kernel<KSW, SL, NS>), grid, block, 0, lc.st, lc.e0, lc.e1, 0, x, w, y, y32, M, N, K, mt0);
 }
 
 template <int MT, int KC>
 void xv_gemm_launch_kloop(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
-                          int M, int N, int K, int mt0, hipStream_t st)
+                          int M, int N, int K, int mt0, const XvLaunch& lc)
 {
     // column blocks per workgroup: as many as keep at least one workgroup per CU busy
     // (callers take this path only for N / 16 >= 2 CUs)
     const int nblk = N / 16, cus = xv_gemm_grid(1 << 30);
     const dim3 block(XV_KL_THREADS);
     if (nblk >= 4 * cus)
-        hipLaunchKernelGGL((xv_gemm_kloop_kernel<MT, 4, KC>), dim3((nblk + 3) / 4), block, 0, st, x, w, y, y32, M, N, K, mt0);
+        hipExtLaunchKernelGGL((xv_gemm_kloop_kernel<MT, 4, KC>), dim3((nblk + 3) / 4), block, 0, lc.st, lc.e0, lc.e1, 0, x, w, y, y32, M, N, K, mt0);
     else
-        hipLaunchKernelGGL((xv_gemm_kloop_kernel<MT, 2, KC>), dim3((nblk + 1) / 2), block, 0, st, x, w, y, y32, M, N, K, mt0);
+        hipExtLaunchKernelGGL((xv_gemm_kloop_kernel<MT, 2, KC>), dim3((nblk + 1) / 2), block, 0, lc.st, lc.e0, lc.e1, 0, x, w, y, y32, M, N, K, mt0);
 }
 
 template <int MT, int U>
 void xv_gemm_launch_xstream(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
-                            int M, int N, int K, int mt0, hipStream_t st)
+                            int M, int N, int K, int mt0, const XvLaunch& lc)
 {
     dim3 grid(xv_gemm_grid(N / 16)), block(XV_GEMM_THREADS);
-    hipLaunchKernelGGL((xv_gemm_xstream_kernel<MT, U>), grid, block, 0, st, x, w, y, y32, M, N, K, mt0);
+    hipExtLaunchKernelGGL((xv_gemm_xstream_kernel<MT, U>), grid, block, 0, lc.st, lc.e0, lc.e1, 0, x, w, y, y32, M, N, K, mt0);
 }
 
 // Launch shape per row-tile count and K.  None of these choices changes any
 // row's arithmetic: every variant runs the same 16-way K split, the same MFMA
 // chains and the same ordered sum.
 void xv_gemm_dispatch(int mt, int ksw, const uint16_t* x, const uint16_t* w, uint16_t* y,
-                      float* y32, int M, int N, int K, int mt0, hipStream_t st)
+                      float* y32, int M, int N, int K, int mt0, const XvLaunch& lc)
 {
     // one row tile and the two K of the 27B-class layer: W through LDS in 1 KB contiguous wave loads
-    if (mt == 1 && K == 5120) { xv_gemm_launch_wlds<10, 40, 4>(x, w, y, y32, M, N, K, mt0, st); return; }
-    if (mt == 1 && K == 6144) { xv_gemm_launch_wlds<12, 48, 4>(x, w, y, y32, M, N, K, mt0, st); return; }
+    if (mt == 1 && K == 5120) { xv_gemm_launch_wlds<10, 40, 4>(x, w, y, y32, M, N, K, mt0, lc); return; }
+    if (mt == 1 && K == 6144) { xv_gemm_launch_wlds<12, 48, 4>(x, w, y, y32, M, N, K, mt0, lc); return; }
     if (mt == 1 && ksw <= 10) {
-        if (ksw <= 2) xv_gemm_launch_xreg<1, 2>(x, w, y, y32, M, N, K, mt0, st);
-        else if (ksw <= 4) xv_gemm_launch_xreg<1, 4>(x, w, y, y32, M, N, K, mt0, st);
-        else if (ksw <= 6) xv_gemm_launch_xreg<1, 6>(x, w, y, y32, M, N, K, mt0, st);
-        else if (ksw <= 8) xv_gemm_launch_xreg<1, 8>(x, w, y, y32, M, N, K, mt0, st);
-        else xv_gemm_launch_xreg<1, 10>(x, w, y, y32, M, N, K, mt0, st);
+        if (ksw <= 2) xv_gemm_launch_xreg<1, 2>(x, w, y, y32, M, N, K, mt0, lc);
+        else if (ksw <= 4) xv_gemm_launch_xreg<1, 4>(x, w, y, y32, M, N, K, mt0, lc);
+        else if (ksw <= 6) xv_gemm_launch_xreg<1, 6>(x, w, y, y32, M, N, K, mt0, lc);
+        else if (ksw <= 8) xv_gemm_launch_xreg<1, 8>(x, w, y, y32, M, N, K, mt0, lc);
+        else xv_gemm_launch_xreg<1, 10>(x, w, y, y32, M, N, K, mt0, lc);
         return;
     }
     // several row tiles and many column blocks: walk K per output tile (x reused over 2-4 column blocks)
     if (mt >= 2 && N / 16 >= 2 * xv_gemm_grid(1 << 30)) {
         switch (mt) {
-            case 2: xv_gemm_launch_kloop<2, 4>(x, w, y, y32, M, N, K, mt0, st); break;
-            case 3: xv_gemm_launch_kloop<3, 4>(x, w, y, y32, M, N, K, mt0, st); break;
-            case 4: xv_gemm_launch_kloop<4, 4>(x, w, y, y32, M, N, K, mt0, st); break;
-            default: xv_gemm_launch_kloop<5, 4>(x, w, y, y32, M, N, K, mt0, st); break;
+            case 2: xv_gemm_launch_kloop<2, 4>(x, w, y, y32, M, N, K, mt0, lc); break;
+            case 3: xv_gemm_launch_kloop<3, 4>(x, w, y, y32, M, N, K, mt0, lc); break;
+            case 4: xv_gemm_launch_kloop<4, 4>(x, w, y, y32, M, N, K, mt0, lc); break;
+            default: xv_gemm_launch_kloop<5, 4>(x, w, y, y32, M, N, K, mt0, lc); break;
         }
         return;
     }
     if (mt == 2 && ksw <= 4) {
-        xv_gemm_launch_xreg<2, 4>(x, w, y, y32, M, N, K, mt0, st);
+        xv_gemm_launch_xreg<2, 4>(x, w, y, y32, M, N, K, mt0, lc);
         return;
     }
     switch (mt) {
-        case 1: xv_gemm_launch_xstream<1, 4>(x, w, y, y32, M, N, K, mt0, st); break;
-        case 2: xv_gemm_launch_xstream<2, 2>(x, w, y, y32, M, N, K, mt0, st); break;
-        case 3: xv_gemm_launch_xstream<3, 1>(x, w, y, y32, M, N, K, mt0, st); break;
-        case 4: xv_gemm_launch_xstream<4, 1>(x, w, y, y32, M, N, K, mt0, st); break;
-        default: xv_gemm_launch_xstream<5, 1>(x, w, y, y32, M, N, K, mt0, st); break;
+        case 1: xv_gemm_launch_xstream<1, 4>(x, w, y, y32, M, N, K, mt0, lc); break;
+        case 2: xv_gemm_launch_xstream<2, 2>(x, w, y, y32, M, N, K, mt0, lc); break;
+        case 3: xv_gemm_launch_xstream<3, 1>(x, w, y, y32, M, N, K, mt0, lc); break;
+        case 4: xv_gemm_launch_xstream<4, 1>(x, w, y, y32, M, N, K, mt0, lc); break;
+        default: xv_gemm_launch_xstream<5, 1>(x, w, y, y32, M, N, K, mt0, lc); break;
     }
 }
 
 }  // namespace
 
-extern "C" int xv_gemm_small_m(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
-                               int M, int N, int K, void* stream)
+extern "C" int xv_gemm_small_m_timed(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
+                                     int M, int N, int K, void* stream, void* start_event,
+                                     void* stop_event)
 {
     XV_REQUIRE(M >= 0 && N >= 16 && N % 16 == 0 && K >= 32 && K % 32 == 0, XV_ERR_SHAPE);
     if (M == 0) return XV_OK;
     XV_REQUIRE(x && w && y, XV_ERR_NULL);
     XV_REQUIRE(xv_aligned16(x) && xv_aligned16(w) && xv_aligned(y, 2) && xv_aligned(y32, 4),
                XV_ERR_ALIGN);
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const int KS = K / 32;
     const int ksw = (KS + XV_GEMM_WAVES - 1) / XV_GEMM_WAVES;   // k-steps of the longest range
     const int tiles = (M + 15) / 16;
     for (int mt0 = 0; mt0 < tiles; mt0 += XV_GEMM_MT_MAX) {
         const int mt = tiles - mt0 < XV_GEMM_MT_MAX ? tiles - mt0 : XV_GEMM_MT_MAX;
-        xv_gemm_dispatch(mt, ksw, x, w, y, y32, M, N, K, mt0, st);
+        // the start event goes with the first launch, the stop event with the last
+        const XvLaunch lc{reinterpret_cast<hipStream_t>(stream),
+                          mt0 == 0 ? reinterpret_cast<hipEvent_t>(start_event) : nullptr,
+                          mt0 + mt >= tiles ? reinterpret_cast<hipEvent_t>(stop_event) : nullptr};
+        xv_gemm_dispatch(mt, ksw, x, w, y, y32, M, N, K, mt0, lc);
         int s = xv_launch_status();
         if (s != XV_OK) return s;
     }
     return XV_OK;
+}
+
+extern "C" int xv_gemm_small_m(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
+                               int M, int N, int K, void* stream)
+{
+    return xv_gemm_small_m_timed(x, w, y, y32, M, N, K, stream, nullptr, nullptr);
 }

@@ -140,9 +140,14 @@ class Layer:
         xv.xv_gemm_small_m(self.x, self.W1, self.y1, self.y1_32 if self.proj_fp32 else None,
                            stream=self.stream)
 
-    def gemm2(self):
-        xv.xv_gemm_small_m(self.x, self.W2, self.y2, self.y2_32 if self.proj_fp32 else None,
-                           stream=self.stream)
+    def gemm2(self, events=None):
+        """events: optional (start, stop) torch.cuda.Event pair timed by the launch itself."""
+        if events is None:
+            xv.xv_gemm_small_m(self.x, self.W2, self.y2, self.y2_32 if self.proj_fp32 else None,
+                               stream=self.stream)
+        else:
+            xv.xv_gemm_small_m_timed(self.x, self.W2, self.y2, self.y2_32 if self.proj_fp32 else None,
+                                     events[0], events[1], stream=self.stream)
 
     def gemms(self):
         self.gemm1()

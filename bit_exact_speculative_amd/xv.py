@@ -35,6 +35,8 @@ _lib.xv_status_string.restype = ctypes.c_char_p
 _lib.xv_status_string.argtypes = [_I]
 _lib.xv_gemm_small_m.restype = _I
 _lib.xv_gemm_small_m.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P]
+_lib.xv_gemm_small_m_timed.restype = _I
+_lib.xv_gemm_small_m_timed.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _P, _P]
 _lib.xv_gdn_verify.restype = _I
 _lib.xv_gdn_verify.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
 _lib.xv_attn_chunk_tokens.restype = _I
@@ -115,6 +117,26 @@ def xv_gemm_small_m(x, w, y, y32=None, stream=None):
         raise ValueError("xv_gemm_small_m: shape mismatch")
     _check("xv_gemm_small_m", _lib.xv_gemm_small_m(_ptr(x), _ptr(w), _ptr(y), _ptr(y32),
                                                   M, N, K, _stream(stream)))
+
+
+def _event(e):
+    """Raw hipEvent_t of a torch.cuda.Event (created on first use), or None."""
+    if e is None:
+        return None
+    if not e.cuda_event:
+        e.record()                     # torch creates the event lazily
+    return e.cuda_event
+
+
+def xv_gemm_small_m_timed(x, w, y, y32=None, start=None, stop=None, stream=None):
+    """xv_gemm_small_m with torch.cuda.Event start / stop recorded by the launch itself."""
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or tuple(y.shape) != (M, N) or (y32 is not None and tuple(y32.shape) != (M, N)):
+        raise ValueError("xv_gemm_small_m_timed: shape mismatch")
+    _check("xv_gemm_small_m_timed", _lib.xv_gemm_small_m_timed(_ptr(x), _ptr(w), _ptr(y), _ptr(y32),
+                                                              M, N, K, _stream(stream),
+                                                              _event(start), _event(stop)))
 
 
 def xv_gdn_verify(q, k, v, a, b, state_in, state_out, o, o32=None, stream=None):

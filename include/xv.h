@@ -77,6 +77,18 @@ int xv_gemm_small_m(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y3
                     int M, int N, int K, void* stream);
 
 /*
+ * xv_gemm_small_m with its kernel execution timed: start_event and stop_event
+ * (hipEvent_t created by the caller, either may be NULL) are recorded when the
+ * call's first kernel starts and its last kernel ends, as the launch itself
+ * records them (hipExtLaunchKernel), so their interval excludes the dispatch
+ * latency that events recorded on the stream around the call include.  Same
+ * results, arguments and errors as xv_gemm_small_m; M == 0 launches nothing
+ * and records nothing.
+ */
+int xv_gemm_small_m_timed(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
+                          int M, int N, int K, void* stream, void* start_event, void* stop_event);
+
+/*
  * GDN verify: T tokens of the gated delta rule per request, fp32 state.
  * The post, the two verify changes (the GDN recurrence through the decode
  * arithmetic, the old verify kernel having tiled the state differently and

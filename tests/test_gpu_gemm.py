@@ -141,3 +141,32 @@ def test_gemm_many_tiles_k_loop_rows_equal_k_split(M, N, K):
     ref = oracle.gemm(xh, wh[cols])
     torch.cuda.synchronize()
     assert max_rel(y32.cpu().numpy()[:, cols], ref) <= OUT_MAX_REL
+
+
+def test_gemm_timed_entry_point_same_bits_and_kernel_interval():
+    """xv_gemm_small_m_timed: the same bits as xv_gemm_small_m, and its launch-recorded interval is
+    positive and no longer than events recorded on the stream around the call."""
+    from bit_exact_speculative_amd.layer import dev_bf16
+    rng = np.random.default_rng(11)
+    xv = _xv()
+    x = dev_bf16(random_bf16(rng, (9, 5120)), "cuda")
+    w = dev_bf16(random_bf16(rng, (4096, 5120), 0.02), "cuda")
+    ref, ref32 = _gemm_dev(x, w)
+    for M in (9, 72, 0):
+        xm = x[:min(M, 9)].contiguous() if M <= 9 else torch.cat([x] * 8, 0).contiguous()
+        y = torch.empty((M, 4096), dtype=torch.bfloat16, device="cuda")
+        y32 = torch.empty((M, 4096), dtype=torch.float32, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s = torch.cuda.current_stream()
+        e0.record(s); e1.record(s)                   # created
+        b0.record(s)
+        xv.xv_gemm_small_m_timed(xm, w, y, y32, e0, e1)
+        b1.record(s)
+        torch.cuda.synchronize()
+        if M == 0:
+            continue
+        rows = ref32 if M == 9 else torch.cat([ref32] * 8, 0)
+        assert torch.equal(y32.view(torch.int32), rows.view(torch.int32))
+        k_ms, b_ms = e0.elapsed_time(e1), b0.elapsed_time(b1)
+        assert 0.0 < k_ms <= b_ms + 1e-3, (M, k_ms, b_ms)
