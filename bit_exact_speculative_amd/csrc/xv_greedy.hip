@@ -99,13 +99,26 @@ void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb
 }
 
 // One thread per request: accepted drafts = leading rows whose id equals the next draft.
+// All of the request's ids and drafts are loaded before the first compare (one round trip).
 __global__ void xv_accept_kernel(const int32_t* __restrict__ draft, const int32_t* __restrict__ ids,
                                  int B, int T, int32_t* __restrict__ n_keep)
 {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= B) return;
+    int dr[XV_TMAX], id[XV_TMAX];
+#pragma unroll
+    for (int t = 0; t < XV_TMAX; ++t) {
+        const int tc = t < T ? t : T - 1;
+        dr[t] = draft[(size_t)b * T + tc];
+        id[t] = ids[(size_t)b * T + tc];
+    }
     int acc = 0;
-    while (acc + 1 < T && draft[(size_t)b * T + acc + 1] == ids[(size_t)b * T + acc]) ++acc;
+    bool run = true;
+#pragma unroll
+    for (int t = 0; t + 1 < XV_TMAX; ++t) {
+        run = run && t + 1 < T && dr[t + 1] == id[t];
+        acc += run ? 1 : 0;
+    }
     n_keep[b] = acc + 1;
 }
 
