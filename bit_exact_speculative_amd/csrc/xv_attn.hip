@@ -43,6 +43,7 @@ constexpr int XV_ATTN_C = 256;      // chunk length (positions), fixed for every
 constexpr int XV_ATTN_WAVES = 8;    // waves of a partial-kernel workgroup
 constexpr int XV_ATTN_MAX_NC = 8192;
 constexpr int XV_ATTN_WIDE_MIN = 128; // (chunk, KV head, request) workgroups from which the wide kernel runs
+constexpr int XV_ATTN_STREAM_MIN = 1024; // ... and from which the persistent streaming kernel runs (about 4 chunks per CU)
 
 // LDS layouts (16-byte granules, XOR-swizzled so that both the cooperative
 // stores and the MFMA fragment reads spread over the banks):
@@ -316,6 +317,283 @@ void xv_attn_partial_wide_kernel(const uint16_t* __restrict__ q, const uint16_t*
     xv_store_acc<D, DB>(ws_acc, oacc, 0, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
 }
 
+// Long contexts: persistent workgroups stream the chunks of one (KV head,
+// request), chunk c = x, x + WPG, x + 2 WPG, ... for workgroup x.  A chunk goes
+// through LDS as four 64-position sub-blocks of K, then four of V^T; each
+// sub-block is a "unit" loaded into registers four units ahead of its use (the
+// next chunk's K units while the current chunk's V is consumed), so HBM loads
+// overlap the MFMA work instead of alternating with it.  Up to 4 tiles of 16
+// pairs; waves t and t + 4 share tile t: wave t forms the score blocks of the
+// chunk's first half, wave t + 4 those of the second, the chunk max meets
+// through LDS, the probabilities go through LDS in fp32, wave t forms the
+// chunk sum, and each wave forms half of the tile's P.V output dims.  Every
+// chain and ordered sum is the wide kernel's, so the bits are the same.
+constexpr int XV_ATTN_SB = 64;              // positions per streamed sub-block
+constexpr int XV_ATTN_UNITS = 4;            // units in flight
+
+template <int D>
+struct XvUnit {
+    static constexpr int NT = XV_ATTN_WAVES * 64;
+    static constexpr int KG = XV_ATTN_SB * (D / 8) / NT;           // K granules per thread
+    static constexpr int VT4 = (XV_ATTN_SB / 4) * (D / 8);         // 4 x 8 V tiles per sub-block
+    static_assert(KG >= 1 && KG <= 4 && VT4 <= NT, "unit split");
+    xv_u32x4 r[4];                                                  // K: KG granules; V: one 4 x 8 tile
+};
+
+template <int D>
+__global__ __launch_bounds__(XV_ATTN_WAVES * 64)
+void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
+                                   const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_cache,
+                                   uint16_t* __restrict__ v_cache, const int32_t* __restrict__ kv_len,
+                                   float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+                                   int T, int Hq, int Hkv, int Lmax, int NC, float scale_log2)
+{
+    constexpr int C = XV_ATTN_C;
+    constexpr int SB = XV_ATTN_SB;
+    constexpr int NSB = C / SB;                 // sub-blocks per chunk
+    constexpr int NT = XV_ATTN_WAVES * 64;
+    constexpr int KS = D / 32;
+    constexpr int DB = D / 16;
+    constexpr int NCB = C / 16;
+    constexpr int NU = XV_ATTN_UNITS;
+    constexpr int CBS = SB / 16;                // score blocks per sub-block
+    constexpr int CBH = NCB / 2;                // score blocks per wave
+    constexpr int DBH = DB / 2;                 // output blocks per wave (half of the head dim)
+    constexpr int PP = C + 4;                   // probability row pitch (floats)
+    constexpr int KG = XvUnit<D>::KG;
+    constexpr int VT4 = XvUnit<D>::VT4;
+    static_assert(NSB == 4 && NU == 4 && XV_ATTN_WAVES == 8, "four units per chunk half, two waves per tile");
+    __shared__ __attribute__((aligned(16))) xv_u32x4 sk[SB * D / 8];    // K sub-block [pos][d], swizzled
+    __shared__ __attribute__((aligned(16))) xv_u32x4 svt[D * SB / 8];   // V^T sub-block [d][pos], swizzled
+    __shared__ __attribute__((aligned(16))) float sp[4 * 16 * PP];      // probabilities per tile [pair][pos]
+    __shared__ float smax[XV_ATTN_WAVES][16];
+
+    const int WPG = gridDim.x;
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int Hg = Hq / Hkv;
+    const int P = Hg * T;
+    int L0 = kv_len[b];
+    L0 = L0 < 0 ? 0 : (L0 > Lmax - T ? Lmax - T : L0);
+    const int Lend = L0 + T;
+    const int nchunks = (Lend + C - 1) / C;
+    if ((int)blockIdx.x >= nchunks) return;     // uniform
+    const int nitems = (nchunks - 1 - (int)blockIdx.x) / WPG + 1;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int tile = wave & 3;
+    const int dh = wave >> 2;                   // which half of the score blocks and of the dims
+    const int lr = lane & 15, lg = lane >> 4;
+    const bool tile_on = tile < (P + 15) / 16;
+    const int pair = tile * 16 + lr;
+    const bool pair_ok = pair < P;
+    const int pr = pair_ok ? pair / Hg : 0;
+    const int ph = g * Hg + (pair_ok ? pair % Hg : 0);
+    const int plen = L0 + pr + 1;
+    const size_t kvbase = ((size_t)b * Hkv + g) * Lmax;
+    const size_t newbase = ((size_t)b * T * Hkv + g) * D;
+    const int newstride = Hkv * D;
+    const xv_u32x4 zero = {0u, 0u, 0u, 0u};
+    float* tp = sp + tile * 16 * PP;
+
+    auto src = [&](const uint16_t* cache, const uint16_t* fresh, int pos) __attribute__((always_inline)) -> const uint16_t* {
+        if (pos < L0) return cache + (kvbase + pos) * D;
+        if (pos < Lend) return fresh + newbase + (size_t)(pos - L0) * newstride;
+        return cache + kvbase * D;
+    };
+    // unit u of item it: u < 4 is K sub-block u, u >= 4 is V sub-block u - 4
+    auto load_unit = [&](XvUnit<D>& U, int it, int u) __attribute__((always_inline)) {
+        const int c0 = ((int)blockIdx.x + it * WPG) * C;
+        const int p0 = c0 + (u & 3) * SB;
+        if (u < 4) {
+#pragma unroll
+            for (int i = 0; i < KG; ++i) {
+                const int idx = tid + i * NT;
+                U.r[i] = xv_load16(src(k_cache, k_new, p0 + idx / (D / 8)) + (idx % (D / 8)) * 8);
+            }
+        } else {
+            const int vt = tid < VT4 ? tid : VT4 - 1;
+            const int pg4 = vt / (D / 8), dg = vt % (D / 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) U.r[e] = xv_load16(src(v_cache, v_new, p0 + pg4 * 4 + e) + dg * 8);
+        }
+    };
+    // into LDS: positions past L0 + T zeroed, new rows appended to the cache
+    auto store_unit = [&](XvUnit<D>& U, int it, int u) __attribute__((always_inline)) {
+        const int c0 = ((int)blockIdx.x + it * WPG) * C;
+        const int p0 = c0 + (u & 3) * SB;
+        if (u < 4) {
+#pragma unroll
+            for (int i = 0; i < KG; ++i) {
+                const int idx = tid + i * NT;
+                const int lp = idx / (D / 8), cc = idx % (D / 8);
+                const int pos = p0 + lp;
+                if (pos >= Lend) U.r[i] = zero;
+                else if (pos >= L0) xv_store16(k_cache + (kvbase + pos) * D + cc * 8, U.r[i]);
+                sk[xv_k_granule<D>(lp, cc)] = U.r[i];
+            }
+        } else if (tid < VT4) {
+            // a 4 (positions) x 8 (dims) tile -> for each of its 8 dims, 4 positions of V^T (8 bytes)
+            const int pg4 = tid / (D / 8), dg = tid % (D / 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int pos = p0 + pg4 * 4 + e;
+                if (pos >= Lend) U.r[e] = zero;
+                else if (pos >= L0) xv_store16(v_cache + (kvbase + pos) * D + dg * 8, U.r[e]);
+            }
+            char* vb = reinterpret_cast<char*>(svt);
+#pragma unroll
+            for (int dd = 0; dd < 8; ++dd) {
+                const uint32_t a0 = U.r[0][dd >> 1], a1 = U.r[1][dd >> 1];
+                const uint32_t a2 = U.r[2][dd >> 1], a3 = U.r[3][dd >> 1];
+                uint2 outv;
+                outv.x = (dd & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
+                outv.y = (dd & 1) ? ((a2 >> 16) | (a3 & 0xFFFF0000u)) : ((a2 & 0xFFFFu) | (a3 << 16));
+                const int d = dg * 8 + dd;
+                const int gi = d * (SB / 8) + ((pg4 >> 1) ^ ((d ^ (d >> 3)) & 7));
+                *reinterpret_cast<uint2*>(vb + gi * 16 + (pg4 & 1) * 8) = outv;
+            }
+        }
+    };
+
+    xv_u32x4 qf[KS];
+    {
+        const uint16_t* qp = q + (((size_t)b * T + pr) * Hq + ph) * D + lg * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = xv_load16(qp + ks * 32);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = pair_ok ? qf[ks] : zero;
+    }
+    XvUnit<D> ub[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) load_unit(ub[u], 0, u);
+
+    for (int it = 0; it < nitems; ++it) {
+        const int c = (int)blockIdx.x + it * WPG;
+        const int c0 = c * C;
+        const bool full = c0 + C <= L0 + 1;
+        const bool more = it + 1 < nitems;
+        // the unit four steps ahead of unit u: in this item, else the next item's (past the
+        // last item: the same K unit of this item again, a cache hit, so the unit kind stays fixed)
+        auto ahead = [&](XvUnit<D>& U, int u) __attribute__((always_inline)) {
+            if (u + NU < 8) load_unit(U, it, u + NU);
+            else load_unit(U, more ? it + 1 : it, u + NU - 8);
+        };
+
+        // ---- this wave's half of the score blocks, one K sub-block at a time ----
+        xv_f32x4 sc[CBH];
+#pragma unroll
+        for (int j = 0; j < CBH; ++j) sc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NSB; ++u) {
+            __syncthreads();                    // K slot free
+            store_unit(ub[u], it, u);
+            ahead(ub[u], u);
+            __syncthreads();
+            if (tile_on && (u * CBS) / CBH == dh) {     // uniform per wave
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int j = 0; j < CBS; ++j)
+                        sc[(u * CBS) % CBH + j] = xv_mfma16x16x32(sk[xv_k_granule<D>(j * 16 + lr, ks * 4 + lg)], qf[ks],
+                                                                  sc[(u * CBS) % CBH + j]);
+            }
+        }
+
+        // ---- chunk max over both waves (exact), probabilities into LDS ----
+        const int cb0 = dh * CBH;
+        float mw = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < CBH; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sv = sc[j][i] * scale_log2;
+                sc[j][i] = sv;
+                if (full || c0 + (cb0 + j) * 16 + 4 * lg + i < plen) mw = fmaxf(mw, sv);
+            }
+        mw = fmaxf(mw, __shfl_xor(mw, 16));
+        mw = fmaxf(mw, __shfl_xor(mw, 32));
+        if (lg == 0) smax[wave][lr] = mw;
+        __syncthreads();                        // also: the previous chunk's P.V is done with sp
+        float m = fmaxf(smax[tile][lr], smax[tile + 4][lr]);
+        if (!pair_ok) m = 0.f;
+        if (tile_on) {
+#pragma unroll
+            for (int j = 0; j < CBH; ++j) {
+                xv_f32x4 pv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool vis = full || c0 + (cb0 + j) * 16 + 4 * lg + i < plen;
+                    pv[i] = vis ? __builtin_amdgcn_exp2f(sc[j][i] - m) : 0.f;
+                }
+                *reinterpret_cast<xv_f32x4*>(tp + lr * PP + (cb0 + j) * 16 + 4 * lg) = pv;
+            }
+        }
+
+        // ---- acc = P V, one V sub-block (two k-slots) at a time; this wave's half of the dims ----
+        xv_f32x4 oacc[DBH];
+#pragma unroll
+        for (int j = 0; j < DBH; ++j) oacc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+        float l = 0.f;
+#pragma unroll
+        for (int u = NSB; u < 2 * NSB; ++u) {
+            __syncthreads();                    // V^T slot free; P of both waves visible
+            store_unit(ub[u - NSB], it, u);
+            ahead(ub[u - NSB], u);
+            __syncthreads();
+            if (u == NSB && tile_on && dh == 0) {       // chunk sum, in the wide kernel's order
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const xv_f32x4 pv = *reinterpret_cast<const xv_f32x4*>(tp + lr * PP + cb * 16 + 4 * lg);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) l = l + pv[i];
+                }
+                l = l + __shfl_xor(l, 16);
+                l = l + __shfl_xor(l, 32);
+            }
+            if (tile_on) {
+#pragma unroll
+                for (int k2 = 0; k2 < SB / 32; ++k2) {
+                    const int kk = (u - NSB) * (SB / 32) + k2;
+                    xv_u32x4 phi, plo;
+                    xv_p_split(*reinterpret_cast<const xv_f32x4*>(tp + lr * PP + kk * 32 + 4 * lg),
+                               *reinterpret_cast<const xv_f32x4*>(tp + lr * PP + kk * 32 + 16 + 4 * lg), phi, plo);
+                    const int ca = k2 * 4 + (lg >> 1);
+#pragma unroll
+                    for (int j0 = 0; j0 < DBH; j0 += 4) {
+                        constexpr int GW = DBH < 4 ? DBH : 4;
+                        xv_u32x4 vf[GW];
+#pragma unroll
+                        for (int w4 = 0; w4 < GW; ++w4) {
+                            const int d = (dh * DBH + j0 + w4) * 16 + lr;
+                            const char* rowp = reinterpret_cast<const char*>(svt) + (size_t)d * (SB * 2) + (lg & 1) * 8;
+                            const int sw = (d ^ (d >> 3)) & 7;
+                            const uint2 va = *reinterpret_cast<const uint2*>(rowp + ((ca ^ sw) << 4));
+                            const uint2 vb = *reinterpret_cast<const uint2*>(rowp + (((ca + 2) ^ sw) << 4));
+                            vf[w4] = xv_u32x4{va.x, va.y, vb.x, vb.y};
+                        }
+#pragma unroll
+                        for (int w4 = 0; w4 < GW; ++w4) oacc[j0 + w4] = xv_mfma16x16x32(phi, vf[w4], oacc[j0 + w4]);
+#pragma unroll
+                        for (int w4 = 0; w4 < GW; ++w4) oacc[j0 + w4] = xv_mfma16x16x32(plo, vf[w4], oacc[j0 + w4]);
+                    }
+                }
+            }
+        }
+
+        // ---- the chunk partials of pairs that see this chunk ----
+        if (tile_on) {
+            if (dh == 0 && lg == 0 && pair_ok && plen > c0) {
+                const size_t idx = (((size_t)b * T + pr) * Hq + ph) * NC + c;
+                ws_ml[idx * 2 + 0] = m;
+                ws_ml[idx * 2 + 1] = l;
+            }
+            xv_store_acc<D, DBH>(ws_acc, oacc, dh * DBH, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
+        }
+    }
+}
+
 // Few workgroups (small batch, short context): one workgroup per (request, KV
 // head, chunk, 16-pair tile, 1/DS of the value dims), so that the chunk's work is
 // spread over more CUs.  The tile's queries are staged once in LDS; the waves
@@ -552,7 +830,19 @@ int xv_attn_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_n
     // one workgroup per (chunk, KV head, request) when those alone fill the chip,
     // otherwise one per 16-pair tile of each.
     const int P = (Hq / Hkv) * T;
-    if ((long long)B * Hkv * NC >= XV_ATTN_WIDE_MIN && P <= 16 * XV_ATTN_WAVES) {
+    const long long groups = (long long)B * Hkv;
+    if (D == 256 && groups * NC >= XV_ATTN_STREAM_MIN && P <= 64) {
+        // about one persistent workgroup per CU, spread evenly over the (KV head, request) groups
+        int cus = 0, dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        long long wpg = cus / groups;
+        wpg = wpg < 1 ? 1 : (wpg > NC ? NC : wpg);
+        hipLaunchKernelGGL(xv_attn_partial_stream_kernel<D>, dim3((int)wpg, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st,
+                           q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
+                           T, Hq, Hkv, Lmax, NC, scale_log2);
+    } else if (groups * NC >= XV_ATTN_WIDE_MIN && P <= 16 * XV_ATTN_WAVES) {
         hipLaunchKernelGGL(xv_attn_partial_wide_kernel<D>, dim3(NC, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st,
                            q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
                            T, Hq, Hkv, Lmax, NC, scale_log2);

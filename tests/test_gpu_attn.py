@@ -140,16 +140,18 @@ def test_attn_capacity_and_workspace_invariance():
 @pytest.mark.parametrize("case", [(1, 9, 24, 4, 256, [640]), (2, 16, 8, 1, 64, [0, 700]),
                                   (1, 5, 6, 2, 128, [257]), (3, 1, 24, 4, 256, [5, 300, 1000])],
                          ids=lambda c: str(c))
-def test_attn_wide_and_tile_kernels_agree(case):
-    """The tile kernel (few (chunk, KV head, request) workgroups) and the wide kernel (at least
-    128 of them) form the same numbers: the same rows at a small and at a large capacity."""
+@pytest.mark.parametrize("grid", [128, 1024])
+def test_attn_wide_and_tile_kernels_agree(case, grid):
+    """The partial kernels form the same numbers: the same rows at a small capacity (few
+    (chunk, KV head, request) workgroups: the tile kernel) and at capacities that give at least
+    128 of them (the wide kernel) or 1024 (the persistent streaming kernel, up to 64 pairs)."""
     B, T, Hq, Hkv, d, L0 = case
     C = _xv().xv_attn_chunk_tokens()
     Lmax = max(L0) + T
     assert B * Hkv * -(-Lmax // C) < 128                     # small capacity: tile kernel
     D = Dev(*_case(123 + sum(L0), B, T, Hq, Hkv, d, L0, Lmax))
     o, o32, kc, vc = _verify(D)
-    extra = -(-128 // (B * Hkv)) * C - Lmax                  # large capacity: wide kernel
+    extra = -(-grid // (B * Hkv)) * C - Lmax                 # large capacity
     o2, o322, kc2, vc2 = _verify(D, Lmax_extra=extra)
     torch.cuda.synchronize()
     assert same_bits(o32, o322) and same_bits(o, o2)
