@@ -363,10 +363,15 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
     constexpr int KG = XvUnit<D>::KG;
     constexpr int VT4 = XvUnit<D>::VT4;
     static_assert(NSB == 4 && NU == 4 && XV_ATTN_WAVES == 8, "four units per chunk half, two waves per tile");
-    __shared__ __attribute__((aligned(16))) xv_u32x4 sk[SB * D / 8];    // K sub-block [pos][d], swizzled
-    __shared__ __attribute__((aligned(16))) xv_u32x4 svt[D * SB / 8];   // V^T sub-block [d][pos], swizzled
+    constexpr int QP = D + 8;                   // query row pitch in LDS (bf16)
+    // one slot holds the current K sub-block [pos][d] or V^T sub-block [d][pos] (swizzled):
+    // the K units of a chunk are consumed before its V units, and those before the next K
+    __shared__ __attribute__((aligned(16))) xv_u32x4 skv[SB * D / 8];
     __shared__ __attribute__((aligned(16))) float sp[4 * 16 * PP];      // probabilities per tile [pair][pos]
+    __shared__ __attribute__((aligned(16))) uint16_t sq[4 * 16 * QP];   // the 4 tiles' queries
     __shared__ float smax[XV_ATTN_WAVES][16];
+    xv_u32x4* const sk = skv;
+    xv_u32x4* const svt = skv;
 
     const int WPG = gridDim.x;
     const int g = blockIdx.y, b = blockIdx.z;
@@ -457,14 +462,21 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
         }
     };
 
-    xv_u32x4 qf[KS];
+    // the 4 tiles' queries into LDS (rows of pairs past P are zero); visible after the first barrier
     {
-        const uint16_t* qp = q + (((size_t)b * T + pr) * Hq + ph) * D + lg * 8;
+        constexpr int QG = (4 * 16 * (D / 8) + NT - 1) / NT;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = xv_load16(qp + ks * 32);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = pair_ok ? qf[ks] : zero;
+        for (int i = 0; i < QG; ++i) {
+            const int e = tid + i * NT;
+            if (e < 4 * 16 * (D / 8)) {
+                const int p2 = e / (D / 8), cc = e % (D / 8);
+                const int p2c = p2 < P ? p2 : 0;
+                const xv_u32x4 v = xv_load16(q + (((size_t)b * T + p2c / Hg) * Hq + g * Hg + p2c % Hg) * D + cc * 8);
+                *reinterpret_cast<xv_u32x4*>(sq + p2 * QP + cc * 8) = p2 < P ? v : zero;
+            }
+        }
     }
+    const uint16_t* const qrow = sq + (tile * 16 + lr) * QP + lg * 8;
     XvUnit<D> ub[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) load_unit(ub[u], 0, u);
@@ -493,11 +505,15 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
             __syncthreads();
             if (tile_on && (u * CBS) / CBH == dh) {     // uniform per wave
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
+                for (int ks = 0; ks < KS; ++ks) {       // per score block one chain over ks
+                    const xv_u32x4 qk = *reinterpret_cast<const xv_u32x4*>(qrow + ks * 32);
+                    xv_u32x4 kf[CBS];
+#pragma unroll
+                    for (int j = 0; j < CBS; ++j) kf[j] = sk[xv_k_granule<D>(j * 16 + lr, ks * 4 + lg)];
 #pragma unroll
                     for (int j = 0; j < CBS; ++j)
-                        sc[(u * CBS) % CBH + j] = xv_mfma16x16x32(sk[xv_k_granule<D>(j * 16 + lr, ks * 4 + lg)], qf[ks],
-                                                                  sc[(u * CBS) % CBH + j]);
+                        sc[(u * CBS) % CBH + j] = xv_mfma16x16x32(kf[j], qk, sc[(u * CBS) % CBH + j]);
+                }
             }
         }
 
