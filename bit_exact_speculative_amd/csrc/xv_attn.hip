@@ -23,15 +23,18 @@
 //     Scores are computed transposed (S^T = K Q^T) so that each lane holds its
 //     pair's probabilities in the order the P.V MFMA consumes them.  New rows
 //     come from k_new/v_new and are appended to the cache by one workgroup.
-//     Two kernels form exactly these numbers with different work splits:
+//     Three kernels form exactly these numbers with different work splits:
 //     xv_attn_partial_wide_kernel (workgroup per chunk, KV head and request,
-//     wave per 16-pair tile) and xv_attn_partial_tile_kernel (workgroup per
-//     16-pair tile as well, the waves splitting its positions and output dims);
-//     the host picks by grid size only, so a pair's bits never depend on it.
+//     wave per 16-pair tile), xv_attn_partial_tile_kernel (workgroup per
+//     16-pair tile as well, the waves splitting its positions and output dims)
+//     and xv_attn_partial_stream_kernel (persistent workgroups streaming the
+//     chunks of one KV head and request, for long contexts); the host picks by
+//     grid size only, so a pair's bits never depend on it.
 //  2. xv_attn_combine_kernel, grid (query head, row, request): with
 //     M = max_c m_c, beta_c = 2^(m_c - M), L = sum_c l_c beta_c and
 //     A = sum_c acc_c beta_c in ascending chunk order; o = A / L, stored as
-//     bf16 (nearest even) and optionally fp32.
+//     bf16 (nearest even) and optionally fp32.  Its two load schedules (by the
+//     capacity's chunk count) fold the same operations in the same order.
 // Masked positions are excluded by index, never by value, and positions at or
 // past L0 + T are never read (their LDS slots are zero-filled).
 #include "xv_common.h"
@@ -44,6 +47,9 @@ constexpr int XV_ATTN_WAVES = 8;    // waves of a partial-kernel workgroup
 constexpr int XV_ATTN_MAX_NC = 8192;
 constexpr int XV_ATTN_WIDE_MIN = 128; // (chunk, KV head, request) workgroups from which the wide kernel runs
 constexpr int XV_ATTN_STREAM_MIN = 1024; // ... and from which the persistent streaming kernel runs (about 4 chunks per CU)
+constexpr int XV_COMBINE_U = 24;    // chunks per block of combine loads kept in flight
+// the combine's per-chunk LDS arrays are padded to whole pairs of load blocks
+__host__ __device__ constexpr int xv_combine_pad(int nc) { return (nc + 2 * XV_COMBINE_U - 1) / (2 * XV_COMBINE_U) * (2 * XV_COMBINE_U); }
 
 // LDS layouts (16-byte granules, XOR-swizzled so that both the cooperative
 // stores and the MFMA fragment reads spread over the banks):
@@ -782,26 +788,9 @@ void xv_attn_partial_tile_kernel(const uint16_t* __restrict__ q, const uint16_t*
     xv_store_acc<D, DBW>(ws_acc, oacc, dpart * DBP + dbl0, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
 }
 
+// the workgroup's maximum of mloc (exact in any order)
 template <int D>
-__global__ __launch_bounds__(D)
-void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
-                            const int32_t* __restrict__ kv_len, uint16_t* __restrict__ o,
-                            float* __restrict__ o32, int T, int Hq, int Lmax, int NC)
-{
-    extern __shared__ float sh[];               // [NC] beta, [NC] l*beta, [D] max scratch
-    float* sbeta = sh;
-    float* slw = sh + NC;
-    float* sred = sh + 2 * NC;
-    const int h = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x;
-    int L0 = kv_len[b];
-    L0 = L0 < 0 ? 0 : (L0 > Lmax - T ? Lmax - T : L0);
-    const int len = L0 + r + 1;
-    const int nc = (len + XV_ATTN_C - 1) / XV_ATTN_C;
-    const size_t base = (((size_t)b * T + r) * Hq + h) * NC;
-
-    float mloc = -INFINITY;
-    for (int cc = tid; cc < nc; cc += D) mloc = fmaxf(mloc, ws_ml[(base + cc) * 2]);
+__device__ __forceinline__ float xv_combine_max(float mloc, float* sred, int tid) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
     if ((tid & 63) == 0) sred[tid >> 6] = mloc;
@@ -812,26 +801,120 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
         sred[0] = mm;
     }
     __syncthreads();
-    const float M = sred[0];
-    for (int cc = tid; cc < nc; cc += D) {
-        const float be = __builtin_amdgcn_exp2f(ws_ml[(base + cc) * 2] - M);
-        sbeta[cc] = be;
-        slw[cc] = ws_ml[(base + cc) * 2 + 1] * be;
-    }
-    __syncthreads();
-    float L = 0.f, A = 0.f;
+    return sred[0];
+}
+
+// DEEP = false: every thread walks its chain loading as it goes (rows of a few
+// chunks).  DEEP = true (long rows): the per-chunk (m, l) are staged in LDS in one
+// pass, and the chain's loads run in two alternating register blocks of
+// XV_COMBINE_U chunks, one block in flight while the other is summed.  Both fold
+// the same operations in the same order.
+template <int D, bool DEEP>
+__global__ __launch_bounds__(D)
+void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
+                            const int32_t* __restrict__ kv_len, uint16_t* __restrict__ o,
+                            float* __restrict__ o32, int T, int Hq, int Lmax, int NC)
+{
+    extern __shared__ __attribute__((aligned(16))) float sh[];   // [NCP] beta, [NCP] l*beta, [D] max scratch
+    const int NCP = DEEP ? xv_combine_pad(NC) : NC;
+    float* sbeta = sh;
+    float* slw = sh + NCP;
+    float* sred = sh + 2 * NCP;
+    const int h = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    int L0 = kv_len[b];
+    L0 = L0 < 0 ? 0 : (L0 > Lmax - T ? Lmax - T : L0);
+    const int len = L0 + r + 1;
+    const int nc = (len + XV_ATTN_C - 1) / XV_ATTN_C;
+    const size_t base = (((size_t)b * T + r) * Hq + h) * NC;
     const float* ap = ws_acc + base * D + tid;
+    float L = 0.f, A = 0.f;
+
+    if constexpr (!DEEP) {
+        float mloc = -INFINITY;
+        for (int cc = tid; cc < nc; cc += D) mloc = fmaxf(mloc, ws_ml[(base + cc) * 2]);
+        const float M = xv_combine_max<D>(mloc, sred, tid);
+        for (int cc = tid; cc < nc; cc += D) {
+            const float be = __builtin_amdgcn_exp2f(ws_ml[(base + cc) * 2] - M);
+            sbeta[cc] = be;
+            slw[cc] = ws_ml[(base + cc) * 2 + 1] * be;
+        }
+        __syncthreads();
 #pragma unroll 8
-    for (int cc = 0; cc < nc; ++cc) {
-        L = L + slw[cc];
-        A = __builtin_fmaf(ap[(size_t)cc * D], sbeta[cc], A);
+        for (int cc = 0; cc < nc; ++cc) {
+            L = L + slw[cc];
+            A = __builtin_fmaf(ap[(size_t)cc * D], sbeta[cc], A);
+        }
+    } else {
+        constexpr int U = XV_COMBINE_U;
+        // indices past nc re-read chunk nc - 1 and are not summed
+        auto fetch = [&](float (&buf)[U], int c0) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int cn = c0 + u;
+                buf[u] = ap[(size_t)(cn < nc ? cn : nc - 1) * D];
+            }
+        };
+        // beta and l * beta four at a time from LDS (padded to a multiple of 2 U); a
+        // chunk past nc leaves both sums as they are
+        auto fold = [&](const float (&buf)[U], int c0) __attribute__((always_inline)) {
+            float be[U], lw[U];
+#pragma unroll
+            for (int u = 0; u < U; u += 4) {
+                const float4 b4 = *reinterpret_cast<const float4*>(sbeta + c0 + u);
+                const float4 l4 = *reinterpret_cast<const float4*>(slw + c0 + u);
+                be[u] = b4.x; be[u + 1] = b4.y; be[u + 2] = b4.z; be[u + 3] = b4.w;
+                lw[u] = l4.x; lw[u + 1] = l4.y; lw[u + 2] = l4.z; lw[u + 3] = l4.w;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool in = c0 + u < nc;
+                const float L2 = L + lw[u];
+                const float A2 = __builtin_fmaf(buf[u], be[u], A);
+                L = in ? L2 : L;
+                A = in ? A2 : A;
+            }
+        };
+        float ba[U], bb[U];
+        fetch(ba, 0);                           // independent of the maximum
+        // (m, l) of every chunk into LDS, four chunks' loads in flight per thread
+        float mloc = -INFINITY;
+        for (int c0 = 0; c0 < nc; c0 += 4 * D) {
+            float2 ml[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int cc = c0 + j * D + tid;
+                ml[j] = cc < nc ? *reinterpret_cast<const float2*>(ws_ml + (base + cc) * 2) : make_float2(-INFINITY, 0.f);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int cc = c0 + j * D + tid;
+                if (cc < nc) {
+                    sbeta[cc] = ml[j].x;
+                    slw[cc] = ml[j].y;
+                    mloc = fmaxf(mloc, ml[j].x);
+                }
+            }
+        }
+        const float M = xv_combine_max<D>(mloc, sred, tid);
+        for (int cc = tid; cc < nc; cc += D) {  // the entries this thread wrote
+            const float be = __builtin_amdgcn_exp2f(sbeta[cc] - M);
+            sbeta[cc] = be;
+            slw[cc] = slw[cc] * be;
+        }
+        __syncthreads();
+        for (int c0 = 0; c0 < nc; c0 += 2 * U) {
+            fetch(bb, c0 + U);
+            fold(ba, c0);
+            fetch(ba, c0 + 2 * U);
+            fold(bb, c0 + U);
+        }
     }
     const float ov = A / L;
     const size_t oi = (((size_t)b * T + r) * Hq + h) * D + tid;
     o[oi] = xv_f32_to_bf16(ov);
     if (o32) o32[oi] = ov;
 }
-
 
 template <int D>
 int xv_attn_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
@@ -873,9 +956,15 @@ int xv_attn_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_n
     }
     int s = xv_launch_status();
     if (s != XV_OK) return s;
-    const size_t shmem = sizeof(float) * (2 * (size_t)NC + D);
-    hipLaunchKernelGGL(xv_attn_combine_kernel<D>, dim3(Hq, T, B), dim3(D), shmem, st,
-                       ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC);
+    if (NC > 2 * XV_COMBINE_U) {
+        const size_t shmem = sizeof(float) * (2 * (size_t)xv_combine_pad(NC) + D);
+        hipLaunchKernelGGL((xv_attn_combine_kernel<D, true>), dim3(Hq, T, B), dim3(D), shmem, st,
+                           ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC);
+    } else {
+        const size_t shmem = sizeof(float) * (2 * (size_t)NC + D);
+        hipLaunchKernelGGL((xv_attn_combine_kernel<D, false>), dim3(Hq, T, B), dim3(D), shmem, st,
+                           ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC);
+    }
     return xv_launch_status();
 }
 
