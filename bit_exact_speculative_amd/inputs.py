@@ -32,6 +32,8 @@ value:
    5. synthetic head: W_head_gdn [NH][Hv*dv] * 0.02; W_head_attn [NH][Hq*d] * 0.02
    6. (stream B) draft ids [B][T] uniform integers in [0, NH)
    7. (stream B) batch8 only: accepted draft counts uniform integers 0..k
+   8. (stream C, composed decoding only) token embedding table [NH][K] (bf16
+      standard normals), then one root token per request, uniform in [0, NH)
 
 Input recipe: q and k are L2-normalised per (token, head) vector in fp64, then
 rounded to fp32 and then to bf16 (round to nearest even); v, x, caches and
@@ -209,7 +211,7 @@ def make_inputs(wl: Workload, *, Lmax: Optional[int] = None, pad_value: int = BF
     with_gemm / with_head=False skip the (large) weight draws; they come last in
     the draw order, so skipping them changes nothing else.
     """
-    sa, sb = np.random.SeedSequence(wl.seed).spawn(2)
+    sa, sb = np.random.SeedSequence(wl.seed).spawn(2)   # stream C is spawned third (composed_inputs)
     rng = np.random.Generator(np.random.PCG64(sa))
     rng_ids = np.random.Generator(np.random.PCG64(sb))
     B, T = wl.B, wl.T
@@ -259,3 +261,16 @@ def random_bf16(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarr
 def random_gdn(rng: np.random.Generator, B, T, Hk, Hv, dk, dv):
     """GDN rows with the workload recipe, for ad-hoc test shapes."""
     return gdn_rows(rng, B, T, Hk, Hv, dk, dv)
+
+
+def composed_inputs(wl: Workload, *, Lmax: Optional[int] = None) -> Inputs:
+    """Inputs of composed decoding on the synthetic layer: every array of
+    :func:`make_inputs` (the weights, the cached prefix: GDN prefix rows and KV
+    cache) plus, from a third stream, the token embedding table (extra["E"],
+    bf16 [NH][K]) and the root tokens (extra["root"], int32 [B])."""
+    inp = make_inputs(wl, Lmax=Lmax, with_gemm=True, with_head=True)
+    sc = np.random.SeedSequence(wl.seed).spawn(3)[2]
+    rng = np.random.Generator(np.random.PCG64(sc))
+    inp.extra["E"] = _normal_bf16(rng, (wl.NH, wl.K))
+    inp.extra["root"] = rng.integers(0, wl.NH, size=wl.B, dtype=np.int64).astype(np.int32)
+    return inp

@@ -48,7 +48,8 @@ def _bind(path: str):
     lib.xo_attn.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D, P]
     lib.xo_attn_row.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, D, I, I, I, P]
     lib.xo_greedy.argtypes = [P, P, I, I, I, P, P]
-    for f in ("xo_gemm", "xo_gdn", "xo_rollback", "xo_attn", "xo_attn_row", "xo_greedy"):
+    lib.xo_logprob.argtypes = [P, P, I, I, I, P]
+    for f in ("xo_gemm", "xo_gdn", "xo_rollback", "xo_attn", "xo_attn_row", "xo_greedy", "xo_logprob"):
         getattr(lib, f).restype = None
     return lib
 
@@ -166,3 +167,13 @@ def greedy(logits: np.ndarray, draft: np.ndarray):
     n_keep = np.empty((B,), np.int32)
     _load().xo_greedy(_p(logits), _p(draft), B, T, N, _p(ids), _p(n_keep))
     return ids, n_keep
+
+
+def logprob(logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """log softmax(logits[b][t])[ids[b][t]] in fp64.  logits fp64 [B][T][N]; ids int32 [B][T]."""
+    logits = _c(logits, np.float64); ids = _c(ids, np.int32)
+    B, T, N = logits.shape
+    assert ids.shape == (B, T) and ids.min() >= 0 and ids.max() < N
+    lp = np.empty((B, T), np.float64)
+    _load().xo_logprob(_p(logits), _p(ids), B, T, N, _p(lp))
+    return lp

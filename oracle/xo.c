@@ -292,3 +292,22 @@ void xo_greedy(const double* logits, const int32_t* draft, int B, int T, int N,
         n_keep[bb] = acc + 1;
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Log-probability of a chosen token (post, first paragraph: the outputs    */
+/* compared were token ids and their logprobs).  With z the row's logits:   */
+/*   lp[b][t] = log softmax(z)[id] = z[id] - max(z) - log sum_n exp(z[n] - max(z)) */
+/* fp64, n ascending.                                                        */
+/* ------------------------------------------------------------------------ */
+void xo_logprob(const double* logits, const int32_t* ids, int B, int T, int N, double* lp)
+{
+    for (long r = 0; r < (long)B * T; ++r) {
+        const double* row = logits + r * N;
+        double m = row[0];
+        for (int n = 1; n < N; ++n)
+            if (row[n] > m) m = row[n];
+        double s = 0.0;
+        for (int n = 0; n < N; ++n) s += exp(row[n] - m);
+        lp[r] = (row[ids[r]] - m) - log(s);
+    }
+}

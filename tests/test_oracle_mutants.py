@@ -46,6 +46,10 @@ MUTANTS = [
     ("rollback_no_length", "for (int bb = 0; bb < B; ++bb) kv_out[bb] = kv_len[bb] + n_keep[bb];",
      "for (int bb = 0; bb < B; ++bb) kv_out[bb] = kv_len[bb];"),
     ("rollback_all_rows", "if (n > T) n = T;", "n = T;"),
+    ("logprob_no_shift_in_sum", "for (int n = 0; n < N; ++n) s += exp(row[n] - m);",
+     "for (int n = 0; n < N; ++n) s += exp(row[n]);"),
+    ("logprob_first_index", "lp[r] = (row[ids[r]] - m) - log(s);", "lp[r] = (row[0] - m) - log(s);"),
+    ("logprob_sign", "lp[r] = (row[ids[r]] - m) - log(s);", "lp[r] = (row[ids[r]] - m) + log(s);"),
 ]
 
 

@@ -417,3 +417,37 @@ def test_greedy_ties_and_acceptance():
                     break
                 acc += 1
             assert n[bb] == acc + 1
+
+
+# ---------------------------------------------------------------------------
+# Logprob of the chosen token (log-softmax at an index)
+# ---------------------------------------------------------------------------
+def test_logprob_closed_forms():
+    N = 37
+    # equal logits (not zero, so that a missing max shift shows): every index has -ln N
+    z = np.full((1, 2, N), 3.25)
+    ids = np.array([[0, 17]], np.int32)
+    assert np.allclose(oracle.logprob(z, ids), -np.log(N), rtol=0, atol=1e-14)
+    # one logit raised by D over the rest: closed forms at the raised index and elsewhere
+    D = 2.5
+    z = np.full((1, 2, N), -1.0)
+    z[0, :, 5] += D
+    lp = oracle.logprob(z, np.array([[5, 9]], np.int32))
+    top = -np.log1p((N - 1) * np.exp(-D))
+    assert abs(lp[0, 0] - top) < 1e-14 and abs(lp[0, 1] - (top - D)) < 1e-14
+
+
+def test_logprob_normalises_and_is_shift_invariant():
+    rng = np.random.default_rng(3)
+    B, T, N = 2, 3, 50
+    z = rng.standard_normal((B, T, N)) * 4.0
+    full = np.stack([oracle.logprob(z, np.full((B, T), n, np.int32)) for n in range(N)], axis=-1)
+    assert np.allclose(np.exp(full).sum(-1), 1.0, rtol=0, atol=1e-13)
+    # the differences between indices are the logit differences
+    assert np.allclose(full - full[..., :1], z - z[..., :1], rtol=0, atol=1e-12)
+    shifted = np.stack([oracle.logprob(z + 100.0, np.full((B, T), n, np.int32)) for n in range(N)], axis=-1)
+    assert np.allclose(shifted, full, rtol=0, atol=1e-12)
+    # each row is its own: permuting the rows permutes the results
+    zp = z[::-1].copy()
+    assert np.array_equal(oracle.logprob(zp, np.full((B, T), 7, np.int32)),
+                          oracle.logprob(z, np.full((B, T), 7, np.int32))[::-1])
