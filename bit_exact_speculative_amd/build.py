@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libxv.so")
-SOURCES = ["xv_api.hip", "xv_gemm.hip", "xv_gdn.hip", "xv_attn.hip", "xv_greedy.hip"]
+SOURCES = ["xv_api.hip", "xv_gemm.hip", "xv_gdn.hip", "xv_attn.hip", "xv_greedy.hip", "xv_compose.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

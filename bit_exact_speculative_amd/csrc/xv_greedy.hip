@@ -8,8 +8,8 @@
 //
 // Two kernels on the caller's stream: one workgroup per verify row reduces the
 // row (running (value, index) per thread over a strided slice, then lane
-// shuffles and LDS across the waves), then one thread per request counts the
-// accepted drafts.
+// shuffles and LDS across the waves) and optionally forms the id's logprob,
+// then one thread per request counts the accepted drafts.
 #include "xv_common.h"
 
 namespace {
@@ -23,63 +23,67 @@ __device__ __forceinline__ bool xv_better(float v1, int n1, float v0, int n0) {
     return v1 > v0 || (v1 == v0 && n1 < n0);
 }
 
-// One workgroup per verify row (grid T x B): argmax of the row's logits.
-// VEC: 16-byte loads (rows 16-byte aligned, N % 4 == 0); otherwise 4-byte loads.
-// Indices past the row re-read its last element and are masked out.
+// One workgroup per verify row (grid T x B): argmax of the row's logits and,
+// when lp is given, the logprob of that id.  Thread t owns the 4-element groups
+// t, t + 256, t + 512, ... of the row (elements 4v .. 4v + 3 of group v), with
+// 16-byte loads (VEC: rows 16-byte aligned, N % 4 == 0) or 4-byte loads; the
+// ownership and every order below are the same either way, and indices past
+// the row re-read its last element and are masked out.
+//
+// Logprob of the argmax (post, first paragraph: logprobs compared as well as
+// ids): with m the row maximum, lp = -ln(sum_n e^(z_n - m)), each term
+// 2^((z_n - m) * log2 e); the sum runs over the thread's groups in order and
+// the 4 elements of a group in order, then a lane butterfly (each level adds
+// two equal-order partials, so all lanes agree) and the 4 waves' partials left
+// to right.  None of it depends on T, B or the other rows.
+template <bool VEC>
+__device__ __forceinline__ void xv_row_groups(const float* __restrict__ la, const float* __restrict__ lb,
+                                              size_t row, int N, int v, float (&x)[4]) {
+    const int G = (N + 3) >> 2;
+    const int vc = v < G ? v : G - 1;
+    if (VEC) {
+        const float4 va = reinterpret_cast<const float4*>(la + row)[vc];
+        float4 vb = va;
+        if (lb) vb = reinterpret_cast<const float4*>(lb + row)[vc];
+        x[0] = va.x; x[1] = va.y; x[2] = va.z; x[3] = va.w;
+        if (lb) { x[0] = x[0] + vb.x; x[1] = x[1] + vb.y; x[2] = x[2] + vb.z; x[3] = x[3] + vb.w; }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = 4 * vc + j;
+            const int nc = n < N ? n : N - 1;
+            x[j] = la[row + nc];
+            if (lb) x[j] = x[j] + lb[row + nc];
+        }
+    }
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(XV_GREEDY_THREADS)
 void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb, int T, int N,
-                      int32_t* __restrict__ ids)
+                      int32_t* __restrict__ ids, float* __restrict__ lp)
 {
     __shared__ float sv[XV_GREEDY_WAVES];
     __shared__ int sn[XV_GREEDY_WAVES];
+    __shared__ float smax;
     const int t = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x;
     const size_t row = ((size_t)b * T + t) * N;
+    const int G = (N + 3) >> 2;
+    constexpr int STEP = XV_GREEDY_THREADS * XV_GREEDY_UNROLL;
     float best = -INFINITY;
     int bn = N;                                  // sentinel: after every real index
-    if (VEC) {
-        const float4* pa = reinterpret_cast<const float4*>(la + row);
-        const float4* pb = reinterpret_cast<const float4*>(lb ? lb + row : la + row);
-        const int N4 = N >> 2;
-        for (int v0 = tid; v0 < N4; v0 += XV_GREEDY_THREADS * XV_GREEDY_UNROLL) {
-            float4 va[XV_GREEDY_UNROLL], vb[XV_GREEDY_UNROLL];
+    for (int v0 = tid; v0 < G; v0 += STEP) {
+        float x[XV_GREEDY_UNROLL][4];
 #pragma unroll
-            for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
-                const int v = v0 + u * XV_GREEDY_THREADS;
-                const int vc = v < N4 ? v : N4 - 1;
-                va[u] = pa[vc];
-                vb[u] = pb[vc];
-            }
+        for (int u = 0; u < XV_GREEDY_UNROLL; ++u) xv_row_groups<VEC>(la, lb, row, N, v0 + u * XV_GREEDY_THREADS, x[u]);
 #pragma unroll
-            for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
-                const int v = v0 + u * XV_GREEDY_THREADS;
-                if (v < N4) {
-                    float4 x = va[u];
-                    if (lb) { x.x = x.x + vb[u].x; x.y = x.y + vb[u].y; x.z = x.z + vb[u].z; x.w = x.w + vb[u].w; }
-                    const int n = 4 * v;
-                    if (xv_better(x.x, n, best, bn)) { best = x.x; bn = n; }
-                    if (xv_better(x.y, n + 1, best, bn)) { best = x.y; bn = n + 1; }
-                    if (xv_better(x.z, n + 2, best, bn)) { best = x.z; bn = n + 2; }
-                    if (xv_better(x.w, n + 3, best, bn)) { best = x.w; bn = n + 3; }
-                }
-            }
-        }
-    } else {
-        for (int n0 = tid; n0 < N; n0 += XV_GREEDY_THREADS * XV_GREEDY_UNROLL) {
-            float va[XV_GREEDY_UNROLL], vb[XV_GREEDY_UNROLL];
+        for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
+            const int v = v0 + u * XV_GREEDY_THREADS;
 #pragma unroll
-            for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
-                const int n = n0 + u * XV_GREEDY_THREADS;
-                const int nc = n < N ? n : N - 1;
-                va[u] = la[row + nc];
-                vb[u] = lb ? lb[row + nc] : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
-                const int n = n0 + u * XV_GREEDY_THREADS;
-                const float x = lb ? va[u] + vb[u] : va[u];
-                if (n < N && xv_better(x, n, best, bn)) { best = x; bn = n; }
+            for (int j = 0; j < 4; ++j) {
+                const int n = 4 * v + j;
+                if (v < G && n < N && xv_better(x[u][j], n, best, bn)) { best = x[u][j]; bn = n; }
             }
         }
     }
@@ -95,6 +99,37 @@ void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb
         for (int w = 1; w < XV_GREEDY_WAVES; ++w)
             if (xv_better(sv[w], sn[w], best, bn)) { best = sv[w]; bn = sn[w]; }
         ids[(size_t)b * T + t] = bn < N ? bn : 0;
+        smax = best;
+    }
+    if (!lp) return;                             // uniform
+    __syncthreads();
+    const float m = smax;
+    constexpr float LOG2E = 1.4426950408889634f;
+    float s = 0.f;
+    for (int v0 = tid; v0 < G; v0 += STEP) {
+        float x[XV_GREEDY_UNROLL][4];
+#pragma unroll
+        for (int u = 0; u < XV_GREEDY_UNROLL; ++u) xv_row_groups<VEC>(la, lb, row, N, v0 + u * XV_GREEDY_THREADS, x[u]);
+#pragma unroll
+        for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
+            const int v = v0 + u * XV_GREEDY_THREADS;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float e = __builtin_amdgcn_exp2f((x[u][j] - m) * LOG2E);
+                s = (v < G && 4 * v + j < N) ? s + e : s;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s = s + __shfl_xor(s, off);
+    __syncthreads();                             // sv is reused
+    if ((tid & 63) == 0) sv[tid >> 6] = s;
+    __syncthreads();
+    if (tid == 0) {
+        float tot = sv[0];
+        for (int w = 1; w < XV_GREEDY_WAVES; ++w) tot = tot + sv[w];
+        constexpr float LN2 = 0.6931471805599453f;
+        lp[(size_t)b * T + t] = -(__builtin_amdgcn_logf(tot) * LN2);
     }
 }
 
@@ -125,20 +160,21 @@ __global__ void xv_accept_kernel(const int32_t* __restrict__ draft, const int32_
 }  // namespace
 
 extern "C" int xv_greedy_accept(const float* logits_a, const float* logits_b, const int32_t* draft,
-                                int B, int T, int N, int32_t* ids, int32_t* n_keep, void* stream)
+                                int B, int T, int N, int32_t* ids, int32_t* n_keep, float* logprob,
+                                void* stream)
 {
     XV_REQUIRE(B >= 0 && T >= 1 && T <= XV_TMAX && N >= 1, XV_ERR_SHAPE);
     if (B == 0) return XV_OK;
     XV_REQUIRE(logits_a && draft && ids && n_keep, XV_ERR_NULL);
     XV_REQUIRE(xv_aligned(logits_a, 4) && xv_aligned(logits_b, 4) && xv_aligned(draft, 4) &&
-               xv_aligned(ids, 4) && xv_aligned(n_keep, 4), XV_ERR_ALIGN);
+               xv_aligned(ids, 4) && xv_aligned(n_keep, 4) && xv_aligned(logprob, 4), XV_ERR_ALIGN);
     (void)hipGetLastError();
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     // 16-byte loads when every row starts 16-byte aligned; the argmax is the same either way
     const bool vec = (N % 4 == 0) && xv_aligned16(logits_a) && xv_aligned16(logits_b);
     const dim3 grid(T, B), block(XV_GREEDY_THREADS);
-    if (vec) hipLaunchKernelGGL(xv_argmax_kernel<true>, grid, block, 0, st, logits_a, logits_b, T, N, ids);
-    else hipLaunchKernelGGL(xv_argmax_kernel<false>, grid, block, 0, st, logits_a, logits_b, T, N, ids);
+    if (vec) hipLaunchKernelGGL(xv_argmax_kernel<true>, grid, block, 0, st, logits_a, logits_b, T, N, ids, logprob);
+    else hipLaunchKernelGGL(xv_argmax_kernel<false>, grid, block, 0, st, logits_a, logits_b, T, N, ids, logprob);
     const int s1 = xv_launch_status();
     if (s1 != XV_OK) return s1;
     hipLaunchKernelGGL(xv_accept_kernel, dim3((B + 63) / 64), dim3(64), 0, st, draft, ids, B, T, n_keep);

@@ -1,0 +1,174 @@
+"""Greedy decoding of one synthetic hybrid layer on the GPU, with or without
+speculative verification, built from libxv calls only.
+
+A decoding step consumes tokens[b] = [root, draft_1 .. draft_k] (k = 0: plain
+decoding) and runs, on one stream:
+
+  xv_embed_rows         x = E[tokens]
+  xv_gemm_small_m (x2)  y1 = x W1^T, y2 = x W2^T
+  xv_split_projections  GDN q, k (L2-normalised), v, decay, beta; attention q, k, v
+  xv_gdn_verify         GDN rows, S_in -> S_T
+  xv_attn_verify_rows   attention rows, KV append
+  xv_gemm_small_m (x2)  head logits from o_gdn and o_attn
+  xv_greedy_accept      ids, logprobs, accepted rows
+  xv_rollback_to_prefix state and KV length of the kept rows
+
+and emits ids[b][0 .. n_keep[b]-1]; the last one is the next root.  The post's
+claim (first paragraph; the paragraph on the two verify changes) is that the
+emitted ids and logprobs do not depend on k or on the drafts; the tests check
+that bit for bit.  Torch provides device memory and the stream only.
+"""
+from __future__ import annotations
+
+from typing import Callable, Optional
+
+import numpy as np
+import torch
+
+from . import xv
+from .inputs import Inputs, PREFIX_TOKENS
+
+
+def _bf16(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def prefix_state(inp: Inputs, device, stream=None) -> torch.Tensor:
+    """The GDN state after the workload's 32 prefix tokens from a zero state (GPU path)."""
+    wl, p = inp.wl, inp.prefix
+    B = wl.B
+    S = torch.zeros((B, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device=device)
+    S2 = torch.empty_like(S)
+    t0 = 0
+    while t0 < PREFIX_TOKENS:
+        tt = min(16, PREFIX_TOKENS - t0)
+        sl = slice(t0, t0 + tt)
+        o = torch.empty((B, tt, wl.Hv, wl.dv), dtype=torch.bfloat16, device=device)
+        xv.xv_gdn_verify(_bf16(p["q"][:, sl], device), _bf16(p["k"][:, sl], device),
+                         _bf16(p["v"][:, sl], device),
+                         torch.from_numpy(np.ascontiguousarray(p["a"][:, sl])).to(device),
+                         torch.from_numpy(np.ascontiguousarray(p["b"][:, sl])).to(device),
+                         S, S2, o, None, stream=stream)
+        S, S2 = S2, S
+        t0 += tt
+    return S
+
+
+class _Rows:
+    """Device buffers for steps of T rows per request."""
+
+    def __init__(self, wl, T: int, Lmax: int, device):
+        B, M = wl.B, wl.B * T
+        e = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=device)
+        f = lambda *s: torch.empty(s, dtype=torch.float32, device=device)
+        self.T = T
+        self.tokens = torch.empty((B, T), dtype=torch.int32, device=device)
+        self.x = e(M, wl.K)
+        self.y1, self.y2 = e(M, wl.N1), e(M, wl.N2)
+        self.q, self.k = e(B, T, wl.Hk, wl.dk), e(B, T, wl.Hk, wl.dk)
+        self.v = e(B, T, wl.Hv, wl.dv)
+        self.a, self.b = f(B, T, wl.Hv), f(B, T, wl.Hv)
+        self.qa = e(B, T, wl.Hq, wl.d)
+        self.kn, self.vn = e(B, T, wl.Hkv, wl.d), e(B, T, wl.Hkv, wl.d)
+        self.o_gdn, self.o_attn = e(B, T, wl.Hv, wl.dv), e(B, T, wl.Hq, wl.d)
+        self.lg, self.la = e(M, wl.NH), e(M, wl.NH)
+        self.lg32, self.la32 = f(M, wl.NH), f(M, wl.NH)
+        self.ids = torch.empty((B, T), dtype=torch.int32, device=device)
+        self.lp = f(B, T)
+        self.n_keep = torch.empty((B,), dtype=torch.int32, device=device)
+        wsb = xv.xv_attn_workspace_bytes(B, T, wl.Hq, wl.d, Lmax)
+        self.ws = torch.empty((max(wsb, 16) + 15) // 16 * 4, dtype=torch.float32, device=device)
+
+
+class Decoder:
+    """The synthetic layer's weights and decoding state on one device.
+
+    inp: :func:`inputs.composed_inputs` (weights, embedding table, cached prefix).
+    S0: optional fp32 [B][Hv][dk][dv] start state (default: the prefix on the GPU).
+    Lmax: KV capacity (at least the cached length + every token decoded + one step).
+    """
+
+    def __init__(self, inp: Inputs, Lmax: int, device="cuda", S0: Optional[np.ndarray] = None, stream=None):
+        wl = inp.wl
+        self.wl, self.device, self.stream = wl, device, stream
+        if Lmax < inp.k_cache.shape[2]:
+            raise ValueError("Lmax below the inputs' cache capacity")
+        self.E = _bf16(inp.extra["E"], device)
+        self.W1, self.W2 = _bf16(inp.W1, device), _bf16(inp.W2, device)
+        self.Wh_g, self.Wh_a = _bf16(inp.Wh_gdn, device), _bf16(inp.Wh_attn, device)
+        B = wl.B
+        self.Kc = torch.zeros((B, wl.Hkv, Lmax, wl.d), dtype=torch.bfloat16, device=device)
+        self.Vc = torch.zeros_like(self.Kc)
+        L = inp.k_cache.shape[2]
+        self.Kc[:, :, :L] = _bf16(inp.k_cache, device)
+        self.Vc[:, :, :L] = _bf16(inp.v_cache, device)
+        self.kv_len = torch.from_numpy(inp.L0.astype(np.int32)).to(device)
+        if S0 is None:
+            self.S = prefix_state(inp, device, stream)
+        else:
+            self.S = torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).to(device)
+        self.S2 = torch.empty_like(self.S)
+        self.Lmax = Lmax
+        self.scale = 1.0 / float(wl.d) ** 0.5
+        self._rows = {}
+
+    def rows(self, T: int) -> _Rows:
+        if T not in self._rows:
+            self._rows[T] = _Rows(self.wl, T, self.Lmax, self.device)
+        return self._rows[T]
+
+    def step(self, tokens: torch.Tensor) -> _Rows:
+        """One decoding step over tokens int32 [B][T] (device); returns the row buffers,
+        whose ids, lp and n_keep hold the step's results.  The state advances to the kept rows."""
+        wl, st = self.wl, self.stream
+        B, T = tokens.shape
+        R = self.rows(T)
+        if tokens.data_ptr() != R.tokens.data_ptr():
+            R.tokens.copy_(tokens)
+        M = B * T
+        xv.xv_embed_rows(self.E, R.tokens, R.x, stream=st)
+        xv.xv_gemm_small_m(R.x, self.W1, R.y1, None, stream=st)
+        xv.xv_gemm_small_m(R.x, self.W2, R.y2, None, stream=st)
+        xv.xv_split_projections(R.y1, R.y2, R.q, R.k, R.v, R.a, R.b, R.qa, R.kn, R.vn, stream=st)
+        xv.xv_gdn_verify(R.q, R.k, R.v, R.a, R.b, self.S, self.S2, R.o_gdn, None, stream=st)
+        xv.xv_attn_verify_rows(R.qa, R.kn, R.vn, self.Kc, self.Vc, self.kv_len, R.o_attn, None, R.ws,
+                               self.scale, stream=st)
+        xv.xv_gemm_small_m(R.o_gdn.view(M, wl.Hv * wl.dv), self.Wh_g, R.lg, R.lg32, stream=st)
+        xv.xv_gemm_small_m(R.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, R.la, R.la32, stream=st)
+        xv.xv_greedy_accept(R.lg32.view(B, T, wl.NH), R.la32.view(B, T, wl.NH), R.tokens, R.ids,
+                            R.n_keep, R.lp, stream=st)
+        xv.xv_rollback_to_prefix(R.k, R.v, R.a, R.b, self.S, self.S2, self.kv_len, R.n_keep, stream=st)
+        self.S, self.S2 = self.S2, self.S
+        return R
+
+    def generate(self, root: np.ndarray, n_tokens: int,
+                 drafts: Optional[Callable[[int, int, int], np.ndarray]] = None, k: int = 0):
+        """Greedy decoding of n_tokens per request from root (int32 [B]); drafts(b, pos, k)
+        proposes k ids after request b's pos-th emitted token.  Reads each step's results
+        back to the host.  Returns (ids int32 [B][n], logprobs fp32 [B][n], per-step n_keep)."""
+        B = self.wl.B
+        out_ids = [[] for _ in range(B)]
+        out_lp = [[] for _ in range(B)]
+        keeps = []
+        cur = np.asarray(root, np.int32).copy()
+        while min(len(o) for o in out_ids) < n_tokens:
+            tok = np.empty((B, k + 1), np.int32)
+            tok[:, 0] = cur
+            for bb in range(B):
+                if k:
+                    tok[bb, 1:] = drafts(bb, len(out_ids[bb]), k)
+            R = self.rows(k + 1)
+            R.tokens.copy_(torch.from_numpy(tok))
+            self.step(R.tokens)
+            ids = R.ids.cpu().numpy()
+            lp = R.lp.cpu().numpy()
+            nk = R.n_keep.cpu().numpy()
+            keeps.append(nk.copy())
+            for bb in range(B):
+                n = int(nk[bb])
+                out_ids[bb].extend(int(i) for i in ids[bb, :n])
+                out_lp[bb].extend(float(x) for x in lp[bb, :n])
+                cur[bb] = ids[bb, n - 1]
+        ids = np.array([o[:n_tokens] for o in out_ids], np.int32)
+        lps = np.array([o[:n_tokens] for o in out_lp], np.float32)
+        return ids, lps, keeps

@@ -8,7 +8,7 @@ KV cache, the verify rows) and runs, on one stream:
               GDN verify S_in -> S_out, o_gdn    (xv_gdn_verify)
               attention rows + KV append         (xv_attn_verify_rows)
               synthetic head logits              (xv_gemm_small_m on o_gdn and o_attn)
-              greedy ids and accepted rows       (xv_greedy_accept)
+              greedy ids, logprobs, accepted rows (xv_greedy_accept)
               rollback to the accepted prefix    (xv_rollback_to_prefix)
   decode_sequence()  the same layer advanced one token at a time (T = 1, M = B)
               over the same rows, which verify must reproduce bit for bit.
@@ -104,6 +104,7 @@ class Layer:
             self.la32 = torch.empty((M, wl.NH), dtype=torch.float32, device=device)
             self.draft = dev(inp.draft, device)
             self.ids = torch.empty((B, T), dtype=torch.int32, device=device)
+            self.lp = torch.empty((B, T), dtype=torch.float32, device=device)
         self.n_keep = torch.full((B,), T, dtype=torch.int32, device=device)
         self.proj_fp32 = True        # also write the fp32 projection outputs
         self.out_fp32 = True         # also write the fp32 GDN / attention outputs
@@ -172,7 +173,7 @@ class Layer:
     def greedy(self):
         wl = self.wl
         xv.xv_greedy_accept(self.lg32.view(self.B, self.T, wl.NH), self.la32.view(self.B, self.T, wl.NH),
-                            self.draft, self.ids, self.n_keep, stream=self.stream)
+                            self.draft, self.ids, self.n_keep, self.lp, stream=self.stream)
 
     def head(self):
         self.head_gemms()
@@ -220,7 +221,7 @@ class Layer:
         wsb = xv.xv_attn_workspace_bytes(B, 1, wl.Hq, wl.d, self.Lmax)
         ws = torch.empty((max(wsb, 16) + 15) // 16 * 4, dtype=torch.float32, device=d)
         out = {k: [] for k in ("o_gdn", "o_gdn32", "S", "o_attn", "o_attn32", "kv_len",
-                               "y1", "y1_32", "y2", "y2_32", "lg32", "la32", "ids")}
+                               "y1", "y1_32", "y2", "y2_32", "lg32", "la32", "ids", "lp")}
         for t in range(n):
             sl = slice(t, t + 1)
             q, k, v = self.q[:, sl].contiguous(), self.k[:, sl].contiguous(), self.v[:, sl].contiguous()
@@ -259,9 +260,11 @@ class Layer:
                 xv.xv_gemm_small_m(oa.view(B, wl.Hq * wl.d), self.Wh_a, la, la32, stream=st)
                 ids = torch.empty((B, 1), dtype=torch.int32, device=d)
                 nk = torch.empty((B,), dtype=torch.int32, device=d)
+                lp = torch.empty((B, 1), dtype=torch.float32, device=d)
                 dr = self.draft[:, sl].contiguous()
-                xv.xv_greedy_accept(lg32.view(B, 1, wl.NH), la32.view(B, 1, wl.NH), dr, ids, nk, stream=st)
+                xv.xv_greedy_accept(lg32.view(B, 1, wl.NH), la32.view(B, 1, wl.NH), dr, ids, nk, lp, stream=st)
                 out["lg32"].append(lg32); out["la32"].append(la32); out["ids"].append(ids[:, 0].clone())
+                out["lp"].append(lp[:, 0].clone())
         res = {}
         for kname, vals in out.items():
             if vals:

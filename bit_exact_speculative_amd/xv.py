@@ -49,7 +49,11 @@ _lib.xv_attn_verify_rows.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
 _lib.xv_rollback_to_prefix.restype = _I
 _lib.xv_rollback_to_prefix.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
 _lib.xv_greedy_accept.restype = _I
-_lib.xv_greedy_accept.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P]
+_lib.xv_greedy_accept.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P]
+_lib.xv_embed_rows.restype = _I
+_lib.xv_embed_rows.argtypes = [_P, _P, _I, _I, _I, _P, _P]
+_lib.xv_split_projections.restype = _I
+_lib.xv_split_projections.argtypes = [_P, _P, _I, _I, _I] + [_I] * 7 + [_P] * 8 + [_P]
 
 XV_OK = 0
 STATUS = {0: "XV_OK", -1: "XV_ERR_NULL", -2: "XV_ERR_SHAPE", -3: "XV_ERR_ALIGN",
@@ -187,11 +191,43 @@ def xv_rollback_to_prefix(k, v, a, b, state_in, state_out, kv_len, n_keep, strea
         _ptr(n_keep), B, T, Hk, Hv, dk, dv, _stream(stream)))
 
 
-def xv_greedy_accept(logits_a, logits_b, draft, ids, n_keep, stream=None):
-    """ids = argmax(logits_a + logits_b) per row (lowest index on ties); n_keep per request."""
+def xv_greedy_accept(logits_a, logits_b, draft, ids, n_keep, logprob=None, stream=None):
+    """ids = argmax(logits_a + logits_b) per row (lowest index on ties); n_keep per request;
+    logprob (optional fp32 [B][T]) = log-softmax of each row at its id."""
     B, T, N = logits_a.shape
     if (logits_b is not None and tuple(logits_b.shape) != (B, T, N)) or tuple(draft.shape) != (B, T) \
-            or tuple(ids.shape) != (B, T) or tuple(n_keep.shape) != (B,):
+            or tuple(ids.shape) != (B, T) or tuple(n_keep.shape) != (B,) or \
+            (logprob is not None and tuple(logprob.shape) != (B, T)):
         raise ValueError("xv_greedy_accept: shape mismatch")
     _check("xv_greedy_accept", _lib.xv_greedy_accept(_ptr(logits_a), _ptr(logits_b), _ptr(draft),
-                                                    B, T, N, _ptr(ids), _ptr(n_keep), _stream(stream)))
+                                                    B, T, N, _ptr(ids), _ptr(n_keep), _ptr(logprob),
+                                                    _stream(stream)))
+
+
+def xv_embed_rows(table, tokens, x, stream=None):
+    """x[m] = table[tokens[m]] (bf16 rows).  table [V][H]; tokens int32 [M] (any shape of M ids)."""
+    V, H = table.shape
+    M = tokens.numel()
+    if tuple(x.shape) != (M, H):
+        raise ValueError("xv_embed_rows: shape mismatch")
+    _check("xv_embed_rows", _lib.xv_embed_rows(_ptr(table), _ptr(tokens), M, V, H, _ptr(x),
+                                              _stream(stream)))
+
+
+def xv_split_projections(y1, y2, q, k, v, a, b, q_attn, k_new, v_new, stream=None):
+    """Per-head operands from the projection rows y1 [M][N1], y2 [M][N2]; outputs are
+    [M][heads][dim] (or the same memory as [B][T][heads][dim]); a, b fp32 [M][Hv]."""
+    M, N1 = y1.shape
+    N2 = y2.shape[1]
+    Hk, dk = q.shape[-2], q.shape[-1]
+    Hv, dv = v.shape[-2], v.shape[-1]
+    Hq, d = q_attn.shape[-2], q_attn.shape[-1]
+    Hkv = k_new.shape[-2]
+    if y2.shape[0] != M or q.numel() != M * Hk * dk or k.numel() != M * Hk * dk or \
+            v.numel() != M * Hv * dv or a.numel() != M * Hv or b.numel() != M * Hv or \
+            q_attn.numel() != M * Hq * d or k_new.numel() != M * Hkv * d or v_new.numel() != M * Hkv * d:
+        raise ValueError("xv_split_projections: shape mismatch")
+    _check("xv_split_projections", _lib.xv_split_projections(
+        _ptr(y1), _ptr(y2), M, N1, N2, Hk, Hv, dk, dv, Hq, Hkv, d,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(q_attn), _ptr(k_new), _ptr(v_new),
+        _stream(stream)))

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define XV_ABI_VERSION 1
+#define XV_ABI_VERSION 2
 
 typedef enum {
     XV_OK = 0,
@@ -175,18 +175,55 @@ int xv_rollback_to_prefix(const uint16_t* k, const uint16_t* v,
 
 /*
  * Greedy acceptance at temperature 0 on device (the post compares token ids of
- * greedy decoding).  logits[b][t][n] = logits_a[...] + logits_b[...] (one fp32
- * add; logits_b may be NULL).  ids[b][t] = the lowest n among the maxima of row
- * (b, t).  Row t consumed input token draft[b][t] (draft[b][0] is the root);
- * draft t+1 is accepted when it equals ids[b][t] and all earlier drafts were
- * accepted.  n_keep[b] = 1 + accepted drafts (the verify rows to keep, ready
- * for xv_rollback_to_prefix).
+ * greedy decoding, and their logprobs).  logits[b][t][n] = logits_a[...] +
+ * logits_b[...] (one fp32 add; logits_b may be NULL).  ids[b][t] = the lowest n
+ * among the maxima of row (b, t).  Row t consumed input token draft[b][t]
+ * (draft[b][0] is the root); draft t+1 is accepted when it equals ids[b][t] and
+ * all earlier drafts were accepted.  n_keep[b] = 1 + accepted drafts (the verify
+ * rows to keep, ready for xv_rollback_to_prefix).  logprob (may be NULL):
+ * logprob[b][t] = log softmax(logits[b][t])[ids[b][t]] = -ln sum_n e^(z_n - max z),
+ * fp32, in an order fixed by N alone (not by B, T or the pointers' alignment).
  *   logits_a, logits_b : fp32 [B][T][N]     draft : int32 [B][T]
- *   ids : int32 [B][T]   n_keep : int32 [B]
+ *   ids : int32 [B][T]   n_keep : int32 [B]   logprob : fp32 [B][T] or NULL
  * Shapes: B >= 0, 1 <= T <= 16, N >= 1.  Logits must be finite.
  */
 int xv_greedy_accept(const float* logits_a, const float* logits_b, const int32_t* draft,
-                     int B, int T, int N, int32_t* ids, int32_t* n_keep, void* stream);
+                     int B, int T, int N, int32_t* ids, int32_t* n_keep, float* logprob,
+                     void* stream);
+
+/*
+ * Token embedding rows in front of the projection GEMMs of a decoding step
+ * (the post's claim is about whole decoding steps: ids and logprobs of greedy
+ * decoding with and without speculation).  x[m][:] = table[tokens[m]][:], a bit
+ * copy; ids outside [0, V) are clamped (a precondition the host cannot check).
+ *   table  : bf16 [V][H]  [16B]      tokens : int32 [M] device
+ *   x      : bf16 [M][H]  [16B]
+ * Shapes: M >= 0, V >= 1, H >= 8 and H % 8 == 0.
+ */
+int xv_embed_rows(const uint16_t* table, const int32_t* tokens, int M, int V, int H,
+                  uint16_t* x, void* stream);
+
+/*
+ * The per-head operands of the verify calls from the projection rows of one
+ * layer (the synthetic layer's column layout; the pages name the model, not
+ * its tensors).  Row m of each output depends on row m of y1 and y2 only.
+ *   y1 : bf16 [M][N1] [16B]  columns GDN q (Hk*dk) | GDN k (Hk*dk) | GDN v (Hv*dv) | unused
+ *   y2 : bf16 [M][N2] [16B]  columns attention q (Hq*d) | k (Hkv*d) | v (Hkv*d) |
+ *                            decay logit (Hv) | beta logit (Hv) | unused
+ *   q, k   : bf16 [M][Hk][dk] [16B]  u / sqrt(sum u^2 + 1e-6) per head (fp32, fixed order),
+ *                                    rounded to nearest even
+ *   v      : bf16 [M][Hv][dv] [16B]  a copy
+ *   a, b   : fp32 [M][Hv]            a = 1 / (1 + e^alpha) (= exp(-softplus(alpha))),
+ *                                    b = 1 / (1 + e^-beta)
+ *   q_attn : bf16 [M][Hq][d] [16B], k_new, v_new : bf16 [M][Hkv][d] [16B]  copies
+ * With M = B*T these are the [B][T][...] inputs of xv_gdn_verify and
+ * xv_attn_verify_rows.  Shapes: M >= 0, dk in {64, 128}, dv and d multiples of
+ * 8, N1 and N2 multiples of 8, N1 >= 2*Hk*dk + Hv*dv, N2 >= Hq*d + 2*Hkv*d + 2*Hv.
+ */
+int xv_split_projections(const uint16_t* y1, const uint16_t* y2, int M, int N1, int N2,
+                         int Hk, int Hv, int dk, int dv, int Hq, int Hkv, int d,
+                         uint16_t* q, uint16_t* k, uint16_t* v, float* a, float* b,
+                         uint16_t* q_attn, uint16_t* k_new, uint16_t* v_new, void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ def test_every_header_symbol_is_exported(xv):
     assert set(names) >= {"xv_gemm_small_m", "xv_gdn_verify", "xv_attn_verify_rows",
                           "xv_rollback_to_prefix", "xv_attn_workspace_bytes",
                           "xv_attn_chunk_tokens", "xv_abi_version", "xv_status_string",
-                          "xv_greedy_accept"}
+                          "xv_greedy_accept", "xv_embed_rows", "xv_split_projections"}
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -35,7 +35,7 @@ def test_every_header_symbol_is_exported(xv):
 
 
 def test_version_and_constants(xv):
-    assert xv.xv_abi_version() == 1
+    assert xv.xv_abi_version() == 2
     assert xv.xv_attn_chunk_tokens() == 256
     lib = xv.lib()
     assert lib.xv_status_string(0) == b"ok"
@@ -104,11 +104,37 @@ def test_attn_argument_errors(xv):
 
 def test_greedy_argument_errors(xv):
     f = xv.lib().xv_greedy_accept
-    assert f(A, None, A, 0, 9, 4096, A, A, None) == 0
-    assert f(A, None, A, 1, 0, 4096, A, A, None) == -2
-    assert f(A, None, A, 1, 9, 0, A, A, None) == -2
-    assert f(None, None, A, 1, 9, 4096, A, A, None) == -1
-    assert f(A, ODD, A, 1, 9, 4096, A, A, None) == -3
+    assert f(A, None, A, 0, 9, 4096, A, A, None, None) == 0
+    assert f(A, None, A, 1, 0, 4096, A, A, None, None) == -2
+    assert f(A, None, A, 1, 9, 0, A, A, None, None) == -2
+    assert f(None, None, A, 1, 9, 4096, A, A, None, None) == -1
+    assert f(A, ODD, A, 1, 9, 4096, A, A, None, None) == -3
+    assert f(A, None, A, 1, 9, 4096, A, A, A + 2, None) == -3     # logprob: fp32 alignment
+
+
+def test_embed_and_split_argument_errors(xv):
+    e = xv.lib().xv_embed_rows
+    assert e(A, A, 0, 4096, 5120, A, None) == 0
+    assert e(A, A, 9, 0, 5120, A, None) == -2 and e(A, A, 9, 4096, 5124, A, None) == -2
+    assert e(None, A, 9, 4096, 5120, A, None) == -1 and e(A, A, 9, 4096, 5120, None, None) == -1
+    assert e(MIS, A, 9, 4096, 5120, A, None) == -3 and e(A, A + 2, 9, 4096, 5120, A, None) == -3
+    s = xv.lib().xv_split_projections
+    ok = dict(M=9, N1=10240, N2=17408, Hk=16, Hv=48, dk=128, dv=128, Hq=24, Hkv=4, d=256)
+
+    def call(ptrs=None, **kw):
+        a = dict(ok); a.update(kw)
+        p = [A] * 10 if ptrs is None else ptrs
+        return s(p[0], p[1], a["M"], a["N1"], a["N2"], a["Hk"], a["Hv"], a["dk"], a["dv"],
+                 a["Hq"], a["Hkv"], a["d"], *p[2:], None)
+
+    assert call(M=0) == 0
+    assert call(dk=96) == -2 and call(dv=12) == -2 and call(d=20) == -2
+    assert call(N1=10232) == -2                       # too few columns for q, k, v
+    assert call(N2=8280) == -2                        # 6144 + 2048 + 96 = 8288 needed
+    assert call(N1=10244) == -2                       # rows must stay 16-byte aligned
+    assert call(ptrs=[A] * 9 + [None]) == -1
+    assert call(ptrs=[MIS] + [A] * 9) == -3
+    assert call(ptrs=[A] * 5 + [A + 2] + [A] * 4) == -3  # a: fp32 alignment
 
 
 def test_product_path_does_not_touch_the_oracle():

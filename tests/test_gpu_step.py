@@ -33,6 +33,7 @@ def _check_verify_equals_decode(L, dec, n_rows=None):
         assert same_bits(L.lg32.view(B, T, -1)[:, :n], dec["lg32"])
         assert same_bits(L.la32.view(B, T, -1)[:, :n], dec["la32"])
         assert torch.equal(L.ids[:, :n], dec["ids"])
+        assert same_bits(L.lp[:, :n], dec["lp"])
 
 
 def _oracle_ids_consistent(L, inp, S0):
