@@ -118,15 +118,14 @@ class Decoder:
         return self._rows[T]
 
     def step(self, tokens: torch.Tensor) -> _Rows:
-        """One decoding step over tokens int32 [B][T] (device); returns the row buffers,
-        whose ids, lp and n_keep hold the step's results.  The state advances to the kept rows."""
+        """One decoding step over tokens, a contiguous int32 [B][T] device tensor (read in
+        place); returns the row buffers, whose ids, lp and n_keep hold the step's results.
+        The state advances to the kept rows."""
         wl, st = self.wl, self.stream
         B, T = tokens.shape
         R = self.rows(T)
-        if tokens.data_ptr() != R.tokens.data_ptr():
-            R.tokens.copy_(tokens)
         M = B * T
-        xv.xv_embed_rows(self.E, R.tokens, R.x, stream=st)
+        xv.xv_embed_rows(self.E, tokens, R.x, stream=st)
         xv.xv_gemm_small_m(R.x, self.W1, R.y1, None, stream=st)
         xv.xv_gemm_small_m(R.x, self.W2, R.y2, None, stream=st)
         xv.xv_split_projections(R.y1, R.y2, R.q, R.k, R.v, R.a, R.b, R.qa, R.kn, R.vn, stream=st)
@@ -135,17 +134,27 @@ class Decoder:
                                self.scale, stream=st)
         xv.xv_gemm_small_m(R.o_gdn.view(M, wl.Hv * wl.dv), self.Wh_g, R.lg, R.lg32, stream=st)
         xv.xv_gemm_small_m(R.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, R.la, R.la32, stream=st)
-        xv.xv_greedy_accept(R.lg32.view(B, T, wl.NH), R.la32.view(B, T, wl.NH), R.tokens, R.ids,
+        xv.xv_greedy_accept(R.lg32.view(B, T, wl.NH), R.la32.view(B, T, wl.NH), tokens, R.ids,
                             R.n_keep, R.lp, stream=st)
         xv.xv_rollback_to_prefix(R.k, R.v, R.a, R.b, self.S, self.S2, self.kv_len, R.n_keep, stream=st)
         self.S, self.S2 = self.S2, self.S
         return R
 
+    def snapshot(self):
+        """Copies of the decoding state (GDN state, KV cache, lengths)."""
+        return (self.S.clone(), self.Kc.clone(), self.Vc.clone(), self.kv_len.clone())
+
+    def restore(self, snap):
+        S, Kc, Vc, kv = snap
+        self.S.copy_(S); self.Kc.copy_(Kc); self.Vc.copy_(Vc); self.kv_len.copy_(kv)
+
     def generate(self, root: np.ndarray, n_tokens: int,
-                 drafts: Optional[Callable[[int, int, int], np.ndarray]] = None, k: int = 0):
+                 drafts: Optional[Callable[[int, int, int], np.ndarray]] = None, k: int = 0,
+                 record: Optional[list] = None):
         """Greedy decoding of n_tokens per request from root (int32 [B]); drafts(b, pos, k)
         proposes k ids after request b's pos-th emitted token.  Reads each step's results
-        back to the host.  Returns (ids int32 [B][n], logprobs fp32 [B][n], per-step n_keep)."""
+        back to the host.  Returns (ids int32 [B][n], logprobs fp32 [B][n], per-step n_keep);
+        record, when given, receives each step's input tokens (int32 [B][k+1])."""
         B = self.wl.B
         out_ids = [[] for _ in range(B)]
         out_lp = [[] for _ in range(B)]
@@ -157,6 +166,8 @@ class Decoder:
             for bb in range(B):
                 if k:
                     tok[bb, 1:] = drafts(bb, len(out_ids[bb]), k)
+            if record is not None:
+                record.append(tok.copy())
             R = self.rows(k + 1)
             R.tokens.copy_(torch.from_numpy(tok))
             self.step(R.tokens)
