@@ -3,12 +3,12 @@
 
 One step is the whole hot path of a speculative step for one layer, on one
 stream, with every input already resident in HBM:
-    qkv-sized projection GEMM  (M = B*T rows, K = 5120, N = 10240)   xv_gemm_small_m
-    MLP-sized projection GEMM  (M = B*T rows, K = 5120, N = 17408)   xv_gemm_small_m
+    both projection GEMMs in one launch                              xv_gemm_small_m_pair
+      (M = B*T rows, K = 5120, N = 10240 and N = 17408)
     GDN verify, 48 value heads, fp32 state                          xv_gdn_verify
     attention verify rows + KV append, 24 q / 4 KV heads, d = 256  xv_attn_verify_rows
-    synthetic head over both outputs (2 x 6144 -> 4096)             xv_gemm_small_m x 2
-    greedy ids and accepted rows                                    xv_greedy_accept
+    synthetic head over both outputs (2 x 6144 -> 4096, one launch) xv_gemm_small_m_pair
+    greedy ids, logprobs and accepted rows                          xv_greedy_accept
     rollback of state and length to the accepted prefix             xv_rollback_to_prefix
 The default workload is batch 1, k = 8 drafts (9 verify rows), 640 cached
 tokens.  Steps run as a real decoding loop: each step verifies against the
@@ -18,8 +18,9 @@ the 256 MB Infinity Cache cannot serve the weights of the step being timed.
 
 Before timing, verify == sequential decode is checked bit for bit on the same
 buffers; a mismatch reports no throughput.  The JSON line carries the roofline
-of the dominant kernel (the N = 17408 GEMM, timed live with HIP events that its
-launch records at the kernel's own start and end, on the stream it runs on) and the fp64 CPU oracle timed on the host.
+of the dominant kernel (the projection GEMM launch, timed live with HIP events
+that the launch records at the kernel's own start and end, on the stream it runs
+on) and the fp64 CPU oracle timed on the host.
 """
 from __future__ import annotations
 
@@ -36,7 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "verified draft tok/s per layer at k=8 (ctx 640/2.2k/128k); HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 GEMM_EVENT_EVERY = 8          # timed steps per live sample of the dominant GEMM
-PROFILE_PMC = os.path.join(ROOT, "profiles", "gemm_small_m_n17408_short_pmc.md")
+PROFILE_PMC = os.path.join(ROOT, "profiles", "gemm_pair_projections_short_pmc.md")
 GEMM_SOURCES = ["bit_exact_speculative_amd/csrc/xv_gemm.hip", "bit_exact_speculative_amd/csrc/xv_common.h"]
 
 
@@ -127,8 +128,7 @@ def run_steps(layers, stream, steps, warmup, keep_all=False, gemm_events=False):
     full = torch.full((layers[0].B,), layers[0].T, dtype=torch.int32, device="cuda") if keep_all else None
 
     def step(L, ev=None):
-        L.gemm1()
-        L.gemm2(ev)                               # ev: recorded at the kernel's own start and end
+        L.gemms(ev)                               # ev: recorded at the kernel's own start and end
         L.gdn()
         L.attn()
         L.head()
@@ -139,7 +139,7 @@ def run_steps(layers, stream, steps, warmup, keep_all=False, gemm_events=False):
         for s in range(warmup):
             step(layers[s % R])
         torch.cuda.synchronize()
-        # launch-recorded events on every GEMM_EVENT_EVERY-th step's N=17408 GEMM: a sample of
+        # launch-recorded events on every GEMM_EVENT_EVERY-th step's projection launch: a sample of
         # the timed launches, so that the events' own cost (~4.5 us per event-carrying step)
         # stays out of the step time
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -285,13 +285,13 @@ def main():
 
     breakdown = None
     if args.breakdown:
-        names = ["gemm_n%d" % wl.N1, "gemm_n%d" % wl.N2, "gdn_verify", "attn_verify_rows",
+        names = ["projections_n%d_n%d" % (wl.N1, wl.N2), "gdn_verify", "attn_verify_rows",
                  "head_gemms", "greedy_accept", "rollback"]
         acc = {k: [] for k in names}
         with torch.cuda.stream(stream):
             for s in range(min(args.steps, 50)):
                 L = layers[s % R]
-                fns = [L.gemm1, L.gemm2, L.gdn, L.attn, L.head_gemms, L.greedy, L.rollback]
+                fns = [L.gemms, L.gdn, L.attn, L.head_gemms, L.greedy, L.rollback]
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
                 ev[0].record(stream)
                 for i, f in enumerate(fns):
@@ -332,9 +332,9 @@ def main():
         except Exception as exc:
             extras["composed"] = {"error": "%s: %s" % (type(exc).__name__, exc)}
 
-    # algorithmic bytes of the dominant kernel (weights + activations in + bf16 out)
+    # algorithmic bytes of the dominant kernel (both weights + activations in once + bf16 out)
     M = wl.M
-    gemm_bytes = wl.N2 * wl.K * 2 + M * wl.K * 2 + M * wl.N2 * 2
+    gemm_bytes = (wl.N1 + wl.N2) * wl.K * 2 + M * wl.K * 2 + M * (wl.N1 + wl.N2) * 2
     achieved = gemm_bytes / (gemm_avg_us * 1e-6) / 1e9
     value = wl.B * wl.k_drafts / (ms_per_step * 1e-3) if exact else None
 
@@ -376,7 +376,8 @@ def main():
             "note": "same workload, every request keeps all %d rows (no state recompute)" % wl.T,
         },
         "roofline": {
-            "kernel": "xv_gemm_small_m, LDS-staged variant (M=9, K=5120, N=%d)" % wl.N2,
+            "kernel": "xv_gemm_small_m_pair, LDS-staged two-GEMM launch (M=%d, K=%d, N=%d+%d)" % (
+                M, wl.K, wl.N1, wl.N2),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

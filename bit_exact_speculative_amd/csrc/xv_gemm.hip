@@ -139,6 +139,20 @@ void xv_gemm_xreg_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
     }
 }
 
+// Up to two GEMMs with the same M and K in one launch (the other variants take
+// one): their column blocks form one list, problem 0's first, and workgroup i
+// walks blocks i, i + grid, ... of the list, so the chip stays balanced over the
+// union.  A workgroup's blocks ascend, so it crosses from problem 0 to problem 1
+// at most once, and then reloads its x fragments.  Per block the arithmetic is
+// the single-GEMM kernel's.
+struct XvGemmPair {
+    const uint16_t* x[2];
+    const uint16_t* w[2];
+    uint16_t* y[2];
+    float* y32[2];
+    int N[2];
+};
+
 // W staged through LDS: the workgroup streams each column block's 16 rows with
 // 1 KB contiguous wave loads (each 16-byte granule of a stage is one thread's
 // load) into a padded LDS stage; each wave then reads the MFMA B fragments of its
@@ -150,9 +164,7 @@ void xv_gemm_xreg_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
 // Requires K = NS * SL * 32 and SL * NS = 16 * KSW (the 16 ranges split evenly).
 template <int KSW, int SL, int NS>
 __global__ __launch_bounds__(XV_GEMM_THREADS)
-void xv_gemm_wlds_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                         uint16_t* __restrict__ y, float* __restrict__ y32,
-                         int M, int N, int K, int mt0)
+void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0)
 {
     static_assert(NS % 2 == 0 && SL * NS == XV_GEMM_WAVES * KSW, "stages must split the ranges evenly");
     constexpr int WPS = XV_GEMM_WAVES / NS;         // waves whose ranges a stage holds
@@ -169,13 +181,14 @@ void xv_gemm_wlds_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
     const int lr = lane & 15, lg = lane >> 4;
     const int ks0 = wave * KSW;
     const int my_stage = wave / WPS;
-    const int nblk = N >> 4;
+    const int nb0 = pp.N[0] >> 4;
+    const int nblk = nb0 + (pp.N[1] >> 4);
     const int grid = gridDim.x;
     if ((int)blockIdx.x >= nblk) return;            // uniform over the workgroup
     const xv_u32x4 zero = {0u, 0u, 0u, 0u};
 
     xv_u32x4 xr[KSW];
-    {
+    auto load_x = [&](const uint16_t* __restrict__ x) {
         const int row = mt0 * 16 + lr;
         const bool ok = row < M;
         const uint16_t* xp = x + (size_t)(ok ? row : M - 1) * K + (size_t)ks0 * 32 + lg * 8;
@@ -183,7 +196,9 @@ void xv_gemm_wlds_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
         for (int j = 0; j < KSW; ++j) xr[j] = xv_load16(xp + j * 32);
 #pragma unroll
         for (int j = 0; j < KSW; ++j) xr[j] = ok ? xr[j] : zero;
-    }
+    };
+    int cur = (int)blockIdx.x >= nb0 ? 1 : 0;
+    load_x(pp.x[cur]);
 
     // this thread's granules: (row, 16-byte column) of a stage, the same for every stage
     int goff[GPT], loff[GPT];
@@ -196,7 +211,8 @@ void xv_gemm_wlds_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
         loff[i] = r * PITCH + c * 8;
     }
     auto load_stage = [&](xv_u32x4 (&gr)[GPT], int blk, int st) {
-        const uint16_t* base = w + (size_t)blk * 16 * K + st * (SL * 32);
+        const uint16_t* base = (blk < nb0 ? pp.w[0] + (size_t)blk * 16 * K
+                                          : pp.w[1] + (size_t)(blk - nb0) * 16 * K) + st * (SL * 32);
 #pragma unroll
         for (int i = 0; i < GPT; ++i) gr[i] = xv_load16(base + goff[i]);
     };
@@ -233,10 +249,14 @@ void xv_gemm_wlds_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
             }
         }
         xv_f32x4 accs[1] = {acc};
-        xv_gemm_finish<1>(red, accs, lane, wave, blk, mt0, M, N, y, y32);
+        xv_gemm_finish<1>(red, accs, lane, wave, blk - cur * nb0, mt0, M, pp.N[cur], pp.y[cur], pp.y32[cur]);
         acc = xv_f32x4{0.f, 0.f, 0.f, 0.f};
         if (!more) break;
         blk = nb;
+        if (blk >= nb0 && cur == 0) {               // uniform: crossing into problem 1
+            cur = 1;
+            load_x(pp.x[1]);
+        }
     }
 }
 
@@ -496,11 +516,19 @@ void xv_gemm_launch_xreg(const uint16_t* x, const uint16_t* w, uint16_t* y, floa
 }
 
 template <int KSW, int SL, int NS>
-void xv_gemm_launch_wlds(const uint16_t* x, const uint16_t* w, uint16_t* y, float* y32,
-                         int M, int N, int K, int mt0, const XvLaunch& lc)
+void xv_gemm_launch_wlds(const XvGemmPair& pp, int M, int K, int mt0, const XvLaunch& lc)
 {
-    dim3 grid(xv_gemm_grid(N / 16)), block(XV_GEMM_THREADS);
-    hipExtLaunchKernelGGL((xv_gemm_wlds_kernel<KSW, SL, NS>), grid, block, 0, lc.st, lc.e0, lc.e1, 0, x, w, y, y32, M, N, K, mt0);
+    dim3 grid(xv_gemm_grid((pp.N[0] + pp.N[1]) / 16)), block(XV_GEMM_THREADS);
+    hipExtLaunchKernelGGL((xv_gemm_wlds_kernel<KSW, SL, NS>), grid, block, 0, lc.st, lc.e0, lc.e1, 0, pp, M, K, mt0);
+}
+
+// the LDS-staged variant serves one row tile and these K only
+bool xv_gemm_wlds_fits(int mt, int K) { return mt == 1 && (K == 5120 || K == 6144); }
+
+void xv_gemm_launch_wlds_k(const XvGemmPair& pp, int M, int K, int mt0, const XvLaunch& lc)
+{
+    if (K == 5120) xv_gemm_launch_wlds<10, 40, 4>(pp, M, K, mt0, lc);
+    else xv_gemm_launch_wlds<12, 48, 4>(pp, M, K, mt0, lc);
 }
 
 template <int MT, int KC>
@@ -532,8 +560,11 @@ void xv_gemm_dispatch(int mt, int ksw, const uint16_t* x, const uint16_t* w, uin
                       float* y32, int M, int N, int K, int mt0, const XvLaunch& lc)
 {
     // one row tile and the two K of the 27B-class layer: W through LDS in 1 KB contiguous wave loads
-    if (mt == 1 && K == 5120) { xv_gemm_launch_wlds<10, 40, 4>(x, w, y, y32, M, N, K, mt0, lc); return; }
-    if (mt == 1 && K == 6144) { xv_gemm_launch_wlds<12, 48, 4>(x, w, y, y32, M, N, K, mt0, lc); return; }
+    if (xv_gemm_wlds_fits(mt, K)) {
+        const XvGemmPair pp{{x, nullptr}, {w, nullptr}, {y, nullptr}, {y32, nullptr}, {N, 0}};
+        xv_gemm_launch_wlds_k(pp, M, K, mt0, lc);
+        return;
+    }
     if (mt == 1 && ksw <= 10) {
         if (ksw <= 2) xv_gemm_launch_xreg<1, 2>(x, w, y, y32, M, N, K, mt0, lc);
         else if (ksw <= 4) xv_gemm_launch_xreg<1, 4>(x, w, y, y32, M, N, K, mt0, lc);
@@ -597,4 +628,30 @@ extern "C" int xv_gemm_small_m(const uint16_t* x, const uint16_t* w, uint16_t* y
                                int M, int N, int K, void* stream)
 {
     return xv_gemm_small_m_timed(x, w, y, y32, M, N, K, stream, nullptr, nullptr);
+}
+
+extern "C" int xv_gemm_small_m_pair(const uint16_t* x0, const uint16_t* w0, uint16_t* y0, float* y32_0, int N0,
+                                    const uint16_t* x1, const uint16_t* w1, uint16_t* y1, float* y32_1, int N1,
+                                    int M, int K, void* stream, void* start_event, void* stop_event)
+{
+    XV_REQUIRE(M >= 0 && K >= 32 && K % 32 == 0, XV_ERR_SHAPE);
+    XV_REQUIRE(N0 >= 16 && N0 % 16 == 0 && N1 >= 16 && N1 % 16 == 0, XV_ERR_SHAPE);
+    if (M == 0) return XV_OK;
+    XV_REQUIRE(x0 && w0 && y0 && x1 && w1 && y1, XV_ERR_NULL);
+    XV_REQUIRE(xv_aligned16(x0) && xv_aligned16(w0) && xv_aligned(y0, 2) && xv_aligned(y32_0, 4) &&
+               xv_aligned16(x1) && xv_aligned16(w1) && xv_aligned(y1, 2) && xv_aligned(y32_1, 4),
+               XV_ERR_ALIGN);
+    const int tiles = (M + 15) / 16;
+    if (!xv_gemm_wlds_fits(tiles, K)) {
+        // no fused variant for this shape: the two GEMMs one after the other (same bits)
+        int s = xv_gemm_small_m_timed(x0, w0, y0, y32_0, M, N0, K, stream, start_event, nullptr);
+        if (s != XV_OK) return s;
+        return xv_gemm_small_m_timed(x1, w1, y1, y32_1, M, N1, K, stream, nullptr, stop_event);
+    }
+    (void)hipGetLastError();
+    const XvLaunch lc{reinterpret_cast<hipStream_t>(stream), reinterpret_cast<hipEvent_t>(start_event),
+                      reinterpret_cast<hipEvent_t>(stop_event)};
+    const XvGemmPair pp{{x0, x1}, {w0, w1}, {y0, y1}, {y32_0, y32_1}, {N0, N1}};
+    xv_gemm_launch_wlds_k(pp, M, K, 0, lc);
+    return xv_launch_status();
 }

@@ -5,11 +5,11 @@ A decoding step consumes tokens[b] = [root, draft_1 .. draft_k] (k = 0: plain
 decoding) and runs, on one stream:
 
   xv_embed_rows         x = E[tokens]
-  xv_gemm_small_m (x2)  y1 = x W1^T, y2 = x W2^T
+  xv_gemm_small_m_pair  y1 = x W1^T, y2 = x W2^T (one launch)
   xv_split_projections  GDN q, k (L2-normalised), v, decay, beta; attention q, k, v
   xv_gdn_verify         GDN rows, S_in -> S_T
   xv_attn_verify_rows   attention rows, KV append
-  xv_gemm_small_m (x2)  head logits from o_gdn and o_attn
+  xv_gemm_small_m_pair  head logits from o_gdn and o_attn (one launch)
   xv_greedy_accept      ids, logprobs, accepted rows
   xv_rollback_to_prefix state and KV length of the kept rows
 
@@ -126,14 +126,13 @@ class Decoder:
         R = self.rows(T)
         M = B * T
         xv.xv_embed_rows(self.E, tokens, R.x, stream=st)
-        xv.xv_gemm_small_m(R.x, self.W1, R.y1, None, stream=st)
-        xv.xv_gemm_small_m(R.x, self.W2, R.y2, None, stream=st)
+        xv.xv_gemm_small_m_pair(R.x, self.W1, R.y1, None, R.x, self.W2, R.y2, None, stream=st)
         xv.xv_split_projections(R.y1, R.y2, R.q, R.k, R.v, R.a, R.b, R.qa, R.kn, R.vn, stream=st)
         xv.xv_gdn_verify(R.q, R.k, R.v, R.a, R.b, self.S, self.S2, R.o_gdn, None, stream=st)
         xv.xv_attn_verify_rows(R.qa, R.kn, R.vn, self.Kc, self.Vc, self.kv_len, R.o_attn, None, R.ws,
                                self.scale, stream=st)
-        xv.xv_gemm_small_m(R.o_gdn.view(M, wl.Hv * wl.dv), self.Wh_g, R.lg, R.lg32, stream=st)
-        xv.xv_gemm_small_m(R.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, R.la, R.la32, stream=st)
+        xv.xv_gemm_small_m_pair(R.o_gdn.view(M, wl.Hv * wl.dv), self.Wh_g, R.lg, R.lg32,
+                                R.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, R.la, R.la32, stream=st)
         xv.xv_greedy_accept(R.lg32.view(B, T, wl.NH), R.la32.view(B, T, wl.NH), tokens, R.ids,
                             R.n_keep, R.lp, stream=st)
         xv.xv_rollback_to_prefix(R.k, R.v, R.a, R.b, self.S, self.S2, self.kv_len, R.n_keep, stream=st)

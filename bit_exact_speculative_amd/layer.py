@@ -4,10 +4,10 @@ A :class:`Layer` holds the device buffers of one workload (weights, GDN state,
 KV cache, the verify rows) and runs, on one stream:
 
   verify()  the hot path of one speculative step:
-              x W1^T, x W2^T                     (xv_gemm_small_m, M = B*T)
+              x W1^T, x W2^T                     (xv_gemm_small_m_pair, M = B*T)
               GDN verify S_in -> S_out, o_gdn    (xv_gdn_verify)
               attention rows + KV append         (xv_attn_verify_rows)
-              synthetic head logits              (xv_gemm_small_m on o_gdn and o_attn)
+              synthetic head logits              (xv_gemm_small_m_pair on o_gdn and o_attn)
               greedy ids, logprobs, accepted rows (xv_greedy_accept)
               rollback to the accepted prefix    (xv_rollback_to_prefix)
   decode_sequence()  the same layer advanced one token at a time (T = 1, M = B)
@@ -150,9 +150,13 @@ class Layer:
             xv.xv_gemm_small_m_timed(self.x, self.W2, self.y2, self.y2_32 if self.proj_fp32 else None,
                                      events[0], events[1], stream=self.stream)
 
-    def gemms(self):
-        self.gemm1()
-        self.gemm2()
+    def gemms(self, events=None):
+        """Both projections in one launch (the bits of gemm1 and gemm2); events: optional
+        (start, stop) torch.cuda.Event pair timed by the launch itself."""
+        st = events if events is not None else (None, None)
+        xv.xv_gemm_small_m_pair(self.x, self.W1, self.y1, self.y1_32 if self.proj_fp32 else None,
+                                self.x, self.W2, self.y2, self.y2_32 if self.proj_fp32 else None,
+                                st[0], st[1], stream=self.stream)
 
     def gdn(self):
         xv.xv_gdn_verify(self.q, self.k, self.v, self.a, self.b, self.S_in, self.S_out,
@@ -164,11 +168,11 @@ class Layer:
                                self.scale, stream=self.stream)
 
     def head_gemms(self):
+        """Both halves of the synthetic head in one launch."""
         wl, M = self.wl, self.wl.M
-        xv.xv_gemm_small_m(self.o_gdn.view(M, wl.Hv * wl.dv), self.Wh_g, self.lg, self.lg32,
-                           stream=self.stream)
-        xv.xv_gemm_small_m(self.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, self.la, self.la32,
-                           stream=self.stream)
+        xv.xv_gemm_small_m_pair(self.o_gdn.view(M, wl.Hv * wl.dv), self.Wh_g, self.lg, self.lg32,
+                                self.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, self.la, self.la32,
+                                stream=self.stream)
 
     def greedy(self):
         wl = self.wl

@@ -37,6 +37,8 @@ _lib.xv_gemm_small_m.restype = _I
 _lib.xv_gemm_small_m.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P]
 _lib.xv_gemm_small_m_timed.restype = _I
 _lib.xv_gemm_small_m_timed.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _P, _P]
+_lib.xv_gemm_small_m_pair.restype = _I
+_lib.xv_gemm_small_m_pair.argtypes = [_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P]
 _lib.xv_gdn_verify.restype = _I
 _lib.xv_gdn_verify.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
 _lib.xv_attn_chunk_tokens.restype = _I
@@ -141,6 +143,21 @@ def xv_gemm_small_m_timed(x, w, y, y32=None, start=None, stop=None, stream=None)
     _check("xv_gemm_small_m_timed", _lib.xv_gemm_small_m_timed(_ptr(x), _ptr(w), _ptr(y), _ptr(y32),
                                                               M, N, K, _stream(stream),
                                                               _event(start), _event(stop)))
+
+
+def xv_gemm_small_m_pair(x0, w0, y0, y32_0, x1, w1, y1, y32_1, start=None, stop=None, stream=None):
+    """y0 = x0 @ w0^T and y1 = x1 @ w1^T (same M and K) in one launch; optional fp32 copies
+    and torch.cuda.Event start / stop recorded by the launch itself."""
+    M, K = x0.shape
+    N0, N1 = w0.shape[0], w1.shape[0]
+    if tuple(x1.shape) != (M, K) or w0.shape[1] != K or w1.shape[1] != K or \
+            tuple(y0.shape) != (M, N0) or tuple(y1.shape) != (M, N1) or \
+            (y32_0 is not None and tuple(y32_0.shape) != (M, N0)) or \
+            (y32_1 is not None and tuple(y32_1.shape) != (M, N1)):
+        raise ValueError("xv_gemm_small_m_pair: shape mismatch")
+    _check("xv_gemm_small_m_pair", _lib.xv_gemm_small_m_pair(
+        _ptr(x0), _ptr(w0), _ptr(y0), _ptr(y32_0), N0, _ptr(x1), _ptr(w1), _ptr(y1), _ptr(y32_1), N1,
+        M, K, _stream(stream), _event(start), _event(stop)))
 
 
 def xv_gdn_verify(q, k, v, a, b, state_in, state_out, o, o32=None, stream=None):

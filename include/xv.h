@@ -89,6 +89,24 @@ int xv_gemm_small_m_timed(const uint16_t* x, const uint16_t* w, uint16_t* y, flo
                           int M, int N, int K, void* stream, void* start_event, void* stop_event);
 
 /*
+ * Two small-M GEMMs with the same M and K in one launch:
+ *   y0 = x0 w0^T ([M][N0]) and y1 = x1 w1^T ([M][N1]),
+ * each output bit for bit what xv_gemm_small_m gives it (the same per-block
+ * arithmetic; only the launch is shared).  For the decoding step this joins
+ * the two projections (x0 = x1) and the two halves of the synthetic head, so
+ * the persistent workgroups balance over the union of the column blocks.
+ * Where no fused variant exists for the shape (more than 16 rows, or K other
+ * than 5120 and 6144) the two GEMMs run one after the other.  start_event /
+ * stop_event (hipEvent_t or NULL) are recorded when the first kernel starts
+ * and the last one ends, as in xv_gemm_small_m_timed.
+ * Arguments, layouts, shapes and errors per GEMM as xv_gemm_small_m; x0 may
+ * equal x1.
+ */
+int xv_gemm_small_m_pair(const uint16_t* x0, const uint16_t* w0, uint16_t* y0, float* y32_0, int N0,
+                         const uint16_t* x1, const uint16_t* w1, uint16_t* y1, float* y32_1, int N1,
+                         int M, int K, void* stream, void* start_event, void* stop_event);
+
+/*
  * GDN verify: T tokens of the gated delta rule per request, fp32 state.
  * The post, the two verify changes (the GDN recurrence through the decode
  * arithmetic, the old verify kernel having tiled the state differently and

@@ -25,7 +25,8 @@ def test_every_header_symbol_is_exported(xv):
     assert set(names) >= {"xv_gemm_small_m", "xv_gdn_verify", "xv_attn_verify_rows",
                           "xv_rollback_to_prefix", "xv_attn_workspace_bytes",
                           "xv_attn_chunk_tokens", "xv_abi_version", "xv_status_string",
-                          "xv_greedy_accept", "xv_embed_rows", "xv_split_projections"}
+                          "xv_greedy_accept", "xv_embed_rows", "xv_split_projections",
+                          "xv_gemm_small_m_pair"}
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -63,6 +64,18 @@ def test_gemm_argument_errors(xv):
     assert f(A, MIS, A, None, 9, 16, 32, None) == -3
     assert f(A, A, ODD, None, 9, 16, 32, None) == -3
     assert f(A, A, A, A + 2, 9, 16, 32, None) == -3
+
+
+def test_gemm_pair_argument_errors(xv):
+    f = xv.lib().xv_gemm_small_m_pair
+
+    def call(x0=A, w0=A, y0=A, N0=64, x1=A, w1=A, y1=A, N1=32, M=9, K=5120, y32_0=None, y32_1=None):
+        return f(x0, w0, y0, y32_0, N0, x1, w1, y1, y32_1, N1, M, K, None, None, None)
+
+    assert call(M=0) == 0
+    assert call(N0=8) == -2 and call(N1=40) == -2 and call(K=48) == -2 and call(M=-1) == -2
+    assert call(x1=None) == -1 and call(w0=None) == -1 and call(y1=None) == -1
+    assert call(w1=MIS) == -3 and call(x0=MIS) == -3 and call(y0=ODD) == -3 and call(y32_1=A + 2) == -3
 
 
 def test_gdn_argument_errors(xv):

@@ -170,3 +170,43 @@ def test_gemm_timed_entry_point_same_bits_and_kernel_interval():
         assert torch.equal(y32.view(torch.int32), rows.view(torch.int32))
         k_ms, b_ms = e0.elapsed_time(e1), b0.elapsed_time(b1)
         assert 0.0 < k_ms <= b_ms + 1e-3, (M, k_ms, b_ms)
+
+
+PAIR_CASES = [  # M, K, N0, N1, shared x, with fp32 copies
+    (9, 5120, 10240, 17408, True, True),      # the two projections of the short step
+    (9, 6144, 4096, 4096, False, True),       # the two halves of the synthetic head
+    (1, 5120, 16, 48, False, False),          # fewer column blocks than CUs
+    (16, 6144, 4096, 272, True, True),        # a full row tile, uneven split
+    (5, 5120, 8192, 16, False, True),         # problem 1 is one block
+    (20, 5120, 512, 256, True, True),         # two row tiles: no fused variant, one after the other
+    (9, 1024, 512, 512, False, False),        # other K: one after the other
+]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES, ids=[str(c) for c in PAIR_CASES])
+def test_gemm_pair_gives_the_single_gemm_bits(case):
+    """xv_gemm_small_m_pair: each output equals xv_gemm_small_m's bits for it, whether the
+    two GEMMs share a launch or not; the launch-recorded interval is positive."""
+    from bit_exact_speculative_amd.layer import dev_bf16
+    M, K, N0, N1, shared, with32 = case
+    rng = np.random.default_rng(M * 31 + N0 + N1 + K)
+    xv = _xv()
+    x0 = dev_bf16(random_bf16(rng, (M, K)), "cuda")
+    x1 = x0 if shared else dev_bf16(random_bf16(rng, (M, K)), "cuda")
+    w0 = dev_bf16(random_bf16(rng, (N0, K), 0.02), "cuda")
+    w1 = dev_bf16(random_bf16(rng, (N1, K), 0.02), "cuda")
+    r0, r0_32 = _gemm_dev(x0, w0)
+    r1, r1_32 = _gemm_dev(x1, w1)
+    y0 = torch.empty((M, N0), dtype=torch.bfloat16, device="cuda")
+    y1 = torch.empty((M, N1), dtype=torch.bfloat16, device="cuda")
+    y0_32 = torch.empty((M, N0), dtype=torch.float32, device="cuda") if with32 else None
+    y1_32 = torch.empty((M, N1), dtype=torch.float32, device="cuda") if with32 else None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    xv.xv_gemm_small_m_pair(x0, w0, y0, y0_32, x1, w1, y1, y1_32, e0, e1)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), r0.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), r1.view(torch.int16))
+    if with32:
+        assert torch.equal(y0_32.view(torch.int32), r0_32.view(torch.int32))
+        assert torch.equal(y1_32.view(torch.int32), r1_32.view(torch.int32))
+    assert e0.elapsed_time(e1) > 0.0
