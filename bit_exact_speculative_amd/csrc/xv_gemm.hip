@@ -140,11 +140,13 @@ void xv_gemm_xreg_kernel(const uint16_t* __restrict__ x, const uint16_t* __restr
 }
 
 // Up to two GEMMs with the same M and K in one launch (the other variants take
-// one): their column blocks form one list, problem 0's first, and workgroup i
-// walks blocks i, i + grid, ... of the list, so the chip stays balanced over the
-// union.  A workgroup's blocks ascend, so it crosses from problem 0 to problem 1
-// at most once, and then reloads its x fragments.  Per block the arithmetic is
-// the single-GEMM kernel's.
+// one): their column blocks form one list, problem 0's first.  With a shared x,
+// workgroup i walks blocks i, i + grid, ... of the list (neighbouring workgroups
+// read neighbouring blocks); with two different x, workgroup i takes the
+// contiguous range [i nblk / grid, (i + 1) nblk / grid), so that few workgroups
+// cross from problem 0 to problem 1 (a crossing reloads the x fragments, a stall
+// in the stream).  Either way the chip stays balanced over the union, and per
+// block the arithmetic is the single-GEMM kernel's.
 struct XvGemmPair {
     const uint16_t* x[2];
     const uint16_t* w[2];
@@ -164,7 +166,7 @@ struct XvGemmPair {
 // Requires K = NS * SL * 32 and SL * NS = 16 * KSW (the 16 ranges split evenly).
 template <int KSW, int SL, int NS>
 __global__ __launch_bounds__(XV_GEMM_THREADS)
-void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0)
+void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0, int contig)
 {
     static_assert(NS % 2 == 0 && SL * NS == XV_GEMM_WAVES * KSW, "stages must split the ranges evenly");
     constexpr int WPS = XV_GEMM_WAVES / NS;         // waves whose ranges a stage holds
@@ -184,7 +186,11 @@ void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0)
     const int nb0 = pp.N[0] >> 4;
     const int nblk = nb0 + (pp.N[1] >> 4);
     const int grid = gridDim.x;
-    if ((int)blockIdx.x >= nblk) return;            // uniform over the workgroup
+    // this workgroup's blocks: b0, b0 + step, ... below bend
+    const int b0 = contig ? (int)(((long long)blockIdx.x * nblk) / grid) : (int)blockIdx.x;
+    const int bend = contig ? (int)(((long long)(blockIdx.x + 1) * nblk) / grid) : nblk;
+    const int bstep = contig ? 1 : grid;
+    if (b0 >= bend) return;                         // uniform over the workgroup
     const xv_u32x4 zero = {0u, 0u, 0u, 0u};
 
     xv_u32x4 xr[KSW];
@@ -197,7 +203,7 @@ void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0)
 #pragma unroll
         for (int j = 0; j < KSW; ++j) xr[j] = ok ? xr[j] : zero;
     };
-    int cur = (int)blockIdx.x >= nb0 ? 1 : 0;
+    int cur = b0 >= nb0 ? 1 : 0;
     load_x(pp.x[cur]);
 
     // this thread's granules: (row, 16-byte column) of a stage, the same for every stage
@@ -225,12 +231,12 @@ void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0)
     xv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
     xv_u32x4 g0[GPT], g1[GPT];
-    int blk = blockIdx.x;
+    int blk = b0;
     load_stage(g0, blk, 0);
     load_stage(g1, blk, 1);
     for (;;) {
-        const int nb = blk + grid;
-        const bool more = nb < nblk;
+        const int nb = blk + bstep;
+        const bool more = nb < bend;
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
             xv_u32x4 (&gr)[GPT] = (st & 1) ? g1 : g0;
@@ -519,7 +525,8 @@ template <int KSW, int SL, int NS>
 void xv_gemm_launch_wlds(const XvGemmPair& pp, int M, int K, int mt0, const XvLaunch& lc)
 {
     dim3 grid(xv_gemm_grid((pp.N[0] + pp.N[1]) / 16)), block(XV_GEMM_THREADS);
-    hipExtLaunchKernelGGL((xv_gemm_wlds_kernel<KSW, SL, NS>), grid, block, 0, lc.st, lc.e0, lc.e1, 0, pp, M, K, mt0);
+    const int contig = pp.N[1] > 0 && pp.x[0] != pp.x[1];
+    hipExtLaunchKernelGGL((xv_gemm_wlds_kernel<KSW, SL, NS>), grid, block, 0, lc.st, lc.e0, lc.e1, 0, pp, M, K, mt0, contig);
 }
 
 // the LDS-staged variant serves one row tile and these K only
