@@ -331,6 +331,15 @@ def main():
             extras["composed"] = composed_workload(stream)
         except Exception as exc:
             extras["composed"] = {"error": "%s: %s" % (type(exc).__name__, exc)}
+        try:
+            from bit_exact_speculative_amd.diagnose import divergence_margins
+            with torch.cuda.stream(stream):
+                extras["divergence"] = divergence_margins("batch8", n_tokens=24, k=8, p_wrong=0.3,
+                                                          seeds=(0, 1, 2))
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        except Exception as exc:
+            extras["divergence"] = {"error": "%s: %s" % (type(exc).__name__, exc)}
 
     # algorithmic bytes of the dominant kernel (both weights + activations in once + bf16 out)
     M = wl.M

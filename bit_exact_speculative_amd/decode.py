@@ -88,9 +88,13 @@ class Decoder:
     Lmax: KV capacity (at least the cached length + every token decoded + one step).
     """
 
-    def __init__(self, inp: Inputs, Lmax: int, device="cuda", S0: Optional[np.ndarray] = None, stream=None):
+    def __init__(self, inp: Inputs, Lmax: int, device="cuda", S0: Optional[np.ndarray] = None, stream=None,
+                 projections: Optional[Callable] = None):
+        """projections(decoder, rows, tokens): an alternative that fills rows.y1 and rows.y2
+        from rows.x (for diagnostics of non-exact variants); None = xv_gemm_small_m_pair."""
         wl = inp.wl
         self.wl, self.device, self.stream = wl, device, stream
+        self.projections = projections
         if Lmax < inp.k_cache.shape[2]:
             raise ValueError("Lmax below the inputs' cache capacity")
         self.E = _bf16(inp.extra["E"], device)
@@ -126,7 +130,10 @@ class Decoder:
         R = self.rows(T)
         M = B * T
         xv.xv_embed_rows(self.E, tokens, R.x, stream=st)
-        xv.xv_gemm_small_m_pair(R.x, self.W1, R.y1, None, R.x, self.W2, R.y2, None, stream=st)
+        if self.projections is None:
+            xv.xv_gemm_small_m_pair(R.x, self.W1, R.y1, None, R.x, self.W2, R.y2, None, stream=st)
+        else:
+            self.projections(self, R, tokens)
         xv.xv_split_projections(R.y1, R.y2, R.q, R.k, R.v, R.a, R.b, R.qa, R.kn, R.vn, stream=st)
         xv.xv_gdn_verify(R.q, R.k, R.v, R.a, R.b, self.S, self.S2, R.o_gdn, None, stream=st)
         xv.xv_attn_verify_rows(R.qa, R.kn, R.vn, self.Kc, self.Vc, self.kv_len, R.o_attn, None, R.ws,
@@ -149,15 +156,18 @@ class Decoder:
 
     def generate(self, root: np.ndarray, n_tokens: int,
                  drafts: Optional[Callable[[int, int, int], np.ndarray]] = None, k: int = 0,
-                 record: Optional[list] = None):
+                 record: Optional[list] = None, logits: Optional[list] = None):
         """Greedy decoding of n_tokens per request from root (int32 [B]); drafts(b, pos, k)
         proposes k ids after request b's pos-th emitted token.  Reads each step's results
         back to the host.  Returns (ids int32 [B][n], logprobs fp32 [B][n], per-step n_keep);
-        record, when given, receives each step's input tokens (int32 [B][k+1])."""
+        record, when given, receives each step's input tokens (int32 [B][k+1]); logits, when
+        given, receives one list per request of the fp32 logits row of every emitted token."""
         B = self.wl.B
         out_ids = [[] for _ in range(B)]
         out_lp = [[] for _ in range(B)]
         keeps = []
+        if logits is not None:
+            logits.extend([] for _ in range(B))
         cur = np.asarray(root, np.int32).copy()
         while min(len(o) for o in out_ids) < n_tokens:
             tok = np.empty((B, k + 1), np.int32)
@@ -174,8 +184,12 @@ class Decoder:
             lp = R.lp.cpu().numpy()
             nk = R.n_keep.cpu().numpy()
             keeps.append(nk.copy())
+            if logits is not None:
+                z = (R.lg32 + R.la32).view(B, k + 1, -1).cpu().numpy()   # the fp32 sum the greedy kernel forms
             for bb in range(B):
                 n = int(nk[bb])
+                if logits is not None:
+                    logits[bb].extend(z[bb, i].copy() for i in range(n))
                 out_ids[bb].extend(int(i) for i in ids[bb, :n])
                 out_lp[bb].extend(float(x) for x in lp[bb, :n])
                 cur[bb] = ids[bb, n - 1]

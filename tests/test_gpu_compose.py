@@ -218,3 +218,16 @@ def test_composed_decoding_vs_oracle_tiny():
     assert good >= 4, "margins too small to compare"
     assert np.array_equal(ids_g[:, :good], ids_o[:, :good])
     assert np.all(np.abs(lp_g[:, :good] - lp_o[:, :good]) <= 2e-3 * np.maximum(np.abs(lp_o[:, :good]), 1.0))
+
+
+@pytest.mark.parametrize("name,seeds", [("tiny", (0, 1)), ("batch8", (0,))])
+def test_divergence_margin_diagnostic(name, seeds):
+    """The exact speculative run never leaves plain decoding; where the non-exact run (fp32
+    library product for the verify projections) flips an id, the reference's top-1/top-2
+    margin there is within what its logit perturbation can bridge."""
+    from bit_exact_speculative_amd.diagnose import divergence_margins
+    inp = gen.composed_inputs(gen.WORKLOADS[name])
+    r = divergence_margins(name, n_tokens=16, k=8, p_wrong=0.3, seeds=seeds, S0=prefix_state(inp))
+    assert r["exact_spec_diverged"] == 0
+    assert r["flips_within_perturbation"]
+    assert r["requests"] == gen.WORKLOADS[name].B * len(seeds)
