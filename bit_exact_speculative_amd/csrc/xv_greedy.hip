@@ -23,19 +23,26 @@ __device__ __forceinline__ bool xv_better(float v1, int n1, float v0, int n0) {
     return v1 > v0 || (v1 == v0 && n1 < n0);
 }
 
-// One workgroup per verify row (grid T x B): argmax of the row's logits and,
-// when lp is given, the logprob of that id.  Thread t owns the 4-element groups
-// t, t + 256, t + 512, ... of the row (elements 4v .. 4v + 3 of group v), with
-// 16-byte loads (VEC: rows 16-byte aligned, N % 4 == 0) or 4-byte loads; the
-// ownership and every order below are the same either way, and indices past
-// the row re-read its last element and are masked out.
+// One workgroup per verify row (grid T x B), one pass over the row: the argmax
+// of the logits and, when lp is given, the logprob of that id.  Thread t owns the
+// 4-element groups t, t + 256, t + 512, ... of the row (elements 4v .. 4v + 3 of
+// group v), with 16-byte loads (VEC: rows 16-byte aligned, N % 4 == 0) or
+// 4-byte loads; the ownership and every order below are the same either way,
+// and indices past the row re-read its last element and are masked out.
 //
 // Logprob of the argmax (post, first paragraph: logprobs compared as well as
-// ids): with m the row maximum, lp = -ln(sum_n e^(z_n - m)), each term
-// 2^((z_n - m) * log2 e); the sum runs over the thread's groups in order and
-// the 4 elements of a group in order, then a lane butterfly (each level adds
-// two equal-order partials, so all lanes agree) and the 4 waves' partials left
-// to right.  None of it depends on T, B or the other rows.
+// ids), lp = -ln S with S = sum_n e^(z_n - max z), in an order fixed by N:
+//  * the row is cut into 16-column blocks (the last may be partial); a block's
+//    pair (m, s) is its maximum and sum_c e^(z_c - m), the sum as a butterfly
+//    over the columns (c with c ^ 8, then ^ 4, ^ 2, ^ 1; every level adds two
+//    partials that its partner adds the other way round, so all agree);
+//  * pairs combine as (m1, s1) + (m2, s2) = (M, s1 e^(m1 - M) + s2 e^(m2 - M)),
+//    M = max(m1, m2), an empty pair (-inf, 0) contributing nothing; block b
+//    belongs to chain b mod 64, whose blocks fold left to right; the 64 chains
+//    then meet in a butterfly (chain ^ 1, ^ 2, ^ 4, ^ 8) within each group of 16
+//    and the four groups fold left to right.
+// Each e^x is 2^(x log2 e) on the hardware exp2; the result is exact in M (the
+// maximum is), so lp = -ln S.  None of it depends on T, B or the other rows.
 template <bool VEC>
 __device__ __forceinline__ void xv_row_groups(const float* __restrict__ la, const float* __restrict__ lb,
                                               size_t row, int N, int v, float (&x)[4]) {
@@ -58,6 +65,17 @@ __device__ __forceinline__ void xv_row_groups(const float* __restrict__ la, cons
     }
 }
 
+constexpr float XV_LOG2E = 1.4426950408889634f;
+
+// (m, s) += (m2, s2) in the combination above
+__device__ __forceinline__ void xv_lse_add(float& m, float& s, float m2, float s2) {
+    const float mm = fmaxf(m, m2);
+    const float t1 = m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - mm) * XV_LOG2E);
+    const float t2 = m2 == -INFINITY ? 0.f : s2 * __builtin_amdgcn_exp2f((m2 - mm) * XV_LOG2E);
+    m = mm;
+    s = t1 + t2;
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(XV_GREEDY_THREADS)
 void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb, int T, int N,
@@ -65,7 +83,7 @@ void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb
 {
     __shared__ float sv[XV_GREEDY_WAVES];
     __shared__ int sn[XV_GREEDY_WAVES];
-    __shared__ float smax;
+    __shared__ float sm[XV_GREEDY_WAVES], ssum[XV_GREEDY_WAVES];
     const int t = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x;
     const size_t row = ((size_t)b * T + t) * N;
@@ -73,17 +91,41 @@ void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb
     constexpr int STEP = XV_GREEDY_THREADS * XV_GREEDY_UNROLL;
     float best = -INFINITY;
     int bn = N;                                  // sentinel: after every real index
-    for (int v0 = tid; v0 < G; v0 += STEP) {
+    float cm = -INFINITY, cs = 0.f;              // this thread's chain (blocks tid/4 + 64 i)
+    // every lane runs every pass (the quads exchange values), masking what lies past the row
+    const int passes = (G + STEP - 1) / STEP;
+    for (int it = 0; it < passes; ++it) {
+        const int v0 = tid + it * STEP;
         float x[XV_GREEDY_UNROLL][4];
 #pragma unroll
         for (int u = 0; u < XV_GREEDY_UNROLL; ++u) xv_row_groups<VEC>(la, lb, row, N, v0 + u * XV_GREEDY_THREADS, x[u]);
 #pragma unroll
         for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
             const int v = v0 + u * XV_GREEDY_THREADS;
+            float bm = -INFINITY;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = 4 * v + j;
-                if (v < G && n < N && xv_better(x[u][j], n, best, bn)) { best = x[u][j]; bn = n; }
+                const bool ok = v < G && n < N;
+                if (ok && xv_better(x[u][j], n, best, bn)) { best = x[u][j]; bn = n; }
+                bm = ok ? fmaxf(bm, x[u][j]) : bm;
+            }
+            if (lp) {                            // uniform
+                // the block of group v is held by the 4 lanes of this lane's quad
+                bm = fmaxf(bm, __shfl_xor(bm, 1));
+                bm = fmaxf(bm, __shfl_xor(bm, 2));
+                float e[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = v < G && 4 * v + j < N;
+                    e[j] = ok ? __builtin_amdgcn_exp2f((x[u][j] - bm) * XV_LOG2E) : 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) e[j] = e[j] + __shfl_xor(e[j], 2);   // columns ^ 8
+#pragma unroll
+                for (int j = 0; j < 4; ++j) e[j] = e[j] + __shfl_xor(e[j], 1);   // columns ^ 4
+                const float w0 = e[0] + e[2], w1 = e[1] + e[3];                    // columns ^ 2
+                xv_lse_add(cm, cs, bm, w0 + w1);                                   // columns ^ 1
             }
         }
     }
@@ -93,43 +135,22 @@ void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb
         const int on = __shfl_xor(bn, off);
         if (xv_better(ov, on, best, bn)) { best = ov; bn = on; }
     }
-    if ((tid & 63) == 0) { sv[tid >> 6] = best; sn[tid >> 6] = bn; }
+    if (lp) {
+#pragma unroll
+        for (int off = 4; off < 64; off <<= 1) xv_lse_add(cm, cs, __shfl_xor(cm, off), __shfl_xor(cs, off));
+    }
+    if ((tid & 63) == 0) { sv[tid >> 6] = best; sn[tid >> 6] = bn; sm[tid >> 6] = cm; ssum[tid >> 6] = cs; }
     __syncthreads();
     if (tid == 0) {
         for (int w = 1; w < XV_GREEDY_WAVES; ++w)
             if (xv_better(sv[w], sn[w], best, bn)) { best = sv[w]; bn = sn[w]; }
         ids[(size_t)b * T + t] = bn < N ? bn : 0;
-        smax = best;
-    }
-    if (!lp) return;                             // uniform
-    __syncthreads();
-    const float m = smax;
-    constexpr float LOG2E = 1.4426950408889634f;
-    float s = 0.f;
-    for (int v0 = tid; v0 < G; v0 += STEP) {
-        float x[XV_GREEDY_UNROLL][4];
-#pragma unroll
-        for (int u = 0; u < XV_GREEDY_UNROLL; ++u) xv_row_groups<VEC>(la, lb, row, N, v0 + u * XV_GREEDY_THREADS, x[u]);
-#pragma unroll
-        for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
-            const int v = v0 + u * XV_GREEDY_THREADS;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float e = __builtin_amdgcn_exp2f((x[u][j] - m) * LOG2E);
-                s = (v < G && 4 * v + j < N) ? s + e : s;
-            }
+        if (lp) {
+            float m = sm[0], sum = ssum[0];
+            for (int w = 1; w < XV_GREEDY_WAVES; ++w) xv_lse_add(m, sum, sm[w], ssum[w]);
+            constexpr float LN2 = 0.6931471805599453f;
+            lp[(size_t)b * T + t] = -(__builtin_amdgcn_logf(sum) * LN2);
         }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s = s + __shfl_xor(s, off);
-    __syncthreads();                             // sv is reused
-    if ((tid & 63) == 0) sv[tid >> 6] = s;
-    __syncthreads();
-    if (tid == 0) {
-        float tot = sv[0];
-        for (int w = 1; w < XV_GREEDY_WAVES; ++w) tot = tot + sv[w];
-        constexpr float LN2 = 0.6931471805599453f;
-        lp[(size_t)b * T + t] = -(__builtin_amdgcn_logf(tot) * LN2);
     }
 }
 
