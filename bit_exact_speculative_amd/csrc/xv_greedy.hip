@@ -17,7 +17,6 @@ namespace {
 constexpr int XV_GREEDY_THREADS = 256;
 constexpr int XV_GREEDY_WAVES = XV_GREEDY_THREADS / 64;
 constexpr int XV_TMAX = 16;           // verify rows per request, at most
-constexpr int XV_GREEDY_UNROLL = 4;   // strides per pass, all loaded before any compare
 
 __device__ __forceinline__ bool xv_better(float v1, int n1, float v0, int n0) {
     return v1 > v0 || (v1 == v0 && n1 < n0);
@@ -25,42 +24,53 @@ __device__ __forceinline__ bool xv_better(float v1, int n1, float v0, int n0) {
 
 // One workgroup per verify row (grid T x B), one pass over the row: the argmax
 // of the logits and, when lp is given, the logprob of that id.  Thread t owns the
-// 4-element groups t, t + 256, t + 512, ... of the row (elements 4v .. 4v + 3 of
-// group v), with 16-byte loads (VEC: rows 16-byte aligned, N % 4 == 0) or
-// 4-byte loads; the ownership and every order below are the same either way,
-// and indices past the row re-read its last element and are masked out.
+// 16-column blocks t, t + 256, t + 512, ... of the row (block b: columns
+// 16b .. 16b + 15, the last block may be partial), read as four 16-byte loads
+// (VEC: rows 16-byte aligned, N % 4 == 0) or sixteen 4-byte loads; the order of
+// everything below is the same either way, and columns past the row re-read its
+// last element and are masked out.
 //
 // Logprob of the argmax (post, first paragraph: logprobs compared as well as
 // ids), lp = -ln S with S = sum_n e^(z_n - max z), in an order fixed by N:
-//  * the row is cut into 16-column blocks (the last may be partial); a block's
-//    pair (m, s) is its maximum and sum_c e^(z_c - m), the sum as a butterfly
-//    over the columns (c with c ^ 8, then ^ 4, ^ 2, ^ 1; every level adds two
-//    partials that its partner adds the other way round, so all agree);
+//  * a block's pair (m, s) is its maximum and sum_c e^(z_c - m), the sum as a
+//    butterfly over the columns (c with c ^ 8, then ^ 4, ^ 2, ^ 1);
 //  * pairs combine as (m1, s1) + (m2, s2) = (M, s1 e^(m1 - M) + s2 e^(m2 - M)),
 //    M = max(m1, m2), an empty pair (-inf, 0) contributing nothing; block b
-//    belongs to chain b mod 64, whose blocks fold left to right; the 64 chains
-//    then meet in a butterfly (chain ^ 1, ^ 2, ^ 4, ^ 8) within each group of 16
-//    and the four groups fold left to right.
-// Each e^x is 2^(x log2 e) on the hardware exp2; the result is exact in M (the
-// maximum is), so lp = -ln S.  None of it depends on T, B or the other rows.
+//    belongs to chain b mod 256, whose blocks fold left to right; the chains then
+//    meet in a butterfly (chain ^ 1, ^ 2, ..., ^ 32) within each group of 64 and
+//    the four groups fold left to right (every butterfly level adds two partials
+//    that its partner adds the other way round, so all agree).
+// Each e^x is 2^(x log2 e) on the hardware exp2; M is exact (a maximum), so
+// lp = -ln S.  None of it depends on T, B or the other rows, and a producer that
+// forms the 16-column blocks itself (in any order) can reproduce it.
 template <bool VEC>
-__device__ __forceinline__ void xv_row_groups(const float* __restrict__ la, const float* __restrict__ lb,
-                                              size_t row, int N, int v, float (&x)[4]) {
-    const int G = (N + 3) >> 2;
-    const int vc = v < G ? v : G - 1;
+__device__ __forceinline__ void xv_row_block(const float* __restrict__ la, const float* __restrict__ lb,
+                                             size_t row, int N, int blk, float (&x)[16]) {
+    const int nb = (N + 15) >> 4;
+    const int bc = blk < nb ? blk : nb - 1;
     if (VEC) {
-        const float4 va = reinterpret_cast<const float4*>(la + row)[vc];
-        float4 vb = va;
-        if (lb) vb = reinterpret_cast<const float4*>(lb + row)[vc];
-        x[0] = va.x; x[1] = va.y; x[2] = va.z; x[3] = va.w;
-        if (lb) { x[0] = x[0] + vb.x; x[1] = x[1] + vb.y; x[2] = x[2] + vb.z; x[3] = x[3] + vb.w; }
+        // N % 4 == 0: the block's four 16-byte groups, a group past the row re-reading the last
+        const int G = N >> 2;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int gi = bc * 4 + q4;
+            const int gc = gi < G ? gi : G - 1;
+            const float4 va = reinterpret_cast<const float4*>(la + row)[gc];
+            float4 vb = va;
+            if (lb) vb = reinterpret_cast<const float4*>(lb + row)[gc];
+            x[4 * q4] = va.x; x[4 * q4 + 1] = va.y; x[4 * q4 + 2] = va.z; x[4 * q4 + 3] = va.w;
+            if (lb) {
+                x[4 * q4] = x[4 * q4] + vb.x; x[4 * q4 + 1] = x[4 * q4 + 1] + vb.y;
+                x[4 * q4 + 2] = x[4 * q4 + 2] + vb.z; x[4 * q4 + 3] = x[4 * q4 + 3] + vb.w;
+            }
+        }
     } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = 4 * vc + j;
+        for (int c = 0; c < 16; ++c) {
+            const int n = 16 * bc + c;
             const int nc = n < N ? n : N - 1;
-            x[j] = la[row + nc];
-            if (lb) x[j] = x[j] + lb[row + nc];
+            x[c] = la[row + nc];
+            if (lb) x[c] = x[c] + lb[row + nc];
         }
     }
 }
@@ -76,6 +86,8 @@ __device__ __forceinline__ void xv_lse_add(float& m, float& s, float m2, float s
     s = t1 + t2;
 }
 
+constexpr int XV_GREEDY_BPP = 2;      // blocks per thread per pass, all loaded before any compare
+
 template <bool VEC>
 __global__ __launch_bounds__(XV_GREEDY_THREADS)
 void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb, int T, int N,
@@ -87,45 +99,39 @@ void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb
     const int t = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x;
     const size_t row = ((size_t)b * T + t) * N;
-    const int G = (N + 3) >> 2;
-    constexpr int STEP = XV_GREEDY_THREADS * XV_GREEDY_UNROLL;
+    const int nb = (N + 15) >> 4;
     float best = -INFINITY;
     int bn = N;                                  // sentinel: after every real index
-    float cm = -INFINITY, cs = 0.f;              // this thread's chain (blocks tid/4 + 64 i)
-    // every lane runs every pass (the quads exchange values), masking what lies past the row
-    const int passes = (G + STEP - 1) / STEP;
-    for (int it = 0; it < passes; ++it) {
-        const int v0 = tid + it * STEP;
-        float x[XV_GREEDY_UNROLL][4];
+    float cm = -INFINITY, cs = 0.f;              // this thread's chain: blocks tid + 256 i
+    for (int b0 = tid; b0 < nb; b0 += XV_GREEDY_THREADS * XV_GREEDY_BPP) {
+        float x[XV_GREEDY_BPP][16];
 #pragma unroll
-        for (int u = 0; u < XV_GREEDY_UNROLL; ++u) xv_row_groups<VEC>(la, lb, row, N, v0 + u * XV_GREEDY_THREADS, x[u]);
+        for (int u = 0; u < XV_GREEDY_BPP; ++u) xv_row_block<VEC>(la, lb, row, N, b0 + u * XV_GREEDY_THREADS, x[u]);
 #pragma unroll
-        for (int u = 0; u < XV_GREEDY_UNROLL; ++u) {
-            const int v = v0 + u * XV_GREEDY_THREADS;
+        for (int u = 0; u < XV_GREEDY_BPP; ++u) {
+            const int blk = b0 + u * XV_GREEDY_THREADS;
             float bm = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = 4 * v + j;
-                const bool ok = v < G && n < N;
-                if (ok && xv_better(x[u][j], n, best, bn)) { best = x[u][j]; bn = n; }
-                bm = ok ? fmaxf(bm, x[u][j]) : bm;
+            for (int c = 0; c < 16; ++c) {
+                const int n = 16 * blk + c;
+                const bool ok = blk < nb && n < N;
+                if (ok && xv_better(x[u][c], n, best, bn)) { best = x[u][c]; bn = n; }
+                bm = ok ? fmaxf(bm, x[u][c]) : bm;
             }
             if (lp) {                            // uniform
-                // the block of group v is held by the 4 lanes of this lane's quad
-                bm = fmaxf(bm, __shfl_xor(bm, 1));
-                bm = fmaxf(bm, __shfl_xor(bm, 2));
-                float e[4];
+                float e[16];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool ok = v < G && 4 * v + j < N;
-                    e[j] = ok ? __builtin_amdgcn_exp2f((x[u][j] - bm) * XV_LOG2E) : 0.f;
+                for (int c = 0; c < 16; ++c) {
+                    const bool ok = blk < nb && 16 * blk + c < N;
+                    e[c] = ok ? __builtin_amdgcn_exp2f((x[u][c] - bm) * XV_LOG2E) : 0.f;
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) e[j] = e[j] + __shfl_xor(e[j], 2);   // columns ^ 8
+                for (int c = 0; c < 8; ++c) e[c] = e[c] + e[c + 8];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) e[j] = e[j] + __shfl_xor(e[j], 1);   // columns ^ 4
-                const float w0 = e[0] + e[2], w1 = e[1] + e[3];                    // columns ^ 2
-                xv_lse_add(cm, cs, bm, w0 + w1);                                   // columns ^ 1
+                for (int c = 0; c < 4; ++c) e[c] = e[c] + e[c + 4];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) e[c] = e[c] + e[c + 2];
+                xv_lse_add(cm, cs, bm, e[0] + e[1]);
             }
         }
     }
@@ -137,7 +143,7 @@ void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb
     }
     if (lp) {
 #pragma unroll
-        for (int off = 4; off < 64; off <<= 1) xv_lse_add(cm, cs, __shfl_xor(cm, off), __shfl_xor(cs, off));
+        for (int off = 1; off < 64; off <<= 1) xv_lse_add(cm, cs, __shfl_xor(cm, off), __shfl_xor(cs, off));
     }
     if ((tid & 63) == 0) { sv[tid >> 6] = best; sn[tid >> 6] = bn; sm[tid >> 6] = cm; ssum[tid >> 6] = cs; }
     __syncthreads();

@@ -100,11 +100,11 @@ def test_split_rows_do_not_depend_on_the_row_count():
 def _logprob_bound(N: int, lp: np.ndarray) -> np.ndarray:
     """|lp_gpu - lp_exact| for fp32 logits.  Along the kernel's path to S a value passes
     a 16-column block (one exp2 with the rounding of a subtraction and a product in its
-    argument, four additions: under 8 units of 2^-24) and then up to ceil(N / 1024)
-    chain folds, four butterfly levels and three wave folds, each a rescaling by an
+    argument, four additions: under 8 units of 2^-24) and then up to ceil(N / 4096)
+    chain folds, six butterfly levels and three wave folds, each a rescaling by an
     exp2 and a product and one addition (under 18 units); the log2 and the ln 2 product
     add 2^-22 |lp|, and 2^-20 covers the exp2 of the largest arguments."""
-    depth = 8 + 18 * (-(-N // 1024) + 7)
+    depth = 8 + 18 * (-(-N // 4096) + 9)
     return depth * 2.0 ** -24 + 2.0 ** -22 * np.abs(lp) + 2.0 ** -20
 
 
