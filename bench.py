@@ -5,11 +5,13 @@ One step is the whole hot path of a speculative step for one layer, on one
 stream, with every input already resident in HBM:
     both projection GEMMs in one launch                              xv_gemm_small_m_pair
       (M = B*T rows, K = 5120, N = 10240 and N = 17408)
-    GDN verify, 48 value heads, fp32 state                          xv_gdn_verify
+    the previous step's rollback (its kept rows replayed from its start
+      state) and this step's GDN verify, 48 value heads, fp32 state xv_gdn_verify_after
     attention verify rows + KV append, 24 q / 4 KV heads, d = 256  xv_attn_verify_rows
     synthetic head over both outputs (2 x 6144 -> 4096, one launch) xv_gemm_small_m_pair
-    greedy ids, logprobs and accepted rows                          xv_greedy_accept
-    rollback of state and length to the accepted prefix             xv_rollback_to_prefix
+    greedy ids, logprobs, accepted rows and the new KV length       xv_greedy_accept
+The last step's rollback (xv_rollback_to_prefix) runs inside the timed region
+after the last step.
 The default workload is batch 1, k = 8 drafts (9 verify rows), 640 cached
 tokens.  Steps run as a real decoding loop: each step verifies against the
 state and cache the previous step of the same layer left.  Weights, states and
@@ -88,7 +90,8 @@ def parse():
 
 def build_layers(wl, Lmax, R, stream):
     """Inputs for workload wl, R resident layer replicas, and the bit-exact gate
-    (verify == sequential decode on the same buffers, every output bit)."""
+    (verify == sequential decode on the same buffers, every output bit; three lazy steps
+    == three steps of verify + rollback, every state, cache and output bit)."""
     import torch
     from bit_exact_speculative_amd import inputs as gen
     from bit_exact_speculative_amd.layer import Layer
@@ -113,6 +116,16 @@ def build_layers(wl, Lmax, R, stream):
                  same(gate.y2_32.view(wl.B, wl.T, wl.N2), dec["y2_32"]) and
                  torch.equal(gate.ids, dec["ids"]))
         del gate, dec
+        eager, lazy = base.clone(), base.clone()
+        for _ in range(3):
+            eager.verify()
+            eager.advance()
+            lazy.lazy_step()
+            exact = exact and same(eager.o_gdn, lazy.o_gdn) and torch.equal(eager.ids, lazy.ids) and \
+                same(eager.lp, lazy.lp) and torch.equal(eager.kv_len, lazy.kv_len)
+        lazy.settle()
+        exact = exact and same(eager.S_in, lazy.S_in) and same(eager.Kc, lazy.Kc)
+        del eager, lazy
         layers = [base] + [base.clone() for _ in range(R - 1)]
         torch.cuda.synchronize()
     print("# %d layer replicas resident; verify==decode bit-exact: %s" % (R, exact), file=sys.stderr, flush=True)
@@ -121,19 +134,24 @@ def build_layers(wl, Lmax, R, stream):
 
 def run_steps(layers, stream, steps, warmup, keep_all=False, gemm_events=False):
     """Warmup, then `steps` timed steps rotating over the replicas, bracketed by HIP events
-    on the layers' stream.  keep_all: every request keeps all T rows (full acceptance);
-    otherwise the greedy acceptance decides.  Returns (ms per step, per-step N2 GEMM us, wall s)."""
+    on the layers' stream.  keep_all: every request keeps all T rows (full acceptance; each
+    step rolls back at once); otherwise the greedy acceptance decides and each step's
+    rollback runs inside the next step's GDN launch, the last ones before the timed region
+    ends.  Returns (ms per step, per-step projection GEMM us, wall s)."""
     import torch
     R = len(layers)
     full = torch.full((layers[0].B,), layers[0].T, dtype=torch.int32, device="cuda") if keep_all else None
 
     def step(L, ev=None):
-        L.gemms(ev)                               # ev: recorded at the kernel's own start and end
-        L.gdn()
-        L.attn()
-        L.head()
-        L.rollback(full)
-        L.advance()
+        if keep_all:
+            L.gemms(ev)
+            L.gdn()
+            L.attn()
+            L.head()
+            L.rollback(full)
+            L.advance()
+        else:
+            L.lazy_step(ev)                       # ev: recorded at the GEMM's own start and end
 
     with torch.cuda.stream(stream):
         for s in range(warmup):
@@ -155,6 +173,8 @@ def run_steps(layers, stream, steps, warmup, keep_all=False, gemm_events=False):
         e_start.record(stream)
         for s in range(steps):
             step(layers[(warmup + s) % R], evs[s])
+        for L in layers:
+            L.settle()
         e_end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
@@ -285,19 +305,18 @@ def main():
 
     breakdown = None
     if args.breakdown:
-        names = ["projections_n%d_n%d" % (wl.N1, wl.N2), "gdn_verify", "attn_verify_rows",
-                 "head_gemms", "greedy_accept", "rollback"]
+        names = ["projections_n%d_n%d" % (wl.N1, wl.N2), "gdn_verify_after", "attn_verify_rows",
+                 "head_gemms", "greedy_accept"]
         acc = {k: [] for k in names}
         with torch.cuda.stream(stream):
             for s in range(min(args.steps, 50)):
                 L = layers[s % R]
-                fns = [L.gemms, L.gdn, L.attn, L.head_gemms, L.greedy, L.rollback]
+                fns = [L.gemms, L.gdn_lazy, L.attn, L.head_gemms, lambda: L.greedy(count_kv=True)]
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
                 ev[0].record(stream)
                 for i, f in enumerate(fns):
                     f()
                     ev[i + 1].record(stream)
-                L.advance()
                 torch.cuda.synchronize()
                 for i, k in enumerate(names):
                     acc[k].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
@@ -305,6 +324,7 @@ def main():
 
     # the same workload with every draft accepted (rollback keeps S_T as is)
     for L in layers:
+        L.settle()
         L.reset()
     ms_full, _, _ = run_steps(layers, stream, full_steps, full_warmup, keep_all=True)
 

@@ -86,23 +86,39 @@ __device__ __forceinline__ void xv_gdn_token(float (&s)[R], const float (&kk)[R]
     for (int r = 0; r < R; ++r) s[r] = __builtin_fmaf(u, kk[r], s[r]);
 }
 
-// ROLLBACK = false: verify of T tokens from state_in, writes o (and o32) and S_T.
-// ROLLBACK = true : n = n_keep[b]; n == T leaves state_out; otherwise recomputes
-//                   S_n from state_in; kv_len[b] += n.
+// What one launch runs, per request b: first n_pre = clamp(n_pre[b], 0, Tp) rows
+// of a previous call (its k, v, a, b; no outputs), then the T rows of this call
+// (q, k, v, a, b; outputs o), all with xv_gdn_token, from the state S_in; when
+// S_alt is given and n_pre == Tp, from S_alt with no replay instead.  The state
+// after the replayed rows goes to S_mid (when given), the final state to S_out.
+//   verify          : no previous rows (n_pre NULL), T rows
+//   rollback        : previous rows = the verify's, n_pre = n_keep, T = 0; n == Tp
+//                     leaves S_out as it is (it holds S_T); kv_len[b] += n
+//   verify after    : the previous call's kept rows replayed (or its S_T taken),
+//                     then T rows; S_mid receives the kept state of the previous call
+struct XvGdnArgs {
+    const uint16_t* kp; const uint16_t* vp; const float* ap; const float* bp;   // previous rows
+    const int32_t* n_pre;                   // [B] previous rows to replay, or NULL
+    int Tp;                                 // rows per request of the previous call
+    const float* S_alt;                     // S_T of the previous call, or NULL
+    const uint16_t* q; const uint16_t* k; const uint16_t* v; const float* a; const float* b;
+    int T;                                  // rows of this call (0: rollback)
+    const float* S_in; float* S_mid; float* S_out;
+    uint16_t* o; float* o32;
+    int32_t* kv_len;                        // rollback: += n
+    int Hk, Hv, dv;
+};
+
 template <int DK, bool ROLLBACK>
 __global__ __launch_bounds__(XV_GDN_THREADS)
-void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                   const uint16_t* __restrict__ v, const float* __restrict__ a,
-                   const float* __restrict__ beta, const float* __restrict__ S_in,
-                   float* __restrict__ S_out, uint16_t* __restrict__ o, float* __restrict__ o32,
-                   int T, int Hk, int Hv, int dv, int32_t* __restrict__ kv_len,
-                   const int32_t* __restrict__ n_keep)
+void xv_gdn_kernel(XvGdnArgs A)
 {
     constexpr int NT = XV_GDN_THREADS;
     constexpr int R = DK / XV_GDN_LPJ;
-    __shared__ __attribute__((aligned(16))) float skq[XV_GDN_TMAX][2][DK];   // k, q rows, fp32
-    __shared__ uint16_t sv[XV_GDN_TMAX][XV_GDN_JW];
-    __shared__ float sab[XV_GDN_TMAX][2];
+    constexpr int TM = 2 * XV_GDN_TMAX;      // replayed rows + rows of this call
+    __shared__ __attribute__((aligned(16))) float skq[TM][2][DK];   // k, q rows, fp32
+    __shared__ uint16_t sv[TM][XV_GDN_JW];
+    __shared__ float sab[TM][2];
     constexpr int SP = XV_GDN_JW + 1;        // state slab row pitch (floats)
     __shared__ float sst[DK * SP];           // the workgroup's state slab [i][32 values]
 
@@ -115,15 +131,24 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int j = blockIdx.x * XV_GDN_JW + jw;
     const int h = blockIdx.y;
     const int b = blockIdx.z;
+    const int Hk = A.Hk, Hv = A.Hv, dv = A.dv, T = A.T, Tp = A.Tp;
     const int g = h / (Hv / Hk);
 
-    int n = T;
-    if (ROLLBACK) {
-        n = n_keep[b];
-        n = n < 0 ? 0 : (n > T ? T : n);
-        if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) kv_len[b] += n;
-        if (n == T) return;                  // state_out already holds S_T
+    int np = 0;
+    const float* S0 = A.S_in;
+    if (A.n_pre) {
+        np = A.n_pre[b];
+        np = np < 0 ? 0 : (np > Tp ? Tp : np);
+        if (ROLLBACK) {
+            if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) A.kv_len[b] += np;
+            if (np == Tp) return;            // state_out already holds S_T
+        } else if (np == Tp && A.S_alt) {
+            S0 = A.S_alt;                    // every previous row kept: its S_T, nothing to replay
+            np = 0;
+        }
     }
+    const int nm = ROLLBACK ? 0 : T;         // rows of this call
+    const int n = np + nm;
 
     // the state slab S[i][j0 .. j0 + 32) moves through LDS so that global reads and
     // writes are 16-byte, 8 threads per 128-byte row
@@ -133,13 +158,20 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     xv_f32x4 sl[SPASS];
 #pragma unroll
     for (int e = 0; e < SPASS; ++e)
-        sl[e] = *reinterpret_cast<const xv_f32x4*>(S_in + slab + (size_t)(tid / 8 + e * SROWS) * dv);
+        sl[e] = *reinterpret_cast<const xv_f32x4*>(S0 + slab + (size_t)(tid / 8 + e * SROWS) * dv);
 
-    // stage the rows of tokens 0..n-1: every load is issued before any LDS store
-    // (straight-line, clamped to token 0), so the staging costs one round trip
+    // stage the rows of tokens 0..n-1 (replayed rows first): every load is issued
+    // before any LDS store (straight-line, clamped to token 0), so the staging costs
+    // one round trip
     constexpr int CH = DK / 8;               // 16-byte chunks per k or q row
-    constexpr int KQ_PER = (XV_GDN_TMAX * 2 * CH + NT - 1) / NT;
-    constexpr int V_PER = (XV_GDN_TMAX * XV_GDN_JW + NT - 1) / NT;
+    constexpr int KQ_PER = (TM * 2 * CH + NT - 1) / NT;
+    constexpr int V_PER = (TM * XV_GDN_JW + NT - 1) / NT;
+    // row t of the launch: replayed row t of the previous call, or row t - np of this one
+    auto kq_src = [&](int t, int which) -> const uint16_t* {
+        if (t < np) return A.kp + (((size_t)b * Tp + t) * Hk + g) * DK;
+        const size_t row = ((size_t)b * T + (t - np)) * Hk + g;
+        return (which == 0 ? A.k : A.q) + row * DK;
+    };
     if (n > 0) {                             // uniform
         xv_u32x4 kq[KQ_PER];
         uint16_t vv[V_PER];
@@ -149,21 +181,23 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             int idx = tid + e * NT;
             idx = idx < n * 2 * CH ? idx : 0;
             const int t = idx / (2 * CH), rem = idx % (2 * CH);
-            const int which = rem / CH, c = rem % CH;   // 0: k, 1: q
-            const size_t row = ((size_t)b * T + t) * Hk + g;
-            const uint16_t* src = (which == 0 || ROLLBACK ? k : q) + row * DK + c * 8;
-            kq[e] = xv_load16(src);
+            const int which = rem / CH, c = rem % CH;   // 0: k, 1: q (a replayed row: k again)
+            kq[e] = xv_load16(kq_src(t, which) + c * 8);
         }
 #pragma unroll
         for (int e = 0; e < V_PER; ++e) {
             int idx = tid + e * NT;
             idx = idx < n * XV_GDN_JW ? idx : 0;
             const int t = idx / XV_GDN_JW, c = idx % XV_GDN_JW;
-            vv[e] = v[(((size_t)b * T + t) * Hv + h) * dv + blockIdx.x * XV_GDN_JW + c];
+            const int jj = blockIdx.x * XV_GDN_JW + c;
+            vv[e] = t < np ? A.vp[(((size_t)b * Tp + t) * Hv + h) * dv + jj]
+                           : A.v[(((size_t)b * T + (t - np)) * Hv + h) * dv + jj];
         }
         {
             const int idx = tid < 2 * n ? tid : 0;
-            abv = ((idx & 1) ? beta : a)[((size_t)b * T + (idx >> 1)) * Hv + h];
+            const int t = idx >> 1;
+            abv = t < np ? ((idx & 1) ? A.bp : A.ap)[((size_t)b * Tp + t) * Hv + h]
+                         : ((idx & 1) ? A.b : A.a)[((size_t)b * T + (t - np)) * Hv + h];
         }
 #pragma unroll
         for (int e = 0; e < KQ_PER; ++e) {
@@ -199,6 +233,21 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
     for (int r = 0; r < R; ++r) s[r] = sst[(ig * R + r) * SP + jw];
 
+    // the slab of a state: own slots to LDS, then 16-byte rows out
+    auto store_state = [&](float* __restrict__ dst) {
+        __syncthreads();                     // every lane is done reading the slab
+#pragma unroll
+        for (int r = 0; r < R; ++r) sst[(ig * R + r) * SP + jw] = s[r];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < SPASS; ++e) {
+            xv_f32x4 out;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) out[c] = sst[(tid / 8 + e * SROWS) * SP + (tid & 7) * 4 + c];
+            *reinterpret_cast<xv_f32x4*>(dst + slab + (size_t)(tid / 8 + e * SROWS) * dv) = out;
+        }
+    };
+
     // Token t's rows are in registers while token t+1's are already being read from LDS.
     float kc[R], qc[R], kn[R], qn[R];
     float vj = 0.f, at = 0.f, bt = 0.f, vn = 0.f, an = 0.f, bn = 0.f;
@@ -228,29 +277,21 @@ void xv_gdn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         take();
     }
     for (int t = 0; t < n; ++t) {
+        if (!ROLLBACK && A.S_mid && t == np) store_state(A.S_mid);   // uniform: the kept state
         if (t + 1 < n) fetch(t + 1);         // uniform
         xv_gdn_token<R>(s, kc, vj, at, bt);
-        if (!ROLLBACK) {
+        if (!ROLLBACK && t >= np) {
             const float ot = xv_gdn_dot<R>(s, qc);
             if (ig == 0) {
-                const size_t oi = (((size_t)b * T + t) * Hv + h) * dv + j;
-                o[oi] = xv_f32_to_bf16(ot);
-                if (o32) o32[oi] = ot;
+                const size_t oi = (((size_t)b * T + (t - np)) * Hv + h) * dv + j;
+                A.o[oi] = xv_f32_to_bf16(ot);
+                if (A.o32) A.o32[oi] = ot;
             }
         }
         if (t + 1 < n) take();
     }
-
-#pragma unroll
-    for (int r = 0; r < R; ++r) sst[(ig * R + r) * SP + jw] = s[r];   // the lane's own slots
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < SPASS; ++e) {
-        xv_f32x4 out;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) out[c] = sst[(tid / 8 + e * SROWS) * SP + (tid & 7) * 4 + c];
-        *reinterpret_cast<xv_f32x4*>(S_out + slab + (size_t)(tid / 8 + e * SROWS) * dv) = out;
-    }
+    if (!ROLLBACK && A.S_mid && n == np) store_state(A.S_mid);      // no rows of this call
+    store_state(A.S_out);
 }
 
 int xv_gdn_check(const void* k, const void* v, const void* a, const void* b,
@@ -268,19 +309,12 @@ int xv_gdn_check(const void* k, const void* v, const void* a, const void* b,
 }
 
 template <bool ROLLBACK>
-int xv_gdn_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* a,
-                  const float* beta, const float* S_in, float* S_out, uint16_t* o, float* o32,
-                  int B, int T, int Hk, int Hv, int dk, int dv, int32_t* kv_len,
-                  const int32_t* n_keep, hipStream_t st)
+int xv_gdn_launch(const XvGdnArgs& args, int B, int dk, hipStream_t st)
 {
-    dim3 grid(dv / XV_GDN_JW, Hv, B), block(XV_GDN_THREADS);
+    dim3 grid(args.dv / XV_GDN_JW, args.Hv, B), block(XV_GDN_THREADS);
     (void)hipGetLastError();
-    if (dk == 128)
-        hipLaunchKernelGGL((xv_gdn_kernel<128, ROLLBACK>), grid, block, 0, st, q, k, v, a, beta,
-                           S_in, S_out, o, o32, T, Hk, Hv, dv, kv_len, n_keep);
-    else
-        hipLaunchKernelGGL((xv_gdn_kernel<64, ROLLBACK>), grid, block, 0, st, q, k, v, a, beta,
-                           S_in, S_out, o, o32, T, Hk, Hv, dv, kv_len, n_keep);
+    if (dk == 128) hipLaunchKernelGGL((xv_gdn_kernel<128, ROLLBACK>), grid, block, 0, st, args);
+    else hipLaunchKernelGGL((xv_gdn_kernel<64, ROLLBACK>), grid, block, 0, st, args);
     return xv_launch_status();
 }
 
@@ -296,8 +330,43 @@ extern "C" int xv_gdn_verify(const uint16_t* q, const uint16_t* k, const uint16_
     if (s != XV_OK || B == 0) return s;
     XV_REQUIRE(q && o, XV_ERR_NULL);
     XV_REQUIRE(xv_aligned16(q) && xv_aligned(o, 2) && xv_aligned(o32, 4), XV_ERR_ALIGN);
-    return xv_gdn_launch<false>(q, k, v, a, b, state_in, state_out, o, o32, B, T, Hk, Hv, dk, dv,
-                                nullptr, nullptr, reinterpret_cast<hipStream_t>(stream));
+    XvGdnArgs args{};
+    args.q = q; args.k = k; args.v = v; args.a = a; args.b = b; args.T = T;
+    args.S_in = state_in; args.S_out = state_out; args.o = o; args.o32 = o32;
+    args.Hk = Hk; args.Hv = Hv; args.dv = dv;
+    return xv_gdn_launch<false>(args, B, dk, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int xv_gdn_verify_after(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const float* a, const float* b,
+                                   const uint16_t* k_prev, const uint16_t* v_prev,
+                                   const float* a_prev, const float* b_prev,
+                                   const int32_t* n_keep_prev, int T_prev,
+                                   const float* state_prev_in, const float* state_prev_out,
+                                   float* state_kept, float* state_out,
+                                   uint16_t* o, float* o32,
+                                   int B, int T, int Hk, int Hv, int dk, int dv, void* stream)
+{
+    int s = xv_gdn_check(k, v, a, b, state_prev_in, state_out, B, T, Hk, Hv, dk, dv);
+    if (s != XV_OK) return s;
+    XV_REQUIRE(T_prev >= 1 && T_prev <= XV_GDN_TMAX, XV_ERR_SHAPE);
+    if (B == 0) return XV_OK;
+    XV_REQUIRE(q && o && k_prev && v_prev && a_prev && b_prev && n_keep_prev && state_prev_out && state_kept,
+               XV_ERR_NULL);
+    XV_REQUIRE(xv_aligned16(q) && xv_aligned(o, 2) && xv_aligned(o32, 4) && xv_aligned16(k_prev) &&
+               xv_aligned(v_prev, 2) && xv_aligned(a_prev, 4) && xv_aligned(b_prev, 4) &&
+               xv_aligned(n_keep_prev, 4) && xv_aligned16(state_prev_out) && xv_aligned16(state_kept),
+               XV_ERR_ALIGN);
+    XV_REQUIRE(state_out != state_prev_out && state_kept != state_prev_in && state_kept != state_prev_out &&
+               state_kept != state_out, XV_ERR_ALIAS);
+    XvGdnArgs args{};
+    args.kp = k_prev; args.vp = v_prev; args.ap = a_prev; args.bp = b_prev;
+    args.n_pre = n_keep_prev; args.Tp = T_prev; args.S_alt = state_prev_out;
+    args.q = q; args.k = k; args.v = v; args.a = a; args.b = b; args.T = T;
+    args.S_in = state_prev_in; args.S_mid = state_kept; args.S_out = state_out;
+    args.o = o; args.o32 = o32;
+    args.Hk = Hk; args.Hv = Hv; args.dv = dv;
+    return xv_gdn_launch<false>(args, B, dk, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int xv_rollback_to_prefix(const uint16_t* k, const uint16_t* v,
@@ -310,7 +379,9 @@ extern "C" int xv_rollback_to_prefix(const uint16_t* k, const uint16_t* v,
     if (s != XV_OK || B == 0) return s;
     XV_REQUIRE(kv_len && n_keep, XV_ERR_NULL);
     XV_REQUIRE(xv_aligned(kv_len, 4) && xv_aligned(n_keep, 4), XV_ERR_ALIGN);
-    return xv_gdn_launch<true>(nullptr, k, v, a, b, state_in, state_out, nullptr, nullptr,
-                               B, T, Hk, Hv, dk, dv, kv_len, n_keep,
-                               reinterpret_cast<hipStream_t>(stream));
+    XvGdnArgs args{};
+    args.kp = k; args.vp = v; args.ap = a; args.bp = b; args.n_pre = n_keep; args.Tp = T;
+    args.T = 0; args.S_in = state_in; args.S_out = state_out; args.kv_len = kv_len;
+    args.Hk = Hk; args.Hv = Hv; args.dv = dv;
+    return xv_gdn_launch<true>(args, B, dk, reinterpret_cast<hipStream_t>(stream));
 }

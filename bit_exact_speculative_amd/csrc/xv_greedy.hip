@@ -162,8 +162,9 @@ void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb
 
 // One thread per request: accepted drafts = leading rows whose id equals the next draft.
 // All of the request's ids and drafts are loaded before the first compare (one round trip).
+// kv_len (optional): the request's cached length grows by the kept rows.
 __global__ void xv_accept_kernel(const int32_t* __restrict__ draft, const int32_t* __restrict__ ids,
-                                 int B, int T, int32_t* __restrict__ n_keep)
+                                 int B, int T, int32_t* __restrict__ n_keep, int32_t* __restrict__ kv_len)
 {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= B) return;
@@ -182,19 +183,21 @@ __global__ void xv_accept_kernel(const int32_t* __restrict__ draft, const int32_
         acc += run ? 1 : 0;
     }
     n_keep[b] = acc + 1;
+    if (kv_len) kv_len[b] += acc + 1;
 }
 
 }  // namespace
 
 extern "C" int xv_greedy_accept(const float* logits_a, const float* logits_b, const int32_t* draft,
                                 int B, int T, int N, int32_t* ids, int32_t* n_keep, float* logprob,
-                                void* stream)
+                                int32_t* kv_len, void* stream)
 {
     XV_REQUIRE(B >= 0 && T >= 1 && T <= XV_TMAX && N >= 1, XV_ERR_SHAPE);
     if (B == 0) return XV_OK;
     XV_REQUIRE(logits_a && draft && ids && n_keep, XV_ERR_NULL);
     XV_REQUIRE(xv_aligned(logits_a, 4) && xv_aligned(logits_b, 4) && xv_aligned(draft, 4) &&
-               xv_aligned(ids, 4) && xv_aligned(n_keep, 4) && xv_aligned(logprob, 4), XV_ERR_ALIGN);
+               xv_aligned(ids, 4) && xv_aligned(n_keep, 4) && xv_aligned(logprob, 4) &&
+               xv_aligned(kv_len, 4), XV_ERR_ALIGN);
     (void)hipGetLastError();
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     // 16-byte loads when every row starts 16-byte aligned; the argmax is the same either way
@@ -204,6 +207,6 @@ extern "C" int xv_greedy_accept(const float* logits_a, const float* logits_b, co
     else hipLaunchKernelGGL(xv_argmax_kernel<false>, grid, block, 0, st, logits_a, logits_b, T, N, ids, logprob);
     const int s1 = xv_launch_status();
     if (s1 != XV_OK) return s1;
-    hipLaunchKernelGGL(xv_accept_kernel, dim3((B + 63) / 64), dim3(64), 0, st, draft, ids, B, T, n_keep);
+    hipLaunchKernelGGL(xv_accept_kernel, dim3((B + 63) / 64), dim3(64), 0, st, draft, ids, B, T, n_keep, kv_len);
     return xv_launch_status();
 }

@@ -13,7 +13,12 @@ decoding) and runs, on one stream:
   xv_greedy_accept      ids, logprobs, accepted rows
   xv_rollback_to_prefix state and KV length of the kept rows
 
-and emits ids[b][0 .. n_keep[b]-1]; the last one is the next root.  The post's
+and emits ids[b][0 .. n_keep[b]-1]; the last one is the next root.  With
+lazy=True (the default) the rollback is folded into the next step: the greedy
+kernel adds n_keep to the KV length, and the next step's xv_gdn_verify_after
+replays the kept rows from the previous start state (or takes S_T when every
+row was kept) before its own rows; the state of the kept rows is materialised
+only when asked for (settle()).  Both orders give the same bits.  The post's
 claim (first paragraph; the paragraph on the two verify changes) is that the
 emitted ids and logprobs do not depend on k or on the drafts; the tests check
 that bit for bit.  Torch provides device memory and the stream only.
@@ -89,9 +94,10 @@ class Decoder:
     """
 
     def __init__(self, inp: Inputs, Lmax: int, device="cuda", S0: Optional[np.ndarray] = None, stream=None,
-                 projections: Optional[Callable] = None):
+                 projections: Optional[Callable] = None, lazy: bool = True):
         """projections(decoder, rows, tokens): an alternative that fills rows.y1 and rows.y2
-        from rows.x (for diagnostics of non-exact variants); None = xv_gemm_small_m_pair."""
+        from rows.x (for diagnostics of non-exact variants); None = xv_gemm_small_m_pair.
+        lazy: fold each step's rollback into the next step's GDN launch."""
         wl = inp.wl
         self.wl, self.device, self.stream = wl, device, stream
         self.projections = projections
@@ -108,18 +114,42 @@ class Decoder:
         self.Vc[:, :, :L] = _bf16(inp.v_cache, device)
         self.kv_len = torch.from_numpy(inp.L0.astype(np.int32)).to(device)
         if S0 is None:
-            self.S = prefix_state(inp, device, stream)
+            self._S = prefix_state(inp, device, stream)
         else:
-            self.S = torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).to(device)
-        self.S2 = torch.empty_like(self.S)
+            self._S = torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).to(device)
+        self._S2 = torch.empty_like(self._S)
+        self.lazy = lazy
+        # lazy mode: (rows of the last step, its start state, its S_T), and two free states;
+        # while a step is pending, _S and _S2 are its start state and its S_T
+        self._pending = None
+        self._free = (torch.empty_like(self._S), torch.empty_like(self._S)) if lazy else None
+        self._kv_scratch = torch.zeros_like(self.kv_len)
+        self._slot = 0
         self.Lmax = Lmax
         self.scale = 1.0 / float(wl.d) ** 0.5
         self._rows = {}
 
-    def rows(self, T: int) -> _Rows:
-        if T not in self._rows:
-            self._rows[T] = _Rows(self.wl, T, self.Lmax, self.device)
-        return self._rows[T]
+    def rows(self, T: int, slot: int = 0) -> _Rows:
+        key = (T, slot)
+        if key not in self._rows:
+            self._rows[key] = _Rows(self.wl, T, self.Lmax, self.device)
+        return self._rows[key]
+
+    @property
+    def S(self) -> torch.Tensor:
+        """The GDN state after every kept row (settles a pending rollback)."""
+        self.settle()
+        return self._S
+
+    def settle(self):
+        """Lazy mode: run the last step's rollback now (the KV length was already updated)."""
+        if self._pending is None:
+            return
+        Rp, P, Q = self._pending
+        xv.xv_rollback_to_prefix(Rp.k, Rp.v, Rp.a, Rp.b, P, Q, self._kv_scratch, Rp.n_keep,
+                                 stream=self.stream)
+        self._S, self._S2 = Q, P
+        self._pending = None
 
     def step(self, tokens: torch.Tensor) -> _Rows:
         """One decoding step over tokens, a contiguous int32 [B][T] device tensor (read in
@@ -127,7 +157,9 @@ class Decoder:
         The state advances to the kept rows."""
         wl, st = self.wl, self.stream
         B, T = tokens.shape
-        R = self.rows(T)
+        R = self.rows(T, self._slot)
+        if self.lazy:
+            self._slot ^= 1                  # the previous step's rows stay intact for the replay
         M = B * T
         xv.xv_embed_rows(self.E, tokens, R.x, stream=st)
         if self.projections is None:
@@ -135,15 +167,30 @@ class Decoder:
         else:
             self.projections(self, R, tokens)
         xv.xv_split_projections(R.y1, R.y2, R.q, R.k, R.v, R.a, R.b, R.qa, R.kn, R.vn, stream=st)
-        xv.xv_gdn_verify(R.q, R.k, R.v, R.a, R.b, self.S, self.S2, R.o_gdn, None, stream=st)
+        if not self.lazy:
+            xv.xv_gdn_verify(R.q, R.k, R.v, R.a, R.b, self._S, self._S2, R.o_gdn, None, stream=st)
+        elif self._pending is None:
+            xv.xv_gdn_verify(R.q, R.k, R.v, R.a, R.b, self._S, self._S2, R.o_gdn, None, stream=st)
+            self._pending = (R, self._S, self._S2)
+        else:
+            Rp, P, Q = self._pending
+            K, O = self._free
+            xv.xv_gdn_verify_after(R.q, R.k, R.v, R.a, R.b, Rp.k, Rp.v, Rp.a, Rp.b, Rp.n_keep,
+                                   P, Q, K, O, R.o_gdn, None, stream=st)
+            self._pending, self._free = (R, K, O), (P, Q)
+            self._S, self._S2 = K, O         # the pending step's start state and S_T
         xv.xv_attn_verify_rows(R.qa, R.kn, R.vn, self.Kc, self.Vc, self.kv_len, R.o_attn, None, R.ws,
                                self.scale, stream=st)
         xv.xv_gemm_small_m_pair(R.o_gdn.view(M, wl.Hv * wl.dv), self.Wh_g, R.lg, R.lg32,
                                 R.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, R.la, R.la32, stream=st)
-        xv.xv_greedy_accept(R.lg32.view(B, T, wl.NH), R.la32.view(B, T, wl.NH), tokens, R.ids,
-                            R.n_keep, R.lp, stream=st)
-        xv.xv_rollback_to_prefix(R.k, R.v, R.a, R.b, self.S, self.S2, self.kv_len, R.n_keep, stream=st)
-        self.S, self.S2 = self.S2, self.S
+        if self.lazy:
+            xv.xv_greedy_accept(R.lg32.view(B, T, wl.NH), R.la32.view(B, T, wl.NH), tokens, R.ids,
+                                R.n_keep, R.lp, stream=st, kv_len=self.kv_len)
+        else:
+            xv.xv_greedy_accept(R.lg32.view(B, T, wl.NH), R.la32.view(B, T, wl.NH), tokens, R.ids,
+                                R.n_keep, R.lp, stream=st)
+            xv.xv_rollback_to_prefix(R.k, R.v, R.a, R.b, self._S, self._S2, self.kv_len, R.n_keep, stream=st)
+            self._S, self._S2 = self._S2, self._S
         return R
 
     def snapshot(self):
@@ -152,7 +199,8 @@ class Decoder:
 
     def restore(self, snap):
         S, Kc, Vc, kv = snap
-        self.S.copy_(S); self.Kc.copy_(Kc); self.Vc.copy_(Vc); self.kv_len.copy_(kv)
+        self._pending = None
+        self._S.copy_(S); self.Kc.copy_(Kc); self.Vc.copy_(Vc); self.kv_len.copy_(kv)
 
     def generate(self, root: np.ndarray, n_tokens: int,
                  drafts: Optional[Callable[[int, int, int], np.ndarray]] = None, k: int = 0,
@@ -177,7 +225,7 @@ class Decoder:
                     tok[bb, 1:] = drafts(bb, len(out_ids[bb]), k)
             if record is not None:
                 record.append(tok.copy())
-            R = self.rows(k + 1)
+            R = self.rows(k + 1, self._slot)
             R.tokens.copy_(torch.from_numpy(tok))
             self.step(R.tokens)
             ids = R.ids.cpu().numpy()

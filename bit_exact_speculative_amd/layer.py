@@ -10,6 +10,10 @@ KV cache, the verify rows) and runs, on one stream:
               synthetic head logits              (xv_gemm_small_m_pair on o_gdn and o_attn)
               greedy ids, logprobs, accepted rows (xv_greedy_accept)
               rollback to the accepted prefix    (xv_rollback_to_prefix)
+  lazy_step()  the same step with the rollback folded into the next step's GDN
+              launch (xv_gdn_verify_after replays the kept rows; the greedy
+              kernel adds the kept rows to the KV length); settle() runs the
+              last pending rollback.
   decode_sequence()  the same layer advanced one token at a time (T = 1, M = B)
               over the same rows, which verify must reproduce bit for bit.
 
@@ -106,6 +110,10 @@ class Layer:
             self.ids = torch.empty((B, T), dtype=torch.int32, device=device)
             self.lp = torch.empty((B, T), dtype=torch.float32, device=device)
         self.n_keep = torch.full((B,), T, dtype=torch.int32, device=device)
+        self.pending = False         # lazy mode: S_in -> S_out ran, its rollback has not
+        self.S_kept = None           # lazy mode: the two further state buffers
+        self.S_next = None
+        self.kv_scratch = None       # lazy mode: the pending rollback's KV count goes here
         self.proj_fp32 = True        # also write the fp32 projection outputs
         self.out_fp32 = True         # also write the fp32 GDN / attention outputs
 
@@ -174,10 +182,50 @@ class Layer:
                                 self.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, self.la, self.la32,
                                 stream=self.stream)
 
-    def greedy(self):
+    def greedy(self, count_kv: bool = False):
+        """count_kv: the kernel also adds the kept rows to kv_len (lazy mode)."""
         wl = self.wl
         xv.xv_greedy_accept(self.lg32.view(self.B, self.T, wl.NH), self.la32.view(self.B, self.T, wl.NH),
-                            self.draft, self.ids, self.n_keep, self.lp, stream=self.stream)
+                            self.draft, self.ids, self.n_keep, self.lp, stream=self.stream,
+                            kv_len=self.kv_len if count_kv else None)
+
+    def gdn_lazy(self):
+        """GDN of a lazy step: the first one is xv_gdn_verify; later ones replay the previous
+        step's kept rows (the same row buffers, n_keep from its greedy) from its start state,
+        then run this step's rows (xv_gdn_verify_after).  S_in / S_out are the pending step's
+        start state and S_T afterwards."""
+        if self.S_kept is None:
+            self.S_kept, self.S_next = torch.empty_like(self.S_in), torch.empty_like(self.S_in)
+            self.kv_scratch = torch.zeros_like(self.kv_len)
+        if not self.pending:
+            self.gdn()
+            self.pending = True
+            return
+        xv.xv_gdn_verify_after(self.q, self.k, self.v, self.a, self.b, self.k, self.v, self.a, self.b,
+                               self.n_keep, self.S_in, self.S_out, self.S_kept, self.S_next,
+                               self.o_gdn, self.o_gdn32 if self.out_fp32 else None, stream=self.stream)
+        self.S_in, self.S_out, self.S_kept, self.S_next = self.S_kept, self.S_next, self.S_in, self.S_out
+
+    def lazy_step(self, events=None):
+        """One speculative step with the rollback deferred to the next step's GDN launch."""
+        if not self.has_head:
+            raise ValueError("a lazy step needs the head: its acceptance counts the kept rows")
+        if self.has_gemm:
+            self.gemms(events)
+        self.gdn_lazy()
+        self.attn()
+        self.head_gemms()
+        self.greedy(count_kv=True)
+
+    def settle(self):
+        """Lazy mode: the pending rollback (state only; the greedy kernel counted the KV
+        rows), then S_in is the kept state as after verify + rollback + advance."""
+        if not self.pending:
+            return
+        xv.xv_rollback_to_prefix(self.k, self.v, self.a, self.b, self.S_in, self.S_out, self.kv_scratch,
+                                 self.n_keep, stream=self.stream)
+        self.advance()
+        self.pending = False
 
     def head(self):
         self.head_gemms()

@@ -51,7 +51,9 @@ _lib.xv_attn_verify_rows.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
 _lib.xv_rollback_to_prefix.restype = _I
 _lib.xv_rollback_to_prefix.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
 _lib.xv_greedy_accept.restype = _I
-_lib.xv_greedy_accept.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P]
+_lib.xv_greedy_accept.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P]
+_lib.xv_gdn_verify_after.restype = _I
+_lib.xv_gdn_verify_after.argtypes = [_P] * 10 + [_I] + [_P] * 6 + [_I] * 6 + [_P]
 _lib.xv_embed_rows.restype = _I
 _lib.xv_embed_rows.argtypes = [_P, _P, _I, _I, _I, _P, _P]
 _lib.xv_split_projections.restype = _I
@@ -174,6 +176,29 @@ def xv_gdn_verify(q, k, v, a, b, state_in, state_out, o, o32=None, stream=None):
                                               B, T, Hk, Hv, dk, dv, _stream(stream)))
 
 
+def xv_gdn_verify_after(q, k, v, a, b, k_prev, v_prev, a_prev, b_prev, n_keep_prev,
+                        state_prev_in, state_prev_out, state_kept, state_out, o, o32=None, stream=None):
+    """The kept rows of the previous verify (k_prev .. b_prev, n_keep_prev) replayed from
+    state_prev_in (or state_prev_out when all were kept) into state_kept, then a verify of
+    this call's rows from it into state_out; as xv_rollback_to_prefix + xv_gdn_verify."""
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    Tp = k_prev.shape[1]
+    st = (B, Hv, dk, dv)
+    if tuple(k.shape) != (B, T, Hk, dk) or tuple(v.shape[:2]) != (B, T) or \
+            tuple(a.shape) != (B, T, Hv) or tuple(b.shape) != (B, T, Hv) or \
+            tuple(k_prev.shape) != (B, Tp, Hk, dk) or tuple(v_prev.shape) != (B, Tp, Hv, dv) or \
+            tuple(a_prev.shape) != (B, Tp, Hv) or tuple(b_prev.shape) != (B, Tp, Hv) or \
+            tuple(n_keep_prev.shape) != (B,) or \
+            any(tuple(s.shape) != st for s in (state_prev_in, state_prev_out, state_kept, state_out)) or \
+            tuple(o.shape) != (B, T, Hv, dv) or (o32 is not None and tuple(o32.shape) != (B, T, Hv, dv)):
+        raise ValueError("xv_gdn_verify_after: shape mismatch")
+    _check("xv_gdn_verify_after", _lib.xv_gdn_verify_after(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(k_prev), _ptr(v_prev), _ptr(a_prev),
+        _ptr(b_prev), _ptr(n_keep_prev), Tp, _ptr(state_prev_in), _ptr(state_prev_out),
+        _ptr(state_kept), _ptr(state_out), _ptr(o), _ptr(o32), B, T, Hk, Hv, dk, dv, _stream(stream)))
+
+
 def xv_attn_verify_rows(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32=None, workspace=None,
                         scale=None, stream=None):
     """Attention rows + KV append.  q [B][T][Hq][d]; caches [B][Hkv][Lmax][d]; kv_len int32 [B]."""
@@ -208,17 +233,19 @@ def xv_rollback_to_prefix(k, v, a, b, state_in, state_out, kv_len, n_keep, strea
         _ptr(n_keep), B, T, Hk, Hv, dk, dv, _stream(stream)))
 
 
-def xv_greedy_accept(logits_a, logits_b, draft, ids, n_keep, logprob=None, stream=None):
+def xv_greedy_accept(logits_a, logits_b, draft, ids, n_keep, logprob=None, stream=None, kv_len=None):
     """ids = argmax(logits_a + logits_b) per row (lowest index on ties); n_keep per request;
-    logprob (optional fp32 [B][T]) = log-softmax of each row at its id."""
+    logprob (optional fp32 [B][T]) = log-softmax of each row at its id; kv_len (optional
+    int32 [B]) += n_keep."""
     B, T, N = logits_a.shape
     if (logits_b is not None and tuple(logits_b.shape) != (B, T, N)) or tuple(draft.shape) != (B, T) \
             or tuple(ids.shape) != (B, T) or tuple(n_keep.shape) != (B,) or \
-            (logprob is not None and tuple(logprob.shape) != (B, T)):
+            (logprob is not None and tuple(logprob.shape) != (B, T)) or \
+            (kv_len is not None and tuple(kv_len.shape) != (B,)):
         raise ValueError("xv_greedy_accept: shape mismatch")
     _check("xv_greedy_accept", _lib.xv_greedy_accept(_ptr(logits_a), _ptr(logits_b), _ptr(draft),
                                                     B, T, N, _ptr(ids), _ptr(n_keep), _ptr(logprob),
-                                                    _stream(stream)))
+                                                    _ptr(kv_len), _stream(stream)))
 
 
 def xv_embed_rows(table, tokens, x, stream=None):

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define XV_ABI_VERSION 2
+#define XV_ABI_VERSION 3
 
 typedef enum {
     XV_OK = 0,
@@ -134,6 +134,41 @@ int xv_gdn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   int B, int T, int Hk, int Hv, int dk, int dv, void* stream);
 
 /*
+ * GDN verify after a verify whose rollback was not run (a lazy rollback: one
+ * launch instead of a rollback and a verify).  The previous call ran T_prev
+ * rows from state_prev_in to state_prev_out, and n = n_keep_prev[b] of its rows
+ * were kept (clamped to [0, T_prev]).  The state of the kept rows is
+ *   n == T_prev : state_prev_out (S_T of the previous call; nothing replayed)
+ *   otherwise   : S_n, recomputed from state_prev_in over the previous call's
+ *                 rows 0..n-1 with the per-token arithmetic of xv_gdn_verify
+ * and is written to state_kept; then this call's T rows run from it exactly as
+ * in xv_gdn_verify (state_out <- S_T, o and o32 for this call's rows).  Every
+ * result equals xv_rollback_to_prefix followed by xv_gdn_verify, bit for bit.
+ * The cache length is not touched (xv_greedy_accept's kv_len does that).
+ *   q, k, v, a, b, o, o32 : as xv_gdn_verify (this call's rows)
+ *   k_prev, v_prev, a_prev, b_prev : the previous call's rows, layouts as k, v, a, b
+ *                         with T_prev rows ([16B] k_prev); read only
+ *   n_keep_prev         : int32 [B] device
+ *   state_prev_in/out   : fp32 [B][Hv][dk][dv] [16B], read only
+ *   state_kept          : fp32 [B][Hv][dk][dv] [16B], written
+ *   state_out           : fp32 [B][Hv][dk][dv] [16B], written
+ * The four states must be distinct buffers (XV_ERR_ALIAS).  Shapes as
+ * xv_gdn_verify, and 1 <= T_prev <= 16.  After the last step of a sequence,
+ * xv_rollback_to_prefix over the last call's rows leaves the kept state in that
+ * call's state_out; it also adds n_keep to its kv_len argument, so pass it a
+ * scratch array when xv_greedy_accept has already counted the rows.
+ */
+int xv_gdn_verify_after(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const float* a, const float* b,
+                        const uint16_t* k_prev, const uint16_t* v_prev,
+                        const float* a_prev, const float* b_prev,
+                        const int32_t* n_keep_prev, int T_prev,
+                        const float* state_prev_in, const float* state_prev_out,
+                        float* state_kept, float* state_out,
+                        uint16_t* o, float* o32,
+                        int B, int T, int Hk, int Hv, int dk, int dv, void* stream);
+
+/*
  * Attention verify rows with the KV append.
  * The post, the two verify changes (verify attention as one decode row per
  * draft position) and the launch command (BF16 KV cache).  Request b holds
@@ -198,7 +233,10 @@ int xv_rollback_to_prefix(const uint16_t* k, const uint16_t* v,
  * among the maxima of row (b, t).  Row t consumed input token draft[b][t]
  * (draft[b][0] is the root); draft t+1 is accepted when it equals ids[b][t] and
  * all earlier drafts were accepted.  n_keep[b] = 1 + accepted drafts (the verify
- * rows to keep, ready for xv_rollback_to_prefix).  logprob (may be NULL):
+ * rows to keep, ready for xv_rollback_to_prefix or xv_gdn_verify_after).
+ * kv_len (may be NULL): int32 [B] device, kv_len[b] += n_keep[b], the cache
+ * length after the kept rows (then no rollback call may add it again).
+ * logprob (may be NULL):
  * logprob[b][t] = log softmax(logits[b][t])[ids[b][t]] = -ln sum_n e^(z_n - max z),
  * fp32, in an order fixed by N alone (not by B, T or the pointers' alignment).
  *   logits_a, logits_b : fp32 [B][T][N]     draft : int32 [B][T]
@@ -207,7 +245,7 @@ int xv_rollback_to_prefix(const uint16_t* k, const uint16_t* v,
  */
 int xv_greedy_accept(const float* logits_a, const float* logits_b, const int32_t* draft,
                      int B, int T, int N, int32_t* ids, int32_t* n_keep, float* logprob,
-                     void* stream);
+                     int32_t* kv_len, void* stream);
 
 /*
  * Token embedding rows in front of the projection GEMMs of a decoding step

@@ -26,7 +26,7 @@ def test_every_header_symbol_is_exported(xv):
                           "xv_rollback_to_prefix", "xv_attn_workspace_bytes",
                           "xv_attn_chunk_tokens", "xv_abi_version", "xv_status_string",
                           "xv_greedy_accept", "xv_embed_rows", "xv_split_projections",
-                          "xv_gemm_small_m_pair"}
+                          "xv_gemm_small_m_pair", "xv_gdn_verify_after"}
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -36,7 +36,7 @@ def test_every_header_symbol_is_exported(xv):
 
 
 def test_version_and_constants(xv):
-    assert xv.xv_abi_version() == 2
+    assert xv.xv_abi_version() == 3
     assert xv.xv_attn_chunk_tokens() == 256
     lib = xv.lib()
     assert lib.xv_status_string(0) == b"ok"
@@ -99,6 +99,25 @@ def test_gdn_argument_errors(xv):
     assert r(A, A, A, A, A, A + 0x1000, A, A, 0, 9, 16, 48, 128, 128, None) == 0
 
 
+def test_gdn_verify_after_argument_errors(xv):
+    f = xv.lib().xv_gdn_verify_after
+    ok = dict(Tp=9, B=1, T=9, Hk=16, Hv=48, dk=128, dv=128)
+    S = [A + 0x100000 * i for i in range(4)]     # four distinct 16-byte aligned states
+
+    def call(q=A, kp=A, vp=A, nk=A, si=S[0], sp=S[1], sk=S[2], so=S[3], o=A, o32=None, **kw):
+        s = dict(ok); s.update(kw)
+        return f(q, A, A, A, A, kp, vp, A, A, nk, s["Tp"], si, sp, sk, so, o, o32,
+                 s["B"], s["T"], s["Hk"], s["Hv"], s["dk"], s["dv"], None)
+
+    assert call(B=0) == 0
+    assert call(Tp=0) == -2 and call(Tp=17) == -2 and call(T=17) == -2 and call(dk=96) == -2
+    assert call(kp=None) == -1 and call(nk=None) == -1 and call(sk=None) == -1 and call(sp=None) == -1
+    assert call(q=None) == -1 and call(o=None) == -1
+    assert call(kp=MIS) == -3 and call(vp=ODD) == -3 and call(sk=S[2] + 4) == -3 and call(nk=A + 2) == -3
+    for bad in (dict(so=S[0]), dict(so=S[1]), dict(sk=S[0]), dict(sk=S[1]), dict(sk=S[3])):
+        assert call(**bad) == -6, bad
+
+
 def test_attn_argument_errors(xv):
     f = xv.lib().xv_attn_verify_rows
     need = xv.xv_attn_workspace_bytes(1, 9, 24, 256, 649)
@@ -117,12 +136,13 @@ def test_attn_argument_errors(xv):
 
 def test_greedy_argument_errors(xv):
     f = xv.lib().xv_greedy_accept
-    assert f(A, None, A, 0, 9, 4096, A, A, None, None) == 0
-    assert f(A, None, A, 1, 0, 4096, A, A, None, None) == -2
-    assert f(A, None, A, 1, 9, 0, A, A, None, None) == -2
-    assert f(None, None, A, 1, 9, 4096, A, A, None, None) == -1
-    assert f(A, ODD, A, 1, 9, 4096, A, A, None, None) == -3
-    assert f(A, None, A, 1, 9, 4096, A, A, A + 2, None) == -3     # logprob: fp32 alignment
+    assert f(A, None, A, 0, 9, 4096, A, A, None, None, None) == 0
+    assert f(A, None, A, 1, 0, 4096, A, A, None, None, None) == -2
+    assert f(A, None, A, 1, 9, 0, A, A, None, None, None) == -2
+    assert f(None, None, A, 1, 9, 4096, A, A, None, None, None) == -1
+    assert f(A, ODD, A, 1, 9, 4096, A, A, None, None, None) == -3
+    assert f(A, None, A, 1, 9, 4096, A, A, A + 2, None, None) == -3     # logprob: fp32 alignment
+    assert f(A, None, A, 1, 9, 4096, A, A, None, A + 2, None) == -3     # kv_len: int32 alignment
 
 
 def test_embed_and_split_argument_errors(xv):

@@ -233,3 +233,28 @@ def test_divergence_margin_diagnostic(name, seeds):
     assert r["exact_spec_diverged"] == 0
     assert r["flips_within_perturbation"]
     assert r["requests"] == gen.WORKLOADS[name].B * len(seeds)
+
+
+def test_lazy_rollback_decoding_equals_eager():
+    """Decoding with each rollback folded into the next step's GDN launch gives the ids,
+    logprobs, state, KV cache and lengths of verify + rollback per step, bit for bit."""
+    from bit_exact_speculative_amd.decode import Decoder
+    name, n, k = "batch8", 10, 8
+    wl = gen.WORKLOADS[name]
+    inp = gen.composed_inputs(wl)
+    S0 = prefix_state(inp)
+    Lmax = int(inp.L0.max()) + n + 2 * k + 2
+    ref = Decoder(inp, Lmax, S0=S0, lazy=False)
+    root = inp.extra["root"]
+    ids_r, _, _ = ref.generate(root, n + k)
+    runs = []
+    for lazy in (False, True):
+        dec = Decoder(inp, Lmax, S0=S0, lazy=lazy)
+        ids, lp, keeps = dec.generate(root, n, _drafts_from(ids_r, wl, 0.4, 11), k=k)
+        runs.append((ids, lp, keeps, dec.S.clone(), dec.kv_len.clone(), dec.Kc, dec.Vc))
+    (i0, l0, k0, S_0, kv0, K0, V0), (i1, l1, k1, S_1, kv1, K1, V1) = runs
+    assert np.array_equal(i0, i1) and np.array_equal(l0.view(np.int32), l1.view(np.int32))
+    assert all(np.array_equal(a, b) for a, b in zip(k0, k1))
+    assert torch.equal(kv0, kv1) and same_bits(S_0, S_1)
+    L = int(kv0.max())
+    assert same_bits(K0[:, :, :L], K1[:, :, :L]) and same_bits(V0[:, :, :L], V1[:, :, :L])

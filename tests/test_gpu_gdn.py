@@ -148,3 +148,79 @@ def test_gdn_repeatable():
     for _ in range(100):
         o, o32, S = _verify(d, S_in)
         assert same_bits(o32, o320) and same_bits(S, S0d)
+
+
+def _rows(seed, B, T, Hk, Hv, dk, dv):
+    r = random_gdn(np.random.default_rng(seed), B, T, Hk, Hv, dk, dv)
+    return _dev(r)
+
+
+@pytest.mark.parametrize("Tp,T,dk", [(9, 9, 128), (1, 16, 128), (16, 1, 64), (5, 12, 64), (16, 16, 128)])
+def test_verify_after_equals_rollback_then_verify(Tp, T, dk):
+    """One launch = xv_rollback_to_prefix of the previous call + xv_gdn_verify, bit for bit,
+    for every kept count (0, partial, all, and values clamped from outside [0, Tp])."""
+    B, Hk, Hv, dv = 6, 2, 4, 64
+    prev = _rows(1100 + Tp * 17 + T, B, Tp, Hk, Hv, dk, dv)
+    cur = _rows(1200 + Tp * 17 + T, B, T, Hk, Hv, dk, dv)
+    S0 = (np.random.default_rng(1300 + T).standard_normal((B, Hv, dk, dv)) * 0.05).astype(np.float32)
+    P = torch.from_numpy(S0).cuda()
+    _, _, Q = _verify(prev, P)
+    nk_list = [0, Tp, min(1, Tp), Tp // 2, -3, Tp + 4]
+    nk = torch.tensor(nk_list, dtype=torch.int32, device="cuda")
+    # the two-launch reference
+    S_roll = Q.clone()
+    kv = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    _xv().xv_rollback_to_prefix(prev["k"], prev["v"], prev["a"], prev["b"], P, S_roll, kv, nk)
+    o_ref, o32_ref, S_ref = _verify(cur, S_roll)
+    # one launch
+    K, O = torch.full_like(P, float("nan")), torch.full_like(P, float("nan"))
+    o = torch.empty_like(o_ref)
+    o32 = torch.empty_like(o32_ref)
+    P0, Q0 = P.clone(), Q.clone()
+    _xv().xv_gdn_verify_after(cur["q"], cur["k"], cur["v"], cur["a"], cur["b"], prev["k"], prev["v"],
+                              prev["a"], prev["b"], nk, P, Q, K, O, o, o32)
+    torch.cuda.synchronize()
+    assert kv.tolist() == [min(max(n, 0), Tp) for n in nk_list]
+    assert same_bits(K, S_roll) and same_bits(O, S_ref)
+    assert same_bits(o, o_ref) and same_bits(o32, o32_ref)
+    assert same_bits(P, P0) and same_bits(Q, Q0)                 # the previous states are read only
+
+
+def test_verify_after_chain_equals_sequential_decode():
+    """Five lazy steps of 9 rows with random kept counts, then the settling rollback:
+    every output row that was kept, and the final state, equal one-token decoding of the
+    kept rows."""
+    B, T, Hk, Hv, dk, dv = 3, 9, 2, 4, 128, 128
+    rng = np.random.default_rng(1400)
+    S0 = (rng.standard_normal((B, Hv, dk, dv)) * 0.05).astype(np.float32)
+    bufs = [torch.from_numpy(S0).cuda()] + [torch.empty((B, Hv, dk, dv), device="cuda") for _ in range(3)]
+    P, Q, K, O = bufs
+    steps = [_rows(1500 + i, B, T, Hk, Hv, dk, dv) for i in range(5)]
+    keeps = [rng.integers(1, T + 1, size=B).astype(np.int32) for _ in steps]
+    keeps[2][:] = T                                             # one step that keeps every row
+    outs = []
+    for i, d in enumerate(steps):
+        o = torch.empty((B, T, Hv, dv), dtype=torch.bfloat16, device="cuda")
+        o32 = torch.empty((B, T, Hv, dv), dtype=torch.float32, device="cuda")
+        if i == 0:
+            _xv().xv_gdn_verify(d["q"], d["k"], d["v"], d["a"], d["b"], P, Q, o, o32)
+        else:
+            pd, nk = steps[i - 1], torch.from_numpy(keeps[i - 1]).cuda()
+            _xv().xv_gdn_verify_after(d["q"], d["k"], d["v"], d["a"], d["b"], pd["k"], pd["v"], pd["a"],
+                                      pd["b"], nk, P, Q, K, O, o, o32)
+            P, Q, K, O = K, O, P, Q
+        outs.append((o, o32))
+    kv = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    last = steps[-1]
+    _xv().xv_rollback_to_prefix(last["k"], last["v"], last["a"], last["b"], P, Q,
+                                kv, torch.from_numpy(keeps[-1]).cuda())
+    torch.cuda.synchronize()
+    for bb in range(B):
+        S = torch.from_numpy(S0[bb:bb + 1]).cuda()
+        for i, d in enumerate(steps):
+            n = int(keeps[i][bb])
+            db = {k: v[bb:bb + 1, :n].contiguous() for k, v in d.items()}
+            od, o32d, Sd = _decode(db, S, n)
+            assert same_bits(outs[i][0][bb, :n], od[0]) and same_bits(outs[i][1][bb, :n], o32d[0]), (bb, i)
+            S = Sd[-1]
+        assert same_bits(Q[bb], S[0]), bb
