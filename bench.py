@@ -6,8 +6,8 @@ stream, with every input already resident in HBM:
     both projection GEMMs in one launch                              xv_gemm_small_m_pair
       (M = B*T rows, K = 5120, N = 10240 and N = 17408)
     the previous step's rollback (its kept rows replayed from its start
-      state) and this step's GDN verify, 48 value heads, fp32 state xv_gdn_verify_after
-    attention verify rows + KV append, 24 q / 4 KV heads, d = 256  xv_attn_verify_rows
+      state) and this step's GDN verify, 48 value heads, fp32 state, beside
+      attention verify rows + KV append, 24 q / 4 KV heads, d = 256 xv_gdn_attn_verify
     synthetic head over both outputs (2 x 6144 -> 4096, one launch) xv_gemm_small_m_pair
     greedy ids, logprobs, accepted rows and the new KV length       xv_greedy_accept
 The last step's rollback (xv_rollback_to_prefix) runs inside the timed region
@@ -305,13 +305,12 @@ def main():
 
     breakdown = None
     if args.breakdown:
-        names = ["projections_n%d_n%d" % (wl.N1, wl.N2), "gdn_verify_after", "attn_verify_rows",
-                 "head_gemms", "greedy_accept"]
+        names = ["projections_n%d_n%d" % (wl.N1, wl.N2), "gdn_attn_verify", "head_gemms", "greedy_accept"]
         acc = {k: [] for k in names}
         with torch.cuda.stream(stream):
             for s in range(min(args.steps, 50)):
                 L = layers[s % R]
-                fns = [L.gemms, L.gdn_lazy, L.attn, L.head_gemms, lambda: L.greedy(count_kv=True)]
+                fns = [L.gemms, L.gdn_attn_lazy, L.head_gemms, lambda: L.greedy(count_kv=True)]
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
                 ev[0].record(stream)
                 for i, f in enumerate(fns):

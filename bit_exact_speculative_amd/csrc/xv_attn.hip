@@ -38,6 +38,7 @@
 // Masked positions are excluded by index, never by value, and positions at or
 // past L0 + T are never read (their LDS slots are zero-filled).
 #include "xv_common.h"
+#include "xv_gdn_impl.h"
 #include <math.h>
 
 namespace {
@@ -48,6 +49,10 @@ constexpr int XV_ATTN_MAX_NC = 8192;
 constexpr int XV_ATTN_WIDE_MIN = 128; // (chunk, KV head, request) workgroups from which the wide kernel runs
 constexpr int XV_ATTN_STREAM_MIN = 1024; // ... and from which the persistent streaming kernel runs (about 4 chunks per CU)
 constexpr int XV_COMBINE_U = 24;    // chunks per block of combine loads kept in flight
+// GDN + attention in one launch while their workgroups are at most these multiples
+// of the CU count (GDN with one, or else two, column groups per workgroup)
+constexpr double XV_FUSE_ONE_COL = 1.0;
+constexpr double XV_FUSE_TWO_COL = 1.0;
 // the combine's per-chunk LDS arrays are padded to whole pairs of load blocks
 __host__ __device__ constexpr int xv_combine_pad(int nc) { return (nc + 2 * XV_COMBINE_U - 1) / (2 * XV_COMBINE_U) * (2 * XV_COMBINE_U); }
 
@@ -623,15 +628,39 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
 // probabilities go through LDS, and each wave forms the output dims of its
 // slice.  Every chain and ordered sum is the one the wide kernel forms, so the
 // two give the same bits.
+struct XvTileArgs {
+    const uint16_t* q; const uint16_t* k_new; const uint16_t* v_new;
+    uint16_t* k_cache; uint16_t* v_cache; const int32_t* kv_len;
+    float* ws_acc; float* ws_ml;
+    int T, Hq, Hkv, Lmax, NC, NTILE, items, per_xcd;
+    float scale_log2;
+};
+
+template <int D>
+struct XvTileSmem {
+    static constexpr int PP = XV_ATTN_C + 4;    // probability row pitch (floats)
+    static constexpr int QP = D + 8;            // query row pitch in LDS (bf16)
+    xv_u32x4 lds[XV_ATTN_C * D / 8];
+    float sp[16 * PP];
+    uint16_t sq[16 * QP];
+    float smax[XV_ATTN_WAVES][16];
+};
+
+// workgroup bid of the tile grid (its items are laid out for the XCD round robin)
 template <int D, int DS>
-__global__ __launch_bounds__(XV_ATTN_WAVES * 64)
-void xv_attn_partial_tile_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
-                                 const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_cache,
-                                 uint16_t* __restrict__ v_cache, const int32_t* __restrict__ kv_len,
-                                 float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-                                 int T, int Hq, int Hkv, int Lmax, int NC, int NTILE, int items,
-                                 int per_xcd, float scale_log2)
+__device__ __forceinline__ void xv_attn_tile_body(const XvTileArgs A, int bid, XvTileSmem<D>& S)
 {
+    const uint16_t* __restrict__ q = A.q;
+    const uint16_t* __restrict__ k_new = A.k_new;
+    const uint16_t* __restrict__ v_new = A.v_new;
+    uint16_t* __restrict__ k_cache = A.k_cache;
+    uint16_t* __restrict__ v_cache = A.v_cache;
+    const int32_t* __restrict__ kv_len = A.kv_len;
+    float* __restrict__ ws_acc = A.ws_acc;
+    float* __restrict__ ws_ml = A.ws_ml;
+    const int T = A.T, Hq = A.Hq, Hkv = A.Hkv, Lmax = A.Lmax, NC = A.NC, NTILE = A.NTILE;
+    const int items = A.items, per_xcd = A.per_xcd;
+    const float scale_log2 = A.scale_log2;
     constexpr int C = XV_ATTN_C;
     constexpr int NW = XV_ATTN_WAVES;
     constexpr int NT = NW * 64;
@@ -645,13 +674,13 @@ void xv_attn_partial_tile_kernel(const uint16_t* __restrict__ q, const uint16_t*
     constexpr int QP = D + 8;                   // query row pitch in LDS (bf16)
     constexpr int QG = (16 * (D / 8) + NT - 1) / NT;   // query granules per thread
     static_assert(NCB % NW == 0 && DB % DS == 0, "work must split evenly");
-    __shared__ __attribute__((aligned(16))) xv_u32x4 lds[C * D / 8];
-    __shared__ __attribute__((aligned(16))) float sp[16 * PP];
-    __shared__ __attribute__((aligned(16))) uint16_t sq[16 * QP];
-    __shared__ float smax[NW][16];
+    xv_u32x4* lds = S.lds;
+    float* sp = S.sp;
+    uint16_t* sq = S.sq;
+    float (*smax)[16] = S.smax;
 
     // work item: consecutive items (the tiles and d-parts of one chunk) share an XCD's L2
-    const int u = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+    const int u = (bid % 8) * per_xcd + bid / 8;
     if (u >= items) return;
     const int dpart = u % DS;
     const int tile = (u / DS) % NTILE;
@@ -788,6 +817,14 @@ void xv_attn_partial_tile_kernel(const uint16_t* __restrict__ q, const uint16_t*
     xv_store_acc<D, DBW>(ws_acc, oacc, dpart * DBP + dbl0, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
 }
 
+template <int D, int DS>
+__global__ __launch_bounds__(XV_ATTN_WAVES * 64)
+void xv_attn_partial_tile_kernel(XvTileArgs A)
+{
+    __shared__ __attribute__((aligned(16))) XvTileSmem<D> sm;
+    xv_attn_tile_body<D, DS>(A, (int)blockIdx.x, sm);
+}
+
 // the workgroup's maximum of mloc (exact in any order)
 template <int D>
 __device__ __forceinline__ float xv_combine_max(float mloc, float* sred, int tid) {
@@ -916,46 +953,82 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
     if (o32) o32[oi] = ov;
 }
 
+// The partial kernel's work split for a call (a choice by grid size only: the
+// three kernels give the same bits).
+enum XvAttnKind { XV_ATTN_TILE, XV_ATTN_WIDE, XV_ATTN_STREAM };
+
+inline int xv_cu_count() {
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    return cus;
+}
+
 template <int D>
-int xv_attn_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
-                   uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
-                   uint16_t* o, float* o32, float* ws_acc, float* ws_ml,
-                   int B, int T, int Hq, int Hkv, int Lmax, int NC, float scale, hipStream_t st)
-{
-    (void)hipGetLastError();
-    // scores are kept in log2 units: s * log2(e), so that 2^(s' - m') = e^(s - m)
-    const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-    // Both partial kernels give the same bits; the choice only spreads the work:
+XvAttnKind xv_attn_kind(int B, int T, int Hq, int Hkv, int NC) {
     // one workgroup per (chunk, KV head, request) when those alone fill the chip,
-    // otherwise one per 16-pair tile of each.
+    // otherwise one per 16-pair tile of each; persistent streaming for long contexts
     const int P = (Hq / Hkv) * T;
     const long long groups = (long long)B * Hkv;
-    if (D == 256 && groups * NC >= XV_ATTN_STREAM_MIN && P <= 64) {
+    if (D == 256 && groups * NC >= XV_ATTN_STREAM_MIN && P <= 64) return XV_ATTN_STREAM;
+    if (groups * NC >= XV_ATTN_WIDE_MIN && P <= 16 * XV_ATTN_WAVES) return XV_ATTN_WIDE;
+    return XV_ATTN_TILE;
+}
+
+constexpr int xv_attn_ds(int D) { return D == 256 ? 2 : 1; }   // value-dim parts per tile
+
+inline XvTileArgs xv_tile_args(int D, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                               uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
+                               float* ws_acc, float* ws_ml, int B, int T, int Hq, int Hkv, int Lmax, int NC,
+                               float scale_log2) {
+    const int P = (Hq / Hkv) * T;
+    const int ntile = (P + 15) / 16;
+    const int items = B * Hkv * NC * ntile * xv_attn_ds(D);
+    const int per_xcd = (items + 7) / 8;
+    return XvTileArgs{q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
+                      T, Hq, Hkv, Lmax, NC, ntile, items, per_xcd, scale_log2};
+}
+
+// scores are kept in log2 units: s * log2(e), so that 2^(s' - m') = e^(s - m)
+inline float xv_scale_log2(float scale) { return (float)((double)scale * 1.4426950408889634); }
+
+template <int D>
+int xv_attn_partials(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                     uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
+                     float* ws_acc, float* ws_ml,
+                     int B, int T, int Hq, int Hkv, int Lmax, int NC, float scale, hipStream_t st)
+{
+    (void)hipGetLastError();
+    const float scale_log2 = xv_scale_log2(scale);
+    const XvAttnKind kind = xv_attn_kind<D>(B, T, Hq, Hkv, NC);
+    if (kind == XV_ATTN_STREAM) {
         // about one persistent workgroup per CU, spread evenly over the (KV head, request) groups
-        int cus = 0, dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-        long long wpg = cus / groups;
+        const long long groups = (long long)B * Hkv;
+        long long wpg = xv_cu_count() / groups;
         wpg = wpg < 1 ? 1 : (wpg > NC ? NC : wpg);
         hipLaunchKernelGGL(xv_attn_partial_stream_kernel<D>, dim3((int)wpg, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st,
                            q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
                            T, Hq, Hkv, Lmax, NC, scale_log2);
-    } else if (groups * NC >= XV_ATTN_WIDE_MIN && P <= 16 * XV_ATTN_WAVES) {
+    } else if (kind == XV_ATTN_WIDE) {
         hipLaunchKernelGGL(xv_attn_partial_wide_kernel<D>, dim3(NC, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st,
                            q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
                            T, Hq, Hkv, Lmax, NC, scale_log2);
     } else {
-        constexpr int DS = D == 256 ? 2 : 1;    // value-dim parts per tile
-        const int ntile = (P + 15) / 16;
-        const int items = B * Hkv * NC * ntile * DS;
-        const int per_xcd = (items + 7) / 8;
-        hipLaunchKernelGGL((xv_attn_partial_tile_kernel<D, DS>), dim3(8 * per_xcd), dim3(XV_ATTN_WAVES * 64), 0, st,
-                           q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
-                           T, Hq, Hkv, Lmax, NC, ntile, items, per_xcd, scale_log2);
+        constexpr int DS = xv_attn_ds(D);
+        const XvTileArgs ta = xv_tile_args(D, q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
+                                           B, T, Hq, Hkv, Lmax, NC, scale_log2);
+        hipLaunchKernelGGL((xv_attn_partial_tile_kernel<D, DS>), dim3(8 * ta.per_xcd), dim3(XV_ATTN_WAVES * 64),
+                           0, st, ta);
     }
-    int s = xv_launch_status();
-    if (s != XV_OK) return s;
+    return xv_launch_status();
+}
+
+template <int D>
+int xv_attn_combine(const float* ws_acc, const float* ws_ml, const int32_t* kv_len, uint16_t* o, float* o32,
+                    int B, int T, int Hq, int Lmax, int NC, hipStream_t st)
+{
+    (void)hipGetLastError();
     if (NC > 2 * XV_COMBINE_U) {
         const size_t shmem = sizeof(float) * (2 * (size_t)xv_combine_pad(NC) + D);
         hipLaunchKernelGGL((xv_attn_combine_kernel<D, true>), dim3(Hq, T, B), dim3(D), shmem, st,
@@ -966,6 +1039,45 @@ int xv_attn_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_n
                            ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC);
     }
     return xv_launch_status();
+}
+
+template <int D>
+int xv_attn_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                   uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
+                   uint16_t* o, float* o32, float* ws_acc, float* ws_ml,
+                   int B, int T, int Hq, int Hkv, int Lmax, int NC, float scale, hipStream_t st)
+{
+    const int s = xv_attn_partials<D>(q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
+                                      B, T, Hq, Hkv, Lmax, NC, scale, st);
+    if (s != XV_OK) return s;
+    return xv_attn_combine<D>(ws_acc, ws_ml, kv_len, o, o32, B, T, Hq, Lmax, NC, st);
+}
+
+// GDN and the attention partials side by side in one launch: workgroups
+// 0 .. n_attn - 1 are the tile kernel's grid (so its XCD layout is unchanged),
+// the rest the GDN grid (gdn_nx column slices x Hv x B).  The two share no data;
+// each workgroup runs one body exactly as its own launch would (the same bits),
+// in the larger of the two LDS layouts.  Both are latency-bound at small batch,
+// so running them together takes about as long as the longer one.
+template <int DK, int CPT, int D>
+union XvGdnAttnSmem {
+    XvGdnSmem<DK, CPT> g;
+    XvTileSmem<D> t;
+};
+
+template <int DK, int CPT, int D>
+__global__ __launch_bounds__(XV_ATTN_WAVES * 64)
+void xv_gdn_attn_kernel(XvGdnArgs ga, XvTileArgs ta, int n_attn, int gdn_nx)
+{
+    static_assert(XV_GDN_THREADS == XV_ATTN_WAVES * 64, "one workgroup size for both bodies");
+    __shared__ __attribute__((aligned(16))) XvGdnAttnSmem<DK, CPT, D> sm;
+    const int bid = (int)blockIdx.x;
+    if (bid < n_attn) {                          // uniform over the workgroup
+        xv_attn_tile_body<D, xv_attn_ds(D)>(ta, bid, sm.t);
+        return;
+    }
+    const int i = bid - n_attn;
+    xv_gdn_body<DK, false, CPT>(ga, i % gdn_nx, (i / gdn_nx) % ga.Hv, i / (gdn_nx * ga.Hv), sm.g);
 }
 
 size_t xv_attn_ws(int B, int T, int Hq, int d, int Lmax, size_t* acc_bytes) {
@@ -985,11 +1097,15 @@ extern "C" size_t xv_attn_workspace_bytes(int B, int T, int Hq, int d, int Lmax)
     return xv_attn_ws(B, T, Hq, d, Lmax, nullptr);
 }
 
-extern "C" int xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
-                                   uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
-                                   uint16_t* o, float* o32, void* workspace, size_t workspace_bytes,
-                                   int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
-                                   void* stream)
+namespace {
+
+// The argument checks of xv_attn_verify_rows; on success the chunk count and the
+// workspace's two parts.
+int xv_attn_check(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                  const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* kv_len,
+                  const uint16_t* o, const float* o32, void* workspace, size_t workspace_bytes,
+                  int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
+                  int* NC, float** ws_acc, float** ws_ml)
 {
     XV_REQUIRE(B >= 0 && T >= 1 && T <= 16 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, XV_ERR_SHAPE);
     XV_REQUIRE(d == 64 || d == 128 || d == 256, XV_ERR_SHAPE);
@@ -1008,9 +1124,40 @@ extern "C" int xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, con
     size_t acc_bytes = 0;
     const size_t need = xv_attn_ws(B, T, Hq, d, Lmax, &acc_bytes);
     XV_REQUIRE(workspace_bytes >= need, XV_ERR_WORKSPACE);
-    const int NC = (Lmax + XV_ATTN_C - 1) / XV_ATTN_C;
-    float* ws_acc = reinterpret_cast<float*>(workspace);
-    float* ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + acc_bytes);
+    *NC = (Lmax + XV_ATTN_C - 1) / XV_ATTN_C;
+    *ws_acc = reinterpret_cast<float*>(workspace);
+    *ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + acc_bytes);
+    return XV_OK;
+}
+
+template <int D>
+int xv_gdn_attn_fused(const XvGdnArgs& ga, int dk, int cpt, const XvTileArgs& ta, int B, hipStream_t st)
+{
+    const int gdn_nx = ga.dv / (XV_GDN_JW * cpt);
+    const int n_attn = 8 * ta.per_xcd;
+    const dim3 grid(n_attn + gdn_nx * ga.Hv * B), block(XV_ATTN_WAVES * 64);
+    (void)hipGetLastError();
+    if (dk == 128 && cpt == 2) hipLaunchKernelGGL((xv_gdn_attn_kernel<128, 2, D>), grid, block, 0, st, ga, ta, n_attn, gdn_nx);
+    else if (dk == 128) hipLaunchKernelGGL((xv_gdn_attn_kernel<128, 1, D>), grid, block, 0, st, ga, ta, n_attn, gdn_nx);
+    else if (cpt == 2) hipLaunchKernelGGL((xv_gdn_attn_kernel<64, 2, D>), grid, block, 0, st, ga, ta, n_attn, gdn_nx);
+    else hipLaunchKernelGGL((xv_gdn_attn_kernel<64, 1, D>), grid, block, 0, st, ga, ta, n_attn, gdn_nx);
+    return xv_launch_status();
+}
+
+}  // namespace
+
+extern "C" int xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                                   uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
+                                   uint16_t* o, float* o32, void* workspace, size_t workspace_bytes,
+                                   int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
+                                   void* stream)
+{
+    int NC = 0;
+    float* ws_acc = nullptr;
+    float* ws_ml = nullptr;
+    const int s = xv_attn_check(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, workspace, workspace_bytes,
+                                B, T, Hq, Hkv, d, Lmax, scale, &NC, &ws_acc, &ws_ml);
+    if (s != XV_OK || B == 0) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     switch (d) {
         case 64:  return xv_attn_launch<64>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
@@ -1019,5 +1166,74 @@ extern "C" int xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, con
                                              ws_ml, B, T, Hq, Hkv, Lmax, NC, scale, st);
         default:  return xv_attn_launch<256>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
                                              ws_ml, B, T, Hq, Hkv, Lmax, NC, scale, st);
+    }
+}
+
+extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const float* a, const float* b,
+                                  const uint16_t* k_prev, const uint16_t* v_prev,
+                                  const float* a_prev, const float* b_prev,
+                                  const int32_t* n_keep_prev, int T_prev,
+                                  const float* state_in, const float* state_prev_out,
+                                  float* state_kept, float* state_out,
+                                  uint16_t* o, float* o32, int Hk, int Hv, int dk, int dv,
+                                  const uint16_t* q_attn, const uint16_t* k_new, const uint16_t* v_new,
+                                  uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
+                                  uint16_t* o_attn, float* o_attn32, void* workspace, size_t workspace_bytes,
+                                  int Hq, int Hkv, int d, int Lmax, float scale,
+                                  int B, int T, void* stream)
+{
+    XvGdnArgs ga{};
+    int s = n_keep_prev
+        ? xv_gdn_args_after(ga, q, k, v, a, b, k_prev, v_prev, a_prev, b_prev, n_keep_prev, T_prev,
+                            state_in, state_prev_out, state_kept, state_out, o, o32, B, T, Hk, Hv, dk, dv)
+        : xv_gdn_args_verify(ga, q, k, v, a, b, state_in, state_out, o, o32, B, T, Hk, Hv, dk, dv);
+    if (s != XV_OK) return s;
+    int NC = 0;
+    float* ws_acc = nullptr;
+    float* ws_ml = nullptr;
+    s = xv_attn_check(q_attn, k_new, v_new, k_cache, v_cache, kv_len, o_attn, o_attn32, workspace,
+                      workspace_bytes, B, T, Hq, Hkv, d, Lmax, scale, &NC, &ws_acc, &ws_ml);
+    if (s != XV_OK || B == 0) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    // one launch when the attention partials take the tile split and both grids are
+    // resident at once (about: workgroups of chunks past every row exit at once);
+    // the GDN workgroups then take one column group each if that fits, else two
+    bool fuse = false;
+    int cpt = 1;
+    XvTileArgs ta{};
+    switch (d) {
+        case 64:  fuse = xv_attn_kind<64>(B, T, Hq, Hkv, NC) == XV_ATTN_TILE; break;
+        case 128: fuse = xv_attn_kind<128>(B, T, Hq, Hkv, NC) == XV_ATTN_TILE; break;
+        default:  fuse = xv_attn_kind<256>(B, T, Hq, Hkv, NC) == XV_ATTN_TILE; break;
+    }
+    if (fuse) {
+        ta = xv_tile_args(d, q_attn, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml, B, T, Hq, Hkv,
+                          Lmax, NC, xv_scale_log2(scale));
+        const long long n_attn = 8LL * ta.per_xcd, cus = xv_cu_count();
+        const long long gdn1 = (long long)(dv / XV_GDN_JW) * Hv * B;
+        if (n_attn + gdn1 <= XV_FUSE_ONE_COL * cus) cpt = 1;
+        else if (dv % (2 * XV_GDN_JW) == 0 && n_attn + gdn1 / 2 <= XV_FUSE_TWO_COL * cus) cpt = 2;
+        else fuse = false;
+    }
+    if (!fuse) {
+        s = n_keep_prev
+            ? xv_gdn_verify_after(q, k, v, a, b, k_prev, v_prev, a_prev, b_prev, n_keep_prev, T_prev, state_in,
+                                  state_prev_out, state_kept, state_out, o, o32, B, T, Hk, Hv, dk, dv, stream)
+            : xv_gdn_verify(q, k, v, a, b, state_in, state_out, o, o32, B, T, Hk, Hv, dk, dv, stream);
+        if (s != XV_OK) return s;
+        return xv_attn_verify_rows(q_attn, k_new, v_new, k_cache, v_cache, kv_len, o_attn, o_attn32, workspace,
+                                   workspace_bytes, B, T, Hq, Hkv, d, Lmax, scale, stream);
+    }
+    switch (d) {
+        case 64:  s = xv_gdn_attn_fused<64>(ga, dk, cpt, ta, B, st); break;
+        case 128: s = xv_gdn_attn_fused<128>(ga, dk, cpt, ta, B, st); break;
+        default:  s = xv_gdn_attn_fused<256>(ga, dk, cpt, ta, B, st); break;
+    }
+    if (s != XV_OK) return s;
+    switch (d) {
+        case 64:  return xv_attn_combine<64>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, st);
+        case 128: return xv_attn_combine<128>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, st);
+        default:  return xv_attn_combine<256>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, st);
     }
 }

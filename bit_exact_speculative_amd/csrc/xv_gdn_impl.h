@@ -1,0 +1,362 @@
+// xv_gdn_impl.h -- the GDN verify / rollback device code (the per-token rule, its
+// fixed-order dot, and the workgroup body), shared by the GDN launches and by
+// the launch that runs GDN and attention side by side.  The description of the
+// arithmetic and the work mapping is at the top of xv_gdn.hip.
+#pragma once
+
+#include "xv_common.h"
+
+namespace {
+
+
+constexpr int XV_GDN_JW = 32;       // value indices per column group (8 waves x 4)
+constexpr int XV_GDN_LPJ = 16;      // lanes per value index
+constexpr int XV_GDN_THREADS = XV_GDN_JW * XV_GDN_LPJ;
+constexpr int XV_GDN_TMAX = 16;
+constexpr int XV_GDN_TM = 2 * XV_GDN_TMAX;     // rows one launch stages: replayed + this call's
+
+// Exact lane moves within each row of 16 lanes (DPP): swap with lane^1, lane^2,
+// mirror each half-row (lane i <-> 7 - i), mirror the row (lane i <-> 15 - i).
+__device__ __forceinline__ float xv_dpp_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xv_dpp_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xv_dpp_mirror8(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xv_dpp_mirror16(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+}
+
+template <int R>
+__device__ __forceinline__ float xv_gdn_dot(const float (&s)[R], const float (&x)[R]) {
+    static_assert(R % 4 == 0, "four chains");
+    float c0 = s[0] * x[0];
+    float c1 = s[1] * x[1];
+    float c2 = s[2] * x[2];
+    float c3 = s[3] * x[3];
+#pragma unroll
+    for (int r = 4; r < R; r += 4) {
+        c0 = __builtin_fmaf(s[r + 0], x[r + 0], c0);
+        c1 = __builtin_fmaf(s[r + 1], x[r + 1], c1);
+        c2 = __builtin_fmaf(s[r + 2], x[r + 2], c2);
+        c3 = __builtin_fmaf(s[r + 3], x[r + 3], c3);
+    }
+    float p = (c0 + c1) + (c2 + c3);
+    p = p + xv_dpp_xor1(p);
+    p = p + xv_dpp_xor2(p);
+    p = p + xv_dpp_mirror8(p);
+    p = p + xv_dpp_mirror16(p);
+    return p;
+}
+
+// The one per-token state update (decode, verify and rollback all call this).
+template <int R>
+__device__ __forceinline__ void xv_gdn_token(float (&s)[R], const float (&kk)[R],
+                                             float vj, float at, float bt) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = at * s[r];
+    const float kv = xv_gdn_dot<R>(s, kk);
+    const float u = bt * (vj - kv);
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = __builtin_fmaf(u, kk[r], s[r]);
+}
+
+// What one launch runs, per request b: first n_pre = clamp(n_pre[b], 0, Tp) rows
+// of a previous call (its k, v, a, b; no outputs), then the T rows of this call
+// (q, k, v, a, b; outputs o), all with xv_gdn_token, from the state S_in; when
+// S_alt is given and n_pre == Tp, from S_alt with no replay instead.  The state
+// after the replayed rows goes to S_mid (when given), the final state to S_out.
+//   verify          : no previous rows (n_pre NULL), T rows
+//   rollback        : previous rows = the verify's, n_pre = n_keep, T = 0; n == Tp
+//                     leaves S_out as it is (it holds S_T); kv_len[b] += n
+//   verify after    : the previous call's kept rows replayed (or its S_T taken),
+//                     then T rows; S_mid receives the kept state of the previous call
+struct XvGdnArgs {
+    const uint16_t* kp; const uint16_t* vp; const float* ap; const float* bp;   // previous rows
+    const int32_t* n_pre;                   // [B] previous rows to replay, or NULL
+    int Tp;                                 // rows per request of the previous call
+    const float* S_alt;                     // S_T of the previous call, or NULL
+    const uint16_t* q; const uint16_t* k; const uint16_t* v; const float* a; const float* b;
+    int T;                                  // rows of this call (0: rollback)
+    const float* S_in; float* S_mid; float* S_out;
+    uint16_t* o; float* o32;
+    int32_t* kv_len;                        // rollback: += n
+    int Hk, Hv, dv;
+};
+
+// LDS of one workgroup that owns 32 * CPT value indices.
+template <int DK, int CPT>
+struct XvGdnSmem {
+    static constexpr int W = XV_GDN_JW * CPT;
+    static constexpr int SP = W + 1;                 // state slab row pitch (floats)
+    float skq[XV_GDN_TM][2][DK];                     // k, q rows, fp32
+    uint16_t sv[XV_GDN_TM][W];
+    float sab[XV_GDN_TM][2];
+    float sst[DK * SP];                              // the state slab [i][W values]
+};
+
+// The workgroup (bx, h, b): value indices [bx W, bx W + W) of value head h of
+// request b, W = 32 CPT.  Thread (wave, lane) holds key indices ig R .. ig R + R - 1
+// (ig = lane % 16) of the CPT columns jw + 32 c, jw = 4 wave + lane / 16: each
+// column is updated exactly as with one column per thread, the CPT columns only
+// interleave their instructions.
+template <int DK, bool ROLLBACK, int CPT>
+__device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, int b, XvGdnSmem<DK, CPT>& sm)
+{
+    constexpr int NT = XV_GDN_THREADS;
+    constexpr int R = DK / XV_GDN_LPJ;
+    constexpr int TM = XV_GDN_TM;
+    constexpr int W = XV_GDN_JW * CPT;
+    constexpr int SP = W + 1;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int ig = lane & 15;                // key-index group: i in [ig*R, ig*R + R)
+    const int jl = lane >> 4;
+    const int jw = wave * 4 + jl;            // first value index within the workgroup's slice
+    const int j0 = bx * W;
+    const int Hk = A.Hk, Hv = A.Hv, dv = A.dv, T = A.T, Tp = A.Tp;
+    const int g = h / (Hv / Hk);
+
+    int np = 0;
+    const float* S0 = A.S_in;
+    if (A.n_pre) {
+        np = A.n_pre[b];
+        np = np < 0 ? 0 : (np > Tp ? Tp : np);
+        if (ROLLBACK) {
+            if (bx == 0 && h == 0 && tid == 0) A.kv_len[b] += np;
+            if (np == Tp) return;            // state_out already holds S_T
+        } else if (np == Tp && A.S_alt) {
+            S0 = A.S_alt;                    // every previous row kept: its S_T, nothing to replay
+            np = 0;
+        }
+    }
+    const int nm = ROLLBACK ? 0 : T;         // rows of this call
+    const int n = np + nm;
+
+    // the state slab S[i][j0 .. j0 + W) moves through LDS so that global reads and
+    // writes are 16-byte, W / 4 threads per row
+    constexpr int GPR = W / 4;               // 16-byte granules per slab row
+    constexpr int SROWS = NT / GPR;          // slab rows per pass
+    constexpr int SPASS = DK / SROWS;
+    static_assert(DK % SROWS == 0, "the slab must split into whole passes");
+    const size_t slab = (size_t)(b * Hv + h) * DK * dv + j0 + (tid % GPR) * 4;
+    xv_f32x4 sl[SPASS];
+#pragma unroll
+    for (int e = 0; e < SPASS; ++e)
+        sl[e] = *reinterpret_cast<const xv_f32x4*>(S0 + slab + (size_t)(tid / GPR + e * SROWS) * dv);
+
+    // stage the rows of tokens 0..n-1 (replayed rows first): every load is issued
+    // before any LDS store (straight-line, clamped to token 0), so the staging costs
+    // one round trip
+    constexpr int CH = DK / 8;               // 16-byte chunks per k or q row
+    constexpr int KQ_PER = (TM * 2 * CH + NT - 1) / NT;
+    constexpr int V_PER = (TM * W + NT - 1) / NT;
+    // row t of the launch: replayed row t of the previous call, or row t - np of this one
+    auto kq_src = [&](int t, int which) -> const uint16_t* {
+        if (t < np) return A.kp + (((size_t)b * Tp + t) * Hk + g) * DK;
+        const size_t row = ((size_t)b * T + (t - np)) * Hk + g;
+        return (which == 0 ? A.k : A.q) + row * DK;
+    };
+    if (n > 0) {                             // uniform
+        xv_u32x4 kq[KQ_PER];
+        uint16_t vv[V_PER];
+        float abv = 0.f;
+#pragma unroll
+        for (int e = 0; e < KQ_PER; ++e) {
+            int idx = tid + e * NT;
+            idx = idx < n * 2 * CH ? idx : 0;
+            const int t = idx / (2 * CH), rem = idx % (2 * CH);
+            const int which = rem / CH, c = rem % CH;   // 0: k, 1: q (a replayed row: k again)
+            kq[e] = xv_load16(kq_src(t, which) + c * 8);
+        }
+#pragma unroll
+        for (int e = 0; e < V_PER; ++e) {
+            int idx = tid + e * NT;
+            idx = idx < n * W ? idx : 0;
+            const int t = idx / W, c = idx % W;
+            const int jj = j0 + c;
+            vv[e] = t < np ? A.vp[(((size_t)b * Tp + t) * Hv + h) * dv + jj]
+                           : A.v[(((size_t)b * T + (t - np)) * Hv + h) * dv + jj];
+        }
+        {
+            const int idx = tid < 2 * n ? tid : 0;
+            const int t = idx >> 1;
+            abv = t < np ? ((idx & 1) ? A.bp : A.ap)[((size_t)b * Tp + t) * Hv + h]
+                         : ((idx & 1) ? A.b : A.a)[((size_t)b * T + (t - np)) * Hv + h];
+        }
+#pragma unroll
+        for (int e = 0; e < KQ_PER; ++e) {
+            const int idx = tid + e * NT;
+            if (idx < n * 2 * CH) {
+                const int t = idx / (2 * CH), rem = idx % (2 * CH);
+                float* dst = &sm.skq[t][rem / CH][(rem % CH) * 8];
+                xv_f32x4 lo4, hi4;
+#pragma unroll
+                for (int w2 = 0; w2 < 2; ++w2) {
+                    lo4[2 * w2] = xv_bf16_lo(kq[e][w2]);
+                    lo4[2 * w2 + 1] = xv_bf16_hi(kq[e][w2]);
+                    hi4[2 * w2] = xv_bf16_lo(kq[e][2 + w2]);
+                    hi4[2 * w2 + 1] = xv_bf16_hi(kq[e][2 + w2]);
+                }
+                *reinterpret_cast<xv_f32x4*>(dst) = lo4;
+                *reinterpret_cast<xv_f32x4*>(dst + 4) = hi4;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < V_PER; ++e) {
+            const int idx = tid + e * NT;
+            if (idx < n * W) sm.sv[idx / W][idx % W] = vv[e];
+        }
+        if (tid < 2 * n) sm.sab[tid >> 1][tid & 1] = abv;
+    }
+#pragma unroll
+    for (int e = 0; e < SPASS; ++e)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sm.sst[(tid / GPR + e * SROWS) * SP + (tid % GPR) * 4 + c] = sl[e][c];
+    __syncthreads();
+    float s[CPT][R];                         // this lane's part of its columns, for the whole call
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int r = 0; r < R; ++r) s[c][r] = sm.sst[(ig * R + r) * SP + jw + XV_GDN_JW * c];
+
+    // the slab of a state: own slots to LDS, then 16-byte rows out
+    auto store_state = [&](float* __restrict__ dst) {
+        __syncthreads();                     // every lane is done reading the slab
+#pragma unroll
+        for (int c = 0; c < CPT; ++c)
+#pragma unroll
+            for (int r = 0; r < R; ++r) sm.sst[(ig * R + r) * SP + jw + XV_GDN_JW * c] = s[c][r];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < SPASS; ++e) {
+            xv_f32x4 out;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) out[c] = sm.sst[(tid / GPR + e * SROWS) * SP + (tid % GPR) * 4 + c];
+            *reinterpret_cast<xv_f32x4*>(dst + slab + (size_t)(tid / GPR + e * SROWS) * dv) = out;
+        }
+    };
+
+    // Token t's rows are in registers while token t+1's are already being read from LDS.
+    float kc[R], qc[R], kn[R], qn[R];
+    float vj[CPT], vn[CPT];
+    float at = 0.f, bt = 0.f, an = 0.f, bn = 0.f;
+    auto fetch = [&](int t) {
+#pragma unroll
+        for (int c = 0; c < R / 4; ++c) {
+            const xv_f32x4 k4 = *reinterpret_cast<const xv_f32x4*>(&sm.skq[t][0][ig * R + c * 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kn[c * 4 + e] = k4[e];
+            if (!ROLLBACK) {
+                const xv_f32x4 q4 = *reinterpret_cast<const xv_f32x4*>(&sm.skq[t][1][ig * R + c * 4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qn[c * 4 + e] = q4[e];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) vn[c] = xv_bf16_to_f32(sm.sv[t][jw + XV_GDN_JW * c]);
+        an = sm.sab[t][0];
+        bn = sm.sab[t][1];
+    };
+    auto take = [&]() {
+#pragma unroll
+        for (int r = 0; r < R; ++r) { kc[r] = kn[r]; qc[r] = ROLLBACK ? 0.f : qn[r]; }
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) vj[c] = vn[c];
+        at = an; bt = bn;
+    };
+    if (n > 0) {
+        fetch(0);
+        take();
+    }
+    for (int t = 0; t < n; ++t) {
+        if (!ROLLBACK && A.S_mid && t == np) store_state(A.S_mid);   // uniform: the kept state
+        if (t + 1 < n) fetch(t + 1);         // uniform
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) xv_gdn_token<R>(s[c], kc, vj[c], at, bt);
+        if (!ROLLBACK && t >= np) {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const float ot = xv_gdn_dot<R>(s[c], qc);
+                if (ig == 0) {
+                    const size_t oi = (((size_t)b * T + (t - np)) * Hv + h) * dv + j0 + jw + XV_GDN_JW * c;
+                    A.o[oi] = xv_f32_to_bf16(ot);
+                    if (A.o32) A.o32[oi] = ot;
+                }
+            }
+        }
+        if (t + 1 < n) take();
+    }
+    if (!ROLLBACK && A.S_mid && n == np) store_state(A.S_mid);      // no rows of this call
+    store_state(A.S_out);
+}
+
+
+int xv_gdn_check(const void* k, const void* v, const void* a, const void* b,
+                 const void* sin, const void* sout, int B, int T, int Hk, int Hv, int dk, int dv)
+{
+    XV_REQUIRE(B >= 0 && T >= 1 && T <= XV_GDN_TMAX && Hk >= 1 && Hv >= 1 && Hv % Hk == 0, XV_ERR_SHAPE);
+    XV_REQUIRE(dk == 64 || dk == 128, XV_ERR_SHAPE);
+    XV_REQUIRE(dv >= 32 && dv <= 128 && dv % 32 == 0, XV_ERR_SHAPE);
+    if (B == 0) return XV_OK;
+    XV_REQUIRE(k && v && a && b && sin && sout, XV_ERR_NULL);
+    XV_REQUIRE(xv_aligned16(k) && xv_aligned(v, 2) && xv_aligned(a, 4) && xv_aligned(b, 4) &&
+               xv_aligned16(sin) && xv_aligned16(sout), XV_ERR_ALIGN);
+    XV_REQUIRE(sin != sout, XV_ERR_ALIAS);
+    return XV_OK;
+}
+
+
+// The argument checks of xv_gdn_verify and the launch arguments (B == 0: checked, nothing to run).
+inline int xv_gdn_args_verify(XvGdnArgs& args, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const float* a, const float* b, const float* state_in, float* state_out,
+                              uint16_t* o, float* o32, int B, int T, int Hk, int Hv, int dk, int dv)
+{
+    int s = xv_gdn_check(k, v, a, b, state_in, state_out, B, T, Hk, Hv, dk, dv);
+    if (s != XV_OK || B == 0) return s;
+    XV_REQUIRE(q && o, XV_ERR_NULL);
+    XV_REQUIRE(xv_aligned16(q) && xv_aligned(o, 2) && xv_aligned(o32, 4), XV_ERR_ALIGN);
+    args = XvGdnArgs{};
+    args.q = q; args.k = k; args.v = v; args.a = a; args.b = b; args.T = T;
+    args.S_in = state_in; args.S_out = state_out; args.o = o; args.o32 = o32;
+    args.Hk = Hk; args.Hv = Hv; args.dv = dv;
+    return XV_OK;
+}
+
+// The argument checks of xv_gdn_verify_after and the launch arguments.
+inline int xv_gdn_args_after(XvGdnArgs& args, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const float* a, const float* b,
+                             const uint16_t* k_prev, const uint16_t* v_prev, const float* a_prev,
+                             const float* b_prev, const int32_t* n_keep_prev, int T_prev,
+                             const float* state_prev_in, const float* state_prev_out,
+                             float* state_kept, float* state_out, uint16_t* o, float* o32,
+                             int B, int T, int Hk, int Hv, int dk, int dv)
+{
+    int s = xv_gdn_check(k, v, a, b, state_prev_in, state_out, B, T, Hk, Hv, dk, dv);
+    if (s != XV_OK) return s;
+    XV_REQUIRE(T_prev >= 1 && T_prev <= XV_GDN_TMAX, XV_ERR_SHAPE);
+    if (B == 0) return XV_OK;
+    XV_REQUIRE(q && o && k_prev && v_prev && a_prev && b_prev && n_keep_prev && state_prev_out && state_kept,
+               XV_ERR_NULL);
+    XV_REQUIRE(xv_aligned16(q) && xv_aligned(o, 2) && xv_aligned(o32, 4) && xv_aligned16(k_prev) &&
+               xv_aligned(v_prev, 2) && xv_aligned(a_prev, 4) && xv_aligned(b_prev, 4) &&
+               xv_aligned(n_keep_prev, 4) && xv_aligned16(state_prev_out) && xv_aligned16(state_kept),
+               XV_ERR_ALIGN);
+    XV_REQUIRE(state_out != state_prev_out && state_kept != state_prev_in && state_kept != state_prev_out &&
+               state_kept != state_out, XV_ERR_ALIAS);
+    args = XvGdnArgs{};
+    args.kp = k_prev; args.vp = v_prev; args.ap = a_prev; args.bp = b_prev;
+    args.n_pre = n_keep_prev; args.Tp = T_prev; args.S_alt = state_prev_out;
+    args.q = q; args.k = k; args.v = v; args.a = a; args.b = b; args.T = T;
+    args.S_in = state_prev_in; args.S_mid = state_kept; args.S_out = state_out;
+    args.o = o; args.o32 = o32;
+    args.Hk = Hk; args.Hv = Hv; args.dv = dv;
+    return XV_OK;
+}
+
+}  // namespace

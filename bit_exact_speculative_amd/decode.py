@@ -8,7 +8,7 @@ decoding) and runs, on one stream:
   xv_gemm_small_m_pair  y1 = x W1^T, y2 = x W2^T (one launch)
   xv_split_projections  GDN q, k (L2-normalised), v, decay, beta; attention q, k, v
   xv_gdn_verify         GDN rows, S_in -> S_T
-  xv_attn_verify_rows   attention rows, KV append
+  xv_attn_verify_rows   attention rows, KV append (with the GDN rows: xv_gdn_attn_verify)
   xv_gemm_small_m_pair  head logits from o_gdn and o_attn (one launch)
   xv_greedy_accept      ids, logprobs, accepted rows
   xv_rollback_to_prefix state and KV length of the kept rows
@@ -17,8 +17,9 @@ and emits ids[b][0 .. n_keep[b]-1]; the last one is the next root.  With
 lazy=True (the default) the rollback is folded into the next step: the greedy
 kernel adds n_keep to the KV length, and the next step's xv_gdn_verify_after
 replays the kept rows from the previous start state (or takes S_T when every
-row was kept) before its own rows; the state of the kept rows is materialised
-only when asked for (settle()).  Both orders give the same bits.  The post's
+row was kept) before its own rows, in one xv_gdn_attn_verify call with the
+attention rows; the state of the kept rows is materialised only when asked for
+(settle()).  Both ways give the same bits.  The post's
 claim (first paragraph; the paragraph on the two verify changes) is that the
 emitted ids and logprobs do not depend on k or on the drafts; the tests check
 that bit for bit.  Torch provides device memory and the stream only.
@@ -169,18 +170,23 @@ class Decoder:
         xv.xv_split_projections(R.y1, R.y2, R.q, R.k, R.v, R.a, R.b, R.qa, R.kn, R.vn, stream=st)
         if not self.lazy:
             xv.xv_gdn_verify(R.q, R.k, R.v, R.a, R.b, self._S, self._S2, R.o_gdn, None, stream=st)
-        elif self._pending is None:
-            xv.xv_gdn_verify(R.q, R.k, R.v, R.a, R.b, self._S, self._S2, R.o_gdn, None, stream=st)
-            self._pending = (R, self._S, self._S2)
+            xv.xv_attn_verify_rows(R.qa, R.kn, R.vn, self.Kc, self.Vc, self.kv_len, R.o_attn, None, R.ws,
+                                   self.scale, stream=st)
         else:
-            Rp, P, Q = self._pending
-            K, O = self._free
-            xv.xv_gdn_verify_after(R.q, R.k, R.v, R.a, R.b, Rp.k, Rp.v, Rp.a, Rp.b, Rp.n_keep,
-                                   P, Q, K, O, R.o_gdn, None, stream=st)
-            self._pending, self._free = (R, K, O), (P, Q)
-            self._S, self._S2 = K, O         # the pending step's start state and S_T
-        xv.xv_attn_verify_rows(R.qa, R.kn, R.vn, self.Kc, self.Vc, self.kv_len, R.o_attn, None, R.ws,
-                               self.scale, stream=st)
+            # GDN (after the pending step's rollback) and attention in one call
+            if self._pending is None:
+                out, prev = self._S2, None
+            else:
+                Rp, P, Q = self._pending
+                K, O = self._free
+                out, prev = O, (Rp.k, Rp.v, Rp.a, Rp.b, Rp.n_keep, Q, K)
+            xv.xv_gdn_attn_verify(R.q, R.k, R.v, R.a, R.b, self._S, out, R.o_gdn, R.qa, R.kn, R.vn,
+                                  self.Kc, self.Vc, self.kv_len, R.o_attn, R.ws, self.scale, prev=prev, stream=st)
+            if self._pending is None:
+                self._pending = (R, self._S, self._S2)
+            else:
+                self._pending, self._free = (R, K, O), (P, Q)
+                self._S, self._S2 = K, O     # the pending step's start state and S_T
         xv.xv_gemm_small_m_pair(R.o_gdn.view(M, wl.Hv * wl.dv), self.Wh_g, R.lg, R.lg32,
                                 R.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, R.la, R.la32, stream=st)
         if self.lazy:

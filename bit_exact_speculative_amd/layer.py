@@ -11,9 +11,9 @@ KV cache, the verify rows) and runs, on one stream:
               greedy ids, logprobs, accepted rows (xv_greedy_accept)
               rollback to the accepted prefix    (xv_rollback_to_prefix)
   lazy_step()  the same step with the rollback folded into the next step's GDN
-              launch (xv_gdn_verify_after replays the kept rows; the greedy
-              kernel adds the kept rows to the KV length); settle() runs the
-              last pending rollback.
+              launch (the kept rows are replayed there; the greedy kernel adds
+              them to the KV length), and GDN and attention in one call
+              (xv_gdn_attn_verify); settle() runs the last pending rollback.
   decode_sequence()  the same layer advanced one token at a time (T = 1, M = B)
               over the same rows, which verify must reproduce bit for bit.
 
@@ -206,14 +206,31 @@ class Layer:
                                self.o_gdn, self.o_gdn32 if self.out_fp32 else None, stream=self.stream)
         self.S_in, self.S_out, self.S_kept, self.S_next = self.S_kept, self.S_next, self.S_in, self.S_out
 
+    def gdn_attn_lazy(self):
+        """gdn_lazy() and attn() in one xv_gdn_attn_verify call (the same bits)."""
+        if self.S_kept is None:
+            self.S_kept, self.S_next = torch.empty_like(self.S_in), torch.empty_like(self.S_in)
+            self.kv_scratch = torch.zeros_like(self.kv_len)
+        if self.pending:
+            out = self.S_next
+            prev = (self.k, self.v, self.a, self.b, self.n_keep, self.S_out, self.S_kept)
+        else:
+            out, prev = self.S_out, None
+        xv.xv_gdn_attn_verify(self.q, self.k, self.v, self.a, self.b, self.S_in, out, self.o_gdn,
+                              self.qa, self.kn, self.vn, self.Kc, self.Vc, self.kv_len, self.o_attn, self.ws,
+                              self.scale, o32=self.o_gdn32 if self.out_fp32 else None,
+                              o_attn32=self.o_attn32 if self.out_fp32 else None, prev=prev, stream=self.stream)
+        if self.pending:
+            self.S_in, self.S_out, self.S_kept, self.S_next = self.S_kept, self.S_next, self.S_in, self.S_out
+        self.pending = True
+
     def lazy_step(self, events=None):
         """One speculative step with the rollback deferred to the next step's GDN launch."""
         if not self.has_head:
             raise ValueError("a lazy step needs the head: its acceptance counts the kept rows")
         if self.has_gemm:
             self.gemms(events)
-        self.gdn_lazy()
-        self.attn()
+        self.gdn_attn_lazy()
         self.head_gemms()
         self.greedy(count_kv=True)
 

@@ -52,6 +52,9 @@ _lib.xv_rollback_to_prefix.restype = _I
 _lib.xv_rollback_to_prefix.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
 _lib.xv_greedy_accept.restype = _I
 _lib.xv_greedy_accept.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P]
+_lib.xv_gdn_attn_verify.restype = _I
+_lib.xv_gdn_attn_verify.argtypes = ([_P] * 10 + [_I] + [_P] * 6 + [_I] * 4 + [_P] * 9 + [_S] +
+                                    [_I] * 4 + [_F] + [_I, _I, _P])
 _lib.xv_gdn_verify_after.restype = _I
 _lib.xv_gdn_verify_after.argtypes = [_P] * 10 + [_I] + [_P] * 6 + [_I] * 6 + [_P]
 _lib.xv_embed_rows.restype = _I
@@ -197,6 +200,48 @@ def xv_gdn_verify_after(q, k, v, a, b, k_prev, v_prev, a_prev, b_prev, n_keep_pr
         _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(k_prev), _ptr(v_prev), _ptr(a_prev),
         _ptr(b_prev), _ptr(n_keep_prev), Tp, _ptr(state_prev_in), _ptr(state_prev_out),
         _ptr(state_kept), _ptr(state_out), _ptr(o), _ptr(o32), B, T, Hk, Hv, dk, dv, _stream(stream)))
+
+
+def xv_gdn_attn_verify(q, k, v, a, b, state_in, state_out, o, q_attn, k_new, v_new, k_cache, v_cache,
+                       kv_len, o_attn, workspace, scale=None, o32=None, o_attn32=None, prev=None,
+                       stream=None):
+    """GDN verify and attention verify rows in one call (one launch when they fit the chip).
+    prev: None (as xv_gdn_verify), or (k_prev, v_prev, a_prev, b_prev, n_keep_prev,
+    state_prev_out, state_kept) for xv_gdn_verify_after from state_in; then as
+    xv_attn_verify_rows."""
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    Hq, d = q_attn.shape[2], q_attn.shape[3]
+    Hkv, Lmax = k_new.shape[2], k_cache.shape[2]
+    st = (B, Hv, dk, dv)
+    bad = tuple(k.shape) != (B, T, Hk, dk) or tuple(v.shape[:2]) != (B, T) or \
+        tuple(a.shape) != (B, T, Hv) or tuple(b.shape) != (B, T, Hv) or \
+        tuple(state_in.shape) != st or tuple(state_out.shape) != st or tuple(o.shape) != (B, T, Hv, dv) or \
+        (o32 is not None and tuple(o32.shape) != (B, T, Hv, dv)) or \
+        tuple(q_attn.shape[:2]) != (B, T) or tuple(k_new.shape) != (B, T, Hkv, d) or \
+        tuple(v_new.shape) != (B, T, Hkv, d) or tuple(k_cache.shape) != (B, Hkv, Lmax, d) or \
+        tuple(v_cache.shape) != (B, Hkv, Lmax, d) or tuple(kv_len.shape) != (B,) or \
+        tuple(o_attn.shape) != (B, T, Hq, d) or (o_attn32 is not None and tuple(o_attn32.shape) != (B, T, Hq, d))
+    Tp = 0
+    if prev is not None:
+        kp, vp, ap, bp, nk, sp, sk = prev
+        Tp = kp.shape[1]
+        bad = bad or tuple(kp.shape) != (B, Tp, Hk, dk) or tuple(vp.shape) != (B, Tp, Hv, dv) or \
+            tuple(ap.shape) != (B, Tp, Hv) or tuple(bp.shape) != (B, Tp, Hv) or tuple(nk.shape) != (B,) or \
+            tuple(sp.shape) != st or tuple(sk.shape) != st
+    else:
+        kp = vp = ap = bp = nk = sp = sk = None
+    if bad:
+        raise ValueError("xv_gdn_attn_verify: shape mismatch")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    wbytes = workspace.numel() * workspace.element_size()
+    _check("xv_gdn_attn_verify", _lib.xv_gdn_attn_verify(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(kp), _ptr(vp), _ptr(ap), _ptr(bp), _ptr(nk), Tp,
+        _ptr(state_in), _ptr(sp), _ptr(sk), _ptr(state_out), _ptr(o), _ptr(o32), Hk, Hv, dk, dv,
+        _ptr(q_attn), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
+        _ptr(o_attn), _ptr(o_attn32), _ptr(workspace), wbytes, Hq, Hkv, d, Lmax, float(scale),
+        B, T, _stream(stream)))
 
 
 def xv_attn_verify_rows(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32=None, workspace=None,

@@ -203,6 +203,42 @@ int    xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, const uint1
                            void* stream);
 
 /*
+ * GDN verify and attention verify rows in one call.  The two are independent
+ * (the post's two verify changes, each with the decode arithmetic) and, at small
+ * batch, both are bound by latency rather than bandwidth, so when the attention
+ * partials take their per-tile split and both grids fit on the chip at once, one
+ * launch runs the GDN workgroups beside the attention partial workgroups,
+ * followed by the attention combine; otherwise the two calls below run one after
+ * the other.  Either way every output is bit-identical to
+ *   n_keep_prev != NULL : xv_gdn_verify_after(q .. b, k_prev .. b_prev,
+ *                         n_keep_prev, T_prev, state_in, state_prev_out,
+ *                         state_kept, state_out, o, o32, B, T, Hk, Hv, dk, dv)
+ *   n_keep_prev == NULL : xv_gdn_verify(q .. b, state_in, state_out, o, o32,
+ *                         B, T, Hk, Hv, dk, dv)  (k_prev .. b_prev, T_prev,
+ *                         state_prev_out and state_kept are not used)
+ * followed by
+ *   xv_attn_verify_rows(q_attn, k_new, v_new, k_cache, v_cache, kv_len, o_attn,
+ *                       o_attn32, workspace, workspace_bytes, B, T, Hq, Hkv, d,
+ *                       Lmax, scale)
+ * with each argument's meaning, layout, shape rule and error code as there
+ * (the first failing check is reported; nothing is launched then).  The GDN
+ * buffers and the attention buffers must not overlap.
+ */
+int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const float* a, const float* b,
+                       const uint16_t* k_prev, const uint16_t* v_prev,
+                       const float* a_prev, const float* b_prev,
+                       const int32_t* n_keep_prev, int T_prev,
+                       const float* state_in, const float* state_prev_out,
+                       float* state_kept, float* state_out,
+                       uint16_t* o, float* o32, int Hk, int Hv, int dk, int dv,
+                       const uint16_t* q_attn, const uint16_t* k_new, const uint16_t* v_new,
+                       uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
+                       uint16_t* o_attn, float* o_attn32, void* workspace, size_t workspace_bytes,
+                       int Hq, int Hkv, int d, int Lmax, float scale,
+                       int B, int T, void* stream);
+
+/*
  * Rollback to the accepted prefix.
  * The post: the exactness held also with every draft forced to reject and
  * with 8 requests in flight, i.e. keeping any prefix of the verify rows must

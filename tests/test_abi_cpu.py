@@ -26,7 +26,7 @@ def test_every_header_symbol_is_exported(xv):
                           "xv_rollback_to_prefix", "xv_attn_workspace_bytes",
                           "xv_attn_chunk_tokens", "xv_abi_version", "xv_status_string",
                           "xv_greedy_accept", "xv_embed_rows", "xv_split_projections",
-                          "xv_gemm_small_m_pair", "xv_gdn_verify_after"}
+                          "xv_gemm_small_m_pair", "xv_gdn_verify_after", "xv_gdn_attn_verify"}
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -116,6 +116,27 @@ def test_gdn_verify_after_argument_errors(xv):
     assert call(kp=MIS) == -3 and call(vp=ODD) == -3 and call(sk=S[2] + 4) == -3 and call(nk=A + 2) == -3
     for bad in (dict(so=S[0]), dict(so=S[1]), dict(sk=S[0]), dict(sk=S[1]), dict(sk=S[3])):
         assert call(**bad) == -6, bad
+
+
+def test_gdn_attn_argument_errors(xv):
+    """The combined call reports the first failing check of the two calls it stands for."""
+    f = xv.lib().xv_gdn_attn_verify
+    need = xv.xv_attn_workspace_bytes(1, 9, 24, 256, 649)
+    S = [A + 0x100000 * i for i in range(4)]
+
+    def call(nk=None, kp=None, si=S[0], sp=None, sk=None, so=S[1], T=9, dk=128, d=256, B=1, wsb=need,
+             q=A, qa=A, kvl=A, Tp=0):
+        return f(q, A, A, A, A, kp, kp, kp, kp, nk, Tp, si, sp, sk, so, A, None, 16, 48, dk, 128,
+                 qa, A, A, A, A, kvl, A, None, A, wsb, 24, 4, d, 649, 0.0625, B, T, None)
+
+    assert call(B=0) == 0
+    assert call(T=17) == -2 and call(dk=96) == -2 and call(d=96) == -2
+    assert call(q=None) == -1 and call(qa=None) == -1 and call(kvl=None) == -1
+    assert call(so=S[0]) == -6                                  # GDN state_out aliases state_in
+    assert call(wsb=need - 4) == -4
+    assert call(nk=A, Tp=9) == -1                               # after a verify: its rows are needed
+    assert call(nk=A, Tp=0, kp=A, sp=S[2], sk=S[3]) == -2       # T_prev
+    assert call(nk=A, Tp=9, kp=A, sp=S[2], sk=S[0]) == -6       # state_kept aliases state_in
 
 
 def test_attn_argument_errors(xv):
