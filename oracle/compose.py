@@ -114,8 +114,9 @@ class State:
         return State(self.S.copy(), self.kc.copy(), self.vc.copy(), self.kv_len.copy())
 
 
-def step(m: Model, st: State, tokens: np.ndarray):
-    """One verify step over tokens int32 [B][T]; updates ``st`` in place to the kept prefix.
+def step(m: Model, st: State, tokens: np.ndarray, keep_all: bool = False):
+    """One verify step over tokens int32 [B][T]; updates ``st`` in place to the kept prefix
+    (the greedy acceptance; every row with keep_all, as in ``prefill``).
 
     Returns (ids [B][T], logprobs fp64 [B][T], n_keep [B], logits fp64 [B][T][V]).
     """
@@ -148,6 +149,8 @@ def step(m: Model, st: State, tokens: np.ndarray):
     logits = (gemm(round_bf16(o_gdn).reshape(M, s.Hv * s.dv), m.Wh_gdn)
               + gemm(round_bf16(o_attn).reshape(M, s.Hq * s.d), m.Wh_attn)).reshape(B, T, -1)
     ids, n_keep = greedy(logits, np.ascontiguousarray(tokens, dtype=np.int32))
+    if keep_all:
+        n_keep = np.full((B,), T, np.int32)
     lp = logprob(logits, ids)
     for bb in range(B):
         n = int(n_keep[bb])
@@ -157,6 +160,22 @@ def step(m: Model, st: State, tokens: np.ndarray):
         st.vc[bb, :, L0:L0 + n] = vn[bb, :n].transpose(1, 0, 2)
         st.kv_len[bb] = L0 + n
     return ids, lp, n_keep, logits
+
+
+def prefill(m: Model, st: State, prompt: np.ndarray):
+    """The prompt (int32 [B][P]) through the layer with every row kept: the step before
+    decoding, which leaves the GDN state, the KV cache and the length after the prompt
+    (post, launch command: chunked prefill of 8192 tokens; the chunking is a schedule,
+    not part of what is computed, so there is none here).  Returns (id [B], logprob [B],
+    logits [B][V]) of the last prompt row: the first generated token.
+
+    The rows are those of ``step`` with the acceptance replaced by "keep all P": one
+    token at a time for the state (stored in fp32 after every token), attention rows
+    over the cache, the head and the greedy id of each row.
+    """
+    P = prompt.shape[1]
+    ids, lp, _, logits = step(m, st, np.ascontiguousarray(prompt, dtype=np.int32), keep_all=True)
+    return ids[:, P - 1].copy(), lp[:, P - 1].copy(), logits[:, P - 1].copy()
 
 
 def generate(m: Model, st: State, root: np.ndarray, n_tokens: int, drafts=None, k: int = 0):

@@ -141,3 +141,29 @@ def test_step_rows_are_independent_of_the_other_rows():
         ids2, lp2, _, logits2 = C.step(m, st0.copy(), toks[:, :T].copy())
         assert np.array_equal(logits2, logits[:, :T]) and np.array_equal(ids2, ids[:, :T])
         assert np.array_equal(lp2, lp[:, :T])
+
+
+def test_prefill_equals_forced_one_token_steps_in_the_oracle():
+    """The oracle's prefill (every prompt row kept) leaves the state, cache and length of
+    feeding the prompt one token at a time, and its last row's logits, id and logprob are
+    those of the last one-token step; splitting the prompt in two changes nothing."""
+    m, st0, root, wl = _tiny_model()
+    rng = np.random.default_rng(21)
+    P = 11
+    prompt = rng.integers(0, wl.NH, size=(wl.B, P)).astype(np.int32)
+    st_a = st0.copy()
+    id_a, lp_a, z_a = C.prefill(m, st_a, prompt)
+    st_b = st0.copy()
+    for t in range(P):
+        ids, lp, n_keep, z = C.step(m, st_b, prompt[:, t:t + 1].copy())
+        assert np.all(n_keep == 1)
+    assert np.array_equal(z[:, 0], z_a) and np.array_equal(ids[:, 0], id_a) and np.array_equal(lp[:, 0], lp_a)
+    assert np.array_equal(st_a.S, st_b.S) and np.array_equal(st_a.kv_len, st_b.kv_len)
+    assert np.array_equal(st_a.kc, st_b.kc) and np.array_equal(st_a.vc, st_b.vc)
+    assert np.all(st_a.kv_len == st0.kv_len + P)
+    st_c = st0.copy()
+    C.prefill(m, st_c, prompt[:, :4].copy())
+    id_c, lp_c, z_c = C.prefill(m, st_c, prompt[:, 4:].copy())
+    assert np.array_equal(z_c, z_a) and np.array_equal(st_c.S, st_a.S) and np.array_equal(st_c.kc, st_a.kc)
+    # the first generated token is the argmax of the last row (lowest index on ties)
+    assert np.array_equal(id_a, np.argmax(z_a, axis=-1))
