@@ -417,6 +417,135 @@ void xv_gemm_kloop_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
     }
 }
 
+// Many rows (prefill): 128 x 128 output tiles, 4 waves of 64 x 64 (4 x 4 MFMA
+// tiles each), K walked in ascending k-steps with x and W staged through
+// double-buffered LDS, KC k-steps per stage, the next stage's loads in flight in
+// registers.  For each of its output tiles a wave runs the 16 range chains one
+// after the other and folds each finished range into the running sum in range
+// order, the operations of the other variants: a row's bits are its bits at any M.
+// Workgroup i takes column tile i / mb and row tile i % mb (the row tiles of one
+// column tile run together, so its W rows are read from HBM about once).
+constexpr int XV_BIG_BM = 128, XV_BIG_BN = 128, XV_BIG_KC = 2;
+constexpr int XV_BIG_MIN_M = 256;   // rows from which the tiled kernel runs
+constexpr int XV_BIG_THREADS = 256;
+
+__global__ __launch_bounds__(XV_BIG_THREADS, 2)
+void xv_gemm_big_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                        uint16_t* __restrict__ y, float* __restrict__ y32, int M, int N, int K, int mb)
+{
+    constexpr int NTH = XV_BIG_THREADS;
+    constexpr int KC = XV_BIG_KC;
+    constexpr int PITCH = KC * 32 + 8;          // LDS row pitch (bf16): 16 rows fall on distinct banks
+    constexpr int GR = KC * 4;                  // 16-byte granules per row per stage
+    constexpr int XG = XV_BIG_BM * GR / NTH;    // x granules per thread per stage
+    constexpr int WG = XV_BIG_BN * GR / NTH;
+    static_assert(XV_BIG_BM * GR % NTH == 0 && XV_BIG_BN * GR % NTH == 0, "granules must split evenly");
+    __shared__ __attribute__((aligned(16))) uint16_t sx[2][XV_BIG_BM * PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t sw[2][XV_BIG_BN * PITCH];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int wm = wave & 1, wn = wave >> 1;    // the wave's 64 x 64 quarter
+    const int m0 = ((int)blockIdx.x % mb) * XV_BIG_BM;
+    const int n0 = ((int)blockIdx.x / mb) * XV_BIG_BN;
+    const int KS = K >> 5;
+    const int nst = (KS + KC - 1) / KC;
+
+    // this thread's granules of a stage: rows tid / GR + i (NTH / GR), column tid % GR, the
+    // same for every stage; rows past the buffers re-read the last one
+    constexpr int RSTEP = NTH / GR;
+    const int r0 = tid / GR, c8 = (tid % GR) * 8;
+    const int l0 = r0 * PITCH + c8;
+    xv_u32x4 xreg[XG], wreg[WG];
+    auto load = [&](int s) {                    // stage s; columns past K re-read the row's last granule
+        const int k0 = s * (KC * 32);
+        const int kc = k0 + c8 < K ? k0 + c8 : K - 8;
+#pragma unroll
+        for (int i = 0; i < XG; ++i) {
+            const int row = m0 + r0 + i * RSTEP < M ? m0 + r0 + i * RSTEP : M - 1;
+            xreg[i] = xv_load16(x + (size_t)row * K + kc);
+        }
+#pragma unroll
+        for (int i = 0; i < WG; ++i) {
+            const int col = n0 + r0 + i * RSTEP < N ? n0 + r0 + i * RSTEP : N - 1;
+            wreg[i] = xv_load16(w + (size_t)col * K + kc);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < XG; ++i) *reinterpret_cast<xv_u32x4*>(&sx[buf][l0 + i * RSTEP * PITCH]) = xreg[i];
+#pragma unroll
+        for (int i = 0; i < WG; ++i) *reinterpret_cast<xv_u32x4*>(&sw[buf][l0 + i * RSTEP * PITCH]) = wreg[i];
+    };
+
+    xv_f32x4 acc[4][4], sum[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { acc[i][j] = xv_f32x4{0.f, 0.f, 0.f, 0.f}; sum[i][j] = acc[i][j]; }
+    int r = 0;                                  // the range whose chains are running
+    auto fold = [&]() {                         // range r is complete
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sum[i][j] = r == 0 ? acc[i][j] : sum[i][j] + acc[i][j];
+                acc[i][j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        ++r;
+    };
+
+    load(0);
+    store(0);
+    load(nst > 1 ? 1 : 0);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        const int buf = s & 1;
+#pragma unroll
+        for (int jj = 0; jj < KC; ++jj) {
+            const int ks = s * KC + jj;
+            while (r < XV_GEMM_WAVES && ((r + 1) * KS) / XV_GEMM_WAVES <= ks) fold();   // uniform
+            if (ks < KS) {
+                xv_u32x4 af[4], bf[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    af[i] = *reinterpret_cast<const xv_u32x4*>(&sx[buf][(wm * 64 + i * 16 + lr) * PITCH + jj * 32 + lg * 8]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    bf[j] = *reinterpret_cast<const xv_u32x4*>(&sw[buf][(wn * 64 + j * 16 + lr) * PITCH + jj * 32 + lg * 8]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = xv_mfma16x16x32(af[i], bf[j], acc[i][j]);
+            }
+        }
+        if (s + 1 < nst) {                      // stage s+1 into the other buffer, stage s+2 in flight
+            store(buf ^ 1);
+            load(s + 2 < nst ? s + 2 : s + 1);
+        }
+        __syncthreads();
+    }
+    while (r < XV_GEMM_WAVES) fold();
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + wn * 64 + j * 16 + lr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = m0 + wm * 64 + i * 16 + 4 * lg + e;
+                if (row < M && col < N) {
+                    const size_t o = (size_t)row * N + col;
+                    y[o] = xv_f32_to_bf16(sum[i][j][e]);
+                    if (y32) y32[o] = sum[i][j][e];
+                }
+            }
+        }
+}
+
 // x fragments re-read per k-step (many row tiles or long K): U k-steps per stage.
 template <int MT, int U>
 __global__ __launch_bounds__(XV_GEMM_THREADS)
@@ -618,6 +747,14 @@ extern "C" int xv_gemm_small_m_timed(const uint16_t* x, const uint16_t* w, uint1
     const int KS = K / 32;
     const int ksw = (KS + XV_GEMM_WAVES - 1) / XV_GEMM_WAVES;   // k-steps of the longest range
     const int tiles = (M + 15) / 16;
+    if (M >= XV_BIG_MIN_M) {                    // many rows: one launch of 128 x 128 tiles
+        const int mb = (M + XV_BIG_BM - 1) / XV_BIG_BM, nb = (N + XV_BIG_BN - 1) / XV_BIG_BN;
+        XV_REQUIRE((long long)mb * nb < (1LL << 31), XV_ERR_SHAPE);
+        hipExtLaunchKernelGGL(xv_gemm_big_kernel, dim3(mb * nb), dim3(XV_BIG_THREADS), 0,
+                              reinterpret_cast<hipStream_t>(stream), reinterpret_cast<hipEvent_t>(start_event),
+                              reinterpret_cast<hipEvent_t>(stop_event), 0, x, w, y, y32, M, N, K, mb);
+        return xv_launch_status();
+    }
     for (int mt0 = 0; mt0 < tiles; mt0 += XV_GEMM_MT_MAX) {
         const int mt = tiles - mt0 < XV_GEMM_MT_MAX ? tiles - mt0 : XV_GEMM_MT_MAX;
         // the start event goes with the first launch, the stop event with the last

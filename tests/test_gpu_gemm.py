@@ -210,3 +210,29 @@ def test_gemm_pair_gives_the_single_gemm_bits(case):
         assert torch.equal(y0_32.view(torch.int32), r0_32.view(torch.int32))
         assert torch.equal(y1_32.view(torch.int32), r1_32.view(torch.int32))
     assert e0.elapsed_time(e1) > 0.0
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 400, 5120), (300, 10240, 5120), (1000, 272, 6144),
+                                   (257, 48, 96), (384, 1040, 544), (2048, 17408, 5120)])
+def test_gemm_many_rows_tiled_kernel_rows_equal_k_split(M, N, K):
+    """From 256 rows the 128 x 128 tiled kernel runs (prefill); every row must equal the same
+    row computed at M <= 16 by the K-split kernels (sampled 9-row slices, including the last
+    partial row tile and a column tile cut by N), and sampled columns must match the oracle.
+    K = 96 leaves 13 of the 16 ranges empty."""
+    from bit_exact_speculative_amd.layer import dev_bf16
+    rng = np.random.default_rng(M * 3 + N + K)
+    xh = random_bf16(rng, (M, K))
+    wh = random_bf16(rng, (N, K), 0.02)
+    x = dev_bf16(xh, "cuda"); w = dev_bf16(wh, "cuda")
+    y, y32 = _gemm_dev(x, w)
+    starts = sorted(set([0, 120, 128, M - 9] + [int(v) for v in rng.integers(0, M - 9, size=4)]))
+    for r0 in starts:
+        r1 = min(M, r0 + 9)
+        ys, ys32 = _gemm_dev(x[r0:r1].contiguous(), w)
+        assert torch.equal(ys32.view(torch.int32), y32[r0:r1].view(torch.int32)), r0
+        assert torch.equal(ys.view(torch.int16), y[r0:r1].view(torch.int16)), r0
+    cols = np.sort(rng.choice(N, size=min(N, 48), replace=False))
+    rows = np.sort(rng.choice(M, size=min(M, 64), replace=False))
+    ref = oracle.gemm(xh[rows], wh[cols])
+    torch.cuda.synchronize()
+    assert max_rel(y32.cpu().numpy()[rows][:, cols], ref) <= OUT_MAX_REL
