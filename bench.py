@@ -207,6 +207,54 @@ def extra_workload(name, stream, steps, warmup, R):
     return res
 
 
+def prefill_workload(stream, P=8192, check=256, reps=2):
+    """Prefill of a P-token prompt (one chunk of 8192) on the synthetic layer, short workload
+    shapes, appended to its 640 cached tokens: embedding, both projections and the split over
+    all rows, then GDN beside attention in steps of 16 rows, the head and the first token.
+    Gated on the first `check` prompt tokens giving the state, cache, first token and logprob
+    of one-token decoding bit for bit."""
+    import numpy as np
+    import torch
+    from bit_exact_speculative_amd import inputs as gen
+    from bit_exact_speculative_amd.decode import Decoder
+    wl = gen.WORKLOADS["short"]
+    inp = gen.composed_inputs(wl)
+    Lmax = int(inp.L0.max()) + P + 32
+    prompt = np.random.default_rng(777).integers(0, wl.NH, size=(wl.B, P)).astype(np.int32)
+    with torch.cuda.stream(stream):
+        dec = Decoder(inp, Lmax, stream=stream)
+        snap = dec.snapshot()
+        id_a, lp_a = dec.prefill(prompt[:, :check])
+        got = (dec.S.clone(), dec.Kc.clone(), dec.kv_len.clone(), id_a.clone(), lp_a.clone())
+        dec.restore(snap)
+        for t in range(check):
+            R = dec.step(torch.from_numpy(prompt[:, t:t + 1].copy()).to("cuda"))
+        want = (dec.S, dec.Kc, dec.kv_len, R.ids[:, 0], R.lp[:, 0])
+        torch.cuda.synchronize()
+        same = lambda a, b: torch.equal(a.contiguous().view(torch.int16 if a.element_size() == 2 else torch.int32),
+                                        b.contiguous().view(torch.int16 if b.element_size() == 2 else torch.int32))
+        exact = all(same(a, b) for a, b in zip(got, want))
+        best = None
+        for _ in range(reps + 1):                    # the first pass warms up
+            dec.restore(snap)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dec.prefill(prompt)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None or ms < best else best
+    res = {"prompt_tokens": P, "ctx_before": int(inp.L0[0]), "batch": wl.B, "chunk": 8192, "rows_per_step": 16,
+           "bit_exact_prefill_equals_decode": bool(exact), "check_tokens": check,
+           "tok_s": round(wl.B * P / (best * 1e-3), 1) if exact else None, "ms": round(best, 3),
+           "note": "one layer; every prompt row kept; first token formed"}
+    del dec
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def composed_workload(stream, n_tokens=48, k=8, p_wrong=0.2, reps=3):
     """Greedy decoding on the synthetic layer, short workload shapes: every step embeds its
     tokens, runs both projections, the split, GDN, attention, the head, logprobs, acceptance
@@ -350,6 +398,10 @@ def main():
             extras["composed"] = composed_workload(stream)
         except Exception as exc:
             extras["composed"] = {"error": "%s: %s" % (type(exc).__name__, exc)}
+        try:
+            extras["prefill"] = prefill_workload(stream)
+        except Exception as exc:
+            extras["prefill"] = {"error": "%s: %s" % (type(exc).__name__, exc)}
         try:
             from bit_exact_speculative_amd.diagnose import divergence_margins
             with torch.cuda.stream(stream):
