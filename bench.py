@@ -83,6 +83,8 @@ def parse():
     ap.add_argument("--breakdown", action="store_true", help="per-kernel event timing pass")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the medium / batch-8 / long workloads reported beside the headline")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="print only the prefill leg (other_workloads.prefill) as one JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -338,6 +340,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.prefill_only:                         # one leg, for profiling the prefill path
+        print(json.dumps(prefill_workload(torch.cuda.Stream())), flush=True)
+        return
     wl = gen.WORKLOADS[args.workload]
     R = max(1, args.replicas)
     full_steps, full_warmup = max(args.steps // 2, 1), max(args.warmup // 2, 1)

@@ -126,6 +126,7 @@ class Decoder:
         self._free = (torch.empty_like(self._S), torch.empty_like(self._S)) if lazy else None
         self._kv_scratch = torch.zeros_like(self.kv_len)
         self._slot = 0
+        self._keep_all = {}
         self.Lmax = Lmax
         self.scale = 1.0 / float(wl.d) ** 0.5
         self._rows = {}
@@ -217,7 +218,6 @@ class Decoder:
         self.settle()
         e = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=dev)
         f = lambda *sh: torch.empty(sh, dtype=torch.float32, device=dev)
-        full = {}
         ws = None
         for c0 in range(0, P, chunk):
             cp = min(chunk, P - c0)
@@ -240,8 +240,8 @@ class Decoder:
                 sl = slice(m0, m0 + B * tt)
                 m0 += B * tt
                 rs = lambda t, *tail: t[sl].view(B, tt, *tail)
-                if tt not in full:
-                    full[tt] = torch.full((B,), tt, dtype=torch.int32, device=dev)
+                if (B, tt) not in self._keep_all:     # n_keep = tt for every request (host-made)
+                    self._keep_all[(B, tt)] = torch.from_numpy(np.full((B,), tt, np.int32)).to(dev)
                 nb = xv.xv_attn_workspace_bytes(B, tt, wl.Hq, wl.d, self.Lmax)
                 if ws is None or ws.numel() * 4 < nb:
                     ws = f((max(nb, 16) + 15) // 16 * 4)
@@ -252,7 +252,8 @@ class Decoder:
                                       stream=st)
                 # every row kept: the state is S_T as computed, the length grows by tt
                 xv.xv_rollback_to_prefix(rs(k, wl.Hk, wl.dk), rs(v, wl.Hv, wl.dv), rs(a, wl.Hv),
-                                         rs(b, wl.Hv), self._S, self._S2, self.kv_len, full[tt], stream=st)
+                                         rs(b, wl.Hv), self._S, self._S2, self.kv_len, self._keep_all[(B, tt)],
+                                         stream=st)
                 self._S, self._S2 = self._S2, self._S
         # the head and the greedy id of the last step's rows; the last row is the answer
         Mt = B * tt
