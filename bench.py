@@ -212,7 +212,8 @@ def extra_workload(name, stream, steps, warmup, R):
 def prefill_workload(stream, P=8192, check=256, reps=2):
     """Prefill of a P-token prompt (one chunk of 8192) on the synthetic layer, short workload
     shapes, appended to its 640 cached tokens: embedding, both projections and the split over
-    all rows, then GDN beside attention in steps of 16 rows, the head and the first token.
+    all rows, GDN and attention over all rows (decode arithmetic per row), the head and the
+    first token.
     Gated on the first `check` prompt tokens giving the state, cache, first token and logprob
     of one-token decoding bit for bit."""
     import numpy as np
@@ -247,7 +248,7 @@ def prefill_workload(stream, P=8192, check=256, reps=2):
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1)
             best = ms if best is None or ms < best else best
-    res = {"prompt_tokens": P, "ctx_before": int(inp.L0[0]), "batch": wl.B, "chunk": 8192, "rows_per_step": 16,
+    res = {"prompt_tokens": P, "ctx_before": int(inp.L0[0]), "batch": wl.B, "chunk": 8192,
            "bit_exact_prefill_equals_decode": bool(exact), "check_tokens": check,
            "tok_s": round(wl.B * P / (best * 1e-3), 1) if exact else None, "ms": round(best, 3),
            "note": "one layer; every prompt row kept; first token formed"}

@@ -1237,3 +1237,341 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
         default:  return xv_attn_combine<256>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, st);
     }
 }
+
+// ---------------------------------------------------------------------------
+// Prefill: P rows appended at once, each row with the decode row's arithmetic.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int XV_PF_WAVES = 8;                  // 16-pair tiles per workgroup
+constexpr int XV_PF_THREADS = XV_PF_WAVES * 64;
+constexpr int XV_PF_PAIRS = XV_PF_WAVES * 16;
+
+// kv_len[b] += n (one thread per request), after the kernels that read it.
+__global__ void xv_kv_advance_kernel(int32_t* __restrict__ kv_len, int B, int n)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) kv_len[b] += n;
+}
+
+// Rows r = 0..P-1 of k_new / v_new ([B][P][Hkv][d]) to cache positions L0 + r.
+__global__ void xv_kv_append_kernel(const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                                    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
+                                    const int32_t* __restrict__ kv_len, int P, int Hkv, int d, int Lmax)
+{
+    const int gpr = d / 8;
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long long)P * Hkv * gpr) return;
+    const int b = blockIdx.y;
+    const int c = (int)(idx % gpr);
+    const int h = (int)((idx / gpr) % Hkv);
+    const int r = (int)(idx / ((long long)gpr * Hkv));
+    int L0 = kv_len[b];
+    L0 = L0 < 0 ? 0 : (L0 > Lmax - P ? Lmax - P : L0);
+    const size_t src = (((size_t)b * P + r) * Hkv + h) * d + c * 8;
+    const size_t dst = (((size_t)b * Hkv + h) * Lmax + L0 + r) * d + c * 8;
+    xv_store16(k_cache + dst, xv_load16(k_new + src));
+    xv_store16(v_cache + dst, xv_load16(v_new + src));
+}
+
+// Workgroup (request b, KV head g, block of 128 (row, head) pairs, pair = row * Hg + h as in
+// the verify kernels); wave w owns pairs 16 w .. 16 w + 15 of the block.  Row r (position
+// L0 + r) gets exactly the decode row's numbers: per chunk c (absolute boundaries) the
+// scores (the same MFMA chain, K as A and q as B), the exact chunk maximum m_c, the
+// probabilities 2^(s - m_c), their sum in the partial kernels' order and the P.V chains
+// (p as bf16 hi + lo, k-steps ascending); then the combine's fold in ascending c with
+// M = max_c m_c:  L = L + l_c 2^(m_c - M),  A = fma(acc_c, 2^(m_c - M), A),  o = A / L.
+// M is needed before the first fold, so the chunks are walked twice: pass 1 forms each
+// row's maximum from the same scores, pass 2 the partials and the fold, all in registers.
+// Every chunk is read from the cache (the rows were appended first); positions at or past
+// L0 + P are zero-filled in LDS and never visible.
+template <int D>
+__global__ __launch_bounds__(XV_PF_THREADS)
+void xv_attn_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+                            const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ kv_len,
+                            uint16_t* __restrict__ o, float* __restrict__ o32,
+                            int P, int Hq, int Hkv, int Lmax, int NRB, float scale_log2)
+{
+    constexpr int C = XV_ATTN_C;
+    constexpr int NT = XV_PF_THREADS;
+    constexpr int KS = D / 32;                  // k-steps of a score
+    constexpr int NCB = C / 16;                 // score blocks of a chunk
+    constexpr int DB = D / 16;                  // output blocks
+    constexpr int KG = C * (D / 8) / NT;        // K granules per thread
+    constexpr int VTILES = (C / 8) * (D / 8);   // 8 x 8 V tiles of a chunk
+    constexpr int VT = (VTILES + NT - 1) / NT;
+    static_assert(C * (D / 8) % NT == 0 && NCB % 2 == 0, "chunk must split evenly");
+    // LDS: K as [pos][d] (row pitch KP bytes), later V^T as [d][pos] (pitch VP); the 16-byte
+    // pads put the 16 rows of a fragment read on distinct banks, and every fragment is a
+    // per-lane base plus a constant offset
+    constexpr int KP = D * 2 + 16, VP = C * 2 + 16;
+    constexpr int LDSB = (C * KP > D * VP ? C * KP : D * VP);
+    __shared__ __attribute__((aligned(16))) char lds[LDSB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int bid = (int)blockIdx.x;
+    const int rb = NRB - 1 - bid % NRB;         // the blocks of the last rows (most chunks) first
+    const int g = (bid / NRB) % Hkv;
+    const int b = bid / (NRB * Hkv);
+    const int Hg = Hq / Hkv;
+    const int Ptot = Hg * P;
+    int L0 = kv_len[b];
+    L0 = L0 < 0 ? 0 : (L0 > Lmax - P ? Lmax - P : L0);
+    const int Lend = L0 + P;
+    const int pair0 = rb * XV_PF_PAIRS;
+    const int last_pair = pair0 + XV_PF_PAIRS - 1 < Ptot ? pair0 + XV_PF_PAIRS - 1 : Ptot - 1;
+    const int nc = (L0 + last_pair / Hg + 1 + C - 1) / C;          // chunks the block's last row sees
+    const int tpair0 = pair0 + wave * 16;       // this wave's tile
+    // the wave's tile sees chunk c while its last row does
+    const int tlast = tpair0 + 15 < Ptot ? tpair0 + 15 : Ptot - 1;
+    const int tnc = tpair0 < Ptot ? (L0 + tlast / Hg + 1 + C - 1) / C : 0;
+    // this lane's score pair (lr) and its output pairs (4 lg + i)
+    const int pair = tpair0 + lr;
+    const bool pair_ok = pair < Ptot;
+    const int plen = pair_ok ? L0 + pair / Hg + 1 : 0;
+    const size_t kvbase = ((size_t)b * Hkv + g) * Lmax;
+    const xv_u32x4 zero = {0u, 0u, 0u, 0u};
+
+    const int pcq = pair_ok ? pair : 0;
+    const uint16_t* qp = q + (((size_t)b * P + pcq / Hg) * Hq + g * Hg + pcq % Hg) * D + lg * 8;
+
+    constexpr int KB = KG < 4 ? KG : 4;         // K granules per thread in flight
+    auto k_to_lds = [&](int c0) {
+#pragma unroll 1
+        for (int i0 = 0; i0 < KG; i0 += KB) {
+            xv_u32x4 kr[KB];
+#pragma unroll
+            for (int i = 0; i < KB; ++i) {
+                const int idx = tid + (i0 + i) * NT;
+                const int pos = c0 + idx / (D / 8);
+                kr[i] = xv_load16(k_cache + (kvbase + (pos < Lend ? pos : 0)) * D + (idx % (D / 8)) * 8);
+                if (pos >= Lend) kr[i] = zero;
+            }
+#pragma unroll
+            for (int i = 0; i < KB; ++i) {
+                const int idx = tid + (i0 + i) * NT;
+                *reinterpret_cast<xv_u32x4*>(lds + (idx / (D / 8)) * KP + (idx % (D / 8)) * 16) = kr[i];
+            }
+        }
+    };
+    auto vt_to_lds = [&](int c0) {
+#pragma unroll 1
+        for (int i = 0; i < VT; ++i) {
+            const int vt = tid + i * NT;
+            if (VTILES % NT == 0 || vt < VTILES) {
+                const int pg = vt / (D / 8), dg = vt % (D / 8);
+                xv_u32x4 vr[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int pos = c0 + pg * 8 + e;
+                    vr[e] = xv_load16(v_cache + (kvbase + (pos < Lend ? pos : 0)) * D + dg * 8);
+                    if (pos >= Lend) vr[e] = zero;
+                }
+#pragma unroll
+                for (int dd = 0; dd < 8; ++dd) {
+                    xv_u32x4 outv;
+#pragma unroll
+                    for (int w2 = 0; w2 < 4; ++w2) {
+                        const uint32_t lo = vr[2 * w2][dd >> 1], hi = vr[2 * w2 + 1][dd >> 1];
+                        outv[w2] = (dd & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+                    }
+                    *reinterpret_cast<xv_u32x4*>(lds + (dg * 8 + dd) * VP + pg * 16) = outv;
+                }
+            }
+        }
+    };
+    // scores of the chunk in LDS, in log2 units: sc[cb][i] = position cb*16 + 4 lg + i, pair lr
+    xv_f32x4 sc[NCB];
+    auto scores = [&]() {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) sc[cb] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const xv_u32x4 qk = pair_ok ? xv_load16(qp + ks * 32) : zero;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                sc[cb] = xv_mfma16x16x32(*reinterpret_cast<const xv_u32x4*>(lds + (cb * 16 + lr) * KP + ks * 64 + lg * 16),
+                                         qk, sc[cb]);
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[cb][i] = sc[cb][i] * scale_log2;
+    };
+
+    // ---- pass 1: each pair's maximum over its visible positions ----
+    float M = -INFINITY;
+    for (int c = 0; c < nc; ++c) {
+        const int c0 = c * C;
+        __syncthreads();                        // LDS free
+        k_to_lds(c0);
+        __syncthreads();
+        if (c < tnc) {                          // uniform per wave
+            scores();
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (c0 + cb * 16 + 4 * lg + i < plen) M = fmaxf(M, sc[cb][i]);
+        }
+    }
+    M = fmaxf(M, __shfl_xor(M, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+
+    // ---- pass 2: chunk partials, folded in ascending chunk order ----
+    xv_f32x4 A[DB];
+#pragma unroll
+    for (int j = 0; j < DB; ++j) A[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    int orow[4];
+    bool ook[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p2 = tpair0 + 4 * lg + i;
+        ook[i] = p2 < Ptot;
+        orow[i] = ook[i] ? p2 / Hg : 0;
+    }
+    for (int c = 0; c < nc; ++c) {
+        const int c0 = c * C;
+        __syncthreads();                        // LDS free
+        k_to_lds(c0);
+        __syncthreads();
+        const bool active = c < tnc;            // uniform per wave
+        float beta = 0.f;
+        if (active) {
+            scores();
+            float m = -INFINITY;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (c0 + cb * 16 + 4 * lg + i < plen) m = fmaxf(m, sc[cb][i]);
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            const bool sees = plen > c0;        // the pair has a partial for this chunk
+            if (!sees) m = 0.f;                 // keep finite (no position is visible)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool vis = c0 + cb * 16 + 4 * lg + i < plen;
+                    sc[cb][i] = vis ? __builtin_amdgcn_exp2f(sc[cb][i] - m) : 0.f;
+                }
+            float l = 0.f;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) l = l + sc[cb][i];
+            l = l + __shfl_xor(l, 16);
+            l = l + __shfl_xor(l, 32);
+            if (sees) {
+                beta = __builtin_amdgcn_exp2f(m - M);
+                L = L + l * beta;
+            }
+#pragma unroll
+            for (int kk = 0; kk < C / 32; ++kk) {   // the P.V A operands, bf16 hi + lo
+                xv_u32x4 phi, plo;
+                xv_p_split(sc[2 * kk], sc[2 * kk + 1], phi, plo);
+                sc[2 * kk] = __builtin_bit_cast(xv_f32x4, phi);
+                sc[2 * kk + 1] = __builtin_bit_cast(xv_f32x4, plo);
+            }
+        }
+        __syncthreads();                        // every wave is done reading K
+        vt_to_lds(c0);
+        __syncthreads();
+        if (active) {
+            float bi[4];
+            bool si[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bi[i] = __shfl(beta, 4 * lg + i);
+                si[i] = ook[i] && L0 + orow[i] + 1 > c0;
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                xv_f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < C / 32; ++kk) {
+                    // V^T rows db*16 + lr at positions kk*32 + 4 lg .. + 3 and kk*32 + 16 + 4 lg .. + 3
+                    const char* vp = lds + (db * 16 + lr) * VP + kk * 64 + lg * 8;
+                    const uint2 va = *reinterpret_cast<const uint2*>(vp);
+                    const uint2 vb = *reinterpret_cast<const uint2*>(vp + 32);
+                    const xv_u32x4 vf = {va.x, va.y, vb.x, vb.y};
+                    oacc = xv_mfma16x16x32(__builtin_bit_cast(xv_u32x4, sc[2 * kk]), vf, oacc);
+                    oacc = xv_mfma16x16x32(__builtin_bit_cast(xv_u32x4, sc[2 * kk + 1]), vf, oacc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) A[db][i] = si[i] ? __builtin_fmaf(oacc[i], bi[i], A[db][i]) : A[db][i];
+            }
+        }
+    }
+    float Lp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Lp[i] = __shfl(L, 4 * lg + i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (!ook[i]) continue;
+        const int p2 = tpair0 + 4 * lg + i;
+        const size_t ob = (((size_t)b * P + orow[i]) * Hq + g * Hg + p2 % Hg) * D + lr;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const float ov = A[db][i] / Lp[i];
+            o[ob + db * 16] = xv_f32_to_bf16(ov);
+            if (o32) o32[ob + db * 16] = ov;
+        }
+    }
+}
+
+template <int D>
+int xv_attn_prefill_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                           uint16_t* k_cache, uint16_t* v_cache, int32_t* kv_len,
+                           uint16_t* o, float* o32, int B, int P, int Hq, int Hkv, int Lmax, float scale,
+                           int advance, hipStream_t st)
+{
+    (void)hipGetLastError();
+    const long long gran = (long long)P * Hkv * (D / 8);
+    hipLaunchKernelGGL(xv_kv_append_kernel, dim3((unsigned)((gran + 255) / 256), B), dim3(256), 0, st,
+                       k_new, v_new, k_cache, v_cache, kv_len, P, Hkv, D, Lmax);
+    int s = xv_launch_status();
+    if (s != XV_OK) return s;
+    const int NRB = ((Hq / Hkv) * P + XV_PF_PAIRS - 1) / XV_PF_PAIRS;
+    hipLaunchKernelGGL(xv_attn_prefill_kernel<D>, dim3(NRB * Hkv * B), dim3(XV_PF_THREADS), 0, st,
+                       q, k_cache, v_cache, kv_len, o, o32, P, Hq, Hkv, Lmax, NRB, xv_scale_log2(scale));
+    s = xv_launch_status();
+    if (s != XV_OK || !advance) return s;
+    hipLaunchKernelGGL(xv_kv_advance_kernel, dim3((B + 63) / 64), dim3(64), 0, st, kv_len, B, P);
+    return xv_launch_status();
+}
+
+}  // namespace
+
+extern "C" int xv_attn_prefill(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                               uint16_t* k_cache, uint16_t* v_cache, int32_t* kv_len,
+                               uint16_t* o, float* o32, int B, int P, int Hq, int Hkv, int d, int Lmax,
+                               float scale, int advance, void* stream)
+{
+    XV_REQUIRE(B >= 0 && P >= 1 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, XV_ERR_SHAPE);
+    XV_REQUIRE(d == 64 || d == 128 || d == 256, XV_ERR_SHAPE);
+    XV_REQUIRE(Lmax >= P && (Lmax + XV_ATTN_C - 1) / XV_ATTN_C <= XV_ATTN_MAX_NC, XV_ERR_SHAPE);
+    XV_REQUIRE((long long)((Hq / Hkv) * (long long)P + XV_PF_PAIRS - 1) / XV_PF_PAIRS * Hkv * B < (1LL << 31),
+               XV_ERR_SHAPE);
+    XV_REQUIRE((long long)P * Hkv * (d / 8) / 256 < (1LL << 31) && B < 65536, XV_ERR_SHAPE);
+    XV_REQUIRE(scale == scale, XV_ERR_SHAPE);
+    if (B == 0) return XV_OK;
+    XV_REQUIRE(q && k_new && v_new && k_cache && v_cache && kv_len && o, XV_ERR_NULL);
+    XV_REQUIRE(xv_aligned16(q) && xv_aligned16(k_new) && xv_aligned16(v_new) && xv_aligned16(k_cache) &&
+               xv_aligned16(v_cache) && xv_aligned(kv_len, 4) && xv_aligned(o, 2) && xv_aligned(o32, 4),
+               XV_ERR_ALIGN);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    switch (d) {
+        case 64:  return xv_attn_prefill_launch<64>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, B, P, Hq,
+                                                    Hkv, Lmax, scale, advance, st);
+        case 128: return xv_attn_prefill_launch<128>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, B, P, Hq,
+                                                     Hkv, Lmax, scale, advance, st);
+        default:  return xv_attn_prefill_launch<256>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, B, P, Hq,
+                                                     Hkv, Lmax, scale, advance, st);
+    }
+}

@@ -42,6 +42,14 @@ void xv_gdn_kernel(XvGdnArgs A)
     xv_gdn_body<DK, ROLLBACK, CPT>(A, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
+template <int DK>
+__global__ __launch_bounds__(XV_GDN_THREADS)
+void xv_gdn_prefill_kernel(XvGdnArgs A)
+{
+    __shared__ __attribute__((aligned(16))) XvGdnPrefillSmem<DK> sm;
+    xv_gdn_prefill_body<DK>(A, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+}
+
 template <bool ROLLBACK>
 int xv_gdn_launch(const XvGdnArgs& args, int B, int dk, hipStream_t st)
 {
@@ -83,6 +91,28 @@ extern "C" int xv_gdn_verify_after(const uint16_t* q, const uint16_t* k, const u
                                     B, T, Hk, Hv, dk, dv);
     if (s != XV_OK || B == 0) return s;
     return xv_gdn_launch<false>(args, B, dk, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int xv_gdn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const float* a, const float* b,
+                              const float* state_in, float* state_out,
+                              uint16_t* o, float* o32,
+                              int B, int T, int Hk, int Hv, int dk, int dv, void* stream)
+{
+    int s = xv_gdn_check(k, v, a, b, state_in, state_out, B, T, Hk, Hv, dk, dv, 1 << 30);
+    if (s != XV_OK || B == 0) return s;
+    XV_REQUIRE(q && o, XV_ERR_NULL);
+    XV_REQUIRE(xv_aligned16(q) && xv_aligned(o, 2) && xv_aligned(o32, 4), XV_ERR_ALIGN);
+    XvGdnArgs args{};
+    args.q = q; args.k = k; args.v = v; args.a = a; args.b = b; args.T = T;
+    args.S_in = state_in; args.S_out = state_out; args.o = o; args.o32 = o32;
+    args.Hk = Hk; args.Hv = Hv; args.dv = dv;
+    dim3 grid(dv / XV_GDN_JW, Hv, B), block(XV_GDN_THREADS);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (dk == 128) hipLaunchKernelGGL(xv_gdn_prefill_kernel<128>, grid, block, 0, st, args);
+    else hipLaunchKernelGGL(xv_gdn_prefill_kernel<64>, grid, block, 0, st, args);
+    return xv_launch_status();
 }
 
 extern "C" int xv_rollback_to_prefix(const uint16_t* k, const uint16_t* v,

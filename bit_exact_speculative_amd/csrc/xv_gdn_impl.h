@@ -298,9 +298,10 @@ __device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, in
 
 
 int xv_gdn_check(const void* k, const void* v, const void* a, const void* b,
-                 const void* sin, const void* sout, int B, int T, int Hk, int Hv, int dk, int dv)
+                 const void* sin, const void* sout, int B, int T, int Hk, int Hv, int dk, int dv,
+                 int tmax = XV_GDN_TMAX)
 {
-    XV_REQUIRE(B >= 0 && T >= 1 && T <= XV_GDN_TMAX && Hk >= 1 && Hv >= 1 && Hv % Hk == 0, XV_ERR_SHAPE);
+    XV_REQUIRE(B >= 0 && T >= 1 && T <= tmax && Hk >= 1 && Hv >= 1 && Hv % Hk == 0, XV_ERR_SHAPE);
     XV_REQUIRE(dk == 64 || dk == 128, XV_ERR_SHAPE);
     XV_REQUIRE(dv >= 32 && dv <= 128 && dv % 32 == 0, XV_ERR_SHAPE);
     if (B == 0) return XV_OK;
@@ -311,6 +312,167 @@ int xv_gdn_check(const void* k, const void* v, const void* a, const void* b,
     return XV_OK;
 }
 
+
+// Prefill: the T rows of a long prompt (any T) through the same per-token routine, state
+// in registers for the whole call.  Rows move through LDS in blocks of 16: the next
+// block's loads are issued before the current block is computed, and stored to the other
+// LDS buffer after it.  Outputs for every row; S_in -> S_out.
+constexpr int XV_GDN_PB = 16;
+
+template <int DK>
+struct XvGdnPrefillSmem {
+    static constexpr int SP = XV_GDN_JW + 1;
+    float skq[2][XV_GDN_PB][2][DK];
+    uint16_t sv[2][XV_GDN_PB][XV_GDN_JW];
+    float sab[2][XV_GDN_PB][2];
+    float sst[DK * SP];
+};
+
+template <int DK>
+__device__ __forceinline__ void xv_gdn_prefill_body(const XvGdnArgs A, int bx, int h, int b,
+                                                    XvGdnPrefillSmem<DK>& sm)
+{
+    constexpr int NT = XV_GDN_THREADS;
+    constexpr int R = DK / XV_GDN_LPJ;
+    constexpr int W = XV_GDN_JW;
+    constexpr int SP = W + 1;
+    constexpr int PB = XV_GDN_PB;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int ig = lane & 15;
+    const int jw = wave * 4 + (lane >> 4);
+    const int j0 = bx * W;
+    const int Hk = A.Hk, Hv = A.Hv, dv = A.dv, T = A.T;
+    const int g = h / (Hv / Hk);
+
+    constexpr int GPR = W / 4;
+    constexpr int SROWS = NT / GPR;
+    constexpr int SPASS = DK / SROWS;
+    const size_t slab = (size_t)(b * Hv + h) * DK * dv + j0 + (tid % GPR) * 4;
+    xv_f32x4 sl[SPASS];
+#pragma unroll
+    for (int e = 0; e < SPASS; ++e)
+        sl[e] = *reinterpret_cast<const xv_f32x4*>(A.S_in + slab + (size_t)(tid / GPR + e * SROWS) * dv);
+
+    // one block's rows: every load issued first (clamped to the call's first row), stored later
+    constexpr int CH = DK / 8;
+    constexpr int KQ_PER = (PB * 2 * CH + NT - 1) / NT;
+    constexpr int V_PER = (PB * W + NT - 1) / NT;
+    xv_u32x4 kq[KQ_PER];
+    uint16_t vv[V_PER];
+    float abv = 0.f;
+    auto fetch_block = [&](int t0, int n) {
+#pragma unroll
+        for (int e = 0; e < KQ_PER; ++e) {
+            int idx = tid + e * NT;
+            idx = idx < n * 2 * CH ? idx : 0;
+            const int t = t0 + idx / (2 * CH), rem = idx % (2 * CH);
+            const size_t row = ((size_t)b * T + t) * Hk + g;
+            kq[e] = xv_load16((rem / CH == 0 ? A.k : A.q) + row * DK + (rem % CH) * 8);
+        }
+#pragma unroll
+        for (int e = 0; e < V_PER; ++e) {
+            int idx = tid + e * NT;
+            idx = idx < n * W ? idx : 0;
+            vv[e] = A.v[(((size_t)b * T + t0 + idx / W) * Hv + h) * dv + j0 + idx % W];
+        }
+        const int idx = tid < 2 * n ? tid : 0;
+        abv = ((idx & 1) ? A.b : A.a)[((size_t)b * T + t0 + (idx >> 1)) * Hv + h];
+    };
+    auto stage_block = [&](int buf, int n) {
+#pragma unroll
+        for (int e = 0; e < KQ_PER; ++e) {
+            const int idx = tid + e * NT;
+            if (idx < n * 2 * CH) {
+                const int t = idx / (2 * CH), rem = idx % (2 * CH);
+                float* dst = &sm.skq[buf][t][rem / CH][(rem % CH) * 8];
+                xv_f32x4 lo4, hi4;
+#pragma unroll
+                for (int w2 = 0; w2 < 2; ++w2) {
+                    lo4[2 * w2] = xv_bf16_lo(kq[e][w2]);
+                    lo4[2 * w2 + 1] = xv_bf16_hi(kq[e][w2]);
+                    hi4[2 * w2] = xv_bf16_lo(kq[e][2 + w2]);
+                    hi4[2 * w2 + 1] = xv_bf16_hi(kq[e][2 + w2]);
+                }
+                *reinterpret_cast<xv_f32x4*>(dst) = lo4;
+                *reinterpret_cast<xv_f32x4*>(dst + 4) = hi4;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < V_PER; ++e) {
+            const int idx = tid + e * NT;
+            if (idx < n * W) sm.sv[buf][idx / W][idx % W] = vv[e];
+        }
+        if (tid < 2 * n) sm.sab[buf][tid >> 1][tid & 1] = abv;
+    };
+
+    const int nb = (T + PB - 1) / PB;
+    fetch_block(0, T < PB ? T : PB);
+#pragma unroll
+    for (int e = 0; e < SPASS; ++e)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sm.sst[(tid / GPR + e * SROWS) * SP + (tid % GPR) * 4 + c] = sl[e][c];
+    stage_block(0, T < PB ? T : PB);
+    __syncthreads();
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = sm.sst[(ig * R + r) * SP + jw];
+
+    float kc[R], qc[R], kn[R], qn[R];
+    float vj = 0.f, at = 0.f, bt = 0.f, vn = 0.f, an = 0.f, bn = 0.f;
+    for (int blk = 0; blk < nb; ++blk) {
+        const int buf = blk & 1;
+        const int t0 = blk * PB;
+        const int n = T - t0 < PB ? T - t0 : PB;
+        const int t1 = t0 + PB;
+        const int n1 = T - t1 < PB ? T - t1 : PB;
+        if (blk + 1 < nb) fetch_block(t1, n1);   // uniform: the next block's loads in flight
+        auto fetch = [&](int t) {
+#pragma unroll
+            for (int c = 0; c < R / 4; ++c) {
+                const xv_f32x4 k4 = *reinterpret_cast<const xv_f32x4*>(&sm.skq[buf][t][0][ig * R + c * 4]);
+                const xv_f32x4 q4 = *reinterpret_cast<const xv_f32x4*>(&sm.skq[buf][t][1][ig * R + c * 4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { kn[c * 4 + e] = k4[e]; qn[c * 4 + e] = q4[e]; }
+            }
+            vn = xv_bf16_to_f32(sm.sv[buf][t][jw]);
+            an = sm.sab[buf][t][0];
+            bn = sm.sab[buf][t][1];
+        };
+        auto take = [&]() {
+#pragma unroll
+            for (int r = 0; r < R; ++r) { kc[r] = kn[r]; qc[r] = qn[r]; }
+            vj = vn; at = an; bt = bn;
+        };
+        fetch(0);
+        take();
+        for (int t = 0; t < n; ++t) {
+            if (t + 1 < n) fetch(t + 1);
+            xv_gdn_token<R>(s, kc, vj, at, bt);
+            const float ot = xv_gdn_dot<R>(s, qc);
+            if (ig == 0) {
+                const size_t oi = (((size_t)b * T + t0 + t) * Hv + h) * dv + j0 + jw;
+                A.o[oi] = xv_f32_to_bf16(ot);
+                if (A.o32) A.o32[oi] = ot;
+            }
+            if (t + 1 < n) take();
+        }
+        if (blk + 1 < nb) stage_block(buf ^ 1, n1);   // the other buffer: last read a block ago
+        __syncthreads();
+    }
+    // the slab out
+#pragma unroll
+    for (int r = 0; r < R; ++r) sm.sst[(ig * R + r) * SP + jw] = s[r];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < SPASS; ++e) {
+        xv_f32x4 out;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) out[c] = sm.sst[(tid / GPR + e * SROWS) * SP + (tid % GPR) * 4 + c];
+        *reinterpret_cast<xv_f32x4*>(A.S_out + slab + (size_t)(tid / GPR + e * SROWS) * dv) = out;
+    }
+}
 
 // The argument checks of xv_gdn_verify and the launch arguments (B == 0: checked, nothing to run).
 inline int xv_gdn_args_verify(XvGdnArgs& args, const uint16_t* q, const uint16_t* k, const uint16_t* v,

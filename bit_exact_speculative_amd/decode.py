@@ -126,7 +126,6 @@ class Decoder:
         self._free = (torch.empty_like(self._S), torch.empty_like(self._S)) if lazy else None
         self._kv_scratch = torch.zeros_like(self.kv_len)
         self._slot = 0
-        self._keep_all = {}
         self.Lmax = Lmax
         self.scale = 1.0 / float(wl.d) ** 0.5
         self._rows = {}
@@ -200,73 +199,56 @@ class Decoder:
             self._S, self._S2 = self._S2, self._S
         return R
 
-    def prefill(self, prompt, chunk: int = 8192, rows: int = 16):
+    def prefill(self, prompt, chunk: int = 8192):
         """Runs a prompt (int32 [B][P], one length for every request) through the layer, every
         row kept: the step before decoding.  The prompt goes in chunks of ``chunk`` tokens in
         order; per chunk the embedding, both projections and the split run over all of its
-        rows at once (each row's bits are its bits at any M), then GDN and attention run as
-        verify steps of ``rows`` rows that keep every row (decode arithmetic per row); the
-        head, the greedy id and its logprob are formed for the last prompt row.  Neither
-        ``chunk`` nor ``rows`` changes a bit of the result, which equals feeding the prompt
-        one token at a time.  Returns (ids [B], logprobs [B]) of the first generated token
-        (device tensors); the state, KV cache and lengths advance by P."""
+        rows at once (each row's bits are its bits at any M), GDN over the chunk's rows
+        (xv_gdn_prefill) and attention over them (xv_attn_prefill, which appends the rows
+        and advances the length), each row with the decode arithmetic; then the head, the
+        greedy id and its logprob for the last prompt row.  ``chunk`` changes no bit of the
+        result, which equals feeding the prompt one token at a time.  Returns (ids [B],
+        logprobs [B]) of the first generated token (device tensors); the state, KV cache and
+        lengths advance by P."""
         wl, st, dev = self.wl, self.stream, self.device
         prompt = np.ascontiguousarray(prompt, dtype=np.int32)
         B, P = prompt.shape
-        if B != wl.B or P < 1 or chunk < 1 or not 1 <= rows <= 16:
-            raise ValueError("prefill: bad prompt shape, chunk or rows")
+        if B != wl.B or P < 1 or chunk < 1:
+            raise ValueError("prefill: bad prompt shape or chunk")
         self.settle()
         e = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=dev)
         f = lambda *sh: torch.empty(sh, dtype=torch.float32, device=dev)
-        ws = None
         for c0 in range(0, P, chunk):
             cp = min(chunk, P - c0)
-            # rows in step-major order (step, request, row of the step): each step's rows
-            # are then one contiguous [B][tt] block of every chunk buffer
-            steps = [(t0, min(rows, cp - t0)) for t0 in range(0, cp, rows)]
-            order = np.concatenate([prompt[:, c0 + t0:c0 + t0 + tt].reshape(-1) for t0, tt in steps])
-            order = torch.from_numpy(order).to(dev)
             M = B * cp
+            ids = torch.from_numpy(np.ascontiguousarray(prompt[:, c0:c0 + cp]).reshape(-1)).to(dev)
             x, y1, y2 = e(M, wl.K), e(M, wl.N1), e(M, wl.N2)
-            q, k, v = e(M, wl.Hk, wl.dk), e(M, wl.Hk, wl.dk), e(M, wl.Hv, wl.dv)
-            a, b = f(M, wl.Hv), f(M, wl.Hv)
-            qa, kn, vn = e(M, wl.Hq, wl.d), e(M, wl.Hkv, wl.d), e(M, wl.Hkv, wl.d)
-            og, oa = e(M, wl.Hv, wl.dv), e(M, wl.Hq, wl.d)
-            xv.xv_embed_rows(self.E, order, x, stream=st)
+            q, k, v = e(B, cp, wl.Hk, wl.dk), e(B, cp, wl.Hk, wl.dk), e(B, cp, wl.Hv, wl.dv)
+            a, b = f(B, cp, wl.Hv), f(B, cp, wl.Hv)
+            qa, kn, vn = e(B, cp, wl.Hq, wl.d), e(B, cp, wl.Hkv, wl.d), e(B, cp, wl.Hkv, wl.d)
+            og, oa = e(B, cp, wl.Hv, wl.dv), e(B, cp, wl.Hq, wl.d)
+            xv.xv_embed_rows(self.E, ids, x, stream=st)
             xv.xv_gemm_small_m_pair(x, self.W1, y1, None, x, self.W2, y2, None, stream=st)
             xv.xv_split_projections(y1, y2, q, k, v, a, b, qa, kn, vn, stream=st)
-            m0 = 0
-            for t0, tt in steps:
-                sl = slice(m0, m0 + B * tt)
-                m0 += B * tt
-                rs = lambda t, *tail: t[sl].view(B, tt, *tail)
-                if (B, tt) not in self._keep_all:     # n_keep = tt for every request (host-made)
-                    self._keep_all[(B, tt)] = torch.from_numpy(np.full((B,), tt, np.int32)).to(dev)
-                nb = xv.xv_attn_workspace_bytes(B, tt, wl.Hq, wl.d, self.Lmax)
-                if ws is None or ws.numel() * 4 < nb:
-                    ws = f((max(nb, 16) + 15) // 16 * 4)
-                xv.xv_gdn_attn_verify(rs(q, wl.Hk, wl.dk), rs(k, wl.Hk, wl.dk), rs(v, wl.Hv, wl.dv),
-                                      rs(a, wl.Hv), rs(b, wl.Hv), self._S, self._S2, rs(og, wl.Hv, wl.dv),
-                                      rs(qa, wl.Hq, wl.d), rs(kn, wl.Hkv, wl.d), rs(vn, wl.Hkv, wl.d),
-                                      self.Kc, self.Vc, self.kv_len, rs(oa, wl.Hq, wl.d), ws, self.scale,
-                                      stream=st)
-                # every row kept: the state is S_T as computed, the length grows by tt
-                xv.xv_rollback_to_prefix(rs(k, wl.Hk, wl.dk), rs(v, wl.Hv, wl.dv), rs(a, wl.Hv),
-                                         rs(b, wl.Hv), self._S, self._S2, self.kv_len, self._keep_all[(B, tt)],
-                                         stream=st)
-                self._S, self._S2 = self._S2, self._S
-        # the head and the greedy id of the last step's rows; the last row is the answer
-        Mt = B * tt
-        lg, la = e(Mt, wl.NH), e(Mt, wl.NH)
-        lg32, la32 = f(Mt, wl.NH), f(Mt, wl.NH)
-        xv.xv_gemm_small_m_pair(og[sl].view(Mt, wl.Hv * wl.dv), self.Wh_g, lg, lg32,
-                                oa[sl].view(Mt, wl.Hq * wl.d), self.Wh_a, la, la32, stream=st)
-        ids = torch.empty((B, tt), dtype=torch.int32, device=dev)
+            xv.xv_gdn_prefill(q, k, v, a, b, self._S, self._S2, og, None, stream=st)
+            self._S, self._S2 = self._S2, self._S
+            xv.xv_attn_prefill(qa, kn, vn, self.Kc, self.Vc, self.kv_len, oa, None, self.scale, advance=True,
+                               stream=st)
+        # the head and the greedy id of each request's last prompt row (rows gathered by the
+        # library's row-copy kernel)
+        last = torch.from_numpy((np.arange(B, dtype=np.int32) * cp + cp - 1).astype(np.int32)).to(dev)
+        xg, xa = e(B, wl.Hv * wl.dv), e(B, wl.Hq * wl.d)
+        xv.xv_embed_rows(og.view(M, wl.Hv * wl.dv), last, xg, stream=st)
+        xv.xv_embed_rows(oa.view(M, wl.Hq * wl.d), last, xa, stream=st)
+        lg, la = e(B, wl.NH), e(B, wl.NH)
+        lg32, la32 = f(B, wl.NH), f(B, wl.NH)
+        xv.xv_gemm_small_m_pair(xg, self.Wh_g, lg, lg32, xa, self.Wh_a, la, la32, stream=st)
+        out = torch.empty((B, 1), dtype=torch.int32, device=dev)
         nk = torch.empty((B,), dtype=torch.int32, device=dev)
-        lp = f(B, tt)
-        toks = order[M - Mt:].view(B, tt)
-        xv.xv_greedy_accept(lg32.view(B, tt, wl.NH), la32.view(B, tt, wl.NH), toks, ids, nk, lp, stream=st)
-        return ids[:, tt - 1], lp[:, tt - 1]
+        lp = f(B, 1)
+        toks = torch.from_numpy(np.ascontiguousarray(prompt[:, P - 1:])).to(dev)
+        xv.xv_greedy_accept(lg32.view(B, 1, wl.NH), la32.view(B, 1, wl.NH), toks, out, nk, lp, stream=st)
+        return out[:, 0], lp[:, 0]
 
     def snapshot(self):
         """Copies of the decoding state (GDN state, KV cache, lengths)."""

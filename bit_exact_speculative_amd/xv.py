@@ -52,6 +52,10 @@ _lib.xv_rollback_to_prefix.restype = _I
 _lib.xv_rollback_to_prefix.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
 _lib.xv_greedy_accept.restype = _I
 _lib.xv_greedy_accept.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P]
+_lib.xv_gdn_prefill.restype = _I
+_lib.xv_gdn_prefill.argtypes = [_P] * 9 + [_I] * 6 + [_P]
+_lib.xv_attn_prefill.restype = _I
+_lib.xv_attn_prefill.argtypes = [_P] * 8 + [_I] * 6 + [_F, _I, _P]
 _lib.xv_gdn_attn_verify.restype = _I
 _lib.xv_gdn_attn_verify.argtypes = ([_P] * 10 + [_I] + [_P] * 6 + [_I] * 4 + [_P] * 9 + [_S] +
                                     [_I] * 4 + [_F] + [_I, _I, _P])
@@ -242,6 +246,40 @@ def xv_gdn_attn_verify(q, k, v, a, b, state_in, state_out, o, q_attn, k_new, v_n
         _ptr(q_attn), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
         _ptr(o_attn), _ptr(o_attn32), _ptr(workspace), wbytes, Hq, Hkv, d, Lmax, float(scale),
         B, T, _stream(stream)))
+
+
+def xv_gdn_prefill(q, k, v, a, b, state_in, state_out, o, o32=None, stream=None):
+    """GDN over a whole prompt (any T), every row kept; shapes as xv_gdn_verify."""
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, T, Hk, dk) or tuple(v.shape[:2]) != (B, T) or \
+            tuple(a.shape) != (B, T, Hv) or tuple(b.shape) != (B, T, Hv) or \
+            tuple(state_in.shape) != (B, Hv, dk, dv) or tuple(state_out.shape) != (B, Hv, dk, dv) or \
+            tuple(o.shape) != (B, T, Hv, dv) or (o32 is not None and tuple(o32.shape) != (B, T, Hv, dv)):
+        raise ValueError("xv_gdn_prefill: shape mismatch")
+    _check("xv_gdn_prefill", _lib.xv_gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                                _ptr(state_in), _ptr(state_out), _ptr(o), _ptr(o32),
+                                                B, T, Hk, Hv, dk, dv, _stream(stream)))
+
+
+def xv_attn_prefill(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32=None, scale=None, advance=False,
+                    stream=None):
+    """P prompt rows at once: appends k_new / v_new at kv_len and forms every row's attention
+    with the decode row's arithmetic (advance: then kv_len += P).  q [B][P][Hq][d]; k_new,
+    v_new [B][P][Hkv][d]."""
+    B, P, Hq, d = q.shape
+    Hkv = k_new.shape[2]
+    Lmax = k_cache.shape[2]
+    if tuple(k_new.shape) != (B, P, Hkv, d) or tuple(v_new.shape) != (B, P, Hkv, d) or \
+            tuple(k_cache.shape) != (B, Hkv, Lmax, d) or tuple(v_cache.shape) != (B, Hkv, Lmax, d) or \
+            tuple(kv_len.shape) != (B,) or tuple(o.shape) != (B, P, Hq, d) or \
+            (o32 is not None and tuple(o32.shape) != (B, P, Hq, d)):
+        raise ValueError("xv_attn_prefill: shape mismatch")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    _check("xv_attn_prefill", _lib.xv_attn_prefill(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(o), _ptr(o32),
+        B, P, Hq, Hkv, d, Lmax, float(scale), 1 if advance else 0, _stream(stream)))
 
 
 def xv_attn_verify_rows(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32=None, workspace=None,

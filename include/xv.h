@@ -134,6 +134,19 @@ int xv_gdn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   int B, int T, int Hk, int Hv, int dk, int dv, void* stream);
 
 /*
+ * GDN over the T rows of a prompt (prefill; any T >= 1), every row kept: the same
+ * per-token arithmetic as xv_gdn_verify, so the outputs and S_T equal T one-token
+ * calls bit for bit.  The state stays in registers for the whole call and the rows
+ * stream through LDS in blocks of 16.  Arguments, layouts and errors as
+ * xv_gdn_verify except 1 <= T < 2^30.
+ */
+int xv_gdn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   const float* a, const float* b,
+                   const float* state_in, float* state_out,
+                   uint16_t* o, float* o32,
+                   int B, int T, int Hk, int Hv, int dk, int dv, void* stream);
+
+/*
  * GDN verify after a verify whose rollback was not run (a lazy rollback: one
  * launch instead of a rollback and a verify).  The previous call ran T_prev
  * rows from state_prev_in to state_prev_out, and n = n_keep_prev[b] of its rows
@@ -237,6 +250,27 @@ int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        uint16_t* o_attn, float* o_attn32, void* workspace, size_t workspace_bytes,
                        int Hq, int Hkv, int d, int Lmax, float scale,
                        int B, int T, void* stream);
+
+/*
+ * Attention of P prompt rows at once (prefill; launch command: chunked prefill).
+ * The P new key/value rows are appended at cache positions L0..L0+P-1
+ * (L0 = kv_len[b]), then row r attends positions 0..L0+r with
+ * exactly the arithmetic of xv_attn_verify_rows for that row (the same chunk
+ * partials and the same ordered combine), so every output equals the decode
+ * row's bit for bit.  No workspace: each workgroup keeps 128 (row, head) pairs'
+ * partials in registers, after a first pass over the chunks for each row's
+ * maximum.
+ *   q      : bf16 [B][P][Hq][d]  [16B]     k_new, v_new : bf16 [B][P][Hkv][d] [16B]
+ *   k_cache, v_cache : bf16 [B][Hkv][Lmax][d] [16B]; rows L0..L0+P-1 are written
+ *   kv_len : int32 [B] device; advance != 0: kv_len[b] += P after the rows are formed
+ *   o : bf16 [B][P][Hq][d]   o32 : fp32 or NULL
+ * Shapes: B >= 0, P >= 1, Hq % Hkv == 0, d in {64, 128, 256}, Lmax >= P.  Device
+ * precondition: 0 <= L0 and L0 + P <= Lmax (positions are clamped otherwise).
+ */
+int xv_attn_prefill(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                    uint16_t* k_cache, uint16_t* v_cache, int32_t* kv_len,
+                    uint16_t* o, float* o32, int B, int P, int Hq, int Hkv, int d, int Lmax,
+                    float scale, int advance, void* stream);
 
 /*
  * Rollback to the accepted prefix.

@@ -26,7 +26,8 @@ def test_every_header_symbol_is_exported(xv):
                           "xv_rollback_to_prefix", "xv_attn_workspace_bytes",
                           "xv_attn_chunk_tokens", "xv_abi_version", "xv_status_string",
                           "xv_greedy_accept", "xv_embed_rows", "xv_split_projections",
-                          "xv_gemm_small_m_pair", "xv_gdn_verify_after", "xv_gdn_attn_verify"}
+                          "xv_gemm_small_m_pair", "xv_gdn_verify_after", "xv_gdn_attn_verify",
+                          "xv_attn_prefill", "xv_gdn_prefill"}
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -99,6 +100,18 @@ def test_gdn_argument_errors(xv):
     assert r(A, A, A, A, A, A + 0x1000, A, A, 0, 9, 16, 48, 128, 128, None) == 0
 
 
+def test_gdn_prefill_argument_errors(xv):
+    f = xv.lib().xv_gdn_prefill
+
+    def call(q=A, si=A, so=A + 0x100000, o=A, T=9000, B=1, dk=128, dv=128):
+        return f(q, A, A, A, A, si, so, o, None, B, T, 16, 48, dk, dv, None)
+
+    assert call(B=0) == 0
+    assert call(T=0) == -2 and call(dk=96) == -2 and call(dv=16) == -2
+    assert call(q=None) == -1 and call(o=None) == -1
+    assert call(q=MIS) == -3 and call(so=A) == -6
+
+
 def test_gdn_verify_after_argument_errors(xv):
     f = xv.lib().xv_gdn_verify_after
     ok = dict(Tp=9, B=1, T=9, Hk=16, Hv=48, dk=128, dv=128)
@@ -137,6 +150,19 @@ def test_gdn_attn_argument_errors(xv):
     assert call(nk=A, Tp=9) == -1                               # after a verify: its rows are needed
     assert call(nk=A, Tp=0, kp=A, sp=S[2], sk=S[3]) == -2       # T_prev
     assert call(nk=A, Tp=9, kp=A, sp=S[2], sk=S[0]) == -6       # state_kept aliases state_in
+
+
+def test_attn_prefill_argument_errors(xv):
+    f = xv.lib().xv_attn_prefill
+
+    def call(q=A, o=A, kvl=A, B=1, P=100, Hq=24, Hkv=4, d=256, Lmax=1000, scale=0.0625):
+        return f(q, A, A, A, A, kvl, o, None, B, P, Hq, Hkv, d, Lmax, scale, 0, None)
+
+    assert call(B=0) == 0
+    assert call(P=0) == -2 and call(Hq=25) == -2 and call(d=96) == -2 and call(Lmax=99) == -2
+    assert call(scale=float("nan")) == -2
+    assert call(q=None) == -1 and call(kvl=None) == -1 and call(o=None) == -1
+    assert call(q=MIS) == -3 and call(o=ODD) == -3
 
 
 def test_attn_argument_errors(xv):

@@ -224,3 +224,26 @@ def test_verify_after_chain_equals_sequential_decode():
             assert same_bits(outs[i][0][bb, :n], od[0]) and same_bits(outs[i][1][bb, :n], o32d[0]), (bb, i)
             S = Sd[-1]
         assert same_bits(Q[bb], S[0]), bb
+
+
+@pytest.mark.parametrize("T,dk,dv", [(1, 128, 128), (16, 128, 128), (17, 64, 64), (45, 128, 96), (300, 128, 128)])
+def test_gdn_prefill_equals_verify_steps(T, dk, dv):
+    """xv_gdn_prefill over T rows gives the outputs and final state of verify steps of at
+    most 16 rows (and so of one-token decoding), bit for bit."""
+    B, Hk, Hv = 2, 2, 4
+    r, S0 = _case(1600 + T + dk, B, T, Hk, Hv, dk, dv)
+    d = _dev(r)
+    S_in = torch.from_numpy(S0).cuda()
+    S_out = torch.empty_like(S_in)
+    o = torch.empty((B, T, Hv, dv), dtype=torch.bfloat16, device="cuda")
+    o32 = torch.empty((B, T, Hv, dv), dtype=torch.float32, device="cuda")
+    _xv().xv_gdn_prefill(d["q"], d["k"], d["v"], d["a"], d["b"], S_in, S_out, o, o32)
+    S = S_in.clone()
+    o_r, o32_r = torch.empty_like(o), torch.empty_like(o32)
+    for t0 in range(0, T, 16):
+        tt = min(16, T - t0)
+        dt = {k: v[:, t0:t0 + tt].contiguous() for k, v in d.items()}
+        os_, o32s, S = _verify(dt, S)
+        o_r[:, t0:t0 + tt] = os_; o32_r[:, t0:t0 + tt] = o32s
+    torch.cuda.synchronize()
+    assert same_bits(o, o_r) and same_bits(o32, o32_r) and same_bits(S_out, S)

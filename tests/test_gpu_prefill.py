@@ -38,12 +38,12 @@ def _one_token_at_a_time(dec, prompt):
     return R.ids[:, 0].clone(), R.lp[:, 0].clone()
 
 
-@pytest.mark.parametrize("name,P,chunk,rows", [("tiny", 37, 8192, 16), ("tiny", 37, 10, 7),
-                                               ("short", 45, 16, 16), ("batch8", 21, 8, 5)])
-def test_prefill_equals_one_token_decoding(name, P, chunk, rows):
+@pytest.mark.parametrize("name,P,chunk", [("tiny", 37, 8192), ("tiny", 37, 10), ("short", 45, 16),
+                                         ("short", 300, 128), ("batch8", 21, 8)])
+def test_prefill_equals_one_token_decoding(name, P, chunk):
     dec_a, inp, wl = _decoder(name, P + 8)
-    prompt = _prompt(wl, P, P + rows)
-    id_a, lp_a = dec_a.prefill(prompt, chunk=chunk, rows=rows)
+    prompt = _prompt(wl, P, P + chunk)
+    id_a, lp_a = dec_a.prefill(prompt, chunk=chunk)
     torch.cuda.synchronize()
     dec_b, _, _ = _decoder(name, P + 8)
     id_b, lp_b = _one_token_at_a_time(dec_b, prompt)
@@ -86,7 +86,7 @@ def test_prefill_vs_oracle_tiny():
     P = 40
     dec, _, _ = _decoder("tiny", P + 8, S0=S0)
     prompt = _prompt(wl, P, 11)
-    id_g, lp_g = dec.prefill(prompt, chunk=16, rows=16)
+    id_g, lp_g = dec.prefill(prompt, chunk=16)
     torch.cuda.synchronize()
     s = C.Shapes(wl.Hk, wl.Hv, wl.dk, wl.dv, wl.Hq, wl.Hkv, wl.d)
     m = C.Model(inp.extra["E"], inp.W1, inp.W2, inp.Wh_gdn, inp.Wh_attn, s)
