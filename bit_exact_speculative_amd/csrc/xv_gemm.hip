@@ -546,6 +546,122 @@ void xv_gemm_big_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
         }
 }
 
+// 2 to 5 row tiles (a batch of requests' verify rows) and K a multiple of 512: the
+// 16 ranges have KSW = K / 512 k-steps each.  A workgroup (16 waves) owns NBW column
+// blocks of one problem of the pair and walks the ranges in order, each in two parts of
+// KSP = KSW / 2 k-steps; a part's x slice (all row tiles) and W slice (the NBW blocks) go
+// through double-buffered LDS, the next part's loads in flight in registers.  Wave w owns
+// the (row tile, column block) tiles i = w, w + 16, ...; per tile one chain per range from
+// zero, folded into the running sum in range order: the bits of every other variant.
+// Each W byte is read once; x is re-read from L2 by every workgroup (it is small).
+template <int MT, int KSP, int NBW>
+__global__ __launch_bounds__(XV_GEMM_THREADS)
+void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
+{
+    constexpr int NT = XV_GEMM_THREADS;
+    constexpr int XR = MT * 16, WR = NBW * 16;  // rows of a part: x, W
+    constexpr int GR = KSP * 4;                 // 16-byte granules per row of a part
+    constexpr int PITCH = KSP * 32 + 8;         // LDS row pitch (bf16): 16 rows fall on distinct banks
+    constexpr int GPT = ((XR + WR) * GR + NT - 1) / NT;
+    constexpr int NTILE = MT * NBW;
+    constexpr int PPW = (NTILE + XV_GEMM_WAVES - 1) / XV_GEMM_WAVES;
+    constexpr int NPARTS = XV_GEMM_WAVES * 2;
+    __shared__ __attribute__((aligned(16))) uint16_t sm[(XR + WR) * PITCH];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int cur = (int)blockIdx.x < nwg0 ? 0 : 1;
+    const int blk0 = ((int)blockIdx.x - cur * nwg0) * NBW;     // first column block, local to the problem
+    const uint16_t* __restrict__ x = pp.x[cur];
+    const uint16_t* __restrict__ w = pp.w[cur];
+    const int N = pp.N[cur];
+
+    // this thread's granules of a part: g = tid + i NT over the x rows, then the W rows;
+    // rows past the buffers re-read the last one (their outputs are not stored)
+    const uint16_t* src[GPT];
+    int dst[GPT];
+    bool live[GPT];
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+        int g = tid + i * NT;
+        live[i] = g < (XR + WR) * GR;
+        g = live[i] ? g : 0;
+        const int r = g / GR, c = g % GR;
+        if (r < XR) {
+            src[i] = x + (size_t)(r < M ? r : M - 1) * K + c * 8;
+        } else {
+            const int n = blk0 * 16 + (r - XR);
+            src[i] = w + (size_t)(n < N ? n : N - 1) * K + c * 8;
+        }
+        dst[i] = r * PITCH + c * 8;
+    }
+    auto load = [&](xv_u32x4 (&reg)[GPT], int part) {   // k-steps part * KSP ..; past the end re-read
+        const int k0 = (part < NPARTS ? part : NPARTS - 1) * (KSP * 32);
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) reg[i] = xv_load16(src[i] + k0);
+    };
+    auto store = [&](const xv_u32x4 (&reg)[GPT]) {
+#pragma unroll
+        for (int i = 0; i < GPT; ++i)
+            if (live[i]) *reinterpret_cast<xv_u32x4*>(&sm[dst[i]]) = reg[i];
+    };
+
+    xv_f32x4 acc[PPW], sum[PPW];
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) { acc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f}; sum[j] = acc[j]; }
+
+    xv_u32x4 r0[GPT], r1[GPT];
+    load(r0, 0);
+    load(r1, 1);
+    for (int part = 0; part < NPARTS; part += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {           // parts of range part / 2: even in r0, odd in r1
+            xv_u32x4 (&reg)[GPT] = h ? r1 : r0;
+            __syncthreads();                    // LDS free
+            store(reg);
+            load(reg, part + h + 2);            // this buffer's next part (past the end: a re-read)
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < PPW; ++j) {
+                const int ti = wave + j * XV_GEMM_WAVES;
+                if (ti < NTILE) {               // uniform per wave
+                    const int t = ti / NBW, bk = ti % NBW;
+                    const uint16_t* ap = &sm[(t * 16 + lr) * PITCH + lg * 8];
+                    const uint16_t* bp = &sm[(XR + bk * 16 + lr) * PITCH + lg * 8];
+#pragma unroll
+                    for (int kk = 0; kk < KSP; ++kk)
+                        acc[j] = xv_mfma16x16x32(*reinterpret_cast<const xv_u32x4*>(ap + kk * 32),
+                                                 *reinterpret_cast<const xv_u32x4*>(bp + kk * 32), acc[j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) {         // range part / 2 complete: folded in order
+            sum[j] = part == 0 ? acc[j] : sum[j] + acc[j];
+            acc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+        const int ti = wave + j * XV_GEMM_WAVES;
+        if (ti >= NTILE) continue;
+        const int t = ti / NBW, bk = ti % NBW;
+        const int col = (blk0 + bk) * 16 + lr;
+        if (col >= N) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = t * 16 + 4 * lg + i;
+            if (row < M) {
+                const size_t o = (size_t)row * N + col;
+                pp.y[cur][o] = xv_f32_to_bf16(sum[j][i]);
+                if (pp.y32[cur]) pp.y32[cur][o] = sum[j][i];
+            }
+        }
+    }
+}
+
 // x fragments re-read per k-step (many row tiles or long K): U k-steps per stage.
 template <int MT, int U>
 __global__ __launch_bounds__(XV_GEMM_THREADS)
@@ -689,6 +805,54 @@ void xv_gemm_launch_xstream(const uint16_t* x, const uint16_t* w, uint16_t* y, f
     hipExtLaunchKernelGGL((xv_gemm_xstream_kernel<MT, U>), grid, block, 0, lc.st, lc.e0, lc.e1, 0, x, w, y, y32, M, N, K, mt0);
 }
 
+// Launch of the 2..5-row-tile kernel for one or two problems (N[1] = 0: one): the fewest
+// column blocks per workgroup that still fit every workgroup on the chip at once (one
+// per CU), so that no CU runs a second round.
+bool xv_gemm_mt_fits(int mt, int K) { return mt >= 2 && mt <= XV_GEMM_MT_MAX && (K == 5120 || K == 6144); }
+
+template <int MT, int KSP>
+void xv_gemm_launch_mt_n(const XvGemmPair& pp, int M, int K, const XvLaunch& lc)
+{
+    const int nb0 = pp.N[0] / 16, nb1 = pp.N[1] / 16;
+    const int cus = xv_gemm_grid(1 << 30);
+    auto wgs = [&](int nbw) { return (nb0 + nbw - 1) / nbw + (nb1 + nbw - 1) / nbw; };
+    int nbw = 1;
+    while (nbw < 8 && wgs(nbw) > cus) ++nbw;
+#define XV_MT_LAUNCH(NBWV)                                                                                   \
+    hipExtLaunchKernelGGL((xv_gemm_mt_kernel<MT, KSP, NBWV>), dim3(wgs(NBWV)), dim3(XV_GEMM_THREADS), 0,    \
+                          lc.st, lc.e0, lc.e1, 0, pp, M, K, (nb0 + NBWV - 1) / NBWV)
+    switch (nbw) {
+        case 1: XV_MT_LAUNCH(1); break;
+        case 2: XV_MT_LAUNCH(2); break;
+        case 3: XV_MT_LAUNCH(3); break;
+        case 4: XV_MT_LAUNCH(4); break;
+        case 5: XV_MT_LAUNCH(5); break;
+        case 6: XV_MT_LAUNCH(6); break;
+        case 7: XV_MT_LAUNCH(7); break;
+        default: XV_MT_LAUNCH(8); break;
+    }
+#undef XV_MT_LAUNCH
+}
+
+void xv_gemm_launch_mt(const XvGemmPair& pp, int mt, int M, int K, const XvLaunch& lc)
+{
+    if (K == 5120) {
+        switch (mt) {
+            case 2: xv_gemm_launch_mt_n<2, 5>(pp, M, K, lc); break;
+            case 3: xv_gemm_launch_mt_n<3, 5>(pp, M, K, lc); break;
+            case 4: xv_gemm_launch_mt_n<4, 5>(pp, M, K, lc); break;
+            default: xv_gemm_launch_mt_n<5, 5>(pp, M, K, lc); break;
+        }
+    } else {
+        switch (mt) {
+            case 2: xv_gemm_launch_mt_n<2, 6>(pp, M, K, lc); break;
+            case 3: xv_gemm_launch_mt_n<3, 6>(pp, M, K, lc); break;
+            case 4: xv_gemm_launch_mt_n<4, 6>(pp, M, K, lc); break;
+            default: xv_gemm_launch_mt_n<5, 6>(pp, M, K, lc); break;
+        }
+    }
+}
+
 // Launch shape per row-tile count and K.  None of these choices changes any
 // row's arithmetic: every variant runs the same 16-way K split, the same MFMA
 // chains and the same ordered sum.
@@ -707,6 +871,12 @@ void xv_gemm_dispatch(int mt, int ksw, const uint16_t* x, const uint16_t* w, uin
         else if (ksw <= 6) xv_gemm_launch_xreg<1, 6>(x, w, y, y32, M, N, K, mt0, lc);
         else if (ksw <= 8) xv_gemm_launch_xreg<1, 8>(x, w, y, y32, M, N, K, mt0, lc);
         else xv_gemm_launch_xreg<1, 10>(x, w, y, y32, M, N, K, mt0, lc);
+        return;
+    }
+    // 2..5 row tiles and the two K of the layer: W streamed once, x from L2
+    if (mt0 == 0 && M <= XV_GEMM_MT_MAX * 16 && xv_gemm_mt_fits(mt, K)) {
+        const XvGemmPair pp{{x, nullptr}, {w, nullptr}, {y, nullptr}, {y32, nullptr}, {N, 0}};
+        xv_gemm_launch_mt(pp, mt, M, K, lc);
         return;
     }
     // several row tiles and many column blocks: walk K per output tile (x reused over 2-4 column blocks)
@@ -786,6 +956,14 @@ extern "C" int xv_gemm_small_m_pair(const uint16_t* x0, const uint16_t* w0, uint
                xv_aligned16(x1) && xv_aligned16(w1) && xv_aligned(y1, 2) && xv_aligned(y32_1, 4),
                XV_ERR_ALIGN);
     const int tiles = (M + 15) / 16;
+    if (tiles >= 2 && tiles <= XV_GEMM_MT_MAX && xv_gemm_mt_fits(tiles, K)) {
+        (void)hipGetLastError();
+        const XvLaunch lc{reinterpret_cast<hipStream_t>(stream), reinterpret_cast<hipEvent_t>(start_event),
+                          reinterpret_cast<hipEvent_t>(stop_event)};
+        const XvGemmPair pp{{x0, x1}, {w0, w1}, {y0, y1}, {y32_0, y32_1}, {N0, N1}};
+        xv_gemm_launch_mt(pp, tiles, M, K, lc);
+        return xv_launch_status();
+    }
     if (!xv_gemm_wlds_fits(tiles, K)) {
         // no fused variant for this shape: the two GEMMs one after the other (same bits)
         int s = xv_gemm_small_m_timed(x0, w0, y0, y32_0, M, N0, K, stream, start_event, nullptr);

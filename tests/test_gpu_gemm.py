@@ -178,8 +178,12 @@ PAIR_CASES = [  # M, K, N0, N1, shared x, with fp32 copies
     (1, 5120, 16, 48, False, False),          # fewer column blocks than CUs
     (16, 6144, 4096, 272, True, True),        # a full row tile, uneven split
     (5, 5120, 8192, 16, False, True),         # problem 1 is one block
-    (20, 5120, 512, 256, True, True),         # two row tiles: no fused variant, one after the other
+    (20, 5120, 512, 256, True, True),         # two row tiles: the row-tile kernel, both problems
+    (72, 5120, 10240, 17408, True, True),     # batch 8: the two projections in one row-tile launch
+    (72, 6144, 4096, 4096, False, True),      # batch 8: the two head halves
+    (40, 6144, 4096, 272, False, False),      # three row tiles, uneven
     (9, 1024, 512, 512, False, False),        # other K: one after the other
+    (40, 1024, 512, 512, True, False),        # other K, several row tiles: one after the other
 ]
 
 
@@ -236,3 +240,25 @@ def test_gemm_many_rows_tiled_kernel_rows_equal_k_split(M, N, K):
     ref = oracle.gemm(xh[rows], wh[cols])
     torch.cuda.synchronize()
     assert max_rel(y32.cpu().numpy()[rows][:, cols], ref) <= OUT_MAX_REL
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 400, 5120), (33, 10240, 5120), (48, 272, 6144), (64, 4096, 6144),
+                                   (72, 17408, 5120), (80, 1040, 5120), (72, 4096, 6144)])
+def test_gemm_row_tiles_weight_streaming_rows_equal_k_split(M, N, K):
+    """2 to 5 row tiles at K = 5120 / 6144 take the weight-streaming row-tile kernel (x from
+    L2, W once, 1 to 6 column blocks per workgroup); every row must equal its M <= 16 bits
+    and sampled entries the oracle."""
+    from bit_exact_speculative_amd.layer import dev_bf16
+    rng = np.random.default_rng(M * 5 + N + K)
+    xh = random_bf16(rng, (M, K))
+    wh = random_bf16(rng, (N, K), 0.02)
+    x = dev_bf16(xh, "cuda"); w = dev_bf16(wh, "cuda")
+    y, y32 = _gemm_dev(x, w)
+    for r0 in sorted(set([0, 16, M - 9] + [int(v) for v in rng.integers(0, M - 9, size=3)])):
+        ys, ys32 = _gemm_dev(x[r0:r0 + 9].contiguous(), w)
+        assert torch.equal(ys32.view(torch.int32), y32[r0:r0 + 9].view(torch.int32)), r0
+        assert torch.equal(ys.view(torch.int16), y[r0:r0 + 9].view(torch.int16)), r0
+    cols = np.sort(rng.choice(N, size=min(N, 48), replace=False))
+    ref = oracle.gemm(xh, wh[cols])
+    torch.cuda.synchronize()
+    assert max_rel(y32.cpu().numpy()[:, cols], ref) <= OUT_MAX_REL
