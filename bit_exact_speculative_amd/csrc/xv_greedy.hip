@@ -88,22 +88,18 @@ __device__ __forceinline__ void xv_lse_add(float& m, float& s, float m2, float s
 
 constexpr int XV_GREEDY_BPP = 2;      // blocks per thread per pass, all loaded before any compare
 
+// One row's scan by 256 threads (ltid = 0..255): the thread's chain of 16-column blocks
+// and its running argmax, then the 64-lane butterflies.
 template <bool VEC>
-__global__ __launch_bounds__(XV_GREEDY_THREADS)
-void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb, int T, int N,
-                      int32_t* __restrict__ ids, float* __restrict__ lp)
+__device__ __forceinline__ void xv_row_scan(const float* __restrict__ la, const float* __restrict__ lb,
+                                            size_t row, int N, int ltid, bool want_lp,
+                                            float& best, int& bn, float& cm, float& cs)
 {
-    __shared__ float sv[XV_GREEDY_WAVES];
-    __shared__ int sn[XV_GREEDY_WAVES];
-    __shared__ float sm[XV_GREEDY_WAVES], ssum[XV_GREEDY_WAVES];
-    const int t = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x;
-    const size_t row = ((size_t)b * T + t) * N;
     const int nb = (N + 15) >> 4;
-    float best = -INFINITY;
-    int bn = N;                                  // sentinel: after every real index
-    float cm = -INFINITY, cs = 0.f;              // this thread's chain: blocks tid + 256 i
-    for (int b0 = tid; b0 < nb; b0 += XV_GREEDY_THREADS * XV_GREEDY_BPP) {
+    best = -INFINITY;
+    bn = N;                                      // sentinel: after every real index
+    cm = -INFINITY; cs = 0.f;                    // this thread's chain: blocks ltid + 256 i
+    for (int b0 = ltid; b0 < nb; b0 += XV_GREEDY_THREADS * XV_GREEDY_BPP) {
         float x[XV_GREEDY_BPP][16];
 #pragma unroll
         for (int u = 0; u < XV_GREEDY_BPP; ++u) xv_row_block<VEC>(la, lb, row, N, b0 + u * XV_GREEDY_THREADS, x[u]);
@@ -118,7 +114,7 @@ void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb
                 if (ok && xv_better(x[u][c], n, best, bn)) { best = x[u][c]; bn = n; }
                 bm = ok ? fmaxf(bm, x[u][c]) : bm;
             }
-            if (lp) {                            // uniform
+            if (want_lp) {                       // uniform
                 float e[16];
 #pragma unroll
                 for (int c = 0; c < 16; ++c) {
@@ -141,22 +137,49 @@ void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb
         const int on = __shfl_xor(bn, off);
         if (xv_better(ov, on, best, bn)) { best = ov; bn = on; }
     }
-    if (lp) {
+    if (want_lp) {
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) xv_lse_add(cm, cs, __shfl_xor(cm, off), __shfl_xor(cs, off));
     }
+}
+
+// The four waves of a row folded left to right: the id (lowest index among the maxima) and
+// lp = -ln S.
+__device__ __forceinline__ void xv_row_fold(const float* sv, const int* sn, const float* sm, const float* ssum,
+                                            int N, int& id, float& lpv)
+{
+    float best = sv[0];
+    int bn = sn[0];
+    for (int w = 1; w < XV_GREEDY_WAVES; ++w)
+        if (xv_better(sv[w], sn[w], best, bn)) { best = sv[w]; bn = sn[w]; }
+    id = bn < N ? bn : 0;
+    float m = sm[0], sum = ssum[0];
+    for (int w = 1; w < XV_GREEDY_WAVES; ++w) xv_lse_add(m, sum, sm[w], ssum[w]);
+    constexpr float LN2 = 0.6931471805599453f;
+    lpv = -(__builtin_amdgcn_logf(sum) * LN2);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(XV_GREEDY_THREADS)
+void xv_argmax_kernel(const float* __restrict__ la, const float* __restrict__ lb, int T, int N,
+                      int32_t* __restrict__ ids, float* __restrict__ lp)
+{
+    __shared__ float sv[XV_GREEDY_WAVES];
+    __shared__ int sn[XV_GREEDY_WAVES];
+    __shared__ float sm[XV_GREEDY_WAVES], ssum[XV_GREEDY_WAVES];
+    const int t = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x;
+    float best, cm, cs;
+    int bn;
+    xv_row_scan<VEC>(la, lb, ((size_t)b * T + t) * N, N, tid, lp != nullptr, best, bn, cm, cs);
     if ((tid & 63) == 0) { sv[tid >> 6] = best; sn[tid >> 6] = bn; sm[tid >> 6] = cm; ssum[tid >> 6] = cs; }
     __syncthreads();
     if (tid == 0) {
-        for (int w = 1; w < XV_GREEDY_WAVES; ++w)
-            if (xv_better(sv[w], sn[w], best, bn)) { best = sv[w]; bn = sn[w]; }
-        ids[(size_t)b * T + t] = bn < N ? bn : 0;
-        if (lp) {
-            float m = sm[0], sum = ssum[0];
-            for (int w = 1; w < XV_GREEDY_WAVES; ++w) xv_lse_add(m, sum, sm[w], ssum[w]);
-            constexpr float LN2 = 0.6931471805599453f;
-            lp[(size_t)b * T + t] = -(__builtin_amdgcn_logf(sum) * LN2);
-        }
+        int id;
+        float lpv;
+        xv_row_fold(sv, sn, sm, ssum, N, id, lpv);
+        ids[(size_t)b * T + t] = id;
+        if (lp) lp[(size_t)b * T + t] = lpv;
     }
 }
 
