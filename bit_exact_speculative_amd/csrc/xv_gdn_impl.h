@@ -242,47 +242,36 @@ __device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, in
         }
     };
 
-    // Token t's rows are in registers while token t+1's are already being read from LDS.
-    float kc[R], qc[R], kn[R], qn[R];
-    float vj[CPT], vn[CPT];
-    float at = 0.f, bt = 0.f, an = 0.f, bn = 0.f;
-    auto fetch = [&](int t) {
+    // Two register sets used alternately: token t's rows are in one while token t+1's are
+    // read from LDS into the other (no copies between them).
+    float k0[R], q0[R], k1[R], q1[R];
+    float v0[CPT], v1[CPT];
+    float a0 = 0.f, b0 = 0.f, a1 = 0.f, b1 = 0.f;
+    auto fetch = [&](int t, float (&kk)[R], float (&qq)[R], float (&vv2)[CPT], float& aa, float& bb) {
 #pragma unroll
         for (int c = 0; c < R / 4; ++c) {
             const xv_f32x4 k4 = *reinterpret_cast<const xv_f32x4*>(&sm.skq[t][0][ig * R + c * 4]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) kn[c * 4 + e] = k4[e];
+            for (int e = 0; e < 4; ++e) kk[c * 4 + e] = k4[e];
             if (!ROLLBACK) {
                 const xv_f32x4 q4 = *reinterpret_cast<const xv_f32x4*>(&sm.skq[t][1][ig * R + c * 4]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) qn[c * 4 + e] = q4[e];
+                for (int e = 0; e < 4; ++e) qq[c * 4 + e] = q4[e];
             }
         }
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) vn[c] = xv_bf16_to_f32(sm.sv[t][jw + XV_GDN_JW * c]);
-        an = sm.sab[t][0];
-        bn = sm.sab[t][1];
+        for (int c = 0; c < CPT; ++c) vv2[c] = xv_bf16_to_f32(sm.sv[t][jw + XV_GDN_JW * c]);
+        aa = sm.sab[t][0];
+        bb = sm.sab[t][1];
     };
-    auto take = [&]() {
-#pragma unroll
-        for (int r = 0; r < R; ++r) { kc[r] = kn[r]; qc[r] = ROLLBACK ? 0.f : qn[r]; }
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) vj[c] = vn[c];
-        at = an; bt = bn;
-    };
-    if (n > 0) {
-        fetch(0);
-        take();
-    }
-    for (int t = 0; t < n; ++t) {
+    auto step = [&](int t, const float (&kk)[R], const float (&qq)[R], const float (&vv2)[CPT], float aa, float bb) {
         if (!ROLLBACK && A.S_mid && t == np) store_state(A.S_mid);   // uniform: the kept state
-        if (t + 1 < n) fetch(t + 1);         // uniform
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) xv_gdn_token<R>(s[c], kc, vj[c], at, bt);
+        for (int c = 0; c < CPT; ++c) xv_gdn_token<R>(s[c], kk, vv2[c], aa, bb);
         if (!ROLLBACK && t >= np) {
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                const float ot = xv_gdn_dot<R>(s[c], qc);
+                const float ot = xv_gdn_dot<R>(s[c], qq);
                 if (ig == 0) {
                     const size_t oi = (((size_t)b * T + (t - np)) * Hv + h) * dv + j0 + jw + XV_GDN_JW * c;
                     A.o[oi] = xv_f32_to_bf16(ot);
@@ -290,7 +279,15 @@ __device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, in
                 }
             }
         }
-        if (t + 1 < n) take();
+    };
+    if (n > 0) fetch(0, k0, q0, v0, a0, b0);
+    for (int t = 0; t < n; t += 2) {            // uniform
+        if (t + 1 < n) fetch(t + 1, k1, q1, v1, a1, b1);
+        step(t, k0, q0, v0, a0, b0);
+        if (t + 1 < n) {
+            if (t + 2 < n) fetch(t + 2, k0, q0, v0, a0, b0);
+            step(t + 1, k1, q1, v1, a1, b1);
+        }
     }
     if (!ROLLBACK && A.S_mid && n == np) store_state(A.S_mid);      // no rows of this call
     store_state(A.S_out);
@@ -419,8 +416,10 @@ __device__ __forceinline__ void xv_gdn_prefill_body(const XvGdnArgs A, int bx, i
 #pragma unroll
     for (int r = 0; r < R; ++r) s[r] = sm.sst[(ig * R + r) * SP + jw];
 
-    float kc[R], qc[R], kn[R], qn[R];
-    float vj = 0.f, at = 0.f, bt = 0.f, vn = 0.f, an = 0.f, bn = 0.f;
+    // two register sets, used alternately: token t's rows are in one while token t+1's are
+    // read from LDS into the other (no copies between them)
+    float k0[R], q0[R], k1[R], q1[R];
+    float v0 = 0.f, a0 = 0.f, b0 = 0.f, v1 = 0.f, a1 = 0.f, b1 = 0.f;
     for (int blk = 0; blk < nb; ++blk) {
         const int buf = blk & 1;
         const int t0 = blk * PB;
@@ -428,35 +427,36 @@ __device__ __forceinline__ void xv_gdn_prefill_body(const XvGdnArgs A, int bx, i
         const int t1 = t0 + PB;
         const int n1 = T - t1 < PB ? T - t1 : PB;
         if (blk + 1 < nb) fetch_block(t1, n1);   // uniform: the next block's loads in flight
-        auto fetch = [&](int t) {
+        auto fetch = [&](int t, float (&kk)[R], float (&qq)[R], float& vv2, float& aa, float& bb) {
 #pragma unroll
             for (int c = 0; c < R / 4; ++c) {
                 const xv_f32x4 k4 = *reinterpret_cast<const xv_f32x4*>(&sm.skq[buf][t][0][ig * R + c * 4]);
                 const xv_f32x4 q4 = *reinterpret_cast<const xv_f32x4*>(&sm.skq[buf][t][1][ig * R + c * 4]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) { kn[c * 4 + e] = k4[e]; qn[c * 4 + e] = q4[e]; }
+                for (int e = 0; e < 4; ++e) { kk[c * 4 + e] = k4[e]; qq[c * 4 + e] = q4[e]; }
             }
-            vn = xv_bf16_to_f32(sm.sv[buf][t][jw]);
-            an = sm.sab[buf][t][0];
-            bn = sm.sab[buf][t][1];
+            vv2 = xv_bf16_to_f32(sm.sv[buf][t][jw]);
+            aa = sm.sab[buf][t][0];
+            bb = sm.sab[buf][t][1];
         };
-        auto take = [&]() {
-#pragma unroll
-            for (int r = 0; r < R; ++r) { kc[r] = kn[r]; qc[r] = qn[r]; }
-            vj = vn; at = an; bt = bn;
-        };
-        fetch(0);
-        take();
-        for (int t = 0; t < n; ++t) {
-            if (t + 1 < n) fetch(t + 1);
-            xv_gdn_token<R>(s, kc, vj, at, bt);
-            const float ot = xv_gdn_dot<R>(s, qc);
+        auto out = [&](int t, const float (&qq)[R]) {
+            const float ot = xv_gdn_dot<R>(s, qq);
             if (ig == 0) {
                 const size_t oi = (((size_t)b * T + t0 + t) * Hv + h) * dv + j0 + jw;
                 A.o[oi] = xv_f32_to_bf16(ot);
                 if (A.o32) A.o32[oi] = ot;
             }
-            if (t + 1 < n) take();
+        };
+        fetch(0, k0, q0, v0, a0, b0);
+        for (int t = 0; t < n; t += 2) {        // uniform
+            if (t + 1 < n) fetch(t + 1, k1, q1, v1, a1, b1);
+            xv_gdn_token<R>(s, k0, v0, a0, b0);
+            out(t, q0);
+            if (t + 1 < n) {
+                if (t + 2 < n) fetch(t + 2, k0, q0, v0, a0, b0);
+                xv_gdn_token<R>(s, k1, v1, a1, b1);
+                out(t + 1, q1);
+            }
         }
         if (blk + 1 < nb) stage_block(buf ^ 1, n1);   // the other buffer: last read a block ago
         __syncthreads();
