@@ -209,7 +209,7 @@ def extra_workload(name, stream, steps, warmup, R):
     return res
 
 
-def prefill_workload(stream, P=8192, check=256, reps=2):
+def prefill_workload(stream, P=8192, check=256, reps=2, chunk=8192):
     """Prefill of a P-token prompt (one chunk of 8192) on the synthetic layer, short workload
     shapes, appended to its 640 cached tokens: embedding, both projections and the split over
     all rows, GDN and attention over all rows (decode arithmetic per row), the head and the
@@ -243,12 +243,12 @@ def prefill_workload(stream, P=8192, check=256, reps=2):
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            dec.prefill(prompt)
+            dec.prefill(prompt, chunk=chunk)
             e1.record(stream)
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1)
             best = ms if best is None or ms < best else best
-    res = {"prompt_tokens": P, "ctx_before": int(inp.L0[0]), "batch": wl.B, "chunk": 8192,
+    res = {"prompt_tokens": P, "ctx_before": int(inp.L0[0]), "batch": wl.B, "chunk": chunk,
            "bit_exact_prefill_equals_decode": bool(exact), "check_tokens": check,
            "tok_s": round(wl.B * P / (best * 1e-3), 1) if exact else None, "ms": round(best, 3),
            "note": "one layer; every prompt row kept; first token formed"}
@@ -408,6 +408,10 @@ def main():
             extras["prefill"] = prefill_workload(stream)
         except Exception as exc:
             extras["prefill"] = {"error": "%s: %s" % (type(exc).__name__, exc)}
+        try:                                      # the pages' 128k prompt, one layer
+            extras["prefill_128k"] = prefill_workload(stream, P=127735, reps=1)
+        except Exception as exc:
+            extras["prefill_128k"] = {"error": "%s: %s" % (type(exc).__name__, exc)}
         try:
             from bit_exact_speculative_amd.diagnose import divergence_margins
             with torch.cuda.stream(stream):
