@@ -1338,7 +1338,7 @@ void xv_attn_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     const int pcq = pair_ok ? pair : 0;
     const uint16_t* qp = q + (((size_t)b * P + pcq / Hg) * Hq + g * Hg + pcq % Hg) * D + lg * 8;
 
-    constexpr int KB = KG < 4 ? KG : 4;         // K granules per thread in flight
+    constexpr int KB = KG < 8 ? KG : 8;         // K granules per thread in flight
     auto k_to_lds = [&](int c0) {
 #pragma unroll 1
         for (int i0 = 0; i0 < KG; i0 += KB) {
@@ -1402,20 +1402,65 @@ void xv_attn_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             for (int i = 0; i < 4; ++i) sc[cb][i] = sc[cb][i] * scale_log2;
     };
 
-    // ---- pass 1: each pair's maximum over its visible positions ----
+    // ---- pass 1: each pair's maximum over its visible positions.  K streams in 64-position
+    // sub-blocks through one LDS buffer, the next two sub-blocks in flight in registers; the
+    // scores are the same MFMA chains as in pass 2, four score blocks at a time ----
+    constexpr int SB = 64;                      // positions per sub-block
+    constexpr int NSB = C / SB;
+    constexpr int SKG = SB * (D / 8) / NT;      // K granules per thread per sub-block
+    static_assert(SB * (D / 8) % NT == 0, "sub-blocks must split evenly");
     float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) {
-        const int c0 = c * C;
-        __syncthreads();                        // LDS free
-        k_to_lds(c0);
-        __syncthreads();
-        if (c < tnc) {                          // uniform per wave
-            scores();
+    {
+        xv_u32x4 qf[KS];
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = pair_ok ? xv_load16(qp + ks * 32) : zero;
+        const int nsb = nc * NSB;
+        auto kload = [&](xv_u32x4 (&kr)[SKG], int u) {
+            u = u < nsb ? u : nsb - 1;          // past the end: a re-read, never used
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (c0 + cb * 16 + 4 * lg + i < plen) M = fmaxf(M, sc[cb][i]);
+            for (int i = 0; i < SKG; ++i) {
+                const int idx = tid + i * NT;
+                const int pos = u * SB + idx / (D / 8);
+                kr[i] = xv_load16(k_cache + (kvbase + (pos < Lend ? pos : 0)) * D + (idx % (D / 8)) * 8);
+                if (pos >= Lend) kr[i] = zero;
+            }
+        };
+        auto kstore = [&](const xv_u32x4 (&kr)[SKG]) {
+#pragma unroll
+            for (int i = 0; i < SKG; ++i) {
+                const int idx = tid + i * NT;
+                *reinterpret_cast<xv_u32x4*>(lds + (idx / (D / 8)) * KP + (idx % (D / 8)) * 16) = kr[i];
+            }
+        };
+        xv_u32x4 kr0[SKG], kr1[SKG];
+        kload(kr0, 0);
+        kload(kr1, 1);
+        for (int u = 0; u < nsb; u += 2) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                xv_u32x4 (&kr)[SKG] = h ? kr1 : kr0;
+                const int uu = u + h;
+                __syncthreads();                // the buffer is free
+                kstore(kr);
+                kload(kr, uu + 2);
+                __syncthreads();
+                if (uu < nsb && uu / NSB < tnc) {   // uniform per wave
+                    xv_f32x4 s4[SB / 16];
+#pragma unroll
+                    for (int j = 0; j < SB / 16; ++j) s4[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                        for (int j = 0; j < SB / 16; ++j)
+                            s4[j] = xv_mfma16x16x32(*reinterpret_cast<const xv_u32x4*>(lds + (j * 16 + lr) * KP + ks * 64 + lg * 16),
+                                                    qf[ks], s4[j]);
+#pragma unroll
+                    for (int j = 0; j < SB / 16; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (uu * SB + j * 16 + 4 * lg + i < plen) M = fmaxf(M, s4[j][i] * scale_log2);
+                }
+            }
         }
     }
     M = fmaxf(M, __shfl_xor(M, 16));
