@@ -868,20 +868,17 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
     float L = 0.f, A = 0.f;
 
     if constexpr (!DEEP) {
-        float mloc = -INFINITY;
-        for (int cc = tid; cc < nc; cc += D) mloc = fmaxf(mloc, ws_ml[(base + cc) * 2]);
-        const float M = xv_combine_max<D>(mloc, sred, tid);
-        for (int cc = tid; cc < nc; cc += D) {
-            const float be = __builtin_amdgcn_exp2f(ws_ml[(base + cc) * 2] - M);
-            sbeta[cc] = be;
-            slw[cc] = ws_ml[(base + cc) * 2 + 1] * be;
-        }
-        __syncthreads();
+        // few chunks: every thread reads all (m, l) itself (the same addresses across the
+        // workgroup) and forms the same maximum and weights, so no LDS and no barrier
+        float M = -INFINITY;
+        for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, ws_ml[(base + cc) * 2]);
 #pragma unroll 8
         for (int cc = 0; cc < nc; ++cc) {
-            L = L + slw[cc];
-            A = __builtin_fmaf(ap[(size_t)cc * D], sbeta[cc], A);
+            const float be = __builtin_amdgcn_exp2f(ws_ml[(base + cc) * 2] - M);
+            L = L + ws_ml[(base + cc) * 2 + 1] * be;
+            A = __builtin_fmaf(ap[(size_t)cc * D], be, A);
         }
+        (void)sbeta; (void)slw; (void)sred;
     } else {
         constexpr int U = XV_COMBINE_U;
         // indices past nc re-read chunk nc - 1 and are not summed
@@ -1034,8 +1031,7 @@ int xv_attn_combine(const float* ws_acc, const float* ws_ml, const int32_t* kv_l
         hipLaunchKernelGGL((xv_attn_combine_kernel<D, true>), dim3(Hq, T, B), dim3(D), shmem, st,
                            ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC);
     } else {
-        const size_t shmem = sizeof(float) * (2 * (size_t)NC + D);
-        hipLaunchKernelGGL((xv_attn_combine_kernel<D, false>), dim3(Hq, T, B), dim3(D), shmem, st,
+        hipLaunchKernelGGL((xv_attn_combine_kernel<D, false>), dim3(Hq, T, B), dim3(D), 0, st,
                            ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC);
     }
     return xv_launch_status();
