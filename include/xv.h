@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define XV_ABI_VERSION 3
+#define XV_ABI_VERSION 4
 
 typedef enum {
     XV_OK = 0,
