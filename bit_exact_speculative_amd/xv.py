@@ -33,6 +33,11 @@ _lib.xv_abi_version.restype = _I
 _lib.xv_abi_version.argtypes = []
 _lib.xv_status_string.restype = ctypes.c_char_p
 _lib.xv_status_string.argtypes = [_I]
+# the argument lists below are those of this ABI version of include/xv.h
+ABI_VERSION = 4
+if _lib.xv_abi_version() != ABI_VERSION:
+    raise ImportError("libxv.so has ABI version %d, this binding expects %d; rebuild it"
+                      % (_lib.xv_abi_version(), ABI_VERSION))
 _lib.xv_gemm_small_m.restype = _I
 _lib.xv_gemm_small_m.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P]
 _lib.xv_gemm_small_m_timed.restype = _I
