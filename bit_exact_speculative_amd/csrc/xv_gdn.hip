@@ -34,8 +34,11 @@
 
 namespace {
 
+// Six waves per SIMD (at most 80 VGPRs; two 8-byte addresses go to scratch outside the token
+// loop): three workgroups share a CU, which their LDS (51 KB each at dk = 128) also allows,
+// so a batch of 8 (1536 workgroups) runs in two rounds instead of three.
 template <int DK, bool ROLLBACK, int CPT>
-__global__ __launch_bounds__(XV_GDN_THREADS)
+__global__ __launch_bounds__(XV_GDN_THREADS, 6)
 void xv_gdn_kernel(XvGdnArgs A)
 {
     __shared__ __attribute__((aligned(16))) XvGdnSmem<DK, CPT> sm;

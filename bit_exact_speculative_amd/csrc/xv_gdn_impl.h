@@ -280,12 +280,14 @@ __device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, in
             }
         }
     };
+    // The next row's LDS reads are issued on every path (row n - 1 again past the end, never
+    // used), so the wait before a token's update covers only the reads of that token's rows.
     if (n > 0) fetch(0, k0, q0, v0, a0, b0);
     for (int t = 0; t < n; t += 2) {            // uniform
-        if (t + 1 < n) fetch(t + 1, k1, q1, v1, a1, b1);
+        fetch(t + 1 < n ? t + 1 : n - 1, k1, q1, v1, a1, b1);
         step(t, k0, q0, v0, a0, b0);
         if (t + 1 < n) {
-            if (t + 2 < n) fetch(t + 2, k0, q0, v0, a0, b0);
+            fetch(t + 2 < n ? t + 2 : n - 1, k0, q0, v0, a0, b0);
             step(t + 1, k1, q1, v1, a1, b1);
         }
     }
@@ -448,12 +450,12 @@ __device__ __forceinline__ void xv_gdn_prefill_body(const XvGdnArgs A, int bx, i
             }
         };
         fetch(0, k0, q0, v0, a0, b0);
-        for (int t = 0; t < n; t += 2) {        // uniform
-            if (t + 1 < n) fetch(t + 1, k1, q1, v1, a1, b1);
+        for (int t = 0; t < n; t += 2) {        // uniform; reads on every path, as in verify
+            fetch(t + 1 < n ? t + 1 : n - 1, k1, q1, v1, a1, b1);
             xv_gdn_token<R>(s, k0, v0, a0, b0);
             out(t, q0);
             if (t + 1 < n) {
-                if (t + 2 < n) fetch(t + 2, k0, q0, v0, a0, b0);
+                fetch(t + 2 < n ? t + 2 : n - 1, k0, q0, v0, a0, b0);
                 xv_gdn_token<R>(s, k1, v1, a1, b1);
                 out(t + 1, q1);
             }
