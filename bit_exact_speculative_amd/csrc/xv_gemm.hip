@@ -155,6 +155,19 @@ struct XvGemmPair {
     int N[2];
 };
 
+// LDS row pitch (bf16 elements) for rows of n bf16 values that 16 lanes read as MFMA
+// fragments (lane lr: row lr, lane quarter lg: granule lg): the smallest pitch >= n of
+// 4k + 2 16-byte granules.  The bank-conflict counter on gfx950 fits 16-byte accesses served
+// for two lane octets at a time (0-7 with 16-23, 8-15 with 24-31, ...); such a pitch puts
+// rows 0..7 at granules lg and lg + 1 on sixteen distinct 16-byte bank groups (measured: 128-
+// and 144-byte rows conflict, 160-byte rows do not).
+constexpr int xv_frag_pitch(int n) {
+    const int g = (n + 7) / 8;
+    return (g + (6 - g % 4) % 4) * 8;
+}
+static_assert(xv_frag_pitch(64) == 80 && xv_frag_pitch(320) == 336 && xv_frag_pitch(160) == 176 &&
+              xv_frag_pitch(80) == 80, "pitch rule");
+
 // W staged through LDS: the workgroup streams each column block's 16 rows with
 // 1 KB contiguous wave loads (each 16-byte granule of a stage is one thread's
 // load) into a padded LDS stage; each wave then reads the MFMA B fragments of its
@@ -170,7 +183,7 @@ void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0, int contig)
 {
     static_assert(NS % 2 == 0 && SL * NS == XV_GEMM_WAVES * KSW, "stages must split the ranges evenly");
     constexpr int WPS = XV_GEMM_WAVES / NS;         // waves whose ranges a stage holds
-    constexpr int PITCH = SL * 32 + 8;              // LDS row pitch (bf16): rows fall 4 banks apart
+    constexpr int PITCH = xv_frag_pitch(SL * 32);   // LDS row pitch (bf16)
     constexpr int PER_ROW = SL * 4;                 // 16-byte granules per row per stage
     constexpr int TOTAL = 16 * PER_ROW;
     constexpr int GPT = (TOTAL + XV_GEMM_THREADS - 1) / XV_GEMM_THREADS;
@@ -288,7 +301,9 @@ void xv_gemm_kloop_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
     constexpr int NTH = XV_KL_THREADS;
     constexpr int RW = XV_KL_WAVES / NB;        // waves sharing a column block
     constexpr int MTW = (MT + RW - 1) / RW;     // row tiles per wave (the last may be past MT)
-    constexpr int PITCH = KC * 32 + 8;          // LDS row pitch (bf16): rows fall 4 banks apart
+    // LDS row pitch (bf16): rows fall 4 banks apart (the fragment-read pitch would take the
+    // widest instance past half the CU's LDS)
+    constexpr int PITCH = KC * 32 + 8;
     constexpr int WROWS = NB * 16;
     constexpr int XROWS = MT * 16;
     constexpr int GR = KC * 4;                  // 16-byte granules per row per stage
@@ -435,7 +450,8 @@ void xv_gemm_big_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
 {
     constexpr int NTH = XV_BIG_THREADS;
     constexpr int KC = XV_BIG_KC;
-    constexpr int PITCH = KC * 32 + 8;          // LDS row pitch (bf16): 16 rows fall on distinct banks
+    // LDS row pitch (bf16): 160-byte rows; two workgroups' buffers then fill the CU's 160 KB
+    constexpr int PITCH = xv_frag_pitch(KC * 32);
     constexpr int GR = KC * 4;                  // 16-byte granules per row per stage
     constexpr int XG = XV_BIG_BM * GR / NTH;    // x granules per thread per stage
     constexpr int WG = XV_BIG_BN * GR / NTH;
@@ -561,7 +577,7 @@ void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
     constexpr int NT = XV_GEMM_THREADS;
     constexpr int XR = MT * 16, WR = NBW * 16;  // rows of a part: x, W
     constexpr int GR = KSP * 4;                 // 16-byte granules per row of a part
-    constexpr int PITCH = KSP * 32 + 8;         // LDS row pitch (bf16): 16 rows fall on distinct banks
+    constexpr int PITCH = xv_frag_pitch(KSP * 32);  // LDS row pitch (bf16)
     constexpr int GPT = ((XR + WR) * GR + NT - 1) / NT;
     constexpr int NTILE = MT * NBW;
     constexpr int PPW = (NTILE + XV_GEMM_WAVES - 1) / XV_GEMM_WAVES;
