@@ -973,15 +973,30 @@ XvAttnKind xv_attn_kind(int B, int T, int Hq, int Hkv, int NC) {
     return XV_ATTN_TILE;
 }
 
-constexpr int xv_attn_ds(int D) { return D == 256 ? 2 : 1; }   // value-dim parts per tile
+// workgroups of the tile split: (request, KV head, chunk, 16-pair tile, value-dim part)
+inline long long xv_tile_items(int B, int T, int Hq, int Hkv, int NC, int ds) {
+    const long long ntile = ((long long)(Hq / Hkv) * T + 15) / 16;
+    return (long long)B * Hkv * NC * ntile * ds;
+}
 
-inline XvTileArgs xv_tile_args(int D, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+// Value-dim parts per tile workgroup: at d = 256 two (each workgroup forms half of the
+// output dims, so a chunk's work spreads over twice the CUs) when that grid, padded to the
+// XCD round robin, leaves `room` CUs of the chip; otherwise one, which halves the grid
+// (the work of a chunk on one CU instead of a second round of workgroups).  Both give the
+// same bits.
+inline int xv_attn_tile_ds(int D, int B, int T, int Hq, int Hkv, int NC, long long room) {
+    if (D != 256) return 1;
+    const long long n2 = 8 * ((xv_tile_items(B, T, Hq, Hkv, NC, 2) + 7) / 8);
+    return n2 <= room ? 2 : 1;
+}
+
+inline XvTileArgs xv_tile_args(int ds, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                                uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                                float* ws_acc, float* ws_ml, int B, int T, int Hq, int Hkv, int Lmax, int NC,
                                float scale_log2) {
     const int P = (Hq / Hkv) * T;
     const int ntile = (P + 15) / 16;
-    const int items = B * Hkv * NC * ntile * xv_attn_ds(D);
+    const int items = (int)xv_tile_items(B, T, Hq, Hkv, NC, ds);
     const int per_xcd = (items + 7) / 8;
     return XvTileArgs{q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
                       T, Hq, Hkv, Lmax, NC, ntile, items, per_xcd, scale_log2};
@@ -1012,11 +1027,15 @@ int xv_attn_partials(const uint16_t* q, const uint16_t* k_new, const uint16_t* v
                            q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
                            T, Hq, Hkv, Lmax, NC, scale_log2);
     } else {
-        constexpr int DS = xv_attn_ds(D);
-        const XvTileArgs ta = xv_tile_args(D, q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
+        const int ds = xv_attn_tile_ds(D, B, T, Hq, Hkv, NC, xv_cu_count());
+        const XvTileArgs ta = xv_tile_args(ds, q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
                                            B, T, Hq, Hkv, Lmax, NC, scale_log2);
-        hipLaunchKernelGGL((xv_attn_partial_tile_kernel<D, DS>), dim3(8 * ta.per_xcd), dim3(XV_ATTN_WAVES * 64),
-                           0, st, ta);
+        if (D == 256 && ds == 2)
+            hipLaunchKernelGGL((xv_attn_partial_tile_kernel<D, (D == 256 ? 2 : 1)>), dim3(8 * ta.per_xcd),
+                               dim3(XV_ATTN_WAVES * 64), 0, st, ta);
+        else
+            hipLaunchKernelGGL((xv_attn_partial_tile_kernel<D, 1>), dim3(8 * ta.per_xcd), dim3(XV_ATTN_WAVES * 64),
+                               0, st, ta);
     }
     return xv_launch_status();
 }
@@ -1061,7 +1080,7 @@ union XvGdnAttnSmem {
     XvTileSmem<D> t;
 };
 
-template <int DK, int CPT, int D>
+template <int DK, int CPT, int D, int DS>
 __global__ __launch_bounds__(XV_ATTN_WAVES * 64)
 void xv_gdn_attn_kernel(XvGdnArgs ga, XvTileArgs ta, int n_attn, int gdn_nx)
 {
@@ -1069,7 +1088,7 @@ void xv_gdn_attn_kernel(XvGdnArgs ga, XvTileArgs ta, int n_attn, int gdn_nx)
     __shared__ __attribute__((aligned(16))) XvGdnAttnSmem<DK, CPT, D> sm;
     const int bid = (int)blockIdx.x;
     if (bid < n_attn) {                          // uniform over the workgroup
-        xv_attn_tile_body<D, xv_attn_ds(D)>(ta, bid, sm.t);
+        xv_attn_tile_body<D, DS>(ta, bid, sm.t);
         return;
     }
     const int i = bid - n_attn;
@@ -1126,17 +1145,24 @@ int xv_attn_check(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
     return XV_OK;
 }
 
-template <int D>
-int xv_gdn_attn_fused(const XvGdnArgs& ga, int dk, int cpt, const XvTileArgs& ta, int B, hipStream_t st)
+template <int D, int DS>
+void xv_gdn_attn_fused_ds(const XvGdnArgs& ga, int dk, int cpt, const XvTileArgs& ta, int B, hipStream_t st)
 {
     const int gdn_nx = ga.dv / (XV_GDN_JW * cpt);
     const int n_attn = 8 * ta.per_xcd;
     const dim3 grid(n_attn + gdn_nx * ga.Hv * B), block(XV_ATTN_WAVES * 64);
+    if (dk == 128 && cpt == 2) hipLaunchKernelGGL((xv_gdn_attn_kernel<128, 2, D, DS>), grid, block, 0, st, ga, ta, n_attn, gdn_nx);
+    else if (dk == 128) hipLaunchKernelGGL((xv_gdn_attn_kernel<128, 1, D, DS>), grid, block, 0, st, ga, ta, n_attn, gdn_nx);
+    else if (cpt == 2) hipLaunchKernelGGL((xv_gdn_attn_kernel<64, 2, D, DS>), grid, block, 0, st, ga, ta, n_attn, gdn_nx);
+    else hipLaunchKernelGGL((xv_gdn_attn_kernel<64, 1, D, DS>), grid, block, 0, st, ga, ta, n_attn, gdn_nx);
+}
+
+template <int D>
+int xv_gdn_attn_fused(const XvGdnArgs& ga, int dk, int cpt, int ds, const XvTileArgs& ta, int B, hipStream_t st)
+{
     (void)hipGetLastError();
-    if (dk == 128 && cpt == 2) hipLaunchKernelGGL((xv_gdn_attn_kernel<128, 2, D>), grid, block, 0, st, ga, ta, n_attn, gdn_nx);
-    else if (dk == 128) hipLaunchKernelGGL((xv_gdn_attn_kernel<128, 1, D>), grid, block, 0, st, ga, ta, n_attn, gdn_nx);
-    else if (cpt == 2) hipLaunchKernelGGL((xv_gdn_attn_kernel<64, 2, D>), grid, block, 0, st, ga, ta, n_attn, gdn_nx);
-    else hipLaunchKernelGGL((xv_gdn_attn_kernel<64, 1, D>), grid, block, 0, st, ga, ta, n_attn, gdn_nx);
+    if (D == 256 && ds == 2) xv_gdn_attn_fused_ds<D, (D == 256 ? 2 : 1)>(ga, dk, cpt, ta, B, st);
+    else xv_gdn_attn_fused_ds<D, 1>(ga, dk, cpt, ta, B, st);
     return xv_launch_status();
 }
 
@@ -1196,7 +1222,7 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
     // resident at once (about: workgroups of chunks past every row exit at once);
     // the GDN workgroups then take one column group each if that fits, else two
     bool fuse = false;
-    int cpt = 1;
+    int cpt = 1, ds = 1;
     XvTileArgs ta{};
     switch (d) {
         case 64:  fuse = xv_attn_kind<64>(B, T, Hq, Hkv, NC) == XV_ATTN_TILE; break;
@@ -1204,13 +1230,20 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
         default:  fuse = xv_attn_kind<256>(B, T, Hq, Hkv, NC) == XV_ATTN_TILE; break;
     }
     if (fuse) {
-        ta = xv_tile_args(d, q_attn, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml, B, T, Hq, Hkv,
-                          Lmax, NC, xv_scale_log2(scale));
-        const long long n_attn = 8LL * ta.per_xcd, cus = xv_cu_count();
+        // the GDN workgroups take one column group each if everything fits, else two; the
+        // tile grid takes two value-dim parts if that still fits beside them, else one
+        const long long cus = xv_cu_count();
         const long long gdn1 = (long long)(dv / XV_GDN_JW) * Hv * B;
-        if (n_attn + gdn1 <= XV_FUSE_ONE_COL * cus) cpt = 1;
-        else if (dv % (2 * XV_GDN_JW) == 0 && n_attn + gdn1 / 2 <= XV_FUSE_TWO_COL * cus) cpt = 2;
-        else fuse = false;
+        const bool two_col = dv % (2 * XV_GDN_JW) == 0;
+        fuse = false;
+        for (int dsv = (d == 256 ? 2 : 1); dsv >= 1 && !fuse; --dsv) {
+            const long long n_attn = 8 * ((xv_tile_items(B, T, Hq, Hkv, NC, dsv) + 7) / 8);
+            if (n_attn + gdn1 <= XV_FUSE_ONE_COL * cus) { fuse = true; cpt = 1; ds = dsv; }
+            else if (two_col && n_attn + gdn1 / 2 <= XV_FUSE_TWO_COL * cus) { fuse = true; cpt = 2; ds = dsv; }
+        }
+        if (fuse)
+            ta = xv_tile_args(ds, q_attn, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml, B, T, Hq, Hkv,
+                              Lmax, NC, xv_scale_log2(scale));
     }
     if (!fuse) {
         s = n_keep_prev
@@ -1222,9 +1255,9 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
                                    workspace_bytes, B, T, Hq, Hkv, d, Lmax, scale, stream);
     }
     switch (d) {
-        case 64:  s = xv_gdn_attn_fused<64>(ga, dk, cpt, ta, B, st); break;
-        case 128: s = xv_gdn_attn_fused<128>(ga, dk, cpt, ta, B, st); break;
-        default:  s = xv_gdn_attn_fused<256>(ga, dk, cpt, ta, B, st); break;
+        case 64:  s = xv_gdn_attn_fused<64>(ga, dk, cpt, ds, ta, B, st); break;
+        case 128: s = xv_gdn_attn_fused<128>(ga, dk, cpt, ds, ta, B, st); break;
+        default:  s = xv_gdn_attn_fused<256>(ga, dk, cpt, ds, ta, B, st); break;
     }
     if (s != XV_OK) return s;
     switch (d) {

@@ -158,6 +158,20 @@ def test_attn_wide_and_tile_kernels_agree(case, grid):
     assert same_bits(kc, kc2[:, :, :Lmax]) and same_bits(vc, vc2[:, :, :Lmax])
 
 
+def test_attn_tile_value_dim_parts_agree():
+    """At d = 256 a tile workgroup forms half of a chunk's output dims while that grid fits
+    the chip, all of them beyond (capacity 2304: 9 chunks x 4 KV heads x 4 tiles x 2 halves =
+    288 workgroups, more than 256 CUs): the same bits either way."""
+    B, T, Hq, Hkv, d, L0 = 1, 9, 24, 4, 256, [640]
+    Lmax = max(L0) + T
+    D = Dev(*_case(321, B, T, Hq, Hkv, d, L0, Lmax))
+    o, o32, kc, vc = _verify(D)
+    o2, o322, kc2, vc2 = _verify(D, Lmax_extra=2304 - Lmax)
+    torch.cuda.synchronize()
+    assert same_bits(o32, o322) and same_bits(o, o2)
+    assert same_bits(kc, kc2[:, :, :Lmax]) and same_bits(vc, vc2[:, :, :Lmax])
+
+
 def test_attn_batch_invariance():
     D = Dev(*_case(88, 8, 9, 24, 4, 256, [560, 740, 600, 611, 699, 573, 720, 640], 749))
     o, o32, kc, vc = _verify(D)

@@ -51,7 +51,7 @@ def _outs(B, T, Hv, dv, Hq, d, dk, Lmax):
                 kept=f(B, Hv, dk, dv), out=f(B, Hv, dk, dv), ws=f((nb + 15) // 16 * 4))
 
 
-# (B, T, Hk, Hv, dk, dv, Hq, Hkv, d, L0, Lmax, Tp).  The first three fit one launch:
+# (B, T, Hk, Hv, dk, dv, Hq, Hkv, d, L0, Lmax, Tp).  The first three and the last fit one launch:
 # 8 * ceil(items / 8) tile workgroups (items = B Hkv ceil(Lmax/256) ceil(Hq/Hkv T/16) DS)
 # plus B Hv dv / 64 (or / 32) GDN workgroups at most 256; e.g. 160 + 96 for the first.
 CASES = [
@@ -59,10 +59,12 @@ CASES = [
     (2, 5, 2, 4, 64, 64, 8, 2, 128, [300, 17], 600, 3),
     (1, 3, 1, 2, 128, 96, 4, 1, 64, [40], 100, 16),
     (8, 9, 16, 48, 128, 128, 24, 4, 256, [640, 1, 300, 255, 256, 257, 512, 700], 1024, 9),   # two launches
+    # 10 chunks: 320 tile workgroups of halves would not fit beside GDN, 160 of whole chunks do
+    (1, 9, 16, 48, 128, 128, 24, 4, 256, [2183], 2471, 9),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=["short", "small", "dv96", "batch8"])
+@pytest.mark.parametrize("case", CASES, ids=["short", "small", "dv96", "batch8", "medium"])
 @pytest.mark.parametrize("after", [False, True])
 def test_gdn_attn_equals_the_two_calls(case, after):
     B, T, Hk, Hv, dk, dv, Hq, Hkv, d, L0, Lmax, Tp = case
