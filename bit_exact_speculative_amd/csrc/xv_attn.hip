@@ -49,6 +49,7 @@ constexpr int XV_ATTN_MAX_NC = 8192;
 constexpr int XV_ATTN_WIDE_MIN = 128; // (chunk, KV head, request) workgroups from which the wide kernel runs
 constexpr int XV_ATTN_STREAM_MIN = 1024; // ... and from which the persistent streaming kernel runs (about 4 chunks per CU)
 constexpr int XV_COMBINE_U = 24;    // chunks per block of combine loads kept in flight
+constexpr int XV_COMBINE_PRE = 8;   // chunks a short row's combine loads before its maximum
 // GDN + attention in one launch while their workgroups are at most these multiples
 // of the CU count (GDN with one, or else two, column groups per workgroup)
 constexpr double XV_FUSE_ONE_COL = 1.0;
@@ -869,11 +870,33 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
 
     if constexpr (!DEEP) {
         // few chunks: every thread reads all (m, l) itself (the same addresses across the
-        // workgroup) and forms the same maximum and weights, so no LDS and no barrier
+        // workgroup) and forms the same maximum and weights, so no LDS and no barrier.  The
+        // first XV_COMBINE_PRE chunks' values and (m, l) are loaded together, before the
+        // maximum is formed (one round trip for short rows; indices past nc re-read chunk
+        // nc - 1 and are not used)
+        constexpr int PRE = XV_COMBINE_PRE;
+        float pacc[PRE];
+        float2 pml[PRE];
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) {
+            const int cc = u < nc ? u : nc - 1;
+            pacc[u] = ap[(size_t)cc * D];
+            pml[u] = *reinterpret_cast<const float2*>(ws_ml + (base + cc) * 2);
+        }
         float M = -INFINITY;
-        for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, ws_ml[(base + cc) * 2]);
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) M = u < nc ? fmaxf(M, pml[u].x) : M;
+        for (int cc = PRE; cc < nc; ++cc) M = fmaxf(M, ws_ml[(base + cc) * 2]);
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) {
+            if (u < nc) {
+                const float be = __builtin_amdgcn_exp2f(pml[u].x - M);
+                L = L + pml[u].y * be;
+                A = __builtin_fmaf(pacc[u], be, A);
+            }
+        }
 #pragma unroll 8
-        for (int cc = 0; cc < nc; ++cc) {
+        for (int cc = PRE; cc < nc; ++cc) {
             const float be = __builtin_amdgcn_exp2f(ws_ml[(base + cc) * 2] - M);
             L = L + ws_ml[(base + cc) * 2 + 1] * be;
             A = __builtin_fmaf(ap[(size_t)cc * D], be, A);
