@@ -331,7 +331,8 @@ def composed_workload(stream, n_tokens=48, k=8, p_wrong=0.2, reps=3):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU; --gpus %d is not supported (use --gpus 1)" % args.gpus,
+        print("bench.py: the benchmark runs on one GPU (requests would shard across GPUs with no exchange); "
+              "--gpus %d is not supported (use --gpus 1)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
