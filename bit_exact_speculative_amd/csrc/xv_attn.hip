@@ -30,11 +30,13 @@
 //     and xv_attn_partial_stream_kernel (persistent workgroups streaming the
 //     chunks of one KV head and request, for long contexts); the host picks by
 //     grid size only, so a pair's bits never depend on it.
-//  2. xv_attn_combine_kernel, grid (query head, row, request): with
-//     M = max_c m_c, beta_c = 2^(m_c - M), L = sum_c l_c beta_c and
-//     A = sum_c acc_c beta_c in ascending chunk order; o = A / L, stored as
-//     bf16 (nearest even) and optionally fp32.  Its two load schedules (by the
-//     capacity's chunk count) fold the same operations in the same order.
+//  2. xv_attn_combine_kernel, grid (query head, row, request): in ascending
+//     chunk order with the running maximum M (-inf at first), M' = max(M, m_c),
+//     a = 2^(M - M'), b = 2^(m_c - M'), L = fma(L, a, l_c b),
+//     A = fma(A, a, acc_c b); o = A / L, stored as bf16 (nearest even) and
+//     optionally fp32.  Its two load schedules (by the capacity's chunk count)
+//     fold the same operations in the same order, and the prefill kernel folds
+//     its chunks with them too.
 // Masked positions are excluded by index, never by value, and positions at or
 // past L0 + T are never read (their LDS slots are zero-filled).
 #include "xv_common.h"
@@ -45,7 +47,7 @@ namespace {
 
 constexpr int XV_ATTN_C = 256;      // chunk length (positions), fixed for every call
 constexpr int XV_ATTN_WAVES = 8;    // waves of a partial-kernel workgroup
-constexpr int XV_ATTN_MAX_NC = 8192;
+constexpr int XV_ATTN_MAX_NC = 5120;   // chunks of the capacity (1,310,720 positions), at most
 constexpr int XV_ATTN_WIDE_MIN = 128; // (chunk, KV head, request) workgroups from which the wide kernel runs
 constexpr int XV_ATTN_STREAM_MIN = 1024; // ... and from which the persistent streaming kernel runs (about 4 chunks per CU)
 constexpr int XV_COMBINE_U = 24;    // chunks per block of combine loads kept in flight
@@ -56,6 +58,9 @@ constexpr double XV_FUSE_ONE_COL = 1.0;
 constexpr double XV_FUSE_TWO_COL = 1.0;
 // the combine's per-chunk LDS arrays are padded to whole pairs of load blocks
 __host__ __device__ constexpr int xv_combine_pad(int nc) { return (nc + 2 * XV_COMBINE_U - 1) / (2 * XV_COMBINE_U) * (2 * XV_COMBINE_U); }
+// the long-row combine's LDS (three per-chunk arrays and a scan array of 256) stays within
+// the 64 KB of dynamic LDS a launch gets without an attribute
+static_assert(sizeof(float) * (3 * xv_combine_pad(XV_ATTN_MAX_NC) + 256) <= 65536, "combine LDS");
 
 // LDS layouts (16-byte granules, XOR-swizzled so that both the cooperative
 // stores and the MFMA fragment reads spread over the banks):
@@ -826,38 +831,38 @@ void xv_attn_partial_tile_kernel(XvTileArgs A)
     xv_attn_tile_body<D, DS>(A, (int)blockIdx.x, sm);
 }
 
-// the workgroup's maximum of mloc (exact in any order)
-template <int D>
-__device__ __forceinline__ float xv_combine_max(float mloc, float* sred, int tid) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
-    if ((tid & 63) == 0) sred[tid >> 6] = mloc;
-    __syncthreads();
-    if (tid == 0) {
-        float mm = sred[0];
-        for (int i = 1; i < D / 64; ++i) mm = fmaxf(mm, sred[i]);
-        sred[0] = mm;
-    }
-    __syncthreads();
-    return sred[0];
+// The fold of a row's chunk partials, in ascending chunk order, with the running
+// maximum M (-inf before the first chunk):
+//     M' = max(M, m_c),  a_c = 2^(M - M'),  b_c = 2^(m_c - M')
+//     L  = fma(L, a_c, l_c b_c),  A = fma(A, a_c, acc_c b_c),  M = M'
+// and o = A / L.  The first chunk gives a = 0, b = 1: A = acc_0, L = l_0 exactly.  The
+// prefill kernel folds its chunks with these operations in the same order.
+__device__ __forceinline__ void xv_fold_factors(float& M, float m, float& a, float& b) {
+    const float Mn = fmaxf(M, m);
+    a = __builtin_amdgcn_exp2f(M - Mn);
+    b = __builtin_amdgcn_exp2f(m - Mn);
+    M = Mn;
 }
 
-// DEEP = false: every thread walks its chain loading as it goes (rows of a few
-// chunks).  DEEP = true (long rows): the per-chunk (m, l) are staged in LDS in one
-// pass, and the chain's loads run in two alternating register blocks of
-// XV_COMBINE_U chunks, one block in flight while the other is summed.  Both fold
-// the same operations in the same order.
+// DEEP = false: every thread walks the chain itself, forming the same factors from the
+// (m, l) it loads (rows of a few chunks; the first XV_COMBINE_PRE chunks' loads are issued
+// together).  DEEP = true (long rows): the factors are formed once per chunk in LDS (the
+// running maximum as a prefix maximum: a per-thread segment, then a scan over the
+// segments; a maximum is exact in any order), and the chain's loads run in two
+// alternating register blocks of XV_COMBINE_U chunks, one block in flight while the
+// other is summed.  Both fold the same operations in the same order.
 template <int D, bool DEEP>
 __global__ __launch_bounds__(D)
 void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
                             const int32_t* __restrict__ kv_len, uint16_t* __restrict__ o,
                             float* __restrict__ o32, int T, int Hq, int Lmax, int NC)
 {
-    extern __shared__ __attribute__((aligned(16))) float sh[];   // [NCP] beta, [NCP] l*beta, [D] max scratch
+    extern __shared__ __attribute__((aligned(16))) float sh[];   // [NCP] a, [NCP] b, [NCP] l b, [D] scan
     const int NCP = DEEP ? xv_combine_pad(NC) : NC;
-    float* sbeta = sh;
-    float* slw = sh + NCP;
-    float* sred = sh + 2 * NCP;
+    float* sa = sh;
+    float* sb = sh + NCP;
+    float* slb = sh + 2 * NCP;
+    float* sred = sh + 3 * NCP;
     const int h = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     int L0 = kv_len[b];
@@ -869,11 +874,7 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
     float L = 0.f, A = 0.f;
 
     if constexpr (!DEEP) {
-        // few chunks: every thread reads all (m, l) itself (the same addresses across the
-        // workgroup) and forms the same maximum and weights, so no LDS and no barrier.  The
-        // first XV_COMBINE_PRE chunks' values and (m, l) are loaded together, before the
-        // maximum is formed (one round trip for short rows; indices past nc re-read chunk
-        // nc - 1 and are not used)
+        // indices past nc re-read chunk nc - 1 and are not used
         constexpr int PRE = XV_COMBINE_PRE;
         float pacc[PRE];
         float2 pml[PRE];
@@ -885,23 +886,23 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
         }
         float M = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < PRE; ++u) M = u < nc ? fmaxf(M, pml[u].x) : M;
-        for (int cc = PRE; cc < nc; ++cc) M = fmaxf(M, ws_ml[(base + cc) * 2]);
-#pragma unroll
         for (int u = 0; u < PRE; ++u) {
             if (u < nc) {
-                const float be = __builtin_amdgcn_exp2f(pml[u].x - M);
-                L = L + pml[u].y * be;
-                A = __builtin_fmaf(pacc[u], be, A);
+                float fa, fb;
+                xv_fold_factors(M, pml[u].x, fa, fb);
+                L = __builtin_fmaf(L, fa, pml[u].y * fb);
+                A = __builtin_fmaf(A, fa, pacc[u] * fb);
             }
         }
-#pragma unroll 8
+#pragma unroll 4
         for (int cc = PRE; cc < nc; ++cc) {
-            const float be = __builtin_amdgcn_exp2f(ws_ml[(base + cc) * 2] - M);
-            L = L + ws_ml[(base + cc) * 2 + 1] * be;
-            A = __builtin_fmaf(ap[(size_t)cc * D], be, A);
+            const float2 ml = *reinterpret_cast<const float2*>(ws_ml + (base + cc) * 2);
+            float fa, fb;
+            xv_fold_factors(M, ml.x, fa, fb);
+            L = __builtin_fmaf(L, fa, ml.y * fb);
+            A = __builtin_fmaf(A, fa, ap[(size_t)cc * D] * fb);
         }
-        (void)sbeta; (void)slw; (void)sred;
+        (void)sa; (void)sb; (void)slb; (void)sred;
     } else {
         constexpr int U = XV_COMBINE_U;
         // indices past nc re-read chunk nc - 1 and are not summed
@@ -912,59 +913,65 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
                 buf[u] = ap[(size_t)(cn < nc ? cn : nc - 1) * D];
             }
         };
-        // beta and l * beta four at a time from LDS (padded to a multiple of 2 U); a
-        // chunk past nc leaves both sums as they are
+        // a, b and l b four at a time from LDS (padded to a multiple of 2 U); a chunk past
+        // nc leaves both sums as they are
         auto fold = [&](const float (&buf)[U], int c0) __attribute__((always_inline)) {
-            float be[U], lw[U];
+            float fa[U], fb[U], lb[U];
 #pragma unroll
             for (int u = 0; u < U; u += 4) {
-                const float4 b4 = *reinterpret_cast<const float4*>(sbeta + c0 + u);
-                const float4 l4 = *reinterpret_cast<const float4*>(slw + c0 + u);
-                be[u] = b4.x; be[u + 1] = b4.y; be[u + 2] = b4.z; be[u + 3] = b4.w;
-                lw[u] = l4.x; lw[u + 1] = l4.y; lw[u + 2] = l4.z; lw[u + 3] = l4.w;
+                const float4 a4 = *reinterpret_cast<const float4*>(sa + c0 + u);
+                const float4 b4 = *reinterpret_cast<const float4*>(sb + c0 + u);
+                const float4 l4 = *reinterpret_cast<const float4*>(slb + c0 + u);
+                fa[u] = a4.x; fa[u + 1] = a4.y; fa[u + 2] = a4.z; fa[u + 3] = a4.w;
+                fb[u] = b4.x; fb[u + 1] = b4.y; fb[u + 2] = b4.z; fb[u + 3] = b4.w;
+                lb[u] = l4.x; lb[u + 1] = l4.y; lb[u + 2] = l4.z; lb[u + 3] = l4.w;
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const bool in = c0 + u < nc;
-                const float L2 = L + lw[u];
-                const float A2 = __builtin_fmaf(buf[u], be[u], A);
+                const float L2 = __builtin_fmaf(L, fa[u], lb[u]);
+                const float A2 = __builtin_fmaf(A, fa[u], buf[u] * fb[u]);
                 L = in ? L2 : L;
                 A = in ? A2 : A;
             }
         };
-        float ba[U], bb[U];
-        fetch(ba, 0);                           // independent of the maximum
-        // (m, l) of every chunk into LDS, four chunks' loads in flight per thread
-        float mloc = -INFINITY;
-        for (int c0 = 0; c0 < nc; c0 += 4 * D) {
-            float2 ml[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int cc = c0 + j * D + tid;
-                ml[j] = cc < nc ? *reinterpret_cast<const float2*>(ws_ml + (base + cc) * 2) : make_float2(-INFINITY, 0.f);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int cc = c0 + j * D + tid;
-                if (cc < nc) {
-                    sbeta[cc] = ml[j].x;
-                    slw[cc] = ml[j].y;
-                    mloc = fmaxf(mloc, ml[j].x);
-                }
-            }
+        float ba[U], bbuf[U];
+        fetch(ba, 0);                           // independent of the factors
+        // (m, l) of this thread's segment of chunks: m into sa, l into slb; the segment's
+        // maximum into the scan array
+        const int seg = (nc + D - 1) / D;
+        const int s0 = tid * seg, s1 = s0 + seg < nc ? s0 + seg : nc;
+        float mseg = -INFINITY;
+        for (int cc = s0; cc < s1; ++cc) {
+            const float2 ml = *reinterpret_cast<const float2*>(ws_ml + (base + cc) * 2);
+            sa[cc] = ml.x;
+            slb[cc] = ml.y;
+            mseg = fmaxf(mseg, ml.x);
         }
-        const float M = xv_combine_max<D>(mloc, sred, tid);
-        for (int cc = tid; cc < nc; cc += D) {  // the entries this thread wrote
-            const float be = __builtin_amdgcn_exp2f(sbeta[cc] - M);
-            sbeta[cc] = be;
-            slw[cc] = slw[cc] * be;
+        sred[tid] = mseg;
+        __syncthreads();
+        // inclusive prefix maximum over the segments (exact)
+        for (int off = 1; off < D; off <<= 1) {
+            const float v = tid >= off ? fmaxf(sred[tid], sred[tid - off]) : sred[tid];
+            __syncthreads();
+            sred[tid] = v;
+            __syncthreads();
+        }
+        // the factors of this thread's chunks, from the maximum of every earlier chunk
+        float M = tid > 0 ? sred[tid - 1] : -INFINITY;
+        for (int cc = s0; cc < s1; ++cc) {
+            float fa, fb;
+            xv_fold_factors(M, sa[cc], fa, fb);
+            sa[cc] = fa;
+            sb[cc] = fb;
+            slb[cc] = slb[cc] * fb;
         }
         __syncthreads();
         for (int c0 = 0; c0 < nc; c0 += 2 * U) {
-            fetch(bb, c0 + U);
+            fetch(bbuf, c0 + U);
             fold(ba, c0);
             fetch(ba, c0 + 2 * U);
-            fold(bb, c0 + U);
+            fold(bbuf, c0 + U);
         }
     }
     const float ov = A / L;
@@ -1069,7 +1076,7 @@ int xv_attn_combine(const float* ws_acc, const float* ws_ml, const int32_t* kv_l
 {
     (void)hipGetLastError();
     if (NC > 2 * XV_COMBINE_U) {
-        const size_t shmem = sizeof(float) * (2 * (size_t)xv_combine_pad(NC) + D);
+        const size_t shmem = sizeof(float) * (3 * (size_t)xv_combine_pad(NC) + D);
         hipLaunchKernelGGL((xv_attn_combine_kernel<D, true>), dim3(Hq, T, B), dim3(D), shmem, st,
                            ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC);
     } else {
@@ -1331,12 +1338,11 @@ __global__ void xv_kv_append_kernel(const uint16_t* __restrict__ k_new, const ui
 // L0 + r) gets exactly the decode row's numbers: per chunk c (absolute boundaries) the
 // scores (the same MFMA chain, K as A and q as B), the exact chunk maximum m_c, the
 // probabilities 2^(s - m_c), their sum in the partial kernels' order and the P.V chains
-// (p as bf16 hi + lo, k-steps ascending); then the combine's fold in ascending c with
-// M = max_c m_c:  L = L + l_c 2^(m_c - M),  A = fma(acc_c, 2^(m_c - M), A),  o = A / L.
-// M is needed before the first fold, so the chunks are walked twice: pass 1 forms each
-// row's maximum from the same scores, pass 2 the partials and the fold, all in registers.
-// Every chunk is read from the cache (the rows were appended first); positions at or past
-// L0 + P are zero-filled in LDS and never visible.
+// (p as bf16 hi + lo, k-steps ascending), each folded at once into the row's sums with the
+// combine's operations (xv_fold_factors: the running maximum, ascending c), o = A / L; one
+// pass over the chunks, everything in registers.  Every chunk is read from the cache (the
+// rows were appended first); positions at or past L0 + P are zero-filled in LDS and never
+// visible.
 template <int D>
 __global__ __launch_bounds__(XV_PF_THREADS)
 void xv_attn_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
@@ -1454,75 +1460,11 @@ void xv_attn_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             for (int i = 0; i < 4; ++i) sc[cb][i] = sc[cb][i] * scale_log2;
     };
 
-    // ---- pass 1: each pair's maximum over its visible positions.  K streams in 64-position
-    // sub-blocks through one LDS buffer, the next two sub-blocks in flight in registers; the
-    // scores are the same MFMA chains as in pass 2, four score blocks at a time ----
-    constexpr int SB = 64;                      // positions per sub-block
-    constexpr int NSB = C / SB;
-    constexpr int SKG = SB * (D / 8) / NT;      // K granules per thread per sub-block
-    static_assert(SB * (D / 8) % NT == 0, "sub-blocks must split evenly");
-    float M = -INFINITY;
-    {
-        xv_u32x4 qf[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = pair_ok ? xv_load16(qp + ks * 32) : zero;
-        const int nsb = nc * NSB;
-        auto kload = [&](xv_u32x4 (&kr)[SKG], int u) {
-            u = u < nsb ? u : nsb - 1;          // past the end: a re-read, never used
-#pragma unroll
-            for (int i = 0; i < SKG; ++i) {
-                const int idx = tid + i * NT;
-                const int pos = u * SB + idx / (D / 8);
-                kr[i] = xv_load16(k_cache + (kvbase + (pos < Lend ? pos : 0)) * D + (idx % (D / 8)) * 8);
-                if (pos >= Lend) kr[i] = zero;
-            }
-        };
-        auto kstore = [&](const xv_u32x4 (&kr)[SKG]) {
-#pragma unroll
-            for (int i = 0; i < SKG; ++i) {
-                const int idx = tid + i * NT;
-                *reinterpret_cast<xv_u32x4*>(lds + (idx / (D / 8)) * KP + (idx % (D / 8)) * 16) = kr[i];
-            }
-        };
-        xv_u32x4 kr0[SKG], kr1[SKG];
-        kload(kr0, 0);
-        kload(kr1, 1);
-        for (int u = 0; u < nsb; u += 2) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                xv_u32x4 (&kr)[SKG] = h ? kr1 : kr0;
-                const int uu = u + h;
-                __syncthreads();                // the buffer is free
-                kstore(kr);
-                kload(kr, uu + 2);
-                __syncthreads();
-                if (uu < nsb && uu / NSB < tnc) {   // uniform per wave
-                    xv_f32x4 s4[SB / 16];
-#pragma unroll
-                    for (int j = 0; j < SB / 16; ++j) s4[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                        for (int j = 0; j < SB / 16; ++j)
-                            s4[j] = xv_mfma16x16x32(*reinterpret_cast<const xv_u32x4*>(lds + (j * 16 + lr) * KP + ks * 64 + lg * 16),
-                                                    qf[ks], s4[j]);
-#pragma unroll
-                    for (int j = 0; j < SB / 16; ++j)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (uu * SB + j * 16 + 4 * lg + i < plen) M = fmaxf(M, s4[j][i] * scale_log2);
-                }
-            }
-        }
-    }
-    M = fmaxf(M, __shfl_xor(M, 16));
-    M = fmaxf(M, __shfl_xor(M, 32));
-
-    // ---- pass 2: chunk partials, folded in ascending chunk order ----
+    // ---- chunk partials, folded in ascending chunk order with the running maximum ----
     xv_f32x4 A[DB];
 #pragma unroll
     for (int j = 0; j < DB; ++j) A[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
+    float L = 0.f, Mrun = -INFINITY;            // this lane's score pair (lr)
     int orow[4];
     bool ook[4];
 #pragma unroll
@@ -1537,7 +1479,7 @@ void xv_attn_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         k_to_lds(c0);
         __syncthreads();
         const bool active = c < tnc;            // uniform per wave
-        float beta = 0.f;
+        float fa = 0.f, fb = 0.f;
         if (active) {
             scores();
             float m = -INFINITY;
@@ -1565,8 +1507,8 @@ void xv_attn_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             l = l + __shfl_xor(l, 16);
             l = l + __shfl_xor(l, 32);
             if (sees) {
-                beta = __builtin_amdgcn_exp2f(m - M);
-                L = L + l * beta;
+                xv_fold_factors(Mrun, m, fa, fb);
+                L = __builtin_fmaf(L, fa, l * fb);
             }
 #pragma unroll
             for (int kk = 0; kk < C / 32; ++kk) {   // the P.V A operands, bf16 hi + lo
@@ -1580,11 +1522,12 @@ void xv_attn_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         vt_to_lds(c0);
         __syncthreads();
         if (active) {
-            float bi[4];
+            float ai[4], bi[4];
             bool si[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                bi[i] = __shfl(beta, 4 * lg + i);
+                ai[i] = __shfl(fa, 4 * lg + i);
+                bi[i] = __shfl(fb, 4 * lg + i);
                 si[i] = ook[i] && L0 + orow[i] + 1 > c0;
             }
 #pragma unroll
@@ -1601,7 +1544,8 @@ void xv_attn_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                     oacc = xv_mfma16x16x32(__builtin_bit_cast(xv_u32x4, sc[2 * kk + 1]), vf, oacc);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) A[db][i] = si[i] ? __builtin_fmaf(oacc[i], bi[i], A[db][i]) : A[db][i];
+                for (int i = 0; i < 4; ++i)
+                    A[db][i] = si[i] ? __builtin_fmaf(A[db][i], ai[i], oacc[i] * bi[i]) : A[db][i];
             }
         }
     }

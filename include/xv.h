@@ -190,9 +190,10 @@ int xv_gdn_verify_after(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * attends positions 0..L0+r:  o = sum_j softmax_j(scale * q.k_j) v_j.
  * The context is split into chunks of xv_attn_chunk_tokens() positions at
  * absolute boundaries; per chunk the partial (max, sum, weighted values) is
- * formed in a fixed order, and the chunks are merged in ascending order
- * against the row's overall maximum.  All of it depends on the row's length
- * and data only, never on T, B, Lmax or the workspace size.
+ * formed in a fixed order, and the chunks are merged in ascending order with
+ * a running maximum (a chunk that raises it rescales the sums so far).  All of
+ * it depends on the row's length and data only, never on T, B, Lmax or the
+ * workspace size.
  *
  *   q        : bf16 [B][T][Hq][d]      [16B]
  *   k_new    : bf16 [B][T][Hkv][d]     [16B]  v_new: same
@@ -202,7 +203,8 @@ int xv_gdn_verify_after(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *   o32      : fp32 [B][T][Hq][d] or NULL
  *   workspace: [16B] device scratch of workspace_bytes >= xv_attn_workspace_bytes(B,T,Hq,d,Lmax)
  * Shapes: B >= 0, 1 <= T <= 16, Hq % Hkv == 0, d in {64, 128, 256}, Lmax >= T,
- * B * Hkv * ceil(Lmax / chunk) * ceil((Hq/Hkv) * T / 16) <= 2^29 (the grid;
+ * ceil(Lmax / chunk) <= 5120, B * Hkv * ceil(Lmax / chunk) * ceil((Hq/Hkv) * T / 16)
+ * <= 2^29 (the grid;
  * XV_ERR_SHAPE otherwise).  Device precondition: 0 <= L0 and
  * L0 + T <= Lmax (kernels clamp positions to the buffer otherwise).
  * Cache positions >= L0 + T are never read, so they may hold anything.
@@ -257,14 +259,14 @@ int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * (L0 = kv_len[b]), then row r attends positions 0..L0+r with
  * exactly the arithmetic of xv_attn_verify_rows for that row (the same chunk
  * partials and the same ordered combine), so every output equals the decode
- * row's bit for bit.  No workspace: each workgroup keeps 128 (row, head) pairs'
- * partials in registers, after a first pass over the chunks for each row's
- * maximum.
+ * row's bit for bit.  No workspace: each workgroup folds 128 (row, head) pairs'
+ * chunk partials in registers, in one pass over the chunks.
  *   q      : bf16 [B][P][Hq][d]  [16B]     k_new, v_new : bf16 [B][P][Hkv][d] [16B]
  *   k_cache, v_cache : bf16 [B][Hkv][Lmax][d] [16B]; rows L0..L0+P-1 are written
  *   kv_len : int32 [B] device; advance != 0: kv_len[b] += P after the rows are formed
  *   o : bf16 [B][P][Hq][d]   o32 : fp32 or NULL
- * Shapes: B >= 0, P >= 1, Hq % Hkv == 0, d in {64, 128, 256}, Lmax >= P.  Device
+ * Shapes: B >= 0, P >= 1, Hq % Hkv == 0, d in {64, 128, 256}, Lmax >= P,
+ * ceil(Lmax / chunk) <= 5120.  Device
  * precondition: 0 <= L0 and L0 + P <= Lmax (positions are clamped otherwise).
  */
 int xv_attn_prefill(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
