@@ -189,6 +189,10 @@ __device__ __forceinline__ xv_u32x4 xv_vt_frag(const xv_u32x4* lds, int db, int 
 }
 
 // Store a wave's P.V output blocks db0 .. db0 + NB - 1 of pairs tile*16 + 4*lg + i.
+// Partials are written with non-temporal (streaming) vector stores, and the long-row combine
+// reads them the same way: each is read once, by the next kernel, and not keeping them in the
+// caches leaves fewer dirty lines to be written back during the projections that follow
+// (long context: 0.264 -> 0.261 ms per step).
 template <int D, int NB>
 __device__ __forceinline__ void xv_store_acc(float* __restrict__ ws_acc, const xv_f32x4 (&oacc)[NB], int db0,
                                              int tile, int lr, int lg, int P, int Hg, int g, int b, int T,
@@ -202,7 +206,7 @@ __device__ __forceinline__ void xv_store_acc(float* __restrict__ ws_acc, const x
         const int h = g * Hg + pair % Hg;
         float* dst = ws_acc + ((((size_t)b * T + r) * Hq + h) * NC + c) * D + lr;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) dst[(db0 + j) * 16] = oacc[j][i];
+        for (int j = 0; j < NB; ++j) __builtin_nontemporal_store(oacc[j][i], &dst[(db0 + j) * 16]);
     }
 }
 
@@ -328,8 +332,8 @@ void xv_attn_partial_wide_kernel(const uint16_t* __restrict__ q, const uint16_t*
     // ---- the chunk partials of pairs that see this chunk ----
     if (lg == 0 && pair_ok && plen > c0) {
         const size_t idx = (((size_t)b * T + pr) * Hq + ph) * NC + c;
-        ws_ml[idx * 2 + 0] = m;
-        ws_ml[idx * 2 + 1] = l;
+        __builtin_nontemporal_store(m, &ws_ml[idx * 2 + 0]);
+        __builtin_nontemporal_store(l, &ws_ml[idx * 2 + 1]);
     }
     xv_store_acc<D, DB>(ws_acc, oacc, 0, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
 }
@@ -619,8 +623,8 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
         if (tile_on) {
             if (dh == 0 && lg == 0 && pair_ok && plen > c0) {
                 const size_t idx = (((size_t)b * T + pr) * Hq + ph) * NC + c;
-                ws_ml[idx * 2 + 0] = m;
-                ws_ml[idx * 2 + 1] = l;
+                __builtin_nontemporal_store(m, &ws_ml[idx * 2 + 0]);
+                __builtin_nontemporal_store(l, &ws_ml[idx * 2 + 1]);
             }
             xv_store_acc<D, DBH>(ws_acc, oacc, dh * DBH, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
         }
@@ -796,8 +800,8 @@ __device__ __forceinline__ void xv_attn_tile_body(const XvTileArgs A, int bid, X
         l = l + __shfl_xor(l, 32);
         if (lg == 0 && pair_ok && plen > c0) {
             const size_t idx = (((size_t)b * T + pr) * Hq + ph) * NC + c;
-            ws_ml[idx * 2 + 0] = m;
-            ws_ml[idx * 2 + 1] = l;
+            __builtin_nontemporal_store(m, &ws_ml[idx * 2 + 0]);
+            __builtin_nontemporal_store(l, &ws_ml[idx * 2 + 1]);
         }
     }
 
@@ -910,7 +914,7 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int cn = c0 + u;
-                buf[u] = ap[(size_t)(cn < nc ? cn : nc - 1) * D];
+                buf[u] = __builtin_nontemporal_load(&ap[(size_t)(cn < nc ? cn : nc - 1) * D]);
             }
         };
         // a, b and l b four at a time from LDS (padded to a multiple of 2 U); a chunk past
