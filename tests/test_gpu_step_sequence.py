@@ -1,11 +1,14 @@
-"""The speculative step exactly as the throughput benchmark launches it, at the short
-workload's full sizes (5120-wide projections, 48 GDN heads, 24 query heads over a 640-token
-cache, a 4096-wide head): the projection pair in one launch, GDN and attention in one launch
-(from the second step on with the previous step's rollback folded in), the head pair, the
-greedy acceptance that also counts the kept KV rows, and the settle after the last step;
+"""The speculative step exactly as the throughput benchmark launches it, at full sizes
+(5120-wide projections, 48 GDN heads, 24 query heads, a 4096-wide head) for batch 1 over a
+640-token cache, batch 8 over 560-740 tokens and batch 1 over 127,735 tokens: the
+projection pair in one launch, GDN and attention in one launch where they fit (from the
+second step on with the previous step's rollback folded in), the head pair, the greedy
+acceptance that also counts the kept KV rows, and the settle after the last step;
 bf16-only projection, GDN and attention outputs as in the benchmark.  Every step is
 checked against the oracle run on the same inputs from the same state, carried from step
-to step with the GPU's acceptance counts (whose rule is checked on the GPU's ids)."""
+to step with the GPU's acceptance counts (whose rule is checked on the GPU's ids); at
+127,735 tokens the attention rows are checked on a sample (the oracle takes one row at a
+time there)."""
 import numpy as np
 import pytest
 import torch
@@ -34,11 +37,13 @@ def _sum_bound(x, w):
     return (K * u / (1 - K * u)) * oracle.gemm(x & 0x7FFF, w & 0x7FFF)
 
 
-def test_benchmark_step_sequence_vs_oracle_short():
+@pytest.mark.parametrize("name", ["short", "batch8", "long"])
+def test_benchmark_step_sequence_vs_oracle(name):
     from bit_exact_speculative_amd.layer import Layer
-    wl = gen.WORKLOADS["short"]
+    wl = gen.WORKLOADS[name]
     B, T, M = wl.B, wl.T, wl.M
-    inp = gen.make_inputs(wl, Lmax=wl.L0 + T * (STEPS + 4))
+    L0max = wl.L0 if wl.L0 is not None else wl.L0_range[1]
+    inp = gen.make_inputs(wl, Lmax=L0max + T * (STEPS + 4))
     S0 = prefix_state(inp)
     L = Layer(inp, "cuda", state_in=S0)
     L.proj_fp32 = False
@@ -63,9 +68,15 @@ def test_benchmark_step_sequence_vs_oracle_short():
         o_ref, _, _ = oracle.gdn(g["q"], g["k"], g["v"], g["a"], g["b"], S)
         fg = _bits(L.o_gdn).reshape(M, -1)
         assert max_rel(bf16_value(fg), o_ref.reshape(M, -1)) <= BF16_REL, s
-        a_ref = oracle.attn(inp.q_attn, inp.k_new, inp.v_new, kc, vc, kv, L.scale)
         fa = _bits(L.o_attn).reshape(M, -1)
-        assert max_rel(bf16_value(fa), a_ref.reshape(M, -1)) <= BF16_REL, s
+        if name == "long":
+            fa4 = bf16_value(fa).reshape(B, T, wl.Hq, wl.d)
+            for (bb, r, h) in [(0, 0, 0), (0, 8, 23), (0, 4, 11)]:
+                ref = oracle.attn_row(inp.q_attn, inp.k_new, inp.v_new, kc, vc, kv, L.scale, bb, r, h)
+                assert max_rel(fa4[bb, r, h], ref) <= BF16_REL, (s, bb, r, h)
+        else:
+            a_ref = oracle.attn(inp.q_attn, inp.k_new, inp.v_new, kc, vc, kv, L.scale)
+            assert max_rel(bf16_value(fa), a_ref.reshape(M, -1)) <= BF16_REL, s
         # the head on the GPU's own bf16 features
         lg_ref = oracle.gemm(fg, inp.Wh_gdn)
         la_ref = oracle.gemm(fa, inp.Wh_attn)
@@ -102,7 +113,8 @@ def test_benchmark_step_sequence_vs_oracle_short():
     L.settle()
     torch.cuda.synchronize()
     assert rel_l2(L.S_in.cpu().numpy(), S) <= STATE_REL_L2
-    n = int(kv.max())
-    assert np.array_equal(_bits(L.Kc)[:, :, :n], kc[:, :, :n])
-    assert np.array_equal(_bits(L.Vc)[:, :, :n], vc[:, :, :n])
+    Kg, Vg = _bits(L.Kc), _bits(L.Vc)
+    for bb in range(B):                             # each request's cache up to its own length
+        n = int(kv[bb])
+        assert np.array_equal(Kg[bb, :, :n], kc[bb, :, :n]) and np.array_equal(Vg[bb, :, :n], vc[bb, :, :n]), bb
     assert not same_bits(L.S_in, torch.from_numpy(S0).cuda())     # the state moved
