@@ -1,6 +1,6 @@
 """The speculative step exactly as the throughput benchmark launches it, at full sizes
-(5120-wide projections, 48 GDN heads, 24 query heads, a 4096-wide head) for batch 1 over a
-640-token cache, batch 8 over 560-740 tokens and batch 1 over 127,735 tokens: the
+(5120-wide projections, 48 GDN heads, 24 query heads, a 4096-wide head) for batch 1 over
+640 and 2183 cached tokens, batch 8 over 560-740 and batch 1 over 127,735: the
 projection pair in one launch, GDN and attention in one launch where they fit (from the
 second step on with the previous step's rollback folded in), the head pair, the greedy
 acceptance that also counts the kept KV rows, and the settle after the last step;
@@ -37,7 +37,7 @@ def _sum_bound(x, w):
     return (K * u / (1 - K * u)) * oracle.gemm(x & 0x7FFF, w & 0x7FFF)
 
 
-@pytest.mark.parametrize("name", ["short", "batch8", "long"])
+@pytest.mark.parametrize("name", ["short", "medium", "batch8", "long"])
 def test_benchmark_step_sequence_vs_oracle(name):
     from bit_exact_speculative_amd.layer import Layer
     wl = gen.WORKLOADS[name]
