@@ -988,14 +988,6 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
 // three kernels give the same bits).
 enum XvAttnKind { XV_ATTN_TILE, XV_ATTN_WIDE, XV_ATTN_STREAM };
 
-inline int xv_cu_count() {
-    int cus = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
-    return cus;
-}
-
 template <int D>
 XvAttnKind xv_attn_kind(int B, int T, int Hq, int Hkv, int NC) {
     // one workgroup per (chunk, KV head, request) when those alone fill the chip,

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <atomic>
 
 #include "../../include/xv.h"
 
@@ -82,4 +83,18 @@ static inline bool xv_aligned(const void* p, unsigned n) { return (((uintptr_t)p
 static inline int xv_launch_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? XV_OK : XV_ERR_LAUNCH;
+}
+
+// The current device's compute-unit count (for grid sizes; 256 on MI355X), queried once per
+// device and kept; several host threads may call it at once.
+inline int xv_cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    int cus = dev < 64 ? cached[dev].load(std::memory_order_relaxed) : 0;
+    if (cus > 0) return cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }

@@ -756,14 +756,7 @@ void xv_gemm_xstream_kernel(const uint16_t* __restrict__ x, const uint16_t* __re
 }
 
 int xv_gemm_grid(int nblk) {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-    }
+    const int cus = xv_cu_count();
     return nblk < cus ? nblk : cus;
 }
 
