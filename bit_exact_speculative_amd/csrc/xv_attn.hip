@@ -51,6 +51,7 @@ constexpr int XV_ATTN_MAX_NC = 5120;   // chunks of the capacity (1,310,720 posi
 constexpr int XV_ATTN_WIDE_MIN = 128; // (chunk, KV head, request) workgroups from which the wide kernel runs
 constexpr int XV_ATTN_STREAM_MIN = 1024; // ... and from which the persistent streaming kernel runs (about 4 chunks per CU)
 constexpr int XV_COMBINE_U = 24;    // chunks per block of combine loads kept in flight
+static_assert(XV_COMBINE_U % 4 == 0, "the long-row combine reads its per-chunk factors four at a time");
 constexpr int XV_COMBINE_PRE = 8;   // chunks a short row's combine loads before its maximum
 // GDN + attention in one launch while their workgroups are at most these multiples
 // of the CU count (GDN with one, or else two, column groups per workgroup)
