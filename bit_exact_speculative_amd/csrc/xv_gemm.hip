@@ -182,6 +182,7 @@ __global__ __launch_bounds__(XV_GEMM_THREADS)
 void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0, int contig)
 {
     static_assert(NS % 2 == 0 && SL * NS == XV_GEMM_WAVES * KSW, "stages must split the ranges evenly");
+    static_assert(XV_GEMM_WAVES % NS == 0, "each stage must hold whole K ranges of the same number of waves");
     constexpr int WPS = XV_GEMM_WAVES / NS;         // waves whose ranges a stage holds
     constexpr int PITCH = xv_frag_pitch(SL * 32);   // LDS row pitch (bf16)
     constexpr int PER_ROW = SL * 4;                 // 16-byte granules per row per stage
