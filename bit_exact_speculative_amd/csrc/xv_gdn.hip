@@ -15,21 +15,30 @@
 //     o_j  = sum_i s_i q_i                 (same fixed-order dot)
 // which is S_t = a S_{t-1} (I - b k k^T) + b v k^T, o = S_t q.
 //
-// Work mapping (gfx950, wave64): a workgroup of 8 waves owns 32 value indices
-// of one (request, value head) (64, two columns per lane, when it shares a launch
-// with attention and the chip is short of CUs for one column); in a wave,
-// 16 lanes share a column and each holds R = dk/16 consecutive key indices of it
-// in VGPRs, for the whole call (so the recurrence's dependency chain per token is
-// short, and a batch-1 call still gives every SIMD more than one wave to
-// interleave).
-// The fixed dot order: in each lane four fp32 chains over i mod 4 in ascending
-// i, combined as (c0 + c1) + (c2 + c3); then a butterfly over the 16 lanes
-// (DPP: partner lane^1, lane^2, the mirrored half of each 8, the mirrored
-// half of the 16).  Every lane ends with the same bits (each step adds the
-// same two values in either order), so all lanes of a column compute the same
-// u.  The state is read once and written once per call; the rows of all
-// tokens are staged in LDS (k and q already widened to fp32) before the token
-// loop starts.
+// The fixed dot order (xv_gdn_dot): the dk key indices form 16 partials of dk/16
+// consecutive indices, each two fp32 chains (even and odd indices, ascending) then
+// their sum; the partials meet in a balanced tree ((p0 + p1) + (p2 + p3)) + ...
+// A kernel may spread a column over L lanes (L dividing 16): each lane forms its
+// 16/L partials and the first tree levels in registers, the last log2 L levels run
+// across the lanes by DPP.  Every tree node adds the same two values whatever L is
+// (fp32 addition is commutative), so the bits do not depend on L, and every lane of
+// a column ends with them: all lanes of a column compute the same u.
+//
+// Two work mappings (gfx950, wave64), the same arithmetic:
+//  - 16 lanes per column (few requests: the shortest per-token dependency chain,
+//    and a batch-1 call still gives every SIMD more than one wave to interleave):
+//    a workgroup of 8 waves owns 32 value indices of one (request, value head) (64,
+//    two columns per lane, when it shares a launch with attention and the chip is
+//    short of CUs for one column); each lane holds dk/16 consecutive key indices of
+//    its column in VGPRs for the whole call; the state slab moves through LDS so
+//    that its global reads and writes are 16-byte.
+//  - 4 lanes per column (many requests: a quarter of the cross-lane steps and of the
+//    per-lane overhead per column, so the VALU issues about 40% fewer instructions per
+//    state element): a workgroup of 4 waves owns 64 value indices, a lane dk/4 key
+//    indices of one column, read and written straight from global memory (each
+//    instruction moves four 64-byte runs of a state row).
+// The state is read once and written once per call; the rows of all tokens are
+// staged in LDS (k and q already widened to fp32) before the token loop starts.
 #include "xv_gdn_impl.h"
 
 namespace {
@@ -53,12 +62,111 @@ void xv_gdn_prefill_kernel(XvGdnArgs A)
     xv_gdn_prefill_body<DK>(A, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
+// 4 lanes per column: a workgroup of 4 waves owns 64 value indices of one (request,
+// value head); lane (jc, ig) = 4 jc + ig of wave w holds key indices ig R .. ig R + R - 1
+// of value index 16 w + jc, R = dk / 4.  Three workgroups share a CU (at most 168 VGPRs).
+constexpr int XV_GDN4_WAVES = 4;
+constexpr int XV_GDN4_W = XV_GDN4_WAVES * 16;
+
+template <int DK>
+struct XvGdn4Smem {
+    float skq[XV_GDN_TM][2][DK];
+    uint16_t sv[XV_GDN_TM][XV_GDN4_W];
+    float sab[XV_GDN_TM][2];
+};
+
+template <int DK, int DV, bool ROLLBACK>
+__global__ __launch_bounds__(XV_GDN4_WAVES * 64, 3)
+void xv_gdn4_kernel(XvGdnArgs A)
+{
+    constexpr int L = 4;
+    constexpr int R = DK / L;
+    constexpr int W = XV_GDN4_W;
+    __shared__ __attribute__((aligned(16))) XvGdn4Smem<DK> sm;
+    const int bx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int ig = lane & (L - 1);
+    const int jw = (tid >> 6) * 16 + (lane >> 2);   // value index within the workgroup
+    const int j0 = bx * W;
+    const int Hv = A.Hv, T = A.T, Tp = A.Tp;
+    const int g = h / (Hv / A.Hk);
+
+    int np = 0;
+    const float* S0 = A.S_in;
+    if (A.n_pre) {
+        np = A.n_pre[b];
+        np = np < 0 ? 0 : (np > Tp ? Tp : np);
+        if (ROLLBACK) {
+            if (bx == 0 && h == 0 && tid == 0) A.kv_len[b] += np;
+            if (np == Tp) return;                // state_out already holds S_T
+        } else if (np == Tp && A.S_alt) {
+            S0 = A.S_alt;                        // every previous row kept: its S_T, nothing to replay
+            np = 0;
+        }
+    }
+    const int n = np + (ROLLBACK ? 0 : T);
+
+    const size_t sofs = ((size_t)(b * Hv + h) * DK + ig * R) * DV + j0 + jw;
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = S0[sofs + (size_t)r * DV];
+    xv_gdn_stage<DK, W, XV_GDN4_WAVES * 64>(A, b, h, g, j0, np, n, sm.skq, sm.sv, sm.sab);
+    __syncthreads();
+
+    auto store_state = [&](float* __restrict__ dst) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) dst[sofs + (size_t)r * DV] = s[r];
+    };
+    auto read_row = [&](int t, int which, float (&x)[R]) {
+#pragma unroll
+        for (int c = 0; c < R / 4; ++c) {
+            const xv_f32x4 v4 = *reinterpret_cast<const xv_f32x4*>(&sm.skq[t][which][ig * R + c * 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[c * 4 + e] = v4[e];
+        }
+    };
+    float kk[R], qq[R];
+    if (n > 0) read_row(0, 0, kk);
+    for (int t = 0; t < n; ++t) {                // uniform
+        if (!ROLLBACK && A.S_mid && t == np) store_state(A.S_mid);   // the kept state
+        const bool out = !ROLLBACK && t >= np;
+        if (out) read_row(t, 1, qq);
+        xv_gdn_token<L, R>(s, kk, xv_bf16_to_f32(sm.sv[t][jw]), sm.sab[t][0], sm.sab[t][1]);
+        read_row(t + 1 < n ? t + 1 : t, 0, kk);  // the next token's k (read on every path)
+        if (out) {
+            const float ot = xv_gdn_dot<L, R>(s, qq);
+            if (ig == 0) {
+                const size_t oi = (((size_t)b * T + (t - np)) * Hv + h) * DV + j0 + jw;
+                A.o[oi] = xv_f32_to_bf16(ot);
+                if (A.o32) A.o32[oi] = ot;
+            }
+        }
+    }
+    if (!ROLLBACK && A.S_mid && n == np) store_state(A.S_mid);      // no rows of this call
+    store_state(A.S_out);
+}
+
+// 4 lanes per column when the 16-lane grid would take more than about two workgroups per
+// CU (the same bits either way).
+inline bool xv_gdn_use4(int B, int Hv, int dv) {
+    return (dv == 64 || dv == 128) && (long long)B * Hv * (dv / XV_GDN4_W) >= 2LL * xv_cu_count();
+}
+
 template <bool ROLLBACK>
 int xv_gdn_launch(const XvGdnArgs& args, int B, int dk, hipStream_t st)
 {
+    (void)hipGetLastError();
+    if (xv_gdn_use4(B, args.Hv, args.dv)) {
+        dim3 grid(args.dv / XV_GDN4_W, args.Hv, B), block(XV_GDN4_WAVES * 64);
+        if (dk == 128 && args.dv == 128) hipLaunchKernelGGL((xv_gdn4_kernel<128, 128, ROLLBACK>), grid, block, 0, st, args);
+        else if (dk == 128) hipLaunchKernelGGL((xv_gdn4_kernel<128, 64, ROLLBACK>), grid, block, 0, st, args);
+        else if (args.dv == 128) hipLaunchKernelGGL((xv_gdn4_kernel<64, 128, ROLLBACK>), grid, block, 0, st, args);
+        else hipLaunchKernelGGL((xv_gdn4_kernel<64, 64, ROLLBACK>), grid, block, 0, st, args);
+        return xv_launch_status();
+    }
     // one column group per workgroup: the shortest latency when the GDN runs alone
     dim3 grid(args.dv / XV_GDN_JW, args.Hv, B), block(XV_GDN_THREADS);
-    (void)hipGetLastError();
     if (dk == 128) hipLaunchKernelGGL((xv_gdn_kernel<128, ROLLBACK, 1>), grid, block, 0, st, args);
     else hipLaunchKernelGGL((xv_gdn_kernel<64, ROLLBACK, 1>), grid, block, 0, st, args);
     return xv_launch_status();

@@ -30,35 +30,57 @@ __device__ __forceinline__ float xv_dpp_mirror16(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
 }
 
-template <int R>
-__device__ __forceinline__ float xv_gdn_dot(const float (&s)[R], const float (&x)[R]) {
-    static_assert(R % 4 == 0, "four chains");
+// The one dot product of the rule, sum_i s_i x_i over the dk key indices of a state
+// column.  The dk indices form 16 partials of P = dk / 16 consecutive indices; a partial
+// is two fp32 chains, over its even and its odd indices in ascending order, then their
+// sum; the 16 partials meet in a balanced tree, ((p0 + p1) + (p2 + p3)) + ..., level by
+// level.  A kernel may spread a column over L = 1, 2, 4, 8 or 16 lanes: lane ig of the L
+// holds the R = dk / L indices [ig R, ig R + R), forms its 16 / L partials and the tree's
+// first levels over them in registers, and the last log2 L levels run across the lanes
+// (DPP within each row of 16 lanes: lane^1, lane^2, the mirrored half of each 8, the
+// mirrored half of the 16).  Each tree node adds the same two values in every
+// arrangement (fp32 addition is commutative), so the result has the same bits for every
+// L, and every lane of a column ends with them.
+template <int P>
+__device__ __forceinline__ float xv_gdn_partial(const float* s, const float* x) {
+    static_assert(P % 2 == 0, "two chains");
     float c0 = s[0] * x[0];
     float c1 = s[1] * x[1];
-    float c2 = s[2] * x[2];
-    float c3 = s[3] * x[3];
 #pragma unroll
-    for (int r = 4; r < R; r += 4) {
-        c0 = __builtin_fmaf(s[r + 0], x[r + 0], c0);
+    for (int r = 2; r < P; r += 2) {
+        c0 = __builtin_fmaf(s[r], x[r], c0);
         c1 = __builtin_fmaf(s[r + 1], x[r + 1], c1);
-        c2 = __builtin_fmaf(s[r + 2], x[r + 2], c2);
-        c3 = __builtin_fmaf(s[r + 3], x[r + 3], c3);
     }
-    float p = (c0 + c1) + (c2 + c3);
-    p = p + xv_dpp_xor1(p);
-    p = p + xv_dpp_xor2(p);
-    p = p + xv_dpp_mirror8(p);
-    p = p + xv_dpp_mirror16(p);
-    return p;
+    return c0 + c1;
+}
+
+template <int L, int R>
+__device__ __forceinline__ float xv_gdn_dot(const float (&s)[R], const float (&x)[R]) {
+    static_assert(L == 1 || L == 2 || L == 4 || L == 8 || L == 16, "L divides 16");
+    constexpr int PL = 16 / L;                       // partials per lane
+    constexpr int P = R / PL;                        // indices per partial
+    float p[PL];
+#pragma unroll
+    for (int g = 0; g < PL; ++g) p[g] = xv_gdn_partial<P>(s + g * P, x + g * P);
+#pragma unroll
+    for (int w = 1; w < PL; w *= 2)                  // in-lane tree levels
+#pragma unroll
+        for (int g = 0; g < PL; g += 2 * w) p[g] = p[g] + p[g + w];
+    float t = p[0];
+    if constexpr (L >= 2) t = t + xv_dpp_xor1(t);
+    if constexpr (L >= 4) t = t + xv_dpp_xor2(t);
+    if constexpr (L >= 8) t = t + xv_dpp_mirror8(t);
+    if constexpr (L >= 16) t = t + xv_dpp_mirror16(t);
+    return t;
 }
 
 // The one per-token state update (decode, verify and rollback all call this).
-template <int R>
+template <int L, int R>
 __device__ __forceinline__ void xv_gdn_token(float (&s)[R], const float (&kk)[R],
                                              float vj, float at, float bt) {
 #pragma unroll
     for (int r = 0; r < R; ++r) s[r] = at * s[r];
-    const float kv = xv_gdn_dot<R>(s, kk);
+    const float kv = xv_gdn_dot<L, R>(s, kk);
     const float u = bt * (vj - kv);
 #pragma unroll
     for (int r = 0; r < R; ++r) s[r] = __builtin_fmaf(u, kk[r], s[r]);
@@ -98,6 +120,79 @@ struct XvGdnSmem {
     float sst[DK * SP];                              // the state slab [i][W values]
 };
 
+// Stage the rows of tokens 0..n-1 of a launch (the np replayed rows of the previous call
+// first, then this call's) for the W value indices [j0, j0 + W) of value head h of request
+// b into LDS: k and q widened to fp32, v as bf16, a and b.  Every load is issued before any
+// LDS store (straight-line, clamped to token 0), so the staging costs one round trip.
+template <int DK, int W, int NT>
+__device__ __forceinline__ void xv_gdn_stage(const XvGdnArgs A, int b, int h, int g, int j0, int np, int n,
+                                             float (*skq)[2][DK], uint16_t (*sv)[W], float (*sab)[2])
+{
+    if (n <= 0) return;                      // uniform
+    const int tid = threadIdx.x;
+    const int Hk = A.Hk, Hv = A.Hv, dv = A.dv, T = A.T, Tp = A.Tp;
+    constexpr int TM = XV_GDN_TM;
+    constexpr int CH = DK / 8;               // 16-byte chunks per k or q row
+    constexpr int KQ_PER = (TM * 2 * CH + NT - 1) / NT;
+    constexpr int V_PER = (TM * W + NT - 1) / NT;
+    // row t of the launch: replayed row t of the previous call, or row t - np of this one
+    auto kq_src = [&](int t, int which) -> const uint16_t* {
+        if (t < np) return A.kp + (((size_t)b * Tp + t) * Hk + g) * DK;
+        const size_t row = ((size_t)b * T + (t - np)) * Hk + g;
+        return (which == 0 ? A.k : A.q) + row * DK;
+    };
+    xv_u32x4 kq[KQ_PER];
+    uint16_t vv[V_PER];
+    float abv = 0.f;
+#pragma unroll
+    for (int e = 0; e < KQ_PER; ++e) {
+        int idx = tid + e * NT;
+        idx = idx < n * 2 * CH ? idx : 0;
+        const int t = idx / (2 * CH), rem = idx % (2 * CH);
+        const int which = rem / CH, c = rem % CH;   // 0: k, 1: q (a replayed row: k again)
+        kq[e] = xv_load16(kq_src(t, which) + c * 8);
+    }
+#pragma unroll
+    for (int e = 0; e < V_PER; ++e) {
+        int idx = tid + e * NT;
+        idx = idx < n * W ? idx : 0;
+        const int t = idx / W, c = idx % W;
+        const int jj = j0 + c;
+        vv[e] = t < np ? A.vp[(((size_t)b * Tp + t) * Hv + h) * dv + jj]
+                       : A.v[(((size_t)b * T + (t - np)) * Hv + h) * dv + jj];
+    }
+    {
+        const int idx = tid < 2 * n ? tid : 0;
+        const int t = idx >> 1;
+        abv = t < np ? ((idx & 1) ? A.bp : A.ap)[((size_t)b * Tp + t) * Hv + h]
+                     : ((idx & 1) ? A.b : A.a)[((size_t)b * T + (t - np)) * Hv + h];
+    }
+#pragma unroll
+    for (int e = 0; e < KQ_PER; ++e) {
+        const int idx = tid + e * NT;
+        if (idx < n * 2 * CH) {
+            const int t = idx / (2 * CH), rem = idx % (2 * CH);
+            float* dst = &skq[t][rem / CH][(rem % CH) * 8];
+            xv_f32x4 lo4, hi4;
+#pragma unroll
+            for (int w2 = 0; w2 < 2; ++w2) {
+                lo4[2 * w2] = xv_bf16_lo(kq[e][w2]);
+                lo4[2 * w2 + 1] = xv_bf16_hi(kq[e][w2]);
+                hi4[2 * w2] = xv_bf16_lo(kq[e][2 + w2]);
+                hi4[2 * w2 + 1] = xv_bf16_hi(kq[e][2 + w2]);
+            }
+            *reinterpret_cast<xv_f32x4*>(dst) = lo4;
+            *reinterpret_cast<xv_f32x4*>(dst + 4) = hi4;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < V_PER; ++e) {
+        const int idx = tid + e * NT;
+        if (idx < n * W) sv[idx / W][idx % W] = vv[e];
+    }
+    if (tid < 2 * n) sab[tid >> 1][tid & 1] = abv;
+}
+
 // The workgroup (bx, h, b): value indices [bx W, bx W + W) of value head h of
 // request b, W = 32 CPT.  Thread (wave, lane) holds key indices ig R .. ig R + R - 1
 // (ig = lane % 16) of the CPT columns jw + 32 c, jw = 4 wave + lane / 16: each
@@ -108,7 +203,6 @@ __device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, in
 {
     constexpr int NT = XV_GDN_THREADS;
     constexpr int R = DK / XV_GDN_LPJ;
-    constexpr int TM = XV_GDN_TM;
     constexpr int W = XV_GDN_JW * CPT;
     constexpr int SP = W + 1;
 
@@ -150,70 +244,7 @@ __device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, in
     for (int e = 0; e < SPASS; ++e)
         sl[e] = *reinterpret_cast<const xv_f32x4*>(S0 + slab + (size_t)(tid / GPR + e * SROWS) * dv);
 
-    // stage the rows of tokens 0..n-1 (replayed rows first): every load is issued
-    // before any LDS store (straight-line, clamped to token 0), so the staging costs
-    // one round trip
-    constexpr int CH = DK / 8;               // 16-byte chunks per k or q row
-    constexpr int KQ_PER = (TM * 2 * CH + NT - 1) / NT;
-    constexpr int V_PER = (TM * W + NT - 1) / NT;
-    // row t of the launch: replayed row t of the previous call, or row t - np of this one
-    auto kq_src = [&](int t, int which) -> const uint16_t* {
-        if (t < np) return A.kp + (((size_t)b * Tp + t) * Hk + g) * DK;
-        const size_t row = ((size_t)b * T + (t - np)) * Hk + g;
-        return (which == 0 ? A.k : A.q) + row * DK;
-    };
-    if (n > 0) {                             // uniform
-        xv_u32x4 kq[KQ_PER];
-        uint16_t vv[V_PER];
-        float abv = 0.f;
-#pragma unroll
-        for (int e = 0; e < KQ_PER; ++e) {
-            int idx = tid + e * NT;
-            idx = idx < n * 2 * CH ? idx : 0;
-            const int t = idx / (2 * CH), rem = idx % (2 * CH);
-            const int which = rem / CH, c = rem % CH;   // 0: k, 1: q (a replayed row: k again)
-            kq[e] = xv_load16(kq_src(t, which) + c * 8);
-        }
-#pragma unroll
-        for (int e = 0; e < V_PER; ++e) {
-            int idx = tid + e * NT;
-            idx = idx < n * W ? idx : 0;
-            const int t = idx / W, c = idx % W;
-            const int jj = j0 + c;
-            vv[e] = t < np ? A.vp[(((size_t)b * Tp + t) * Hv + h) * dv + jj]
-                           : A.v[(((size_t)b * T + (t - np)) * Hv + h) * dv + jj];
-        }
-        {
-            const int idx = tid < 2 * n ? tid : 0;
-            const int t = idx >> 1;
-            abv = t < np ? ((idx & 1) ? A.bp : A.ap)[((size_t)b * Tp + t) * Hv + h]
-                         : ((idx & 1) ? A.b : A.a)[((size_t)b * T + (t - np)) * Hv + h];
-        }
-#pragma unroll
-        for (int e = 0; e < KQ_PER; ++e) {
-            const int idx = tid + e * NT;
-            if (idx < n * 2 * CH) {
-                const int t = idx / (2 * CH), rem = idx % (2 * CH);
-                float* dst = &sm.skq[t][rem / CH][(rem % CH) * 8];
-                xv_f32x4 lo4, hi4;
-#pragma unroll
-                for (int w2 = 0; w2 < 2; ++w2) {
-                    lo4[2 * w2] = xv_bf16_lo(kq[e][w2]);
-                    lo4[2 * w2 + 1] = xv_bf16_hi(kq[e][w2]);
-                    hi4[2 * w2] = xv_bf16_lo(kq[e][2 + w2]);
-                    hi4[2 * w2 + 1] = xv_bf16_hi(kq[e][2 + w2]);
-                }
-                *reinterpret_cast<xv_f32x4*>(dst) = lo4;
-                *reinterpret_cast<xv_f32x4*>(dst + 4) = hi4;
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < V_PER; ++e) {
-            const int idx = tid + e * NT;
-            if (idx < n * W) sm.sv[idx / W][idx % W] = vv[e];
-        }
-        if (tid < 2 * n) sm.sab[tid >> 1][tid & 1] = abv;
-    }
+    xv_gdn_stage<DK, W, NT>(A, b, h, g, j0, np, n, sm.skq, sm.sv, sm.sab);
 #pragma unroll
     for (int e = 0; e < SPASS; ++e)
 #pragma unroll
@@ -267,11 +298,11 @@ __device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, in
     auto step = [&](int t, const float (&kk)[R], const float (&qq)[R], const float (&vv2)[CPT], float aa, float bb) {
         if (!ROLLBACK && A.S_mid && t == np) store_state(A.S_mid);   // uniform: the kept state
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) xv_gdn_token<R>(s[c], kk, vv2[c], aa, bb);
+        for (int c = 0; c < CPT; ++c) xv_gdn_token<XV_GDN_LPJ, R>(s[c], kk, vv2[c], aa, bb);
         if (!ROLLBACK && t >= np) {
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                const float ot = xv_gdn_dot<R>(s[c], qq);
+                const float ot = xv_gdn_dot<XV_GDN_LPJ, R>(s[c], qq);
                 if (ig == 0) {
                     const size_t oi = (((size_t)b * T + (t - np)) * Hv + h) * dv + j0 + jw + XV_GDN_JW * c;
                     A.o[oi] = xv_f32_to_bf16(ot);
@@ -442,7 +473,7 @@ __device__ __forceinline__ void xv_gdn_prefill_body(const XvGdnArgs A, int bx, i
             bb = sm.sab[buf][t][1];
         };
         auto out = [&](int t, const float (&qq)[R]) {
-            const float ot = xv_gdn_dot<R>(s, qq);
+            const float ot = xv_gdn_dot<XV_GDN_LPJ, R>(s, qq);
             if (ig == 0) {
                 const size_t oi = (((size_t)b * T + t0 + t) * Hv + h) * dv + j0 + jw;
                 A.o[oi] = xv_f32_to_bf16(ot);
@@ -452,11 +483,11 @@ __device__ __forceinline__ void xv_gdn_prefill_body(const XvGdnArgs A, int bx, i
         fetch(0, k0, q0, v0, a0, b0);
         for (int t = 0; t < n; t += 2) {        // uniform; reads on every path, as in verify
             fetch(t + 1 < n ? t + 1 : n - 1, k1, q1, v1, a1, b1);
-            xv_gdn_token<R>(s, k0, v0, a0, b0);
+            xv_gdn_token<XV_GDN_LPJ, R>(s, k0, v0, a0, b0);
             out(t, q0);
             if (t + 1 < n) {
                 fetch(t + 2 < n ? t + 2 : n - 1, k0, q0, v0, a0, b0);
-                xv_gdn_token<R>(s, k1, v1, a1, b1);
+                xv_gdn_token<XV_GDN_LPJ, R>(s, k1, v1, a1, b1);
                 out(t + 1, q1);
             }
         }

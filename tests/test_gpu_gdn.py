@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from bit_exact_speculative_amd.inputs import f32_to_bf16_bits, random_gdn
-from tests.gpu_util import OUT_MAX_REL, STATE_REL_L2, max_rel, rel_l2, same_bits, workload
+from tests.gpu_util import OUT_MAX_REL, OUT_REL_L2, STATE_REL_L2, max_rel, rel_l2, same_bits, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +61,7 @@ def test_gdn_matches_oracle(shape):
     o_ref, S_ref, _ = oracle.gdn(r["q"], r["k"], r["v"], r["a"], r["b"], S0)
     assert rel_l2(S.cpu().numpy(), S_ref) <= STATE_REL_L2
     assert max_rel(o32.cpu().numpy(), o_ref) <= OUT_MAX_REL
+    assert rel_l2(o32.cpu().numpy(), o_ref) <= OUT_REL_L2
     from bit_exact_speculative_amd.layer import host_bits
     assert np.array_equal(host_bits(o), f32_to_bf16_bits(o32.cpu().numpy()))
 
@@ -75,6 +76,59 @@ def test_gdn_real_shapes_vs_oracle():
     o_ref, S_ref, Sall = oracle.gdn(g["q"], g["k"], g["v"], g["a"], g["b"], S0, want_all=True)
     assert rel_l2(S.cpu().numpy(), S_ref) <= STATE_REL_L2
     assert max_rel(o32.cpu().numpy(), o_ref) <= OUT_MAX_REL
+    assert rel_l2(o32.cpu().numpy(), o_ref) <= OUT_REL_L2
+
+
+# Large batches run the kernel with 4 lanes per state column (the library takes it when
+# batch x value heads x dv / 64 reaches twice the CU count: 8 requests of 48 heads at
+# dv = 128 on a 256-CU part); a request alone runs the 16-lane kernel.  The dot's
+# partial tree gives both the same bits.
+@pytest.mark.parametrize("dk,dv,B", [(128, 128, 8), (64, 64, 16), (128, 64, 16), (64, 128, 8)])
+def test_gdn_lane_split_kernels_agree(dk, dv, B):
+    T, Tp, Hk, Hv = 9, 9, 16, 48
+    rng = np.random.default_rng(2000 + dk + dv + B)
+    r = random_gdn(rng, B, T, Hk, Hv, dk, dv)
+    S0 = (rng.standard_normal((B, Hv, dk, dv)) * 0.05).astype(np.float32)
+    d = _dev(r)
+    S_in = torch.from_numpy(S0).cuda()
+    o, o32, S = _verify(d, S_in)
+    # verify after a previous call (every kept count, clamped ones included) and rollback
+    prev = _rows(2100 + dk + dv, B, Tp, Hk, Hv, dk, dv)
+    _, _, Q = _verify(prev, S_in)
+    nk_list = [(-2, 0, 1, 4, Tp, Tp + 5, 7, 2)[i % 8] for i in range(B)]
+    nk = torch.tensor(nk_list, dtype=torch.int32, device="cuda")
+    K, O = torch.full_like(S_in, float("nan")), torch.full_like(S_in, float("nan"))
+    oa = torch.empty_like(o)
+    oa32 = torch.empty_like(o32)
+    _xv().xv_gdn_verify_after(d["q"], d["k"], d["v"], d["a"], d["b"], prev["k"], prev["v"], prev["a"],
+                              prev["b"], nk, S_in, Q, K, O, oa, oa32)
+    Sr = Q.clone()
+    kv = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    _xv().xv_rollback_to_prefix(prev["k"], prev["v"], prev["a"], prev["b"], S_in, Sr, kv, nk)
+    torch.cuda.synchronize()
+    assert kv.tolist() == [min(max(n, 0), Tp) for n in nk_list]
+    o_ref, S_ref, _ = oracle.gdn(r["q"], r["k"], r["v"], r["a"], r["b"], S0)
+    assert rel_l2(S.cpu().numpy(), S_ref) <= STATE_REL_L2
+    assert max_rel(o32.cpu().numpy(), o_ref) <= OUT_MAX_REL
+    assert rel_l2(o32.cpu().numpy(), o_ref) <= OUT_REL_L2
+    for bb in range(B):
+        db = {k: v[bb:bb + 1].contiguous() for k, v in d.items()}
+        pb = {k: v[bb:bb + 1].contiguous() for k, v in prev.items()}
+        s1 = S_in[bb:bb + 1].contiguous()
+        o1, o321, S1 = _verify(db, s1)
+        assert same_bits(o1[0], o[bb]) and same_bits(o321[0], o32[bb]) and same_bits(S1[0], S[bb]), bb
+        K1, O1 = torch.empty_like(s1), torch.empty_like(s1)
+        oa1, oa321 = torch.empty_like(o1), torch.empty_like(o321)
+        _xv().xv_gdn_verify_after(db["q"], db["k"], db["v"], db["a"], db["b"], pb["k"], pb["v"], pb["a"],
+                                  pb["b"], nk[bb:bb + 1].contiguous(), s1, Q[bb:bb + 1].contiguous(), K1, O1,
+                                  oa1, oa321)
+        Sr1 = Q[bb:bb + 1].clone()
+        kv1 = torch.zeros((1,), dtype=torch.int32, device="cuda")
+        _xv().xv_rollback_to_prefix(pb["k"], pb["v"], pb["a"], pb["b"], s1, Sr1, kv1, nk[bb:bb + 1].contiguous())
+        torch.cuda.synchronize()
+        assert same_bits(K1[0], K[bb]) and same_bits(O1[0], O[bb]), bb
+        assert same_bits(oa1[0], oa[bb]) and same_bits(oa321[0], oa32[bb]), bb
+        assert same_bits(Sr1[0], Sr[bb]), bb
 
 
 @pytest.mark.parametrize("T", list(range(1, 17)))
