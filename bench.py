@@ -87,6 +87,9 @@ def parse():
                     help="print only the prefill leg (other_workloads.prefill) as one JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--profile", action="store_true",
+                    help="only the gate and the timed steps (no full-acceptance pass, no extras, no CPU "
+                         "baseline): the launches a profiler run selects by position")
     return ap.parse_args()
 
 
@@ -377,10 +380,12 @@ def main():
         breakdown = {k: round(float(np.median(v)), 2) for k, v in acc.items()}
 
     # the same workload with every draft accepted (rollback keeps S_T as is)
-    for L in layers:
-        L.settle()
-        L.reset()
-    ms_full, _, _ = run_steps(layers, stream, full_steps, full_warmup, keep_all=True)
+    ms_full = None
+    if not args.profile:
+        for L in layers:
+            L.settle()
+            L.reset()
+        ms_full, _, _ = run_steps(layers, stream, full_steps, full_warmup, keep_all=True)
 
     if args.calib_copy_mib > 0:
         with torch.cuda.stream(stream):
@@ -391,7 +396,7 @@ def main():
             del src, dst
 
     extras = None
-    if not args.no_extras and args.workload == "short":
+    if not args.no_extras and not args.profile and args.workload == "short":
         del layers
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
@@ -430,7 +435,7 @@ def main():
     value = wl.B * wl.k_drafts / (ms_per_step * 1e-3) if exact else None
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.profile:
         cpu = cpu_baseline(inp, args.cpu_seconds)
 
     out = {
@@ -460,7 +465,7 @@ def main():
             "rows_kept_per_step": round(float(np.mean(n_keep)) / wl.B, 2) if n_keep else None,
             "compute": "bf16 x bf16 -> fp32 MFMA GEMMs and attention; fp32 GDN state and VALU",
         },
-        "full_accept": {
+        "full_accept": None if ms_full is None else {
             "value": round(wl.B * wl.k_drafts / (ms_full * 1e-3), 1) if exact else None,
             "ms_per_step": round(ms_full, 5),
             "steps": full_steps,
