@@ -42,6 +42,7 @@
 #include "xv_common.h"
 #include "xv_gdn_impl.h"
 #include <math.h>
+#include <mutex>
 
 namespace {
 
@@ -1147,7 +1148,7 @@ int xv_attn_check(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
                   const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* kv_len,
                   const uint16_t* o, const float* o32, void* workspace, size_t workspace_bytes,
                   int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
-                  int* NC, float** ws_acc, float** ws_ml)
+                  int* NC, float** ws_acc, float** ws_ml, bool ws_pointer = true)
 {
     XV_REQUIRE(B >= 0 && T >= 1 && T <= 16 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, XV_ERR_SHAPE);
     XV_REQUIRE(d == 64 || d == 128 || d == 256, XV_ERR_SHAPE);
@@ -1159,7 +1160,7 @@ int xv_attn_check(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
     }
     XV_REQUIRE(scale == scale, XV_ERR_SHAPE);
     if (B == 0) return XV_OK;
-    XV_REQUIRE(q && k_new && v_new && k_cache && v_cache && kv_len && o && workspace, XV_ERR_NULL);
+    XV_REQUIRE(q && k_new && v_new && k_cache && v_cache && kv_len && o && (workspace || !ws_pointer), XV_ERR_NULL);
     XV_REQUIRE(xv_aligned16(q) && xv_aligned16(k_new) && xv_aligned16(v_new) &&
                xv_aligned16(k_cache) && xv_aligned16(v_cache) && xv_aligned(kv_len, 4) &&
                xv_aligned(o, 2) && xv_aligned(o32, 4) && xv_aligned16(workspace), XV_ERR_ALIGN);
@@ -1195,6 +1196,52 @@ int xv_gdn_attn_fused(const XvGdnArgs& ga, int dk, int cpt, int ds, const XvTile
 
 }  // namespace
 
+namespace {
+
+int xv_attn_launch_d(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                     uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
+                     uint16_t* o, float* o32, float* ws_acc, float* ws_ml,
+                     int B, int T, int Hq, int Hkv, int d, int Lmax, int NC, float scale, hipStream_t st)
+{
+    switch (d) {
+        case 64:  return xv_attn_launch<64>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
+                                            ws_ml, B, T, Hq, Hkv, Lmax, NC, scale, st);
+        case 128: return xv_attn_launch<128>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
+                                             ws_ml, B, T, Hq, Hkv, Lmax, NC, scale, st);
+        default:  return xv_attn_launch<256>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
+                                             ws_ml, B, T, Hq, Hkv, Lmax, NC, scale, st);
+    }
+}
+
+// The chunk partials of xv_attn_verify_rows_noalloc: one file-scope array on every GPU
+// the library runs on, held until the process ends.  In host code its name is only a
+// stand-in for the symbol; kernels get the device address that hipGetSymbolAddress
+// returns, looked up once per device (with that device current) and kept.
+constexpr size_t XV_SCRATCH_BYTES = XV_ATTN_NOALLOC_MAX_BYTES;
+static_assert(XV_SCRATCH_BYTES % 256 == 0, "whole 256-byte blocks");
+static __device__ __align__(256) unsigned char xv_scratch[XV_SCRATCH_BYTES];
+
+constexpr int XV_SCRATCH_MAX_DEVICES = 64;
+std::mutex xv_scratch_mu;
+void* xv_scratch_dev[XV_SCRATCH_MAX_DEVICES];
+
+// The current device's copy of xv_scratch (its address, never the host-side name).
+int xv_scratch_address(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= XV_SCRATCH_MAX_DEVICES) return XV_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(xv_scratch_mu);
+    if (!xv_scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(xv_scratch)) != hipSuccess || !p) return XV_ERR_LAUNCH;
+        xv_scratch_dev[dev] = p;
+    }
+    *out = xv_scratch_dev[dev];
+    return XV_OK;
+}
+
+}  // namespace
+
 extern "C" int xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                                    uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                                    uint16_t* o, float* o32, void* workspace, size_t workspace_bytes,
@@ -1207,15 +1254,32 @@ extern "C" int xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, con
     const int s = xv_attn_check(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, workspace, workspace_bytes,
                                 B, T, Hq, Hkv, d, Lmax, scale, &NC, &ws_acc, &ws_ml);
     if (s != XV_OK || B == 0) return s;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    switch (d) {
-        case 64:  return xv_attn_launch<64>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
-                                            ws_ml, B, T, Hq, Hkv, Lmax, NC, scale, st);
-        case 128: return xv_attn_launch<128>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
-                                             ws_ml, B, T, Hq, Hkv, Lmax, NC, scale, st);
-        default:  return xv_attn_launch<256>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
-                                             ws_ml, B, T, Hq, Hkv, Lmax, NC, scale, st);
-    }
+    return xv_attn_launch_d(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc, ws_ml,
+                            B, T, Hq, Hkv, d, Lmax, NC, scale, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int xv_attn_verify_rows_noalloc(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                                           uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
+                                           uint16_t* o, float* o32,
+                                           int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
+                                           void* stream)
+{
+    int NC = 0;
+    float* ws_acc = nullptr;
+    float* ws_ml = nullptr;
+    // every argument and the size first (no device call), then the buffer's address
+    int s = xv_attn_check(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, nullptr, XV_SCRATCH_BYTES,
+                          B, T, Hq, Hkv, d, Lmax, scale, &NC, &ws_acc, &ws_ml, false);
+    if (s != XV_OK || B == 0) return s;
+    void* ws = nullptr;
+    s = xv_scratch_address(&ws);
+    if (s != XV_OK) return s;
+    size_t acc_bytes = 0;
+    (void)xv_attn_ws(B, T, Hq, d, Lmax, &acc_bytes);
+    ws_acc = reinterpret_cast<float*>(ws);
+    ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + acc_bytes);
+    return xv_attn_launch_d(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc, ws_ml,
+                            B, T, Hq, Hkv, d, Lmax, NC, scale, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -34,7 +34,7 @@ _lib.xv_abi_version.argtypes = []
 _lib.xv_status_string.restype = ctypes.c_char_p
 _lib.xv_status_string.argtypes = [_I]
 # the argument lists below are those of this ABI version of include/xv.h
-ABI_VERSION = 4
+ABI_VERSION = 5
 if _lib.xv_abi_version() != ABI_VERSION:
     raise ImportError("libxv.so has ABI version %d, this binding expects %d; rebuild it"
                       % (_lib.xv_abi_version(), ABI_VERSION))
@@ -53,6 +53,9 @@ _lib.xv_attn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.xv_attn_verify_rows.restype = _I
 _lib.xv_attn_verify_rows.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                                      _I, _I, _I, _I, _I, _I, _F, _P]
+_lib.xv_attn_verify_rows_noalloc.restype = _I
+_lib.xv_attn_verify_rows_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P,
+                                             _I, _I, _I, _I, _I, _I, _F, _P]
 _lib.xv_rollback_to_prefix.restype = _I
 _lib.xv_rollback_to_prefix.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
 _lib.xv_greedy_accept.restype = _I
@@ -307,6 +310,24 @@ def xv_attn_verify_rows(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32=None, 
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
         _ptr(o), _ptr(o32), _ptr(workspace), wbytes, B, T, Hq, Hkv, d, Lmax, float(scale),
         _stream(stream)))
+
+
+def xv_attn_verify_rows_noalloc(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32=None, scale=None,
+                                stream=None):
+    """xv_attn_verify_rows with the library's own device buffer for the partials (no workspace)."""
+    B, T, Hq, d = q.shape
+    Hkv = k_new.shape[2]
+    Lmax = k_cache.shape[2]
+    if tuple(k_new.shape) != (B, T, Hkv, d) or tuple(v_new.shape) != (B, T, Hkv, d) or \
+            tuple(k_cache.shape) != (B, Hkv, Lmax, d) or tuple(v_cache.shape) != (B, Hkv, Lmax, d) or \
+            tuple(kv_len.shape) != (B,) or tuple(o.shape) != (B, T, Hq, d) or \
+            (o32 is not None and tuple(o32.shape) != (B, T, Hq, d)):
+        raise ValueError("xv_attn_verify_rows_noalloc: shape mismatch")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    _check("xv_attn_verify_rows_noalloc", _lib.xv_attn_verify_rows_noalloc(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
+        _ptr(o), _ptr(o32), B, T, Hq, Hkv, d, Lmax, float(scale), _stream(stream)))
 
 
 def xv_rollback_to_prefix(k, v, a, b, state_in, state_out, kv_len, n_keep, stream=None):

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define XV_ABI_VERSION 4
+#define XV_ABI_VERSION 5
 
 typedef enum {
     XV_OK = 0,
@@ -216,6 +216,28 @@ int    xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, const uint1
                            uint16_t* o, float* o32, void* workspace, size_t workspace_bytes,
                            int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
                            void* stream);
+
+/*
+ * xv_attn_verify_rows for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, and the same bits, for calls whose workspace
+ * (xv_attn_workspace_bytes(B, T, Hq, d, Lmax)) is at most
+ * XV_ATTN_NOALLOC_MAX_BYTES.  The chunk partials go to a device array inside the
+ * library (one per GPU it runs on, XV_ATTN_NOALLOC_MAX_BYTES each, held until
+ * the process ends); the call allocates nothing.  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (other streams, other host threads)
+ * race and give undefined results, so serialise them.  Nothing in the array needs
+ * to start at zero (each call writes every partial it reads).
+ * Errors: as xv_attn_verify_rows; XV_ERR_WORKSPACE when the call needs more than
+ * XV_ATTN_NOALLOC_MAX_BYTES (checked before any launch); XV_ERR_LAUNCH also when
+ * the runtime cannot give the array's address on the current device.
+ */
+#define XV_ATTN_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+int xv_attn_verify_rows_noalloc(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                                uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
+                                uint16_t* o, float* o32,
+                                int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
+                                void* stream);
 
 /*
  * GDN verify and attention verify rows in one call.  The two are independent

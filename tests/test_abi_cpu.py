@@ -27,7 +27,7 @@ def test_every_header_symbol_is_exported(xv):
                           "xv_attn_chunk_tokens", "xv_abi_version", "xv_status_string",
                           "xv_greedy_accept", "xv_embed_rows", "xv_split_projections",
                           "xv_gemm_small_m_pair", "xv_gdn_verify_after", "xv_gdn_attn_verify",
-                          "xv_attn_prefill", "xv_gdn_prefill"}
+                          "xv_attn_prefill", "xv_gdn_prefill", "xv_attn_verify_rows_noalloc"}
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -37,7 +37,7 @@ def test_every_header_symbol_is_exported(xv):
 
 
 def test_version_and_constants(xv):
-    assert xv.xv_abi_version() == xv.ABI_VERSION == 4
+    assert xv.xv_abi_version() == xv.ABI_VERSION == 5
     assert xv.xv_attn_chunk_tokens() == 256
     lib = xv.lib()
     assert lib.xv_status_string(0) == b"ok"
@@ -179,6 +179,27 @@ def test_attn_argument_errors(xv):
     assert call(q=None) == -1 and call(kvl=None) == -1 and call(ws=None) == -1
     assert call(q=MIS) == -3
     assert call(wsb=need - 4) == -4
+
+
+def test_attn_noalloc_argument_errors(xv):
+    """Every failing check returns before any device call (only error cases are called: a
+    valid call would launch on the fake pointers)."""
+    f = xv.lib().xv_attn_verify_rows_noalloc
+    limit = 32 << 20
+
+    def call(B=1, T=9, Hq=24, Hkv=4, d=256, Lmax=649, q=A, kvl=A, o=A, scale=0.0625):
+        return f(q, A, A, A, A, kvl, o, None, B, T, Hq, Hkv, d, Lmax, scale, None)
+
+    assert call(B=0) == 0
+    assert call(T=17) == -2 and call(Hq=25) == -2 and call(d=96) == -2 and call(Lmax=8) == -2
+    assert call(scale=float("nan")) == -2
+    assert call(q=None) == -1 and call(kvl=None) == -1 and call(o=None) == -1
+    assert call(q=MIS) == -3
+    # the library's array holds 32 MiB: the long context (127,744 positions) does not fit
+    assert xv.xv_attn_workspace_bytes(1, 9, 24, 256, 127744) > limit
+    assert call(Lmax=127744) == -4
+    big_b = limit // xv.xv_attn_workspace_bytes(1, 9, 24, 256, 2560) + 1
+    assert call(B=big_b, Lmax=2560) == -4
 
 
 def test_greedy_argument_errors(xv):
