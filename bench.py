@@ -71,6 +71,35 @@ def traffic_from_profile():
         return None
 
 
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def kernel_bytes(wl, ctx_mean):
+    """Algorithmic bytes per launch of each call of a lazy step (the unit figures of the
+    per-kernel roofline): every weight, state, cache and activation byte the call must
+    read or write once; the attention workspace round trip is traffic, not counted."""
+    B, T, M = wl.B, wl.T, wl.M
+    bf, f4 = 2, 4
+    proj = (wl.N1 + wl.N2) * wl.K * bf + M * wl.K * bf + M * (wl.N1 + wl.N2) * bf
+    state = B * wl.Hv * wl.dk * wl.dv * f4
+    gdn_rows = B * T * (2 * wl.Hk * wl.dk * bf + wl.Hv * wl.dv * bf + 2 * wl.Hv * f4) + B * T * wl.Hv * wl.dv * bf
+    gdn = 3 * state + gdn_rows          # start state in, kept state and S_T out
+    attn = (B * wl.Hkv * (ctx_mean + T) * wl.d * bf * 2 + B * T * wl.Hq * wl.d * bf * 2
+            + B * T * wl.Hkv * wl.d * bf * 2)
+    kh = wl.Hv * wl.dv
+    head = 2 * wl.NH * kh * bf + 2 * M * kh * bf + 2 * M * wl.NH * (bf + f4)
+    greedy = 2 * M * wl.NH * f4
+    return {"projections": proj, "gdn": gdn, "attention": attn, "gdn_attn": gdn + attn, "head": head,
+            "greedy": greedy}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,7 +109,10 @@ def parse():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline time budget")
-    ap.add_argument("--breakdown", action="store_true", help="per-kernel event timing pass")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the per-kernel event pass (per-launch us and GB/s) after the timed steps")
+    ap.add_argument("--roofline-samples", type=int, default=32,
+                    help="launches of the dominant GEMM timed with launch-recorded events (at least 25)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the medium / batch-8 / long workloads reported beside the headline")
     ap.add_argument("--prefill-only", action="store_true",
@@ -351,33 +383,83 @@ def main():
     wl = gen.WORKLOADS[args.workload]
     R = max(1, args.replicas)
     full_steps, full_warmup = max(args.steps // 2, 1), max(args.warmup // 2, 1)
-    Lmax = lmax_for(wl, (args.warmup + args.steps + R - 1) // R, (full_warmup + full_steps + R - 1) // R)
+    n_extra = max(args.roofline_samples, 25, 0 if args.no_breakdown else 50)     # longest post-timing pass
+    Lmax = lmax_for(wl, max(args.warmup + args.steps, n_extra + args.warmup) // R + 1,
+                    (full_warmup + full_steps + R - 1) // R)
     stream = torch.cuda.Stream()
     inp, layers, exact = build_layers(wl, Lmax, R, stream)
 
     # headline: greedy acceptance on the synthetic head (mostly the root row kept, so the
     # rollback recomputes the state), live HIP events on the dominant GEMM's launch
     ms_per_step, gemm_us, wall = run_steps(layers, stream, args.steps, args.warmup, gemm_events=True)
-    gemm_avg_us = float(np.mean(gemm_us))
     n_keep = [int(L.n_keep.sum().item()) for L in layers]
 
+    # more launch-recorded samples of the dominant GEMM (steps exactly like the timed ones,
+    # after the timed region so that the events' own cost stays out of the step time)
+    post_us = []
+    for L in layers:                              # back to the pre-verify caches and lengths
+        L.settle()
+        L.reset()
+    with torch.cuda.stream(stream):
+        n_post = max(args.roofline_samples - len(gemm_us), 25 - len(gemm_us), 0)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_post)]
+        for s_ in range(n_post):
+            layers[(args.warmup + args.steps + s_) % R].lazy_step(evs[s_])
+        torch.cuda.synchronize()
+        post_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
+    all_gemm_us = gemm_us + post_us
+
+    # the streaming-read ceiling of the same bytes: both projection weights of a replica last
+    # read R steps ago, read once by xv_stream_read (launch-recorded events)
+    from bit_exact_speculative_amd import xv
+    read_us = []
+    with torch.cuda.stream(stream):
+        sink = torch.empty((4096,), dtype=torch.int32, device="cuda")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(12)]
+        for i, (e0, e1) in enumerate(evs):
+            L = layers[i % R]
+            xv.xv_stream_read(L.W1, L.W2, sink, e0, e1)
+        torch.cuda.synchronize()
+        read_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
+    read_bytes = (wl.N1 + wl.N2) * wl.K * 2
+    read_med_us = float(np.median(read_us[R:])) if len(read_us) > R else float(np.median(read_us))
+
+    # per-call time of a lazy step: events between the calls of 50 steps queued back to back
     breakdown = None
-    if args.breakdown:
-        names = ["projections_n%d_n%d" % (wl.N1, wl.N2), "gdn_attn_verify", "head_gemms", "greedy_accept"]
+    if not args.no_breakdown:
+        names = ["projections", "gdn_attn", "head", "greedy"]
         acc = {k: [] for k in names}
+        nb = 50
+        for L in layers:
+            L.settle()
+            L.reset()
         with torch.cuda.stream(stream):
-            for s in range(min(args.steps, 50)):
-                L = layers[s % R]
+            rec = []
+            for s_ in range(nb):
+                L = layers[s_ % R]
                 fns = [L.gemms, L.gdn_attn_lazy, L.head_gemms, lambda: L.greedy(count_kv=True)]
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
                 ev[0].record(stream)
                 for i, f in enumerate(fns):
                     f()
                     ev[i + 1].record(stream)
-                torch.cuda.synchronize()
+                rec.append(ev)
+            torch.cuda.synchronize()
+            for ev in rec[2:]:
                 for i, k in enumerate(names):
                     acc[k].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
-        breakdown = {k: round(float(np.median(v)), 2) for k, v in acc.items()}
+        ctx_mean = float(np.mean(inp.L0))
+        kb = kernel_bytes(wl, ctx_mean)
+        breakdown = {}
+        for k in names:
+            us = float(np.median(acc[k]))
+            breakdown[k] = {"us": round(us, 2), "algorithmic_bytes": int(kb[k]),
+                            "GB_s": round(kb[k] / (us * 1e-6) / 1e9, 1)}
+        breakdown["gdn_attn"]["parts_bytes"] = {"gdn": int(kb["gdn"]), "attention": int(kb["attention"])}
+        breakdown["note"] = ("median over 48 steps of events recorded between the calls of a lazy step "
+                             "(gdn_attn: GDN verify after the previous rollback, attention partials with the "
+                             "KV append and the combine); bytes: every weight, state, cache and activation "
+                             "byte the call must move once")
 
     # the same workload with every draft accepted (rollback keeps S_T as is)
     ms_full = None
@@ -431,6 +513,7 @@ def main():
     # algorithmic bytes of the dominant kernel (both weights + activations in once + bf16 out)
     M = wl.M
     gemm_bytes = (wl.N1 + wl.N2) * wl.K * 2 + M * wl.K * 2 + M * (wl.N1 + wl.N2) * 2
+    gemm_avg_us = float(np.mean(all_gemm_us))
     achieved = gemm_bytes / (gemm_avg_us * 1e-6) / 1e9
     value = wl.B * wl.k_drafts / (ms_per_step * 1e-3) if exact else None
 
@@ -463,6 +546,7 @@ def main():
             "layer_replicas": R,
             "bit_exact_verify_equals_decode": bool(exact),
             "rows_kept_per_step": round(float(np.mean(n_keep)) / wl.B, 2) if n_keep else None,
+            "verify_rows_per_s": round(wl.B * wl.T / (ms_per_step * 1e-3), 1),
             "compute": "bf16 x bf16 -> fp32 MFMA GEMMs and attention; fp32 GDN state and VALU",
         },
         "full_accept": None if ms_full is None else {
@@ -482,7 +566,16 @@ def main():
             "traffic": traffic_from_profile(),
             "algorithmic_bytes": gemm_bytes,
             "avg_us": round(gemm_avg_us, 3),
-            "samples": len(gemm_us),
+            "samples": len(all_gemm_us),
+            "samples_in_timed_region": len(gemm_us),
+            "avg_us_in_timed_region": round(float(np.mean(gemm_us)), 3) if gemm_us else None,
+            "read_ceiling": {
+                "kernel": "xv_stream_read of the same two weight buffers, read R steps after their last use",
+                "bytes": read_bytes,
+                "us": round(read_med_us, 3),
+                "GB_s": round(read_bytes / (read_med_us * 1e-6) / 1e9, 1),
+                "achieved_over_ceiling": round(achieved * read_med_us * 1e-6 * 1e9 / read_bytes, 4),
+            },
         },
         "cpu_baseline": cpu,
         "wall_s": round(wall, 4),
@@ -490,7 +583,7 @@ def main():
     if extras is not None:
         out["other_workloads"] = extras
     if breakdown is not None:
-        out["breakdown_us"] = breakdown
+        out["per_call"] = breakdown
     print(json.dumps(out), flush=True)
 
 
@@ -529,7 +622,9 @@ def cpu_baseline(inp, budget_s: float):
     return {"value": round(wl.B * wl.k_drafts / t, 3), "unit": "tok/s", "cores": threads,
             "kind": "oracle",
             "sample": "the full %s step (all rows of every kernel), fp64 C oracle with OpenMP, "
-                      "median of %d runs of %.2f s" % (wl.name, len(times), t)}
+                      "median of %d runs of %.2f s" % (wl.name, len(times), t),
+            "verify_rows_per_s": round(wl.B * wl.T / t, 3),
+            "cpu_model": cpu_model(), "host_cpu_count": os.cpu_count()}
 
 
 if __name__ == "__main__":

@@ -56,6 +56,8 @@ _lib.xv_attn_verify_rows.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
 _lib.xv_attn_verify_rows_noalloc.restype = _I
 _lib.xv_attn_verify_rows_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P,
                                              _I, _I, _I, _I, _I, _I, _F, _P]
+_lib.xv_stream_read.restype = _I
+_lib.xv_stream_read.argtypes = [_P, _S, _P, _S, _P, _I, _P, _P, _P]
 _lib.xv_rollback_to_prefix.restype = _I
 _lib.xv_rollback_to_prefix.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
 _lib.xv_greedy_accept.restype = _I
@@ -328,6 +330,15 @@ def xv_attn_verify_rows_noalloc(q, k_new, v_new, k_cache, v_cache, kv_len, o, o3
     _check("xv_attn_verify_rows_noalloc", _lib.xv_attn_verify_rows_noalloc(
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
         _ptr(o), _ptr(o32), B, T, Hq, Hkv, d, Lmax, float(scale), _stream(stream)))
+
+
+def xv_stream_read(src0, src1, sink, start_event=None, stop_event=None, stream=None):
+    """Read src0 and src1 once (measurement helper); sink: int32/uint32 [workgroups]."""
+    b0 = src0.numel() * src0.element_size()
+    b1 = 0 if src1 is None else src1.numel() * src1.element_size()
+    _check("xv_stream_read", _lib.xv_stream_read(
+        _ptr(src0), b0, _ptr(src1), b1, _ptr(sink), sink.numel(), _stream(stream),
+        _event(start_event), _event(stop_event)))
 
 
 def xv_rollback_to_prefix(k, v, a, b, state_in, state_out, kv_len, n_keep, stream=None):

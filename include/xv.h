@@ -375,6 +375,19 @@ int xv_split_projections(const uint16_t* y1, const uint16_t* y2, int M, int N1, 
                          uint16_t* q, uint16_t* k, uint16_t* v, float* a, float* b,
                          uint16_t* q_attn, uint16_t* k_new, uint16_t* v_new, void* stream);
 
+/*
+ * Measurement helper (not part of the verify step): reads bytes0 bytes of src0
+ * and bytes1 bytes of src1 once with 16-byte loads, each of sink_words workgroups
+ * streaming one contiguous share of their concatenation; workgroup i writes the
+ * XOR of the words it read to sink[i] (uint32 [sink_words], device).  start_event / stop_event
+ * (hipEvent_t or NULL) are recorded at the kernel's own start and end.  It gives
+ * the streaming-read rate of the same bytes a weight-streaming GEMM reads, as the
+ * practical ceiling beside the HBM peak.  bytes0, bytes1 multiples of 16,
+ * src0, src1 [16B]; XV_ERR_SHAPE / XV_ERR_NULL / XV_ERR_ALIGN otherwise.
+ */
+int xv_stream_read(const void* src0, size_t bytes0, const void* src1, size_t bytes1,
+                   uint32_t* sink, int sink_words, void* stream, void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -202,6 +202,16 @@ def test_attn_noalloc_argument_errors(xv):
     assert call(B=big_b, Lmax=2560) == -4
 
 
+def test_stream_read_argument_errors(xv):
+    f = xv.lib().xv_stream_read
+    assert f(A, 0, A, 0, A, 1, None, None, None) == 0                # nothing to read: no launch
+    assert f(A, 1024, A, 1024, A, 0, None, None, None) == -2          # no workgroups
+    assert f(A, 1000, A, 1024, A, 8, None, None, None) == -2          # not whole 16-byte words
+    assert f(None, 1024, A, 1024, A, 8, None, None, None) == -1
+    assert f(A, 1024, A, 1024, None, 8, None, None, None) == -1
+    assert f(MIS, 1024, A, 1024, A, 8, None, None, None) == -3
+
+
 def test_greedy_argument_errors(xv):
     f = xv.lib().xv_greedy_accept
     assert f(A, None, A, 0, 9, 4096, A, A, None, None, None) == 0
