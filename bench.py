@@ -503,8 +503,8 @@ def main():
         try:
             from bit_exact_speculative_amd.diagnose import divergence_margins
             with torch.cuda.stream(stream):
-                extras["divergence"] = divergence_margins("batch8", n_tokens=24, k=8, p_wrong=0.3,
-                                                          seeds=(0, 1, 2))
+                extras["divergence"] = divergence_margins("batch8", n_tokens=512, k=8, p_wrong=0.3,
+                                                          seeds=(0, 1, 2, 3, 4, 5))
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
         except Exception as exc:

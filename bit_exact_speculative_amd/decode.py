@@ -95,13 +95,16 @@ class Decoder:
     """
 
     def __init__(self, inp: Inputs, Lmax: int, device="cuda", S0: Optional[np.ndarray] = None, stream=None,
-                 projections: Optional[Callable] = None, lazy: bool = True):
+                 projections: Optional[Callable] = None, lazy: bool = True, after_split: Optional[Callable] = None):
         """projections(decoder, rows, tokens): an alternative that fills rows.y1 and rows.y2
         from rows.x (for diagnostics of non-exact variants); None = xv_gemm_small_m_pair.
+        after_split(decoder, rows, tokens): diagnostics only, called after the split (it may
+        change the operands of GDN and attention in place, as a non-exact variant would).
         lazy: fold each step's rollback into the next step's GDN launch."""
         wl = inp.wl
         self.wl, self.device, self.stream = wl, device, stream
         self.projections = projections
+        self.after_split = after_split
         if Lmax < inp.k_cache.shape[2]:
             raise ValueError("Lmax below the inputs' cache capacity")
         self.E = _bf16(inp.extra["E"], device)
@@ -168,6 +171,8 @@ class Decoder:
         else:
             self.projections(self, R, tokens)
         xv.xv_split_projections(R.y1, R.y2, R.q, R.k, R.v, R.a, R.b, R.qa, R.kn, R.vn, stream=st)
+        if self.after_split is not None:
+            self.after_split(self, R, tokens)
         if not self.lazy:
             xv.xv_gdn_verify(R.q, R.k, R.v, R.a, R.b, self._S, self._S2, R.o_gdn, None, stream=st)
             xv.xv_attn_verify_rows(R.qa, R.kn, R.vn, self.Kc, self.Vc, self.kv_len, R.o_attn, None, R.ws,
