@@ -45,5 +45,27 @@ def build(out: str = LIB, extra=None, verbose: bool = False) -> str:
     return out
 
 
+def build_sanitized_host_checks(out_dir: str, verbose: bool = False) -> str:
+    """The library's sources and a host program that calls every entry point with arguments
+    breaking one of its checks (csrc/abi_sanitize_main.cpp), as one executable whose host
+    code is built with AddressSanitizer and UndefinedBehaviorSanitizer (device code is
+    built as usual and never runs: every call returns before any launch).  A CPU check of
+    the host-side validation."""
+    out = os.path.join(out_dir, "abi_sanitize")
+    srcs = [os.path.join(CSRC, s) for s in SOURCES] + [os.path.join(CSRC, "abi_sanitize_main.cpp")]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fno-omit-frame-pointer",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all",
+           "-ffp-contract=off", "-fno-fast-math", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include")] + srcs + ["-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout)
+        raise RuntimeError("hipcc failed (exit %d)" % r.returncode)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

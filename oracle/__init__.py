@@ -65,6 +65,18 @@ def compile_c(src: str, out: str) -> str:
     return out
 
 
+def build_sanitized(out_dir: str) -> str:
+    """The oracle and its driver (sanitize_main.c: every function on edge shapes, with
+    property checks) as one program built with AddressSanitizer and UndefinedBehavior-
+    Sanitizer (a CPU check of the oracle's indexing; test infrastructure)."""
+    out = os.path.join(out_dir, "xo_sanitize")
+    cmd = ["gcc", "-O1", "-g", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-Wall", "-Wextra", _SRC, os.path.join(_HERE, "sanitize_main.c"), "-o", out, "-lm"]
+    subprocess.check_call(cmd)
+    return out
+
+
 def _load():
     global _lib
     if _lib is None:
