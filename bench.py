@@ -244,13 +244,15 @@ def extra_workload(name, stream, steps, warmup, R):
     return res
 
 
-def prefill_workload(stream, P=8192, check=256, reps=2, chunk=8192):
+def prefill_workload(stream, P=8192, check=256, reps=2, chunk=8192, tail=16):
     """Prefill of a P-token prompt (one chunk of 8192) on the synthetic layer, short workload
     shapes, appended to its 640 cached tokens: embedding, both projections and the split over
     all rows, GDN and attention over all rows (decode arithmetic per row), the head and the
     first token.
-    Gated on the first `check` prompt tokens giving the state, cache, first token and logprob
-    of one-token decoding bit for bit."""
+    Gated, bit for bit, on (1) the first `check` prompt tokens giving the state, cache, first
+    token and logprob of one-token decoding, and (2) the whole prompt: its prefill against the
+    prefill of all but its last `tail` tokens followed by `tail` one-token steps (the final
+    state, the cache rows of the whole prompt, the first token and its logprob)."""
     import numpy as np
     import torch
     from bit_exact_speculative_amd import inputs as gen
@@ -272,6 +274,22 @@ def prefill_workload(stream, P=8192, check=256, reps=2, chunk=8192):
         same = lambda a, b: torch.equal(a.contiguous().view(torch.int16 if a.element_size() == 2 else torch.int32),
                                         b.contiguous().view(torch.int16 if b.element_size() == 2 else torch.int32))
         exact = all(same(a, b) for a, b in zip(got, want))
+        # the whole prompt: prefill of P - tail tokens then tail one-token steps, against the
+        # prefill of all P
+        dec.restore(snap)
+        dec.prefill(prompt[:, :P - tail], chunk=chunk)
+        for t in range(P - tail, P):
+            R = dec.step(torch.from_numpy(prompt[:, t:t + 1].copy()).to("cuda"))
+        m = int(inp.L0.max()) + P
+        want = (dec.S.clone(), dec.Kc[:, :, :m].clone(), dec.kv_len.clone(), R.ids[:, 0].clone(),
+                R.lp[:, 0].clone())
+        dec.restore(snap)
+        id_f, lp_f = dec.prefill(prompt, chunk=chunk)
+        got = (dec.S, dec.Kc[:, :, :m], dec.kv_len, id_f, lp_f)
+        torch.cuda.synchronize()
+        exact_full = all(same(a, b) for a, b in zip(got, want))
+        del want, got
+        exact = exact and exact_full
         best = None
         for _ in range(reps + 1):                    # the first pass warms up
             dec.restore(snap)
@@ -285,6 +303,7 @@ def prefill_workload(stream, P=8192, check=256, reps=2, chunk=8192):
             best = ms if best is None or ms < best else best
     res = {"prompt_tokens": P, "ctx_before": int(inp.L0[0]), "batch": wl.B, "chunk": chunk,
            "bit_exact_prefill_equals_decode": bool(exact), "check_tokens": check,
+           "check_whole_prompt": "prefill of %d tokens == prefill of %d + %d one-token steps" % (P, P - tail, tail),
            "tok_s": round(wl.B * P / (best * 1e-3), 1) if exact else None, "ms": round(best, 3),
            "note": "one layer; every prompt row kept; first token formed"}
     del dec

@@ -301,3 +301,22 @@ def test_gdn_prefill_equals_verify_steps(T, dk, dv):
         o_r[:, t0:t0 + tt] = os_; o32_r[:, t0:t0 + tt] = o32s
     torch.cuda.synchronize()
     assert same_bits(o, o_r) and same_bits(o32, o32_r) and same_bits(S_out, S)
+
+
+@pytest.mark.parametrize("T,dk,dv", [(300, 128, 128), (1000, 64, 64)])
+def test_gdn_prefill_vs_oracle(T, dk, dv):
+    """xv_gdn_prefill against the fp64 oracle from the same bf16 / fp32 inputs over a long
+    prompt: the state within 1e-4 relative L2, the outputs within the output tolerances."""
+    B, Hk, Hv = 1, 2, 4
+    r, S0 = _case(1700 + T + dk, B, T, Hk, Hv, dk, dv)
+    d = _dev(r)
+    S_in = torch.from_numpy(S0).cuda()
+    S_out = torch.empty_like(S_in)
+    o = torch.empty((B, T, Hv, dv), dtype=torch.bfloat16, device="cuda")
+    o32 = torch.empty((B, T, Hv, dv), dtype=torch.float32, device="cuda")
+    _xv().xv_gdn_prefill(d["q"], d["k"], d["v"], d["a"], d["b"], S_in, S_out, o, o32)
+    torch.cuda.synchronize()
+    o_ref, S_ref, _ = oracle.gdn(r["q"], r["k"], r["v"], r["a"], r["b"], S0)
+    assert rel_l2(S_out.cpu().numpy(), S_ref) <= STATE_REL_L2
+    assert max_rel(o32.cpu().numpy(), o_ref) <= OUT_MAX_REL
+    assert rel_l2(o32.cpu().numpy(), o_ref) <= OUT_REL_L2
