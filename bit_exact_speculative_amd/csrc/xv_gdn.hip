@@ -114,9 +114,9 @@ void xv_gdn4_kernel(XvGdnArgs A)
     xv_gdn_stage<DK, W, XV_GDN4_WAVES * 64>(A, b, h, g, j0, np, n, sm.skq, sm.sv, sm.sab);
     __syncthreads();
 
-    auto store_state = [&](float* __restrict__ dst) {
+    auto store_state = [&](float* __restrict__ dst) {   // streamed out: see the L = 16 helper
 #pragma unroll
-        for (int r = 0; r < R; ++r) dst[sofs + (size_t)r * DV] = s[r];
+        for (int r = 0; r < R; ++r) __builtin_nontemporal_store(s[r], &dst[sofs + (size_t)r * DV]);
     };
     auto read_row = [&](int t, int which, float (&x)[R]) {
 #pragma unroll

@@ -256,7 +256,10 @@ __device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, in
 #pragma unroll
         for (int r = 0; r < R; ++r) s[c][r] = sm.sst[(ig * R + r) * SP + jw + XV_GDN_JW * c];
 
-    // the slab of a state: own slots to LDS, then 16-byte rows out
+    // the slab of a state: own slots to LDS, then 16-byte rows out.  The stores are
+    // non-temporal: no one reads a state in the same step, and dirty state lines left in
+    // the caches would be written back while the next kernel (the weight stream of the
+    // projections) competes for HBM; streamed out, they drain during this kernel.
     auto store_state = [&](float* __restrict__ dst) {
         __syncthreads();                     // every lane is done reading the slab
 #pragma unroll
@@ -269,7 +272,7 @@ __device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, in
             xv_f32x4 out;
 #pragma unroll
             for (int c = 0; c < 4; ++c) out[c] = sm.sst[(tid / GPR + e * SROWS) * SP + (tid % GPR) * 4 + c];
-            *reinterpret_cast<xv_f32x4*>(dst + slab + (size_t)(tid / GPR + e * SROWS) * dv) = out;
+            __builtin_nontemporal_store(out, reinterpret_cast<xv_f32x4*>(dst + slab + (size_t)(tid / GPR + e * SROWS) * dv));
         }
     };
 

@@ -563,14 +563,16 @@ void xv_gemm_big_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
         }
 }
 
-// 2 to 5 row tiles (a batch of requests' verify rows) and K a multiple of 512: the
-// 16 ranges have KSW = K / 512 k-steps each.  A workgroup (16 waves) owns NBW column
-// blocks of one problem of the pair and walks the ranges in order, each in two parts of
-// KSP = KSW / 2 k-steps; a part's x slice (all row tiles) and W slice (the NBW blocks) go
-// through double-buffered LDS, the next part's loads in flight in registers.  Wave w owns
-// the (row tile, column block) tiles i = w, w + 16, ...; per tile one chain per range from
-// zero, folded into the running sum in range order: the bits of every other variant.
-// Each W byte is read once; x is re-read from L2 by every workgroup (it is small).
+// 2 to 5 row tiles (a batch of requests' verify rows) and K = 5120 or 6144: the 16 ranges
+// have KSW = K / 512 k-steps each.  A workgroup (16 waves) owns NBW column blocks of one
+// problem of the pair and walks K in parts of KSP k-steps (KSW / KSP parts per range).  A
+// part's x slice (all row tiles) and W slice (the NBW blocks) are staged by every thread
+// into one of two LDS buffers while the other buffer is consumed (one barrier per part),
+// with the next part's loads in flight in a second register buffer.  Compute wave
+// (t, g) owns row tile t and column blocks g BG .. g BG + BG - 1: per k-step it reads the
+// A fragment once and one B fragment per block.  Per tile one chain per range from zero,
+// folded into the running sum in range order: the bits of every other variant.  Each W
+// byte is read once; x is re-read from L2 by every workgroup (it is small).
 template <int MT, int KSP, int NBW>
 __global__ __launch_bounds__(XV_GEMM_THREADS)
 void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
@@ -580,10 +582,10 @@ void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
     constexpr int GR = KSP * 4;                 // 16-byte granules per row of a part
     constexpr int PITCH = xv_frag_pitch(KSP * 32);  // LDS row pitch (bf16)
     constexpr int GPT = ((XR + WR) * GR + NT - 1) / NT;
-    constexpr int NTILE = MT * NBW;
-    constexpr int PPW = (NTILE + XV_GEMM_WAVES - 1) / XV_GEMM_WAVES;
-    constexpr int NPARTS = XV_GEMM_WAVES * 2;
-    __shared__ __attribute__((aligned(16))) uint16_t sm[(XR + WR) * PITCH];
+    constexpr int BG = NBW < 4 ? NBW : 4;       // column blocks per compute wave
+    constexpr int NBG = (NBW + BG - 1) / BG;
+    static_assert(MT * NBG <= XV_GEMM_WAVES, "one compute wave per (row tile, block group)");
+    __shared__ __attribute__((aligned(16))) uint16_t sm[2][(XR + WR) * PITCH];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -594,6 +596,8 @@ void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
     const uint16_t* __restrict__ x = pp.x[cur];
     const uint16_t* __restrict__ w = pp.w[cur];
     const int N = pp.N[cur];
+    const int NPARTS = (K >> 5) / KSP;
+    const int PPR = NPARTS / XV_GEMM_WAVES;     // parts per K range
 
     // this thread's granules of a part: g = tid + i NT over the x rows, then the W rows;
     // rows past the buffers re-read the last one (their outputs are not stored)
@@ -619,61 +623,69 @@ void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
 #pragma unroll
         for (int i = 0; i < GPT; ++i) reg[i] = xv_load16(src[i] + k0);
     };
-    auto store = [&](const xv_u32x4 (&reg)[GPT]) {
+    auto store = [&](uint16_t* sb, const xv_u32x4 (&reg)[GPT]) {
 #pragma unroll
         for (int i = 0; i < GPT; ++i)
-            if (live[i]) *reinterpret_cast<xv_u32x4*>(&sm[dst[i]]) = reg[i];
+            if (live[i]) *reinterpret_cast<xv_u32x4*>(sb + dst[i]) = reg[i];
     };
 
-    xv_f32x4 acc[PPW], sum[PPW];
+    const int t = wave / NBG, bg = wave % NBG;
+    const bool comp = wave < MT * NBG;          // uniform per wave
+    xv_f32x4 acc[BG], sum[BG];
 #pragma unroll
-    for (int j = 0; j < PPW; ++j) { acc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f}; sum[j] = acc[j]; }
+    for (int j = 0; j < BG; ++j) { acc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f}; sum[j] = acc[j]; }
 
+    // register buffer u & 1 holds part p + 1 when part p (u = p % 2) is consumed
     xv_u32x4 r0[GPT], r1[GPT];
     load(r0, 0);
     load(r1, 1);
-    for (int part = 0; part < NPARTS; part += 2) {
+    store(sm[0], r0);
+    load(r0, 2);
+    __syncthreads();
+    for (int p0 = 0; p0 < NPARTS; p0 += 2) {    // NPARTS is even (16 ranges)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {           // parts of range part / 2: even in r0, odd in r1
-            xv_u32x4 (&reg)[GPT] = h ? r1 : r0;
-            __syncthreads();                    // LDS free
-            store(reg);
-            load(reg, part + h + 2);            // this buffer's next part (past the end: a re-read)
-            __syncthreads();
+        for (int u = 0; u < 2; ++u) {
+            const int p = p0 + u;
+            xv_u32x4 (&rn)[GPT] = u ? r0 : r1;  // holds part p + 1
+            if (p + 1 < NPARTS) {               // stage part p + 1; its buffer was freed by the last barrier
+                store(sm[u ^ 1], rn);
+                load(rn, p + 3);
+            }
+            if (comp) {
+                const uint16_t* ap = sm[u] + (t * 16 + lr) * PITCH + lg * 8;
+                const uint16_t* bp = sm[u] + (XR + bg * BG * 16 + lr) * PITCH + lg * 8;
 #pragma unroll
-            for (int j = 0; j < PPW; ++j) {
-                const int ti = wave + j * XV_GEMM_WAVES;
-                if (ti < NTILE) {               // uniform per wave
-                    const int t = ti / NBW, bk = ti % NBW;
-                    const uint16_t* ap = &sm[(t * 16 + lr) * PITCH + lg * 8];
-                    const uint16_t* bp = &sm[(XR + bk * 16 + lr) * PITCH + lg * 8];
+                for (int kk = 0; kk < KSP; ++kk) {
+                    const xv_u32x4 a = *reinterpret_cast<const xv_u32x4*>(ap + kk * 32);
 #pragma unroll
-                    for (int kk = 0; kk < KSP; ++kk)
-                        acc[j] = xv_mfma16x16x32(*reinterpret_cast<const xv_u32x4*>(ap + kk * 32),
-                                                 *reinterpret_cast<const xv_u32x4*>(bp + kk * 32), acc[j]);
+                    for (int j = 0; j < BG; ++j)
+                        if (bg * BG + j < NBW)  // uniform
+                            acc[j] = xv_mfma16x16x32(a, *reinterpret_cast<const xv_u32x4*>(bp + j * 16 * PITCH + kk * 32), acc[j]);
+                }
+                if ((p + 1) % PPR == 0) {       // a range complete: folded in order
+#pragma unroll
+                    for (int j = 0; j < BG; ++j) {
+                        sum[j] = p + 1 == PPR ? acc[j] : sum[j] + acc[j];
+                        acc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
                 }
             }
-        }
-#pragma unroll
-        for (int j = 0; j < PPW; ++j) {         // range part / 2 complete: folded in order
-            sum[j] = part == 0 ? acc[j] : sum[j] + acc[j];
-            acc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+            __syncthreads();                    // part p consumed, part p + 1 staged
         }
     }
+    if (!comp) return;
 #pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-        const int ti = wave + j * XV_GEMM_WAVES;
-        if (ti >= NTILE) continue;
-        const int t = ti / NBW, bk = ti % NBW;
+    for (int j = 0; j < BG; ++j) {
+        const int bk = bg * BG + j;
         const int col = (blk0 + bk) * 16 + lr;
-        if (col >= N) continue;
+        if (bk >= NBW || col >= N) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = t * 16 + 4 * lg + i;
+        for (int e = 0; e < 4; ++e) {
+            const int row = t * 16 + 4 * lg + e;
             if (row < M) {
                 const size_t o = (size_t)row * N + col;
-                pp.y[cur][o] = xv_f32_to_bf16(sum[j][i]);
-                if (pp.y32[cur]) pp.y32[cur][o] = sum[j][i];
+                pp.y[cur][o] = xv_f32_to_bf16(sum[j][e]);
+                if (pp.y32[cur]) pp.y32[cur][o] = sum[j][e];
             }
         }
     }
@@ -817,7 +829,8 @@ void xv_gemm_launch_xstream(const uint16_t* x, const uint16_t* w, uint16_t* y, f
 
 // Launch of the 2..5-row-tile kernel for one or two problems (N[1] = 0: one): the fewest
 // column blocks per workgroup that still fit every workgroup on the chip at once (one
-// per CU), so that no CU runs a second round.
+// per CU), so that no CU runs a second round; at most 7 (two LDS buffers of 5 row tiles
+// and 7 blocks at K = 6144 fill the 160 KB of LDS).
 bool xv_gemm_mt_fits(int mt, int K) { return mt >= 2 && mt <= XV_GEMM_MT_MAX && (K == 5120 || K == 6144); }
 
 template <int MT, int KSP>
@@ -827,7 +840,7 @@ void xv_gemm_launch_mt_n(const XvGemmPair& pp, int M, int K, const XvLaunch& lc)
     const int cus = xv_gemm_grid(1 << 30);
     auto wgs = [&](int nbw) { return (nb0 + nbw - 1) / nbw + (nb1 + nbw - 1) / nbw; };
     int nbw = 1;
-    while (nbw < 8 && wgs(nbw) > cus) ++nbw;
+    while (nbw < 7 && wgs(nbw) > cus) ++nbw;
 #define XV_MT_LAUNCH(NBWV)                                                                                   \
     hipExtLaunchKernelGGL((xv_gemm_mt_kernel<MT, KSP, NBWV>), dim3(wgs(NBWV)), dim3(XV_GEMM_THREADS), 0,    \
                           lc.st, lc.e0, lc.e1, 0, pp, M, K, (nb0 + NBWV - 1) / NBWV)
@@ -838,8 +851,7 @@ void xv_gemm_launch_mt_n(const XvGemmPair& pp, int M, int K, const XvLaunch& lc)
         case 4: XV_MT_LAUNCH(4); break;
         case 5: XV_MT_LAUNCH(5); break;
         case 6: XV_MT_LAUNCH(6); break;
-        case 7: XV_MT_LAUNCH(7); break;
-        default: XV_MT_LAUNCH(8); break;
+        default: XV_MT_LAUNCH(7); break;
     }
 #undef XV_MT_LAUNCH
 }
