@@ -68,11 +68,16 @@ void xv_gdn_prefill_kernel(XvGdnArgs A)
 constexpr int XV_GDN4_WAVES = 4;
 constexpr int XV_GDN4_W = XV_GDN4_WAVES * 16;
 
+constexpr int XV_GDN4_SP = XV_GDN4_W;       // row pitch (floats) of the outgoing half slab (unpadded: three
+                                            // workgroups per CU must still fit their LDS)
+static_assert(XV_GDN4_W == 64 && XV_GDN4_WAVES * 64 == 256, "the slab store: 16 threads per 64-float row");
+
 template <int DK>
 struct XvGdn4Smem {
     float skq[XV_GDN_TM][2][DK];
     uint16_t sv[XV_GDN_TM][XV_GDN4_W];
     float sab[XV_GDN_TM][2];
+    float sst[DK / 2][XV_GDN4_SP];           // half of the state slab on its way out
 };
 
 template <int DK, int DV, bool ROLLBACK>
@@ -114,9 +119,25 @@ void xv_gdn4_kernel(XvGdnArgs A)
     xv_gdn_stage<DK, W, XV_GDN4_WAVES * 64>(A, b, h, g, j0, np, n, sm.skq, sm.sv, sm.sab);
     __syncthreads();
 
-    auto store_state = [&](float* __restrict__ dst) {   // streamed out: see the L = 16 helper
+    // the slab out in two halves of dk / 2 rows through LDS, so that every store is a
+    // 16-byte piece of a 256-byte row run (non-temporal: see the L = 16 helper)
+    const size_t slab0 = (size_t)(b * Hv + h) * DK * DV + j0;
+    auto store_state = [&](float* __restrict__ dst) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) __builtin_nontemporal_store(s[r], &dst[sofs + (size_t)r * DV]);
+        for (int half = 0; half < 2; ++half) {
+            __syncthreads();                     // the half buffer is free
+            if ((ig >> 1) == half) {             // lanes holding rows half dk/2 ..
+#pragma unroll
+                for (int r = 0; r < R; ++r) sm.sst[(ig & 1) * R + r][jw] = s[r];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < DK / 32; ++e) {
+                const int rr = (tid >> 4) + 16 * e, cc = (tid & 15) * 4;
+                const xv_f32x4 out = *reinterpret_cast<const xv_f32x4*>(&sm.sst[rr][cc]);
+                __builtin_nontemporal_store(out, reinterpret_cast<xv_f32x4*>(dst + slab0 + (size_t)(half * (DK / 2) + rr) * DV + cc));
+            }
+        }
     };
     auto read_row = [&](int t, int which, float (&x)[R]) {
 #pragma unroll
