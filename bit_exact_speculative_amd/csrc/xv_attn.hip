@@ -27,16 +27,17 @@
 //     xv_attn_partial_wide_kernel (workgroup per chunk, KV head and request,
 //     wave per 16-pair tile), xv_attn_partial_tile_kernel (workgroup per
 //     16-pair tile as well, the waves splitting its positions and output dims)
-//     and xv_attn_partial_stream_kernel (persistent workgroups streaming the
-//     chunks of one KV head and request, for long contexts); the host picks by
+//     and xv_attn_stream_kernel (persistent workgroups streaming the chunk
+//     groups of one KV head and request, for long contexts); the host picks by
 //     grid size only, so a pair's bits never depend on it.
-//  2. xv_attn_combine_kernel, grid (query head, row, request): in ascending
-//     chunk order with the running maximum M (-inf at first), M' = max(M, m_c),
-//     a = 2^(M - M'), b = 2^(m_c - M'), L = fma(L, a, l_c b),
-//     A = fma(A, a, acc_c b); o = A / L, stored as bf16 (nearest even) and
-//     optionally fp32.  Its two load schedules (by the capacity's chunk count)
-//     fold the same operations in the same order, and the prefill kernel folds
-//     its chunks with them too.
+//  2. xv_attn_combine_kernel, grid (query head, row, request): the row's chunk
+//     partials folded in two levels (xv_fold_factors): the chunks of each group
+//     of XV_ATTN_G = 8 in ascending order with a running maximum, then the group
+//     partials in ascending order the same way; o = A / L, stored as bf16
+//     (nearest even) and optionally fp32.  The streaming kernel folds each
+//     group's chunks itself and hands the combine group partials; the prefill
+//     mode of the same kernel folds both levels for its rows.  Every form uses
+//     the same operations in the same order.
 // Masked positions are excluded by index, never by value, and positions at or
 // past L0 + T are never read (their LDS slots are zero-filled).
 #include "xv_common.h"
@@ -48,7 +49,8 @@ namespace {
 
 constexpr int XV_ATTN_C = 256;      // chunk length (positions), fixed for every call
 constexpr int XV_ATTN_WAVES = 8;    // waves of a partial-kernel workgroup
-constexpr int XV_ATTN_MAX_NC = 5120;   // chunks of the capacity (1,310,720 positions), at most
+constexpr int XV_ATTN_MAX_NC = 4608;   // chunks of the capacity (1,179,648 positions), at most
+constexpr int XV_ATTN_G = 8;           // chunks per group of the two-level fold (2048 positions)
 constexpr int XV_ATTN_WIDE_MIN = 128; // (chunk, KV head, request) workgroups from which the wide kernel runs
 constexpr int XV_ATTN_STREAM_MIN = 1024; // ... and from which the persistent streaming kernel runs (about 4 chunks per CU)
 constexpr int XV_COMBINE_U = 24;    // chunks per block of combine loads kept in flight
@@ -60,9 +62,11 @@ constexpr double XV_FUSE_ONE_COL = 1.0;
 constexpr double XV_FUSE_TWO_COL = 1.0;
 // the combine's per-chunk LDS arrays are padded to whole pairs of load blocks
 __host__ __device__ constexpr int xv_combine_pad(int nc) { return (nc + 2 * XV_COMBINE_U - 1) / (2 * XV_COMBINE_U) * (2 * XV_COMBINE_U); }
-// the long-row combine's LDS (three per-chunk arrays and a scan array of 256) stays within
-// the 64 KB of dynamic LDS a launch gets without an attribute
-static_assert(sizeof(float) * (3 * xv_combine_pad(XV_ATTN_MAX_NC) + 256) <= 65536, "combine LDS");
+// the long-row combine's LDS (three per-chunk arrays, three per-group arrays and a scan
+// array of 256) stays within the 64 KB of dynamic LDS a launch gets without an attribute
+static_assert(sizeof(float) * (3 * xv_combine_pad(XV_ATTN_MAX_NC) + 3 * xv_combine_pad(XV_ATTN_MAX_NC) / XV_ATTN_G + 256)
+              <= 65536, "combine LDS");
+static_assert((2 * XV_COMBINE_U) % XV_ATTN_G == 0, "a block of combine loads holds whole groups");
 
 // LDS layouts (16-byte granules, XOR-swizzled so that both the cooperative
 // stores and the MFMA fragment reads spread over the banks):
@@ -164,6 +168,24 @@ struct XvChunk {
         }
     }
 };
+
+// The fold of partials (m, l, acc) in ascending order, with the running maximum M (-inf
+// before the first):
+//     M' = max(M, m),  a = 2^(M - M'),  b = 2^(m - M')
+//     L  = fma(L, a, l b),  A = fma(A, a, acc b),  M = M'
+// The first partial gives a = 0, b = 1: A = acc, L = l exactly.  A row's output is folded
+// in two levels: the chunk partials of each group of XV_ATTN_G consecutive chunks (chunks
+// 8 g .. 8 g + 7 that the row sees) are folded into a group partial (M_g, L_g, A_g), and the
+// group partials, in ascending group order, into (M, L, A); o = A / L.  A row with at most
+// one group gets exactly the fold of its chunks.  Whoever forms a level (the streaming
+// kernel in registers, the combine from chunk or group partials, the prefill kernel) uses
+// these operations in this order, so the bits never depend on who did.
+__device__ __forceinline__ void xv_fold_factors(float& M, float m, float& a, float& b) {
+    const float Mn = fmaxf(M, m);
+    a = __builtin_amdgcn_exp2f(M - Mn);
+    b = __builtin_amdgcn_exp2f(m - Mn);
+    M = Mn;
+}
 
 // The P.V MFMA operands for k-slot group kk (chunk positions kk*32 ..): k-slot e
 // of lane group lg is position kk*32 + 4*lg + e (e < 4) or kk*32 + 16 + 4*lg + (e - 4),
@@ -340,19 +362,27 @@ void xv_attn_partial_wide_kernel(const uint16_t* __restrict__ q, const uint16_t*
     xv_store_acc<D, DB>(ws_acc, oacc, 0, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
 }
 
-// Long contexts: persistent workgroups stream the chunks of one (KV head,
-// request), chunk c = x, x + WPG, x + 2 WPG, ... for workgroup x.  A chunk goes
-// through LDS as four 64-position sub-blocks of K, then four of V^T; each
-// sub-block is a "unit" loaded into registers four units ahead of its use (the
-// next chunk's K units while the current chunk's V is consumed), so HBM loads
-// overlap the MFMA work instead of alternating with it.  Up to 4 tiles of 16
-// pairs; waves t and t + 4 share tile t: wave t forms the score blocks of the
-// chunk's first half, wave t + 4 those of the second, the chunk max meets
-// through LDS, the probabilities go through LDS in fp32, wave t forms the
-// chunk sum, and each wave forms half of the tile's P.V output dims.  Every
-// chain and ordered sum is the wide kernel's, so the bits are the same.
+// Streaming partial kernel, two modes over one body.
+//  * Verify (PF = false, long contexts): persistent workgroups stream the chunk groups of
+//    one (KV head, request), group x, x + WPG, x + 2 WPG, ... for workgroup x, the chunks
+//    of a group in ascending order, and write one partial per group (the group's chunks
+//    folded in registers).
+//  * Prefill (PF = true): one workgroup per (request, KV head, block
+//    of 64 (row, head) pairs) walks every chunk its last row sees, in ascending order, and
+//    folds both levels in registers into the rows' outputs (no workspace).
+// A chunk goes through LDS as four 64-position sub-blocks of K, then four of V^T; each
+// sub-block is a "unit" loaded into registers four units ahead of its use (the next
+// chunk's K units while the current chunk's V is consumed), so HBM loads overlap the MFMA
+// work instead of alternating with it.  Up to 4 tiles of 16 pairs; waves t and t + 4
+// share tile t: wave t forms the score blocks of the chunk's first half, wave t + 4 those
+// of the second, the chunk max meets through LDS, the probabilities go through LDS in
+// fp32, both waves form the chunk sum, and each wave forms half of the tile's P.V output
+// dims.  Every chain and ordered sum of a chunk is the wide kernel's, and the folds are the
+// combine's operations in its order (xv_fold_factors), so every bit is the same as the
+// per-chunk kernels followed by the combine.
 constexpr int XV_ATTN_SB = 64;              // positions per streamed sub-block
-constexpr int XV_ATTN_UNITS = 4;            // units in flight
+constexpr int XV_ATTN_UNITS = 2;            // units in flight
+constexpr int XV_ATTN_SPAIRS = 64;          // (row, head) pairs per workgroup: 4 tiles of 16
 
 template <int D>
 struct XvUnit {
@@ -363,15 +393,30 @@ struct XvUnit {
     xv_u32x4 r[4];                                                  // K: KG granules; V: one 4 x 8 tile
 };
 
-template <int D>
+struct XvStreamArgs {
+    const uint16_t* q;          // [B][R][Hq][D]
+    const uint16_t* k_new;      // verify: the rows to append, [B][R][Hkv][D]
+    const uint16_t* v_new;
+    uint16_t* k_cache;          // [B][Hkv][Lmax][D]
+    uint16_t* v_cache;
+    const int32_t* kv_len;      // [B]: cached length before the R rows
+    float* ws_acc;              // verify: group partials [B][R][Hq][NG][D]
+    float* ws_ml;               // verify: [B][R][Hq][NG][2] (max, sum)
+    uint16_t* o;                // prefill: outputs [B][R][Hq][D]
+    float* o32;
+    int R;                      // rows per request (verify T, prefill P)
+    int Hq, Hkv, Lmax;
+    int NG;                     // verify: groups of the capacity (the partials' stride)
+    int NRB;                    // prefill: pair blocks per (request, KV head)
+    float scale_log2;
+};
+
+template <int D, bool PF>
 __global__ __launch_bounds__(XV_ATTN_WAVES * 64)
-void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
-                                   const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_cache,
-                                   uint16_t* __restrict__ v_cache, const int32_t* __restrict__ kv_len,
-                                   float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-                                   int T, int Hq, int Hkv, int Lmax, int NC, float scale_log2)
+void xv_attn_stream_kernel(const XvStreamArgs A)
 {
     constexpr int C = XV_ATTN_C;
+    constexpr int G = XV_ATTN_G;
     constexpr int SB = XV_ATTN_SB;
     constexpr int NSB = C / SB;                 // sub-blocks per chunk
     constexpr int NT = XV_ATTN_WAVES * 64;
@@ -385,7 +430,7 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
     constexpr int PP = C + 4;                   // probability row pitch (floats)
     constexpr int KG = XvUnit<D>::KG;
     constexpr int VT4 = XvUnit<D>::VT4;
-    static_assert(NSB == 4 && NU == 4 && XV_ATTN_WAVES == 8, "four units per chunk half, two waves per tile");
+    static_assert(NSB == 4 && 8 % NU == 0 && XV_ATTN_WAVES == 8, "four units per chunk half, unit k in buffer k % NU, two waves per tile");
     constexpr int QP = D + 8;                   // query row pitch in LDS (bf16)
     // one slot holds the current K sub-block [pos][d] or V^T sub-block [d][pos] (swizzled):
     // the K units of a chunk are consumed before its V units, and those before the next K
@@ -396,16 +441,42 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
     xv_u32x4* const sk = skv;
     xv_u32x4* const svt = skv;
 
-    const int WPG = gridDim.x;
-    const int g = blockIdx.y, b = blockIdx.z;
-    const int Hg = Hq / Hkv;
-    const int P = Hg * T;
-    int L0 = kv_len[b];
-    L0 = L0 < 0 ? 0 : (L0 > Lmax - T ? Lmax - T : L0);
-    const int Lend = L0 + T;
-    const int nchunks = (Lend + C - 1) / C;
-    if ((int)blockIdx.x >= nchunks) return;     // uniform
-    const int nitems = (nchunks - 1 - (int)blockIdx.x) / WPG + 1;
+    const int Hg = A.Hq / A.Hkv;
+    const int Ptot = Hg * A.R;
+    int g, b, pair0;
+    if constexpr (PF) {                         // the blocks of the last rows (most chunks) first
+        const int bid = (int)blockIdx.x;
+        pair0 = (A.NRB - 1 - bid % A.NRB) * XV_ATTN_SPAIRS;
+        g = (bid / A.NRB) % A.Hkv;
+        b = bid / (A.NRB * A.Hkv);
+    } else {
+        pair0 = 0;
+        g = blockIdx.y;
+        b = blockIdx.z;
+    }
+    int L0 = A.kv_len[b];
+    L0 = L0 < 0 ? 0 : (L0 > A.Lmax - A.R ? A.Lmax - A.R : L0);
+    const int Lend = L0 + A.R;
+    const int npair = Ptot - pair0 < XV_ATTN_SPAIRS ? Ptot - pair0 : XV_ATTN_SPAIRS;
+    const int first_len = L0 + pair0 / Hg + 1;                  // every pair sees the positions below
+    const int nchunks = (L0 + (pair0 + npair - 1) / Hg + 1 + C - 1) / C;   // chunks the last row sees
+    // this workgroup's chunks, in order: verify, the chunks of its groups; prefill, all of them
+    int x = 0, WPG = 1, nitems;
+    if constexpr (PF) {
+        nitems = nchunks;
+    } else {
+        x = (int)blockIdx.x;
+        WPG = (int)gridDim.x;
+        const int ngr = (nchunks + G - 1) / G;
+        if (x >= ngr) return;                   // uniform
+        const int ngw = (ngr - 1 - x) / WPG + 1;
+        const int lastg = x + (ngw - 1) * WPG;
+        nitems = (ngw - 1) * G + (nchunks - lastg * G < G ? nchunks - lastg * G : G);
+    }
+    auto chunk_of = [&](int it) __attribute__((always_inline)) -> int {
+        if constexpr (PF) return it;
+        else return (x + (it / G) * WPG) * G + it % G;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -413,44 +484,64 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
     const int tile = wave & 3;
     const int dh = wave >> 2;                   // which half of the score blocks and of the dims
     const int lr = lane & 15, lg = lane >> 4;
-    const bool tile_on = tile < (P + 15) / 16;
-    const int pair = tile * 16 + lr;
-    const bool pair_ok = pair < P;
-    const int pr = pair_ok ? pair / Hg : 0;
-    const int ph = g * Hg + (pair_ok ? pair % Hg : 0);
+    const bool tile_on = tile * 16 < npair;
+    const int tlast = pair0 + (tile * 16 + 15 < npair ? tile * 16 + 15 : npair - 1);
+    const int tlen = L0 + tlast / Hg + 1;       // the tile's last row: it sees a chunk when that row does
+    const int pl = tile * 16 + lr;              // this lane's score pair
+    const bool pair_ok = pl < npair;
+    const int gp = pair0 + (pair_ok ? pl : 0);
+    const int pr = gp / Hg;
+    const int ph = g * Hg + gp % Hg;
     const int plen = L0 + pr + 1;
-    const size_t kvbase = ((size_t)b * Hkv + g) * Lmax;
-    const size_t newbase = ((size_t)b * T * Hkv + g) * D;
-    const int newstride = Hkv * D;
+    // this lane's output pairs tile*16 + 4 lg + i
+    int orow[4], ohead[4];
+    bool ook[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ol = tile * 16 + 4 * lg + i;
+        ook[i] = ol < npair;
+        const int og = pair0 + (ook[i] ? ol : 0);
+        orow[i] = og / Hg;
+        ohead[i] = g * Hg + og % Hg;
+    }
+    const size_t kvbase = ((size_t)b * A.Hkv + g) * A.Lmax;
+    const size_t newbase = ((size_t)b * A.R * A.Hkv + g) * D;
+    const int newstride = A.Hkv * D;
     const xv_u32x4 zero = {0u, 0u, 0u, 0u};
     float* tp = sp + tile * 16 * PP;
 
+    // verify: positions before L0 from the cache, the new rows from k_new / v_new; prefill:
+    // every visible position from the cache (its rows were appended first).  Past L0 + R:
+    // cache position 0 (never used, zeroed before it reaches LDS).
     auto src = [&](const uint16_t* cache, const uint16_t* fresh, int pos) __attribute__((always_inline)) -> const uint16_t* {
-        if (pos < L0) return cache + (kvbase + pos) * D;
-        if (pos < Lend) return fresh + newbase + (size_t)(pos - L0) * newstride;
-        return cache + kvbase * D;
+        if constexpr (PF) {
+            (void)fresh;
+            return cache + (kvbase + (pos < Lend ? pos : 0)) * D;
+        } else {
+            if (pos < L0) return cache + (kvbase + pos) * D;
+            if (pos < Lend) return fresh + newbase + (size_t)(pos - L0) * newstride;
+            return cache + kvbase * D;
+        }
     };
     // unit u of item it: u < 4 is K sub-block u, u >= 4 is V sub-block u - 4
     auto load_unit = [&](XvUnit<D>& U, int it, int u) __attribute__((always_inline)) {
-        const int c0 = ((int)blockIdx.x + it * WPG) * C;
-        const int p0 = c0 + (u & 3) * SB;
+        const int p0 = chunk_of(it) * C + (u & 3) * SB;
         if (u < 4) {
 #pragma unroll
             for (int i = 0; i < KG; ++i) {
                 const int idx = tid + i * NT;
-                U.r[i] = xv_load16(src(k_cache, k_new, p0 + idx / (D / 8)) + (idx % (D / 8)) * 8);
+                U.r[i] = xv_load16(src(A.k_cache, A.k_new, p0 + idx / (D / 8)) + (idx % (D / 8)) * 8);
             }
         } else {
             const int vt = tid < VT4 ? tid : VT4 - 1;
             const int pg4 = vt / (D / 8), dg = vt % (D / 8);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) U.r[e] = xv_load16(src(v_cache, v_new, p0 + pg4 * 4 + e) + dg * 8);
+            for (int e = 0; e < 4; ++e) U.r[e] = xv_load16(src(A.v_cache, A.v_new, p0 + pg4 * 4 + e) + dg * 8);
         }
     };
-    // into LDS: positions past L0 + T zeroed, new rows appended to the cache
+    // into LDS: positions past L0 + R zeroed; verify appends the new rows to the cache
     auto store_unit = [&](XvUnit<D>& U, int it, int u) __attribute__((always_inline)) {
-        const int c0 = ((int)blockIdx.x + it * WPG) * C;
-        const int p0 = c0 + (u & 3) * SB;
+        const int p0 = chunk_of(it) * C + (u & 3) * SB;
         if (u < 4) {
 #pragma unroll
             for (int i = 0; i < KG; ++i) {
@@ -458,7 +549,7 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
                 const int lp = idx / (D / 8), cc = idx % (D / 8);
                 const int pos = p0 + lp;
                 if (pos >= Lend) U.r[i] = zero;
-                else if (pos >= L0) xv_store16(k_cache + (kvbase + pos) * D + cc * 8, U.r[i]);
+                else if (!PF && pos >= L0) xv_store16(A.k_cache + (kvbase + pos) * D + cc * 8, U.r[i]);
                 sk[xv_k_granule<D>(lp, cc)] = U.r[i];
             }
         } else if (tid < VT4) {
@@ -468,7 +559,7 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
             for (int e = 0; e < 4; ++e) {
                 const int pos = p0 + pg4 * 4 + e;
                 if (pos >= Lend) U.r[e] = zero;
-                else if (pos >= L0) xv_store16(v_cache + (kvbase + pos) * D + dg * 8, U.r[e]);
+                else if (!PF && pos >= L0) xv_store16(A.v_cache + (kvbase + pos) * D + dg * 8, U.r[e]);
             }
             char* vb = reinterpret_cast<char*>(svt);
 #pragma unroll
@@ -485,7 +576,7 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
         }
     };
 
-    // the 4 tiles' queries into LDS (rows of pairs past P are zero); visible after the first barrier
+    // the 4 tiles' queries into LDS (rows of pairs past the block are zero); visible after the first barrier
     {
         constexpr int QG = (4 * 16 * (D / 8) + NT - 1) / NT;
 #pragma unroll
@@ -493,9 +584,9 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
             const int e = tid + i * NT;
             if (e < 4 * 16 * (D / 8)) {
                 const int p2 = e / (D / 8), cc = e % (D / 8);
-                const int p2c = p2 < P ? p2 : 0;
-                const xv_u32x4 v = xv_load16(q + (((size_t)b * T + p2c / Hg) * Hq + g * Hg + p2c % Hg) * D + cc * 8);
-                *reinterpret_cast<xv_u32x4*>(sq + p2 * QP + cc * 8) = p2 < P ? v : zero;
+                const int gq = pair0 + (p2 < npair ? p2 : 0);
+                const xv_u32x4 v = xv_load16(A.q + (((size_t)b * A.R + gq / Hg) * A.Hq + g * Hg + gq % Hg) * D + cc * 8);
+                *reinterpret_cast<xv_u32x4*>(sq + p2 * QP + cc * 8) = p2 < npair ? v : zero;
             }
         }
     }
@@ -504,11 +595,21 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
 #pragma unroll
     for (int u = 0; u < NU; ++u) load_unit(ub[u], 0, u);
 
+    // the fold of the current group (and, prefill, of the groups so far): per score pair
+    // (lane lr) the running maximum and sum, per output pair 4 lg + i the P.V sums
+    float Mg = -INFINITY, Lg = 0.f, Mt = -INFINITY, Lt = 0.f;
+    xv_f32x4 Ag[DBH], At[PF ? DBH : 1];
+#pragma unroll
+    for (int j = 0; j < DBH; ++j) Ag[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < (PF ? DBH : 1); ++j) At[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+
     for (int it = 0; it < nitems; ++it) {
-        const int c = (int)blockIdx.x + it * WPG;
+        const int c = chunk_of(it);
         const int c0 = c * C;
-        const bool full = c0 + C <= L0 + 1;
+        const bool full = c0 + C <= first_len;
         const bool more = it + 1 < nitems;
+        const bool tsee = tile_on && c0 < tlen;     // uniform per wave
         // the unit four steps ahead of unit u: in this item, else the next item's (past the
         // last item: the same K unit of this item again, a cache hit, so the unit kind stays fixed)
         auto ahead = [&](XvUnit<D>& U, int u) __attribute__((always_inline)) {
@@ -523,10 +624,10 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
 #pragma unroll
         for (int u = 0; u < NSB; ++u) {
             __syncthreads();                    // K slot free
-            store_unit(ub[u], it, u);
-            ahead(ub[u], u);
+            store_unit(ub[u % NU], it, u);
+            ahead(ub[u % NU], u);
             __syncthreads();
-            if (tile_on && (u * CBS) / CBH == dh) {     // uniform per wave
+            if (tsee && (u * CBS) / CBH == dh) {        // uniform per wave
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {       // per score block one chain over ks
                     const xv_u32x4 qk = *reinterpret_cast<const xv_u32x4*>(qrow + ks * 32);
@@ -547,7 +648,7 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
         for (int j = 0; j < CBH; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float sv = sc[j][i] * scale_log2;
+                const float sv = sc[j][i] * A.scale_log2;
                 sc[j][i] = sv;
                 if (full || c0 + (cb0 + j) * 16 + 4 * lg + i < plen) mw = fmaxf(mw, sv);
             }
@@ -557,7 +658,7 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
         __syncthreads();                        // also: the previous chunk's P.V is done with sp
         float m = fmaxf(smax[tile][lr], smax[tile + 4][lr]);
         if (!pair_ok) m = 0.f;
-        if (tile_on) {
+        if (tsee) {
 #pragma unroll
             for (int j = 0; j < CBH; ++j) {
                 xv_f32x4 pv;
@@ -578,10 +679,10 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
 #pragma unroll
         for (int u = NSB; u < 2 * NSB; ++u) {
             __syncthreads();                    // V^T slot free; P of both waves visible
-            store_unit(ub[u - NSB], it, u);
-            ahead(ub[u - NSB], u);
+            store_unit(ub[u % NU], it, u);
+            ahead(ub[u % NU], u);
             __syncthreads();
-            if (u == NSB && tile_on && dh == 0) {       // chunk sum, in the wide kernel's order
+            if (u == NSB && tsee) {             // chunk sum, in the wide kernel's order (both waves)
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
                     const xv_f32x4 pv = *reinterpret_cast<const xv_f32x4*>(tp + lr * PP + cb * 16 + 4 * lg);
@@ -591,7 +692,7 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
                 l = l + __shfl_xor(l, 16);
                 l = l + __shfl_xor(l, 32);
             }
-            if (tile_on) {
+            if (tsee) {
 #pragma unroll
                 for (int k2 = 0; k2 < SB / 32; ++k2) {
                     const int kk = (u - NSB) * (SB / 32) + k2;
@@ -621,14 +722,76 @@ void xv_attn_partial_stream_kernel(const uint16_t* __restrict__ q, const uint16_
             }
         }
 
-        // ---- the chunk partials of pairs that see this chunk ----
-        if (tile_on) {
-            if (dh == 0 && lg == 0 && pair_ok && plen > c0) {
-                const size_t idx = (((size_t)b * T + pr) * Hq + ph) * NC + c;
-                __builtin_nontemporal_store(m, &ws_ml[idx * 2 + 0]);
-                __builtin_nontemporal_store(l, &ws_ml[idx * 2 + 1]);
+        // ---- the chunk folded into its group, for the pairs that see it ----
+        if (tsee) {
+            float Mn = Mg, fa, fb;
+            xv_fold_factors(Mn, m, fa, fb);
+            const bool sees = pair_ok && plen > c0;
+            if (sees) {
+                Mg = Mn;
+                Lg = __builtin_fmaf(Lg, fa, l * fb);
             }
-            xv_store_acc<D, DBH>(ws_acc, oacc, dh * DBH, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai = __shfl(fa, 4 * lg + i), bi = __shfl(fb, 4 * lg + i);
+                const bool si = ook[i] && L0 + orow[i] + 1 > c0;
+#pragma unroll
+                for (int j = 0; j < DBH; ++j)
+                    Ag[j][i] = si ? __builtin_fmaf(Ag[j][i], ai, oacc[j][i] * bi) : Ag[j][i];
+            }
+        }
+
+        // ---- a group complete: verify writes its partial, prefill folds it into the total ----
+        if (c % G == G - 1 || !more) {
+            const int gi = c / G;
+            const int gc0 = gi * G * C;
+            if constexpr (!PF) {
+                if (tile_on) {
+                    if (lg == 0 && dh == 0 && pair_ok && plen > gc0) {
+                        const size_t idx = (((size_t)b * A.R + pr) * A.Hq + ph) * A.NG + gi;
+                        __builtin_nontemporal_store(Mg, &A.ws_ml[idx * 2 + 0]);
+                        __builtin_nontemporal_store(Lg, &A.ws_ml[idx * 2 + 1]);
+                    }
+                    xv_store_acc<D, DBH>(A.ws_acc, Ag, dh * DBH, tile, lr, lg, Ptot, Hg, g, b, A.R, A.Hq, A.NG, gi, L0, gc0);
+                }
+            } else {
+                if (tile_on) {
+                    float Mn = Mt, fa, fb;
+                    xv_fold_factors(Mn, Mg, fa, fb);
+                    if (pair_ok && plen > gc0) {
+                        Mt = Mn;
+                        Lt = __builtin_fmaf(Lt, fa, Lg * fb);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float ai = __shfl(fa, 4 * lg + i), bi = __shfl(fb, 4 * lg + i);
+                        const bool si = ook[i] && L0 + orow[i] + 1 > gc0;
+#pragma unroll
+                        for (int j = 0; j < DBH; ++j)
+                            At[j][i] = si ? __builtin_fmaf(At[j][i], ai, Ag[j][i] * bi) : At[j][i];
+                    }
+                }
+            }
+            Mg = -INFINITY;
+            Lg = 0.f;
+#pragma unroll
+            for (int j = 0; j < DBH; ++j) Ag[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    if constexpr (PF) {                         // o = A / L: this wave's half of the dims
+        if (!tile_on) return;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float Li = __shfl(Lt, 4 * lg + i);
+            if (!ook[i]) continue;
+            const size_t ob = (((size_t)b * A.R + orow[i]) * A.Hq + ohead[i]) * D + lr;
+#pragma unroll
+            for (int j = 0; j < DBH; ++j) {
+                const float ov = At[j][i] / Li;
+                A.o[ob + (dh * DBH + j) * 16] = xv_f32_to_bf16(ov);
+                if (A.o32) A.o32[ob + (dh * DBH + j) * 16] = ov;
+            }
         }
     }
 }
@@ -837,122 +1000,179 @@ void xv_attn_partial_tile_kernel(XvTileArgs A)
     xv_attn_tile_body<D, DS>(A, (int)blockIdx.x, sm);
 }
 
-// The fold of a row's chunk partials, in ascending chunk order, with the running
-// maximum M (-inf before the first chunk):
-//     M' = max(M, m_c),  a_c = 2^(M - M'),  b_c = 2^(m_c - M')
-//     L  = fma(L, a_c, l_c b_c),  A = fma(A, a_c, acc_c b_c),  M = M'
-// and o = A / L.  The first chunk gives a = 0, b = 1: A = acc_0, L = l_0 exactly.  The
-// prefill kernel folds its chunks with these operations in the same order.
-__device__ __forceinline__ void xv_fold_factors(float& M, float m, float& a, float& b) {
-    const float Mn = fmaxf(M, m);
-    a = __builtin_amdgcn_exp2f(M - Mn);
-    b = __builtin_amdgcn_exp2f(m - Mn);
-    M = Mn;
-}
-
-// DEEP = false: every thread walks the chain itself, forming the same factors from the
-// (m, l) it loads (rows of a few chunks; the first XV_COMBINE_PRE chunks' loads are issued
-// together).  DEEP = true (long rows): the factors are formed once per chunk in LDS (the
-// running maximum as a prefix maximum: a per-thread segment, then a scan over the
-// segments; a maximum is exact in any order), and the chain's loads run in two
-// alternating register blocks of XV_COMBINE_U chunks, one block in flight while the
-// other is summed.  Both fold the same operations in the same order.
-template <int D, bool DEEP>
+// One workgroup per (query head, row, request), one thread per output dim.  GRP: the
+// partials are group partials (the streaming kernel), folded in ascending group order; else
+// chunk partials, folded in two levels (each group's chunks, then the groups).  NI: the
+// partials' stride per row (chunks or groups of the capacity).
+// DEEP = false: every thread walks the chain itself, forming the factors from the (m, l) it
+// loads (rows of a few items; the first XV_COMBINE_PRE items' loads are issued together).
+// DEEP = true (long rows): the factors are formed once per item in LDS (a running maximum
+// as a prefix maximum: a per-thread segment, then a scan over the segments; a maximum is
+// exact in any order), and the chain's loads run in two alternating register blocks of
+// XV_COMBINE_U chunk (or group) partials, one block in flight while the other is summed.
+// All four forms fold the same operations in the same order.
+template <int D, bool DEEP, bool GRP>
 __global__ __launch_bounds__(D)
 void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
                             const int32_t* __restrict__ kv_len, uint16_t* __restrict__ o,
-                            float* __restrict__ o32, int T, int Hq, int Lmax, int NC)
+                            float* __restrict__ o32, int T, int Hq, int Lmax, int NI)
 {
-    extern __shared__ __attribute__((aligned(16))) float sh[];   // [NCP] a, [NCP] b, [NCP] l b, [D] scan
-    const int NCP = DEEP ? xv_combine_pad(NC) : NC;
+    constexpr int G = XV_ATTN_G;
+    // LDS: [NIP] a, [NIP] b, [NIP] l b (GRP) or l (chunks), then (chunks) [NIP / G] x 3 group
+    // factors, then [D] scan
+    extern __shared__ __attribute__((aligned(16))) float sh[];
+    const int NIP = DEEP ? xv_combine_pad(NI) : NI;
     float* sa = sh;
-    float* sb = sh + NCP;
-    float* slb = sh + 2 * NCP;
-    float* sred = sh + 3 * NCP;
+    float* sb = sh + NIP;
+    float* sl = sh + 2 * NIP;
+    float* ga = sh + 3 * NIP;
+    float* gb = ga + (GRP ? 0 : NIP / G);
+    float* gl = gb + (GRP ? 0 : NIP / G);
+    float* sred = gl + (GRP ? 0 : NIP / G);
     const int h = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     int L0 = kv_len[b];
     L0 = L0 < 0 ? 0 : (L0 > Lmax - T ? Lmax - T : L0);
     const int len = L0 + r + 1;
     const int nc = (len + XV_ATTN_C - 1) / XV_ATTN_C;
-    const size_t base = (((size_t)b * T + r) * Hq + h) * NC;
+    const int ng = (nc + G - 1) / G;
+    const int ni = GRP ? ng : nc;               // this row's partials
+    const size_t base = (((size_t)b * T + r) * Hq + h) * NI;
     const float* ap = ws_acc + base * D + tid;
     float L = 0.f, A = 0.f;
 
     if constexpr (!DEEP) {
-        // indices past nc re-read chunk nc - 1 and are not used
+        // indices past ni re-read item ni - 1 and are not used
         constexpr int PRE = XV_COMBINE_PRE;
+        static_assert(PRE == G, "the first block of loads is one group of chunks");
         float pacc[PRE];
         float2 pml[PRE];
+        auto load_block = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < PRE; ++u) {
-            const int cc = u < nc ? u : nc - 1;
-            pacc[u] = ap[(size_t)cc * D];
-            pml[u] = *reinterpret_cast<const float2*>(ws_ml + (base + cc) * 2);
-        }
-        float M = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < PRE; ++u) {
-            if (u < nc) {
-                float fa, fb;
-                xv_fold_factors(M, pml[u].x, fa, fb);
-                L = __builtin_fmaf(L, fa, pml[u].y * fb);
-                A = __builtin_fmaf(A, fa, pacc[u] * fb);
-            }
-        }
-#pragma unroll 4
-        for (int cc = PRE; cc < nc; ++cc) {
-            const float2 ml = *reinterpret_cast<const float2*>(ws_ml + (base + cc) * 2);
-            float fa, fb;
-            xv_fold_factors(M, ml.x, fa, fb);
-            L = __builtin_fmaf(L, fa, ml.y * fb);
-            A = __builtin_fmaf(A, fa, ap[(size_t)cc * D] * fb);
-        }
-        (void)sa; (void)sb; (void)slb; (void)sred;
-    } else {
-        constexpr int U = XV_COMBINE_U;
-        // indices past nc re-read chunk nc - 1 and are not summed
-        auto fetch = [&](float (&buf)[U], int c0) __attribute__((always_inline)) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int cn = c0 + u;
-                buf[u] = __builtin_nontemporal_load(&ap[(size_t)(cn < nc ? cn : nc - 1) * D]);
+            for (int u = 0; u < PRE; ++u) {
+                const int cc = i0 + u < ni ? i0 + u : ni - 1;
+                pacc[u] = ap[(size_t)cc * D];
+                pml[u] = *reinterpret_cast<const float2*>(ws_ml + (base + cc) * 2);
             }
         };
-        // a, b and l b four at a time from LDS (padded to a multiple of 2 U); a chunk past
-        // nc leaves both sums as they are
-        auto fold = [&](const float (&buf)[U], int c0) __attribute__((always_inline)) {
-            float fa[U], fb[U], lb[U];
+        float M = -INFINITY;
+        if constexpr (GRP) {
+            load_block(0);
 #pragma unroll
-            for (int u = 0; u < U; u += 4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(sa + c0 + u);
-                const float4 b4 = *reinterpret_cast<const float4*>(sb + c0 + u);
-                const float4 l4 = *reinterpret_cast<const float4*>(slb + c0 + u);
-                fa[u] = a4.x; fa[u + 1] = a4.y; fa[u + 2] = a4.z; fa[u + 3] = a4.w;
-                fb[u] = b4.x; fb[u + 1] = b4.y; fb[u + 2] = b4.z; fb[u + 3] = b4.w;
-                lb[u] = l4.x; lb[u + 1] = l4.y; lb[u + 2] = l4.z; lb[u + 3] = l4.w;
+            for (int u = 0; u < PRE; ++u) {
+                if (u < ni) {
+                    float fa, fb;
+                    xv_fold_factors(M, pml[u].x, fa, fb);
+                    L = __builtin_fmaf(L, fa, pml[u].y * fb);
+                    A = __builtin_fmaf(A, fa, pacc[u] * fb);
+                }
             }
+#pragma unroll 4
+            for (int cc = PRE; cc < ni; ++cc) {
+                const float2 ml = *reinterpret_cast<const float2*>(ws_ml + (base + cc) * 2);
+                float fa, fb;
+                xv_fold_factors(M, ml.x, fa, fb);
+                L = __builtin_fmaf(L, fa, ml.y * fb);
+                A = __builtin_fmaf(A, fa, ap[(size_t)cc * D] * fb);
+            }
+        } else {
+            for (int gi = 0; gi < ng; ++gi) {   // a group's chunk loads issued together
+                load_block(gi * G);
+                float Mg = -INFINITY, Lg = 0.f, Ag = 0.f;
+#pragma unroll
+                for (int u = 0; u < G; ++u) {
+                    if (gi * G + u < nc) {
+                        float fa, fb;
+                        xv_fold_factors(Mg, pml[u].x, fa, fb);
+                        Lg = __builtin_fmaf(Lg, fa, pml[u].y * fb);
+                        Ag = __builtin_fmaf(Ag, fa, pacc[u] * fb);
+                    }
+                }
+                float fa, fb;
+                xv_fold_factors(M, Mg, fa, fb);
+                L = __builtin_fmaf(L, fa, Lg * fb);
+                A = __builtin_fmaf(A, fa, Ag * fb);
+            }
+        }
+        (void)sa; (void)sb; (void)sl; (void)ga; (void)gb; (void)gl; (void)sred;
+    } else {
+        constexpr int U = XV_COMBINE_U;
+        // indices past ni re-read item ni - 1 and are not summed
+        auto fetch = [&](float (&buf)[U], int i0) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const bool in = c0 + u < nc;
-                const float L2 = __builtin_fmaf(L, fa[u], lb[u]);
-                const float A2 = __builtin_fmaf(A, fa[u], buf[u] * fb[u]);
-                L = in ? L2 : L;
-                A = in ? A2 : A;
+                const int cn = i0 + u;
+                buf[u] = __builtin_nontemporal_load(&ap[(size_t)(cn < ni ? cn : ni - 1) * D]);
+            }
+        };
+        // GRP: each item folds into the row's sums with its factors; chunks: each chunk
+        // folds into its group's sum, and a group into the row's sums after its last chunk
+        // (a block of loads holds whole groups); an item past ni leaves the sums as they are
+        auto fold = [&](const float (&buf)[U], int i0) __attribute__((always_inline)) {
+            if constexpr (GRP) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const bool in = i0 + u < ni;
+                    const float L2 = __builtin_fmaf(L, sa[i0 + u], sl[i0 + u]);
+                    const float A2 = __builtin_fmaf(A, sa[i0 + u], buf[u] * sb[i0 + u]);
+                    L = in ? L2 : L;
+                    A = in ? A2 : A;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < U / G; ++q) {
+                    float Ag = 0.f;
+#pragma unroll
+                    for (int u = 0; u < G; ++u) {
+                        const int c = i0 + q * G + u;
+                        const float A2 = __builtin_fmaf(Ag, sa[c], buf[q * G + u] * sb[c]);
+                        Ag = c < nc ? A2 : Ag;
+                    }
+                    const int gi = (i0 + q * G) / G;
+                    const bool in = gi < ng;
+                    const float L2 = __builtin_fmaf(L, ga[gi], gl[gi]);
+                    const float A2 = __builtin_fmaf(A, ga[gi], Ag * gb[gi]);
+                    L = in ? L2 : L;
+                    A = in ? A2 : A;
+                }
             }
         };
         float ba[U], bbuf[U];
         fetch(ba, 0);                           // independent of the factors
-        // (m, l) of this thread's segment of chunks: m into sa, l into slb; the segment's
-        // maximum into the scan array
-        const int seg = (nc + D - 1) / D;
-        const int s0 = tid * seg, s1 = s0 + seg < nc ? s0 + seg : nc;
         float mseg = -INFINITY;
-        for (int cc = s0; cc < s1; ++cc) {
-            const float2 ml = *reinterpret_cast<const float2*>(ws_ml + (base + cc) * 2);
-            sa[cc] = ml.x;
-            slb[cc] = ml.y;
-            mseg = fmaxf(mseg, ml.x);
+        int s0, s1;                             // this thread's segment of items (chunks: whole groups)
+        if constexpr (GRP) {
+            // (m, l) of the segment's groups: m into sa, l into sl; the segment's maximum
+            const int seg = (ni + D - 1) / D;
+            s0 = tid * seg;
+            s1 = s0 + seg < ni ? s0 + seg : ni;
+            for (int cc = s0; cc < s1; ++cc) {
+                const float2 ml = *reinterpret_cast<const float2*>(ws_ml + (base + cc) * 2);
+                sa[cc] = ml.x;
+                sl[cc] = ml.y;
+                mseg = fmaxf(mseg, ml.x);
+            }
+        } else {
+            // the segment's groups: each chunk's factors within its group (into sa, sb), the
+            // group's (M_g, L_g) (into ga, gl); the segment's maximum over the M_g
+            const int seg = (ng + D - 1) / D;
+            s0 = tid * seg;
+            s1 = s0 + seg < ng ? s0 + seg : ng;
+            for (int gi = s0; gi < s1; ++gi) {
+                float Mg = -INFINITY, Lg = 0.f;
+                const int c1 = (gi + 1) * G < nc ? (gi + 1) * G : nc;
+                for (int cc = gi * G; cc < c1; ++cc) {
+                    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + (base + cc) * 2);
+                    float fa, fb;
+                    xv_fold_factors(Mg, ml.x, fa, fb);
+                    sa[cc] = fa;
+                    sb[cc] = fb;
+                    Lg = __builtin_fmaf(Lg, fa, ml.y * fb);
+                }
+                ga[gi] = Mg;
+                gl[gi] = Lg;
+                mseg = fmaxf(mseg, Mg);
+            }
         }
         sred[tid] = mseg;
         __syncthreads();
@@ -963,21 +1183,28 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
             sred[tid] = v;
             __syncthreads();
         }
-        // the factors of this thread's chunks, from the maximum of every earlier chunk
+        // the row-level factors of this thread's items, from the maximum of every earlier one
         float M = tid > 0 ? sred[tid - 1] : -INFINITY;
         for (int cc = s0; cc < s1; ++cc) {
             float fa, fb;
-            xv_fold_factors(M, sa[cc], fa, fb);
-            sa[cc] = fa;
-            sb[cc] = fb;
-            slb[cc] = slb[cc] * fb;
+            if constexpr (GRP) {
+                xv_fold_factors(M, sa[cc], fa, fb);
+                sa[cc] = fa;
+                sb[cc] = fb;
+                sl[cc] = sl[cc] * fb;
+            } else {
+                xv_fold_factors(M, ga[cc], fa, fb);
+                ga[cc] = fa;
+                gb[cc] = fb;
+                gl[cc] = gl[cc] * fb;
+            }
         }
         __syncthreads();
-        for (int c0 = 0; c0 < nc; c0 += 2 * U) {
-            fetch(bbuf, c0 + U);
-            fold(ba, c0);
-            fetch(ba, c0 + 2 * U);
-            fold(bbuf, c0 + U);
+        for (int i0 = 0; i0 < ni; i0 += 2 * U) {
+            fetch(bbuf, i0 + U);
+            fold(ba, i0);
+            fetch(ba, i0 + 2 * U);
+            fold(bbuf, i0 + U);
         }
     }
     const float ov = A / L;
@@ -1043,13 +1270,15 @@ int xv_attn_partials(const uint16_t* q, const uint16_t* k_new, const uint16_t* v
     const float scale_log2 = xv_scale_log2(scale);
     const XvAttnKind kind = xv_attn_kind<D>(B, T, Hq, Hkv, NC);
     if (kind == XV_ATTN_STREAM) {
-        // about one persistent workgroup per CU, spread evenly over the (KV head, request) groups
+        // about one persistent workgroup per CU, spread evenly over the (KV head, request)
+        // groups; each walks whole chunk groups and writes one partial per group
         const long long groups = (long long)B * Hkv;
+        const int NG = (NC + XV_ATTN_G - 1) / XV_ATTN_G;
         long long wpg = xv_cu_count() / groups;
-        wpg = wpg < 1 ? 1 : (wpg > NC ? NC : wpg);
-        hipLaunchKernelGGL(xv_attn_partial_stream_kernel<D>, dim3((int)wpg, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st,
-                           q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
-                           T, Hq, Hkv, Lmax, NC, scale_log2);
+        wpg = wpg < 1 ? 1 : (wpg > NG ? NG : wpg);
+        const XvStreamArgs sa{q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml, nullptr, nullptr,
+                              T, Hq, Hkv, Lmax, NG, 0, scale_log2};
+        hipLaunchKernelGGL((xv_attn_stream_kernel<D, false>), dim3((int)wpg, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st, sa);
     } else if (kind == XV_ATTN_WIDE) {
         hipLaunchKernelGGL(xv_attn_partial_wide_kernel<D>, dim3(NC, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st,
                            q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
@@ -1068,17 +1297,31 @@ int xv_attn_partials(const uint16_t* q, const uint16_t* k_new, const uint16_t* v
     return xv_launch_status();
 }
 
+// The combine for chunk partials (grp = false: the tile and wide kernels) or group partials
+// (grp = true: the streaming kernel); NC is the capacity's chunk count.
 template <int D>
 int xv_attn_combine(const float* ws_acc, const float* ws_ml, const int32_t* kv_len, uint16_t* o, float* o32,
-                    int B, int T, int Hq, int Lmax, int NC, hipStream_t st)
+                    int B, int T, int Hq, int Lmax, int NC, bool grp, hipStream_t st)
 {
     (void)hipGetLastError();
-    if (NC > 2 * XV_COMBINE_U) {
-        const size_t shmem = sizeof(float) * (3 * (size_t)xv_combine_pad(NC) + D);
-        hipLaunchKernelGGL((xv_attn_combine_kernel<D, true>), dim3(Hq, T, B), dim3(D), shmem, st,
+    const dim3 grid(Hq, T, B), block(D);
+    if (grp) {
+        const int NG = (NC + XV_ATTN_G - 1) / XV_ATTN_G;
+        if (NG > XV_COMBINE_PRE) {
+            const size_t shmem = sizeof(float) * (3 * (size_t)xv_combine_pad(NG) + D);
+            hipLaunchKernelGGL((xv_attn_combine_kernel<D, true, true>), grid, block, shmem, st,
+                               ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NG);
+        } else {
+            hipLaunchKernelGGL((xv_attn_combine_kernel<D, false, true>), grid, block, 0, st,
+                               ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NG);
+        }
+    } else if (NC > 2 * XV_COMBINE_U) {
+        const size_t pad = xv_combine_pad(NC);
+        const size_t shmem = sizeof(float) * (3 * pad + 3 * (pad / XV_ATTN_G) + D);
+        hipLaunchKernelGGL((xv_attn_combine_kernel<D, true, false>), grid, block, shmem, st,
                            ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC);
     } else {
-        hipLaunchKernelGGL((xv_attn_combine_kernel<D, false>), dim3(Hq, T, B), dim3(D), 0, st,
+        hipLaunchKernelGGL((xv_attn_combine_kernel<D, false, false>), grid, block, 0, st,
                            ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC);
     }
     return xv_launch_status();
@@ -1093,7 +1336,8 @@ int xv_attn_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_n
     const int s = xv_attn_partials<D>(q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
                                       B, T, Hq, Hkv, Lmax, NC, scale, st);
     if (s != XV_OK) return s;
-    return xv_attn_combine<D>(ws_acc, ws_ml, kv_len, o, o32, B, T, Hq, Lmax, NC, st);
+    const bool grp = xv_attn_kind<D>(B, T, Hq, Hkv, NC) == XV_ATTN_STREAM;
+    return xv_attn_combine<D>(ws_acc, ws_ml, kv_len, o, o32, B, T, Hq, Lmax, NC, grp, st);
 }
 
 // GDN and the attention partials side by side in one launch: workgroups
@@ -1352,9 +1596,9 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
     }
     if (s != XV_OK) return s;
     switch (d) {
-        case 64:  return xv_attn_combine<64>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, st);
-        case 128: return xv_attn_combine<128>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, st);
-        default:  return xv_attn_combine<256>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, st);
+        case 64:  return xv_attn_combine<64>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, false, st);
+        case 128: return xv_attn_combine<128>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, false, st);
+        default:  return xv_attn_combine<256>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, false, st);
     }
 }
 
@@ -1363,9 +1607,6 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr int XV_PF_WAVES = 8;                  // 16-pair tiles per workgroup
-constexpr int XV_PF_THREADS = XV_PF_WAVES * 64;
-constexpr int XV_PF_PAIRS = XV_PF_WAVES * 16;
 
 // kv_len[b] += n (one thread per request), after the kernels that read it.
 __global__ void xv_kv_advance_kernel(int32_t* __restrict__ kv_len, int B, int n)
@@ -1394,239 +1635,9 @@ __global__ void xv_kv_append_kernel(const uint16_t* __restrict__ k_new, const ui
     xv_store16(v_cache + dst, xv_load16(v_new + src));
 }
 
-// Workgroup (request b, KV head g, block of 128 (row, head) pairs, pair = row * Hg + h as in
-// the verify kernels); wave w owns pairs 16 w .. 16 w + 15 of the block.  Row r (position
-// L0 + r) gets exactly the decode row's numbers: per chunk c (absolute boundaries) the
-// scores (the same MFMA chain, K as A and q as B), the exact chunk maximum m_c, the
-// probabilities 2^(s - m_c), their sum in the partial kernels' order and the P.V chains
-// (p as bf16 hi + lo, k-steps ascending), each folded at once into the row's sums with the
-// combine's operations (xv_fold_factors: the running maximum, ascending c), o = A / L; one
-// pass over the chunks, everything in registers.  Every chunk is read from the cache (the
-// rows were appended first); positions at or past L0 + P are zero-filled in LDS and never
-// visible.
-template <int D>
-__global__ __launch_bounds__(XV_PF_THREADS)
-void xv_attn_prefill_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-                            const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ kv_len,
-                            uint16_t* __restrict__ o, float* __restrict__ o32,
-                            int P, int Hq, int Hkv, int Lmax, int NRB, float scale_log2)
-{
-    constexpr int C = XV_ATTN_C;
-    constexpr int NT = XV_PF_THREADS;
-    constexpr int KS = D / 32;                  // k-steps of a score
-    constexpr int NCB = C / 16;                 // score blocks of a chunk
-    constexpr int DB = D / 16;                  // output blocks
-    constexpr int KG = C * (D / 8) / NT;        // K granules per thread
-    constexpr int VTILES = (C / 8) * (D / 8);   // 8 x 8 V tiles of a chunk
-    constexpr int VT = (VTILES + NT - 1) / NT;
-    static_assert(C * (D / 8) % NT == 0 && NCB % 2 == 0, "chunk must split evenly");
-    // LDS: K as [pos][d] (row pitch KP bytes), later V^T as [d][pos] (pitch VP); the 16-byte
-    // pads put the 16 rows of a fragment read on distinct banks, and every fragment is a
-    // per-lane base plus a constant offset
-    constexpr int KP = D * 2 + 16, VP = C * 2 + 16;
-    constexpr int LDSB = (C * KP > D * VP ? C * KP : D * VP);
-    __shared__ __attribute__((aligned(16))) char lds[LDSB];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    const int bid = (int)blockIdx.x;
-    const int rb = NRB - 1 - bid % NRB;         // the blocks of the last rows (most chunks) first
-    const int g = (bid / NRB) % Hkv;
-    const int b = bid / (NRB * Hkv);
-    const int Hg = Hq / Hkv;
-    const int Ptot = Hg * P;
-    int L0 = kv_len[b];
-    L0 = L0 < 0 ? 0 : (L0 > Lmax - P ? Lmax - P : L0);
-    const int Lend = L0 + P;
-    const int pair0 = rb * XV_PF_PAIRS;
-    const int last_pair = pair0 + XV_PF_PAIRS - 1 < Ptot ? pair0 + XV_PF_PAIRS - 1 : Ptot - 1;
-    const int nc = (L0 + last_pair / Hg + 1 + C - 1) / C;          // chunks the block's last row sees
-    const int tpair0 = pair0 + wave * 16;       // this wave's tile
-    // the wave's tile sees chunk c while its last row does
-    const int tlast = tpair0 + 15 < Ptot ? tpair0 + 15 : Ptot - 1;
-    const int tnc = tpair0 < Ptot ? (L0 + tlast / Hg + 1 + C - 1) / C : 0;
-    // this lane's score pair (lr) and its output pairs (4 lg + i)
-    const int pair = tpair0 + lr;
-    const bool pair_ok = pair < Ptot;
-    const int plen = pair_ok ? L0 + pair / Hg + 1 : 0;
-    const size_t kvbase = ((size_t)b * Hkv + g) * Lmax;
-    const xv_u32x4 zero = {0u, 0u, 0u, 0u};
-
-    const int pcq = pair_ok ? pair : 0;
-    const uint16_t* qp = q + (((size_t)b * P + pcq / Hg) * Hq + g * Hg + pcq % Hg) * D + lg * 8;
-
-    constexpr int KB = KG < 8 ? KG : 8;         // K granules per thread in flight
-    auto k_to_lds = [&](int c0) {
-#pragma unroll 1
-        for (int i0 = 0; i0 < KG; i0 += KB) {
-            xv_u32x4 kr[KB];
-#pragma unroll
-            for (int i = 0; i < KB; ++i) {
-                const int idx = tid + (i0 + i) * NT;
-                const int pos = c0 + idx / (D / 8);
-                kr[i] = xv_load16(k_cache + (kvbase + (pos < Lend ? pos : 0)) * D + (idx % (D / 8)) * 8);
-                if (pos >= Lend) kr[i] = zero;
-            }
-#pragma unroll
-            for (int i = 0; i < KB; ++i) {
-                const int idx = tid + (i0 + i) * NT;
-                *reinterpret_cast<xv_u32x4*>(lds + (idx / (D / 8)) * KP + (idx % (D / 8)) * 16) = kr[i];
-            }
-        }
-    };
-    auto vt_to_lds = [&](int c0) {
-#pragma unroll 1
-        for (int i = 0; i < VT; ++i) {
-            const int vt = tid + i * NT;
-            if (VTILES % NT == 0 || vt < VTILES) {
-                const int pg = vt / (D / 8), dg = vt % (D / 8);
-                xv_u32x4 vr[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int pos = c0 + pg * 8 + e;
-                    vr[e] = xv_load16(v_cache + (kvbase + (pos < Lend ? pos : 0)) * D + dg * 8);
-                    if (pos >= Lend) vr[e] = zero;
-                }
-#pragma unroll
-                for (int dd = 0; dd < 8; ++dd) {
-                    xv_u32x4 outv;
-#pragma unroll
-                    for (int w2 = 0; w2 < 4; ++w2) {
-                        const uint32_t lo = vr[2 * w2][dd >> 1], hi = vr[2 * w2 + 1][dd >> 1];
-                        outv[w2] = (dd & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-                    }
-                    *reinterpret_cast<xv_u32x4*>(lds + (dg * 8 + dd) * VP + pg * 16) = outv;
-                }
-            }
-        }
-    };
-    // scores of the chunk in LDS, in log2 units: sc[cb][i] = position cb*16 + 4 lg + i, pair lr
-    xv_f32x4 sc[NCB];
-    auto scores = [&]() {
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) sc[cb] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const xv_u32x4 qk = pair_ok ? xv_load16(qp + ks * 32) : zero;
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-                sc[cb] = xv_mfma16x16x32(*reinterpret_cast<const xv_u32x4*>(lds + (cb * 16 + lr) * KP + ks * 64 + lg * 16),
-                                         qk, sc[cb]);
-        }
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc[cb][i] = sc[cb][i] * scale_log2;
-    };
-
-    // ---- chunk partials, folded in ascending chunk order with the running maximum ----
-    xv_f32x4 A[DB];
-#pragma unroll
-    for (int j = 0; j < DB; ++j) A[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
-    float L = 0.f, Mrun = -INFINITY;            // this lane's score pair (lr)
-    int orow[4];
-    bool ook[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p2 = tpair0 + 4 * lg + i;
-        ook[i] = p2 < Ptot;
-        orow[i] = ook[i] ? p2 / Hg : 0;
-    }
-    for (int c = 0; c < nc; ++c) {
-        const int c0 = c * C;
-        __syncthreads();                        // LDS free
-        k_to_lds(c0);
-        __syncthreads();
-        const bool active = c < tnc;            // uniform per wave
-        float fa = 0.f, fb = 0.f;
-        if (active) {
-            scores();
-            float m = -INFINITY;
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (c0 + cb * 16 + 4 * lg + i < plen) m = fmaxf(m, sc[cb][i]);
-            m = fmaxf(m, __shfl_xor(m, 16));
-            m = fmaxf(m, __shfl_xor(m, 32));
-            const bool sees = plen > c0;        // the pair has a partial for this chunk
-            if (!sees) m = 0.f;                 // keep finite (no position is visible)
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool vis = c0 + cb * 16 + 4 * lg + i < plen;
-                    sc[cb][i] = vis ? __builtin_amdgcn_exp2f(sc[cb][i] - m) : 0.f;
-                }
-            float l = 0.f;
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) l = l + sc[cb][i];
-            l = l + __shfl_xor(l, 16);
-            l = l + __shfl_xor(l, 32);
-            if (sees) {
-                xv_fold_factors(Mrun, m, fa, fb);
-                L = __builtin_fmaf(L, fa, l * fb);
-            }
-#pragma unroll
-            for (int kk = 0; kk < C / 32; ++kk) {   // the P.V A operands, bf16 hi + lo
-                xv_u32x4 phi, plo;
-                xv_p_split(sc[2 * kk], sc[2 * kk + 1], phi, plo);
-                sc[2 * kk] = __builtin_bit_cast(xv_f32x4, phi);
-                sc[2 * kk + 1] = __builtin_bit_cast(xv_f32x4, plo);
-            }
-        }
-        __syncthreads();                        // every wave is done reading K
-        vt_to_lds(c0);
-        __syncthreads();
-        if (active) {
-            float ai[4], bi[4];
-            bool si[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ai[i] = __shfl(fa, 4 * lg + i);
-                bi[i] = __shfl(fb, 4 * lg + i);
-                si[i] = ook[i] && L0 + orow[i] + 1 > c0;
-            }
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                xv_f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < C / 32; ++kk) {
-                    // V^T rows db*16 + lr at positions kk*32 + 4 lg .. + 3 and kk*32 + 16 + 4 lg .. + 3
-                    const char* vp = lds + (db * 16 + lr) * VP + kk * 64 + lg * 8;
-                    const uint2 va = *reinterpret_cast<const uint2*>(vp);
-                    const uint2 vb = *reinterpret_cast<const uint2*>(vp + 32);
-                    const xv_u32x4 vf = {va.x, va.y, vb.x, vb.y};
-                    oacc = xv_mfma16x16x32(__builtin_bit_cast(xv_u32x4, sc[2 * kk]), vf, oacc);
-                    oacc = xv_mfma16x16x32(__builtin_bit_cast(xv_u32x4, sc[2 * kk + 1]), vf, oacc);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    A[db][i] = si[i] ? __builtin_fmaf(A[db][i], ai[i], oacc[i] * bi[i]) : A[db][i];
-            }
-        }
-    }
-    float Lp[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Lp[i] = __shfl(L, 4 * lg + i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (!ook[i]) continue;
-        const int p2 = tpair0 + 4 * lg + i;
-        const size_t ob = (((size_t)b * P + orow[i]) * Hq + g * Hg + p2 % Hg) * D + lr;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const float ov = A[db][i] / Lp[i];
-            o[ob + db * 16] = xv_f32_to_bf16(ov);
-            if (o32) o32[ob + db * 16] = ov;
-        }
-    }
-}
-
+// Attention of P appended rows: the rows go into the cache first, then the streaming
+// kernel in prefill mode (one workgroup per block of 64 (row, head) pairs; each row gets the
+// decode row's chunk partials and two-level fold), then the lengths advance when asked.
 template <int D>
 int xv_attn_prefill_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                            uint16_t* k_cache, uint16_t* v_cache, int32_t* kv_len,
@@ -1639,9 +1650,10 @@ int xv_attn_prefill_launch(const uint16_t* q, const uint16_t* k_new, const uint1
                        k_new, v_new, k_cache, v_cache, kv_len, P, Hkv, D, Lmax);
     int s = xv_launch_status();
     if (s != XV_OK) return s;
-    const int NRB = ((Hq / Hkv) * P + XV_PF_PAIRS - 1) / XV_PF_PAIRS;
-    hipLaunchKernelGGL(xv_attn_prefill_kernel<D>, dim3(NRB * Hkv * B), dim3(XV_PF_THREADS), 0, st,
-                       q, k_cache, v_cache, kv_len, o, o32, P, Hq, Hkv, Lmax, NRB, xv_scale_log2(scale));
+    const int NRB = ((Hq / Hkv) * P + XV_ATTN_SPAIRS - 1) / XV_ATTN_SPAIRS;
+    const XvStreamArgs sa{q, nullptr, nullptr, k_cache, v_cache, kv_len, nullptr, nullptr, o, o32,
+                          P, Hq, Hkv, Lmax, 0, NRB, xv_scale_log2(scale)};
+    hipLaunchKernelGGL((xv_attn_stream_kernel<D, true>), dim3(NRB * Hkv * B), dim3(XV_ATTN_WAVES * 64), 0, st, sa);
     s = xv_launch_status();
     if (s != XV_OK || !advance) return s;
     hipLaunchKernelGGL(xv_kv_advance_kernel, dim3((B + 63) / 64), dim3(64), 0, st, kv_len, B, P);
@@ -1658,7 +1670,7 @@ extern "C" int xv_attn_prefill(const uint16_t* q, const uint16_t* k_new, const u
     XV_REQUIRE(B >= 0 && P >= 1 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, XV_ERR_SHAPE);
     XV_REQUIRE(d == 64 || d == 128 || d == 256, XV_ERR_SHAPE);
     XV_REQUIRE(Lmax >= P && (Lmax + XV_ATTN_C - 1) / XV_ATTN_C <= XV_ATTN_MAX_NC, XV_ERR_SHAPE);
-    XV_REQUIRE((long long)((Hq / Hkv) * (long long)P + XV_PF_PAIRS - 1) / XV_PF_PAIRS * Hkv * B < (1LL << 31),
+    XV_REQUIRE((long long)((Hq / Hkv) * (long long)P + XV_ATTN_SPAIRS - 1) / XV_ATTN_SPAIRS * Hkv * B < (1LL << 31),
                XV_ERR_SHAPE);
     XV_REQUIRE((long long)P * Hkv * (d / 8) / 256 < (1LL << 31) && B < 65536, XV_ERR_SHAPE);
     XV_REQUIRE(scale == scale, XV_ERR_SHAPE);

@@ -190,10 +190,11 @@ int xv_gdn_verify_after(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * attends positions 0..L0+r:  o = sum_j softmax_j(scale * q.k_j) v_j.
  * The context is split into chunks of xv_attn_chunk_tokens() positions at
  * absolute boundaries; per chunk the partial (max, sum, weighted values) is
- * formed in a fixed order, and the chunks are merged in ascending order with
- * a running maximum (a chunk that raises it rescales the sums so far).  All of
- * it depends on the row's length and data only, never on T, B, Lmax or the
- * workspace size.
+ * formed in a fixed order, and the partials are merged in two levels, each in
+ * ascending order with a running maximum (a partial that raises it rescales the
+ * sums so far): the chunks of each group of 8 consecutive chunks, then the
+ * groups.  All of it depends on the row's length and data only, never on T, B,
+ * Lmax or the workspace size.
  *
  *   q        : bf16 [B][T][Hq][d]      [16B]
  *   k_new    : bf16 [B][T][Hkv][d]     [16B]  v_new: same
@@ -203,7 +204,7 @@ int xv_gdn_verify_after(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *   o32      : fp32 [B][T][Hq][d] or NULL
  *   workspace: [16B] device scratch of workspace_bytes >= xv_attn_workspace_bytes(B,T,Hq,d,Lmax)
  * Shapes: B >= 0, 1 <= T <= 16, Hq % Hkv == 0, d in {64, 128, 256}, Lmax >= T,
- * ceil(Lmax / chunk) <= 5120, B * Hkv * ceil(Lmax / chunk) * ceil((Hq/Hkv) * T / 16)
+ * ceil(Lmax / chunk) <= 4608, B * Hkv * ceil(Lmax / chunk) * ceil((Hq/Hkv) * T / 16)
  * <= 2^29 (the grid;
  * XV_ERR_SHAPE otherwise).  Device precondition: 0 <= L0 and
  * L0 + T <= Lmax (kernels clamp positions to the buffer otherwise).
@@ -288,7 +289,7 @@ int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *   kv_len : int32 [B] device; advance != 0: kv_len[b] += P after the rows are formed
  *   o : bf16 [B][P][Hq][d]   o32 : fp32 or NULL
  * Shapes: B >= 0, P >= 1, Hq % Hkv == 0, d in {64, 128, 256}, Lmax >= P,
- * ceil(Lmax / chunk) <= 5120.  Device
+ * ceil(Lmax / chunk) <= 4608.  Device
  * precondition: 0 <= L0 and L0 + P <= Lmax (positions are clamped otherwise).
  */
 int xv_attn_prefill(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
