@@ -523,9 +523,35 @@ void xv_attn_stream_kernel(const XvStreamArgs A)
             return cache + kvbase * D;
         }
     };
+    // this thread's granules of a unit, as element offsets from the unit's first cache row:
+    // K granule i is position idx / (D/8), dims (idx % (D/8)) * 8 (idx = tid + i NT); V: a 4 x 8
+    // tile, positions pg4 * 4 .. + 3, dims dg * 8 ..
+    int koff[KG];
+#pragma unroll
+    for (int i = 0; i < KG; ++i) {
+        const int idx = tid + i * NT;
+        koff[i] = (idx / (D / 8)) * D + (idx % (D / 8)) * 8;
+    }
+    const int vtc = tid < VT4 ? tid : VT4 - 1;
+    const int voff = (vtc / (D / 8)) * 4 * D + (vtc % (D / 8)) * 8;
+    // a unit whose 64 positions all precede the new rows (verify) or the end of the rows
+    // (prefill) is read straight from the cache: one base for the workgroup, no per-position
+    // choice, no zeroing, no append
+    const int plain_end = PF ? Lend : L0;
     // unit u of item it: u < 4 is K sub-block u, u >= 4 is V sub-block u - 4
     auto load_unit = [&](XvUnit<D>& U, int it, int u) __attribute__((always_inline)) {
         const int p0 = chunk_of(it) * C + (u & 3) * SB;
+        if (p0 + SB <= plain_end) {             // uniform
+            const uint16_t* base = (u < 4 ? A.k_cache : A.v_cache) + (kvbase + p0) * D;
+            if (u < 4) {
+#pragma unroll
+                for (int i = 0; i < KG; ++i) U.r[i] = xv_load16(base + koff[i]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) U.r[e] = xv_load16(base + voff + e * D);
+            }
+            return;
+        }
         if (u < 4) {
 #pragma unroll
             for (int i = 0; i < KG; ++i) {
@@ -542,24 +568,29 @@ void xv_attn_stream_kernel(const XvStreamArgs A)
     // into LDS: positions past L0 + R zeroed; verify appends the new rows to the cache
     auto store_unit = [&](XvUnit<D>& U, int it, int u) __attribute__((always_inline)) {
         const int p0 = chunk_of(it) * C + (u & 3) * SB;
+        const bool plain = p0 + SB <= plain_end;     // uniform
         if (u < 4) {
 #pragma unroll
             for (int i = 0; i < KG; ++i) {
                 const int idx = tid + i * NT;
                 const int lp = idx / (D / 8), cc = idx % (D / 8);
                 const int pos = p0 + lp;
-                if (pos >= Lend) U.r[i] = zero;
-                else if (!PF && pos >= L0) xv_store16(A.k_cache + (kvbase + pos) * D + cc * 8, U.r[i]);
+                if (!plain) {
+                    if (pos >= Lend) U.r[i] = zero;
+                    else if (!PF && pos >= L0) xv_store16(A.k_cache + (kvbase + pos) * D + cc * 8, U.r[i]);
+                }
                 sk[xv_k_granule<D>(lp, cc)] = U.r[i];
             }
         } else if (tid < VT4) {
             // a 4 (positions) x 8 (dims) tile -> for each of its 8 dims, 4 positions of V^T (8 bytes)
             const int pg4 = tid / (D / 8), dg = tid % (D / 8);
+            if (!plain) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int pos = p0 + pg4 * 4 + e;
-                if (pos >= Lend) U.r[e] = zero;
-                else if (!PF && pos >= L0) xv_store16(A.v_cache + (kvbase + pos) * D + dg * 8, U.r[e]);
+                for (int e = 0; e < 4; ++e) {
+                    const int pos = p0 + pg4 * 4 + e;
+                    if (pos >= Lend) U.r[e] = zero;
+                    else if (!PF && pos >= L0) xv_store16(A.v_cache + (kvbase + pos) * D + dg * 8, U.r[e]);
+                }
             }
             char* vb = reinterpret_cast<char*>(svt);
 #pragma unroll
