@@ -226,18 +226,20 @@ def lmax_for(wl, steps_per_replica_n1, steps_per_replica_full):
     return L0max + max(wl.T * (steps_per_replica_n1 + 4), wl.T * (steps_per_replica_full + 4))
 
 
-def extra_workload(name, stream, steps, warmup, R):
-    """Verified draft tok/s of another workload (bit-exact gate included)."""
+def extra_workload(name, stream, steps, warmup, R, capacity=None):
+    """Verified draft tok/s of another workload (bit-exact gate included); capacity: the
+    cache's position count (default: the steps' need)."""
     import torch
     from bit_exact_speculative_amd import inputs as gen
     wl = gen.WORKLOADS[name]
     per = (steps + warmup + R - 1) // R
-    _, layers, exact = build_layers(wl, lmax_for(wl, per, 0), R, stream)
+    Lmax = lmax_for(wl, per, 0) if capacity is None else max(capacity, lmax_for(wl, per, 0))
+    _, layers, exact = build_layers(wl, Lmax, R, stream)
     ms, _, _ = run_steps(layers, stream, steps, warmup)
     ctx = wl.L0 if wl.L0 is not None else "%d-%d" % wl.L0_range
     res = {"ctx": ctx, "batch": wl.B, "tok_s": round(wl.B * wl.k_drafts / (ms * 1e-3), 1) if exact else None,
            "ms_per_step": round(ms, 5), "bit_exact_verify_equals_decode": exact, "steps": steps,
-           "layer_replicas": R}
+           "layer_replicas": R, "cache_positions": Lmax}
     del layers
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -507,6 +509,13 @@ def main():
                 extras[name] = extra_workload(name, stream, steps, warmup, reps)
             except Exception as exc:                  # reported, never hides the headline line
                 extras[name] = {"error": "%s: %s" % (type(exc).__name__, exc)}
+        try:                                      # the launch command's context length, short rows
+            extras["short_capacity_262144"] = extra_workload("short", stream, 100, 10, 4, capacity=262144)
+            extras["short_capacity_262144"]["note"] = (
+                "the short workload in caches of 262,144 positions: the attention work split is chosen by "
+                "capacity (the lengths live on the device), here the streaming kernel and the long-row combine")
+        except Exception as exc:
+            extras["short_capacity_262144"] = {"error": "%s: %s" % (type(exc).__name__, exc)}
         try:
             extras["composed"] = composed_workload(stream)
         except Exception as exc:

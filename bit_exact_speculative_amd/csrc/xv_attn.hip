@@ -366,7 +366,11 @@ void xv_attn_partial_wide_kernel(const uint16_t* __restrict__ q, const uint16_t*
 //  * Verify (PF = false, long contexts): persistent workgroups stream the chunk groups of
 //    one (KV head, request), group x, x + WPG, x + 2 WPG, ... for workgroup x, the chunks
 //    of a group in ascending order, and write one partial per group (the group's chunks
-//    folded in registers).
+//    folded in registers).  A request whose groups would leave most of its WPG workgroups
+//    idle (2 x groups <= WPG: a short row in a large cache) is streamed by chunks instead,
+//    one chunk partial each (a group of one chunk is the chunk's partial, bit for bit);
+//    xv_stream_grouped() is that choice, and the combine makes it again from the same
+//    inputs.
 //  * Prefill (PF = true): one workgroup per (request, KV head, block
 //    of 64 (row, head) pairs) walks every chunk its last row sees, in ascending order, and
 //    folds both levels in registers into the rows' outputs (no workspace).
@@ -393,6 +397,13 @@ struct XvUnit {
     xv_u32x4 r[4];                                                  // K: KG granules; V: one 4 x 8 tile
 };
 
+// whether the streaming kernel folds request b's chunks in groups of XV_ATTN_G (else it
+// writes chunk partials): nchunks, the chunks the request's last row sees; wpg, the
+// streaming grid's workgroups per (KV head, request)
+__host__ __device__ inline bool xv_stream_grouped(int nchunks, int wpg) {
+    return 2 * ((nchunks + XV_ATTN_G - 1) / XV_ATTN_G) > wpg;
+}
+
 struct XvStreamArgs {
     const uint16_t* q;          // [B][R][Hq][D]
     const uint16_t* k_new;      // verify: the rows to append, [B][R][Hkv][D]
@@ -406,7 +417,7 @@ struct XvStreamArgs {
     float* o32;
     int R;                      // rows per request (verify T, prefill P)
     int Hq, Hkv, Lmax;
-    int NG;                     // verify: groups of the capacity (the partials' stride)
+    int NC, NG;                 // verify: chunks and groups of the capacity (the partials' strides)
     int NRB;                    // prefill: pair blocks per (request, KV head)
     float scale_log2;
 };
@@ -460,22 +471,27 @@ void xv_attn_stream_kernel(const XvStreamArgs A)
     const int npair = Ptot - pair0 < XV_ATTN_SPAIRS ? Ptot - pair0 : XV_ATTN_SPAIRS;
     const int first_len = L0 + pair0 / Hg + 1;                  // every pair sees the positions below
     const int nchunks = (L0 + (pair0 + npair - 1) / Hg + 1 + C - 1) / C;   // chunks the last row sees
-    // this workgroup's chunks, in order: verify, the chunks of its groups; prefill, all of them
-    int x = 0, WPG = 1, nitems;
+    // this workgroup's chunks, in order: verify, the chunks of its groups (gs = log2 of the
+    // group size: 3, or 0 for chunk partials); prefill, all of them, in groups of G
+    int x = 0, WPG = 1, nitems, gs = 3, NI = 0;
     if constexpr (PF) {
         nitems = nchunks;
     } else {
         x = (int)blockIdx.x;
         WPG = (int)gridDim.x;
-        const int ngr = (nchunks + G - 1) / G;
+        gs = xv_stream_grouped(nchunks, WPG) ? 3 : 0;
+        NI = gs ? A.NG : A.NC;
+        const int ge = 1 << gs;
+        const int ngr = (nchunks + ge - 1) >> gs;
         if (x >= ngr) return;                   // uniform
         const int ngw = (ngr - 1 - x) / WPG + 1;
         const int lastg = x + (ngw - 1) * WPG;
-        nitems = (ngw - 1) * G + (nchunks - lastg * G < G ? nchunks - lastg * G : G);
+        nitems = ((ngw - 1) << gs) + (nchunks - (lastg << gs) < ge ? nchunks - (lastg << gs) : ge);
     }
+    static_assert(G == 8, "group size 1 << 3");
     auto chunk_of = [&](int it) __attribute__((always_inline)) -> int {
         if constexpr (PF) return it;
-        else return (x + (it / G) * WPG) * G + it % G;
+        else return ((x + (it >> gs) * WPG) << gs) + (it & ((1 << gs) - 1));
     };
 
     const int tid = threadIdx.x;
@@ -773,17 +789,17 @@ void xv_attn_stream_kernel(const XvStreamArgs A)
         }
 
         // ---- a group complete: verify writes its partial, prefill folds it into the total ----
-        if (c % G == G - 1 || !more) {
-            const int gi = c / G;
-            const int gc0 = gi * G * C;
+        if ((c & ((1 << gs) - 1)) == (1 << gs) - 1 || !more) {
+            const int gi = c >> gs;
+            const int gc0 = (gi << gs) * C;
             if constexpr (!PF) {
                 if (tile_on) {
                     if (lg == 0 && dh == 0 && pair_ok && plen > gc0) {
-                        const size_t idx = (((size_t)b * A.R + pr) * A.Hq + ph) * A.NG + gi;
+                        const size_t idx = (((size_t)b * A.R + pr) * A.Hq + ph) * NI + gi;
                         __builtin_nontemporal_store(Mg, &A.ws_ml[idx * 2 + 0]);
                         __builtin_nontemporal_store(Lg, &A.ws_ml[idx * 2 + 1]);
                     }
-                    xv_store_acc<D, DBH>(A.ws_acc, Ag, dh * DBH, tile, lr, lg, Ptot, Hg, g, b, A.R, A.Hq, A.NG, gi, L0, gc0);
+                    xv_store_acc<D, DBH>(A.ws_acc, Ag, dh * DBH, tile, lr, lg, Ptot, Hg, g, b, A.R, A.Hq, NI, gi, L0, gc0);
                 }
             } else {
                 if (tile_on) {
@@ -1031,35 +1047,27 @@ void xv_attn_partial_tile_kernel(XvTileArgs A)
     xv_attn_tile_body<D, DS>(A, (int)blockIdx.x, sm);
 }
 
-// One workgroup per (query head, row, request), one thread per output dim.  GRP: the
-// partials are group partials (the streaming kernel), folded in ascending group order; else
-// chunk partials, folded in two levels (each group's chunks, then the groups).  NI: the
-// partials' stride per row (chunks or groups of the capacity).
-// DEEP = false: every thread walks the chain itself, forming the factors from the (m, l) it
-// loads (rows of a few items; the first XV_COMBINE_PRE items' loads are issued together).
-// DEEP = true (long rows): the factors are formed once per item in LDS (a running maximum
-// as a prefix maximum: a per-thread segment, then a scan over the segments; a maximum is
-// exact in any order), and the chain's loads run in two alternating register blocks of
-// XV_COMBINE_U chunk (or group) partials, one block in flight while the other is summed.
-// All four forms fold the same operations in the same order.
-template <int D, bool DEEP, bool GRP>
+// One workgroup per (query head, row, request), one thread per output dim.  The partials are
+// chunk partials (the tile and wide kernels; STREAM = false), folded in two levels (each
+// group's chunks, then the groups), or what the streaming kernel wrote for the request
+// (STREAM = true): group partials, folded in ascending group order, or chunk partials,
+// decided by xv_stream_grouped() from the same inputs.  NC, NG: the capacity's chunks and
+// groups (the partials' strides); wpg: the streaming grid's workgroups per (KV head, request).
+// Rows of at most XV_COMBINE_PRE partials (and every row when DEEP = false): every thread
+// walks the chain itself, forming the factors from the (m, l) it loads (the first
+// XV_COMBINE_PRE partials' loads issued together).  Longer rows when DEEP = true: the
+// factors are formed once per partial in LDS (a running maximum as a prefix maximum: a
+// per-thread segment, then a scan over the segments; a maximum is exact in any order), and
+// the chain's loads run in two alternating register blocks of XV_COMBINE_U partials, one
+// block in flight while the other is summed.  Every form folds the same operations in the
+// same order.
+template <int D, bool DEEP, bool STREAM>
 __global__ __launch_bounds__(D)
 void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
                             const int32_t* __restrict__ kv_len, uint16_t* __restrict__ o,
-                            float* __restrict__ o32, int T, int Hq, int Lmax, int NI)
+                            float* __restrict__ o32, int T, int Hq, int Lmax, int NC, int NG, int wpg)
 {
     constexpr int G = XV_ATTN_G;
-    // LDS: [NIP] a, [NIP] b, [NIP] l b (GRP) or l (chunks), then (chunks) [NIP / G] x 3 group
-    // factors, then [D] scan
-    extern __shared__ __attribute__((aligned(16))) float sh[];
-    const int NIP = DEEP ? xv_combine_pad(NI) : NI;
-    float* sa = sh;
-    float* sb = sh + NIP;
-    float* sl = sh + 2 * NIP;
-    float* ga = sh + 3 * NIP;
-    float* gb = ga + (GRP ? 0 : NIP / G);
-    float* gl = gb + (GRP ? 0 : NIP / G);
-    float* sred = gl + (GRP ? 0 : NIP / G);
     const int h = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     int L0 = kv_len[b];
@@ -1067,12 +1075,26 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
     const int len = L0 + r + 1;
     const int nc = (len + XV_ATTN_C - 1) / XV_ATTN_C;
     const int ng = (nc + G - 1) / G;
-    const int ni = GRP ? ng : nc;               // this row's partials
+    // group partials (uniform over the workgroup): as the streaming kernel chose for the request
+    const bool grp = STREAM && xv_stream_grouped((L0 + T + XV_ATTN_C - 1) / XV_ATTN_C, wpg);
+    const int NI = grp ? NG : NC;
+    const int ni = grp ? ng : nc;               // this row's partials
+    // LDS (DEEP): [NIP] a, [NIP] b, [NIP] l b (groups) or l (chunks), then (chunks) [NIP / G] x 3
+    // group factors, then [D] scan
+    extern __shared__ __attribute__((aligned(16))) float sh[];
+    const int NIP = DEEP ? xv_combine_pad(NI) : NI;
+    float* sa = sh;
+    float* sb = sh + NIP;
+    float* sl = sh + 2 * NIP;
+    float* ga = sh + 3 * NIP;
+    float* gb = ga + (grp ? 0 : NIP / G);
+    float* gl = gb + (grp ? 0 : NIP / G);
+    float* sred = gl + (grp ? 0 : NIP / G);
     const size_t base = (((size_t)b * T + r) * Hq + h) * NI;
     const float* ap = ws_acc + base * D + tid;
     float L = 0.f, A = 0.f;
 
-    if constexpr (!DEEP) {
+    if (!DEEP || ni <= XV_COMBINE_PRE) {       // uniform
         // indices past ni re-read item ni - 1 and are not used
         constexpr int PRE = XV_COMBINE_PRE;
         static_assert(PRE == G, "the first block of loads is one group of chunks");
@@ -1087,7 +1109,7 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
             }
         };
         float M = -INFINITY;
-        if constexpr (GRP) {
+        if (grp) {
             load_block(0);
 #pragma unroll
             for (int u = 0; u < PRE; ++u) {
@@ -1140,7 +1162,7 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
         // folds into its group's sum, and a group into the row's sums after its last chunk
         // (a block of loads holds whole groups); an item past ni leaves the sums as they are
         auto fold = [&](const float (&buf)[U], int i0) __attribute__((always_inline)) {
-            if constexpr (GRP) {
+            if (grp) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const bool in = i0 + u < ni;
@@ -1172,7 +1194,7 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
         fetch(ba, 0);                           // independent of the factors
         float mseg = -INFINITY;
         int s0, s1;                             // this thread's segment of items (chunks: whole groups)
-        if constexpr (GRP) {
+        if (grp) {
             // (m, l) of the segment's groups: m into sa, l into sl; the segment's maximum
             const int seg = (ni + D - 1) / D;
             s0 = tid * seg;
@@ -1218,7 +1240,7 @@ void xv_attn_combine_kernel(const float* __restrict__ ws_acc, const float* __res
         float M = tid > 0 ? sred[tid - 1] : -INFINITY;
         for (int cc = s0; cc < s1; ++cc) {
             float fa, fb;
-            if constexpr (GRP) {
+            if (grp) {
                 xv_fold_factors(M, sa[cc], fa, fb);
                 sa[cc] = fa;
                 sb[cc] = fb;
@@ -1257,6 +1279,16 @@ XvAttnKind xv_attn_kind(int B, int T, int Hq, int Hkv, int NC) {
     if (D == 256 && groups * NC >= XV_ATTN_STREAM_MIN && P <= 64) return XV_ATTN_STREAM;
     if (groups * NC >= XV_ATTN_WIDE_MIN && P <= 16 * XV_ATTN_WAVES) return XV_ATTN_WIDE;
     return XV_ATTN_TILE;
+}
+
+// the streaming grid: about one persistent workgroup per CU, spread evenly over the (KV
+// head, request) groups, at most one per chunk group of the capacity
+inline int xv_stream_wpg(int B, int Hkv, int NC) {
+    const long long groups = (long long)B * Hkv;
+    const long long NG = (NC + XV_ATTN_G - 1) / XV_ATTN_G;
+    long long wpg = xv_cu_count() / groups;
+    wpg = wpg < 1 ? 1 : (wpg > NG ? NG : wpg);
+    return (int)wpg;
 }
 
 // workgroups of the tile split: (request, KV head, chunk, 16-pair tile, value-dim part)
@@ -1301,15 +1333,11 @@ int xv_attn_partials(const uint16_t* q, const uint16_t* k_new, const uint16_t* v
     const float scale_log2 = xv_scale_log2(scale);
     const XvAttnKind kind = xv_attn_kind<D>(B, T, Hq, Hkv, NC);
     if (kind == XV_ATTN_STREAM) {
-        // about one persistent workgroup per CU, spread evenly over the (KV head, request)
-        // groups; each walks whole chunk groups and writes one partial per group
-        const long long groups = (long long)B * Hkv;
         const int NG = (NC + XV_ATTN_G - 1) / XV_ATTN_G;
-        long long wpg = xv_cu_count() / groups;
-        wpg = wpg < 1 ? 1 : (wpg > NG ? NG : wpg);
         const XvStreamArgs sa{q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml, nullptr, nullptr,
-                              T, Hq, Hkv, Lmax, NG, 0, scale_log2};
-        hipLaunchKernelGGL((xv_attn_stream_kernel<D, false>), dim3((int)wpg, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st, sa);
+                              T, Hq, Hkv, Lmax, NC, NG, 0, scale_log2};
+        hipLaunchKernelGGL((xv_attn_stream_kernel<D, false>), dim3(xv_stream_wpg(B, Hkv, NC), Hkv, B),
+                           dim3(XV_ATTN_WAVES * 64), 0, st, sa);
     } else if (kind == XV_ATTN_WIDE) {
         hipLaunchKernelGGL(xv_attn_partial_wide_kernel<D>, dim3(NC, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st,
                            q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
@@ -1328,32 +1356,27 @@ int xv_attn_partials(const uint16_t* q, const uint16_t* k_new, const uint16_t* v
     return xv_launch_status();
 }
 
-// The combine for chunk partials (grp = false: the tile and wide kernels) or group partials
-// (grp = true: the streaming kernel); NC is the capacity's chunk count.
+// The combine for chunk partials (the tile and wide kernels) or for what the streaming
+// kernel wrote (stream = true, its grid of wpg workgroups per (KV head, request)); NC is the
+// capacity's chunk count.
 template <int D>
 int xv_attn_combine(const float* ws_acc, const float* ws_ml, const int32_t* kv_len, uint16_t* o, float* o32,
-                    int B, int T, int Hq, int Lmax, int NC, bool grp, hipStream_t st)
+                    int B, int T, int Hq, int Lmax, int NC, bool stream, int wpg, hipStream_t st)
 {
     (void)hipGetLastError();
     const dim3 grid(Hq, T, B), block(D);
-    if (grp) {
-        const int NG = (NC + XV_ATTN_G - 1) / XV_ATTN_G;
-        if (NG > XV_COMBINE_PRE) {
-            const size_t shmem = sizeof(float) * (3 * (size_t)xv_combine_pad(NG) + D);
-            hipLaunchKernelGGL((xv_attn_combine_kernel<D, true, true>), grid, block, shmem, st,
-                               ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NG);
-        } else {
-            hipLaunchKernelGGL((xv_attn_combine_kernel<D, false, true>), grid, block, 0, st,
-                               ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NG);
-        }
+    const int NG = (NC + XV_ATTN_G - 1) / XV_ATTN_G;
+    const size_t pad = xv_combine_pad(NC);
+    const size_t shmem = sizeof(float) * (3 * pad + 3 * (pad / XV_ATTN_G) + D);   // either layout
+    if (stream) {
+        hipLaunchKernelGGL((xv_attn_combine_kernel<D, true, true>), grid, block, shmem, st,
+                           ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC, NG, wpg);
     } else if (NC > 2 * XV_COMBINE_U) {
-        const size_t pad = xv_combine_pad(NC);
-        const size_t shmem = sizeof(float) * (3 * pad + 3 * (pad / XV_ATTN_G) + D);
         hipLaunchKernelGGL((xv_attn_combine_kernel<D, true, false>), grid, block, shmem, st,
-                           ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC);
+                           ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC, NG, 0);
     } else {
         hipLaunchKernelGGL((xv_attn_combine_kernel<D, false, false>), grid, block, 0, st,
-                           ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC);
+                           ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC, NG, 0);
     }
     return xv_launch_status();
 }
@@ -1367,8 +1390,9 @@ int xv_attn_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_n
     const int s = xv_attn_partials<D>(q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
                                       B, T, Hq, Hkv, Lmax, NC, scale, st);
     if (s != XV_OK) return s;
-    const bool grp = xv_attn_kind<D>(B, T, Hq, Hkv, NC) == XV_ATTN_STREAM;
-    return xv_attn_combine<D>(ws_acc, ws_ml, kv_len, o, o32, B, T, Hq, Lmax, NC, grp, st);
+    const bool stream = xv_attn_kind<D>(B, T, Hq, Hkv, NC) == XV_ATTN_STREAM;
+    return xv_attn_combine<D>(ws_acc, ws_ml, kv_len, o, o32, B, T, Hq, Lmax, NC, stream,
+                              stream ? xv_stream_wpg(B, Hkv, NC) : 0, st);
 }
 
 // GDN and the attention partials side by side in one launch: workgroups
@@ -1627,9 +1651,9 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
     }
     if (s != XV_OK) return s;
     switch (d) {
-        case 64:  return xv_attn_combine<64>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, false, st);
-        case 128: return xv_attn_combine<128>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, false, st);
-        default:  return xv_attn_combine<256>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, false, st);
+        case 64:  return xv_attn_combine<64>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, false, 0, st);
+        case 128: return xv_attn_combine<128>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, false, 0, st);
+        default:  return xv_attn_combine<256>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, false, 0, st);
     }
 }
 
@@ -1683,7 +1707,7 @@ int xv_attn_prefill_launch(const uint16_t* q, const uint16_t* k_new, const uint1
     if (s != XV_OK) return s;
     const int NRB = ((Hq / Hkv) * P + XV_ATTN_SPAIRS - 1) / XV_ATTN_SPAIRS;
     const XvStreamArgs sa{q, nullptr, nullptr, k_cache, v_cache, kv_len, nullptr, nullptr, o, o32,
-                          P, Hq, Hkv, Lmax, 0, NRB, xv_scale_log2(scale)};
+                          P, Hq, Hkv, Lmax, 0, 0, NRB, xv_scale_log2(scale)};
     hipLaunchKernelGGL((xv_attn_stream_kernel<D, true>), dim3(NRB * Hkv * B), dim3(XV_ATTN_WAVES * 64), 0, st, sa);
     s = xv_launch_status();
     if (s != XV_OK || !advance) return s;

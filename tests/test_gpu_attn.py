@@ -158,6 +158,29 @@ def test_attn_wide_and_tile_kernels_agree(case, grid):
     assert same_bits(kc, kc2[:, :, :Lmax]) and same_bits(vc, vc2[:, :, :Lmax])
 
 
+def test_attn_stream_group_partials_agree_with_chunk_partials():
+    """A 40,000-position row (157 chunks, 20 groups of 8): at a capacity that takes the wide
+    kernel the combine folds the chunk partials in two levels; at one that takes the
+    streaming kernel (65,536 positions: 32 workgroups per KV head, fewer than twice the
+    groups) the kernel folds each group's chunks itself and the combine folds the groups.
+    Every output bit and the appended rows agree, and the outputs meet the oracle's bounds."""
+    B, T, Hq, Hkv, d, L0 = 1, 9, 24, 4, 256, [40000]
+    C = _xv().xv_attn_chunk_tokens()
+    Lmax = max(L0) + T
+    assert 128 <= B * Hkv * -(-Lmax // C) < 1024            # the wide kernel
+    arrs = _case(4242, B, T, Hq, Hkv, d, L0, Lmax)
+    D = Dev(*arrs)
+    o, o32, kc, vc = _verify(D)
+    o2, o322, kc2, vc2 = _verify(D, Lmax_extra=65536 - Lmax)   # the streaming kernel, group partials
+    torch.cuda.synchronize()
+    assert same_bits(o32, o322) and same_bits(o, o2)
+    assert same_bits(kc, kc2[:, :, :Lmax]) and same_bits(vc, vc2[:, :, :Lmax])
+    q, kn, vn, kc0, vc0, L0a = arrs
+    ref = oracle.attn(q, kn, vn, kc0, vc0, L0a, 1.0 / d ** 0.5)
+    o32h = o322.cpu().numpy()
+    assert max_rel(o32h, ref) <= OUT_MAX_REL and rel_l2(o32h, ref) <= OUT_REL_L2
+
+
 def test_attn_tile_value_dim_parts_agree():
     """At d = 256 a tile workgroup forms half of a chunk's output dims while that grid fits
     the chip, all of them beyond (capacity 2304: 9 chunks x 4 KV heads x 4 tiles x 2 halves =
