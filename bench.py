@@ -8,8 +8,9 @@ stream, with every input already resident in HBM:
     the previous step's rollback (its kept rows replayed from its start
       state) and this step's GDN verify, 48 value heads, fp32 state, beside
       attention verify rows + KV append, 24 q / 4 KV heads, d = 256 xv_gdn_attn_verify
-    synthetic head over both outputs (2 x 6144 -> 4096, one launch) xv_gemm_small_m_pair
-    greedy ids, logprobs, accepted rows and the new KV length       xv_greedy_accept
+    synthetic head over both outputs (2 x 6144 -> 4096) with the   xv_head_greedy_accept
+      greedy ids, logprobs, accepted rows and the new KV length
+      (one launch at batch 1)
 The last step's rollback (xv_rollback_to_prefix) runs inside the timed region
 after the last step.
 The default workload is batch 1, k = 8 drafts (9 verify rows), 640 cached
@@ -97,7 +98,7 @@ def kernel_bytes(wl, ctx_mean):
     head = 2 * wl.NH * kh * bf + 2 * M * kh * bf + 2 * M * wl.NH * (bf + f4)
     greedy = 2 * M * wl.NH * f4
     return {"projections": proj, "gdn": gdn, "attention": attn, "gdn_attn": gdn + attn, "head": head,
-            "greedy": greedy}
+            "greedy": greedy, "head_greedy": head}
 
 
 def parse():
@@ -448,7 +449,7 @@ def main():
     # per-call time of a lazy step: events between the calls of 50 steps queued back to back
     breakdown = None
     if not args.no_breakdown:
-        names = ["projections", "gdn_attn", "head", "greedy"]
+        names = ["projections", "gdn_attn", "head_greedy"]
         acc = {k: [] for k in names}
         nb = 50
         for L in layers:
@@ -458,7 +459,7 @@ def main():
             rec = []
             for s_ in range(nb):
                 L = layers[s_ % R]
-                fns = [L.gemms, L.gdn_attn_lazy, L.head_gemms, lambda: L.greedy(count_kv=True)]
+                fns = [L.gemms, L.gdn_attn_lazy, lambda: L.head_greedy(count_kv=True)]
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
                 ev[0].record(stream)
                 for i, f in enumerate(fns):

@@ -84,6 +84,17 @@ int main()
            XV_ERR_SHAPE);
     EXPECT(xv_greedy_accept(reinterpret_cast<float*>(A), reinterpret_cast<float*>(ODD), I, 1, 9, 4096, I, I,
                             nullptr, nullptr, nullptr), XV_ERR_ALIGN);
+    {
+        const size_t wsb = xv_head_greedy_workspace_bytes(1, 9, 4096);
+        EXPECT(xv_head_greedy_accept(A, A, A, F, A, A, A, F, I, I, I, nullptr, nullptr, A, wsb, 1, 17, 4096, 6144,
+                                     nullptr), XV_ERR_SHAPE);
+        EXPECT(xv_head_greedy_accept(A, A, A, F, A, A, A, F, I, I, I, nullptr, nullptr, nullptr, wsb, 1, 9, 4096,
+                                     6144, nullptr), XV_ERR_NULL);
+        EXPECT(xv_head_greedy_accept(A, A, A, F, A, A, A, F, I, I, I, nullptr, nullptr, A, wsb - 1, 1, 9, 4096,
+                                     6144, nullptr), XV_ERR_WORKSPACE);
+        EXPECT(xv_head_greedy_accept(A, A, A, F, A, A, A, F, I, I, I, nullptr, nullptr, A, wsb, 0, 9, 4096, 6144,
+                                     nullptr), XV_OK);
+    }
     EXPECT(xv_embed_rows(A, I, 9, 4096, 5124, A, nullptr), XV_ERR_SHAPE);
     EXPECT(xv_stream_read(A, 1000, A, 1024, reinterpret_cast<uint32_t*>(I), 8, nullptr, nullptr, nullptr), XV_ERR_SHAPE);
     EXPECT(xv_stream_read(nullptr, 1024, A, 1024, reinterpret_cast<uint32_t*>(I), 8, nullptr, nullptr, nullptr),

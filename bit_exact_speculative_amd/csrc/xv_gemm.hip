@@ -29,6 +29,7 @@
 //    gives each wave whole output tiles: it runs the 16 range chains of a tile
 //    one after the other and folds them in range order, the same operations.
 #include "xv_common.h"
+#include "xv_greedy_impl.h"
 #include <hip/hip_ext.h>
 
 namespace {
@@ -37,12 +38,17 @@ constexpr int XV_GEMM_WAVES = 16;   // K ranges per column block; fixes the sum 
 constexpr int XV_GEMM_THREADS = XV_GEMM_WAVES * 64;
 constexpr int XV_GEMM_MT_MAX = 5;   // 16-row tiles per pass over W (more would spill registers)
 
-// Ordered sum of the 16 wave partials of one column block and the store.
+// Ordered sum of the 16 wave partials of one column block and the store.  Returns the
+// last tile's sum of the calling thread's (row, column) for threads below 256 (row
+// 16 (mt0 + MT - 1) + threadIdx.x / 16, column 16 blk + threadIdx.x % 16), 0 otherwise.
+// With store false the caller stores that sum itself (MT = 1).
 template <int MT>
-__device__ __forceinline__ void xv_gemm_finish(float (&red)[XV_GEMM_WAVES][64][4], xv_f32x4 (&acc)[MT],
-                                               int lane, int wave, int blk, int mt0, int M, int N,
-                                               uint16_t* __restrict__ y, float* __restrict__ y32)
+__device__ __forceinline__ float xv_gemm_finish(float (&red)[XV_GEMM_WAVES][64][4], xv_f32x4 (&acc)[MT],
+                                                int lane, int wave, int blk, int mt0, int M, int N,
+                                                uint16_t* __restrict__ y, float* __restrict__ y32,
+                                                bool store = true)
 {
+    float kept = 0.f;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         *reinterpret_cast<xv_f32x4*>(&red[wave][lane][0]) = acc[t];
@@ -56,13 +62,15 @@ __device__ __forceinline__ void xv_gemm_finish(float (&red)[XV_GEMM_WAVES][64][4
             for (int wv = 1; wv < XV_GEMM_WAVES; ++wv) sum = sum + red[wv][slane][si];
             const int row = (mt0 + t) * 16 + rr;
             const int col = blk * 16 + cc;
-            if (row < M) {
+            if (row < M && store) {
                 y[(size_t)row * N + col] = xv_f32_to_bf16(sum);
                 if (y32) y32[(size_t)row * N + col] = sum;
             }
+            kept = sum;
         }
         __syncthreads();
     }
+    return kept;
 }
 
 // x fragments in registers: a wave's range has at most KSW k-steps, streamed in
@@ -168,6 +176,169 @@ constexpr int xv_frag_pitch(int n) {
 static_assert(xv_frag_pitch(64) == 80 && xv_frag_pitch(320) == 336 && xv_frag_pitch(160) == 176 &&
               xv_frag_pitch(80) == 80, "pitch rule");
 
+// Greedy acceptance fused into the head GEMM (one row tile, both halves of the head):
+// the workgroup that formed column block i of both problems holds z = logits_a + logits_b
+// of that block for every row (threads 0..255: row tid / 16, column tid % 16).  It forms
+// the block's pair (m, s) and its argmax, stores them, and the last workgroup to arrive
+// (a counter in the workspace) folds the pairs of every row in the greedy kernel's order,
+// writes ids and logprobs, counts the accepted drafts and resets the counter.
+//
+// The pairs cross workgroups (and XCDs) through device-scope accesses only: stores and
+// loads with device coherence (relaxed atomics at agent scope, which the compiler emits as
+// plain loads and stores with that scope bit), the stores completed (vmcnt 0) before the
+// workgroup's barrier and its counter increment, the loads issued only by the workgroup
+// that saw the final count.  No L2 write-back or invalidation is needed for them (a fence
+// at agent scope would do both, once per wave, for data that never enters a non-coherent
+// cache line).
+struct XvHeadPair {
+    uint64_t ms;                // m (low word) and s (high word), fp32 bits
+    uint32_t n;                 // the block's argmax column
+    uint32_t pad;
+};
+static_assert(sizeof(XvHeadPair) == 16, "pair layout");
+
+struct XvHeadGreedy {
+    const int32_t* draft;       // int32 [B][T]
+    int32_t* ids;               // int32 [B][T]
+    int32_t* n_keep;            // int32 [B]
+    float* lp;                  // fp32 [B][T] or null
+    int32_t* kv_len;            // int32 [B] or null
+    XvHeadPair* pairs;          // [B T][N / 16]
+    int* counter;               // 0 on entry, 0 on exit
+    int B, T;
+};
+
+__device__ __forceinline__ void xv_pair_store(XvHeadPair* p, float m, float s, int n) {
+    const uint64_t ms = (uint64_t)__float_as_uint(m) | ((uint64_t)__float_as_uint(s) << 32);
+    __hip_atomic_store(&p->ms, ms, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p->n, (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void xv_pair_load(const XvHeadPair* p, float& m, float& s, int& n) {
+    const uint64_t ms = __hip_atomic_load(&p->ms, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    n = (int)__hip_atomic_load(&p->n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    m = __uint_as_float((uint32_t)ms);
+    s = __uint_as_float((uint32_t)(ms >> 32));
+}
+
+// dr: row tid's draft (tid < B T) and kv: kv_len[tid] (tid < B), loaded at the kernel's start
+// (nothing else writes them during the call); store_b: stores the second
+// block's outputs (after the pairs, so that the wait for the pair stores does not wait for them).
+template <typename StoreFn>
+__device__ __forceinline__ void xv_head_greedy_tail(const XvHeadGreedy& g, float za, float zb, int blk,
+                                                    int M, int N, int dr, int kv, StoreFn store_b)
+{
+    __shared__ int s_last;
+    __shared__ int s_ids[XV_TMAX], s_draft[XV_TMAX];
+    __shared__ float2 s_v[XV_TMAX][256];          // last workgroup: chain and tree values per row
+    __shared__ float s_bv[XV_TMAX][256];          // and the chains' argmax
+    __shared__ int s_bn[XV_TMAX][256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nb = N >> 4;
+    if (tid < 256) {                              // waves 0..3, uniform
+        const int rr = tid >> 4, cc = tid & 15;
+        const float z = za + zb;
+        float bm = z, best = z;
+        int bn = blk * 16 + cc;
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+            bm = fmaxf(bm, __shfl_xor(bm, off));
+            const float ov = __shfl_xor(best, off);
+            const int on = __shfl_xor(bn, off);
+            if (xv_better(ov, on, best, bn)) { best = ov; bn = on; }
+        }
+        float e = __builtin_amdgcn_exp2f((z - bm) * XV_LOG2E);
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) e = e + __shfl_xor(e, off);
+        if (cc == 0 && rr < M) xv_pair_store(g.pairs + (size_t)rr * nb + blk, bm, e, bn);
+        __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): the pair stores have completed
+        store_b();
+    }
+    if (tid < M) s_draft[tid] = dr;
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(g.counter, 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!s_last) return;                          // uniform over the workgroup
+    // chain c of row r (c < 256): the pairs of blocks c, c + 256, ... folded left to right
+    // from the empty pair, and the chain's argmax; all of a thread's first loads at once
+    float cm[4], cs[4], bv[4];
+    int bi[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {                 // tasks tid + 1024 u: row task / 256, chain task % 256
+        const int task = tid + u * XV_GEMM_THREADS, r = task >> 8, c = task & 255;
+        cm[u] = -INFINITY; cs[u] = 0.f; bv[u] = -INFINITY; bi[u] = N;
+        if (r < M && c < nb) xv_pair_load(g.pairs + (size_t)r * nb + c, bv[u], cs[u], bi[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int task = tid + u * XV_GEMM_THREADS, r = task >> 8, c = task & 255;
+        if (r >= M) continue;
+        if (c < nb) {
+            const float m1 = bv[u], s1 = cs[u];
+            cs[u] = 0.f;
+            xv_lse_add(cm[u], cs[u], m1, s1);
+        }
+        for (int b = c + 256; b < nb; b += 256) {
+            float m2, s2;
+            int n2;
+            xv_pair_load(g.pairs + (size_t)r * nb + b, m2, s2, n2);
+            xv_lse_add(cm[u], cs[u], m2, s2);
+            if (xv_better(m2, n2, bv[u], bi[u])) { bv[u] = m2; bi[u] = n2; }
+        }
+        s_v[r][c] = make_float2(cm[u], cs[u]);
+        s_bv[r][c] = bv[u];
+        s_bn[r][c] = bi[u];
+    }
+    __syncthreads();
+    // each group of 64 chains: the value of its butterfly (chain ^ 1, ^ 2, ..., ^ 32), which
+    // every lane of it ends with and lane 0's is a binary tree: at distance h the node at c
+    // (a multiple of 2h) becomes xv_lse_add(node c, node c + h)
+    for (int h = 1; h < 64; h <<= 1) {
+        const int per_row = 128 / h;
+        for (int task = tid; task < M * per_row; task += XV_GEMM_THREADS) {
+            const int r = task / per_row, c = (task % per_row) * 2 * h;
+            float2 a = s_v[r][c];
+            const float2 b = s_v[r][c + h];
+            xv_lse_add(a.x, a.y, b.x, b.y);
+            s_v[r][c] = a;
+        }
+        __syncthreads();
+    }
+    if (wave < M) {                               // row r = wave: the argmax over the chains, the four
+        const int r = wave;                       // groups folded left to right, id and logprob
+        float best = -INFINITY;
+        int bn = N;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = 64 * q + lane;
+            if (xv_better(s_bv[r][c], s_bn[r][c], best, bn)) { best = s_bv[r][c]; bn = s_bn[r][c]; }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(best, off);
+            const int on = __shfl_xor(bn, off);
+            if (xv_better(ov, on, best, bn)) { best = ov; bn = on; }
+        }
+        float m = s_v[r][0].x, sum = s_v[r][0].y;
+#pragma unroll
+        for (int q = 1; q < 4; ++q) xv_lse_add(m, sum, s_v[r][64 * q].x, s_v[r][64 * q].y);
+        if (lane == 0) {
+            const int id = bn < N ? bn : 0;
+            g.ids[r] = id;
+            if (g.lp) g.lp[r] = xv_neg_log(sum);
+            s_ids[r] = id;
+        }
+    }
+    __syncthreads();
+    if (tid < g.B) {
+        const int acc = xv_accepted(g.T, [&](int t) { return s_draft[tid * g.T + t]; },
+                                    [&](int t) { return s_ids[tid * g.T + t]; });
+        g.n_keep[tid] = acc + 1;
+        if (g.kv_len) g.kv_len[tid] = kv + acc + 1;
+    }
+    if (tid == 0) __hip_atomic_store(g.counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // W staged through LDS: the workgroup streams each column block's 16 rows with
 // 1 KB contiguous wave loads (each 16-byte granule of a stage is one thread's
 // load) into a padded LDS stage; each wave then reads the MFMA B fragments of its
@@ -177,9 +348,13 @@ static_assert(xv_frag_pitch(64) == 80 && xv_frag_pitch(320) == 336 && xv_frag_pi
 // flight.  x fragments of the wave's range live in registers.  Same K split,
 // MFMA chains and ordered sum as the other variants.
 // Requires K = NS * SL * 32 and SL * NS = 16 * KSW (the 16 ranges split evenly).
-template <int KSW, int SL, int NS>
+// GR: the head with its greedy acceptance; the grid is N / 16 workgroups of two problems
+// with N columns each and contig = 0, so that workgroup i computes column block i of
+// problem 0 and then of problem 1 (each wave reloads its x fragments right after its
+// MFMAs of the first block), then runs xv_head_greedy_tail.
+template <int KSW, int SL, int NS, bool GR>
 __global__ __launch_bounds__(XV_GEMM_THREADS)
-void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0, int contig)
+void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0, int contig, XvHeadGreedy hg)
 {
     static_assert(NS % 2 == 0 && SL * NS == XV_GEMM_WAVES * KSW, "stages must split the ranges evenly");
     static_assert(XV_GEMM_WAVES % NS == 0, "each stage must hold whole K ranges of the same number of waves");
@@ -214,11 +389,18 @@ void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0, int contig)
         const uint16_t* xp = x + (size_t)(ok ? row : M - 1) * K + (size_t)ks0 * 32 + lg * 8;
 #pragma unroll
         for (int j = 0; j < KSW; ++j) xr[j] = xv_load16(xp + j * 32);
+        // rows >= M: zeroed, or under GR left as copies of row M - 1 (MFMA rows are
+        // independent and those rows are never stored), so that the reload is not waited for here
+        if (!GR) {
 #pragma unroll
-        for (int j = 0; j < KSW; ++j) xr[j] = ok ? xr[j] : zero;
+            for (int j = 0; j < KSW; ++j) xr[j] = ok ? xr[j] : zero;
+        }
     };
     int cur = b0 >= nb0 ? 1 : 0;
     load_x(pp.x[cur]);
+    int dr = 0, kv = 0;                             // GR: row tid's draft, request tid's cache length
+    if (GR && tid < M) dr = hg.draft[tid];
+    if (GR && hg.kv_len && tid < hg.B) kv = hg.kv_len[tid];
 
     // this thread's granules: (row, 16-byte column) of a stage, the same for every stage
     int goff[GPT], loff[GPT];
@@ -243,6 +425,7 @@ void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0, int contig)
                 *reinterpret_cast<xv_u32x4*>(stage + loff[i]) = gr[i];
     };
     xv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float za = 0.f, zb = 0.f;                       // GR: this thread's sums of problems 0 and 1
 
     xv_u32x4 g0[GPT], g1[GPT];
     int blk = b0;
@@ -266,17 +449,32 @@ void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0, int contig)
 #pragma unroll
                 for (int j = 0; j < KSW; ++j)
                     acc = xv_mfma16x16x32(xr[j], *reinterpret_cast<const xv_u32x4*>(bp + j * 32), acc);
+                // GR: this wave's x fragments of problem 1, in flight through the block's other stages
+                if (GR && more && nb >= nb0 && cur == 0) load_x(pp.x[1]);
             }
         }
+        const bool cross = more && nb >= nb0 && cur == 0;   // uniform: next block in problem 1
         xv_f32x4 accs[1] = {acc};
-        xv_gemm_finish<1>(red, accs, lane, wave, blk - cur * nb0, mt0, M, pp.N[cur], pp.y[cur], pp.y32[cur]);
+        const float z = xv_gemm_finish<1>(red, accs, lane, wave, blk - cur * nb0, mt0, M, pp.N[cur], pp.y[cur],
+                                          pp.y32[cur], !(GR && cur == 1));
+        if (cur == 0) za = z;
+        else zb = z;
         acc = xv_f32x4{0.f, 0.f, 0.f, 0.f};
         if (!more) break;
         blk = nb;
-        if (blk >= nb0 && cur == 0) {               // uniform: crossing into problem 1
+        if (cross) {
             cur = 1;
-            load_x(pp.x[1]);
+            if (!GR) load_x(pp.x[1]);
         }
+    }
+    if constexpr (GR) {
+        xv_head_greedy_tail(hg, za, zb, b0, M, pp.N[0], dr, kv, [&] {
+            const int row = tid >> 4, col = b0 * 16 + (tid & 15), N1 = pp.N[1];
+            if (row < M) {
+                pp.y[1][(size_t)row * N1 + col] = xv_f32_to_bf16(zb);
+                if (pp.y32[1]) pp.y32[1][(size_t)row * N1 + col] = zb;
+            }
+        });
     }
 }
 
@@ -793,7 +991,16 @@ void xv_gemm_launch_wlds(const XvGemmPair& pp, int M, int K, int mt0, const XvLa
 {
     dim3 grid(xv_gemm_grid((pp.N[0] + pp.N[1]) / 16)), block(XV_GEMM_THREADS);
     const int contig = pp.N[1] > 0 && pp.x[0] != pp.x[1];
-    hipExtLaunchKernelGGL((xv_gemm_wlds_kernel<KSW, SL, NS>), grid, block, 0, lc.st, lc.e0, lc.e1, 0, pp, M, K, mt0, contig);
+    hipExtLaunchKernelGGL((xv_gemm_wlds_kernel<KSW, SL, NS, false>), grid, block, 0, lc.st, lc.e0, lc.e1, 0, pp, M,
+                          K, mt0, contig, XvHeadGreedy{});
+}
+
+// The head with greedy acceptance: N / 16 workgroups, block i of both problems each.
+template <int KSW, int SL, int NS>
+void xv_gemm_launch_head_greedy(const XvGemmPair& pp, int M, int K, const XvHeadGreedy& hg, const XvLaunch& lc)
+{
+    hipExtLaunchKernelGGL((xv_gemm_wlds_kernel<KSW, SL, NS, true>), dim3(pp.N[0] / 16), dim3(XV_GEMM_THREADS), 0,
+                          lc.st, lc.e0, lc.e1, 0, pp, M, K, 0, 0, hg);
 }
 
 // the LDS-staged variant serves one row tile and these K only
@@ -998,4 +1205,47 @@ extern "C" int xv_gemm_small_m_pair(const uint16_t* x0, const uint16_t* w0, uint
     const XvGemmPair pp{{x0, x1}, {w0, w1}, {y0, y1}, {y32_0, y32_1}, {N0, N1}};
     xv_gemm_launch_wlds_k(pp, M, K, 0, lc);
     return xv_launch_status();
+}
+
+extern "C" size_t xv_head_greedy_workspace_bytes(int B, int T, int N)
+{
+    const long long rows = B > 0 && T > 0 ? (long long)B * T : 0;
+    const long long nb = N > 0 ? (N + 15LL) / 16 : 0;
+    return (size_t)(256 + 16 * rows * nb);
+}
+
+extern "C" int xv_head_greedy_accept(const uint16_t* x_a, const uint16_t* w_a, uint16_t* y_a, float* logits_a,
+                                     const uint16_t* x_b, const uint16_t* w_b, uint16_t* y_b, float* logits_b,
+                                     const int32_t* draft, int32_t* ids, int32_t* n_keep, float* logprob,
+                                     int32_t* kv_len, void* workspace, size_t workspace_bytes,
+                                     int B, int T, int N, int K, void* stream)
+{
+    XV_REQUIRE(B >= 0 && B <= (1 << 20) && T >= 1 && T <= XV_TMAX, XV_ERR_SHAPE);
+    XV_REQUIRE(N >= 16 && N % 16 == 0 && K >= 32 && K % 32 == 0, XV_ERR_SHAPE);
+    if (B == 0) return XV_OK;
+    XV_REQUIRE(x_a && w_a && y_a && logits_a && x_b && w_b && y_b && logits_b && draft && ids && n_keep &&
+               workspace, XV_ERR_NULL);
+    XV_REQUIRE(xv_aligned16(x_a) && xv_aligned16(w_a) && xv_aligned(y_a, 2) && xv_aligned(logits_a, 4) &&
+               xv_aligned16(x_b) && xv_aligned16(w_b) && xv_aligned(y_b, 2) && xv_aligned(logits_b, 4) &&
+               xv_aligned(draft, 4) && xv_aligned(ids, 4) && xv_aligned(n_keep, 4) &&
+               xv_aligned(logprob, 4) && xv_aligned(kv_len, 4) && xv_aligned16(workspace), XV_ERR_ALIGN);
+    XV_REQUIRE(workspace_bytes >= xv_head_greedy_workspace_bytes(B, T, N), XV_ERR_WORKSPACE);
+    const int M = B * T;
+    if (M <= 16 && (K == 5120 || K == 6144)) {
+        // one row tile and the layer's K: the fused launch
+        (void)hipGetLastError();
+        const XvLaunch lc{reinterpret_cast<hipStream_t>(stream), nullptr, nullptr};
+        const XvGemmPair pp{{x_a, x_b}, {w_a, w_b}, {y_a, y_b}, {logits_a, logits_b}, {N, N}};
+        char* ws = static_cast<char*>(workspace);
+        const XvHeadGreedy hg{draft, ids, n_keep, logprob, kv_len, reinterpret_cast<XvHeadPair*>(ws + 256),
+                              reinterpret_cast<int*>(ws), B, T};
+        if (K == 5120) xv_gemm_launch_head_greedy<10, 40, 4>(pp, M, K, hg, lc);
+        else xv_gemm_launch_head_greedy<12, 48, 4>(pp, M, K, hg, lc);
+        return xv_launch_status();
+    }
+    // otherwise the pair and the greedy kernels (the same bits)
+    const int s = xv_gemm_small_m_pair(x_a, w_a, y_a, logits_a, N, x_b, w_b, y_b, logits_b, N, M, K, stream,
+                                       nullptr, nullptr);
+    if (s != XV_OK) return s;
+    return xv_greedy_accept(logits_a, logits_b, draft, B, T, N, ids, n_keep, logprob, kv_len, stream);
 }

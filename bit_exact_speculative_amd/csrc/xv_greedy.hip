@@ -10,17 +10,12 @@
 // row (running (value, index) per thread over a strided slice, then lane
 // shuffles and LDS across the waves) and optionally forms the id's logprob,
 // then one thread per request counts the accepted drafts.
-#include "xv_common.h"
+#include "xv_greedy_impl.h"
 
 namespace {
 
 constexpr int XV_GREEDY_THREADS = 256;
 constexpr int XV_GREEDY_WAVES = XV_GREEDY_THREADS / 64;
-constexpr int XV_TMAX = 16;           // verify rows per request, at most
-
-__device__ __forceinline__ bool xv_better(float v1, int n1, float v0, int n0) {
-    return v1 > v0 || (v1 == v0 && n1 < n0);
-}
 
 // One workgroup per verify row (grid T x B), one pass over the row: the argmax
 // of the logits and, when lp is given, the logprob of that id.  Thread t owns the
@@ -73,17 +68,6 @@ __device__ __forceinline__ void xv_row_block(const float* __restrict__ la, const
             if (lb) x[c] = x[c] + lb[row + nc];
         }
     }
-}
-
-constexpr float XV_LOG2E = 1.4426950408889634f;
-
-// (m, s) += (m2, s2) in the combination above
-__device__ __forceinline__ void xv_lse_add(float& m, float& s, float m2, float s2) {
-    const float mm = fmaxf(m, m2);
-    const float t1 = m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - mm) * XV_LOG2E);
-    const float t2 = m2 == -INFINITY ? 0.f : s2 * __builtin_amdgcn_exp2f((m2 - mm) * XV_LOG2E);
-    m = mm;
-    s = t1 + t2;
 }
 
 constexpr int XV_GREEDY_BPP = 2;      // blocks per thread per pass, all loaded before any compare
@@ -155,8 +139,7 @@ __device__ __forceinline__ void xv_row_fold(const float* sv, const int* sn, cons
     id = bn < N ? bn : 0;
     float m = sm[0], sum = ssum[0];
     for (int w = 1; w < XV_GREEDY_WAVES; ++w) xv_lse_add(m, sum, sm[w], ssum[w]);
-    constexpr float LN2 = 0.6931471805599453f;
-    lpv = -(__builtin_amdgcn_logf(sum) * LN2);
+    lpv = xv_neg_log(sum);
 }
 
 template <bool VEC>
@@ -191,20 +174,8 @@ __global__ void xv_accept_kernel(const int32_t* __restrict__ draft, const int32_
 {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= B) return;
-    int dr[XV_TMAX], id[XV_TMAX];
-#pragma unroll
-    for (int t = 0; t < XV_TMAX; ++t) {
-        const int tc = t < T ? t : T - 1;
-        dr[t] = draft[(size_t)b * T + tc];
-        id[t] = ids[(size_t)b * T + tc];
-    }
-    int acc = 0;
-    bool run = true;
-#pragma unroll
-    for (int t = 0; t + 1 < XV_TMAX; ++t) {
-        run = run && t + 1 < T && dr[t + 1] == id[t];
-        acc += run ? 1 : 0;
-    }
+    const int acc = xv_accepted(T, [&](int t) { return draft[(size_t)b * T + t]; },
+                                [&](int t) { return ids[(size_t)b * T + t]; });
     n_keep[b] = acc + 1;
     if (kv_len) kv_len[b] += acc + 1;
 }

@@ -9,8 +9,7 @@ decoding) and runs, on one stream:
   xv_split_projections  GDN q, k (L2-normalised), v, decay, beta; attention q, k, v
   xv_gdn_verify         GDN rows, S_in -> S_T
   xv_attn_verify_rows   attention rows, KV append (with the GDN rows: xv_gdn_attn_verify)
-  xv_gemm_small_m_pair  head logits from o_gdn and o_attn (one launch)
-  xv_greedy_accept      ids, logprobs, accepted rows
+  xv_head_greedy_accept head logits from o_gdn and o_attn, ids, logprobs, accepted rows
   xv_rollback_to_prefix state and KV length of the kept rows
 
 and emits ids[b][0 .. n_keep[b]-1]; the last one is the next root.  With
@@ -132,6 +131,14 @@ class Decoder:
         self.Lmax = Lmax
         self.scale = 1.0 / float(wl.d) ** 0.5
         self._rows = {}
+        self._hg = None
+
+    def _hg_ws(self, B: int, T: int) -> torch.Tensor:
+        """The head + greedy call's workspace (zero at allocation; each call leaves it so)."""
+        n = xv.xv_head_greedy_workspace_bytes(B, T, self.wl.NH)
+        if getattr(self, "_hg", None) is None or self._hg.numel() < n:
+            self._hg = torch.zeros((n,), dtype=torch.uint8, device=self.device)
+        return self._hg
 
     def rows(self, T: int, slot: int = 0) -> _Rows:
         key = (T, slot)
@@ -192,14 +199,11 @@ class Decoder:
             else:
                 self._pending, self._free = (R, K, O), (P, Q)
                 self._S, self._S2 = K, O     # the pending step's start state and S_T
-        xv.xv_gemm_small_m_pair(R.o_gdn.view(M, wl.Hv * wl.dv), self.Wh_g, R.lg, R.lg32,
-                                R.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, R.la, R.la32, stream=st)
-        if self.lazy:
-            xv.xv_greedy_accept(R.lg32.view(B, T, wl.NH), R.la32.view(B, T, wl.NH), tokens, R.ids,
-                                R.n_keep, R.lp, stream=st, kv_len=self.kv_len)
-        else:
-            xv.xv_greedy_accept(R.lg32.view(B, T, wl.NH), R.la32.view(B, T, wl.NH), tokens, R.ids,
-                                R.n_keep, R.lp, stream=st)
+        xv.xv_head_greedy_accept(R.o_gdn.view(M, wl.Hv * wl.dv), self.Wh_g, R.lg, R.lg32,
+                                 R.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, R.la, R.la32, tokens, R.ids,
+                                 R.n_keep, self._hg_ws(B, T), logprob=R.lp,
+                                 kv_len=self.kv_len if self.lazy else None, stream=st)
+        if not self.lazy:
             xv.xv_rollback_to_prefix(R.k, R.v, R.a, R.b, self._S, self._S2, self.kv_len, R.n_keep, stream=st)
             self._S, self._S2 = self._S2, self._S
         return R
@@ -247,12 +251,12 @@ class Decoder:
         xv.xv_embed_rows(oa.view(M, wl.Hq * wl.d), last, xa, stream=st)
         lg, la = e(B, wl.NH), e(B, wl.NH)
         lg32, la32 = f(B, wl.NH), f(B, wl.NH)
-        xv.xv_gemm_small_m_pair(xg, self.Wh_g, lg, lg32, xa, self.Wh_a, la, la32, stream=st)
         out = torch.empty((B, 1), dtype=torch.int32, device=dev)
         nk = torch.empty((B,), dtype=torch.int32, device=dev)
         lp = f(B, 1)
         toks = torch.from_numpy(np.ascontiguousarray(prompt[:, P - 1:])).to(dev)
-        xv.xv_greedy_accept(lg32.view(B, 1, wl.NH), la32.view(B, 1, wl.NH), toks, out, nk, lp, stream=st)
+        xv.xv_head_greedy_accept(xg, self.Wh_g, lg, lg32, xa, self.Wh_a, la, la32, toks, out, nk,
+                                 self._hg_ws(B, 1), logprob=lp, stream=st)
         return out[:, 0], lp[:, 0]
 
     def snapshot(self):

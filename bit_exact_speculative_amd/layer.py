@@ -7,8 +7,8 @@ KV cache, the verify rows) and runs, on one stream:
               x W1^T, x W2^T                     (xv_gemm_small_m_pair, M = B*T)
               GDN verify S_in -> S_out, o_gdn    (xv_gdn_verify)
               attention rows + KV append         (xv_attn_verify_rows)
-              synthetic head logits              (xv_gemm_small_m_pair on o_gdn and o_attn)
-              greedy ids, logprobs, accepted rows (xv_greedy_accept)
+              synthetic head logits, greedy ids, logprobs, accepted rows
+                                                 (xv_head_greedy_accept on o_gdn and o_attn)
               rollback to the accepted prefix    (xv_rollback_to_prefix)
   lazy_step()  the same step with the rollback folded into the next step's GDN
               launch (the kept rows are replayed there; the greedy kernel adds
@@ -109,6 +109,8 @@ class Layer:
             self.draft = dev(inp.draft, device)
             self.ids = torch.empty((B, T), dtype=torch.int32, device=device)
             self.lp = torch.empty((B, T), dtype=torch.float32, device=device)
+            self.hg_ws = torch.zeros((xv.xv_head_greedy_workspace_bytes(B, T, wl.NH),), dtype=torch.uint8,
+                                     device=device)
         self.n_keep = torch.full((B,), T, dtype=torch.int32, device=device)
         self.pending = False         # lazy mode: S_in -> S_out ran, its rollback has not
         self.S_kept = None           # lazy mode: the two further state buffers
@@ -189,6 +191,14 @@ class Layer:
                             self.draft, self.ids, self.n_keep, self.lp, stream=self.stream,
                             kv_len=self.kv_len if count_kv else None)
 
+    def head_greedy(self, count_kv: bool = False):
+        """head_gemms() and greedy(count_kv) in one xv_head_greedy_accept call (the same bits)."""
+        wl, M = self.wl, self.wl.M
+        xv.xv_head_greedy_accept(self.o_gdn.view(M, wl.Hv * wl.dv), self.Wh_g, self.lg, self.lg32,
+                                 self.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, self.la, self.la32,
+                                 self.draft, self.ids, self.n_keep, self.hg_ws, logprob=self.lp,
+                                 kv_len=self.kv_len if count_kv else None, stream=self.stream)
+
     def gdn_lazy(self):
         """GDN of a lazy step: the first one is xv_gdn_verify; later ones replay the previous
         step's kept rows (the same row buffers, n_keep from its greedy) from its start state,
@@ -231,8 +241,7 @@ class Layer:
         if self.has_gemm:
             self.gemms(events)
         self.gdn_attn_lazy()
-        self.head_gemms()
-        self.greedy(count_kv=True)
+        self.head_greedy(count_kv=True)
 
     def settle(self):
         """Lazy mode: the pending rollback (state only; the greedy kernel counted the KV
@@ -245,8 +254,7 @@ class Layer:
         self.pending = False
 
     def head(self):
-        self.head_gemms()
-        self.greedy()
+        self.head_greedy()
 
     def rollback(self, n_keep: Optional[torch.Tensor] = None):
         xv.xv_rollback_to_prefix(self.k, self.v, self.a, self.b, self.S_in, self.S_out, self.kv_len,

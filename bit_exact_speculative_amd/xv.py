@@ -34,7 +34,7 @@ _lib.xv_abi_version.argtypes = []
 _lib.xv_status_string.restype = ctypes.c_char_p
 _lib.xv_status_string.argtypes = [_I]
 # the argument lists below are those of this ABI version of include/xv.h
-ABI_VERSION = 5
+ABI_VERSION = 6
 if _lib.xv_abi_version() != ABI_VERSION:
     raise ImportError("libxv.so has ABI version %d, this binding expects %d; rebuild it"
                       % (_lib.xv_abi_version(), ABI_VERSION))
@@ -62,6 +62,10 @@ _lib.xv_rollback_to_prefix.restype = _I
 _lib.xv_rollback_to_prefix.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
 _lib.xv_greedy_accept.restype = _I
 _lib.xv_greedy_accept.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P]
+_lib.xv_head_greedy_workspace_bytes.restype = _S
+_lib.xv_head_greedy_workspace_bytes.argtypes = [_I, _I, _I]
+_lib.xv_head_greedy_accept.restype = _I
+_lib.xv_head_greedy_accept.argtypes = [_P] * 14 + [_S] + [_I] * 4 + [_P]
 _lib.xv_gdn_prefill.restype = _I
 _lib.xv_gdn_prefill.argtypes = [_P] * 9 + [_I] * 6 + [_P]
 _lib.xv_attn_prefill.restype = _I
@@ -366,6 +370,32 @@ def xv_greedy_accept(logits_a, logits_b, draft, ids, n_keep, logprob=None, strea
     _check("xv_greedy_accept", _lib.xv_greedy_accept(_ptr(logits_a), _ptr(logits_b), _ptr(draft),
                                                     B, T, N, _ptr(ids), _ptr(n_keep), _ptr(logprob),
                                                     _ptr(kv_len), _stream(stream)))
+
+
+def xv_head_greedy_workspace_bytes(B: int, T: int, N: int) -> int:
+    return int(_lib.xv_head_greedy_workspace_bytes(B, T, N))
+
+
+def xv_head_greedy_accept(x_a, w_a, y_a, logits_a, x_b, w_b, y_b, logits_b, draft, ids, n_keep,
+                          workspace, logprob=None, kv_len=None, stream=None):
+    """The head pair (x_a @ w_a^T, x_b @ w_b^T over M = B*T rows) and greedy acceptance on
+    logits_a + logits_b in one call: the outputs of xv_gemm_small_m_pair followed by
+    xv_greedy_accept.  workspace: a uint8 device tensor of xv_head_greedy_workspace_bytes
+    bytes, zero before its first use (each call leaves it ready for the next)."""
+    B, T = draft.shape
+    M, K = x_a.shape
+    N = w_a.shape[0]
+    if M != B * T or tuple(x_b.shape) != (M, K) or tuple(w_a.shape) != (N, K) or \
+            tuple(w_b.shape) != (N, K) or tuple(y_a.shape) != (M, N) or tuple(y_b.shape) != (M, N) or \
+            tuple(logits_a.shape) != (M, N) or tuple(logits_b.shape) != (M, N) or \
+            tuple(ids.shape) != (B, T) or tuple(n_keep.shape) != (B,) or \
+            (logprob is not None and tuple(logprob.shape) != (B, T)) or \
+            (kv_len is not None and tuple(kv_len.shape) != (B,)):
+        raise ValueError("xv_head_greedy_accept: shape mismatch")
+    _check("xv_head_greedy_accept", _lib.xv_head_greedy_accept(
+        _ptr(x_a), _ptr(w_a), _ptr(y_a), _ptr(logits_a), _ptr(x_b), _ptr(w_b), _ptr(y_b), _ptr(logits_b),
+        _ptr(draft), _ptr(ids), _ptr(n_keep), _ptr(logprob), _ptr(kv_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), B, T, N, K, _stream(stream)))
 
 
 def xv_embed_rows(table, tokens, x, stream=None):

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define XV_ABI_VERSION 5
+#define XV_ABI_VERSION 6
 
 typedef enum {
     XV_OK = 0,
@@ -341,6 +341,37 @@ int xv_rollback_to_prefix(const uint16_t* k, const uint16_t* v,
 int xv_greedy_accept(const float* logits_a, const float* logits_b, const int32_t* draft,
                      int B, int T, int N, int32_t* ids, int32_t* n_keep, float* logprob,
                      int32_t* kv_len, void* stream);
+
+/*
+ * The synthetic head and greedy acceptance in one call (the post's first
+ * paragraph: ids and logprobs of greedy decoding; its DeepGEMM paragraph: the
+ * head GEMM bound by reading the weights).  Exactly
+ *   xv_gemm_small_m_pair(x_a, w_a, y_a, logits_a, N, x_b, w_b, y_b, logits_b, N, B*T, K)
+ *   xv_greedy_accept(logits_a, logits_b, draft, B, T, N, ids, n_keep, logprob, kv_len)
+ * bit for bit, every output included.  With B*T <= 16 and K = 5120 or 6144 it is
+ * one launch: each workgroup computes one 16-column block of both halves and the
+ * block's part of the greedy reduction, and the last workgroup to finish folds
+ * them in xv_greedy_accept's order and counts the accepted drafts; otherwise it
+ * runs those two calls.
+ *   x_a, x_b : bf16 [B*T][K] [16B]     w_a, w_b : bf16 [N][K] [16B]
+ *   y_a, y_b : bf16 [B*T][N]           logits_a, logits_b : fp32 [B*T][N]
+ *   draft, ids, n_keep, logprob, kv_len : as xv_greedy_accept
+ *   workspace : [16B] device memory of workspace_bytes >=
+ *               xv_head_greedy_workspace_bytes(B, T, N), all zero before its
+ *               first use; each call returns it with its first 256 bytes zero
+ *               again (an arrival counter), so it needs no clearing between
+ *               calls.  Calls that share a workspace must not overlap in time
+ *               (other streams, other host threads).
+ * Inputs and outputs must not overlap.  Shapes: 0 <= B <= 2^20, 1 <= T <= 16,
+ * N >= 16 and N % 16 == 0, K >= 32 and K % 32 == 0 (XV_ERR_SHAPE otherwise);
+ * XV_ERR_WORKSPACE for a short workspace.  Logits must be finite.
+ */
+size_t xv_head_greedy_workspace_bytes(int B, int T, int N);
+int xv_head_greedy_accept(const uint16_t* x_a, const uint16_t* w_a, uint16_t* y_a, float* logits_a,
+                          const uint16_t* x_b, const uint16_t* w_b, uint16_t* y_b, float* logits_b,
+                          const int32_t* draft, int32_t* ids, int32_t* n_keep, float* logprob,
+                          int32_t* kv_len, void* workspace, size_t workspace_bytes,
+                          int B, int T, int N, int K, void* stream);
 
 /*
  * Token embedding rows in front of the projection GEMMs of a decoding step

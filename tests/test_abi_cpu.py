@@ -27,7 +27,8 @@ def test_every_header_symbol_is_exported(xv):
                           "xv_attn_chunk_tokens", "xv_abi_version", "xv_status_string",
                           "xv_greedy_accept", "xv_embed_rows", "xv_split_projections",
                           "xv_gemm_small_m_pair", "xv_gdn_verify_after", "xv_gdn_attn_verify",
-                          "xv_attn_prefill", "xv_gdn_prefill", "xv_attn_verify_rows_noalloc"}
+                          "xv_attn_prefill", "xv_gdn_prefill", "xv_attn_verify_rows_noalloc",
+                          "xv_head_greedy_accept", "xv_head_greedy_workspace_bytes"}
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -37,7 +38,7 @@ def test_every_header_symbol_is_exported(xv):
 
 
 def test_version_and_constants(xv):
-    assert xv.xv_abi_version() == xv.ABI_VERSION == 5
+    assert xv.xv_abi_version() == xv.ABI_VERSION == 6
     assert xv.xv_attn_chunk_tokens() == 256
     lib = xv.lib()
     assert lib.xv_status_string(0) == b"ok"
@@ -221,6 +222,24 @@ def test_greedy_argument_errors(xv):
     assert f(A, ODD, A, 1, 9, 4096, A, A, None, None, None) == -3
     assert f(A, None, A, 1, 9, 4096, A, A, A + 2, None, None) == -3     # logprob: fp32 alignment
     assert f(A, None, A, 1, 9, 4096, A, A, None, A + 2, None) == -3     # kv_len: int32 alignment
+
+
+def test_head_greedy_argument_errors(xv):
+    f = xv.lib().xv_head_greedy_accept
+    wsb = xv.xv_head_greedy_workspace_bytes(1, 9, 4096)
+    assert wsb == 256 + 16 * 9 * 256
+    assert xv.xv_head_greedy_workspace_bytes(0, 9, 4096) == 256
+    args = lambda **kw: [kw.get(k, v) for k, v in (
+        ("xa", A), ("wa", A), ("ya", A), ("la", A), ("xb", A), ("wb", A), ("yb", A), ("lb", A),
+        ("draft", A), ("ids", A), ("nk", A), ("lp", None), ("kv", None), ("ws", A), ("wsb", wsb),
+        ("B", 1), ("T", 9), ("N", 4096), ("K", 6144), ("st", None))]
+    assert f(*args(B=0)) == 0                          # nothing to do
+    assert f(*args(T=0)) == -2 and f(*args(T=17)) == -2 and f(*args(B=-1)) == -2
+    assert f(*args(N=4100)) == -2 and f(*args(K=6100)) == -2 and f(*args(N=0)) == -2
+    assert f(*args(xa=None)) == -1 and f(*args(lb=None)) == -1 and f(*args(ws=None)) == -1
+    assert f(*args(draft=None)) == -1 and f(*args(nk=None)) == -1
+    assert f(*args(wb=MIS)) == -3 and f(*args(ws=A + 4)) == -3 and f(*args(lp=A + 2)) == -3
+    assert f(*args(wsb=wsb - 1)) == -4
 
 
 def test_embed_and_split_argument_errors(xv):
