@@ -464,7 +464,7 @@ void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0, int contig, XvHea
         blk = nb;
         if (cross) {
             cur = 1;
-            if (!GR) load_x(pp.x[1]);
+            if (!GR && pp.x[1] != pp.x[0]) load_x(pp.x[1]);     // uniform; a shared x is kept
         }
     }
     if constexpr (GR) {
