@@ -126,10 +126,12 @@ def parse():
     return ap.parse_args()
 
 
-def build_layers(wl, Lmax, R, stream):
+def build_layers(wl, Lmax, R, stream, len_bound=True):
     """Inputs for workload wl, R resident layer replicas, and the bit-exact gate
     (verify == sequential decode on the same buffers, every output bit; three lazy steps
-    == three steps of verify + rollback, every state, cache and output bit)."""
+    == three steps of verify + rollback, every state, cache and output bit).  len_bound:
+    the layers pass their host bound on the lengths to the attention calls (the decode
+    sequence of the gate passes none)."""
     import torch
     from bit_exact_speculative_amd import inputs as gen
     from bit_exact_speculative_amd.layer import Layer
@@ -141,6 +143,7 @@ def build_layers(wl, Lmax, R, stream):
         base = Layer(inp, "cuda")                 # prefix state computed by the GPU path
         base.proj_fp32 = False                    # projections: bf16 outputs only
         base.out_fp32 = False                     # GDN / attention: bf16 outputs only
+        base.use_len_bound = len_bound
         gate = base.clone()
         gate.proj_fp32 = True
         gate.verify(rollback=False)
@@ -227,15 +230,15 @@ def lmax_for(wl, steps_per_replica_n1, steps_per_replica_full):
     return L0max + max(wl.T * (steps_per_replica_n1 + 4), wl.T * (steps_per_replica_full + 4))
 
 
-def extra_workload(name, stream, steps, warmup, R, capacity=None):
+def extra_workload(name, stream, steps, warmup, R, capacity=None, len_bound=True):
     """Verified draft tok/s of another workload (bit-exact gate included); capacity: the
-    cache's position count (default: the steps' need)."""
+    cache's position count (default: the steps' need); len_bound: as build_layers."""
     import torch
     from bit_exact_speculative_amd import inputs as gen
     wl = gen.WORKLOADS[name]
     per = (steps + warmup + R - 1) // R
     Lmax = lmax_for(wl, per, 0) if capacity is None else max(capacity, lmax_for(wl, per, 0))
-    _, layers, exact = build_layers(wl, Lmax, R, stream)
+    _, layers, exact = build_layers(wl, Lmax, R, stream, len_bound)
     ms, _, _ = run_steps(layers, stream, steps, warmup)
     ctx = wl.L0 if wl.L0 is not None else "%d-%d" % wl.L0_range
     res = {"ctx": ctx, "batch": wl.B, "tok_s": round(wl.B * wl.k_drafts / (ms * 1e-3), 1) if exact else None,
@@ -510,13 +513,21 @@ def main():
                 extras[name] = extra_workload(name, stream, steps, warmup, reps)
             except Exception as exc:                  # reported, never hides the headline line
                 extras[name] = {"error": "%s: %s" % (type(exc).__name__, exc)}
-        try:                                      # the launch command's context length, short rows
-            extras["short_capacity_262144"] = extra_workload("short", stream, 100, 10, 4, capacity=262144)
-            extras["short_capacity_262144"]["note"] = (
-                "the short workload in caches of 262,144 positions: the attention work split is chosen by "
-                "capacity (the lengths live on the device), here the streaming kernel and the long-row combine")
-        except Exception as exc:
-            extras["short_capacity_262144"] = {"error": "%s: %s" % (type(exc).__name__, exc)}
+        # the launch command's context length, short rows: with the host's bound on the lengths
+        # (the launch sized for the rows) and without it (sized for the capacity)
+        for key, lb, note in (
+                ("short_capacity_262144", True,
+                 "the short workload in caches of 262,144 positions; the layer passes its host bound on the "
+                 "lengths (max L0 + T per step), so the attention launch is sized for the rows: the per-tile "
+                 "split, in one launch with GDN"),
+                ("short_capacity_262144_no_bound", False,
+                 "as short_capacity_262144 without the bound: the launch is sized for the capacity (the "
+                 "streaming kernel and the long-row combine); the same bits")):
+            try:
+                extras[key] = extra_workload("short", stream, 100, 10, 4, capacity=262144, len_bound=lb)
+                extras[key]["note"] = note
+            except Exception as exc:
+                extras[key] = {"error": "%s: %s" % (type(exc).__name__, exc)}
         try:
             extras["composed"] = composed_workload(stream)
         except Exception as exc:

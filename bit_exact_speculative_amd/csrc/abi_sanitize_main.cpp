@@ -61,23 +61,25 @@ int main()
 
     // attention
     const size_t need = xv_attn_workspace_bytes(1, 9, 24, 256, 649);
-    EXPECT(xv_attn_verify_rows(A, A, A, A, A, I, A, nullptr, F, need, 0, 9, 24, 4, 256, 649, 0.0625f, nullptr), XV_OK);
-    EXPECT(xv_attn_verify_rows(A, A, A, A, A, I, A, nullptr, F, need, 1, 17, 24, 4, 256, 649, 0.0625f, nullptr),
+    EXPECT(xv_attn_verify_rows(A, A, A, A, A, I, A, nullptr, F, need, 0, 9, 24, 4, 256, 649, 0.0625f, 0, nullptr), XV_OK);
+    EXPECT(xv_attn_verify_rows(A, A, A, A, A, I, A, nullptr, F, need, 1, 17, 24, 4, 256, 649, 0.0625f, 0, nullptr),
            XV_ERR_SHAPE);
-    EXPECT(xv_attn_verify_rows(A, A, A, A, A, I, A, nullptr, F, need, 1, 9, 24, 4, 256, 649, NAN, nullptr),
+    EXPECT(xv_attn_verify_rows(A, A, A, A, A, I, A, nullptr, F, need, 1, 9, 24, 4, 256, 649, NAN, 0, nullptr),
            XV_ERR_SHAPE);
-    EXPECT(xv_attn_verify_rows(A, A, A, A, A, I, A, nullptr, nullptr, need, 1, 9, 24, 4, 256, 649, 0.0625f, nullptr),
+    EXPECT(xv_attn_verify_rows(A, A, A, A, A, I, A, nullptr, nullptr, need, 1, 9, 24, 4, 256, 649, 0.0625f, 0, nullptr),
            XV_ERR_NULL);
-    EXPECT(xv_attn_verify_rows(A, A, A, A, A, I, A, nullptr, F, need - 4, 1, 9, 24, 4, 256, 649, 0.0625f, nullptr),
+    EXPECT(xv_attn_verify_rows(A, A, A, A, A, I, A, nullptr, F, need - 4, 1, 9, 24, 4, 256, 649, 0.0625f, 0, nullptr),
            XV_ERR_WORKSPACE);
-    EXPECT(xv_attn_verify_rows_noalloc(A, A, A, A, A, I, A, nullptr, 1, 9, 24, 4, 256, 127744, 0.0625f, nullptr),
+    EXPECT(xv_attn_verify_rows_noalloc(A, A, A, A, A, I, A, nullptr, 1, 9, 24, 4, 256, 127744, 0.0625f, 0, nullptr),
            XV_ERR_WORKSPACE);
-    EXPECT(xv_attn_verify_rows_noalloc(MIS, A, A, A, A, I, A, nullptr, 1, 9, 24, 4, 256, 649, 0.0625f, nullptr),
+    EXPECT(xv_attn_verify_rows_noalloc(MIS, A, A, A, A, I, A, nullptr, 1, 9, 24, 4, 256, 649, 0.0625f, 0, nullptr),
            XV_ERR_ALIGN);
+    EXPECT(xv_attn_verify_rows(A, A, A, A, A, I, A, nullptr, F, need, 1, 9, 24, 4, 256, 649, 0.0625f, 8, nullptr),
+           XV_ERR_SHAPE);                       // a length bound below T
     EXPECT(xv_attn_prefill(A, A, A, A, A, I, A, nullptr, 1, 8, 24, 4, 96, 649, 0.0625f, 1, nullptr), XV_ERR_SHAPE);
     EXPECT(xv_gdn_attn_verify(A, A, A, F, F, nullptr, nullptr, nullptr, nullptr, nullptr, 0, F, nullptr, nullptr, G,
                               A, nullptr, 16, 48, 128, 128, A, A, A, A, A, I, A, nullptr, F, need,
-                              24, 4, 256, 649, 0.0625f, 1, 17, nullptr), XV_ERR_SHAPE);
+                              24, 4, 256, 649, 0.0625f, 1, 17, 0, nullptr), XV_ERR_SHAPE);
 
     // greedy, embedding, split, streaming read
     EXPECT(xv_greedy_accept(reinterpret_cast<float*>(A), nullptr, I, 1, 0, 4096, I, I, nullptr, nullptr, nullptr),

@@ -855,6 +855,7 @@ struct XvTileArgs {
     uint16_t* k_cache; uint16_t* v_cache; const int32_t* kv_len;
     float* ws_acc; float* ws_ml;
     int T, Hq, Hkv, Lmax, NC, NTILE, items, per_xcd;
+    int NCG;                    // chunks in the grid (NC, or fewer under a length bound); NC is the stride
     float scale_log2;
 };
 
@@ -880,7 +881,7 @@ __device__ __forceinline__ void xv_attn_tile_body(const XvTileArgs A, int bid, X
     const int32_t* __restrict__ kv_len = A.kv_len;
     float* __restrict__ ws_acc = A.ws_acc;
     float* __restrict__ ws_ml = A.ws_ml;
-    const int T = A.T, Hq = A.Hq, Hkv = A.Hkv, Lmax = A.Lmax, NC = A.NC, NTILE = A.NTILE;
+    const int T = A.T, Hq = A.Hq, Hkv = A.Hkv, Lmax = A.Lmax, NC = A.NC, NTILE = A.NTILE, NCG = A.NCG;
     const int items = A.items, per_xcd = A.per_xcd;
     const float scale_log2 = A.scale_log2;
     constexpr int C = XV_ATTN_C;
@@ -906,9 +907,9 @@ __device__ __forceinline__ void xv_attn_tile_body(const XvTileArgs A, int bid, X
     if (u >= items) return;
     const int dpart = u % DS;
     const int tile = (u / DS) % NTILE;
-    const int c = (u / (DS * NTILE)) % NC;
-    const int g = (u / (DS * NTILE * NC)) % Hkv;
-    const int b = u / (DS * NTILE * NC * Hkv);
+    const int c = (u / (DS * NTILE)) % NCG;
+    const int g = (u / (DS * NTILE * NCG)) % Hkv;
+    const int b = u / (DS * NTILE * NCG * Hkv);
     const int Hg = Hq / Hkv;
     const int P = Hg * T;
     int L0 = kv_len[b];
@@ -1311,41 +1312,43 @@ inline int xv_attn_tile_ds(int D, int B, int T, int Hq, int Hkv, int NC, long lo
 inline XvTileArgs xv_tile_args(int ds, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                                uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                                float* ws_acc, float* ws_ml, int B, int T, int Hq, int Hkv, int Lmax, int NC,
-                               float scale_log2) {
+                               int NCg, float scale_log2) {
     const int P = (Hq / Hkv) * T;
     const int ntile = (P + 15) / 16;
-    const int items = (int)xv_tile_items(B, T, Hq, Hkv, NC, ds);
+    const int items = (int)xv_tile_items(B, T, Hq, Hkv, NCg, ds);
     const int per_xcd = (items + 7) / 8;
     return XvTileArgs{q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
-                      T, Hq, Hkv, Lmax, NC, ntile, items, per_xcd, scale_log2};
+                      T, Hq, Hkv, Lmax, NC, ntile, items, per_xcd, NCg, scale_log2};
 }
 
 // scores are kept in log2 units: s * log2(e), so that 2^(s' - m') = e^(s - m)
 inline float xv_scale_log2(float scale) { return (float)((double)scale * 1.4426950408889634); }
 
+// NC: the capacity's chunks (the partials' stride); NCg: the chunks any row can see (NC, or
+// fewer under the caller's length bound), which sizes the grids and picks the kernels
 template <int D>
 int xv_attn_partials(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                      uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                      float* ws_acc, float* ws_ml,
-                     int B, int T, int Hq, int Hkv, int Lmax, int NC, float scale, hipStream_t st)
+                     int B, int T, int Hq, int Hkv, int Lmax, int NC, int NCg, float scale, hipStream_t st)
 {
     (void)hipGetLastError();
     const float scale_log2 = xv_scale_log2(scale);
-    const XvAttnKind kind = xv_attn_kind<D>(B, T, Hq, Hkv, NC);
+    const XvAttnKind kind = xv_attn_kind<D>(B, T, Hq, Hkv, NCg);
     if (kind == XV_ATTN_STREAM) {
         const int NG = (NC + XV_ATTN_G - 1) / XV_ATTN_G;
         const XvStreamArgs sa{q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml, nullptr, nullptr,
                               T, Hq, Hkv, Lmax, NC, NG, 0, scale_log2};
-        hipLaunchKernelGGL((xv_attn_stream_kernel<D, false>), dim3(xv_stream_wpg(B, Hkv, NC), Hkv, B),
+        hipLaunchKernelGGL((xv_attn_stream_kernel<D, false>), dim3(xv_stream_wpg(B, Hkv, NCg), Hkv, B),
                            dim3(XV_ATTN_WAVES * 64), 0, st, sa);
     } else if (kind == XV_ATTN_WIDE) {
-        hipLaunchKernelGGL(xv_attn_partial_wide_kernel<D>, dim3(NC, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st,
+        hipLaunchKernelGGL(xv_attn_partial_wide_kernel<D>, dim3(NCg, Hkv, B), dim3(XV_ATTN_WAVES * 64), 0, st,
                            q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
                            T, Hq, Hkv, Lmax, NC, scale_log2);
     } else {
-        const int ds = xv_attn_tile_ds(D, B, T, Hq, Hkv, NC, xv_cu_count());
+        const int ds = xv_attn_tile_ds(D, B, T, Hq, Hkv, NCg, xv_cu_count());
         const XvTileArgs ta = xv_tile_args(ds, q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
-                                           B, T, Hq, Hkv, Lmax, NC, scale_log2);
+                                           B, T, Hq, Hkv, Lmax, NC, NCg, scale_log2);
         if (D == 256 && ds == 2)
             hipLaunchKernelGGL((xv_attn_partial_tile_kernel<D, (D == 256 ? 2 : 1)>), dim3(8 * ta.per_xcd),
                                dim3(XV_ATTN_WAVES * 64), 0, st, ta);
@@ -1361,7 +1364,7 @@ int xv_attn_partials(const uint16_t* q, const uint16_t* k_new, const uint16_t* v
 // capacity's chunk count.
 template <int D>
 int xv_attn_combine(const float* ws_acc, const float* ws_ml, const int32_t* kv_len, uint16_t* o, float* o32,
-                    int B, int T, int Hq, int Lmax, int NC, bool stream, int wpg, hipStream_t st)
+                    int B, int T, int Hq, int Lmax, int NC, int NCg, bool stream, int wpg, hipStream_t st)
 {
     (void)hipGetLastError();
     const dim3 grid(Hq, T, B), block(D);
@@ -1371,7 +1374,7 @@ int xv_attn_combine(const float* ws_acc, const float* ws_ml, const int32_t* kv_l
     if (stream) {
         hipLaunchKernelGGL((xv_attn_combine_kernel<D, true, true>), grid, block, shmem, st,
                            ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC, NG, wpg);
-    } else if (NC > 2 * XV_COMBINE_U) {
+    } else if (NCg > 2 * XV_COMBINE_U) {
         hipLaunchKernelGGL((xv_attn_combine_kernel<D, true, false>), grid, block, shmem, st,
                            ws_acc, ws_ml, kv_len, o, o32, T, Hq, Lmax, NC, NG, 0);
     } else {
@@ -1385,14 +1388,14 @@ template <int D>
 int xv_attn_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                    uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                    uint16_t* o, float* o32, float* ws_acc, float* ws_ml,
-                   int B, int T, int Hq, int Hkv, int Lmax, int NC, float scale, hipStream_t st)
+                   int B, int T, int Hq, int Hkv, int Lmax, int NC, int NCg, float scale, hipStream_t st)
 {
     const int s = xv_attn_partials<D>(q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
-                                      B, T, Hq, Hkv, Lmax, NC, scale, st);
+                                      B, T, Hq, Hkv, Lmax, NC, NCg, scale, st);
     if (s != XV_OK) return s;
-    const bool stream = xv_attn_kind<D>(B, T, Hq, Hkv, NC) == XV_ATTN_STREAM;
-    return xv_attn_combine<D>(ws_acc, ws_ml, kv_len, o, o32, B, T, Hq, Lmax, NC, stream,
-                              stream ? xv_stream_wpg(B, Hkv, NC) : 0, st);
+    const bool stream = xv_attn_kind<D>(B, T, Hq, Hkv, NCg) == XV_ATTN_STREAM;
+    return xv_attn_combine<D>(ws_acc, ws_ml, kv_len, o, o32, B, T, Hq, Lmax, NC, NCg, stream,
+                              stream ? xv_stream_wpg(B, Hkv, NCg) : 0, st);
 }
 
 // GDN and the attention partials side by side in one launch: workgroups
@@ -1441,13 +1444,13 @@ extern "C" size_t xv_attn_workspace_bytes(int B, int T, int Hq, int d, int Lmax)
 
 namespace {
 
-// The argument checks of xv_attn_verify_rows; on success the chunk count and the
-// workspace's two parts.
+// The argument checks of xv_attn_verify_rows; on success the capacity's chunk count, the
+// chunks any row can see (the length bound's, when given) and the workspace's two parts.
 int xv_attn_check(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                   const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* kv_len,
                   const uint16_t* o, const float* o32, void* workspace, size_t workspace_bytes,
-                  int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
-                  int* NC, float** ws_acc, float** ws_ml, bool ws_pointer = true)
+                  int B, int T, int Hq, int Hkv, int d, int Lmax, float scale, int len_bound,
+                  int* NC, int* NCg, float** ws_acc, float** ws_ml, bool ws_pointer = true)
 {
     XV_REQUIRE(B >= 0 && T >= 1 && T <= 16 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, XV_ERR_SHAPE);
     XV_REQUIRE(d == 64 || d == 128 || d == 256, XV_ERR_SHAPE);
@@ -1458,6 +1461,7 @@ int xv_attn_check(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
         XV_REQUIRE(items <= (1LL << 30), XV_ERR_SHAPE);
     }
     XV_REQUIRE(scale == scale, XV_ERR_SHAPE);
+    XV_REQUIRE(len_bound == 0 || len_bound >= T, XV_ERR_SHAPE);
     if (B == 0) return XV_OK;
     XV_REQUIRE(q && k_new && v_new && k_cache && v_cache && kv_len && o && (workspace || !ws_pointer), XV_ERR_NULL);
     XV_REQUIRE(xv_aligned16(q) && xv_aligned16(k_new) && xv_aligned16(v_new) &&
@@ -1467,6 +1471,8 @@ int xv_attn_check(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
     const size_t need = xv_attn_ws(B, T, Hq, d, Lmax, &acc_bytes);
     XV_REQUIRE(workspace_bytes >= need, XV_ERR_WORKSPACE);
     *NC = (Lmax + XV_ATTN_C - 1) / XV_ATTN_C;
+    const int nb = len_bound > 0 && len_bound < Lmax ? (len_bound + XV_ATTN_C - 1) / XV_ATTN_C : *NC;
+    *NCg = nb < *NC ? nb : *NC;
     *ws_acc = reinterpret_cast<float*>(workspace);
     *ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + acc_bytes);
     return XV_OK;
@@ -1500,15 +1506,15 @@ namespace {
 int xv_attn_launch_d(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                      uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                      uint16_t* o, float* o32, float* ws_acc, float* ws_ml,
-                     int B, int T, int Hq, int Hkv, int d, int Lmax, int NC, float scale, hipStream_t st)
+                     int B, int T, int Hq, int Hkv, int d, int Lmax, int NC, int NCg, float scale, hipStream_t st)
 {
     switch (d) {
         case 64:  return xv_attn_launch<64>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
-                                            ws_ml, B, T, Hq, Hkv, Lmax, NC, scale, st);
+                                            ws_ml, B, T, Hq, Hkv, Lmax, NC, NCg, scale, st);
         case 128: return xv_attn_launch<128>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
-                                             ws_ml, B, T, Hq, Hkv, Lmax, NC, scale, st);
+                                             ws_ml, B, T, Hq, Hkv, Lmax, NC, NCg, scale, st);
         default:  return xv_attn_launch<256>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
-                                             ws_ml, B, T, Hq, Hkv, Lmax, NC, scale, st);
+                                             ws_ml, B, T, Hq, Hkv, Lmax, NC, NCg, scale, st);
     }
 }
 
@@ -1545,30 +1551,30 @@ extern "C" int xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, con
                                    uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                                    uint16_t* o, float* o32, void* workspace, size_t workspace_bytes,
                                    int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
-                                   void* stream)
+                                   int len_bound, void* stream)
 {
-    int NC = 0;
+    int NC = 0, NCg = 0;
     float* ws_acc = nullptr;
     float* ws_ml = nullptr;
     const int s = xv_attn_check(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, workspace, workspace_bytes,
-                                B, T, Hq, Hkv, d, Lmax, scale, &NC, &ws_acc, &ws_ml);
+                                B, T, Hq, Hkv, d, Lmax, scale, len_bound, &NC, &NCg, &ws_acc, &ws_ml);
     if (s != XV_OK || B == 0) return s;
     return xv_attn_launch_d(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc, ws_ml,
-                            B, T, Hq, Hkv, d, Lmax, NC, scale, reinterpret_cast<hipStream_t>(stream));
+                            B, T, Hq, Hkv, d, Lmax, NC, NCg, scale, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int xv_attn_verify_rows_noalloc(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                                            uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                                            uint16_t* o, float* o32,
                                            int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
-                                           void* stream)
+                                           int len_bound, void* stream)
 {
-    int NC = 0;
+    int NC = 0, NCg = 0;
     float* ws_acc = nullptr;
     float* ws_ml = nullptr;
     // every argument and the size first (no device call), then the buffer's address
     int s = xv_attn_check(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, nullptr, XV_SCRATCH_BYTES,
-                          B, T, Hq, Hkv, d, Lmax, scale, &NC, &ws_acc, &ws_ml, false);
+                          B, T, Hq, Hkv, d, Lmax, scale, len_bound, &NC, &NCg, &ws_acc, &ws_ml, false);
     if (s != XV_OK || B == 0) return s;
     void* ws = nullptr;
     s = xv_scratch_address(&ws);
@@ -1578,7 +1584,7 @@ extern "C" int xv_attn_verify_rows_noalloc(const uint16_t* q, const uint16_t* k_
     ws_acc = reinterpret_cast<float*>(ws);
     ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + acc_bytes);
     return xv_attn_launch_d(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc, ws_ml,
-                            B, T, Hq, Hkv, d, Lmax, NC, scale, reinterpret_cast<hipStream_t>(stream));
+                            B, T, Hq, Hkv, d, Lmax, NC, NCg, scale, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -1593,7 +1599,7 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
                                   uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                                   uint16_t* o_attn, float* o_attn32, void* workspace, size_t workspace_bytes,
                                   int Hq, int Hkv, int d, int Lmax, float scale,
-                                  int B, int T, void* stream)
+                                  int B, int T, int len_bound, void* stream)
 {
     XvGdnArgs ga{};
     int s = n_keep_prev
@@ -1601,11 +1607,11 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
                             state_in, state_prev_out, state_kept, state_out, o, o32, B, T, Hk, Hv, dk, dv)
         : xv_gdn_args_verify(ga, q, k, v, a, b, state_in, state_out, o, o32, B, T, Hk, Hv, dk, dv);
     if (s != XV_OK) return s;
-    int NC = 0;
+    int NC = 0, NCg = 0;
     float* ws_acc = nullptr;
     float* ws_ml = nullptr;
     s = xv_attn_check(q_attn, k_new, v_new, k_cache, v_cache, kv_len, o_attn, o_attn32, workspace,
-                      workspace_bytes, B, T, Hq, Hkv, d, Lmax, scale, &NC, &ws_acc, &ws_ml);
+                      workspace_bytes, B, T, Hq, Hkv, d, Lmax, scale, len_bound, &NC, &NCg, &ws_acc, &ws_ml);
     if (s != XV_OK || B == 0) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     // one launch when the attention partials take the tile split and both grids are
@@ -1615,9 +1621,9 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
     int cpt = 1, ds = 1;
     XvTileArgs ta{};
     switch (d) {
-        case 64:  fuse = xv_attn_kind<64>(B, T, Hq, Hkv, NC) == XV_ATTN_TILE; break;
-        case 128: fuse = xv_attn_kind<128>(B, T, Hq, Hkv, NC) == XV_ATTN_TILE; break;
-        default:  fuse = xv_attn_kind<256>(B, T, Hq, Hkv, NC) == XV_ATTN_TILE; break;
+        case 64:  fuse = xv_attn_kind<64>(B, T, Hq, Hkv, NCg) == XV_ATTN_TILE; break;
+        case 128: fuse = xv_attn_kind<128>(B, T, Hq, Hkv, NCg) == XV_ATTN_TILE; break;
+        default:  fuse = xv_attn_kind<256>(B, T, Hq, Hkv, NCg) == XV_ATTN_TILE; break;
     }
     if (fuse) {
         // the GDN workgroups take one column group each if everything fits, else two; the
@@ -1627,13 +1633,13 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
         const bool two_col = dv % (2 * XV_GDN_JW) == 0;
         fuse = false;
         for (int dsv = (d == 256 ? 2 : 1); dsv >= 1 && !fuse; --dsv) {
-            const long long n_attn = 8 * ((xv_tile_items(B, T, Hq, Hkv, NC, dsv) + 7) / 8);
+            const long long n_attn = 8 * ((xv_tile_items(B, T, Hq, Hkv, NCg, dsv) + 7) / 8);
             if (n_attn + gdn1 <= XV_FUSE_ONE_COL * cus) { fuse = true; cpt = 1; ds = dsv; }
             else if (two_col && n_attn + gdn1 / 2 <= XV_FUSE_TWO_COL * cus) { fuse = true; cpt = 2; ds = dsv; }
         }
         if (fuse)
             ta = xv_tile_args(ds, q_attn, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml, B, T, Hq, Hkv,
-                              Lmax, NC, xv_scale_log2(scale));
+                              Lmax, NC, NCg, xv_scale_log2(scale));
     }
     if (!fuse) {
         s = n_keep_prev
@@ -1642,7 +1648,7 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
             : xv_gdn_verify(q, k, v, a, b, state_in, state_out, o, o32, B, T, Hk, Hv, dk, dv, stream);
         if (s != XV_OK) return s;
         return xv_attn_verify_rows(q_attn, k_new, v_new, k_cache, v_cache, kv_len, o_attn, o_attn32, workspace,
-                                   workspace_bytes, B, T, Hq, Hkv, d, Lmax, scale, stream);
+                                   workspace_bytes, B, T, Hq, Hkv, d, Lmax, scale, len_bound, stream);
     }
     switch (d) {
         case 64:  s = xv_gdn_attn_fused<64>(ga, dk, cpt, ds, ta, B, st); break;
@@ -1651,9 +1657,9 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
     }
     if (s != XV_OK) return s;
     switch (d) {
-        case 64:  return xv_attn_combine<64>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, false, 0, st);
-        case 128: return xv_attn_combine<128>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, false, 0, st);
-        default:  return xv_attn_combine<256>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, false, 0, st);
+        case 64:  return xv_attn_combine<64>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, NCg, false, 0, st);
+        case 128: return xv_attn_combine<128>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, NCg, false, 0, st);
+        default:  return xv_attn_combine<256>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, NCg, false, 0, st);
     }
 }
 

@@ -116,6 +116,9 @@ class Decoder:
         self.Kc[:, :, :L] = _bf16(inp.k_cache, device)
         self.Vc[:, :, :L] = _bf16(inp.v_cache, device)
         self.kv_len = torch.from_numpy(inp.L0.astype(np.int32)).to(device)
+        # host upper bound on max(kv_len) (a step adds at most T rows, a prefill P): the
+        # attention launch is sized for _kv_hi + T positions, not the capacity (the same bits)
+        self._kv_hi = int(inp.L0.max()) if B else 0
         if S0 is None:
             self._S = prefix_state(inp, device, stream)
         else:
@@ -180,10 +183,11 @@ class Decoder:
         xv.xv_split_projections(R.y1, R.y2, R.q, R.k, R.v, R.a, R.b, R.qa, R.kn, R.vn, stream=st)
         if self.after_split is not None:
             self.after_split(self, R, tokens)
+        lb = min(self._kv_hi + T, self.Lmax)
         if not self.lazy:
             xv.xv_gdn_verify(R.q, R.k, R.v, R.a, R.b, self._S, self._S2, R.o_gdn, None, stream=st)
             xv.xv_attn_verify_rows(R.qa, R.kn, R.vn, self.Kc, self.Vc, self.kv_len, R.o_attn, None, R.ws,
-                                   self.scale, stream=st)
+                                   self.scale, len_bound=lb, stream=st)
         else:
             # GDN (after the pending step's rollback) and attention in one call
             if self._pending is None:
@@ -193,7 +197,8 @@ class Decoder:
                 K, O = self._free
                 out, prev = O, (Rp.k, Rp.v, Rp.a, Rp.b, Rp.n_keep, Q, K)
             xv.xv_gdn_attn_verify(R.q, R.k, R.v, R.a, R.b, self._S, out, R.o_gdn, R.qa, R.kn, R.vn,
-                                  self.Kc, self.Vc, self.kv_len, R.o_attn, R.ws, self.scale, prev=prev, stream=st)
+                                  self.Kc, self.Vc, self.kv_len, R.o_attn, R.ws, self.scale, prev=prev,
+                                  len_bound=lb, stream=st)
             if self._pending is None:
                 self._pending = (R, self._S, self._S2)
             else:
@@ -206,6 +211,7 @@ class Decoder:
         if not self.lazy:
             xv.xv_rollback_to_prefix(R.k, R.v, R.a, R.b, self._S, self._S2, self.kv_len, R.n_keep, stream=st)
             self._S, self._S2 = self._S2, self._S
+        self._kv_hi = lb
         return R
 
     def prefill(self, prompt, chunk: int = 8192):
@@ -243,6 +249,7 @@ class Decoder:
             self._S, self._S2 = self._S2, self._S
             xv.xv_attn_prefill(qa, kn, vn, self.Kc, self.Vc, self.kv_len, oa, None, self.scale, advance=True,
                                stream=st)
+            self._kv_hi = min(self._kv_hi + cp, self.Lmax)
         # the head and the greedy id of each request's last prompt row (rows gathered by the
         # library's row-copy kernel)
         last = torch.from_numpy((np.arange(B, dtype=np.int32) * cp + cp - 1).astype(np.int32)).to(dev)
@@ -267,6 +274,7 @@ class Decoder:
         S, Kc, Vc, kv = snap
         self._pending = None
         self._S.copy_(S); self.Kc.copy_(Kc); self.Vc.copy_(Vc); self.kv_len.copy_(kv)
+        self._kv_hi = int(kv.max()) if kv.numel() else 0
 
     def generate(self, root: np.ndarray, n_tokens: int,
                  drafts: Optional[Callable[[int, int, int], np.ndarray]] = None, k: int = 0,

@@ -82,6 +82,11 @@ class Layer:
         self.Vc = self.Vc0.clone()
         self.L0 = dev(inp.L0.astype(np.int32), device)
         self.kv_len = self.L0.clone()
+        # host upper bound on max(kv_len): each step adds at most T rows; the attention
+        # launch is sized for kv_hi + T positions instead of the capacity (the same bits)
+        self.L0_max = int(inp.L0.max()) if B else 0
+        self.kv_hi = self.L0_max
+        self.use_len_bound = True
         self.o_attn = torch.empty((B, T, wl.Hq, wl.d), dtype=torch.bfloat16, device=device)
         self.o_attn32 = torch.empty((B, T, wl.Hq, wl.d), dtype=torch.float32, device=device)
         wsb = xv.xv_attn_workspace_bytes(B, T, wl.Hq, wl.d, self.Lmax)
@@ -145,6 +150,15 @@ class Layer:
         self.Kc.copy_(self.Kc0)
         self.Vc.copy_(self.Vc0)
         self.kv_len.copy_(self.L0)
+        self.kv_hi = self.L0_max
+
+    def len_bound(self) -> int:
+        """The attention calls' len_bound: max(kv_len) + T at most (0: size for the capacity)."""
+        return min(self.kv_hi + self.T, self.Lmax) if self.use_len_bound else 0
+
+    def _grew(self):
+        """A call added up to T rows to kv_len."""
+        self.kv_hi = min(self.kv_hi + self.T, self.Lmax)
 
     # ------------------------------------------------------------------
     def gemm1(self):
@@ -175,7 +189,7 @@ class Layer:
     def attn(self):
         xv.xv_attn_verify_rows(self.qa, self.kn, self.vn, self.Kc, self.Vc, self.kv_len,
                                self.o_attn, self.o_attn32 if self.out_fp32 else None, self.ws,
-                               self.scale, stream=self.stream)
+                               self.scale, len_bound=self.len_bound(), stream=self.stream)
 
     def head_gemms(self):
         """Both halves of the synthetic head in one launch."""
@@ -190,6 +204,8 @@ class Layer:
         xv.xv_greedy_accept(self.lg32.view(self.B, self.T, wl.NH), self.la32.view(self.B, self.T, wl.NH),
                             self.draft, self.ids, self.n_keep, self.lp, stream=self.stream,
                             kv_len=self.kv_len if count_kv else None)
+        if count_kv:
+            self._grew()
 
     def head_greedy(self, count_kv: bool = False):
         """head_gemms() and greedy(count_kv) in one xv_head_greedy_accept call (the same bits)."""
@@ -198,6 +214,8 @@ class Layer:
                                  self.o_attn.view(M, wl.Hq * wl.d), self.Wh_a, self.la, self.la32,
                                  self.draft, self.ids, self.n_keep, self.hg_ws, logprob=self.lp,
                                  kv_len=self.kv_len if count_kv else None, stream=self.stream)
+        if count_kv:
+            self._grew()
 
     def gdn_lazy(self):
         """GDN of a lazy step: the first one is xv_gdn_verify; later ones replay the previous
@@ -229,7 +247,8 @@ class Layer:
         xv.xv_gdn_attn_verify(self.q, self.k, self.v, self.a, self.b, self.S_in, out, self.o_gdn,
                               self.qa, self.kn, self.vn, self.Kc, self.Vc, self.kv_len, self.o_attn, self.ws,
                               self.scale, o32=self.o_gdn32 if self.out_fp32 else None,
-                              o_attn32=self.o_attn32 if self.out_fp32 else None, prev=prev, stream=self.stream)
+                              o_attn32=self.o_attn32 if self.out_fp32 else None, prev=prev,
+                              len_bound=self.len_bound(), stream=self.stream)
         if self.pending:
             self.S_in, self.S_out, self.S_kept, self.S_next = self.S_kept, self.S_next, self.S_in, self.S_out
         self.pending = True
@@ -259,6 +278,7 @@ class Layer:
     def rollback(self, n_keep: Optional[torch.Tensor] = None):
         xv.xv_rollback_to_prefix(self.k, self.v, self.a, self.b, self.S_in, self.S_out, self.kv_len,
                                  self.n_keep if n_keep is None else n_keep, stream=self.stream)
+        self._grew()
 
     def verify(self, n_keep: Optional[torch.Tensor] = None, rollback: bool = True):
         """One speculative step; n_keep overrides the greedy acceptance when given."""

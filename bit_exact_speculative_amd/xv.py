@@ -34,7 +34,7 @@ _lib.xv_abi_version.argtypes = []
 _lib.xv_status_string.restype = ctypes.c_char_p
 _lib.xv_status_string.argtypes = [_I]
 # the argument lists below are those of this ABI version of include/xv.h
-ABI_VERSION = 6
+ABI_VERSION = 7
 if _lib.xv_abi_version() != ABI_VERSION:
     raise ImportError("libxv.so has ABI version %d, this binding expects %d; rebuild it"
                       % (_lib.xv_abi_version(), ABI_VERSION))
@@ -52,10 +52,10 @@ _lib.xv_attn_workspace_bytes.restype = _S
 _lib.xv_attn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.xv_attn_verify_rows.restype = _I
 _lib.xv_attn_verify_rows.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
-                                     _I, _I, _I, _I, _I, _I, _F, _P]
+                                     _I, _I, _I, _I, _I, _I, _F, _I, _P]
 _lib.xv_attn_verify_rows_noalloc.restype = _I
 _lib.xv_attn_verify_rows_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P,
-                                             _I, _I, _I, _I, _I, _I, _F, _P]
+                                             _I, _I, _I, _I, _I, _I, _F, _I, _P]
 _lib.xv_stream_read.restype = _I
 _lib.xv_stream_read.argtypes = [_P, _S, _P, _S, _P, _I, _P, _P, _P]
 _lib.xv_rollback_to_prefix.restype = _I
@@ -72,7 +72,7 @@ _lib.xv_attn_prefill.restype = _I
 _lib.xv_attn_prefill.argtypes = [_P] * 8 + [_I] * 6 + [_F, _I, _P]
 _lib.xv_gdn_attn_verify.restype = _I
 _lib.xv_gdn_attn_verify.argtypes = ([_P] * 10 + [_I] + [_P] * 6 + [_I] * 4 + [_P] * 9 + [_S] +
-                                    [_I] * 4 + [_F] + [_I, _I, _P])
+                                    [_I] * 4 + [_F] + [_I, _I, _I, _P])
 _lib.xv_gdn_verify_after.restype = _I
 _lib.xv_gdn_verify_after.argtypes = [_P] * 10 + [_I] + [_P] * 6 + [_I] * 6 + [_P]
 _lib.xv_embed_rows.restype = _I
@@ -222,11 +222,11 @@ def xv_gdn_verify_after(q, k, v, a, b, k_prev, v_prev, a_prev, b_prev, n_keep_pr
 
 def xv_gdn_attn_verify(q, k, v, a, b, state_in, state_out, o, q_attn, k_new, v_new, k_cache, v_cache,
                        kv_len, o_attn, workspace, scale=None, o32=None, o_attn32=None, prev=None,
-                       stream=None):
+                       len_bound=0, stream=None):
     """GDN verify and attention verify rows in one call (one launch when they fit the chip).
     prev: None (as xv_gdn_verify), or (k_prev, v_prev, a_prev, b_prev, n_keep_prev,
     state_prev_out, state_kept) for xv_gdn_verify_after from state_in; then as
-    xv_attn_verify_rows."""
+    xv_attn_verify_rows (len_bound: 0, or an upper bound on kv_len[b] + T)."""
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     Hq, d = q_attn.shape[2], q_attn.shape[3]
@@ -259,7 +259,7 @@ def xv_gdn_attn_verify(q, k, v, a, b, state_in, state_out, o, q_attn, k_new, v_n
         _ptr(state_in), _ptr(sp), _ptr(sk), _ptr(state_out), _ptr(o), _ptr(o32), Hk, Hv, dk, dv,
         _ptr(q_attn), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
         _ptr(o_attn), _ptr(o_attn32), _ptr(workspace), wbytes, Hq, Hkv, d, Lmax, float(scale),
-        B, T, _stream(stream)))
+        B, T, int(len_bound), _stream(stream)))
 
 
 def xv_gdn_prefill(q, k, v, a, b, state_in, state_out, o, o32=None, stream=None):
@@ -297,8 +297,9 @@ def xv_attn_prefill(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32=None, scal
 
 
 def xv_attn_verify_rows(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32=None, workspace=None,
-                        scale=None, stream=None):
-    """Attention rows + KV append.  q [B][T][Hq][d]; caches [B][Hkv][Lmax][d]; kv_len int32 [B]."""
+                        scale=None, len_bound=0, stream=None):
+    """Attention rows + KV append.  q [B][T][Hq][d]; caches [B][Hkv][Lmax][d]; kv_len int32 [B];
+    len_bound: 0, or an upper bound on kv_len[b] + T that sizes the launch (the same bits)."""
     B, T, Hq, d = q.shape
     Hkv = k_new.shape[2]
     Lmax = k_cache.shape[2]
@@ -315,11 +316,11 @@ def xv_attn_verify_rows(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32=None, 
     _check("xv_attn_verify_rows", _lib.xv_attn_verify_rows(
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
         _ptr(o), _ptr(o32), _ptr(workspace), wbytes, B, T, Hq, Hkv, d, Lmax, float(scale),
-        _stream(stream)))
+        int(len_bound), _stream(stream)))
 
 
 def xv_attn_verify_rows_noalloc(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32=None, scale=None,
-                                stream=None):
+                                len_bound=0, stream=None):
     """xv_attn_verify_rows with the library's own device buffer for the partials (no workspace)."""
     B, T, Hq, d = q.shape
     Hkv = k_new.shape[2]
@@ -333,7 +334,7 @@ def xv_attn_verify_rows_noalloc(q, k_new, v_new, k_cache, v_cache, kv_len, o, o3
         scale = 1.0 / float(d) ** 0.5
     _check("xv_attn_verify_rows_noalloc", _lib.xv_attn_verify_rows_noalloc(
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
-        _ptr(o), _ptr(o32), B, T, Hq, Hkv, d, Lmax, float(scale), _stream(stream)))
+        _ptr(o), _ptr(o32), B, T, Hq, Hkv, d, Lmax, float(scale), int(len_bound), _stream(stream)))
 
 
 def xv_stream_read(src0, src1, sink, start_event=None, stop_event=None, stream=None):

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define XV_ABI_VERSION 6
+#define XV_ABI_VERSION 7
 
 typedef enum {
     XV_OK = 0,
@@ -203,10 +203,18 @@ int xv_gdn_verify_after(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *   o        : bf16 [B][T][Hq][d]
  *   o32      : fp32 [B][T][Hq][d] or NULL
  *   workspace: [16B] device scratch of workspace_bytes >= xv_attn_workspace_bytes(B,T,Hq,d,Lmax)
+ *   len_bound: 0, or an upper bound on kv_len[b] + T over the batch, known to
+ *              the caller (a serving loop tracks its lengths): the launch is then
+ *              sized for that many positions instead of the capacity Lmax (in a
+ *              262,144-position cache, rows of a few hundred positions keep the
+ *              per-tile split and the shared GDN launch).  The results are the
+ *              same bits whatever the bound, as long as it holds; a request with
+ *              kv_len[b] + T above a nonzero bound gets undefined outputs (memory
+ *              accesses stay within the buffers).
  * Shapes: B >= 0, 1 <= T <= 16, Hq % Hkv == 0, d in {64, 128, 256}, Lmax >= T,
  * ceil(Lmax / chunk) <= 4608, B * Hkv * ceil(Lmax / chunk) * ceil((Hq/Hkv) * T / 16)
- * <= 2^29 (the grid;
- * XV_ERR_SHAPE otherwise).  Device precondition: 0 <= L0 and
+ * <= 2^29 (the grid), len_bound == 0 or len_bound >= T
+ * (XV_ERR_SHAPE otherwise).  Device precondition: 0 <= L0 and
  * L0 + T <= Lmax (kernels clamp positions to the buffer otherwise).
  * Cache positions >= L0 + T are never read, so they may hold anything.
  */
@@ -216,7 +224,7 @@ int    xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, const uint1
                            uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                            uint16_t* o, float* o32, void* workspace, size_t workspace_bytes,
                            int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
-                           void* stream);
+                           int len_bound, void* stream);
 
 /*
  * xv_attn_verify_rows for callers that cannot allocate (code under HIP graph
@@ -238,7 +246,7 @@ int xv_attn_verify_rows_noalloc(const uint16_t* q, const uint16_t* k_new, const 
                                 uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                                 uint16_t* o, float* o32,
                                 int B, int T, int Hq, int Hkv, int d, int Lmax, float scale,
-                                void* stream);
+                                int len_bound, void* stream);
 
 /*
  * GDN verify and attention verify rows in one call.  The two are independent
@@ -257,7 +265,7 @@ int xv_attn_verify_rows_noalloc(const uint16_t* q, const uint16_t* k_new, const 
  * followed by
  *   xv_attn_verify_rows(q_attn, k_new, v_new, k_cache, v_cache, kv_len, o_attn,
  *                       o_attn32, workspace, workspace_bytes, B, T, Hq, Hkv, d,
- *                       Lmax, scale)
+ *                       Lmax, scale, len_bound)
  * with each argument's meaning, layout, shape rule and error code as there
  * (the first failing check is reported; nothing is launched then).  The GDN
  * buffers and the attention buffers must not overlap.
@@ -274,7 +282,7 @@ int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                        uint16_t* o_attn, float* o_attn32, void* workspace, size_t workspace_bytes,
                        int Hq, int Hkv, int d, int Lmax, float scale,
-                       int B, int T, void* stream);
+                       int B, int T, int len_bound, void* stream);
 
 /*
  * Attention of P prompt rows at once (prefill; launch command: chunked prefill).

@@ -38,7 +38,7 @@ def test_every_header_symbol_is_exported(xv):
 
 
 def test_version_and_constants(xv):
-    assert xv.xv_abi_version() == xv.ABI_VERSION == 6
+    assert xv.xv_abi_version() == xv.ABI_VERSION == 7
     assert xv.xv_attn_chunk_tokens() == 256
     lib = xv.lib()
     assert lib.xv_status_string(0) == b"ok"
@@ -139,12 +139,13 @@ def test_gdn_attn_argument_errors(xv):
     S = [A + 0x100000 * i for i in range(4)]
 
     def call(nk=None, kp=None, si=S[0], sp=None, sk=None, so=S[1], T=9, dk=128, d=256, B=1, wsb=need,
-             q=A, qa=A, kvl=A, Tp=0):
+             q=A, qa=A, kvl=A, Tp=0, lb=0):
         return f(q, A, A, A, A, kp, kp, kp, kp, nk, Tp, si, sp, sk, so, A, None, 16, 48, dk, 128,
-                 qa, A, A, A, A, kvl, A, None, A, wsb, 24, 4, d, 649, 0.0625, B, T, None)
+                 qa, A, A, A, A, kvl, A, None, A, wsb, 24, 4, d, 649, 0.0625, B, T, lb, None)
 
     assert call(B=0) == 0
     assert call(T=17) == -2 and call(dk=96) == -2 and call(d=96) == -2
+    assert call(lb=8) == -2 and call(lb=-1) == -2                # a length bound below T
     assert call(q=None) == -1 and call(qa=None) == -1 and call(kvl=None) == -1
     assert call(so=S[0]) == -6                                  # GDN state_out aliases state_in
     assert call(wsb=need - 4) == -4
@@ -170,11 +171,12 @@ def test_attn_argument_errors(xv):
     f = xv.lib().xv_attn_verify_rows
     need = xv.xv_attn_workspace_bytes(1, 9, 24, 256, 649)
 
-    def call(ws=A, wsb=need, B=1, T=9, Hq=24, Hkv=4, d=256, Lmax=649, q=A, kvl=A, scale=0.0625):
-        return f(q, A, A, A, A, kvl, A, None, ws, wsb, B, T, Hq, Hkv, d, Lmax, scale, None)
+    def call(ws=A, wsb=need, B=1, T=9, Hq=24, Hkv=4, d=256, Lmax=649, q=A, kvl=A, scale=0.0625, lb=0):
+        return f(q, A, A, A, A, kvl, A, None, ws, wsb, B, T, Hq, Hkv, d, Lmax, scale, lb, None)
 
-    assert call(B=0) == 0
+    assert call(B=0) == 0 and call(B=0, lb=649) == 0
     assert call(T=17) == -2 and call(Hq=25) == -2 and call(d=96) == -2 and call(Lmax=8) == -2
+    assert call(lb=8) == -2 and call(lb=-5) == -2                # a length bound below T
     assert call(B=1 << 13, T=16, Hq=64, Hkv=64, Lmax=1 << 20) == -2   # grid past 2^30 workgroups
     assert call(scale=float("nan")) == -2
     assert call(q=None) == -1 and call(kvl=None) == -1 and call(ws=None) == -1
@@ -188,8 +190,8 @@ def test_attn_noalloc_argument_errors(xv):
     f = xv.lib().xv_attn_verify_rows_noalloc
     limit = 32 << 20
 
-    def call(B=1, T=9, Hq=24, Hkv=4, d=256, Lmax=649, q=A, kvl=A, o=A, scale=0.0625):
-        return f(q, A, A, A, A, kvl, o, None, B, T, Hq, Hkv, d, Lmax, scale, None)
+    def call(B=1, T=9, Hq=24, Hkv=4, d=256, Lmax=649, q=A, kvl=A, o=A, scale=0.0625, lb=0):
+        return f(q, A, A, A, A, kvl, o, None, B, T, Hq, Hkv, d, Lmax, scale, lb, None)
 
     assert call(B=0) == 0
     assert call(T=17) == -2 and call(Hq=25) == -2 and call(d=96) == -2 and call(Lmax=8) == -2
