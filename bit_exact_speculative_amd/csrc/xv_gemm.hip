@@ -230,26 +230,30 @@ __device__ __forceinline__ void xv_head_greedy_tail(const XvHeadGreedy& g, float
 {
     __shared__ int s_last;
     __shared__ int s_ids[XV_TMAX], s_draft[XV_TMAX];
-    __shared__ float2 s_v[XV_TMAX][256];          // last workgroup: chain and tree values per row
-    __shared__ float s_bv[XV_TMAX][256];          // and the chains' argmax
+    __shared__ float s_cm[XV_TMAX][256], s_cs[XV_TMAX][256], s_bv[XV_TMAX][256];   // last workgroup: chains
     __shared__ int s_bn[XV_TMAX][256];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int nb = N >> 4;
-    if (tid < 256) {                              // waves 0..3, uniform
+    if (tid < 256) {                              // waves 0..3, uniform: row tid / 16, column tid % 16
         const int rr = tid >> 4, cc = tid & 15;
         const float z = za + zb;
         float bm = z, best = z;
         int bn = blk * 16 + cc;
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) {
-            bm = fmaxf(bm, __shfl_xor(bm, off));
-            const float ov = __shfl_xor(best, off);
-            const int on = __shfl_xor(bn, off);
+        // the block's maximum and argmax (exact in any order), then the sum of e^(z - m) in the
+        // butterfly order c ^ 8, ^ 4, ^ 2, ^ 1 (each lane adds its partner's value to its own)
+        auto mx = [&](float ov, int on) {
+            bm = fmaxf(bm, ov);
             if (xv_better(ov, on, best, bn)) { best = ov; bn = on; }
-        }
+        };
+        mx(xv_dpp<XV_DPP_ROR8>(best), xv_dpp<XV_DPP_ROR8>(bn));
+        mx(xv_dpp<XV_DPP_ROR12>(best), xv_dpp<XV_DPP_ROR12>(bn));
+        mx(xv_dpp<XV_DPP_XOR2>(best), xv_dpp<XV_DPP_XOR2>(bn));
+        mx(xv_dpp<XV_DPP_XOR1>(best), xv_dpp<XV_DPP_XOR1>(bn));
         float e = __builtin_amdgcn_exp2f((z - bm) * XV_LOG2E);
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) e = e + __shfl_xor(e, off);
+        e = e + xv_dpp<XV_DPP_ROR8>(e);
+        e = e + xv_dpp<XV_DPP_ROR12>(e);
+        e = e + xv_dpp<XV_DPP_XOR2>(e);
+        e = e + xv_dpp<XV_DPP_XOR1>(e);
         if (cc == 0 && rr < M) xv_pair_store(g.pairs + (size_t)rr * nb + blk, bm, e, bn);
         __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): the pair stores have completed
         store_b();
@@ -259,73 +263,100 @@ __device__ __forceinline__ void xv_head_greedy_tail(const XvHeadGreedy& g, float
     if (tid == 0) s_last = atomicAdd(g.counter, 1) == (int)gridDim.x - 1;
     __syncthreads();
     if (!s_last) return;                          // uniform over the workgroup
-    // chain c of row r (c < 256): the pairs of blocks c, c + 256, ... folded left to right
-    // from the empty pair, and the chain's argmax; all of a thread's first loads at once
-    float cm[4], cs[4], bv[4];
-    int bi[4];
+    // The last workgroup.  Chain c (c < 256) of row r folds blocks c, c + 256, ... left to right
+    // from the empty pair; thread tid forms chains tid + 1024 u (row task / 256, chain task % 256),
+    // so that each wave's loads read 64 consecutive pairs, all of a thread's loads issued together.
+    const int nu = (M * 256 + XV_GEMM_THREADS - 1) / XV_GEMM_THREADS;   // uniform
+    {
+        float cm[4], cs[4], bv[4];
+        int bi[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {                 // tasks tid + 1024 u: row task / 256, chain task % 256
-        const int task = tid + u * XV_GEMM_THREADS, r = task >> 8, c = task & 255;
-        cm[u] = -INFINITY; cs[u] = 0.f; bv[u] = -INFINITY; bi[u] = N;
-        if (r < M && c < nb) xv_pair_load(g.pairs + (size_t)r * nb + c, bv[u], cs[u], bi[u]);
-    }
+        for (int u = 0; u < 4; ++u) {             // straight-line: tasks past the rows read pair 0
+            const int task = tid + u * XV_GEMM_THREADS, r = task >> 8, c = task & 255;
+            const size_t at = u < nu && r < M ? (size_t)r * nb + (c < nb ? c : nb - 1) : 0;
+            xv_pair_load(g.pairs + at, bv[u], cs[u], bi[u]);
+        }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int task = tid + u * XV_GEMM_THREADS, r = task >> 8, c = task & 255;
-        if (r >= M) continue;
-        if (c < nb) {
+        for (int u = 0; u < 4; ++u) {
+            const int task = tid + u * XV_GEMM_THREADS, r = task >> 8, c = task & 255;
+            if (u >= nu || r >= M) continue;      // uniform per wave
+            const bool ok = c < nb;
             const float m1 = bv[u], s1 = cs[u];
+            cm[u] = -INFINITY;
             cs[u] = 0.f;
-            xv_lse_add(cm[u], cs[u], m1, s1);
+            xv_lse_add(cm[u], cs[u], ok ? m1 : -INFINITY, ok ? s1 : 0.f);
+            bv[u] = ok ? bv[u] : -INFINITY;
+            bi[u] = ok ? bi[u] : N;
+            for (int b = c + 256; b < nb; b += 256) {
+                float m2, s2;
+                int n2;
+                xv_pair_load(g.pairs + (size_t)r * nb + b, m2, s2, n2);
+                xv_lse_add(cm[u], cs[u], m2, s2);
+                if (xv_better(m2, n2, bv[u], bi[u])) { bv[u] = m2; bi[u] = n2; }
+            }
+            s_cm[r][c] = cm[u];
+            s_cs[r][c] = cs[u];
+            s_bv[r][c] = bv[u];
+            s_bn[r][c] = bi[u];
         }
-        for (int b = c + 256; b < nb; b += 256) {
-            float m2, s2;
-            int n2;
-            xv_pair_load(g.pairs + (size_t)r * nb + b, m2, s2, n2);
-            xv_lse_add(cm[u], cs[u], m2, s2);
-            if (xv_better(m2, n2, bv[u], bi[u])) { bv[u] = m2; bi[u] = n2; }
-        }
-        s_v[r][c] = make_float2(cm[u], cs[u]);
-        s_bv[r][c] = bv[u];
-        s_bn[r][c] = bi[u];
     }
     __syncthreads();
-    // each group of 64 chains: the value of its butterfly (chain ^ 1, ^ 2, ..., ^ 32), which
-    // every lane of it ends with and lane 0's is a binary tree: at distance h the node at c
-    // (a multiple of 2h) becomes xv_lse_add(node c, node c + h)
-    for (int h = 1; h < 64; h <<= 1) {
-        const int per_row = 128 / h;
-        for (int task = tid; task < M * per_row; task += XV_GEMM_THREADS) {
-            const int r = task / per_row, c = (task % per_row) * 2 * h;
-            float2 a = s_v[r][c];
-            const float2 b = s_v[r][c + h];
-            xv_lse_add(a.x, a.y, b.x, b.y);
-            s_v[r][c] = a;
-        }
-        __syncthreads();
-    }
-    if (wave < M) {                               // row r = wave: the argmax over the chains, the four
-        const int r = wave;                       // groups folded left to right, id and logprob
-        float best = -INFINITY;
-        int bn = N;
+    // Thread t < 32 M: row r = t / 32, group q = (t / 8) % 4 of 64 chains, chains 64 q + 8 k + j
+    // (k = t % 8, j = 0..7).  The group's tree (node c at distance h becomes lse(node c,
+    // node c + h)) runs over j in registers for h = 1, 2, 4 and across the group's 8 lanes for
+    // h = 8, 16, 32, where each lane combines its node with the partner's (the two lanes of a
+    // pair form the same bits, fp32 addition being commutative); the four groups then fold
+    // left to right.  The argmax is exact in any order.
+    const int r = tid >> 5, q = (tid >> 3) & 3, k = tid & 7;
+    if (r < M) {                                  // whole 8-lane groups
+        float cm[8], cs[8], bv[8];
+        int bi[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = 64 * q + lane;
-            if (xv_better(s_bv[r][c], s_bn[r][c], best, bn)) { best = s_bv[r][c]; bn = s_bn[r][c]; }
+        for (int j = 0; j < 8; ++j) {
+            const int c = 64 * q + 8 * k + j;
+            cm[j] = s_cm[r][c];
+            cs[j] = s_cs[r][c];
+            bv[j] = s_bv[r][c];
+            bi[j] = s_bn[r][c];
         }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(best, off);
-            const int on = __shfl_xor(bn, off);
+        for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+            for (int j = 0; j < 8; j += 2 * h) {
+                xv_lse_add(cm[j], cs[j], cm[j + h], cs[j + h]);
+                if (xv_better(bv[j + h], bi[j + h], bv[j], bi[j])) { bv[j] = bv[j + h]; bi[j] = bi[j + h]; }
+            }
+        float m = cm[0], sm = cs[0], best = bv[0];
+        int bn = bi[0];
+        auto level = [&](float m2, float s2, float ov, int on) {
+            xv_lse_add(m, sm, m2, s2);
             if (xv_better(ov, on, best, bn)) { best = ov; bn = on; }
-        }
-        float m = s_v[r][0].x, sum = s_v[r][0].y;
+        };
+        level(xv_dpp<XV_DPP_XOR1>(m), xv_dpp<XV_DPP_XOR1>(sm), xv_dpp<XV_DPP_XOR1>(best), xv_dpp<XV_DPP_XOR1>(bn));
+        level(xv_dpp<XV_DPP_XOR2>(m), xv_dpp<XV_DPP_XOR2>(sm), xv_dpp<XV_DPP_XOR2>(best), xv_dpp<XV_DPP_XOR2>(bn));
+        level(xv_dpp<XV_DPP_HALF_MIRROR>(m), xv_dpp<XV_DPP_HALF_MIRROR>(sm), xv_dpp<XV_DPP_HALF_MIRROR>(best),
+              xv_dpp<XV_DPP_HALF_MIRROR>(bn));
+        // groups 1..3 of the row (lanes +8, +16, +24 of its 32), folded after group 0
+        const int row0 = lane & ~31;
+        float gm[3], gs[3], gv[3];
+        int gn[3];
 #pragma unroll
-        for (int q = 1; q < 4; ++q) xv_lse_add(m, sum, s_v[r][64 * q].x, s_v[r][64 * q].y);
-        if (lane == 0) {
+        for (int u = 0; u < 3; ++u) {
+            const int src = row0 + 8 * (u + 1);
+            gm[u] = __shfl(m, src);
+            gs[u] = __shfl(sm, src);
+            gv[u] = __shfl(best, src);
+            gn[u] = __shfl(bn, src);
+        }
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            xv_lse_add(m, sm, gm[u], gs[u]);
+            if (xv_better(gv[u], gn[u], best, bn)) { best = gv[u]; bn = gn[u]; }
+        }
+        if ((tid & 31) == 0) {
             const int id = bn < N ? bn : 0;
             g.ids[r] = id;
-            if (g.lp) g.lp[r] = xv_neg_log(sum);
+            if (g.lp) g.lp[r] = xv_neg_log(sm);
             s_ids[r] = id;
         }
     }

@@ -30,6 +30,22 @@ __device__ __forceinline__ void xv_lse_add(float& m, float& s, float m2, float s
     s = t1 + t2;
 }
 
+// Lane moves within each row of 16 lanes (DPP; every source lane lies in the row):
+// XOR1 / XOR2 give lane c ^ 1 / c ^ 2, ROR8 lane c ^ 8, ROR12 lane (c + 4) mod 16, and
+// HALF_MIRROR lane 7 - c within each 8.  Where a butterfly level has made lanes c and c ^ m
+// equal, a move to any lane of the partner's class gives the partner's value: ROR12 after
+// the ^ 8 level stands for ^ 4, HALF_MIRROR after the ^ 1 and ^ 2 levels for ^ 4.
+constexpr int XV_DPP_XOR1 = 0xB1, XV_DPP_XOR2 = 0x4E, XV_DPP_ROR8 = 0x128, XV_DPP_ROR12 = 0x12C,
+              XV_DPP_HALF_MIRROR = 0x141;
+template <int CTRL>
+__device__ __forceinline__ float xv_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int xv_dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
 // lp = -ln S (S > 0: the row's maximum contributes e^0 = 1)
 __device__ __forceinline__ float xv_neg_log(float s) {
     constexpr float LN2 = 0.6931471805599453f;
