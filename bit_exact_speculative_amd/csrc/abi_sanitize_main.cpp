@@ -30,7 +30,7 @@ int main()
     for (int s = 1; s >= -7; --s) (void)xv_status_string(s);
     EXPECT(xv_attn_chunk_tokens(), 256);
     EXPECT((int)(xv_attn_workspace_bytes(0, 9, 24, 256, 256) == 0), 1);
-    EXPECT((int)(xv_attn_workspace_bytes(1, 9, 24, 256, 649) == (size_t)9 * 24 * 3 * 258 * 4), 1);
+    EXPECT((int)(xv_attn_workspace_bytes(1, 9, 24, 256, 649) == 4096 + (size_t)9 * 24 * 3 * 258 * 4), 1);
 
     // GEMMs
     EXPECT(xv_gemm_small_m(A, A, A, nullptr, 0, 16, 32, nullptr), XV_OK);

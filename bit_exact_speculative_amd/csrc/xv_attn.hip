@@ -56,6 +56,10 @@ constexpr int XV_ATTN_STREAM_MIN = 1024; // ... and from which the persistent st
 constexpr int XV_COMBINE_U = 24;    // chunks per block of combine loads kept in flight
 static_assert(XV_COMBINE_U % 4 == 0, "the long-row combine reads its per-chunk factors four at a time");
 constexpr int XV_COMBINE_PRE = 8;   // chunks a short row's combine loads before its maximum
+// arrival counters at the start of the workspace: the per-tile split folds its rows in the same
+// launch when its (request, KV head, tile) groups are at most this many, else a combine follows
+constexpr int XV_ATTN_COUNTERS = 1024;
+constexpr size_t XV_ATTN_COUNTER_BYTES = XV_ATTN_COUNTERS * sizeof(int);
 // GDN + attention in one launch while their workgroups are at most these multiples
 // of the CU count (GDN with one, or else two, column groups per workgroup)
 constexpr double XV_FUSE_ONE_COL = 1.0;
@@ -216,8 +220,18 @@ __device__ __forceinline__ xv_u32x4 xv_vt_frag(const xv_u32x4* lds, int db, int 
 // Partials are written with non-temporal (streaming) vector stores, and the long-row combine
 // reads them the same way: each is read once, by the next kernel, and not keeping them in the
 // caches leaves fewer dirty lines to be written back during the projections that follow
-// (long context: 0.264 -> 0.261 ms per step).
-template <int D, int NB>
+// (long context: 0.264 -> 0.261 ms per step).  AGENT: device-coherent stores instead, for a
+// combine by another workgroup of the same launch (the per-tile split).
+__device__ __forceinline__ void xv_store_agent(float* p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 xv_load2_agent(const float* p) {
+    const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+template <int D, int NB, bool AGENT = false>
 __device__ __forceinline__ void xv_store_acc(float* __restrict__ ws_acc, const xv_f32x4 (&oacc)[NB], int db0,
                                              int tile, int lr, int lg, int P, int Hg, int g, int b, int T,
                                              int Hq, int NC, int c, int L0, int c0) {
@@ -230,7 +244,10 @@ __device__ __forceinline__ void xv_store_acc(float* __restrict__ ws_acc, const x
         const int h = g * Hg + pair % Hg;
         float* dst = ws_acc + ((((size_t)b * T + r) * Hq + h) * NC + c) * D + lr;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) __builtin_nontemporal_store(oacc[j][i], &dst[(db0 + j) * 16]);
+        for (int j = 0; j < NB; ++j) {
+            if (AGENT) xv_store_agent(&dst[(db0 + j) * 16], oacc[j][i]);
+            else __builtin_nontemporal_store(oacc[j][i], &dst[(db0 + j) * 16]);
+        }
     }
 }
 
@@ -857,6 +874,8 @@ struct XvTileArgs {
     int T, Hq, Hkv, Lmax, NC, NTILE, items, per_xcd;
     int NCG;                    // chunks in the grid (NC, or fewer under a length bound); NC is the stride
     float scale_log2;
+    uint16_t* o; float* o32;    // the rows' outputs (the in-launch combine)
+    int* counters;              // arrival counters, one per (request, KV head, tile); zero between calls
 };
 
 template <int D>
@@ -867,7 +886,81 @@ struct XvTileSmem {
     float sp[16 * PP];
     uint16_t sq[16 * QP];
     float smax[XV_ATTN_WAVES][16];
+    int last;
 };
+
+// The rows of one tile's pairs, the dims of one d-part, folded from their chunk partials
+// exactly as xv_attn_combine_kernel folds them without DEEP (each group's chunks, then the
+// groups, o = A / L), by the last of that (tile, d-part)'s chunk workgroups to finish.  The
+// partials cross workgroups (and XCDs) through device-scope accesses only: relaxed
+// agent-scope stores, completed (vmcnt 0) before the workgroup's barrier and its counter
+// increment, and loads issued only by the workgroup that saw the final count; no cache
+// write-back is needed.  Thread t: pair t / 32 of the tile, dims 2 (t % 32) + 64 e and the
+// next of the d-part (each load instruction reads 256 contiguous bytes of a pair's
+// partial).  GU: chunks whose loads are issued together (8, a whole group, or 4 when the
+// tile's rows see at most 4 chunks; the chunks past a row are skipped either way).
+template <int D, int DS, int GU>
+__device__ __forceinline__ void xv_tile_combine(const XvTileArgs& A, int b, int g, int tile, int dpart, int L0)
+{
+    constexpr int C = XV_ATTN_C;
+    constexpr int G = XV_ATTN_G;
+    constexpr int E = D / DS / 64;              // dim pairs per thread
+    static_assert(E >= 1 && GU <= G, "layout");
+    const int tid = threadIdx.x;
+    const int Hq = A.Hq, Hg = Hq / A.Hkv, T = A.T, NC = A.NC;
+    const int pair = tile * 16 + (tid >> 5);
+    if (pair >= Hg * T) return;                 // uniform per half wave
+    const int pr = pair / Hg, ph = g * Hg + pair % Hg;
+    const int nc = (L0 + pr + 1 + C - 1) / C;   // the row's chunks
+    const int ng = (nc + G - 1) / G;
+    const size_t base = (((size_t)b * T + pr) * Hq + ph) * NC;
+    const int d0 = dpart * (D / DS) + 2 * (tid & 31);
+    float M = -INFINITY, L = 0.f;
+    float Ao[2 * E];
+#pragma unroll
+    for (int e = 0; e < 2 * E; ++e) Ao[e] = 0.f;
+    for (int gi = 0; gi < ng; ++gi) {
+        // the group's loads issued together; chunks past the row re-read the group's first
+        float2 ml[GU], pa[GU][E];
+#pragma unroll
+        for (int u = 0; u < GU; ++u) {
+            const int cc = gi * G + u < nc ? gi * G + u : gi * G;
+            ml[u] = xv_load2_agent(A.ws_ml + (base + cc) * 2);
+#pragma unroll
+            for (int e = 0; e < E; ++e) pa[u][e] = xv_load2_agent(A.ws_acc + (base + cc) * D + d0 + 64 * e);
+        }
+        float Mg = -INFINITY, Lg = 0.f;
+        float Ag[2 * E];
+#pragma unroll
+        for (int e = 0; e < 2 * E; ++e) Ag[e] = 0.f;
+#pragma unroll
+        for (int u = 0; u < GU; ++u) {
+            if (gi * G + u < nc) {
+                float fa, fb;
+                xv_fold_factors(Mg, ml[u].x, fa, fb);
+                Lg = __builtin_fmaf(Lg, fa, ml[u].y * fb);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    Ag[2 * e] = __builtin_fmaf(Ag[2 * e], fa, pa[u][e].x * fb);
+                    Ag[2 * e + 1] = __builtin_fmaf(Ag[2 * e + 1], fa, pa[u][e].y * fb);
+                }
+            }
+        }
+        float fa, fb;
+        xv_fold_factors(M, Mg, fa, fb);
+        L = __builtin_fmaf(L, fa, Lg * fb);
+#pragma unroll
+        for (int e = 0; e < 2 * E; ++e) Ao[e] = __builtin_fmaf(Ao[e], fa, Ag[e] * fb);
+    }
+    const size_t ob = (((size_t)b * T + pr) * Hq + ph) * D + d0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const float o0 = Ao[2 * e] / L, o1 = Ao[2 * e + 1] / L;
+        *reinterpret_cast<uint32_t*>(A.o + ob + 64 * e) =
+            (uint32_t)xv_f32_to_bf16(o0) | ((uint32_t)xv_f32_to_bf16(o1) << 16);
+        if (A.o32) *reinterpret_cast<float2*>(A.o32 + ob + 64 * e) = make_float2(o0, o1);
+    }
+}
 
 // workgroup bid of the tile grid (its items are laid out for the XCD round robin)
 template <int D, int DS>
@@ -1000,8 +1093,10 @@ __device__ __forceinline__ void xv_attn_tile_body(const XvTileArgs A, int bid, X
     ch.vt_to_lds(lds, tid);
     __syncthreads();
 
-    // ---- chunk sum l (wave 0 of d-part 0), in the wide kernel's order ----
-    if (wave == 0 && dpart == 0) {
+    // ---- chunk sum l (wave 0), in the wide kernel's order; every d-part forms the same (m, l)
+    // and stores it (the same bits to the same place), so that each d-part's fold needs only
+    // its own workgroups ----
+    if (wave == 0) {
         float l = 0.f;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
@@ -1013,31 +1108,46 @@ __device__ __forceinline__ void xv_attn_tile_body(const XvTileArgs A, int bid, X
         l = l + __shfl_xor(l, 32);
         if (lg == 0 && pair_ok && plen > c0) {
             const size_t idx = (((size_t)b * T + pr) * Hq + ph) * NC + c;
-            __builtin_nontemporal_store(m, &ws_ml[idx * 2 + 0]);
-            __builtin_nontemporal_store(l, &ws_ml[idx * 2 + 1]);
+            xv_store_agent(&ws_ml[idx * 2 + 0], m);
+            xv_store_agent(&ws_ml[idx * 2 + 1], l);
         }
     }
 
     // ---- acc = P V for this wave's output blocks ----
     const int dbl0 = wave * DBW;                // first block, local to the d-part
-    if (dbl0 >= DBP) return;                    // uniform per wave; no barrier follows
-    xv_f32x4 oacc[DBW];
+    if (dbl0 < DBP) {                           // uniform per wave
+        xv_f32x4 oacc[DBW];
 #pragma unroll
-    for (int j = 0; j < DBW; ++j) oacc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < DBW; ++j) oacc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < C / 32; ++kk) {
-        xv_u32x4 phi, plo;
-        xv_p_split(*reinterpret_cast<const xv_f32x4*>(sp + lr * PP + kk * 32 + 4 * lg),
-                   *reinterpret_cast<const xv_f32x4*>(sp + lr * PP + kk * 32 + 16 + 4 * lg), phi, plo);
-        xv_u32x4 vf[DBW];
+        for (int kk = 0; kk < C / 32; ++kk) {
+            xv_u32x4 phi, plo;
+            xv_p_split(*reinterpret_cast<const xv_f32x4*>(sp + lr * PP + kk * 32 + 4 * lg),
+                       *reinterpret_cast<const xv_f32x4*>(sp + lr * PP + kk * 32 + 16 + 4 * lg), phi, plo);
+            xv_u32x4 vf[DBW];
 #pragma unroll
-        for (int j = 0; j < DBW; ++j) vf[j] = xv_vt_frag(lds, dbl0 + j, kk, lr, lg);
+            for (int j = 0; j < DBW; ++j) vf[j] = xv_vt_frag(lds, dbl0 + j, kk, lr, lg);
 #pragma unroll
-        for (int j = 0; j < DBW; ++j) oacc[j] = xv_mfma16x16x32(phi, vf[j], oacc[j]);
+            for (int j = 0; j < DBW; ++j) oacc[j] = xv_mfma16x16x32(phi, vf[j], oacc[j]);
 #pragma unroll
-        for (int j = 0; j < DBW; ++j) oacc[j] = xv_mfma16x16x32(plo, vf[j], oacc[j]);
+            for (int j = 0; j < DBW; ++j) oacc[j] = xv_mfma16x16x32(plo, vf[j], oacc[j]);
+        }
+        xv_store_acc<D, DBW, true>(ws_acc, oacc, dpart * DBP + dbl0, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c,
+                                   L0, c0);
     }
-    xv_store_acc<D, DBW>(ws_acc, oacc, dpart * DBP + dbl0, tile, lr, lg, P, Hg, g, b, T, Hq, NC, c, L0, c0);
+
+    // ---- the combine of the tile's pairs, by the last of its chunk workgroups to finish ----
+    if (!A.counters) return;                    // too many tiles: a combine launch follows
+    __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0): this thread's partial stores have completed
+    __syncthreads();
+    const int ncb = (Lend + C - 1) / C < NCG ? (Lend + C - 1) / C : NCG;   // chunk workgroups of the d-part
+    int* cnt = A.counters + (((size_t)b * Hkv + g) * NTILE + tile) * DS + dpart;
+    if (tid == 0) S.last = atomicAdd(cnt, 1) == ncb - 1;
+    __syncthreads();
+    if (!S.last) return;                        // uniform over the workgroup
+    if (ncb <= 4) xv_tile_combine<D, DS, 4>(A, b, g, tile, dpart, L0);   // uniform
+    else xv_tile_combine<D, DS, XV_ATTN_G>(A, b, g, tile, dpart, L0);
+    if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int DS>
@@ -1309,16 +1419,24 @@ inline int xv_attn_tile_ds(int D, int B, int T, int Hq, int Hkv, int NC, long lo
     return n2 <= room ? 2 : 1;
 }
 
+// the per-tile split folds its rows in its own launch (each (request, KV head, tile,
+// d-part) has a counter; at most 2 d-parts)
+inline bool xv_tile_folds(int B, int T, int Hq, int Hkv) {
+    return (long long)B * Hkv * (((Hq / Hkv) * T + 15) / 16) * 2 <= XV_ATTN_COUNTERS;
+}
+
 inline XvTileArgs xv_tile_args(int ds, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                                uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
                                float* ws_acc, float* ws_ml, int B, int T, int Hq, int Hkv, int Lmax, int NC,
-                               int NCg, float scale_log2) {
+                               int NCg, float scale_log2, uint16_t* o, float* o32, int* counters) {
     const int P = (Hq / Hkv) * T;
     const int ntile = (P + 15) / 16;
     const int items = (int)xv_tile_items(B, T, Hq, Hkv, NCg, ds);
     const int per_xcd = (items + 7) / 8;
+    const bool fold = xv_tile_folds(B, T, Hq, Hkv);
     return XvTileArgs{q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
-                      T, Hq, Hkv, Lmax, NC, ntile, items, per_xcd, NCg, scale_log2};
+                      T, Hq, Hkv, Lmax, NC, ntile, items, per_xcd, NCg, scale_log2, o, o32,
+                      fold ? counters : nullptr};
 }
 
 // scores are kept in log2 units: s * log2(e), so that 2^(s' - m') = e^(s - m)
@@ -1326,10 +1444,11 @@ inline float xv_scale_log2(float scale) { return (float)((double)scale * 1.44269
 
 // NC: the capacity's chunks (the partials' stride); NCg: the chunks any row can see (NC, or
 // fewer under the caller's length bound), which sizes the grids and picks the kernels
+// The per-tile split also forms the rows' outputs (its in-launch combine, o, o32, counters).
 template <int D>
 int xv_attn_partials(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                      uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
-                     float* ws_acc, float* ws_ml,
+                     float* ws_acc, float* ws_ml, uint16_t* o, float* o32, int* counters,
                      int B, int T, int Hq, int Hkv, int Lmax, int NC, int NCg, float scale, hipStream_t st)
 {
     (void)hipGetLastError();
@@ -1348,7 +1467,7 @@ int xv_attn_partials(const uint16_t* q, const uint16_t* k_new, const uint16_t* v
     } else {
         const int ds = xv_attn_tile_ds(D, B, T, Hq, Hkv, NCg, xv_cu_count());
         const XvTileArgs ta = xv_tile_args(ds, q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
-                                           B, T, Hq, Hkv, Lmax, NC, NCg, scale_log2);
+                                           B, T, Hq, Hkv, Lmax, NC, NCg, scale_log2, o, o32, counters);
         if (D == 256 && ds == 2)
             hipLaunchKernelGGL((xv_attn_partial_tile_kernel<D, (D == 256 ? 2 : 1)>), dim3(8 * ta.per_xcd),
                                dim3(XV_ATTN_WAVES * 64), 0, st, ta);
@@ -1387,13 +1506,15 @@ int xv_attn_combine(const float* ws_acc, const float* ws_ml, const int32_t* kv_l
 template <int D>
 int xv_attn_launch(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                    uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
-                   uint16_t* o, float* o32, float* ws_acc, float* ws_ml,
+                   uint16_t* o, float* o32, float* ws_acc, float* ws_ml, int* counters,
                    int B, int T, int Hq, int Hkv, int Lmax, int NC, int NCg, float scale, hipStream_t st)
 {
-    const int s = xv_attn_partials<D>(q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml,
+    const int s = xv_attn_partials<D>(q, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml, o, o32, counters,
                                       B, T, Hq, Hkv, Lmax, NC, NCg, scale, st);
     if (s != XV_OK) return s;
-    const bool stream = xv_attn_kind<D>(B, T, Hq, Hkv, NCg) == XV_ATTN_STREAM;
+    const XvAttnKind kind = xv_attn_kind<D>(B, T, Hq, Hkv, NCg);
+    if (kind == XV_ATTN_TILE && xv_tile_folds(B, T, Hq, Hkv)) return XV_OK;   // combined in that launch
+    const bool stream = kind == XV_ATTN_STREAM;
     return xv_attn_combine<D>(ws_acc, ws_ml, kv_len, o, o32, B, T, Hq, Lmax, NC, NCg, stream,
                               stream ? xv_stream_wpg(B, Hkv, NCg) : 0, st);
 }
@@ -1425,12 +1546,15 @@ void xv_gdn_attn_kernel(XvGdnArgs ga, XvTileArgs ta, int n_attn, int gdn_nx)
     xv_gdn_body<DK, false, CPT>(ga, i % gdn_nx, (i / gdn_nx) % ga.Hv, i / (gdn_nx * ga.Hv), sm.g);
 }
 
+// The workspace: XV_ATTN_COUNTERS arrival counters of the per-tile split's in-launch combine
+// (at a fixed place, so that every call finds them zero whatever the shapes of the calls
+// before it), then the chunk partials' acc, then their (m, l).
 size_t xv_attn_ws(int B, int T, int Hq, int d, int Lmax, size_t* acc_bytes) {
     const size_t NC = (size_t)((Lmax + XV_ATTN_C - 1) / XV_ATTN_C);
     const size_t pairs = (size_t)B * T * Hq * NC;
     const size_t a = pairs * (size_t)d * sizeof(float);
     if (acc_bytes) *acc_bytes = a;
-    return a + pairs * 2 * sizeof(float);
+    return XV_ATTN_COUNTER_BYTES + a + pairs * 2 * sizeof(float);
 }
 
 }  // namespace
@@ -1450,7 +1574,7 @@ int xv_attn_check(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
                   const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* kv_len,
                   const uint16_t* o, const float* o32, void* workspace, size_t workspace_bytes,
                   int B, int T, int Hq, int Hkv, int d, int Lmax, float scale, int len_bound,
-                  int* NC, int* NCg, float** ws_acc, float** ws_ml, bool ws_pointer = true)
+                  int* NC, int* NCg, float** ws_acc, float** ws_ml, int** counters, bool ws_pointer = true)
 {
     XV_REQUIRE(B >= 0 && T >= 1 && T <= 16 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, XV_ERR_SHAPE);
     XV_REQUIRE(d == 64 || d == 128 || d == 256, XV_ERR_SHAPE);
@@ -1473,8 +1597,9 @@ int xv_attn_check(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_ne
     *NC = (Lmax + XV_ATTN_C - 1) / XV_ATTN_C;
     const int nb = len_bound > 0 && len_bound < Lmax ? (len_bound + XV_ATTN_C - 1) / XV_ATTN_C : *NC;
     *NCg = nb < *NC ? nb : *NC;
-    *ws_acc = reinterpret_cast<float*>(workspace);
-    *ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + acc_bytes);
+    *counters = reinterpret_cast<int*>(workspace);
+    *ws_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + XV_ATTN_COUNTER_BYTES);
+    *ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + XV_ATTN_COUNTER_BYTES + acc_bytes);
     return XV_OK;
 }
 
@@ -1505,16 +1630,16 @@ namespace {
 
 int xv_attn_launch_d(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                      uint16_t* k_cache, uint16_t* v_cache, const int32_t* kv_len,
-                     uint16_t* o, float* o32, float* ws_acc, float* ws_ml,
+                     uint16_t* o, float* o32, float* ws_acc, float* ws_ml, int* counters,
                      int B, int T, int Hq, int Hkv, int d, int Lmax, int NC, int NCg, float scale, hipStream_t st)
 {
     switch (d) {
         case 64:  return xv_attn_launch<64>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
-                                            ws_ml, B, T, Hq, Hkv, Lmax, NC, NCg, scale, st);
+                                            ws_ml, counters, B, T, Hq, Hkv, Lmax, NC, NCg, scale, st);
         case 128: return xv_attn_launch<128>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
-                                             ws_ml, B, T, Hq, Hkv, Lmax, NC, NCg, scale, st);
+                                             ws_ml, counters, B, T, Hq, Hkv, Lmax, NC, NCg, scale, st);
         default:  return xv_attn_launch<256>(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc,
-                                             ws_ml, B, T, Hq, Hkv, Lmax, NC, NCg, scale, st);
+                                             ws_ml, counters, B, T, Hq, Hkv, Lmax, NC, NCg, scale, st);
     }
 }
 
@@ -1556,10 +1681,11 @@ extern "C" int xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, con
     int NC = 0, NCg = 0;
     float* ws_acc = nullptr;
     float* ws_ml = nullptr;
+    int* counters = nullptr;
     const int s = xv_attn_check(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, workspace, workspace_bytes,
-                                B, T, Hq, Hkv, d, Lmax, scale, len_bound, &NC, &NCg, &ws_acc, &ws_ml);
+                                B, T, Hq, Hkv, d, Lmax, scale, len_bound, &NC, &NCg, &ws_acc, &ws_ml, &counters);
     if (s != XV_OK || B == 0) return s;
-    return xv_attn_launch_d(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc, ws_ml,
+    return xv_attn_launch_d(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc, ws_ml, counters,
                             B, T, Hq, Hkv, d, Lmax, NC, NCg, scale, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -1572,18 +1698,20 @@ extern "C" int xv_attn_verify_rows_noalloc(const uint16_t* q, const uint16_t* k_
     int NC = 0, NCg = 0;
     float* ws_acc = nullptr;
     float* ws_ml = nullptr;
+    int* counters = nullptr;
     // every argument and the size first (no device call), then the buffer's address
     int s = xv_attn_check(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, nullptr, XV_SCRATCH_BYTES,
-                          B, T, Hq, Hkv, d, Lmax, scale, len_bound, &NC, &NCg, &ws_acc, &ws_ml, false);
+                          B, T, Hq, Hkv, d, Lmax, scale, len_bound, &NC, &NCg, &ws_acc, &ws_ml, &counters, false);
     if (s != XV_OK || B == 0) return s;
     void* ws = nullptr;
     s = xv_scratch_address(&ws);
     if (s != XV_OK) return s;
     size_t acc_bytes = 0;
     (void)xv_attn_ws(B, T, Hq, d, Lmax, &acc_bytes);
-    ws_acc = reinterpret_cast<float*>(ws);
-    ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + acc_bytes);
-    return xv_attn_launch_d(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc, ws_ml,
+    counters = reinterpret_cast<int*>(ws);
+    ws_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + XV_ATTN_COUNTER_BYTES);
+    ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + XV_ATTN_COUNTER_BYTES + acc_bytes);
+    return xv_attn_launch_d(q, k_new, v_new, k_cache, v_cache, kv_len, o, o32, ws_acc, ws_ml, counters,
                             B, T, Hq, Hkv, d, Lmax, NC, NCg, scale, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -1610,8 +1738,10 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
     int NC = 0, NCg = 0;
     float* ws_acc = nullptr;
     float* ws_ml = nullptr;
+    int* counters = nullptr;
     s = xv_attn_check(q_attn, k_new, v_new, k_cache, v_cache, kv_len, o_attn, o_attn32, workspace,
-                      workspace_bytes, B, T, Hq, Hkv, d, Lmax, scale, len_bound, &NC, &NCg, &ws_acc, &ws_ml);
+                      workspace_bytes, B, T, Hq, Hkv, d, Lmax, scale, len_bound, &NC, &NCg, &ws_acc, &ws_ml,
+                      &counters);
     if (s != XV_OK || B == 0) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     // one launch when the attention partials take the tile split and both grids are
@@ -1639,7 +1769,7 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
         }
         if (fuse)
             ta = xv_tile_args(ds, q_attn, k_new, v_new, k_cache, v_cache, kv_len, ws_acc, ws_ml, B, T, Hq, Hkv,
-                              Lmax, NC, NCg, xv_scale_log2(scale));
+                              Lmax, NC, NCg, xv_scale_log2(scale), o_attn, o_attn32, counters);
     }
     if (!fuse) {
         s = n_keep_prev
@@ -1655,7 +1785,7 @@ extern "C" int xv_gdn_attn_verify(const uint16_t* q, const uint16_t* k, const ui
         case 128: s = xv_gdn_attn_fused<128>(ga, dk, cpt, ds, ta, B, st); break;
         default:  s = xv_gdn_attn_fused<256>(ga, dk, cpt, ds, ta, B, st); break;
     }
-    if (s != XV_OK) return s;
+    if (s != XV_OK || ta.counters) return s;    // the attention workgroups combined their rows
     switch (d) {
         case 64:  return xv_attn_combine<64>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, NCg, false, 0, st);
         case 128: return xv_attn_combine<128>(ws_acc, ws_ml, kv_len, o_attn, o_attn32, B, T, Hq, Lmax, NC, NCg, false, 0, st);

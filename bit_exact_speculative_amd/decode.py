@@ -81,8 +81,7 @@ class _Rows:
         self.ids = torch.empty((B, T), dtype=torch.int32, device=device)
         self.lp = f(B, T)
         self.n_keep = torch.empty((B,), dtype=torch.int32, device=device)
-        wsb = xv.xv_attn_workspace_bytes(B, T, wl.Hq, wl.d, Lmax)
-        self.ws = torch.empty((max(wsb, 16) + 15) // 16 * 4, dtype=torch.float32, device=device)
+        self.ws = xv.xv_attn_workspace(B, T, wl.Hq, wl.d, Lmax, device)
 
 
 class Decoder:

@@ -89,8 +89,7 @@ class Layer:
         self.use_len_bound = True
         self.o_attn = torch.empty((B, T, wl.Hq, wl.d), dtype=torch.bfloat16, device=device)
         self.o_attn32 = torch.empty((B, T, wl.Hq, wl.d), dtype=torch.float32, device=device)
-        wsb = xv.xv_attn_workspace_bytes(B, T, wl.Hq, wl.d, self.Lmax)
-        self.ws = torch.empty((max(wsb, 16) + 15) // 16 * 4, dtype=torch.float32, device=device)
+        self.ws = xv.xv_attn_workspace(B, T, wl.Hq, wl.d, self.Lmax, device)
         self.scale = 1.0 / float(wl.d) ** 0.5
         self.has_gemm = with_gemm and inp.x is not None
         if self.has_gemm:
@@ -315,8 +314,7 @@ class Layer:
         Kc = self.Kc0.clone(); Vc = self.Vc0.clone(); kv = self.L0.clone()
         S = self.S_in.clone(); S2 = torch.empty_like(S)
         one = torch.ones((B,), dtype=torch.int32, device=d)
-        wsb = xv.xv_attn_workspace_bytes(B, 1, wl.Hq, wl.d, self.Lmax)
-        ws = torch.empty((max(wsb, 16) + 15) // 16 * 4, dtype=torch.float32, device=d)
+        ws = xv.xv_attn_workspace(B, 1, wl.Hq, wl.d, self.Lmax, d)
         out = {k: [] for k in ("o_gdn", "o_gdn32", "S", "o_attn", "o_attn32", "kv_len",
                                "y1", "y1_32", "y2", "y2_32", "lg32", "la32", "ids", "lp")}
         for t in range(n):

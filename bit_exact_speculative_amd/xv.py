@@ -34,7 +34,7 @@ _lib.xv_abi_version.argtypes = []
 _lib.xv_status_string.restype = ctypes.c_char_p
 _lib.xv_status_string.argtypes = [_I]
 # the argument lists below are those of this ABI version of include/xv.h
-ABI_VERSION = 7
+ABI_VERSION = 8
 if _lib.xv_abi_version() != ABI_VERSION:
     raise ImportError("libxv.so has ABI version %d, this binding expects %d; rebuild it"
                       % (_lib.xv_abi_version(), ABI_VERSION))
@@ -136,6 +136,20 @@ def xv_attn_chunk_tokens() -> int:
 
 def xv_attn_workspace_bytes(B: int, T: int, Hq: int, d: int, Lmax: int) -> int:
     return int(_lib.xv_attn_workspace_bytes(B, T, Hq, d, Lmax))
+
+
+ATTN_COUNTER_BYTES = 4096    # the attention workspace's leading arrival counters
+
+
+def xv_attn_workspace(B: int, T: int, Hq: int, d: int, Lmax: int, device="cuda", fill=None):
+    """A float32 workspace for the attention calls: its arrival counters (the first 4096
+    bytes) zero, the partials after them zero or `fill`."""
+    import torch
+    n = (max(xv_attn_workspace_bytes(B, T, Hq, d, Lmax), ATTN_COUNTER_BYTES) + 15) // 16 * 4
+    ws = torch.zeros((n,), dtype=torch.float32, device=device)
+    if fill is not None:
+        ws[ATTN_COUNTER_BYTES // 4:].fill_(fill)
+    return ws
 
 
 def xv_gemm_small_m(x, w, y, y32=None, stream=None):

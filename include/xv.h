@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define XV_ABI_VERSION 7
+#define XV_ABI_VERSION 8
 
 typedef enum {
     XV_OK = 0,
@@ -202,7 +202,16 @@ int xv_gdn_verify_after(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *   kv_len   : int32 [B] device        L0 per request; read only
  *   o        : bf16 [B][T][Hq][d]
  *   o32      : fp32 [B][T][Hq][d] or NULL
- *   workspace: [16B] device scratch of workspace_bytes >= xv_attn_workspace_bytes(B,T,Hq,d,Lmax)
+ *   workspace: [16B] device scratch of workspace_bytes >= xv_attn_workspace_bytes(B,T,Hq,d,Lmax),
+ *              owned by the caller and used by one call at a time.  Its first
+ *              4096 bytes are arrival counters: they must be zero before the
+ *              first call, and every call leaves them zero (a buffer zeroed once
+ *              serves any sequence of calls whose sizes fit).  The rest holds the
+ *              chunk partials and needs no initial value.  (When the partials
+ *              take the per-tile split, the last of a tile's chunk workgroups to
+ *              finish folds that tile's rows in the same launch, a counter
+ *              telling it that it is the last; otherwise a second launch folds
+ *              every row.)
  *   len_bound: 0, or an upper bound on kv_len[b] + T over the batch, known to
  *              the caller (a serving loop tracks its lengths): the launch is then
  *              sized for that many positions instead of the capacity Lmax (in a
@@ -235,8 +244,9 @@ int    xv_attn_verify_rows(const uint16_t* q, const uint16_t* k_new, const uint1
  * library (one per GPU it runs on, XV_ATTN_NOALLOC_MAX_BYTES each, held until
  * the process ends); the call allocates nothing.  Every call on a GPU shares that
  * GPU's array: calls that overlap on one GPU (other streams, other host threads)
- * race and give undefined results, so serialise them.  Nothing in the array needs
- * to start at zero (each call writes every partial it reads).
+ * race and give undefined results, so serialise them.  The array is zero when the
+ * library is loaded, and every call leaves its arrival counters at zero (the
+ * workspace rule of xv_attn_verify_rows); the partials need no initial value.
  * Errors: as xv_attn_verify_rows; XV_ERR_WORKSPACE when the call needs more than
  * XV_ATTN_NOALLOC_MAX_BYTES (checked before any launch); XV_ERR_LAUNCH also when
  * the runtime cannot give the array's address on the current device.
@@ -253,9 +263,9 @@ int xv_attn_verify_rows_noalloc(const uint16_t* q, const uint16_t* k_new, const 
  * (the post's two verify changes, each with the decode arithmetic) and, at small
  * batch, both are bound by latency rather than bandwidth, so when the attention
  * partials take their per-tile split and both grids fit on the chip at once, one
- * launch runs the GDN workgroups beside the attention partial workgroups,
- * followed by the attention combine; otherwise the two calls below run one after
- * the other.  Either way every output is bit-identical to
+ * launch runs the GDN workgroups beside the attention partial workgroups (which
+ * also fold their rows, as in xv_attn_verify_rows); otherwise the two calls below
+ * run one after the other.  Either way every output is bit-identical to
  *   n_keep_prev != NULL : xv_gdn_verify_after(q .. b, k_prev .. b_prev,
  *                         n_keep_prev, T_prev, state_in, state_prev_out,
  *                         state_kept, state_out, o, o32, B, T, Hk, Hv, dk, dv)

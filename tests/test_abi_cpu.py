@@ -38,14 +38,14 @@ def test_every_header_symbol_is_exported(xv):
 
 
 def test_version_and_constants(xv):
-    assert xv.xv_abi_version() == xv.ABI_VERSION == 7
+    assert xv.xv_abi_version() == xv.ABI_VERSION == 8
     assert xv.xv_attn_chunk_tokens() == 256
     lib = xv.lib()
     assert lib.xv_status_string(0) == b"ok"
     assert lib.xv_status_string(-4) == b"workspace too small"
-    # workspace: B*T*Hq*nchunks*(d+2) fp32
-    assert xv.xv_attn_workspace_bytes(1, 9, 24, 256, 649) == 1 * 9 * 24 * 3 * 258 * 4
-    assert xv.xv_attn_workspace_bytes(8, 9, 24, 256, 256) == 8 * 9 * 24 * 1 * 258 * 4
+    # workspace: 4096 bytes of arrival counters, then B*T*Hq*nchunks*(d+2) fp32 partials
+    assert xv.xv_attn_workspace_bytes(1, 9, 24, 256, 649) == 4096 + 1 * 9 * 24 * 3 * 258 * 4
+    assert xv.xv_attn_workspace_bytes(8, 9, 24, 256, 256) == 4096 + 8 * 9 * 24 * 1 * 258 * 4
     assert xv.xv_attn_workspace_bytes(0, 9, 24, 256, 256) == 0
 
 

@@ -42,8 +42,10 @@ def _run(D, q, kn, vn, kc, vc, kv_len, ws_extra=0):
     Lmax = kc.shape[2]
     o = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device="cuda")
     o32 = torch.empty((B, T, Hq, d), dtype=torch.float32, device="cuda")
-    nb = _xv().xv_attn_workspace_bytes(B, T, Hq, d, Lmax) + ws_extra
-    ws = torch.full(((nb + 15) // 16 * 4,), float("nan"), dtype=torch.float32, device="cuda")
+    # partials NaN (each call writes what it reads), arrival counters zero; ws_extra: a larger buffer
+    ws = _xv().xv_attn_workspace(B, T, Hq, d, Lmax, fill=float("nan"))
+    if ws_extra:
+        ws = torch.cat([ws, torch.full(((ws_extra + 15) // 16 * 4,), float("nan"), device="cuda")])
     _xv().xv_attn_verify_rows(q, kn, vn, kc, vc, kv_len, o, o32, ws, 1.0 / d ** 0.5)
     return o, o32
 

@@ -43,8 +43,7 @@ def _steps(dev, kv0, T):
     for t0 in range(0, P, T):
         tt = min(T, P - t0)
         sl = slice(t0, t0 + tt)
-        nb = _xv().xv_attn_workspace_bytes(B, tt, Hq, d, Lmax)
-        ws = torch.empty(((nb + 15) // 16 * 4,), dtype=torch.float32, device="cuda")
+        ws = _xv().xv_attn_workspace(B, tt, Hq, d, Lmax)
         os_ = torch.empty((B, tt, Hq, d), dtype=torch.bfloat16, device="cuda")
         o32s = torch.empty((B, tt, Hq, d), dtype=torch.float32, device="cuda")
         _xv().xv_attn_verify_rows(q[:, sl].contiguous(), kn[:, sl].contiguous(), vn[:, sl].contiguous(),

@@ -46,9 +46,9 @@ def _inputs(seed, B, T, Hk, Hv, dk, dv, Hq, Hkv, d, L0, Lmax, Tp):
 def _outs(B, T, Hv, dv, Hq, d, dk, Lmax):
     e = lambda *s: torch.full(s, float("nan"), dtype=torch.bfloat16, device="cuda")
     f = lambda *s: torch.full(s, float("nan"), dtype=torch.float32, device="cuda")
-    nb = _xv().xv_attn_workspace_bytes(B, T, Hq, d, Lmax)
     return dict(o=e(B, T, Hv, dv), o32=f(B, T, Hv, dv), oa=e(B, T, Hq, d), oa32=f(B, T, Hq, d),
-                kept=f(B, Hv, dk, dv), out=f(B, Hv, dk, dv), ws=f((nb + 15) // 16 * 4))
+                kept=f(B, Hv, dk, dv), out=f(B, Hv, dk, dv),
+                ws=_xv().xv_attn_workspace(B, T, Hq, d, Lmax, fill=float("nan")))
 
 
 # (B, T, Hk, Hv, dk, dv, Hq, Hkv, d, L0, Lmax, Tp).  The first three and the last fit one launch:

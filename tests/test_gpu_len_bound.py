@@ -47,8 +47,7 @@ def _run(inp, lb, B, T, Hq, d, Lmax, noalloc=False):
     if noalloc:
         xv.xv_attn_verify_rows_noalloc(q, kn, vn, kc, vc, kv, o, o32, len_bound=lb)
     else:
-        wsb = xv.xv_attn_workspace_bytes(B, T, Hq, d, Lmax)
-        ws = torch.empty(((max(wsb, 16) + 15) // 16 * 4,), dtype=torch.float32, device="cuda")
+        ws = xv.xv_attn_workspace(B, T, Hq, d, Lmax, fill=float("nan"))
         xv.xv_attn_verify_rows(q, kn, vn, kc, vc, kv, o, o32, ws, len_bound=lb)
     torch.cuda.synchronize()
     return o, o32, kc, vc, kv
@@ -107,15 +106,13 @@ def test_gdn_attn_len_bound_same_bits(L0, Lmax, after):
     nk = torch.tensor([5], dtype=torch.int32, device="cuda")
     att = _attn_inputs(17, B, T, Hq, Hkv, d, L0, Lmax)
     scale = 1.0 / d ** 0.5
-    wsb = xv.xv_attn_workspace_bytes(B, T, Hq, d, Lmax)
     f32 = lambda *s: torch.full(s, float("nan"), dtype=torch.float32, device="cuda")
 
     def outs():
         return dict(o=torch.full((B, T, Hv, dv), float("nan"), dtype=torch.bfloat16, device="cuda"),
                     o32=f32(B, T, Hv, dv), kept=f32(B, Hv, dk, dv), out=f32(B, Hv, dk, dv),
                     oa=torch.full((B, T, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda"),
-                    oa32=f32(B, T, Hq, d), ws=torch.empty(((wsb + 15) // 16 * 4,), dtype=torch.float32,
-                                                          device="cuda"),
+                    oa32=f32(B, T, Hq, d), ws=xv.xv_attn_workspace(B, T, Hq, d, Lmax),
                     kc=att[3].clone(), vc=att[4].clone(), kv=att[5].clone())
 
     prev = None

@@ -32,7 +32,7 @@ def _both(case):
     Lmax = kc.shape[2]
     wsb = xv.xv_attn_workspace_bytes(B, T, Hq, d, Lmax)
     assert wsb <= 32 << 20
-    ws = torch.empty((wsb + 15) // 16 * 4, dtype=torch.float32, device="cuda")
+    ws = xv.xv_attn_workspace(B, T, Hq, d, Lmax)
     kc1, vc1, kc2, vc2 = kc.clone(), vc.clone(), kc.clone(), vc.clone()
     o1 = torch.empty((B, T, Hq, d), dtype=torch.bfloat16, device="cuda")
     o321 = torch.empty((B, T, Hq, d), dtype=torch.float32, device="cuda")
