@@ -1274,9 +1274,13 @@ extern "C" int xv_head_greedy_accept(const uint16_t* x_a, const uint16_t* w_a, u
         else xv_gemm_launch_head_greedy<12, 48, 4>(pp, M, K, hg, lc);
         return xv_launch_status();
     }
-    // otherwise the pair and the greedy kernels (the same bits)
+    // otherwise the pair, then the argmax and acceptance in one launch with a counter per request
+    // (ints 1 .. 63 of the workspace's first 256 bytes), or in two for more requests (the same bits)
     const int s = xv_gemm_small_m_pair(x_a, w_a, y_a, logits_a, N, x_b, w_b, y_b, logits_b, N, M, K, stream,
                                        nullptr, nullptr);
     if (s != XV_OK) return s;
+    if (B <= 63)
+        return xv_detail::xv_greedy_accept_counted(logits_a, logits_b, draft, B, T, N, ids, n_keep, logprob, kv_len,
+                                                   static_cast<int*>(workspace) + 1, stream);
     return xv_greedy_accept(logits_a, logits_b, draft, B, T, N, ids, n_keep, logprob, kv_len, stream);
 }

@@ -180,7 +180,66 @@ __global__ void xv_accept_kernel(const int32_t* __restrict__ draft, const int32_
     if (kv_len) kv_len[b] += acc + 1;
 }
 
+// xv_argmax_kernel and xv_accept_kernel in one launch, for callers with a workspace: each
+// row's workgroup stores its id with a device-coherent store, waits for it, and counts the
+// row in its request's counter; the workgroup that sees the request's last row loads the
+// request's ids (device-coherent loads) and counts the accepted drafts, exactly as
+// xv_accept_kernel does, then resets the counter to zero.
+template <bool VEC>
+__global__ __launch_bounds__(XV_GREEDY_THREADS)
+void xv_argmax_accept_kernel(const float* __restrict__ la, const float* __restrict__ lb,
+                             const int32_t* __restrict__ draft, int T, int N, int32_t* ids,
+                             float* __restrict__ lp, int32_t* __restrict__ n_keep, int32_t* __restrict__ kv_len,
+                             int* __restrict__ counters)
+{
+    __shared__ float sv[XV_GREEDY_WAVES];
+    __shared__ int sn[XV_GREEDY_WAVES];
+    __shared__ float sm[XV_GREEDY_WAVES], ssum[XV_GREEDY_WAVES];
+    const int t = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x;
+    float best, cm, cs;
+    int bn;
+    xv_row_scan<VEC>(la, lb, ((size_t)b * T + t) * N, N, tid, lp != nullptr, best, bn, cm, cs);
+    if ((tid & 63) == 0) { sv[tid >> 6] = best; sn[tid >> 6] = bn; sm[tid >> 6] = cm; ssum[tid >> 6] = cs; }
+    __syncthreads();
+    if (tid != 0) return;
+    int id;
+    float lpv;
+    xv_row_fold(sv, sn, sm, ssum, N, id, lpv);
+    __hip_atomic_store(&ids[(size_t)b * T + t], id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lp) lp[(size_t)b * T + t] = lpv;
+    __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): the id store has completed
+    if (atomicAdd(&counters[b], 1) != T - 1) return;
+    const int acc = xv_accepted(T, [&](int r) { return draft[(size_t)b * T + r]; },
+                                [&](int r) { return (int)__hip_atomic_load(&ids[(size_t)b * T + r], __ATOMIC_RELAXED,
+                                                                            __HIP_MEMORY_SCOPE_AGENT); });
+    n_keep[b] = acc + 1;
+    if (kv_len) kv_len[b] += acc + 1;
+    __hip_atomic_store(&counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
+
+namespace xv_detail {
+
+int xv_greedy_accept_counted(const float* logits_a, const float* logits_b, const int32_t* draft,
+                             int B, int T, int N, int32_t* ids, int32_t* n_keep, float* logprob,
+                             int32_t* kv_len, int* counters, void* stream)
+{
+    (void)hipGetLastError();
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const bool vec = (N % 4 == 0) && xv_aligned16(logits_a) && xv_aligned16(logits_b);
+    const dim3 grid(T, B), block(XV_GREEDY_THREADS);
+    if (vec)
+        hipLaunchKernelGGL(xv_argmax_accept_kernel<true>, grid, block, 0, st, logits_a, logits_b, draft, T, N, ids,
+                           logprob, n_keep, kv_len, counters);
+    else
+        hipLaunchKernelGGL(xv_argmax_accept_kernel<false>, grid, block, 0, st, logits_a, logits_b, draft, T, N, ids,
+                           logprob, n_keep, kv_len, counters);
+    return xv_launch_status();
+}
+
+}  // namespace xv_detail
 
 extern "C" int xv_greedy_accept(const float* logits_a, const float* logits_b, const int32_t* draft,
                                 int B, int T, int N, int32_t* ids, int32_t* n_keep, float* logprob,

@@ -52,6 +52,16 @@ __device__ __forceinline__ float xv_neg_log(float s) {
     return -(__builtin_amdgcn_logf(s) * LN2);
 }
 
+// The argmax and acceptance of xv_greedy_accept in one launch (the same bits), with one
+// arrival counter per request in counters[0 .. B) (zero on entry, zero on exit); arguments
+// as xv_greedy_accept, already checked by the caller.
+namespace xv_detail {
+__attribute__((visibility("hidden")))
+int xv_greedy_accept_counted(const float* logits_a, const float* logits_b, const int32_t* draft,
+                             int B, int T, int N, int32_t* ids, int32_t* n_keep, float* logprob,
+                             int32_t* kv_len, int* counters, void* stream);
+}
+
 // Accepted drafts of one request: the leading rows whose id equals the next row's draft.
 // draft_of(t) and id_of(t) give row t's draft and id; all are read before the first compare.
 template <typename DraftFn, typename IdFn>

@@ -370,7 +370,9 @@ int xv_greedy_accept(const float* logits_a, const float* logits_b, const int32_t
  * one launch: each workgroup computes one 16-column block of both halves and the
  * block's part of the greedy reduction, and the last workgroup to finish folds
  * them in xv_greedy_accept's order and counts the accepted drafts; otherwise it
- * runs those two calls.
+ * runs the pair call, then the greedy reduction with the acceptance in the same
+ * launch (B <= 63: the last row of each request to finish counts its accepted
+ * drafts) or as xv_greedy_accept (more requests).
  *   x_a, x_b : bf16 [B*T][K] [16B]     w_a, w_b : bf16 [N][K] [16B]
  *   y_a, y_b : bf16 [B*T][N]           logits_a, logits_b : fp32 [B*T][N]
  *   draft, ids, n_keep, logprob, kv_len : as xv_greedy_accept

@@ -128,3 +128,13 @@ def test_head_greedy_workspace_reused_across_calls():
     ws = torch.zeros((xv.xv_head_greedy_workspace_bytes(2, 8, 4096),), dtype=torch.uint8, device="cuda")
     for (B, T), seed in (((1, 9), 1), ((1, 4), 2), ((2, 8), 3), ((1, 9), 4)):
         _check(B, T, 4096, 6144, seed=seed, ws=ws)
+
+
+def test_head_greedy_unfused_workspace_reused_across_calls():
+    """The unfused path's per-request counters (argmax and acceptance in one launch) are left at
+    zero by every call: consecutive calls of different batch sizes on one workspace."""
+    import bit_exact_speculative_amd.xv as xv
+    ws = torch.zeros((xv.xv_head_greedy_workspace_bytes(8, 9, 4096),), dtype=torch.uint8, device="cuda")
+    for (B, T), seed in (((8, 9), 5), ((3, 4), 6), ((8, 9), 7), ((1, 16), 8)):
+        _check(B, T, 4096, 4096, seed=seed, ws=ws)
+
