@@ -447,7 +447,8 @@ void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0, int contig, XvHea
         const uint16_t* base = (blk < nb0 ? pp.w[0] + (size_t)blk * 16 * K
                                           : pp.w[1] + (size_t)(blk - nb0) * 16 * K) + st * (SL * 32);
 #pragma unroll
-        for (int i = 0; i < GPT; ++i) gr[i] = xv_load16(base + goff[i]);
+        for (int i = 0; i < GPT; ++i)
+            gr[i] = __builtin_nontemporal_load(reinterpret_cast<const xv_u32x4*>(base + goff[i]));
     };
     auto store_stage = [&](const xv_u32x4 (&gr)[GPT]) {
 #pragma unroll
