@@ -45,7 +45,7 @@ void xv_stream_read_kernel(const xv_u32x4* __restrict__ a, size_t na, const xv_u
 #pragma unroll
         for (int u = 0; u < XV_READ_UNROLL; ++u) {
             const size_t j = i + u * XV_READ_THREADS;
-            v[u] = j < na ? a[j] : b[j - na];
+            v[u] = __builtin_nontemporal_load(j < na ? &a[j] : &b[j - na]);
         }
 #pragma unroll
         for (int u = 0; u < XV_READ_UNROLL; ++u) acc ^= v[u];

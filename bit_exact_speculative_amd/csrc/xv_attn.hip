@@ -578,10 +578,11 @@ void xv_attn_stream_kernel(const XvStreamArgs A)
             const uint16_t* base = (u < 4 ? A.k_cache : A.v_cache) + (kvbase + p0) * D;
             if (u < 4) {
 #pragma unroll
-                for (int i = 0; i < KG; ++i) U.r[i] = xv_load16(base + koff[i]);
+                for (int i = 0; i < KG; ++i) U.r[i] = PF ? xv_load16(base + koff[i]) : xv_load16_nt(base + koff[i]);
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) U.r[e] = xv_load16(base + voff + e * D);
+                for (int e = 0; e < 4; ++e)
+                    U.r[e] = PF ? xv_load16(base + voff + e * D) : xv_load16_nt(base + voff + e * D);
             }
             return;
         }

@@ -67,6 +67,12 @@ __device__ __forceinline__ xv_u32x4 xv_load16(const void* p) {
     return *reinterpret_cast<const xv_u32x4*>(p);
 }
 
+// a 16-byte load of data read once per call (weights, states, KV streamed once): the
+// non-temporal hint keeps it from displacing lines that are read again
+__device__ __forceinline__ xv_u32x4 xv_load16_nt(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const xv_u32x4*>(p));
+}
+
 __device__ __forceinline__ void xv_store16(void* p, xv_u32x4 v) {
     *reinterpret_cast<xv_u32x4*>(p) = v;
 }

@@ -242,7 +242,7 @@ __device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, in
     xv_f32x4 sl[SPASS];
 #pragma unroll
     for (int e = 0; e < SPASS; ++e)
-        sl[e] = *reinterpret_cast<const xv_f32x4*>(S0 + slab + (size_t)(tid / GPR + e * SROWS) * dv);
+        sl[e] = __builtin_nontemporal_load(reinterpret_cast<const xv_f32x4*>(S0 + slab + (size_t)(tid / GPR + e * SROWS) * dv));
 
     xv_gdn_stage<DK, W, NT>(A, b, h, g, j0, np, n, sm.skq, sm.sv, sm.sab);
 #pragma unroll
@@ -386,7 +386,7 @@ __device__ __forceinline__ void xv_gdn_prefill_body(const XvGdnArgs A, int bx, i
     xv_f32x4 sl[SPASS];
 #pragma unroll
     for (int e = 0; e < SPASS; ++e)
-        sl[e] = *reinterpret_cast<const xv_f32x4*>(A.S_in + slab + (size_t)(tid / GPR + e * SROWS) * dv);
+        sl[e] = __builtin_nontemporal_load(reinterpret_cast<const xv_f32x4*>(A.S_in + slab + (size_t)(tid / GPR + e * SROWS) * dv));
 
     // one block's rows: every load issued first (clamped to the call's first row), stored later
     constexpr int CH = DK / 8;

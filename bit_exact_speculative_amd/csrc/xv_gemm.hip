@@ -448,7 +448,7 @@ void xv_gemm_wlds_kernel(XvGemmPair pp, int M, int K, int mt0, int contig, XvHea
                                           : pp.w[1] + (size_t)(blk - nb0) * 16 * K) + st * (SL * 32);
 #pragma unroll
         for (int i = 0; i < GPT; ++i)
-            gr[i] = __builtin_nontemporal_load(reinterpret_cast<const xv_u32x4*>(base + goff[i]));
+            gr[i] = xv_load16_nt(base + goff[i]);
     };
     auto store_stage = [&](const xv_u32x4 (&gr)[GPT]) {
 #pragma unroll
@@ -833,13 +833,14 @@ void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
     // rows past the buffers re-read the last one (their outputs are not stored)
     const uint16_t* src[GPT];
     int dst[GPT];
-    bool live[GPT];
+    bool live[GPT], wsrc[GPT];
 #pragma unroll
     for (int i = 0; i < GPT; ++i) {
         int g = tid + i * NT;
         live[i] = g < (XR + WR) * GR;
         g = live[i] ? g : 0;
         const int r = g / GR, c = g % GR;
+        wsrc[i] = r >= XR;
         if (r < XR) {
             src[i] = x + (size_t)(r < M ? r : M - 1) * K + c * 8;
         } else {
@@ -851,7 +852,8 @@ void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
     auto load = [&](xv_u32x4 (&reg)[GPT], int part) {   // k-steps part * KSP ..; past the end re-read
         const int k0 = (part < NPARTS ? part : NPARTS - 1) * (KSP * 32);
 #pragma unroll
-        for (int i = 0; i < GPT; ++i) reg[i] = xv_load16(src[i] + k0);
+        for (int i = 0; i < GPT; ++i)                      // W is read once, x again by every workgroup
+            reg[i] = wsrc[i] ? xv_load16_nt(src[i] + k0) : xv_load16(src[i] + k0);
     };
     auto store = [&](uint16_t* sb, const xv_u32x4 (&reg)[GPT]) {
 #pragma unroll
