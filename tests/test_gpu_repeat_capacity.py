@@ -2,9 +2,12 @@
 command's context length.
 
 The post's repeatability paragraph: without the DeepGEMM fence, 25 of 1,200 requests sent in
-batches of 8 came out different; with it, none.  Here no kernel communicates across
-workgroups, so 1,200 full lazy steps of a batch of 8 must give every bit twice, also when
-two copies of the layer run at the same time on two streams.  The launch command sets a
+batches of 8 came out different; with it, none.  Here the kernels that hand partial results
+from workgroup to workgroup (the greedy acceptance's per-request counters, the batch-1 head's
+greedy tail, the per-tile attention fold) do so through device-coherent stores, loads and
+counters in each caller's own workspace, with fixed fold orders, so 1,200 full lazy steps of a
+batch of 8 (and of batch 1) must give every bit twice, also when two copies of the layer run at
+the same time on two streams.  The launch command sets a
 262,144-token context: a cache of that capacity must give the bits of a cache of exactly
 the verified length."""
 import numpy as np
@@ -20,15 +23,18 @@ STEPS = 1200
 RESET_EVERY = 100          # steps between returns to the pre-verify caches (bounds the capacity)
 
 
-def test_repeatability_batch8_1200_steps_two_streams():
-    """Two copies of the batch-8 layer, 1,200 full lazy steps each (projections, GDN after the
-    previous step's rollback beside attention with the KV append, head, greedy acceptance),
-    step k of copy A on stream k % 2 and of copy B on the other stream, both in flight
-    together: ids, logprobs, projection, GDN and attention outputs equal at every step, states
-    and caches equal at every reset.  Stops at the first difference."""
+@pytest.mark.parametrize("workload", ["batch8", "short"])
+def test_repeatability_1200_steps_two_streams(workload):
+    """Two copies of the layer (batch 8, or batch 1 with the fused head tail and the per-tile
+    attention fold), 1,200 full lazy steps each (projections, GDN after the previous step's
+    rollback beside attention with the KV append, head, greedy acceptance), step k of copy A on
+    stream k % 2 and of copy B on the other stream, both in flight together: ids, logprobs,
+    projection, GDN and attention outputs equal at every step, states and caches equal at
+    every reset.  Stops at the first difference."""
     from bit_exact_speculative_amd.layer import Layer
-    wl = gen.WORKLOADS["batch8"]
-    Lmax = wl.L0_range[1] + wl.T * (RESET_EVERY + 4)
+    wl = gen.WORKLOADS[workload]
+    L0max = wl.L0 if wl.L0 is not None else wl.L0_range[1]
+    Lmax = L0max + wl.T * (RESET_EVERY + 4)
     inp = gen.make_inputs(wl, Lmax=Lmax, pad_value=0)
     S0 = prefix_state(inp)
     A = Layer(inp, "cuda", state_in=S0)
