@@ -29,7 +29,9 @@
  *    stated per call, and kernels clamp them so that no access leaves its
  *    buffer even when a precondition is broken (results are then undefined).
  *  - Stateless and thread-safe; concurrent calls on different streams are
- *    independent as long as their output buffers do not overlap.
+ *    independent as long as their output and workspace buffers do not overlap
+ *    (xv_attn_verify_rows_noalloc shares one device array per GPU: see there).
+ *    Workspaces carry arrival counters that a call leaves zero for the next.
  *  - An empty problem (B == 0 or M == 0) returns XV_OK and launches nothing.
  */
 #ifndef XV_H
