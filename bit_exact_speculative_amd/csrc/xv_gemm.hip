@@ -795,10 +795,10 @@ void xv_gemm_big_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
 
 // 2 to 5 row tiles (a batch of requests' verify rows) and K = 5120 or 6144: the 16 ranges
 // have KSW = K / 512 k-steps each.  A workgroup (16 waves) owns NBW column blocks of one
-// problem of the pair and walks K in parts of KSP k-steps (KSW / KSP parts per range).  A
+// problem of the pair and walks K in parts of KSP k-steps (a range may end inside a part).  A
 // part's x slice (all row tiles) and W slice (the NBW blocks) are staged by every thread
 // into one of two LDS buffers while the other buffer is consumed (one barrier per part),
-// with the next part's loads in flight in a second register buffer.  Compute wave
+// with the loads of the next two parts in flight in two register buffers.  Compute wave
 // (t, g) owns row tile t and column blocks g BG .. g BG + BG - 1: per k-step it reads the
 // A fragment once and one B fragment per block.  Per tile one chain per range from zero,
 // folded into the running sum in range order: the bits of every other variant.  Each W
@@ -815,7 +815,8 @@ void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
     constexpr int BG = NBW < 4 ? NBW : 4;       // column blocks per compute wave
     constexpr int NBG = (NBW + BG - 1) / BG;
     static_assert(MT * NBG <= XV_GEMM_WAVES, "one compute wave per (row tile, block group)");
-    __shared__ __attribute__((aligned(16))) uint16_t sm[2][(XR + WR) * PITCH];
+    constexpr int SPARE = (XR + WR) * PITCH;    // a 16-byte slot past the rows: stores of unused granules
+    __shared__ __attribute__((aligned(16))) uint16_t sm[2][SPARE + 8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -827,18 +828,20 @@ void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
     const uint16_t* __restrict__ w = pp.w[cur];
     const int N = pp.N[cur];
     const int NPARTS = (K >> 5) / KSP;
-    const int PPR = NPARTS / XV_GEMM_WAVES;     // parts per K range
+    const int KSW = (K >> 5) / XV_GEMM_WAVES;   // k-steps per K range (a range may end inside a part)
 
     // this thread's granules of a part: g = tid + i NT over the x rows, then the W rows;
-    // rows past the buffers re-read the last one (their outputs are not stored)
+    // rows past the buffers re-read the last one (their outputs are not stored).  Granules
+    // past the part load granule 0 and store it into the spare slot, so that no load or store
+    // is conditional: under a divergent branch the compiler would wait for every load in flight.
     const uint16_t* src[GPT];
     int dst[GPT];
-    bool live[GPT], wsrc[GPT];
+    bool wsrc[GPT];
 #pragma unroll
     for (int i = 0; i < GPT; ++i) {
         int g = tid + i * NT;
-        live[i] = g < (XR + WR) * GR;
-        g = live[i] ? g : 0;
+        const bool live = g < (XR + WR) * GR;
+        g = live ? g : 0;
         const int r = g / GR, c = g % GR;
         wsrc[i] = r >= XR;
         if (r < XR) {
@@ -847,7 +850,7 @@ void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
             const int n = blk0 * 16 + (r - XR);
             src[i] = w + (size_t)(n < N ? n : N - 1) * K + c * 8;
         }
-        dst[i] = r * PITCH + c * 8;
+        dst[i] = live ? r * PITCH + c * 8 : SPARE;
     }
     auto load = [&](xv_u32x4 (&reg)[GPT], int part) {   // k-steps part * KSP ..; past the end re-read
         const int k0 = (part < NPARTS ? part : NPARTS - 1) * (KSP * 32);
@@ -857,8 +860,7 @@ void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
     };
     auto store = [&](uint16_t* sb, const xv_u32x4 (&reg)[GPT]) {
 #pragma unroll
-        for (int i = 0; i < GPT; ++i)
-            if (live[i]) *reinterpret_cast<xv_u32x4*>(sb + dst[i]) = reg[i];
+        for (int i = 0; i < GPT; ++i) *reinterpret_cast<xv_u32x4*>(sb + dst[i]) = reg[i];
     };
 
     const int t = wave / NBG, bg = wave % NBG;
@@ -867,43 +869,58 @@ void xv_gemm_mt_kernel(XvGemmPair pp, int M, int K, int nwg0)
 #pragma unroll
     for (int j = 0; j < BG; ++j) { acc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f}; sum[j] = acc[j]; }
 
-    // register buffer u & 1 holds part p + 1 when part p (u = p % 2) is consumed
-    xv_u32x4 r0[GPT], r1[GPT];
-    load(r0, 0);
-    load(r1, 1);
-    store(sm[0], r0);
-    load(r0, 2);
+    auto consume = [&](const uint16_t* sb, int p) {    // part p from LDS buffer sb
+        if (!comp) return;
+        const uint16_t* ap = sb + (t * 16 + lr) * PITCH + lg * 8;
+        const uint16_t* bp = sb + (XR + bg * BG * 16 + lr) * PITCH + lg * 8;
+#pragma unroll
+        for (int kk = 0; kk < KSP; ++kk) {
+            const xv_u32x4 a = *reinterpret_cast<const xv_u32x4*>(ap + kk * 32);
+#pragma unroll
+            for (int j = 0; j < BG; ++j)
+                if (bg * BG + j < NBW)          // uniform
+                    acc[j] = xv_mfma16x16x32(a, *reinterpret_cast<const xv_u32x4*>(bp + j * 16 * PITCH + kk * 32), acc[j]);
+            const int ks = p * KSP + kk + 1;    // k-steps done
+            if (ks % KSW == 0) {                // a range complete (uniform): folded in order
+#pragma unroll
+                for (int j = 0; j < BG; ++j) {
+                    sum[j] = ks == KSW ? acc[j] : sum[j] + acc[j];
+                    acc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+    };
+
+    // register buffer q % NR holds part q; part p is consumed from LDS buffer p % 2
+    constexpr int NR = 2;                       // parts in flight (four measured no faster)
+    xv_u32x4 rb[NR][GPT];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) load(rb[q], q);
+    store(sm[0], rb[0]);
+    load(rb[0], NR);
     __syncthreads();
-    for (int p0 = 0; p0 < NPARTS; p0 += 2) {    // NPARTS is even (16 ranges)
+    // whole rounds of NR parts whose successors all exist: the staging of part p + 1 and the
+    // loads of part p + 1 + NR are unconditional, so that the compiler waits for part p + 1
+    // alone (a conditional store or load there makes it wait for every load in flight)
+    int p0 = 0;
+    for (; p0 + NR < NPARTS; p0 += NR) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int p = p0 + u;
-            xv_u32x4 (&rn)[GPT] = u ? r0 : r1;  // holds part p + 1
-            if (p + 1 < NPARTS) {               // stage part p + 1; its buffer was freed by the last barrier
-                store(sm[u ^ 1], rn);
-                load(rn, p + 3);
-            }
-            if (comp) {
-                const uint16_t* ap = sm[u] + (t * 16 + lr) * PITCH + lg * 8;
-                const uint16_t* bp = sm[u] + (XR + bg * BG * 16 + lr) * PITCH + lg * 8;
-#pragma unroll
-                for (int kk = 0; kk < KSP; ++kk) {
-                    const xv_u32x4 a = *reinterpret_cast<const xv_u32x4*>(ap + kk * 32);
-#pragma unroll
-                    for (int j = 0; j < BG; ++j)
-                        if (bg * BG + j < NBW)  // uniform
-                            acc[j] = xv_mfma16x16x32(a, *reinterpret_cast<const xv_u32x4*>(bp + j * 16 * PITCH + kk * 32), acc[j]);
-                }
-                if ((p + 1) % PPR == 0) {       // a range complete: folded in order
-#pragma unroll
-                    for (int j = 0; j < BG; ++j) {
-                        sum[j] = p + 1 == PPR ? acc[j] : sum[j] + acc[j];
-                        acc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
-                    }
-                }
-            }
+        for (int u = 0; u < NR; ++u) {
+            xv_u32x4 (&rn)[GPT] = rb[(u + 1) % NR];  // holds part p0 + u + 1
+            store(sm[(u + 1) & 1], rn);         // its LDS buffer was freed by the last barrier
+            load(rn, p0 + u + 1 + NR);
+            consume(sm[u & 1], p0 + u);
             __syncthreads();                    // part p consumed, part p + 1 staged
         }
+    }
+    // the last round (parts p0 .. NPARTS - 1, all loaded): nothing more to load
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+        const int p = p0 + u;
+        if (p >= NPARTS) break;                 // uniform
+        if (p + 1 < NPARTS) store(sm[(u + 1) & 1], rb[(u + 1) % NR]);
+        consume(sm[u & 1], p);
+        __syncthreads();
     }
     if (!comp) return;
 #pragma unroll
@@ -1099,12 +1116,14 @@ void xv_gemm_launch_mt_n(const XvGemmPair& pp, int M, int K, const XvLaunch& lc)
 
 void xv_gemm_launch_mt(const XvGemmPair& pp, int mt, int M, int K, const XvLaunch& lc)
 {
+    // parts of 4 k-steps at K = 5120 (256-byte row runs: a 5-step part of 320 bytes splits every
+    // other 128-byte line between two parts, which streams measurably slower), 6 at K = 6144
     if (K == 5120) {
         switch (mt) {
-            case 2: xv_gemm_launch_mt_n<2, 5>(pp, M, K, lc); break;
-            case 3: xv_gemm_launch_mt_n<3, 5>(pp, M, K, lc); break;
-            case 4: xv_gemm_launch_mt_n<4, 5>(pp, M, K, lc); break;
-            default: xv_gemm_launch_mt_n<5, 5>(pp, M, K, lc); break;
+            case 2: xv_gemm_launch_mt_n<2, 4>(pp, M, K, lc); break;
+            case 3: xv_gemm_launch_mt_n<3, 4>(pp, M, K, lc); break;
+            case 4: xv_gemm_launch_mt_n<4, 4>(pp, M, K, lc); break;
+            default: xv_gemm_launch_mt_n<5, 4>(pp, M, K, lc); break;
         }
     } else {
         switch (mt) {
