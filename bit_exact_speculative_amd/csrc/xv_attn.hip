@@ -455,19 +455,20 @@ void xv_attn_stream_kernel(const XvStreamArgs A)
     constexpr int CBS = SB / 16;                // score blocks per sub-block
     constexpr int CBH = NCB / 2;                // score blocks per wave
     constexpr int DBH = DB / 2;                 // output blocks per wave (half of the head dim)
-    constexpr int PP = C + 4;                   // probability row pitch (floats)
+    constexpr int PS = SB + 4;                  // probability row pitch of a sub-block slot (floats)
     constexpr int KG = XvUnit<D>::KG;
     constexpr int VT4 = XvUnit<D>::VT4;
     static_assert(NSB == 4 && 8 % NU == 0 && XV_ATTN_WAVES == 8, "four units per chunk half, unit k in buffer k % NU, two waves per tile");
     constexpr int QP = D + 8;                   // query row pitch in LDS (bf16)
-    // one slot holds the current K sub-block [pos][d] or V^T sub-block [d][pos] (swizzled):
-    // the K units of a chunk are consumed before its V units, and those before the next K
-    __shared__ __attribute__((aligned(16))) xv_u32x4 skv[SB * D / 8];
-    __shared__ __attribute__((aligned(16))) float sp[4 * 16 * PP];      // probabilities per tile [pair][pos]
+    // two slots, each a K sub-block [pos][d] or a V^T sub-block [d][pos] (swizzled): unit u of a
+    // chunk (K sub-blocks 0..3, then V^T sub-blocks 0..3) is staged into slot u % 2 while unit
+    // u - 1 is consumed from the other
+    __shared__ __attribute__((aligned(16))) xv_u32x4 skv[2][SB * D / 8];
+    // the probabilities of one sub-block per slot, [tile][pair][pos]: sub-block v in slot v % 3
+    __shared__ __attribute__((aligned(16))) float sp[3][4 * 16 * PS];
     __shared__ __attribute__((aligned(16))) uint16_t sq[4 * 16 * QP];   // the 4 tiles' queries
     __shared__ float smax[XV_ATTN_WAVES][16];
-    xv_u32x4* const sk = skv;
-    xv_u32x4* const svt = skv;
+    __shared__ float sl[4][64];                 // a tile's chunk-sum chains, wave t -> t + 4 -> t
 
     const int Hg = A.Hq / A.Hkv;
     const int Ptot = Hg * A.R;
@@ -541,7 +542,6 @@ void xv_attn_stream_kernel(const XvStreamArgs A)
     const size_t newbase = ((size_t)b * A.R * A.Hkv + g) * D;
     const int newstride = A.Hkv * D;
     const xv_u32x4 zero = {0u, 0u, 0u, 0u};
-    float* tp = sp + tile * 16 * PP;
 
     // verify: positions before L0 from the cache, the new rows from k_new / v_new; prefill:
     // every visible position from the cache (its rows were appended first).  Past L0 + R:
@@ -600,7 +600,7 @@ void xv_attn_stream_kernel(const XvStreamArgs A)
         }
     };
     // into LDS: positions past L0 + R zeroed; verify appends the new rows to the cache
-    auto store_unit = [&](XvUnit<D>& U, int it, int u) __attribute__((always_inline)) {
+    auto store_unit = [&](XvUnit<D>& U, int it, int u, xv_u32x4* slot) __attribute__((always_inline)) {
         const int p0 = chunk_of(it) * C + (u & 3) * SB;
         const bool plain = p0 + SB <= plain_end;     // uniform
         if (u < 4) {
@@ -613,7 +613,7 @@ void xv_attn_stream_kernel(const XvStreamArgs A)
                     if (pos >= Lend) U.r[i] = zero;
                     else if (!PF && pos >= L0) xv_store16(A.k_cache + (kvbase + pos) * D + cc * 8, U.r[i]);
                 }
-                sk[xv_k_granule<D>(lp, cc)] = U.r[i];
+                slot[xv_k_granule<D>(lp, cc)] = U.r[i];
             }
         } else if (tid < VT4) {
             // a 4 (positions) x 8 (dims) tile -> for each of its 8 dims, 4 positions of V^T (8 bytes)
@@ -626,7 +626,7 @@ void xv_attn_stream_kernel(const XvStreamArgs A)
                     else if (!PF && pos >= L0) xv_store16(A.v_cache + (kvbase + pos) * D + dg * 8, U.r[e]);
                 }
             }
-            char* vb = reinterpret_cast<char*>(svt);
+            char* vb = reinterpret_cast<char*>(slot);
 #pragma unroll
             for (int dd = 0; dd < 8; ++dd) {
                 const uint32_t a0 = U.r[0][dd >> 1], a1 = U.r[1][dd >> 1];
@@ -669,123 +669,155 @@ void xv_attn_stream_kernel(const XvStreamArgs A)
 #pragma unroll
     for (int j = 0; j < (PF ? DBH : 1); ++j) At[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // unit k of item it (k >= 8: unit k - 8 of the next item; past the last item the same unit
+    // of this item again, a cache hit, so that every load is unconditional; never consumed)
+    auto load_ahead = [&](XvUnit<D>& U, int it, int k) __attribute__((always_inline)) {
+        if (k < 8) load_unit(U, it, k);
+        else load_unit(U, it + 1 < nitems ? it + 1 : it, k - 8);
+    };
+    store_unit(ub[0], 0, 0, skv[0]);
+    load_ahead(ub[0], 0, NU);
+    __syncthreads();
+
     for (int it = 0; it < nitems; ++it) {
         const int c = chunk_of(it);
         const int c0 = c * C;
         const bool full = c0 + C <= first_len;
         const bool more = it + 1 < nitems;
         const bool tsee = tile_on && c0 < tlen;     // uniform per wave
-        // the unit four steps ahead of unit u: in this item, else the next item's (past the
-        // last item: the same K unit of this item again, a cache hit, so the unit kind stays fixed)
-        auto ahead = [&](XvUnit<D>& U, int u) __attribute__((always_inline)) {
-            if (u + NU < 8) load_unit(U, it, u + NU);
-            else load_unit(U, more ? it + 1 : it, u + NU - 8);
-        };
-
-        // ---- this wave's half of the score blocks, one K sub-block at a time ----
+        const int cb0 = dh * CBH;                   // this wave's half of the score blocks
         xv_f32x4 sc[CBH];
 #pragma unroll
         for (int j = 0; j < CBH; ++j) sc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < NSB; ++u) {
-            __syncthreads();                    // K slot free
-            store_unit(ub[u % NU], it, u);
-            ahead(ub[u % NU], u);
-            __syncthreads();
-            if (tsee && (u * CBS) / CBH == dh) {        // uniform per wave
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {       // per score block one chain over ks
-                    const xv_u32x4 qk = *reinterpret_cast<const xv_u32x4*>(qrow + ks * 32);
-                    xv_u32x4 kf[CBS];
-#pragma unroll
-                    for (int j = 0; j < CBS; ++j) kf[j] = sk[xv_k_granule<D>(j * 16 + lr, ks * 4 + lg)];
-#pragma unroll
-                    for (int j = 0; j < CBS; ++j)
-                        sc[(u * CBS) % CBH + j] = xv_mfma16x16x32(kf[j], qk, sc[(u * CBS) % CBH + j]);
-                }
-            }
-        }
-
-        // ---- chunk max over both waves (exact), probabilities into LDS ----
-        const int cb0 = dh * CBH;
-        float mw = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < CBH; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float sv = sc[j][i] * A.scale_log2;
-                sc[j][i] = sv;
-                if (full || c0 + (cb0 + j) * 16 + 4 * lg + i < plen) mw = fmaxf(mw, sv);
-            }
-        mw = fmaxf(mw, __shfl_xor(mw, 16));
-        mw = fmaxf(mw, __shfl_xor(mw, 32));
-        if (lg == 0) smax[wave][lr] = mw;
-        __syncthreads();                        // also: the previous chunk's P.V is done with sp
-        float m = fmaxf(smax[tile][lr], smax[tile + 4][lr]);
-        if (!pair_ok) m = 0.f;
-        if (tsee) {
-#pragma unroll
-            for (int j = 0; j < CBH; ++j) {
-                xv_f32x4 pv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool vis = full || c0 + (cb0 + j) * 16 + 4 * lg + i < plen;
-                    pv[i] = vis ? __builtin_amdgcn_exp2f(sc[j][i] - m) : 0.f;
-                }
-                *reinterpret_cast<xv_f32x4*>(tp + lr * PP + (cb0 + j) * 16 + 4 * lg) = pv;
-            }
-        }
-
-        // ---- acc = P V, one V sub-block (two k-slots) at a time; this wave's half of the dims ----
         xv_f32x4 oacc[DBH];
 #pragma unroll
         for (int j = 0; j < DBH; ++j) oacc[j] = xv_f32x4{0.f, 0.f, 0.f, 0.f};
-        float l = 0.f;
+        float m = 0.f, l = 0.f;
+        // the probabilities of score blocks j (of this wave's half) into their sub-block's slot
+        auto put_p = [&](int j) __attribute__((always_inline)) {
+            const int cb = cb0 + j, sv = cb / CBS;
+            float* const tp = sp[sv % 3] + tile * 16 * PS;
+            *reinterpret_cast<xv_f32x4*>(tp + lr * PS + (cb % CBS) * 16 + 4 * lg) = sc[j];
+        };
+
+        // step u consumes unit u (slot u % 2) while unit u + 1 goes into the other slot, freed by
+        // the barrier that ended step u - 1, and unit u + 1 + NU is loaded into its registers
 #pragma unroll
-        for (int u = NSB; u < 2 * NSB; ++u) {
-            __syncthreads();                    // V^T slot free; P of both waves visible
-            store_unit(ub[u % NU], it, u);
-            ahead(ub[u % NU], u);
-            __syncthreads();
-            if (u == NSB && tsee) {             // chunk sum, in the wide kernel's order (both waves)
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    const xv_f32x4 pv = *reinterpret_cast<const xv_f32x4*>(tp + lr * PP + cb * 16 + 4 * lg);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) l = l + pv[i];
-                }
-                l = l + __shfl_xor(l, 16);
-                l = l + __shfl_xor(l, 32);
+        for (int u = 0; u < 2 * NSB; ++u) {
+            if (u + 1 < 2 * NSB) {
+                store_unit(ub[(u + 1) % NU], it, u + 1, skv[(u + 1) & 1]);
+                load_ahead(ub[(u + 1) % NU], it, u + 1 + NU);
+            } else {                                // the next item's first unit
+                store_unit(ub[0], more ? it + 1 : it, 0, skv[0]);
+                load_ahead(ub[0], more ? it + 1 : it, NU);
             }
-            if (tsee) {
+            if (u < NSB) {
+                // ---- this wave's half of the score blocks, one K sub-block at a time ----
+                const xv_u32x4* const sk = skv[u & 1];
+                if (tsee && (u * CBS) / CBH == dh) {        // uniform per wave
 #pragma unroll
-                for (int k2 = 0; k2 < SB / 32; ++k2) {
-                    const int kk = (u - NSB) * (SB / 32) + k2;
-                    xv_u32x4 phi, plo;
-                    xv_p_split(*reinterpret_cast<const xv_f32x4*>(tp + lr * PP + kk * 32 + 4 * lg),
-                               *reinterpret_cast<const xv_f32x4*>(tp + lr * PP + kk * 32 + 16 + 4 * lg), phi, plo);
-                    const int ca = k2 * 4 + (lg >> 1);
+                    for (int ks = 0; ks < KS; ++ks) {       // per score block one chain over ks
+                        const xv_u32x4 qk = *reinterpret_cast<const xv_u32x4*>(qrow + ks * 32);
+                        xv_u32x4 kf[CBS];
 #pragma unroll
-                    for (int j0 = 0; j0 < DBH; j0 += 4) {
-                        constexpr int GW = DBH < 4 ? DBH : 4;
-                        xv_u32x4 vf[GW];
+                        for (int j = 0; j < CBS; ++j) kf[j] = sk[xv_k_granule<D>(j * 16 + lr, ks * 4 + lg)];
 #pragma unroll
-                        for (int w4 = 0; w4 < GW; ++w4) {
-                            const int d = (dh * DBH + j0 + w4) * 16 + lr;
-                            const char* rowp = reinterpret_cast<const char*>(svt) + (size_t)d * (SB * 2) + (lg & 1) * 8;
-                            const int sw = (d ^ (d >> 3)) & 7;
-                            const uint2 va = *reinterpret_cast<const uint2*>(rowp + ((ca ^ sw) << 4));
-                            const uint2 vb = *reinterpret_cast<const uint2*>(rowp + (((ca + 2) ^ sw) << 4));
-                            vf[w4] = xv_u32x4{va.x, va.y, vb.x, vb.y};
+                        for (int j = 0; j < CBS; ++j)
+                            sc[(u * CBS) % CBH + j] = xv_mfma16x16x32(kf[j], qk, sc[(u * CBS) % CBH + j]);
+                    }
+                }
+                if (u == NSB - 1) {                 // the chunk's scores complete: this wave's max
+                    float mw = -INFINITY;
+#pragma unroll
+                    for (int j = 0; j < CBH; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float sv = sc[j][i] * A.scale_log2;
+                            sc[j][i] = sv;
+                            if (full || c0 + (cb0 + j) * 16 + 4 * lg + i < plen) mw = fmaxf(mw, sv);
                         }
+                    mw = fmaxf(mw, __shfl_xor(mw, 16));
+                    mw = fmaxf(mw, __shfl_xor(mw, 32));
+                    if (lg == 0) smax[wave][lr] = mw;
+                }
+            } else {
+                const int v = u - NSB;              // V^T sub-block v
+                if (v == 0) {
+                    // ---- chunk max over both waves (exact), probabilities; the chunk sum in the
+                    // wide kernel's order: each lane's chain over score blocks 0 .. 15 (wave t
+                    // runs 0 .. 7 and hands it to wave t + 4), then the two cross-lane levels ----
+                    m = fmaxf(smax[tile][lr], smax[tile + 4][lr]);
+                    if (!pair_ok) m = 0.f;
+                    if (tsee) {
 #pragma unroll
-                        for (int w4 = 0; w4 < GW; ++w4) oacc[j0 + w4] = xv_mfma16x16x32(phi, vf[w4], oacc[j0 + w4]);
+                        for (int j = 0; j < CBH; ++j)
 #pragma unroll
-                        for (int w4 = 0; w4 < GW; ++w4) oacc[j0 + w4] = xv_mfma16x16x32(plo, vf[w4], oacc[j0 + w4]);
+                            for (int i = 0; i < 4; ++i) {
+                                const bool vis = full || c0 + (cb0 + j) * 16 + 4 * lg + i < plen;
+                                sc[j][i] = vis ? __builtin_amdgcn_exp2f(sc[j][i] - m) : 0.f;
+                            }
+                        if (dh == 0) {
+#pragma unroll
+                            for (int j = 0; j < CBH; ++j)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) l = l + sc[j][i];
+                            sl[tile][lane] = l;
+                        }
+                        // sub-blocks 0 and 1 (waves 0-3) and 2 (waves 4-7); sub-block 3 after step 4
+#pragma unroll
+                        for (int j = 0; j < CBH; ++j)
+                            if (dh == 0 || j < CBS) put_p(j);
+                    }
+                    __syncthreads();                // those probabilities and the chains visible
+                    if (tsee && dh == 1) {
+                        l = sl[tile][lane];
+#pragma unroll
+                        for (int j = 0; j < CBH; ++j)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) l = l + sc[j][i];
+                        l = l + __shfl_xor(l, 16);
+                        l = l + __shfl_xor(l, 32);
+                        sl[tile][lane] = l;         // back to wave t, read after this step
+                    }
+                }
+                if (v == 1 && tsee && dh == 1) {    // sub-block 3 into slot 0, which step 4 freed
+#pragma unroll
+                    for (int j = CBS; j < CBH; ++j) put_p(j);
+                }
+                // ---- acc = P V over this sub-block's two k-slot groups; this wave's half of the dims ----
+                if (tsee) {
+                    const char* const svt = reinterpret_cast<const char*>(skv[u & 1]);
+                    const float* const tp = sp[v % 3] + tile * 16 * PS;
+#pragma unroll
+                    for (int k2 = 0; k2 < SB / 32; ++k2) {
+                        xv_u32x4 phi, plo;
+                        xv_p_split(*reinterpret_cast<const xv_f32x4*>(tp + lr * PS + k2 * 32 + 4 * lg),
+                                   *reinterpret_cast<const xv_f32x4*>(tp + lr * PS + k2 * 32 + 16 + 4 * lg), phi, plo);
+                        const int ca = k2 * 4 + (lg >> 1);
+#pragma unroll
+                        for (int j0 = 0; j0 < DBH; j0 += 4) {
+                            constexpr int GW = DBH < 4 ? DBH : 4;
+                            xv_u32x4 vf[GW];
+#pragma unroll
+                            for (int w4 = 0; w4 < GW; ++w4) {
+                                const int d = (dh * DBH + j0 + w4) * 16 + lr;
+                                const char* rowp = svt + (size_t)d * (SB * 2) + (lg & 1) * 8;
+                                const int sw = (d ^ (d >> 3)) & 7;
+                                const uint2 va = *reinterpret_cast<const uint2*>(rowp + ((ca ^ sw) << 4));
+                                const uint2 vb = *reinterpret_cast<const uint2*>(rowp + (((ca + 2) ^ sw) << 4));
+                                vf[w4] = xv_u32x4{va.x, va.y, vb.x, vb.y};
+                            }
+#pragma unroll
+                            for (int w4 = 0; w4 < GW; ++w4) oacc[j0 + w4] = xv_mfma16x16x32(phi, vf[w4], oacc[j0 + w4]);
+#pragma unroll
+                            for (int w4 = 0; w4 < GW; ++w4) oacc[j0 + w4] = xv_mfma16x16x32(plo, vf[w4], oacc[j0 + w4]);
+                        }
                     }
                 }
             }
+            __syncthreads();                        // unit u consumed, unit u + 1 staged
         }
+        if (tsee && dh == 0) l = sl[tile][lane];    // the chunk sum from wave t + 4
 
         // ---- the chunk folded into its group, for the pairs that see it ----
         if (tsee) {
