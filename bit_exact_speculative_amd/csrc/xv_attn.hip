@@ -392,15 +392,17 @@ void xv_attn_partial_wide_kernel(const uint16_t* __restrict__ q, const uint16_t*
 //    of 64 (row, head) pairs) walks every chunk its last row sees, in ascending order, and
 //    folds both levels in registers into the rows' outputs (no workspace).
 // A chunk goes through LDS as four 64-position sub-blocks of K, then four of V^T; each
-// sub-block is a "unit" loaded into registers four units ahead of its use (the next
-// chunk's K units while the current chunk's V is consumed), so HBM loads overlap the MFMA
-// work instead of alternating with it.  Up to 4 tiles of 16 pairs; waves t and t + 4
+// sub-block is a "unit" loaded into registers two units before it is staged (the next
+// chunk's K units while the current chunk's V is consumed), and staged into one of two LDS
+// slots while the unit before it is consumed from the other (one barrier per unit), so HBM
+// loads, LDS staging and the MFMA work overlap.  Up to 4 tiles of 16 pairs; waves t and t + 4
 // share tile t: wave t forms the score blocks of the chunk's first half, wave t + 4 those
-// of the second, the chunk max meets through LDS, the probabilities go through LDS in
-// fp32, both waves form the chunk sum, and each wave forms half of the tile's P.V output
-// dims.  Every chain and ordered sum of a chunk is the wide kernel's, and the folds are the
-// combine's operations in its order (xv_fold_factors), so every bit is the same as the
-// per-chunk kernels followed by the combine.
+// of the second, the chunk max meets through LDS, the fp32 probabilities go through LDS one
+// sub-block at a time (three slots), the chunk sum is one chain per lane that wave t runs
+// over the first half and wave t + 4 continues, and each wave forms half of the tile's P.V
+// output dims.  Every chain and ordered sum of a chunk is the wide kernel's, and the folds
+// are the combine's operations in its order (xv_fold_factors), so every bit is the same as
+// the per-chunk kernels followed by the combine.
 constexpr int XV_ATTN_SB = 64;              // positions per streamed sub-block
 constexpr int XV_ATTN_UNITS = 2;            // units in flight
 constexpr int XV_ATTN_SPAIRS = 64;          // (row, head) pairs per workgroup: 4 tiles of 16
