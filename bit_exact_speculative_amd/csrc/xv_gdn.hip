@@ -97,25 +97,27 @@ void xv_gdn4_kernel(XvGdnArgs A)
     const int Hv = A.Hv, T = A.T, Tp = A.Tp;
     const int g = h / (Hv / A.Hk);
 
+    // the state loads from S_in go out before n_pre is known: S_in is the start state unless
+    // every previous row was kept, when the state is read again from S_alt
+    const size_t sofs = ((size_t)(b * Hv + h) * DK + ig * R) * DV + j0 + jw;
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = A.S_in[sofs + (size_t)r * DV];
+
     int np = 0;
-    const float* S0 = A.S_in;
     if (A.n_pre) {
         np = A.n_pre[b];
         np = np < 0 ? 0 : (np > Tp ? Tp : np);
         if (ROLLBACK) {
             if (bx == 0 && h == 0 && tid == 0) A.kv_len[b] += np;
             if (np == Tp) return;                // state_out already holds S_T
-        } else if (np == Tp && A.S_alt) {
-            S0 = A.S_alt;                        // every previous row kept: its S_T, nothing to replay
+        } else if (np == Tp && A.S_alt) {        // every previous row kept: its S_T, nothing to replay
+#pragma unroll
+            for (int r = 0; r < R; ++r) s[r] = A.S_alt[sofs + (size_t)r * DV];
             np = 0;
         }
     }
     const int n = np + (ROLLBACK ? 0 : T);
-
-    const size_t sofs = ((size_t)(b * Hv + h) * DK + ig * R) * DV + j0 + jw;
-    float s[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) s[r] = S0[sofs + (size_t)r * DV];
     xv_gdn_stage<DK, W, XV_GDN4_WAVES * 64>(A, b, h, g, j0, np, n, sm.skq, sm.sv, sm.sab);
     __syncthreads();
 

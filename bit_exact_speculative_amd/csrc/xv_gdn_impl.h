@@ -216,22 +216,6 @@ __device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, in
     const int Hk = A.Hk, Hv = A.Hv, dv = A.dv, T = A.T, Tp = A.Tp;
     const int g = h / (Hv / Hk);
 
-    int np = 0;
-    const float* S0 = A.S_in;
-    if (A.n_pre) {
-        np = A.n_pre[b];
-        np = np < 0 ? 0 : (np > Tp ? Tp : np);
-        if (ROLLBACK) {
-            if (bx == 0 && h == 0 && tid == 0) A.kv_len[b] += np;
-            if (np == Tp) return;            // state_out already holds S_T
-        } else if (np == Tp && A.S_alt) {
-            S0 = A.S_alt;                    // every previous row kept: its S_T, nothing to replay
-            np = 0;
-        }
-    }
-    const int nm = ROLLBACK ? 0 : T;         // rows of this call
-    const int n = np + nm;
-
     // the state slab S[i][j0 .. j0 + W) moves through LDS so that global reads and
     // writes are 16-byte, W / 4 threads per row
     constexpr int GPR = W / 4;               // 16-byte granules per slab row
@@ -240,9 +224,29 @@ __device__ __forceinline__ void xv_gdn_body(const XvGdnArgs A, int bx, int h, in
     static_assert(DK % SROWS == 0, "the slab must split into whole passes");
     const size_t slab = (size_t)(b * Hv + h) * DK * dv + j0 + (tid % GPR) * 4;
     xv_f32x4 sl[SPASS];
+    auto load_slab = [&](const float* S0) {
 #pragma unroll
-    for (int e = 0; e < SPASS; ++e)
-        sl[e] = __builtin_nontemporal_load(reinterpret_cast<const xv_f32x4*>(S0 + slab + (size_t)(tid / GPR + e * SROWS) * dv));
+        for (int e = 0; e < SPASS; ++e)
+            sl[e] = __builtin_nontemporal_load(reinterpret_cast<const xv_f32x4*>(S0 + slab + (size_t)(tid / GPR + e * SROWS) * dv));
+    };
+    // the slab's loads from S_in go out before n_pre is known: S_in is the start state unless
+    // every previous row was kept, when the slab is read again from S_alt
+    load_slab(A.S_in);
+
+    int np = 0;
+    if (A.n_pre) {
+        np = A.n_pre[b];
+        np = np < 0 ? 0 : (np > Tp ? Tp : np);
+        if (ROLLBACK) {
+            if (bx == 0 && h == 0 && tid == 0) A.kv_len[b] += np;
+            if (np == Tp) return;            // state_out already holds S_T
+        } else if (np == Tp && A.S_alt) {
+            load_slab(A.S_alt);              // every previous row kept: its S_T, nothing to replay
+            np = 0;
+        }
+    }
+    const int nm = ROLLBACK ? 0 : T;         // rows of this call
+    const int n = np + nm;
 
     xv_gdn_stage<DK, W, NT>(A, b, h, g, j0, np, n, sm.skq, sm.sv, sm.sab);
 #pragma unroll
