@@ -51,7 +51,8 @@ constexpr int XV_ATTN_C = 256;      // chunk length (positions), fixed for every
 constexpr int XV_ATTN_WAVES = 8;    // waves of a partial-kernel workgroup
 constexpr int XV_ATTN_MAX_NC = 4608;   // chunks of the capacity (1,179,648 positions), at most
 constexpr int XV_ATTN_G = 8;           // chunks per group of the two-level fold (2048 positions)
-constexpr int XV_ATTN_WIDE_MIN = 128; // (chunk, KV head, request) workgroups from which the wide kernel runs
+constexpr int XV_ATTN_WIDE_MIN = 128; // (chunk, KV head, request) workgroups from which the wide kernel runs (also
+                                      // when the per-tile split would take more than one round)
 constexpr int XV_ATTN_STREAM_MIN = 1024; // ... and from which the persistent streaming kernel runs (about 4 chunks per CU)
 constexpr int XV_COMBINE_U = 24;    // chunks per block of combine loads kept in flight
 static_assert(XV_COMBINE_U % 4 == 0, "the long-row combine reads its per-chunk factors four at a time");
