@@ -69,8 +69,9 @@ def test_gemm_exact_on_integers():
 def test_gemm_row_bits_independent_of_m_and_position(K):
     """Row bits must not depend on M, on the other rows, or on the row's slot in a 16-row tile.
 
-    K = 5120 and 6144 take the LDS-staged kernel for M <= 16 and the x-streaming one for M = 72,
-    K = 1024 the register-streamed one for M <= 32: the bits must agree across all of them."""
+    K = 5120 and 6144 take the LDS-staged kernel for M <= 16 and the row-tile one for M = 72 (at
+    K = 5120 its parts of 4 k-steps end a range inside every other part), K = 1024 the
+    register-streamed one for M <= 32: the bits must agree across all of them."""
     rng = np.random.default_rng(8 + K)
     N = 96
     from bit_exact_speculative_amd.layer import dev_bf16
