@@ -75,10 +75,15 @@ static_assert((2 * XV_COMBINE_U) % XV_ATTN_G == 0, "a block of combine loads hol
 
 // LDS layouts (16-byte granules, XOR-swizzled so that both the cooperative
 // stores and the MFMA fragment reads spread over the banks):
-//   K  : [pos][d]  granule (pos, c = d/8)   at pos * (D/8) + (c ^ (pos & 7))
+//   K  : [pos][d]  granule (pos, c = d/8)   at pos * (D/8) + (c ^ (pos & KX)), KX = 15 (7 at
+//        d = 64): a score MFMA's K fragment (16 positions x 4 granules) then covers sixteen
+//        16-byte bank groups, where pos & 7 left eight
 //   V^T: [d][pos]  granule (d, c = pos/8)   at d * (C/8) + (c ^ ((d ^ (d >> 3)) & 7))
 template <int D>
-__device__ __forceinline__ int xv_k_granule(int pos, int c) { return pos * (D / 8) + (c ^ (pos & 7)); }
+__device__ __forceinline__ int xv_k_granule(int pos, int c) {
+    constexpr int KX = D / 8 > 16 ? 15 : D / 8 - 1;
+    return pos * (D / 8) + (c ^ (pos & KX));
+}
 __device__ __forceinline__ int xv_vt_granule(int d, int c) {
     return d * (XV_ATTN_C / 8) + (c ^ ((d ^ (d >> 3)) & 7));
 }
